@@ -1,0 +1,128 @@
+// C ABI of libttt_mi355x.so: argument validation, workspace queries, dispatch.
+// Every check runs on the host before anything is enqueued; on any error
+// nothing is written.
+#include "../../include/ttt.h"
+#include "ttt_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_enums(int dtype, int loss, int order)
+{
+    return (dtype == TTT_F32 || dtype == TTT_BF16) && (loss == TTT_LOSS_DOT || loss == TTT_LOSS_MSE) &&
+           (order == TTT_CAUSAL || order == TTT_NONCAUSAL);
+}
+
+// Shape checks common to both ops.  Returns TTT_OK or an error code.
+ttt_status check_dims(int B, int H, int Tq, int Tkv, int d, int chunk, int order)
+{
+    if (B < 1 || H < 1 || d < 1 || chunk < 1 || Tq < 0 || Tkv < 0) return TTT_EINVAL;
+    if (order == TTT_CAUSAL && Tq != Tkv) return TTT_EINVAL;
+    // element counts must fit the kernels' 32-bit token indices
+    if ((long long)Tq > (1LL << 30) || (long long)Tkv > (1LL << 30)) return TTT_EUNSUPPORTED;
+    if ((long long)B * H > (1LL << 24)) return TTT_EUNSUPPORTED;
+    return TTT_OK;
+}
+
+bool linear_supported(int d, int chunk) { return (d == 64 || d == 128) && chunk % 16 == 0; }
+
+bool lact_supported(int dtype, int d, int hid, int chunk, int Tkv)
+{
+    if (dtype != TTT_BF16) return false;
+    if (d % 64 != 0 || hid % 64 != 0 || d > 512 || hid > 1024) return false;
+    if (!(chunk % 64 == 0 || chunk >= Tkv)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ttt_status_string(int status)
+{
+    switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_EINVAL: return "invalid argument";
+    case TTT_EUNSUPPORTED: return "unsupported shape or dtype";
+    case TTT_EWORKSPACE: return "workspace too small";
+    case TTT_EHIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+int ttt_abi_version(void) { return 1; }
+
+size_t ttt_linear_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
+                                  int order, int dtype)
+{
+    if (!valid_enums(dtype, loss, order)) return 0;
+    if (check_dims(B, H, Tq, Tkv, d, chunk, order) != TTT_OK) return 0;
+    if (!linear_supported(d, chunk)) return 0;
+    tttk::LinearShape s{B * H, Tq, Tkv, d, chunk, loss, order, dtype == TTT_BF16 ? 1 : 0};
+    return tttk::linear_plan(s).bytes;
+}
+
+ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype, const float *eta,
+                          const float *w_init, void *out, float *w_final, int B, int H, int Tq,
+                          int Tkv, int d, int chunk, int loss, int order, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
+    ttt_status st = check_dims(B, H, Tq, Tkv, d, chunk, order);
+    if (st != TTT_OK) return st;
+    if (!w_init || !w_final || !aligned16(w_init) || !aligned16(w_final)) return TTT_EINVAL;
+    if (Tq > 0 && (!q || !out || !aligned16(q) || !aligned16(out))) return TTT_EINVAL;
+    if (Tkv > 0 && (!k || !v || !eta || !aligned16(k) || !aligned16(v) || !aligned16(eta)))
+        return TTT_EINVAL;
+    if (!linear_supported(d, chunk)) return TTT_EUNSUPPORTED;
+    tttk::LinearShape s{B * H, Tq, Tkv, d, chunk, loss, order, dtype == TTT_BF16 ? 1 : 0};
+    tttk::LinearPlan pl = tttk::linear_plan(s);
+    if (pl.bytes > 0 && (!workspace || !aligned16(workspace))) return TTT_EINVAL;
+    if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
+    hipError_t e = tttk::linear_launch(s, pl, q, k, v, eta, w_init, out, w_final, workspace,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
+size_t lact_swiglu_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden, int chunk,
+                                   int loss, int order, int dtype)
+{
+    if (!valid_enums(dtype, loss, order)) return 0;
+    if (check_dims(B, H, Tq, Tkv, d, chunk, order) != TTT_OK || hidden < 1) return 0;
+    if (!lact_supported(dtype, d, hidden, chunk, Tkv)) return 0;
+    tttk::LactShape s{B * H, Tq, Tkv, d, hidden, chunk, loss, order, 1};
+    return tttk::lact_plan(s).bytes;
+}
+
+ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtype,
+                           const float *eta, const float *w1_init, const float *w2_init,
+                           const float *w3_init, void *out, float *w1_final, float *w2_final,
+                           float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
+                           int chunk, int loss, int order, int rownorm, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
+    ttt_status st = check_dims(B, H, Tq, Tkv, d, chunk, order);
+    if (st != TTT_OK) return st;
+    if (hidden < 1 || (rownorm != 0 && rownorm != 1)) return TTT_EINVAL;
+    const void *ws_ptrs[6] = {w1_init, w2_init, w3_init, w1_final, w2_final, w3_final};
+    for (const void *p : ws_ptrs)
+        if (!p || !aligned16(p)) return TTT_EINVAL;
+    if (Tq > 0 && (!q || !out || !aligned16(q) || !aligned16(out))) return TTT_EINVAL;
+    if (Tkv > 0 && (!k || !v || !eta || !aligned16(k) || !aligned16(v) || !aligned16(eta)))
+        return TTT_EINVAL;
+    if (!lact_supported(dtype, d, hidden, chunk, Tkv)) return TTT_EUNSUPPORTED;
+    tttk::LactShape s{B * H, Tq, Tkv, d, hidden, chunk, loss, order, rownorm};
+    tttk::LactPlan pl = tttk::lact_plan(s);
+    if (pl.bytes > 0 && (!workspace || !aligned16(workspace))) return TTT_EINVAL;
+    if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
+    hipError_t e = tttk::lact_launch(s, pl, q, k, v, eta, w1_init, w2_init, w3_init, out, w1_final,
+                                     w2_final, w3_final, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
+}  // extern "C"

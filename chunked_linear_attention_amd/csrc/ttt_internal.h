@@ -1,0 +1,51 @@
+// Host-side interfaces between the C ABI layer (api.cpp) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace tttk {
+
+// ---- TTT-Linear ---------------------------------------------------------------
+struct LinearShape {
+    int NH;       // batch * heads
+    int Tq, Tkv;  // query and key/value tokens per head
+    int d;        // head dim (64 or 128)
+    int chunk;    // chunk size (multiple of 16)
+    int loss;     // 0 inner product, 1 MSE
+    int order;    // 0 causal, 1 non-causal
+    int bf16;     // 1 bf16 inputs/outputs, 0 fp32
+};
+
+struct LinearPlan {
+    int seg_tokens;   // tokens per segment (multiple of chunk and of 16)
+    int S;            // segments over the key/value sequence
+    int Ssum;         // segments whose affine summary is needed
+    int seg_q;        // tokens per query segment (non-causal apply)
+    int Sq;           // query segments (non-causal apply)
+    size_t offP, offB, offW, bytes;  // workspace layout (bytes)
+};
+
+LinearPlan linear_plan(const LinearShape &s);
+hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void *q, const void *k,
+                         const void *v, const float *eta, const float *w_init, void *out,
+                         float *w_final, void *ws, hipStream_t stream);
+
+// ---- LaCT SwiGLU ---------------------------------------------------------------
+struct LactShape {
+    int NH, Tq, Tkv, d, hid, chunk, loss, order, rownorm;
+};
+struct LactPlan {
+    int nchunks;
+    int maxc;                 // tokens per chunk slot in the workspace
+    size_t bytes;
+    size_t off[16];
+};
+LactPlan lact_plan(const LactShape &s);
+hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
+                       const void *v, const float *eta, const float *w1, const float *w2,
+                       const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
+                       hipStream_t stream);
+
+}  // namespace tttk

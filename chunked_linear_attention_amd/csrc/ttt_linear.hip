@@ -1,0 +1,666 @@
+// TTT-Linear forward on gfx950: segment-parallel chunked gradient descent.
+//
+// What is computed ("Test-Time Training (TTT)" summary page: "TTT definition",
+// examples 1 and 2, "TTT-Linear", "Mini-batch gradient descent"; the parallel
+// formulation of "Test-Time Training with KV Binding Is Secretly Linear
+// Attention"): per (batch, head), with chunk-start state W_c and per-token eta,
+//   U_c     = V_c - K_c W_c (MSE)  or  V_c (inner product)
+//   O_c     = Q_c W_c + ((Q_c K_c^T) * M_incl * eta^T) U_c
+//   W_{c+1} = W_c + K_c^T diag(eta_c) U_c.
+//
+// How it is laid out on the chip (not on the pages):
+//  * Column separability.  Column j of W only ever meets column j of V, U
+//    and O, so one wave owns a 16-column block of the state and runs its
+//    chain with the state resident in MFMA accumulators (fp32), never
+//    leaving registers across chunks.  A workgroup = one wave per column
+//    block, sharing the token tiles it stages in LDS.
+//  * Sub-blocks of 16 tokens.  A chunk of b tokens (b a multiple of 16) is
+//    walked 16 tokens at a time: U uses the chunk-start snapshot of the
+//    state, the inter-chunk read uses the running state (which already holds
+//    the chunk's earlier sub-blocks), and the diagonal 16 x 16 block supplies
+//    the rest of the causal intra-chunk term.  This is the same sum as the
+//    b x b masked product, regrouped; work per token is O(d^2) for every b.
+//  * Segments.  The chunk update is affine in the state,
+//    W_{c+1} = (I - K_c^T H_c K_c) W_c + K_c^T H_c V_c, so a run of whole
+//    chunks (a segment) is one affine map W -> W - P W + B.  Three kernels:
+//      summary : every segment (but the last, causal) computes P and B from
+//                its keys/values alone, all segments in parallel;
+//      prefix  : per (head, column block), W_start(s+1) = W_s - P_s W_s + B_s;
+//      replay  : every segment replays its chunks from W_start(s) and writes
+//                its outputs; the last segment writes the final state.
+//    For the inner-product loss P = 0 and the prefix is a running sum.
+//  * Non-causal order: summary over all segments, prefix to W_final, then an
+//    apply kernel O = Q W_final.
+#include "ttt_device.h"
+#include "ttt_internal.h"
+
+#include <stdlib.h>
+
+namespace tttk {
+
+struct LinParams {
+    const void *q, *k, *v;
+    const float *eta, *w_init;
+    void *out;
+    float *w_final;
+    void *wsP;      // [NH][Ssum][d][d] element type (MSE only)
+    float *wsB;     // [NH][Ssum][d][d]
+    float *wsW;     // [NH][S + 1][d][d]: W_start(s); slot S = final state
+    int NH, Tq, Tkv, chunk, seg_tokens, S, Ssum, seg_q, Sq;
+};
+
+// LDS image of one 16-token sub-block.
+template <typename E, int D> struct alignas(16) SubTile {
+    static constexpr int RP = D + (sizeof(E) == 2 ? 8 : 4);  // padded row pitch (elements)
+    E qs[16][RP];   // Q, token-major
+    E ks[16][RP];   // K, token-major
+    E kt[D][16];    // K, feature-major
+    E vt[D][16];    // V, feature-major
+    float eta[16];
+};
+
+// Which tensors a kernel stages.
+enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
+
+// Cooperative global -> register -> LDS loader with a ring of PD register
+// slots.  The staged tensors are cut into 4-token x 4-feature blocks (D blocks
+// per tensor per sub-block); thread tid moves blocks tid, tid + NT, ... (four
+// row loads each, written token-major and/or feature-major), and threads 0..3
+// also move four eta values each.
+template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
+    typedef typename Vec4<E>::type V4;
+    static constexpr int NTEN = ((STAGE & STAGE_Q) ? 1 : 0) + ((STAGE & STAGE_K) ? 1 : 0) +
+                                ((STAGE & STAGE_V) ? 1 : 0);
+    static constexpr int NBLK = NTEN * D;
+    static constexpr int BPT = (NBLK + NT - 1) / NT;
+    int kind[BPT];  // 0 Q, 1 K, 2 V, -1 none
+    int tb[BPT], fb[BPT];
+    const E *src[BPT];
+    bool eta_thread;
+    V4 r[PD][BPT][4];
+    f32x4 e[PD];
+
+    __device__ void init(int tid, const LinParams &p, int h, int T)
+    {
+        const size_t hoff = (size_t)h * T * D;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int blk = tid + i * NT;
+            const int ten = blk / D, b = blk % D;
+            int k = -1, seen = 0;
+            if (STAGE & STAGE_Q) { if (seen == ten) k = 0; ++seen; }
+            if (STAGE & STAGE_K) { if (seen == ten) k = 1; ++seen; }
+            if (STAGE & STAGE_V) { if (seen == ten) k = 2; ++seen; }
+            if (blk >= NBLK) k = -1;
+            kind[i] = k;
+            tb[i] = b / (D / 4);
+            fb[i] = b % (D / 4);
+            src[i] = (k == 0) ? (const E *)p.q + hoff
+                   : (k == 1) ? (const E *)p.k + hoff
+                   : (k == 2) ? (const E *)p.v + hoff : nullptr;
+        }
+        eta_thread = (STAGE & STAGE_E) && tid < 4;
+    }
+
+    // Issue the loads of the sub-block starting at token tb0 (valid tokens < tend).
+    __device__ __forceinline__ void issue(int s, int tb0, int tend, const float *eta_h)
+    {
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            if (kind[i] >= 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = tb0 + 4 * tb[i] + j;
+                    r[s][i][j] = (t < tend) ? load4<E>(src[i] + (size_t)t * D + 4 * fb[i])
+                                            : zero_vec4<E>();
+                }
+            }
+        }
+        if (eta_thread) {
+            const int ej = threadIdx.x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = tb0 + 4 * ej + j;
+                e[s][j] = (t < tend) ? eta_h[t] : 0.f;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void commit(int s, SubTile<E, D> &tl)
+    {
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int k = kind[i];
+            if (k == 0 || k == 1) {
+                auto rm = (k == 0) ? tl.qs : tl.ks;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) store4<E>(&rm[4 * tb[i] + j][4 * fb[i]], r[s][i][j]);
+            }
+            if (k == 1 || k == 2) {
+                auto fm = (k == 1) ? tl.kt : tl.vt;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    V4 c;
+                    c[0] = r[s][i][0][j];
+                    c[1] = r[s][i][1][j];
+                    c[2] = r[s][i][2][j];
+                    c[3] = r[s][i][3][j];
+                    store4<E>(&fm[4 * fb[i] + j][4 * tb[i]], c);
+                }
+            }
+        }
+        if (eta_thread) *reinterpret_cast<f32x4 *>(&tl.eta[4 * threadIdx.x]) = e[s];
+    }
+};
+
+// Drive the staged loop over the sub-blocks [t0, tend) of one head; `body` is
+// called once per sub-block with the LDS tile and the sub-block's first token.
+template <typename E, int D, int STAGE, int PD, int NT, typename Body>
+__device__ __forceinline__ void run_subblocks(SubTile<E, D> *tiles, Loader<E, D, STAGE, PD, NT> &ld,
+                                              int t0, int tend, const float *eta_h, Body &&body)
+{
+    const int nsb = (tend - t0 + 15) / 16;
+#pragma unroll
+    for (int s = 0; s < PD; ++s)
+        if (s < nsb) ld.issue(s, t0 + 16 * s, tend, eta_h);
+    if (nsb > 0) ld.commit(0, tiles[0]);
+    __syncthreads();
+    for (int sb0 = 0; sb0 < nsb; sb0 += PD) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) {
+            const int sb = sb0 + j;
+            if (sb < nsb) {
+                if (sb + PD < nsb) ld.issue(j, t0 + 16 * (sb + PD), tend, eta_h);
+                if (sb + 1 < nsb) ld.commit((j + 1) % PD, tiles[(sb + 1) & 1]);
+                body(tiles[sb & 1], t0 + 16 * sb);
+                __syncthreads();
+            }
+        }
+    }
+}
+
+template <typename E> __device__ __forceinline__ typename Frag<E>::type lds_frag(const E *p)
+{
+    return load4<E>(p);
+}
+
+// A state tile as MFMA operand.  bf16: hi = bf16(x), lo = bf16(x - hi), so
+// products with exact bf16 inputs keep ~16 mantissa bits of the state (the
+// state sits near the identity, where a single bf16 would lose the update).
+// fp32: hi = x, lo unused.
+template <typename E> struct SplitFrag {
+    typedef typename Frag<E>::type F;
+    static constexpr bool SPLIT = sizeof(E) == 2;
+    F hi, lo;
+    __device__ __forceinline__ void set(f32x4 x)
+    {
+        hi = to_frag<E>(x);
+        if (SPLIT) lo = to_frag<E>(x - frag_to_f32(hi));
+    }
+};
+
+// acc += A(16 x D) * state(D x 16), state as split fragments (B side).
+template <typename E, int ND>
+__device__ __forceinline__ f32x4 mma_state_b(f32x4 acc, const typename Frag<E>::type *A,
+                                             const SplitFrag<E> *S)
+{
+#pragma unroll
+    for (int r = 0; r < ND; r += 2) acc = mma32(acc, A[r], A[r + 1], S[r].hi, S[r + 1].hi);
+    if (SplitFrag<E>::SPLIT) {
+#pragma unroll
+        for (int r = 0; r < ND; r += 2) acc = mma32(acc, A[r], A[r + 1], S[r].lo, S[r + 1].lo);
+    }
+    return acc;
+}
+// acc += state^T(16 x D) * B(D x 16), state as split fragments (A side).
+template <typename E, int ND>
+__device__ __forceinline__ f32x4 mma_state_a(f32x4 acc, const SplitFrag<E> *S,
+                                             const typename Frag<E>::type *B)
+{
+#pragma unroll
+    for (int r = 0; r < ND; r += 2) acc = mma32(acc, S[r].hi, S[r + 1].hi, B[r], B[r + 1]);
+    if (SplitFrag<E>::SPLIT) {
+#pragma unroll
+        for (int r = 0; r < ND; r += 2) acc = mma32(acc, S[r].lo, S[r + 1].lo, B[r], B[r + 1]);
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// summary: P_s (MSE) and B_s of a segment.  The state X = [P | B] starts at 0
+// and follows X <- X + K^T H (R - K X_c) over the segment's chunks, with
+// R = [K | V] (MSE; A = I - P is the product of the chunk transitions) or
+// R = V (inner product, where X_c does not enter).  Column blocks 0..ND-1 of
+// X are P, ND..2ND-1 are B (MSE); each wave owns CPW column blocks.
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool MSE, int CPW, bool SNAP, int PD>
+__global__ __launch_bounds__((MSE ? 2 : 1) * (D / 16) / CPW * 64) void lin_summary(LinParams p)
+{
+    typedef typename Frag<E>::type F;
+    constexpr int ND = D / 16;
+    constexpr int NW = (MSE ? 2 : 1) * ND / CPW;
+    constexpr int NT = NW * 64;
+    __shared__ SubTile<E, D> tiles[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+    const int seg = blockIdx.x % p.Ssum, h = blockIdx.x / p.Ssum;
+    const int T = p.Tkv;
+    const int t0 = seg * p.seg_tokens;
+    const int tend = min(T, t0 + p.seg_tokens);
+
+    Loader<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT> ld;
+    ld.init(threadIdx.x, p, h, T);
+    const float *eta_h = p.eta + (size_t)h * T;
+
+    f32x4 X[CPW][ND];
+    SplitFrag<E> Xr[CPW][ND], Xs[SNAP ? CPW : 1][ND];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            X[c][r] = zero4();
+            Xr[c][r].set(zero4());
+            if (SNAP) Xs[c][r] = Xr[c][r];
+        }
+
+    run_subblocks<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend, eta_h,
+        [&](SubTile<E, D> &tl, int tg) {
+            if (SNAP && MSE && (tg % p.chunk) == 0) {
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                    for (int r = 0; r < ND; ++r) Xs[c][r] = Xr[c][r];
+            }
+            F Ka[ND];
+            if (MSE) {
+#pragma unroll
+                for (int r = 0; r < ND; ++r) Ka[r] = lds_frag<E>(&tl.ks[m][16 * r + 4 * g]);
+            }
+            const f32x4 et = *reinterpret_cast<const f32x4 *>(&tl.eta[4 * g]);
+            F EU[CPW];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const int x = wave * CPW + c;
+                const bool pcol = MSE && x < ND;
+                const int cb = pcol ? x : x - (MSE ? ND : 0);
+                f32x4 U = frag_to_f32(pcol ? lds_frag<E>(&tl.kt[16 * cb + m][4 * g])
+                                           : lds_frag<E>(&tl.vt[16 * cb + m][4 * g]));
+                if (MSE) U = U - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Xs[c] : Xr[c]);
+                EU[c] = to_frag<E>(U * et);
+            }
+            F KtA[ND];
+#pragma unroll
+            for (int r = 0; r < ND; ++r) KtA[r] = lds_frag<E>(&tl.kt[16 * r + m][4 * g]);
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                for (int r = 0; r < ND; ++r) {
+                    X[c][r] = mma16(X[c][r], KtA[r], EU[c]);
+                    if (MSE) Xr[c][r].set(X[c][r]);
+                }
+        });
+
+    const size_t base = ((size_t)h * p.Ssum + seg) * D * D;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int x = wave * CPW + c;
+        const bool pcol = MSE && x < ND;
+        const int cb = pcol ? x : x - (MSE ? ND : 0);
+        if (pcol) {
+            E *dst = (E *)p.wsP + base;
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = (E)X[c][r][j];
+        } else {
+            float *dst = p.wsB + base;
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = X[c][r][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prefix: per (head, column block), one wave per 16-row tile of the state.
+// W_start(0) = w_init; W_start(s+1) = W_start(s) - P_s W_start(s) + B_s.
+// Writes every W_start(s) (slot s of wsW); with WRITE_FINAL also the state
+// after the last summarised segment into slot S and into w_final.
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool MSE, bool WRITE_FINAL>
+__global__ __launch_bounds__((D / 16) * 64) void lin_prefix(LinParams p)
+{
+    typedef typename Frag<E>::type F;
+    constexpr int ND = D / 16;
+    constexpr int PP = 3;  // steps of P/B prefetched ahead
+    __shared__ SplitFrag<E> xch[2][ND][64];
+    const int lane = threadIdx.x & 63, r = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+    const int cb = blockIdx.x % ND, h = blockIdx.x / ND;
+    const float *w0 = p.w_init + (size_t)h * D * D;
+    float *wsW = p.wsW + (size_t)h * (p.S + 1) * D * D;
+
+    f32x4 W;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) W[j] = w0[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wsW[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
+
+    const int nst = p.Ssum;
+    F PA[PP][ND];
+    f32x4 BB[PP];
+    auto issue = [&](int slot, int s) {
+        const size_t base = ((size_t)h * p.Ssum + s) * D * D;
+        if (MSE) {
+            const E *P = (const E *)p.wsP + base;
+#pragma unroll
+            for (int q = 0; q < ND; ++q) PA[slot][q] = load4<E>(P + (size_t)(16 * r + m) * D + 16 * q + 4 * g);
+        }
+        const float *Bm = p.wsB + base;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) BB[slot][j] = Bm[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
+    };
+#pragma unroll
+    for (int s = 0; s < PP; ++s)
+        if (s < nst) issue(s, s);
+    for (int s0 = 0; s0 < nst; s0 += PP) {
+#pragma unroll
+        for (int jj = 0; jj < PP; ++jj) {
+            const int s = s0 + jj;
+            if (s < nst) {
+                if (MSE) {
+                    SplitFrag<E> mine;
+                    mine.set(W);
+                    xch[s & 1][r][lane] = mine;
+                    __syncthreads();
+                    SplitFrag<E> Wb[ND];
+#pragma unroll
+                    for (int q = 0; q < ND; ++q) Wb[q] = xch[s & 1][q][lane];
+                    W = W - mma_state_b<E, ND>(zero4(), PA[jj], Wb);
+                }
+                W = W + BB[jj];
+                if (s + PP < nst) issue(jj, s + PP);
+                float *dst = wsW + (size_t)(s + 1) * D * D;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
+            }
+        }
+    }
+    if (WRITE_FINAL) {
+        float *wf = p.w_final + (size_t)h * D * D;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// replay (causal): outputs of one segment from its start state.  Each wave
+// owns CPW column blocks; the query/key fragments and the masked Q K^T block
+// are shared by them.  SNAP: chunks longer than one sub-block need a separate
+// chunk-start snapshot of the state for the residual.
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool MSE, int CPW, bool SNAP, int PD>
+__global__ __launch_bounds__((D / 16) / CPW * 64) void lin_replay(LinParams p)
+{
+    typedef typename Frag<E>::type F;
+    constexpr int ND = D / 16;
+    constexpr int NW = ND / CPW;
+    constexpr int NT = NW * 64;
+    __shared__ SubTile<E, D> tiles[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+    const int seg = blockIdx.x % p.S, h = blockIdx.x / p.S;
+    const int T = p.Tkv;
+    const int t0 = seg * p.seg_tokens;
+    const int tend = min(T, t0 + p.seg_tokens);
+
+    const float *ws = (p.S > 1) ? p.wsW + ((size_t)h * (p.S + 1) + seg) * D * D
+                                : p.w_init + (size_t)h * D * D;
+    f32x4 W[CPW][ND];
+    SplitFrag<E> Wr[CPW][ND], Ws[SNAP ? CPW : 1][ND];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int cb = wave * CPW + c;
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) W[c][r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
+            Wr[c][r].set(W[c][r]);
+            if (SNAP) Ws[c][r] = Wr[c][r];
+        }
+    }
+
+    Loader<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT> ld;
+    ld.init(threadIdx.x, p, h, T);
+    const float *eta_h = p.eta + (size_t)h * T;
+    E *out_h = (E *)p.out + (size_t)h * T * D;
+
+    run_subblocks<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend, eta_h,
+        [&](SubTile<E, D> &tl, int tg) {
+            if (SNAP && MSE && (tg % p.chunk) == 0) {
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                    for (int r = 0; r < ND; ++r) Ws[c][r] = Wr[c][r];
+            }
+            F Qa[ND], Ka[ND];
+#pragma unroll
+            for (int r = 0; r < ND; ++r) {
+                Qa[r] = lds_frag<E>(&tl.qs[m][16 * r + 4 * g]);
+                Ka[r] = lds_frag<E>(&tl.ks[m][16 * r + 4 * g]);
+            }
+            const f32x4 et = *reinterpret_cast<const f32x4 *>(&tl.eta[4 * g]);
+            // S^T[i][t] = k_i . q_t, kept for i <= t, times eta_i.
+            f32x4 St = zero4();
+#pragma unroll
+            for (int r = 0; r < ND; r += 2) St = mma32(St, Ka[r], Ka[r + 1], Qa[r], Qa[r + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) St[j] = (4 * g + j <= m) ? St[j] * et[j] : 0.f;
+            const F Sf = to_frag<E>(St);
+            const int t = tg + m;
+            F EU[CPW];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const int cb = wave * CPW + c;
+                f32x4 U = frag_to_f32(lds_frag<E>(&tl.vt[16 * cb + m][4 * g]));
+                if (MSE) U = U - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Ws[c] : Wr[c]);
+                // O^T = W_run^T Q^T + U^T S^T
+                f32x4 O = mma_state_a<E, ND>(zero4(), Wr[c], Qa);
+                O = mma16(O, to_frag<E>(U), Sf);
+                if (t < tend) store4<E>(out_h + (size_t)t * D + 16 * cb + 4 * g, out4<E>(O));
+                EU[c] = to_frag<E>(U * et);
+            }
+            // W += K^T (eta * U)
+            F KtA[ND];
+#pragma unroll
+            for (int r = 0; r < ND; ++r) KtA[r] = lds_frag<E>(&tl.kt[16 * r + m][4 * g]);
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                for (int r = 0; r < ND; ++r) {
+                    W[c][r] = mma16(W[c][r], KtA[r], EU[c]);
+                    Wr[c][r].set(W[c][r]);
+                }
+        });
+
+    if (seg == p.S - 1) {
+        float *wf = p.w_final + (size_t)h * D * D;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int cb = wave * CPW + c;
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[c][r][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// apply (non-causal): O = Q W_final over query segments.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int CPW, int PD>
+__global__ __launch_bounds__((D / 16) / CPW * 64) void lin_apply(LinParams p, const float *wsrc,
+                                                                 size_t wsrc_head_stride)
+{
+    typedef typename Frag<E>::type F;
+    constexpr int ND = D / 16;
+    constexpr int NT = ND / CPW * 64;
+    __shared__ SubTile<E, D> tiles[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+    const int seg = blockIdx.x % p.Sq, h = blockIdx.x / p.Sq;
+    const int T = p.Tq;
+    const int t0 = seg * p.seg_q;
+    const int tend = min(T, t0 + p.seg_q);
+    const float *ws = wsrc + (size_t)h * wsrc_head_stride;
+    SplitFrag<E> Wr[CPW][ND];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            f32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * (wave * CPW + c) + m];
+            Wr[c][r].set(w);
+        }
+    Loader<E, D, STAGE_Q, PD, NT> ld;
+    ld.init(threadIdx.x, p, h, T);
+    E *out_h = (E *)p.out + (size_t)h * T * D;
+    run_subblocks<E, D, STAGE_Q, PD, NT>(tiles, ld, t0, tend, nullptr,
+        [&](SubTile<E, D> &tl, int tg) {
+            F Qa[ND];
+#pragma unroll
+            for (int r = 0; r < ND; ++r) Qa[r] = lds_frag<E>(&tl.qs[m][16 * r + 4 * g]);
+            const int t = tg + m;
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const f32x4 O = mma_state_a<E, ND>(zero4(), Wr[c], Qa);
+                if (t < tend) store4<E>(out_h + (size_t)t * D + 16 * (wave * CPW + c) + 4 * g, out4<E>(O));
+            }
+        });
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static int env_int(const char *name, int dflt)
+{
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+LinearPlan linear_plan(const LinearShape &s)
+{
+    LinearPlan pl{};
+    const int T = s.Tkv;
+    // Segment length: whole chunks, enough segments to give every CU a few
+    // workgroups, at least 64 tokens.
+    const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 1024);
+    long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : s.chunk;
+    if (seg < 64) seg = 64;
+    const int forced = env_int("TTT_LINEAR_SEG_TOKENS", 0);
+    if (forced > 0) seg = forced;
+    seg = (seg + s.chunk - 1) / s.chunk * s.chunk;
+    if (T > 0 && seg > T) seg = (T + s.chunk - 1) / s.chunk * s.chunk;
+    pl.seg_tokens = (int)seg;
+    pl.S = (T > 0) ? (int)((T + seg - 1) / seg) : 0;
+    pl.Ssum = (s.order == 0) ? (pl.S > 0 ? pl.S - 1 : 0) : pl.S;
+    long long segq = (s.Tq > 0) ? ((long long)s.NH * s.Tq + target_wg - 1) / target_wg : 16;
+    if (segq < 64) segq = 64;
+    segq = (segq + 15) / 16 * 16;
+    pl.seg_q = (int)segq;
+    pl.Sq = (s.Tq > 0) ? (int)((s.Tq + segq - 1) / segq) : 0;
+    const size_t esz = s.bf16 ? 2 : 4;
+    const size_t dd = (size_t)s.d * s.d;
+    size_t off = 0;
+    pl.offP = off;
+    if (s.loss == 1) off = align_up(off + (size_t)s.NH * pl.Ssum * dd * esz, 256);
+    pl.offB = off;
+    off = align_up(off + (size_t)s.NH * pl.Ssum * dd * 4, 256);
+    pl.offW = off;
+    off = align_up(off + (size_t)s.NH * (pl.S + 1) * dd * 4, 256);
+    pl.bytes = off;
+    return pl;
+}
+
+template <typename E, int D, bool MSE, bool SNAP>
+static hipError_t launch_typed(const LinearShape &s, const LinearPlan &pl, LinParams p,
+                               hipStream_t st)
+{
+    constexpr int ND = D / 16;
+    constexpr int PD = 3;
+    constexpr int CPW_R = (D == 128) ? 2 : 1;             // replay / apply
+    constexpr int CPW_S = (MSE || D == 128) ? 2 : 1;      // summary
+    constexpr int NW_S = (MSE ? 2 : 1) * ND / CPW_S;
+    if (s.Tkv > 0) {
+        if (pl.Ssum > 0) {
+            lin_summary<E, D, MSE, CPW_S, SNAP, PD><<<dim3(s.NH * pl.Ssum), dim3(NW_S * 64), 0, st>>>(p);
+            if (s.order == 0)
+                lin_prefix<E, D, MSE, false><<<dim3(s.NH * ND), dim3(ND * 64), 0, st>>>(p);
+            else
+                lin_prefix<E, D, MSE, true><<<dim3(s.NH * ND), dim3(ND * 64), 0, st>>>(p);
+        }
+        if (s.order == 0) {
+            lin_replay<E, D, MSE, CPW_R, SNAP, PD><<<dim3(s.NH * pl.S), dim3(ND / CPW_R * 64), 0, st>>>(p);
+        } else if (pl.Sq > 0) {
+            lin_apply<E, D, CPW_R, PD><<<dim3(s.NH * pl.Sq), dim3(ND / CPW_R * 64), 0, st>>>(
+                p, p.wsW + (size_t)pl.S * D * D, (size_t)(pl.S + 1) * D * D);
+        }
+    } else {
+        // No key/value tokens: the state is unchanged.
+        if (p.w_final != p.w_init) {
+            hipError_t e = hipMemcpyAsync(p.w_final, p.w_init, (size_t)s.NH * D * D * 4,
+                                          hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return e;
+        }
+        if (s.order == 1 && pl.Sq > 0)
+            lin_apply<E, D, CPW_R, PD><<<dim3(s.NH * pl.Sq), dim3(ND / CPW_R * 64), 0, st>>>(
+                p, p.w_init, (size_t)D * D);
+    }
+    return hipGetLastError();
+}
+
+hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void *q, const void *k,
+                         const void *v, const float *eta, const float *w_init, void *out,
+                         float *w_final, void *ws, hipStream_t stream)
+{
+    LinParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.eta = eta;
+    p.w_init = w_init;
+    p.out = out;
+    p.w_final = w_final;
+    p.wsP = (char *)ws + pl.offP;
+    p.wsB = (float *)((char *)ws + pl.offB);
+    p.wsW = (float *)((char *)ws + pl.offW);
+    p.NH = s.NH;
+    p.Tq = s.Tq;
+    p.Tkv = s.Tkv;
+    p.chunk = s.chunk;
+    p.seg_tokens = pl.seg_tokens;
+    p.S = pl.S;
+    p.Ssum = pl.Ssum;
+    p.seg_q = pl.seg_q;
+    p.Sq = pl.Sq;
+    const bool mse = s.loss == 1;
+    const bool snap = s.chunk > 16;
+#define TTT_DISPATCH(E, D)                                                            \
+    if (mse) return snap ? launch_typed<E, D, true, true>(s, pl, p, stream)           \
+                         : launch_typed<E, D, true, false>(s, pl, p, stream);         \
+    return launch_typed<E, D, false, false>(s, pl, p, stream);
+    if (s.bf16) {
+        if (s.d == 64) { TTT_DISPATCH(__bf16, 64) }
+        if (s.d == 128) { TTT_DISPATCH(__bf16, 128) }
+    } else {
+        if (s.d == 64) { TTT_DISPATCH(float, 64) }
+        if (s.d == 128) { TTT_DISPATCH(float, 128) }
+    }
+#undef TTT_DISPATCH
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tttk

@@ -1,0 +1,108 @@
+"""Python entry points with the C ABI's names: marshalling only.
+
+Tensors follow include/ttt.h: q [B,H,Tq,d], k/v [B,H,Tkv,d] (bf16 or fp32,
+contiguous, on the GPU), eta [B,H,Tkv] fp32, states fp32.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import TTT_OK, TTTError, load
+
+LOSS_DOT, LOSS_MSE = 0, 1
+CAUSAL, NONCAUSAL = 0, 1
+_DT = {torch.float32: 0, torch.bfloat16: 1}
+_LOSS = {"dot": LOSS_DOT, "inner": LOSS_DOT, "mse": LOSS_MSE, LOSS_DOT: LOSS_DOT, LOSS_MSE: LOSS_MSE}
+_ORDER = {"causal": CAUSAL, "noncausal": NONCAUSAL, "non-causal": NONCAUSAL, CAUSAL: CAUSAL,
+          NONCAUSAL: NONCAUSAL}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def ttt_linear_workspace_bytes(B, H, Tq, Tkv, d, chunk, loss, order, dtype) -> int:
+    return int(load().ttt_linear_workspace_bytes(B, H, Tq, Tkv, d, chunk, _LOSS[loss],
+                                                 _ORDER[order], _DT[dtype]))
+
+
+def ttt_linear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
+                   w_init: torch.Tensor, *, chunk: int, loss="mse", order="causal",
+                   out: Optional[torch.Tensor] = None, w_final: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """TTT-Linear forward.  Returns (out [B,H,Tq,d], w_final [B,H,d,d])."""
+    lib = load()
+    B, H, Tq, d = q.shape
+    Tkv = k.shape[2]
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dt)
+    _check(eta, "eta", torch.float32)
+    _check(w_init, "w_init", torch.float32)
+    if out is None:
+        out = torch.empty_like(q)
+    if w_final is None:
+        w_final = torch.empty_like(w_init)
+    ls, od = _LOSS[loss], _ORDER[order]
+    nbytes = lib.ttt_linear_workspace_bytes(B, H, Tq, Tkv, d, chunk, ls, od, _DT[dt])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.ttt_linear_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(eta), _ptr(w_init), _ptr(out),
+                            _ptr(w_final), B, H, Tq, Tkv, d, chunk, ls, od, _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "ttt_linear_fwd")
+    return out, w_final
+
+
+def lact_swiglu_workspace_bytes(B, H, Tq, Tkv, d, hidden, chunk, loss, order, dtype) -> int:
+    return int(load().lact_swiglu_workspace_bytes(B, H, Tq, Tkv, d, hidden, chunk, _LOSS[loss],
+                                                  _ORDER[order], _DT[dtype]))
+
+
+def lact_swiglu_fwd(q, k, v, eta, w1, w2, w3, *, chunk: int, loss="dot", order="causal",
+                    rownorm: bool = True, out=None, w1_final=None, w2_final=None, w3_final=None,
+                    workspace=None, stream=None):
+    """LaCT SwiGLU forward.  Returns (out, w1_final, w2_final, w3_final)."""
+    lib = load()
+    B, H, Tq, d = q.shape
+    Tkv = k.shape[2]
+    hid = w1.shape[2]
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dt)
+    _check(eta, "eta", torch.float32)
+    for t, n in ((w1, "w1"), (w2, "w2"), (w3, "w3")):
+        _check(t, n, torch.float32)
+    out = torch.empty_like(q) if out is None else out
+    w1_final = torch.empty_like(w1) if w1_final is None else w1_final
+    w2_final = torch.empty_like(w2) if w2_final is None else w2_final
+    w3_final = torch.empty_like(w3) if w3_final is None else w3_final
+    ls, od = _LOSS[loss], _ORDER[order]
+    nbytes = lib.lact_swiglu_workspace_bytes(B, H, Tq, Tkv, d, hid, chunk, ls, od, _DT[dt])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.lact_swiglu_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(eta), _ptr(w1), _ptr(w2),
+                             _ptr(w3), _ptr(out), _ptr(w1_final), _ptr(w2_final), _ptr(w3_final),
+                             B, H, Tq, Tkv, d, hid, chunk, ls, od, int(bool(rownorm)),
+                             _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "lact_swiglu_fwd")
+    return out, w1_final, w2_final, w3_final

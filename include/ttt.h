@@ -1,0 +1,147 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) TTT-layer forward library
+ *          (libttt_mi355x.so).
+ *
+ * The library computes the forward pass of a test-time-training layer with
+ * KV binding, entered after the slow projections: per (batch, head) it takes
+ * queries, keys, values, a per-token learning rate eta and an initial fast
+ * weight, runs chunked ("mini-batch") gradient descent on the fast weight and
+ * returns the outputs and the final fast weight.
+ *
+ * Sources (web pages; sections as titled on the pages):
+ *   [TTT]  "Test-Time Training (TTT)" summary of *Learning to (Learn at Test
+ *          Time)*: "TTT definition" (fast weight W_t, W_t = W_{t-1} -
+ *          eta_t grad L, y_t = f(q_t, W_t)); example 1 (inner-product loss
+ *          -(kW).v, the linear-attention update); example 2 (MSE loss
+ *          1/2||kW - v||^2, the delta rule); "TTT-Linear" (f(x, W) = x W);
+ *          "Mini-batch gradient descent" (within a chunk every gradient is
+ *          taken at the chunk-start state and the chunk's gradients summed).
+ *   [KVB]  "Test-Time Training with KV Binding Is Secretly Linear Attention",
+ *          abstract: the layer is a learned linear-attention operator with a
+ *          fully parallel formulation.
+ *   [LaCT] "LaCT: Test-Time Training Done Right": section 3.2 (SwiGLU fast
+ *          weight with three matrices, negative inner-product loss, per-token
+ *          learning rate, chunk gradient summed), section 3.3 (update, then L2
+ *          normalisation of the fast weights), section 4 (causal
+ *          apply-then-update order; update-all-then-apply order).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are HIP device pointers owned by the caller.  The
+ *     library never allocates device memory and keeps no state between calls;
+ *     scratch space is the caller's `workspace` (size from the matching
+ *     *_workspace_bytes query).  Calls on different streams with distinct
+ *     workspaces and outputs may run concurrently.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  Buffers must stay alive
+ *     until the stream has passed the call.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     On any error nothing is written and the status says why.
+ *   - Layouts are dense, row-major (C order), no strides:
+ *       q [B][H][Tq][d], k and v [B][H][Tkv][d] in `dtype`;
+ *       eta [B][H][Tkv] fp32; out [B][H][Tq][d] in `dtype`.
+ *   - Chunk c covers key tokens [c*chunk, min((c+1)*chunk, Tkv)); the last
+ *     chunk may be short.
+ *   - Rounding: bf16 inputs are used as given; products run on bf16 matrix
+ *     cores with fp32 accumulation; the state is kept in fp32 and rounded to
+ *     bf16 only as a matrix-core operand.  fp32 inputs run on fp32 matrix
+ *     cores end to end.  Outputs are rounded to `dtype` (nearest even).
+ */
+#ifndef TTT_MI355X_H
+#define TTT_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TTT_OK = 0,
+    TTT_EINVAL = -1,        /* null pointer, misaligned pointer, bad size or enum   */
+    TTT_EUNSUPPORTED = -2,  /* valid arguments for which no kernel is built         */
+    TTT_EWORKSPACE = -3,    /* workspace smaller than the *_workspace_bytes answer  */
+    TTT_EHIP = -4           /* a HIP launch or query failed                          */
+} ttt_status;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* Inner-product loss L_t = -f(k_t) . v_t ([TTT] example 1; [LaCT] 3.2), or
+ * MSE loss L_t = 1/2 ||f(k_t) - v_t||^2 ([TTT] example 2). */
+typedef enum { TTT_LOSS_DOT = 0, TTT_LOSS_MSE = 1 } ttt_loss;
+
+/* TTT_CAUSAL: Tq == Tkv.  TTT-Linear: y_t = q_t W_t where W_t already holds
+ * the summed gradients of tokens chunk_start..t (inclusive), each taken at the
+ * chunk-start state ([TTT] "TTT definition" and "Mini-batch gradient
+ * descent").  LaCT: the chunk's queries read the chunk-start weights, then
+ * the chunk updates them ([LaCT] section 4).
+ * TTT_NONCAUSAL: all Tkv key/value tokens update the state chunk by chunk,
+ * then every one of the Tq queries reads the final state ([LaCT] section 4,
+ * the view-synthesis order). */
+typedef enum { TTT_CAUSAL = 0, TTT_NONCAUSAL = 1 } ttt_order;
+
+/* Human-readable name of a status code (static storage). */
+const char *ttt_status_string(int status);
+
+/* Version of this ABI (bumped on any incompatible change). */
+int ttt_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * TTT-Linear ([TTT] "TTT-Linear"): f(x, W) = x W with a d x d fp32 fast
+ * weight per (batch, head), row-vector convention.  Per chunk c with
+ * chunk-start state W_c, H_c = diag(eta over the chunk) and M the inclusive
+ * lower-triangular mask (i <= t):
+ *   U_c     = V_c - K_c W_c     (MSE)   or   V_c   (DOT)
+ *   O_c     = Q_c W_c + ((Q_c K_c^T) * M * eta^T) U_c       (causal)
+ *   W_{c+1} = W_c + K_c^T H_c U_c
+ * which is the token-by-token rule with y_t read after token t's update.
+ * Non-causal: the same updates over all key chunks, then O = Q W_final.
+ *
+ * w_init  [B][H][d][d] fp32 (w[in][out]); read only.
+ * w_final [B][H][d][d] fp32; written; may alias w_init exactly (in-place
+ *         state carry), any other overlap with an input is an error of the
+ *         caller's.
+ * Supported: d in {64, 128}; chunk a positive multiple of 16 (any Tkv,
+ * ragged tails included); dtype TTT_F32 or TTT_BF16.  Tkv == 0 copies
+ * w_init to w_final; Tq == 0 writes no output.  16-byte aligned pointers.
+ * Returns TTT_EUNSUPPORTED for other d or chunk values.
+ * ------------------------------------------------------------------------ */
+size_t ttt_linear_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
+                                  int order, int dtype);
+
+ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype,
+                          const float *eta, const float *w_init, void *out, float *w_final,
+                          int B, int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * LaCT SwiGLU ([LaCT] section 3.2): f(x) = W2 (silu(W1 x) * (W3 x)) per
+ * (batch, head), column convention, silu(z) = z * sigmoid(z).
+ *   w1, w3 [B][H][hidden][d] fp32 (out x in); w2 [B][H][d][hidden] fp32.
+ * Per chunk, with the chunk-start weights:
+ *   causal: O_c = f(Q_c) first, then the update;
+ *   update: W <- W - grad_W sum_{t in chunk} eta_t L_t  (plain GD), then,
+ *           when rownorm != 0, every row of W1, W3 (length d) and of W2
+ *           (length hidden) is rescaled to its L2 norm before the update
+ *           ([LaCT] section 3.3); a row whose new norm is 0 is left as is.
+ *   non-causal: all updates, then O = f(Q) with the final weights.
+ * There is no intra-chunk term (causality inside a chunk belongs to the
+ * window attention beside the layer, [LaCT] section 4).
+ * Finals may alias the matching inits exactly.
+ * Supported: dtype TTT_BF16; d and hidden multiples of 64 with d <= 512 and
+ * hidden <= 1024; chunk a positive multiple of 64 or >= Tkv; any loss/order.
+ * ------------------------------------------------------------------------ */
+size_t lact_swiglu_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden, int chunk,
+                                   int loss, int order, int dtype);
+
+ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtype,
+                           const float *eta, const float *w1_init, const float *w2_init,
+                           const float *w3_init, void *out, float *w1_final, float *w2_final,
+                           float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
+                           int chunk, int loss, int order, int rownorm, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_MI355X_H */

@@ -1,0 +1,64 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the GPU, run
+the library, run the oracle on the same (rounded) values, compare.
+
+Tolerances (written out here, used by every test):
+  fp32 path : max|gpu - oracle| / max|oracle| <= 1e-4        (normwise relative)
+  bf16 path : max|gpu - oracle| <= 2e-2 * RMS(oracle)
+The same rule is applied to the state change W_final - W_init (against the
+oracle's change), so that a mis-scaled update cannot hide inside the state.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+FP32_RTOL = 1e-4
+BF16_RMS_TOL = 2e-2
+
+
+def dev(x: np.ndarray, bits: np.ndarray | None = None, dtype=torch.float32) -> torch.Tensor:
+    if dtype == torch.bfloat16:
+        assert bits is not None
+        t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.cuda()
+
+
+def inputs_to_device(inp: dict, dtype: str, names=("q", "k", "v")) -> dict:
+    out = {}
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for n in names:
+        out[n] = dev(inp[n], inp.get(n + "16"), tdt)
+    for n, a in inp.items():
+        if n in names or n.endswith("16"):
+            continue
+        out[n] = dev(a)
+    return out
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def err_stats(got: np.ndarray, ref: np.ndarray) -> dict:
+    diff = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    mx = float(np.max(np.abs(ref))) if ref.size else 0.0
+    md = float(np.max(diff)) if diff.size else 0.0
+    return {"max_abs": md, "rms_ref": rms, "max_ref": mx,
+            "rel_norm": md / mx if mx > 0 else md, "rel_rms": md / rms if rms > 0 else md,
+            "finite": bool(np.all(np.isfinite(got)))}
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    s = err_stats(got, ref)
+    assert s["finite"], f"{what}: non-finite values"
+    if ref.size == 0:
+        return s
+    if dtype == "f32":
+        assert s["rel_norm"] <= FP32_RTOL, f"{what}: max rel err {s['rel_norm']:.3e} > {FP32_RTOL} ({s})"
+    else:
+        assert s["rel_rms"] <= BF16_RMS_TOL, \
+            f"{what}: max abs err {s['max_abs']:.3e} > {BF16_RMS_TOL} x RMS {s['rms_ref']:.3e} ({s})"
+    return s

@@ -1,0 +1,91 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/ttt.h declares, and rejects bad arguments on the host with the
+documented status before any HIP call (no valid device pointer is ever
+passed here, and none is needed: validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_linear_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ttt_abi_version() == 1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert _lib.status_string(code) != "unknown status"
+    assert _lib.status_string(7) == "unknown status"
+
+
+def lin(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w_init=FAKE, out=FAKE, w_final=FAKE, B=1,
+             H=1, Tq=64, Tkv=64, d=64, chunk=16, loss=1, order=0, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.ttt_linear_fwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w_init"], a["out"],
+                              a["w_final"], a["B"], a["H"], a["Tq"], a["Tkv"], a["d"], a["chunk"],
+                              a["loss"], a["order"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.TTT_EINVAL), (dict(k=None), _lib.TTT_EINVAL), (dict(eta=None), _lib.TTT_EINVAL),
+    (dict(w_init=None), _lib.TTT_EINVAL), (dict(w_final=FAKE + 4), _lib.TTT_EINVAL),
+    (dict(q=FAKE + 8), _lib.TTT_EINVAL), (dict(dtype=2), _lib.TTT_EINVAL), (dict(loss=2), _lib.TTT_EINVAL),
+    (dict(order=5), _lib.TTT_EINVAL), (dict(B=0), _lib.TTT_EINVAL), (dict(chunk=0), _lib.TTT_EINVAL),
+    (dict(Tq=32), _lib.TTT_EINVAL), (dict(Tkv=-1, Tq=-1), _lib.TTT_EINVAL),
+    (dict(d=32), _lib.TTT_EUNSUPPORTED), (dict(d=96), _lib.TTT_EUNSUPPORTED),
+    (dict(chunk=8), _lib.TTT_EUNSUPPORTED), (dict(chunk=24), _lib.TTT_EUNSUPPORTED),
+    (dict(wsb=16), _lib.TTT_EWORKSPACE), (dict(ws=None), _lib.TTT_EINVAL),
+])
+def test_linear_validation(kw, code):
+    assert lin(_lib.load(), **kw) == code
+
+
+def test_linear_workspace_query():
+    lib = _lib.load()
+    small = lib.ttt_linear_workspace_bytes(1, 1, 256, 256, 64, 16, 1, 0, 1)
+    big = lib.ttt_linear_workspace_bytes(4, 8, 4096, 4096, 64, 16, 1, 0, 1)
+    assert 0 < small <= big
+    assert lib.ttt_linear_workspace_bytes(1, 1, 256, 256, 32, 16, 1, 0, 1) == 0
+    assert lib.ttt_linear_workspace_bytes(1, 1, 256, 256, 64, 16, 3, 0, 1) == 0
+    # the inner-product loss needs no transition matrices
+    assert lib.ttt_linear_workspace_bytes(4, 8, 4096, 4096, 64, 16, 0, 0, 1) < big
+
+
+def lact(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, out=FAKE,
+             f1=FAKE, f2=FAKE, f3=FAKE, B=1, H=1, Tq=256, Tkv=256, d=64, hid=128, chunk=64, loss=0,
+             order=0, rownorm=1, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.lact_swiglu_fwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w1"], a["w2"],
+                               a["w3"], a["out"], a["f1"], a["f2"], a["f3"], a["B"], a["H"],
+                               a["Tq"], a["Tkv"], a["d"], a["hid"], a["chunk"], a["loss"],
+                               a["order"], a["rownorm"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w2=None), _lib.TTT_EINVAL), (dict(f3=FAKE + 2), _lib.TTT_EINVAL),
+    (dict(rownorm=2), _lib.TTT_EINVAL), (dict(hid=0), _lib.TTT_EINVAL),
+    (dict(Tq=100), _lib.TTT_EINVAL), (dict(dtype=0), _lib.TTT_EUNSUPPORTED),
+    (dict(d=48), _lib.TTT_EUNSUPPORTED), (dict(hid=2048), _lib.TTT_EUNSUPPORTED),
+    (dict(chunk=50), _lib.TTT_EUNSUPPORTED), (dict(wsb=0), _lib.TTT_EWORKSPACE),
+])
+def test_lact_validation(kw, code):
+    assert lact(_lib.load(), **kw) == code
