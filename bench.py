@@ -1,0 +1,314 @@
+"""Benchmark of the TTT-layer forward on one MI355X.
+
+Default workload: TTT-Linear, MSE loss, bf16 inputs with fp32 state, B=4,
+H=8, T=4096, d=64, chunk 16 (causal).  One step = one ttt_linear_fwd call
+over the whole batch (all of the path's kernels), inputs already in HBM.
+
+Prints ONE JSON line: tokens/s (B*T per step), ms per step, the roofline of
+the call (algorithmic HBM bytes per call / average call time, measured with
+HIP events on the stream the library launches on), the chunk-size curve of
+the d=128 workload, the LaCT workloads, and the CPU oracle timed on a bounded
+sample on the host.
+
+Algorithmic bytes of one TTT-Linear call: every head-token reads q, k, v and
+eta and writes o once; every head reads the initial state and writes the final
+state once:  NH*T*((3 + 1)*d*s_in + 4) + NH*2*d*d*4.
+Input sets are rotated (>= 1 GiB in total) so the 256 MiB last-level cache
+cannot hold the working set across steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 matrix, published
+METRIC = "TTT-layer fwd tokens/s + % of roofline (HBM or MFMA) vs chunk size, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def linear_alg_bytes(NH, Tq, Tkv, d, esz):
+    return NH * Tkv * (2 * d * esz + 4) + NH * Tq * 2 * d * esz + NH * 2 * d * d * 4
+
+
+def linear_alg_flops(NH, T, d, b, loss):
+    """Dual-form count: per chunk 2*b*d^2*(3 MSE | 2 DOT) + 2*d*b(b+1)."""
+    full, rem = divmod(T, b)
+    f = 0
+    for n, cnt in ((b, full), (rem, 1 if rem else 0)):
+        f += cnt * (2 * n * d * d * (3 if loss == 1 else 2) + 2 * d * n * (n + 1))
+    return NH * f
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "chunked_linear_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kind: str, workload: str, src_hash: str):
+    """HBM bytes per call from a committed rocprofv3 --pmc summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Rotated:
+    """R copies of a workload's device inputs/outputs, cycled step by step."""
+
+    def __init__(self, make_copy, bytes_per_copy, min_total=1 << 30, max_copies=16):
+        import math
+        self.n = max(1, min(max_copies, math.ceil(min_total / max(bytes_per_copy, 1))))
+        self.sets = [make_copy(i) for i in range(self.n)]
+
+    def __getitem__(self, i):
+        return self.sets[i % self.n]
+
+
+def time_calls(fn, sets, steps, warmup):
+    """Warm up, then time exactly `steps` calls between two device syncs with
+    HIP events recorded on the current stream (the one the library launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i])
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(st)
+    for i in range(steps):
+        fn(sets[i])
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+# ----------------------------------------------------------------------------
+def linear_sets(inp, dtype, R_min_bytes):
+    import numpy as np
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def up(name):
+        if dtype == "bf16":
+            return torch.from_numpy(inp[name + "16"].view(np.int16).copy()).view(torch.bfloat16).cuda()
+        return torch.from_numpy(inp[name]).cuda()
+
+    base = {n: up(n) for n in ("q", "k", "v")}
+    base["eta"] = torch.from_numpy(inp["eta"]).cuda()
+    base["w0"] = torch.from_numpy(inp["w0"]).cuda()
+    per = sum(t.numel() * t.element_size() for t in base.values()) + base["q"].numel() * base["q"].element_size()
+
+    def make(i):
+        if i == 0:
+            d = dict(base)
+        else:
+            d = {n: t.clone() for n, t in base.items()}
+        d["out"] = torch.empty_like(d["q"])
+        d["wf"] = torch.empty_like(d["w0"])
+        return d
+    return Rotated(make, per, R_min_bytes)
+
+
+def bench_linear(B, H, T, d, chunk, loss, dtype, seed, steps, warmup, inp=None, rotate=1 << 30):
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    if inp is None:
+        inp = ti.gen_linear(B, H, T, T, d, seed=seed, dtype=dtype)
+    sets = linear_sets(inp, dtype, rotate)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    nbytes = cla.ttt_linear_workspace_bytes(B, H, T, T, d, chunk, loss, 0, tdt)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call(s):
+        cla.ttt_linear_fwd(s["q"], s["k"], s["v"], s["eta"], s["w0"], chunk=chunk, loss=loss,
+                           out=s["out"], w_final=s["wf"], workspace=ws)
+    ms, wall = time_calls(call, sets, steps, warmup)
+    esz = 2 if dtype == "bf16" else 4
+    NH = B * H
+    alg_b = linear_alg_bytes(NH, T, T, d, esz)
+    alg_f = linear_alg_flops(NH, T, d, chunk, loss)
+    return {"ms": ms, "wall_s": wall, "tokens_per_s": B * T / (ms * 1e-3), "alg_bytes": alg_b,
+            "alg_flops": alg_f, "gbs": alg_b / (ms * 1e-3) / 1e9,
+            "tflops": alg_f / (ms * 1e-3) / 1e12, "copies": sets.n}
+
+
+def lact_alg(NH, Tq, Tkv, d, hid, order):
+    flops = NH * (Tkv * 12 * d * hid + Tq * 6 * d * hid)
+    byts = NH * (Tkv * (2 * d * 2 + 4) + Tq * 2 * d * 2) + NH * 2 * 3 * d * hid * 4
+    return flops, byts
+
+
+def bench_lact(wl, steps, warmup):
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_lact_workload(wl)
+    up = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16).copy()).view(torch.bfloat16).cuda()
+    s = {n: up(n) for n in ("q", "k", "v")}
+    for n in ("eta", "w1", "w2", "w3"):
+        s[n] = torch.from_numpy(inp[n]).cuda()
+    outs = [torch.empty_like(s["q"]), torch.empty_like(s["w1"]), torch.empty_like(s["w2"]),
+            torch.empty_like(s["w3"])]
+    nbytes = cla.lact_swiglu_workspace_bytes(wl.B, wl.H, s["q"].shape[2], wl.Tkv, wl.d, wl.hid,
+                                             wl.chunk, wl.loss, wl.order, torch.bfloat16)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call(_):
+        cla.lact_swiglu_fwd(s["q"], s["k"], s["v"], s["eta"], s["w1"], s["w2"], s["w3"],
+                            chunk=wl.chunk, loss=wl.loss, order=wl.order, rownorm=bool(wl.rownorm),
+                            out=outs[0], w1_final=outs[1], w2_final=outs[2], w3_final=outs[3],
+                            workspace=ws)
+    ms, wall = time_calls(call, [None], steps, warmup)
+    NH = wl.B * wl.H
+    Tq = s["q"].shape[2]
+    flops, byts = lact_alg(NH, Tq, wl.Tkv, wl.d, wl.hid, wl.order)
+    tok = wl.B * (wl.Tkv if wl.order == 0 else wl.Tkv + Tq)
+    return {"workload": wl.name, "ms": ms, "tokens_per_s": tok / (ms * 1e-3),
+            "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "alg_flops": flops, "alg_bytes": byts}
+
+
+def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0):
+    """The oracle as it stands, on the host cores, over whole heads of the workload
+    until about `budget_s` of CPU time has been spent (at least one head)."""
+    import numpy as np
+    import oracle
+    B, H, T, d = inp["q"].shape
+    NH = B * H
+    q = inp["q"].reshape(NH, T, d)
+    k = inp["k"].reshape(NH, T, d)
+    v = inp["v"].reshape(NH, T, d)
+    eta = inp["eta"].reshape(NH, T)
+    w0 = inp["w0"].reshape(NH, d, d)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.ttt_linear(q[:1][None], k[:1][None], v[:1][None], eta[:1][None], w0[:1][None],
+                      chunk=chunk, loss=loss)
+    first = time.perf_counter() - t0
+    # enough whole heads (run in parallel over the host threads) to fill the budget
+    n = int(max(1, min(NH, (budget_s - first) * threads / max(first, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.ttt_linear(q[:n][None], k[:n][None], v[:n][None], eta[:n][None], w0[:n][None],
+                      chunk=chunk, loss=loss)
+    elapsed = first + (time.perf_counter() - t0)
+    heads_done = 1 + n
+    return {"value": heads_done * T / elapsed, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads_done} heads x {T} tokens of the same workload (fp64 token-by-token "
+                      f"C oracle, OpenMP over heads), {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    cla.load_library()
+    torch.cuda.set_device(0)
+
+    wl = ti.MSE_D64
+    seed = ti.WORKLOAD_SEEDS[wl.name]
+    log(f"[bench] generating {wl.name}")
+    inp = ti.gen_linear_workload(wl)
+    log(f"[bench] timing {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    r = bench_linear(wl.B, wl.H, wl.T, wl.d, wl.chunk, wl.loss, wl.dtype, seed, args.steps,
+                     args.warmup, inp=inp)
+    src_hash = kernel_source_hash(["ttt_linear.hip", "ttt_device.h"])
+    traffic = read_traffic("ttt_linear", wl.name, src_hash)
+    line = {
+        "metric": METRIC,
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "seq_len": wl.T,
+                   "head_dim": wl.d, "chunk": wl.chunk, "loss": "mse", "order": "causal",
+                   "state": "fp32", "input_copies_rotated": r["copies"]},
+        "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "unit_of_launch": "one ttt_linear_fwd call (summary, prefix and replay kernels)",
+                     "alg_bytes_per_launch": r["alg_bytes"],
+                     "kernel_source_sha256_16": src_hash},
+    }
+    if not args.no_extras:
+        curve = []
+        log("[bench] generating the d=128 chunk-sweep workload")
+        inp3 = ti.gen_linear_workload(ti.mse_d128(16))
+        for b in (16, 64, 256, 1024):
+            w3 = ti.mse_d128(b)
+            log(f"[bench] timing {w3.name}")
+            c = bench_linear(w3.B, w3.H, w3.T, w3.d, b, w3.loss, w3.dtype, 3, max(20, args.steps // 2),
+                             args.warmup, inp=inp3)
+            pages_r = b / (1 + 2 * b / w3.d)
+            curve.append({"workload": w3.name, "chunk": b, "tokens_per_s": c["tokens_per_s"],
+                          "ms": c["ms"], "hbm_gbs": c["gbs"], "hbm_frac": c["gbs"] / HBM_PEAK_GBS,
+                          "dual_form_tflops": c["tflops"],
+                          "pages_intensity_r_elements": pages_r})
+        del inp3
+        line["chunk_curve"] = curve
+        lact = []
+        for lw in (ti.LACT_CAUSAL, ti.LACT_NONCAUSAL):
+            try:
+                log(f"[bench] timing {lw.name}")
+                lact.append(bench_lact(lw, max(5, args.steps // 10), 2))
+            except Exception as e:  # reported, never hidden
+                lact.append({"workload": lw.name, "error": str(e)})
+        line["lact"] = lact
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline_linear(inp, wl.chunk, wl.loss, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

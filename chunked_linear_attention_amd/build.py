@@ -23,6 +23,8 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           # keep packed fp32 instructions out of the generated code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the VALU work
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -32,13 +32,21 @@ template <> struct Frag<__bf16> { typedef bf16x4 type; };
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // ---- conversions -----------------------------------------------------------
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x)
+// Round to nearest even; compiles to paired v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+
+// x = hi + lo with hi = x truncated to bf16 (low 16 bits cleared, exact in
+// fp32) and lo = bf16(x - hi): about 16 mantissa bits in two bf16 operands.
+__device__ __forceinline__ void split_bf16x4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
 {
-    return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-}
-__device__ __forceinline__ f32x4 to_f32x4(bf16x4 x)
-{
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    const u32x4 xb = __builtin_bit_cast(u32x4, x);
+    const u32x4 hb = xb & 0xFFFF0000u;
+    lo = to_bf16x4(x - __builtin_bit_cast(f32x4, hb));
+    u32x2 h;
+    h[0] = __builtin_amdgcn_perm(xb[1], xb[0], 0x07060302u);
+    h[1] = __builtin_amdgcn_perm(xb[3], xb[2], 0x07060302u);
+    hi = __builtin_bit_cast(bf16x4, h);
 }
 template <typename E> __device__ __forceinline__ typename Frag<E>::type to_frag(f32x4 x);
 template <> __device__ __forceinline__ f32x4 to_frag<float>(f32x4 x) { return x; }
@@ -106,5 +114,18 @@ template <> __device__ __forceinline__ bf16x4 zero_vec4<__bf16>()
 template <typename E> __device__ __forceinline__ typename Vec4<E>::type out4(f32x4 x);
 template <> __device__ __forceinline__ f32x4 out4<float>(f32x4 x) { return x; }
 template <> __device__ __forceinline__ bf16x4 out4<__bf16>(f32x4 x) { return to_bf16x4(x); }
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations (lgkmcnt = 0) and meets the other waves, but leaves global loads
+// in flight (a plain __syncthreads() also drains every outstanding global
+// load, which would defeat the prefetch ring).  The wavefront-scope fences
+// only stop the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt = max, expcnt = max, lgkmcnt = 0
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 }  // namespace tttk

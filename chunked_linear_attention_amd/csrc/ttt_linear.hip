@@ -49,13 +49,15 @@ struct LinParams {
     int NH, Tq, Tkv, chunk, seg_tokens, S, Ssum, seg_q, Sq;
 };
 
-// LDS image of one 16-token sub-block.
+// LDS image of one 16-token sub-block.  Feature-major rows are padded to 20
+// elements so the transposing writes of one wave spread over the banks.
 template <typename E, int D> struct alignas(16) SubTile {
-    static constexpr int RP = D + (sizeof(E) == 2 ? 8 : 4);  // padded row pitch (elements)
+    static constexpr int RP = D + (sizeof(E) == 2 ? 8 : 4);  // token-major row pitch
+    static constexpr int FP = 20;                            // feature-major row pitch
     E qs[16][RP];   // Q, token-major
     E ks[16][RP];   // K, token-major
-    E kt[D][16];    // K, feature-major
-    E vt[D][16];    // V, feature-major
+    E kt[D][FP];    // K, feature-major (tokens 0..15 used)
+    E vt[D][FP];    // V, feature-major
     float eta[16];
 };
 
@@ -63,118 +65,99 @@ template <typename E, int D> struct alignas(16) SubTile {
 enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
 
 // Cooperative global -> register -> LDS loader with a ring of PD register
-// slots.  The staged tensors are cut into 4-token x 4-feature blocks (D blocks
-// per tensor per sub-block); thread tid moves blocks tid, tid + NT, ... (four
-// row loads each, written token-major and/or feature-major), and threads 0..3
-// also move four eta values each.
+// slots.  Every thread runs the same instruction stream: for each staged
+// tensor it moves CPT pieces of 4 consecutive features of one token (8 bytes
+// bf16, 16 bytes fp32) and one eta value, at clamped addresses (rows past the
+// segment end re-read the last valid row), so there is no branch around a
+// load; rows past the end are zeroed when written to LDS.
 template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
     typedef typename Vec4<E>::type V4;
-    static constexpr int NTEN = ((STAGE & STAGE_Q) ? 1 : 0) + ((STAGE & STAGE_K) ? 1 : 0) +
-                                ((STAGE & STAGE_V) ? 1 : 0);
-    static constexpr int NBLK = NTEN * D;
-    static constexpr int BPT = (NBLK + NT - 1) / NT;
-    int kind[BPT];  // 0 Q, 1 K, 2 V, -1 none
-    int tb[BPT], fb[BPT];
-    const E *src[BPT];
-    bool eta_thread;
-    V4 r[PD][BPT][4];
-    f32x4 e[PD];
+    static constexpr bool LQ = STAGE & STAGE_Q, LK = STAGE & STAGE_K, LV = STAGE & STAGE_V,
+                          LE = STAGE & STAGE_E;
+    static constexpr int CPT = (4 * D) / NT;  // pieces per tensor per thread (16 rows x D/4 pieces)
+    static_assert(CPT >= 1 && CPT * NT == 4 * D, "loader shape");
+    int row[CPT], col[CPT];
+    const E *q, *k, *v;
+    V4 rq[PD][CPT], rk[PD][CPT], rv[PD][CPT];
+    float re[PD];
 
     __device__ void init(int tid, const LinParams &p, int h, int T)
     {
         const size_t hoff = (size_t)h * T * D;
+        q = (const E *)p.q + hoff;
+        k = (const E *)p.k + hoff;
+        v = (const E *)p.v + hoff;
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int blk = tid + i * NT;
-            const int ten = blk / D, b = blk % D;
-            int k = -1, seen = 0;
-            if (STAGE & STAGE_Q) { if (seen == ten) k = 0; ++seen; }
-            if (STAGE & STAGE_K) { if (seen == ten) k = 1; ++seen; }
-            if (STAGE & STAGE_V) { if (seen == ten) k = 2; ++seen; }
-            if (blk >= NBLK) k = -1;
-            kind[i] = k;
-            tb[i] = b / (D / 4);
-            fb[i] = b % (D / 4);
-            src[i] = (k == 0) ? (const E *)p.q + hoff
-                   : (k == 1) ? (const E *)p.k + hoff
-                   : (k == 2) ? (const E *)p.v + hoff : nullptr;
+        for (int i = 0; i < CPT; ++i) {
+            const int piece = tid + i * NT;
+            row[i] = piece / (D / 4);
+            col[i] = piece % (D / 4);
         }
-        eta_thread = (STAGE & STAGE_E) && tid < 4;
     }
 
-    // Issue the loads of the sub-block starting at token tb0 (valid tokens < tend).
     __device__ __forceinline__ void issue(int s, int tb0, int tend, const float *eta_h)
     {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            if (kind[i] >= 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = tb0 + 4 * tb[i] + j;
-                    r[s][i][j] = (t < tend) ? load4<E>(src[i] + (size_t)t * D + 4 * fb[i])
-                                            : zero_vec4<E>();
-                }
-            }
+        for (int i = 0; i < CPT; ++i) {
+            const size_t off = (size_t)min(tb0 + row[i], tend - 1) * D + 4 * col[i];
+            if (LQ) rq[s][i] = load4<E>(q + off);
+            if (LK) rk[s][i] = load4<E>(k + off);
+            if (LV) rv[s][i] = load4<E>(v + off);
         }
-        if (eta_thread) {
-            const int ej = threadIdx.x;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = tb0 + 4 * ej + j;
-                e[s][j] = (t < tend) ? eta_h[t] : 0.f;
-            }
-        }
+        if (LE) re[s] = eta_h[min(tb0 + (int)(threadIdx.x & 15), tend - 1)];
     }
 
-    __device__ __forceinline__ void commit(int s, SubTile<E, D> &tl)
+    // Write slot s (the sub-block starting at token tb0) to LDS.
+    __device__ __forceinline__ void commit(int s, SubTile<E, D> &tl, int tb0, int tend)
     {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int k = kind[i];
-            if (k == 0 || k == 1) {
-                auto rm = (k == 0) ? tl.qs : tl.ks;
+        for (int i = 0; i < CPT; ++i) {
+            const bool ok = tb0 + row[i] < tend;
+            const int r = row[i], c = 4 * col[i];
+            if (LQ) store4<E>(&tl.qs[r][c], ok ? rq[s][i] : zero_vec4<E>());
+            if (LK) {
+                const V4 x = ok ? rk[s][i] : zero_vec4<E>();
+                store4<E>(&tl.ks[r][c], x);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) store4<E>(&rm[4 * tb[i] + j][4 * fb[i]], r[s][i][j]);
+                for (int j = 0; j < 4; ++j) tl.kt[c + j][r] = x[j];
             }
-            if (k == 1 || k == 2) {
-                auto fm = (k == 1) ? tl.kt : tl.vt;
+            if (LV) {
+                const V4 x = ok ? rv[s][i] : zero_vec4<E>();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    V4 c;
-                    c[0] = r[s][i][0][j];
-                    c[1] = r[s][i][1][j];
-                    c[2] = r[s][i][2][j];
-                    c[3] = r[s][i][3][j];
-                    store4<E>(&fm[4 * fb[i] + j][4 * tb[i]], c);
-                }
+                for (int j = 0; j < 4; ++j) tl.vt[c + j][r] = x[j];
             }
         }
-        if (eta_thread) *reinterpret_cast<f32x4 *>(&tl.eta[4 * threadIdx.x]) = e[s];
+        if (LE) {
+            const int j = threadIdx.x & 15;
+            tl.eta[j] = (tb0 + j < tend) ? re[s] : 0.f;
+        }
     }
 };
 
 // Drive the staged loop over the sub-blocks [t0, tend) of one head; `body` is
 // called once per sub-block with the LDS tile and the sub-block's first token.
+// The sub-block count is padded up to a multiple of PD so that the ring runs
+// without branches; padded sub-blocks are all-zero (eta = 0) and change
+// nothing, and bodies mask their stores with t < tend.
 template <typename E, int D, int STAGE, int PD, int NT, typename Body>
 __device__ __forceinline__ void run_subblocks(SubTile<E, D> *tiles, Loader<E, D, STAGE, PD, NT> &ld,
                                               int t0, int tend, const float *eta_h, Body &&body)
 {
+    static_assert(PD % 2 == 0, "PD must be even");
     const int nsb = (tend - t0 + 15) / 16;
+    const int ngroups = (nsb + PD - 1) / PD;
 #pragma unroll
-    for (int s = 0; s < PD; ++s)
-        if (s < nsb) ld.issue(s, t0 + 16 * s, tend, eta_h);
-    if (nsb > 0) ld.commit(0, tiles[0]);
-    __syncthreads();
-    for (int sb0 = 0; sb0 < nsb; sb0 += PD) {
+    for (int s = 0; s < PD; ++s) ld.issue(s, t0 + 16 * s, tend, eta_h);
+    ld.commit(0, tiles[0], t0, tend);
+    lds_barrier();
+    for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
         for (int j = 0; j < PD; ++j) {
-            const int sb = sb0 + j;
-            if (sb < nsb) {
-                if (sb + PD < nsb) ld.issue(j, t0 + 16 * (sb + PD), tend, eta_h);
-                if (sb + 1 < nsb) ld.commit((j + 1) % PD, tiles[(sb + 1) & 1]);
-                body(tiles[sb & 1], t0 + 16 * sb);
-                __syncthreads();
-            }
+            const int sb = gi * PD + j;
+            ld.issue(j, t0 + 16 * (sb + PD), tend, eta_h);
+            ld.commit((j + 1) % PD, tiles[(j + 1) & 1], t0 + 16 * (sb + 1), tend);
+            body(tiles[j & 1], t0 + 16 * sb);
+            lds_barrier();
         }
     }
 }
@@ -192,12 +175,20 @@ template <typename E> struct SplitFrag {
     typedef typename Frag<E>::type F;
     static constexpr bool SPLIT = sizeof(E) == 2;
     F hi, lo;
-    __device__ __forceinline__ void set(f32x4 x)
-    {
-        hi = to_frag<E>(x);
-        if (SPLIT) lo = to_frag<E>(x - frag_to_f32(hi));
-    }
+    __device__ __forceinline__ void set(f32x4 x) { set_impl(x, *this); }
+    template <typename S> static __device__ __forceinline__ void set_impl(f32x4 x, S &s);
 };
+
+template <> template <>
+__device__ __forceinline__ void SplitFrag<__bf16>::set_impl(f32x4 x, SplitFrag<__bf16> &s)
+{
+    split_bf16x4(x, s.hi, s.lo);
+}
+template <> template <>
+__device__ __forceinline__ void SplitFrag<float>::set_impl(f32x4 x, SplitFrag<float> &s)
+{
+    s.hi = x;
+}
 
 // acc += A(16 x D) * state(D x 16), state as split fragments (B side).
 template <typename E, int ND>
@@ -333,7 +324,7 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_prefix(LinParams p)
 {
     typedef typename Frag<E>::type F;
     constexpr int ND = D / 16;
-    constexpr int PP = 3;  // steps of P/B prefetched ahead
+    constexpr int PP = (D == 64) ? 8 : 4;  // steps of P/B prefetched ahead (memory latency)
     __shared__ SplitFrag<E> xch[2][ND][64];
     const int lane = threadIdx.x & 63, r = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
     const int cb = blockIdx.x % ND, h = blockIdx.x / ND;
@@ -346,11 +337,15 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_prefix(LinParams p)
 #pragma unroll
     for (int j = 0; j < 4; ++j) wsW[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
 
+    // Steps are padded up to a multiple of PP so the prefetch ring runs
+    // without branches: padded steps read the last valid step's data, add
+    // nothing (masked to zero at use) and rewrite the last slot unchanged.
     const int nst = p.Ssum;
+    const int ngroups = (nst + PP - 1) / PP;
     F PA[PP][ND];
     f32x4 BB[PP];
     auto issue = [&](int slot, int s) {
-        const size_t base = ((size_t)h * p.Ssum + s) * D * D;
+        const size_t base = ((size_t)h * p.Ssum + min(s, nst - 1)) * D * D;
         if (MSE) {
             const E *P = (const E *)p.wsP + base;
 #pragma unroll
@@ -361,29 +356,28 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_prefix(LinParams p)
         for (int j = 0; j < 4; ++j) BB[slot][j] = Bm[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
     };
 #pragma unroll
-    for (int s = 0; s < PP; ++s)
-        if (s < nst) issue(s, s);
-    for (int s0 = 0; s0 < nst; s0 += PP) {
+    for (int s = 0; s < PP; ++s) issue(s, s);
+    for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
         for (int jj = 0; jj < PP; ++jj) {
-            const int s = s0 + jj;
-            if (s < nst) {
-                if (MSE) {
-                    SplitFrag<E> mine;
-                    mine.set(W);
-                    xch[s & 1][r][lane] = mine;
-                    __syncthreads();
-                    SplitFrag<E> Wb[ND];
+            const int s = gi * PP + jj;
+            const bool live = s < nst;
+            f32x4 upd = BB[jj];
+            if (MSE) {
+                SplitFrag<E> mine;
+                mine.set(W);
+                xch[jj & 1][r][lane] = mine;
+                lds_barrier();
+                SplitFrag<E> Wb[ND];
 #pragma unroll
-                    for (int q = 0; q < ND; ++q) Wb[q] = xch[s & 1][q][lane];
-                    W = W - mma_state_b<E, ND>(zero4(), PA[jj], Wb);
-                }
-                W = W + BB[jj];
-                if (s + PP < nst) issue(jj, s + PP);
-                float *dst = wsW + (size_t)(s + 1) * D * D;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
+                for (int q = 0; q < ND; ++q) Wb[q] = xch[jj & 1][q][lane];
+                upd = upd - mma_state_b<E, ND>(zero4(), PA[jj], Wb);
             }
+            W = W + (live ? upd : zero4());
+            issue(jj, s + PP);
+            float *dst = wsW + (size_t)min(s + 1, nst) * D * D;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
         }
     }
     if (WRITE_FINAL) {
@@ -463,9 +457,11 @@ __global__ __launch_bounds__((D / 16) / CPW * 64) void lin_replay(LinParams p)
                 const int cb = wave * CPW + c;
                 f32x4 U = frag_to_f32(lds_frag<E>(&tl.vt[16 * cb + m][4 * g]));
                 if (MSE) U = U - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Ws[c] : Wr[c]);
-                // O^T = W_run^T Q^T + U^T S^T
-                f32x4 O = mma_state_a<E, ND>(zero4(), Wr[c], Qa);
-                O = mma16(O, to_frag<E>(U), Sf);
+                // O^T = W_run^T Q^T + U^T S^T.  The two terms use separate
+                // accumulators: no accumulation chain mixes MFMA shapes
+                // (16x16x32 feeding 16x16x16).
+                const f32x4 Oi = mma16(zero4(), to_frag<E>(U), Sf);
+                const f32x4 O = mma_state_a<E, ND>(zero4(), Wr[c], Qa) + Oi;
                 if (t < tend) store4<E>(out_h + (size_t)t * D + 16 * cb + 4 * g, out4<E>(O));
                 EU[c] = to_frag<E>(U * et);
             }
@@ -557,7 +553,7 @@ LinearPlan linear_plan(const LinearShape &s)
     const int T = s.Tkv;
     // Segment length: whole chunks, enough segments to give every CU a few
     // workgroups, at least 64 tokens.
-    const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 1024);
+    const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 512);
     long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : s.chunk;
     if (seg < 64) seg = 64;
     const int forced = env_int("TTT_LINEAR_SEG_TOKENS", 0);
@@ -590,7 +586,7 @@ static hipError_t launch_typed(const LinearShape &s, const LinearPlan &pl, LinPa
                                hipStream_t st)
 {
     constexpr int ND = D / 16;
-    constexpr int PD = 3;
+    constexpr int PD = (D == 64) ? 8 : 4;  // sub-blocks in flight; even (LDS buffer = slot parity)
     constexpr int CPW_R = (D == 128) ? 2 : 1;             // replay / apply
     constexpr int CPW_S = (MSE || D == 128) ? 2 : 1;      // summary
     constexpr int NW_S = (MSE ? 2 : 1) * ND / CPW_S;
