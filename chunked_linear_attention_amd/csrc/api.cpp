@@ -30,11 +30,13 @@ ttt_status check_dims(int B, int H, int Tq, int Tkv, int d, int chunk, int order
 
 bool linear_supported(int d, int chunk) { return (d == 64 || d == 128) && chunk % 16 == 0; }
 
+// The LaCT kernels tile d and hidden by 128 (GEMM tiles) and never let a
+// 128-token tile straddle two chunks.
 bool lact_supported(int dtype, int d, int hid, int chunk, int Tkv)
 {
     if (dtype != TTT_BF16) return false;
-    if (d % 64 != 0 || hid % 64 != 0 || d > 512 || hid > 1024) return false;
-    if (!(chunk % 64 == 0 || chunk >= Tkv)) return false;
+    if (d % 128 != 0 || hid % 128 != 0 || d > 1024 || hid > 1024) return false;
+    if (!(chunk % 128 == 0 || chunk >= Tkv)) return false;
     return true;
 }
 

@@ -1,8 +1,773 @@
+// LaCT SwiGLU fast-weight forward on gfx950 (bf16 MFMA, fp32 masters).
+//
+// What is computed ("LaCT: Test-Time Training Done Right", sections 3.2,
+// 3.3 and 4): per (batch, head) a fast weight f(x) = W2 (silu(W1 x) * (W3 x))
+// with W1, W3 [hid x d] and W2 [d x hid].  Per chunk of key tokens, with the
+// chunk-start weights:
+//   dY  = -eta * V                       (inner-product loss)
+//       =  eta * (f(K) - V)              (MSE loss)
+//   G   = silu(K W1^T) * (K W3^T)        dG = dY W2
+//   dH3 = dG * silu(K W1^T)              dH1 = dG * (K W3^T) * silu'(K W1^T)
+//   W1 -= dH1^T K,  W3 -= dH3^T K,  W2 -= dY^T G, then (optionally) every row
+//   is rescaled to its L2 norm before the step.
+// Causal: the queries of chunk c read the weights the chunk started with.
+// Non-causal: every query reads the final weights.
+//
+// Kernels (one launch each):
+//   lact_prep     K^T and (-eta V)^T for all tokens; fp32 masters; bf16
+//                 weight copies for chunk 0.
+//   lact_fwdgrad  per (head, 128-token tile, 64-wide hidden slice): the three
+//                 products K W1^T, K W3^T, dY W2 share the d-long contraction;
+//                 the epilogue does the SwiGLU backward and writes G^T, dH1^T,
+//                 dH3^T (hidden-major, token-contiguous: the next GEMM's k).
+//   lact_wgrad    the three weight gradients as NT GEMMs over the chunk's
+//                 tokens, split over tokens, fp32 partials.
+//   lact_update   sums the partials, GD step, row norms, fp32 masters, bf16
+//                 copies of the new weights.
+//   lact_apply1   G_q = silu(Q W1^T) * (Q W3^T) for every query, each with its
+//                 chunk's weights (computed transposed so G_q lands
+//                 token-major).
+//   lact_apply2   O = G_q W2^T (computed transposed so O lands token-major);
+//                 with the MSE loss the same two kernels give f(K) and dY.
+// Every product is a bf16 16x16x32 MFMA with fp32 accumulation; tiles move
+// global -> registers -> LDS with a ring of register stages and LDS-only
+// barriers.
 #include "ttt_device.h"
 #include "ttt_internal.h"
+
 namespace tttk {
-LactPlan lact_plan(const LactShape &s) { LactPlan p{}; (void)s; p.bytes = 256; return p; }
-hipError_t lact_launch(const LactShape &, const LactPlan &, const void *, const void *, const void *,
-                       const float *, const float *, const float *, const float *, void *, float *,
-                       float *, float *, void *, hipStream_t) { return hipErrorNotSupported; }
+
+typedef __bf16 bf16;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// 16 bytes = 8 bf16
+struct alignas(16) B8 {
+    u32x4v v;
+};
+
+__device__ __forceinline__ B8 ld16(const bf16 *p) { return B8{*reinterpret_cast<const u32x4v *>(p)}; }
+__device__ __forceinline__ void st16(bf16 *p, B8 x) { *reinterpret_cast<u32x4v *>(p) = x.v; }
+__device__ __forceinline__ B8 zero16() { return B8{u32x4v{0u, 0u, 0u, 0u}}; }
+__device__ __forceinline__ bf16x8 as_bf8(B8 x) { return __builtin_bit_cast(bf16x8, x.v); }
+
+__device__ __forceinline__ f32x4 mfma32(f32x4 acc, bf16x8 a, bf16x8 b)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Generic NT GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16, k contiguous),
+// block tile 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 32, K a multiple
+// of 32.  Rows of A past M and rows of B past N read as zero.  The epilogue
+// gets the wave's 4 x 4 accumulator tiles: tile (i, q) holds C at rows
+// mbase + 16 i + 4 g + (0..3), column nbase + 16 q + (lane & 15).
+// ---------------------------------------------------------------------------
+constexpr int GBK = 32;
+constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): conflict-free 16-byte fragment reads
+constexpr int GPD = 4;           // register stages in flight (even: LDS buffer = stage parity)
+
+struct GemmLds {
+    bf16 a[2][128][GPITCH];
+    bf16 b[2][128][GPITCH];
+};
+
+// K is cut into nseg segments of kseg (a multiple of 32); segment s reads A
+// from As[s] and B from Bs[s] (same leading dimensions).  This sums products
+// of split operands (hi and lo bf16 parts) in one accumulation.
+template <typename Epi>
+__device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, long lda,
+                                             const bf16 *const *Bs, long ldb, int M, int N,
+                                             int kseg, int nseg, int m0, int n0, Epi &&epi)
+{
+    const int K = kseg * nseg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, mm = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    int lrow[2], lcol[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pc = tid + 256 * i;
+        lrow[i] = pc >> 2;
+        lcol[i] = (pc & 3) * 8;
+    }
+    const int nst = K / GBK;
+    const int ngroups = (nst + GPD - 1) / GPD;
+    B8 ra[GPD][2], rb[GPD][2];
+    auto issue = [&](int s, int st) {
+        const int kk = min(st, nst - 1) * GBK;
+        const int sg = kk / kseg, kin = kk - sg * kseg;
+        const bf16 *A = As[sg], *B = Bs[sg];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol[i]);
+            rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol[i]);
+        }
+    };
+    auto commit = [&](int s, int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            st16(&L.a[buf][lrow[i]][lcol[i]], (m0 + lrow[i] < M) ? ra[s][i] : zero16());
+            st16(&L.b[buf][lrow[i]][lcol[i]], (n0 + lrow[i] < N) ? rb[s][i] : zero16());
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = zero4();
+
+#pragma unroll
+    for (int s = 0; s < GPD; ++s) issue(s, s);
+    commit(0, 0);
+    lds_barrier();
+    for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+        for (int j = 0; j < GPD; ++j) {
+            const int st = gi * GPD + j;
+            issue(j, st + GPD);
+            commit((j + 1) % GPD, (j + 1) & 1);
+            const int buf = j & 1;
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = as_bf8(ld16(&L.a[buf][wm * 64 + 16 * i + mm][8 * g]));
+                bfr[i] = as_bf8(ld16(&L.b[buf][wn * 64 + 16 * i + mm][8 * g]));
+            }
+            if (st < nst) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
+            }
+            lds_barrier();
+        }
+    }
+    epi(acc, m0 + wm * 64, n0 + wn * 64, g, mm);
+}
+
+// ---------------------------------------------------------------------------
+// parameters shared by the kernels
+// ---------------------------------------------------------------------------
+struct LactParams {
+    const bf16 *q, *k, *v;
+    const float *eta;
+    const float *w1i, *w2i, *w3i;
+    bf16 *out;
+    float *w1, *w2, *w3;        // fp32 masters (the final-state buffers)
+    int NH, Tq, Tkv, d, hid, chunk, nchunks, cpad, tpad, qpad, loss, order, rownorm, splitk;
+    bf16 *kt;      // [NH][d][tpad]    K^T
+    bf16 *dyt;     // [NH][d][tpad]    dY^T: (-eta V)^T for all tokens (inner product); per chunk (MSE)
+    bf16 *dy;      // [NH][cpad][d]    dY token-major (MSE)
+    bf16 *w13b;    // [nslots][NH][2 parts][2 hid][d]  W1/W3 rows interleaved by 16; part 0 =
+                   //   bf16(W) (nearest), part 1 = bf16(W - part 0)
+    bf16 *w2b;     // [nslots][NH][2 parts][d][hid]
+    bf16 *gt;      // [NH][hid][cpad]  G^T of the current chunk
+    bf16 *dh1t;    // [NH][hid][cpad]
+    bf16 *dh3t;    // [NH][hid][cpad]
+    bf16 *gq;      // [NH][2 parts][qpad][hid]  G of the queries (or of the keys, MSE), hi/lo
+    float *part;   // [splitk][NH][3][hid * d] gradient partials
+    int nslots;
+};
+
+// Row of W1 (which = 0) or W3 (which = 1) hidden unit h inside the packed
+// [2 hid][d] copy: blocks of 16 W1 rows and 16 W3 rows alternate, so one
+// wave's 64-row tile of a product with the packed copy holds matching
+// W1 and W3 rows.
+__device__ __forceinline__ int packed_row(int h, int which) { return 32 * (h >> 4) + 16 * which + (h & 15); }
+
+__device__ __forceinline__ long slot_off13(const LactParams &p, int slot, int h, int part = 0)
+{
+    return (((long)slot * p.NH + h) * 2 + part) * 2 * p.hid * p.d;
+}
+__device__ __forceinline__ long slot_off2(const LactParams &p, int slot, int h, int part = 0)
+{
+    return (((long)slot * p.NH + h) * 2 + part) * (long)p.d * p.hid;
+}
+// w = hi + lo: hi = bf16(w) (nearest), lo = bf16(w - hi) (w - hi is exact in fp32).
+__device__ __forceinline__ void split1(float w, bf16 &hi, bf16 &lo)
+{
+    hi = (bf16)w;
+    lo = (bf16)(w - (float)hi);
+}
+
+// ---------------------------------------------------------------------------
+// prep: K^T and (inner product) (-eta V)^T for all key tokens, through LDS.
+// One block = 64 tokens of one head; zero rows up to tpad.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lact_prep_tokens(LactParams p)
+{
+    __shared__ bf16 tk[64][72];
+    __shared__ bf16 tv[64][72];
+    const int nb = p.tpad / 64;
+    const int h = blockIdx.x / nb, tb = blockIdx.x % nb;
+    const int t0 = tb * 64;
+    const bf16 *k = p.k + (long)h * p.Tkv * p.d;
+    const bf16 *v = p.v + (long)h * p.Tkv * p.d;
+    const float *eta = p.eta + (long)h * p.Tkv;
+    const bool dot = (p.loss == 0);
+    for (int f0 = 0; f0 < p.d; f0 += 64) {
+        for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+            const int r = i >> 3, c = (i & 7) * 8;
+            const int t = t0 + r;
+            const bool ok = t < p.Tkv;
+            const int tc = ok ? t : 0;
+            const B8 kx = ok ? ld16(k + (long)tc * p.d + f0 + c) : zero16();
+            const B8 vx = ok ? ld16(v + (long)tc * p.d + f0 + c) : zero16();
+            const float e = ok ? -eta[tc] : 0.f;
+            const bf16x8 kb = as_bf8(kx), vb = as_bf8(vx);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                tk[c + j][r] = kb[j];
+                tv[c + j][r] = (bf16)((float)vb[j] * e);
+            }
+        }
+        lds_barrier();
+        for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+            const int f = i >> 3, c = (i & 7) * 8;
+            st16(p.kt + ((long)h * p.d + f0 + f) * p.tpad + t0 + c, ld16(&tk[f][c]));
+            if (dot) st16(p.dyt + ((long)h * p.d + f0 + f) * p.tpad + t0 + c, ld16(&tv[f][c]));
+        }
+        lds_barrier();
+    }
+}
+
+// fp32 masters from the inits (skipped where they alias) and the bf16 copies
+// of slot 0.  Grid-stride over NH * 3 * hid * d elements.
+__global__ __launch_bounds__(256) void lact_prep_weights(LactParams p)
+{
+    const long n13 = (long)p.hid * p.d;
+    const long total = (long)p.NH * 3 * n13;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+        const int h = (int)(i / (3 * n13));
+        const long r = i % (3 * n13);
+        const int which = (int)(r / n13);
+        const long e = r % n13;
+        if (which < 2) {
+            const float *src = which == 0 ? p.w1i : p.w3i;
+            float *dst = which == 0 ? p.w1 : p.w3;
+            const float x = src[(long)h * n13 + e];
+            if (dst != src) dst[(long)h * n13 + e] = x;
+            const int row = (int)(e / p.d), col = (int)(e % p.d);
+            const long o = (long)packed_row(row, which) * p.d + col;
+            bf16 hi, lo;
+            split1(x, hi, lo);
+            p.w13b[slot_off13(p, 0, h, 0) + o] = hi;
+            p.w13b[slot_off13(p, 0, h, 1) + o] = lo;
+        } else {
+            const float x = p.w2i[(long)h * n13 + e];
+            if (p.w2 != p.w2i) p.w2[(long)h * n13 + e] = x;
+            bf16 hi, lo;
+            split1(x, hi, lo);
+            p.w2b[slot_off2(p, 0, h, 0) + e] = hi;
+            p.w2b[slot_off2(p, 0, h, 1) + e] = lo;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fwdgrad: per (head, 128-token tile, 64-wide hidden slice) of chunk c.
+// ---------------------------------------------------------------------------
+struct FwdGradLds {
+    bf16 ak[2][128][GPITCH];   // K tile
+    bf16 ay[2][128][GPITCH];   // dY tile
+    bf16 b1[2][64][GPITCH];    // W1 rows of the slice
+    bf16 b3[2][64][GPITCH];    // W3 rows of the slice
+    bf16 b2[2][64][GPITCH];    // W2 columns of the slice (transposed on the way in)
+};
+
+__global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slot)
+{
+    __shared__ FwdGradLds L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, mm = lane & 15;
+    const int nslice = p.hid / 64;
+    const int ntile = p.cpad / 128;
+    int bid = blockIdx.x;
+    const int sl = bid % nslice;
+    bid /= nslice;
+    const int tt = bid % ntile;
+    const int h = bid / ntile;
+    const int cstart = c * p.chunk;
+    const int clen = min(p.chunk, p.Tkv - cstart);
+    const int r0 = tt * 128;
+    const int h0 = sl * 64;
+    const int d = p.d;
+    const bf16 *kh = p.k + ((long)h * p.Tkv + cstart) * d;
+    const bf16 *vh = p.v + ((long)h * p.Tkv + cstart) * d;
+    const float *eh = p.eta + (long)h * p.Tkv + cstart;
+    const bf16 *dyh = p.dy + (long)h * p.cpad * d;
+    const bf16 *w13 = p.w13b + slot_off13(p, slot, h);
+    const bf16 *w2 = p.w2b + slot_off2(p, slot, h);
+    const bool dot = (p.loss == 0);
+
+    int arow[2], acol[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int pc = tid + 256 * i;
+        arow[i] = pc >> 2;
+        acol[i] = (pc & 3) * 8;
+    }
+    const int brow = tid >> 2, bcol = (tid & 3) * 8;  // W1/W3 slice rows
+    const int orow = tid >> 3, hcol = (tid & 7) * 8;  // W2: o row 0..31, 8 hidden columns
+    float erow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = r0 + arow[i];
+        erow[i] = (t < clen) ? (dot ? -eh[t] : 1.f) : 0.f;
+    }
+    const int nst = d / GBK;
+    const int ngroups = (nst + GPD - 1) / GPD;
+    B8 rk[GPD][2], ry[GPD][2], r1[GPD], r3[GPD], r2[GPD];
+    auto issue = [&](int s, int st) {
+        const int kk = min(st, nst - 1) * GBK;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = min(r0 + arow[i], clen - 1);
+            rk[s][i] = ld16(kh + (long)t * d + kk + acol[i]);
+            ry[s][i] = ld16((dot ? vh : dyh) + (long)t * d + kk + acol[i]);
+        }
+        r1[s] = ld16(w13 + (long)packed_row(h0 + brow, 0) * d + kk + bcol);
+        r3[s] = ld16(w13 + (long)packed_row(h0 + brow, 1) * d + kk + bcol);
+        r2[s] = ld16(w2 + (long)(kk + orow) * p.hid + h0 + hcol);
+    };
+    auto commit = [&](int s, int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bool ok = r0 + arow[i] < clen;
+            st16(&L.ak[buf][arow[i]][acol[i]], ok ? rk[s][i] : zero16());
+            const bf16x8 vb = as_bf8(ry[s][i]);
+            bf16x8 o;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = dot ? (bf16)((float)vb[j] * erow[i]) : (ok ? vb[j] : (bf16)0.f);
+            st16(&L.ay[buf][arow[i]][acol[i]], B8{__builtin_bit_cast(u32x4v, o)});
+        }
+        st16(&L.b1[buf][brow][bcol], r1[s]);
+        st16(&L.b3[buf][brow][bcol], r3[s]);
+        const bf16x8 w = as_bf8(r2[s]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) L.b2[buf][hcol + j][orow] = w[j];
+    };
+    // wave w: tokens 32 w .. 32 w + 31 (2 m-tiles), hidden 0..63 of the slice (4 n-tiles)
+    f32x4 a1[2][4], a3[2][4], a2[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a1[i][q] = a3[i][q] = a2[i][q] = zero4();
+
+#pragma unroll
+    for (int s = 0; s < GPD; ++s) issue(s, s);
+    commit(0, 0);
+    lds_barrier();
+    for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+        for (int j = 0; j < GPD; ++j) {
+            const int st = gi * GPD + j;
+            issue(j, st + GPD);
+            commit((j + 1) % GPD, (j + 1) & 1);
+            const int buf = j & 1;
+            bf16x8 fk[2], fy[2], f1[4], f3[4], f2[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fk[i] = as_bf8(ld16(&L.ak[buf][wave * 32 + 16 * i + mm][8 * g]));
+                fy[i] = as_bf8(ld16(&L.ay[buf][wave * 32 + 16 * i + mm][8 * g]));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f1[q] = as_bf8(ld16(&L.b1[buf][16 * q + mm][8 * g]));
+                f3[q] = as_bf8(ld16(&L.b3[buf][16 * q + mm][8 * g]));
+                f2[q] = as_bf8(ld16(&L.b2[buf][16 * q + mm][8 * g]));
+            }
+            if (st < nst) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        a1[i][q] = mfma32(a1[i][q], fk[i], f1[q]);
+                        a3[i][q] = mfma32(a3[i][q], fk[i], f3[q]);
+                        a2[i][q] = mfma32(a2[i][q], fy[i], f2[q]);
+                    }
+            }
+            lds_barrier();
+        }
+    }
+    // lane: tokens r0 + 32 wave + 16 i + 4 g + (0..3), hidden h0 + 16 q + mm.
+    // Rows past the chunk have K = dY = 0, so every output there is 0.
+    bf16 *gt = p.gt + (long)h * p.hid * p.cpad;
+    bf16 *d1 = p.dh1t + (long)h * p.hid * p.cpad;
+    bf16 *d3 = p.dh3t + (long)h * p.hid * p.cpad;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 gv, v1, v3;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float z1 = a1[i][q][j], z3 = a3[i][q][j], dg = a2[i][q][j];
+                const float sg = sigmoidf_(z1);
+                const float act = z1 * sg;
+                gv[j] = act * z3;
+                v3[j] = dg * act;
+                v1[j] = dg * z3 * (sg * (1.f + z1 * (1.f - sg)));
+            }
+            const long off = (long)(h0 + 16 * q + mm) * p.cpad + r0 + wave * 32 + 16 * i + 4 * g;
+            store4<bf16>(gt + off, to_bf16x4(gv));
+            store4<bf16>(d1 + off, to_bf16x4(v1));
+            store4<bf16>(d3 + off, to_bf16x4(v3));
+        }
+}
+
+// ---------------------------------------------------------------------------
+// wgrad: the three weight gradients of chunk c, split over its tokens.
+//   which 0: dW1[h][i] = sum_t dH1^T[h][t] K^T[i][t]   as GEMM (M = i, N = h)
+//   which 1: dW3 likewise with dH3^T
+//   which 2: dW2[o][h] = sum_t dY^T[o][t] G^T[h][t]     as GEMM (M = h, N = o)
+// A lane's four consecutive M indices are the contiguous dimension of the
+// stored gradient.  Token ranges are whole 32-token steps: past the chunk end
+// dH^T, G^T are zero (and dY^T too), so no guard is needed on k.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
+{
+    __shared__ GemmLds L;
+    const int d = p.d, hid = p.hid;
+    const int t13 = (d / 128) * (hid / 128);
+    int bid = blockIdx.x;
+    const int tile = bid % (3 * t13);
+    bid /= 3 * t13;
+    const int sk = bid % p.splitk;
+    const int h = bid / p.splitk;
+    const int which = tile / t13, ti = tile % t13;
+    const int cstart = c * p.chunk;
+    const int clen32 = (min(p.chunk, p.Tkv - cstart) + 31) / 32 * 32;
+    const int kper = ((clen32 + p.splitk - 1) / p.splitk + 31) / 32 * 32;
+    const int k0 = min(clen32, sk * kper);
+    const int k1 = min(clen32, k0 + kper);
+    float *part = p.part + (((long)sk * p.NH + h) * 3 + which) * (long)hid * d;
+    const int Mdim = (which < 2) ? d : hid, Ndim = (which < 2) ? hid : d;
+    const int tm = ti / (Ndim / 128), tn = ti % (Ndim / 128);
+    if (k1 <= k0) {
+        for (int e = threadIdx.x; e < 128 * 128; e += 256)
+            part[(long)(tn * 128 + (e >> 7)) * Mdim + tm * 128 + (e & 127)] = 0.f;
+        return;
+    }
+    const bf16 *A, *B;
+    long lda, ldb;
+    if (which < 2) {
+        A = p.kt + (long)h * d * p.tpad + cstart + k0;
+        lda = p.tpad;
+        B = (which == 0 ? p.dh1t : p.dh3t) + (long)h * hid * p.cpad + k0;
+        ldb = p.cpad;
+    } else {
+        A = p.gt + (long)h * hid * p.cpad + k0;
+        lda = p.cpad;
+        B = p.dyt + (long)h * d * p.tpad + (p.loss == 0 ? cstart : 0) + k0;
+        ldb = p.tpad;
+    }
+    const bf16 *as[1] = {A}, *bs[1] = {B};
+    gemm_nt_tile(L, as, lda, bs, ldb, Mdim, Ndim, k1 - k0, 1, tm * 128, tn * 128,
+                 [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+                     for (int i = 0; i < 4; ++i)
+#pragma unroll
+                         for (int q = 0; q < 4; ++q)
+                             *reinterpret_cast<f32x4 *>(part + (long)(nb + 16 * q + mm) * Mdim + mb + 16 * i + 4 * g) = acc[i][q];
+                 });
+}
+
+// ---------------------------------------------------------------------------
+// update: one wave per row of W1, W3 (length d) or W2 (length hid):
+// W <- W - sum of the split partials, then the row back to its old L2 norm;
+// writes the fp32 master and the bf16 copy of slot `dst_slot`.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot)
+{
+    const int lane = threadIdx.x & 63;
+    const int rows_per_head = 2 * p.hid + p.d;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= p.NH * rows_per_head) return;
+    const int h = gw / rows_per_head, r = gw % rows_per_head;
+    int which, row, len;
+    if (r < p.hid) { which = 0; row = r; len = p.d; }
+    else if (r < 2 * p.hid) { which = 1; row = r - p.hid; len = p.d; }
+    else { which = 2; row = r - 2 * p.hid; len = p.hid; }
+    const long n13 = (long)p.hid * p.d;
+    float *w = (which == 0 ? p.w1 : which == 1 ? p.w3 : p.w2) + (long)h * n13 + (long)row * len;
+    constexpr int MAXE = 16;  // len <= 1024 = 16 x 64
+    float nv[MAXE];
+    float so = 0.f, sn = 0.f;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        const int col = lane + 64 * e;
+        nv[e] = 0.f;
+        if (col < len) {
+            const float old = w[col];
+            float gsum = 0.f;
+            for (int s = 0; s < p.splitk; ++s)
+                gsum += p.part[(((long)s * p.NH + h) * 3 + which) * n13 + (long)row * len + col];
+            const float x = old - gsum;
+            so += old * old;
+            sn += x * x;
+            nv[e] = x;
+        }
+    }
+    float scale = 1.f;
+    if (p.rownorm) {
+        so = wave_sum(so);
+        sn = wave_sum(sn);
+        scale = (sn > 0.f) ? sqrtf(so) / sqrtf(sn) : 1.f;
+    }
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        const int col = lane + 64 * e;
+        if (col < len) {
+            const float x = nv[e] * scale;
+            w[col] = x;
+            bf16 hi, lo;
+            split1(x, hi, lo);
+            if (which < 2) {
+                const long o = (long)packed_row(row, which) * p.d + col;
+                p.w13b[slot_off13(p, dst_slot, h, 0) + o] = hi;
+                p.w13b[slot_off13(p, dst_slot, h, 1) + o] = lo;
+            } else {
+                const long o = (long)row * p.hid + col;
+                p.w2b[slot_off2(p, dst_slot, h, 0) + o] = hi;
+                p.w2b[slot_off2(p, dst_slot, h, 1) + o] = lo;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// apply1: G[t][hh] = silu(x_t . W1[hh]) * (x_t . W3[hh]) for the rows of X
+// (queries, or the chunk's keys for the MSE loss), computed as the GEMM
+// packed(W1, W3) X^T so each lane holds 4 consecutive hidden units of one token.
+// Token tiles never straddle chunks (chunk % 128 == 0 or one chunk).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, long x_head_stride,
+                                                   int T, int slot_fixed)
+{
+    __shared__ GemmLds L;
+    const int mt = (2 * p.hid) / 128, nt = (T + 127) / 128;
+    int bid = blockIdx.x;
+    const int tm = bid % mt;
+    bid /= mt;
+    const int tn = bid % nt;
+    const int h = bid / nt;
+    const int slot = (slot_fixed >= 0) ? slot_fixed : (tn * 128) / p.chunk;
+    // X (W_hi + W_lo)^T: two K segments over the same X rows
+    const bf16 *as[2] = {p.w13b + slot_off13(p, slot, h, 0), p.w13b + slot_off13(p, slot, h, 1)};
+    const bf16 *B = X + (long)h * x_head_stride;
+    const bf16 *bs[2] = {B, B};
+    bf16 *G = p.gq + (long)h * 2 * p.qpad * p.hid;
+    bf16 *Glo = G + (long)p.qpad * p.hid;
+    gemm_nt_tile(L, as, p.d, bs, p.d, 2 * p.hid, T, p.d, 2, tm * 128, tn * 128,
+                 [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+                     for (int i = 0; i < 4; i += 2)
+#pragma unroll
+                         for (int q = 0; q < 4; ++q) {
+                             const int t = nb + 16 * q + mm;
+                             const int hh = (mb + 16 * i) / 2 + 4 * g;
+                             f32x4 gv;
+#pragma unroll
+                             for (int j = 0; j < 4; ++j) {
+                                 const float z1 = acc[i][q][j], z3 = acc[i + 1][q][j];
+                                 gv[j] = z1 * sigmoidf_(z1) * z3;
+                             }
+                             if (t < T) {
+                                 const bf16x4 hi = to_bf16x4(gv);
+                                 store4<bf16>(G + (long)t * p.hid + hh, hi);
+                                 store4<bf16>(Glo + (long)t * p.hid + hh, to_bf16x4(gv - to_f32x4(hi)));
+                             }
+                         }
+                 });
+}
+
+// apply2: Y[t][o] = G[t] . W2[o], as the GEMM W2 G^T (4 consecutive outputs of
+// one token per lane).  mode 0: out = Y (bf16).  mode 1 (MSE): dY = eta (Y - V)
+// token-major into p.dy and transposed into p.dyt (chunk-local tokens).
+__global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot_fixed, int mode,
+                                                   int c)
+{
+    __shared__ GemmLds L;
+    const int mt = p.d / 128, nt = (T + 127) / 128;
+    int bid = blockIdx.x;
+    const int tm = bid % mt;
+    bid /= mt;
+    const int tn = bid % nt;
+    const int h = bid / nt;
+    const int slot = (slot_fixed >= 0) ? slot_fixed : (tn * 128) / p.chunk;
+    // (W2_hi G_hi + W2_lo G_hi + W2_hi G_lo): three K segments
+    const bf16 *whi = p.w2b + slot_off2(p, slot, h, 0), *wlo = p.w2b + slot_off2(p, slot, h, 1);
+    const bf16 *ghi = p.gq + (long)h * 2 * p.qpad * p.hid, *glo = ghi + (long)p.qpad * p.hid;
+    const bf16 *as[3] = {whi, wlo, whi}, *bs[3] = {ghi, ghi, glo};
+    const int cstart = c * p.chunk;
+    gemm_nt_tile(L, as, p.hid, bs, p.hid, p.d, T, p.hid, 3, tm * 128, tn * 128,
+                 [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+                     for (int i = 0; i < 4; ++i)
+#pragma unroll
+                         for (int q = 0; q < 4; ++q) {
+                             const int t = nb + 16 * q + mm;
+                             const int o = mb + 16 * i + 4 * g;
+                             if (mode == 1 && t >= T) {
+                                 // zero the rest of the chunk's padded columns: the weight
+                                 // gradient reads them (against zero partners)
+#pragma unroll
+                                 for (int j = 0; j < 4; ++j) p.dyt[((long)h * p.d + o + j) * p.tpad + t] = (bf16)0.f;
+                                 continue;
+                             }
+                             if (t >= T) continue;
+                             if (mode == 0) {
+                                 store4<bf16>(p.out + ((long)h * p.Tq + t) * p.d + o, to_bf16x4(acc[i][q]));
+                             } else {
+                                 const long tk = (long)h * p.Tkv + cstart + t;
+                                 const float e = p.eta[tk];
+                                 const f32x4 vv = to_f32x4(load4<bf16>(p.v + tk * p.d + o));
+                                 const f32x4 dyv = (acc[i][q] - vv) * e;
+                                 const bf16x4 db = to_bf16x4(dyv);
+                                 store4<bf16>(p.dy + ((long)h * p.cpad + t) * p.d + o, db);
+#pragma unroll
+                                 for (int j = 0; j < 4; ++j) p.dyt[((long)h * p.d + o + j) * p.tpad + t] = db[j];
+                             }
+                         }
+                 });
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+static int lact_splitk(const LactShape &s, int clen)
+{
+    const int t13 = (s.d / 128) * (s.hid / 128);
+    const int tiles = s.NH * 3 * t13;
+    int sk = (768 + tiles - 1) / tiles;            // aim at ~3 workgroups per CU
+    const int maxsk = (clen + 255) / 256;          // at least 256 tokens per split
+    if (sk > maxsk) sk = maxsk;
+    return sk < 1 ? 1 : sk;
+}
+
+LactPlan lact_plan(const LactShape &s)
+{
+    LactPlan pl{};
+    const int chunk = (s.Tkv > 0 && s.chunk >= s.Tkv) ? s.Tkv : s.chunk;
+    pl.nchunks = (s.Tkv > 0) ? (s.Tkv + chunk - 1) / chunk : 0;
+    const int clen = (s.Tkv > 0) ? (chunk < s.Tkv ? chunk : s.Tkv) : 0;
+    const size_t cpad = (size_t)((clen + 127) / 128 * 128);
+    const size_t tpad = (size_t)((s.Tkv + 127) / 128 * 128);
+    const size_t qpad = (size_t)(((s.Tq > (int)cpad ? s.Tq : (int)cpad) + 127) / 128 * 128);
+    pl.maxc = (int)cpad;
+    const int nslots = (s.order == 0) ? pl.nchunks + 1 : 1;
+    const int splitk = lact_splitk(s, clen);
+    const size_t NH = s.NH, d = s.d, hid = s.hid;
+    size_t off = 0;
+    auto take = [&](int idx, size_t bytes) {
+        pl.off[idx] = off;
+        off = al256(off + bytes);
+    };
+    take(0, NH * d * tpad * 2);                 // kt
+    take(1, NH * d * tpad * 2);                 // dyt
+    take(2, s.loss == 1 ? NH * cpad * d * 2 : 0);  // dy
+    take(3, (size_t)nslots * NH * 2 * 2 * hid * d * 2);  // w13b (hi, lo)
+    take(4, (size_t)nslots * NH * 2 * d * hid * 2);      // w2b (hi, lo)
+    take(5, NH * hid * cpad * 2);               // gt
+    take(6, NH * hid * cpad * 2);               // dh1t
+    take(7, NH * hid * cpad * 2);               // dh3t
+    take(8, NH * 2 * qpad * hid * 2);           // gq (hi, lo)
+    take(9, (size_t)splitk * NH * 3 * hid * d * 4);  // gradient partials
+    pl.off[10] = (size_t)splitk;
+    pl.off[11] = (size_t)nslots;
+    pl.off[12] = cpad;
+    pl.off[13] = tpad;
+    pl.off[14] = qpad;
+    pl.off[15] = (size_t)chunk;
+    pl.bytes = off;
+    return pl;
+}
+
+hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
+                       const void *v, const float *eta, const float *w1, const float *w2,
+                       const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
+                       hipStream_t st)
+{
+    LactParams p;
+    char *base = (char *)ws;
+    p.q = (const bf16 *)q;
+    p.k = (const bf16 *)k;
+    p.v = (const bf16 *)v;
+    p.eta = eta;
+    p.w1i = w1;
+    p.w2i = w2;
+    p.w3i = w3;
+    p.out = (bf16 *)out;
+    p.w1 = w1f;
+    p.w2 = w2f;
+    p.w3 = w3f;
+    p.NH = s.NH;
+    p.Tq = s.Tq;
+    p.Tkv = s.Tkv;
+    p.d = s.d;
+    p.hid = s.hid;
+    p.chunk = (int)pl.off[15];
+    p.nchunks = pl.nchunks;
+    p.cpad = (int)pl.off[12];
+    p.tpad = (int)pl.off[13];
+    p.qpad = (int)pl.off[14];
+    p.loss = s.loss;
+    p.order = s.order;
+    p.rownorm = s.rownorm;
+    p.splitk = (int)pl.off[10];
+    p.nslots = (int)pl.off[11];
+    p.kt = (bf16 *)(base + pl.off[0]);
+    p.dyt = (bf16 *)(base + pl.off[1]);
+    p.dy = (bf16 *)(base + pl.off[2]);
+    p.w13b = (bf16 *)(base + pl.off[3]);
+    p.w2b = (bf16 *)(base + pl.off[4]);
+    p.gt = (bf16 *)(base + pl.off[5]);
+    p.dh1t = (bf16 *)(base + pl.off[6]);
+    p.dh3t = (bf16 *)(base + pl.off[7]);
+    p.gq = (bf16 *)(base + pl.off[8]);
+    p.part = (float *)(base + pl.off[9]);
+
+    const long n3 = (long)s.NH * 3 * s.hid * s.d;
+    const int wblocks = (int)((n3 + 255) / 256 < 4096 ? (n3 + 255) / 256 : 4096);
+    lact_prep_weights<<<dim3(wblocks), dim3(256), 0, st>>>(p);
+    if (s.Tkv > 0) lact_prep_tokens<<<dim3(s.NH * (p.tpad / 64)), dim3(256), 0, st>>>(p);
+    const int t13 = (s.d / 128) * (s.hid / 128);
+    const int urows = s.NH * (2 * s.hid + s.d);
+    for (int c = 0; c < pl.nchunks; ++c) {
+        const int slot = (s.order == 0) ? c : 0;
+        const int dst = (s.order == 0) ? c + 1 : 0;
+        const int clen = (c + 1) * p.chunk <= s.Tkv ? p.chunk : s.Tkv - c * p.chunk;
+        if (s.loss == 1) {
+            // dY = eta (f(K_c) - V_c): G of the chunk's keys, then W2.
+            lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((clen + 127) / 128)), dim3(256), 0, st>>>(
+                p, p.k + (long)c * p.chunk * s.d, (long)s.Tkv * s.d, clen, slot);
+            lact_apply2<<<dim3(s.NH * (s.d / 128) * ((clen + 127) / 128)), dim3(256), 0, st>>>(
+                p, clen, slot, 1, c);
+        }
+        lact_fwdgrad<<<dim3(s.NH * (p.cpad / 128) * (s.hid / 64)), dim3(256), 0, st>>>(p, c, slot);
+        lact_wgrad<<<dim3(s.NH * p.splitk * 3 * t13), dim3(256), 0, st>>>(p, c);
+        lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst);
+    }
+    if (s.Tq > 0) {
+        const int fixed = (s.order == 0) ? -1 : 0;
+        lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(
+            p, p.q, (long)s.Tq * s.d, s.Tq, fixed);
+        lact_apply2<<<dim3(s.NH * (s.d / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(
+            p, s.Tq, fixed, 0, 0);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tttk

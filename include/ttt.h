@@ -127,8 +127,9 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
  * There is no intra-chunk term (causality inside a chunk belongs to the
  * window attention beside the layer, [LaCT] section 4).
  * Finals may alias the matching inits exactly.
- * Supported: dtype TTT_BF16; d and hidden multiples of 64 with d <= 512 and
- * hidden <= 1024; chunk a positive multiple of 64 or >= Tkv; any loss/order.
+ * Supported: dtype TTT_BF16; d and hidden multiples of 128, each <= 1024;
+ * chunk a positive multiple of 128, or >= Tkv (one chunk of any length);
+ * any loss and order.  Other shapes return TTT_EUNSUPPORTED.
  * ------------------------------------------------------------------------ */
 size_t lact_swiglu_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden, int chunk,
                                    int loss, int order, int dtype);

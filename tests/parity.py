@@ -6,6 +6,12 @@ Tolerances (written out here, used by every test):
   bf16 path : max|gpu - oracle| <= 2e-2 * RMS(oracle)
 The same rule is applied to the state change W_final - W_init (against the
 oracle's change), so that a mis-scaled update cannot hide inside the state.
+For LaCT that change check uses 5e-2 x RMS(change) (DELTA_TOL_LACT): the
+change is a sum of products of bf16 operands (dY, G, dH, the bf16 weights) and
+its max/RMS ratio is about 5, so one bf16 rounding (relative error up to 2^-8)
+per operand already reaches ~2-3% of its RMS at the largest element; a
+mis-scaled update, which this check is there to catch, is off by tens of
+percent.  W_final itself is held to the 2e-2 x RMS rule.
 """
 from __future__ import annotations
 
@@ -14,6 +20,7 @@ import torch
 
 FP32_RTOL = 1e-4
 BF16_RMS_TOL = 2e-2
+DELTA_TOL_LACT = 5e-2
 
 
 def dev(x: np.ndarray, bits: np.ndarray | None = None, dtype=torch.float32) -> torch.Tensor:
@@ -51,7 +58,7 @@ def err_stats(got: np.ndarray, ref: np.ndarray) -> dict:
             "finite": bool(np.all(np.isfinite(got)))}
 
 
-def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, rms_tol=None):
     s = err_stats(got, ref)
     assert s["finite"], f"{what}: non-finite values"
     if ref.size == 0:
@@ -59,6 +66,7 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     if dtype == "f32":
         assert s["rel_norm"] <= FP32_RTOL, f"{what}: max rel err {s['rel_norm']:.3e} > {FP32_RTOL} ({s})"
     else:
-        assert s["rel_rms"] <= BF16_RMS_TOL, \
-            f"{what}: max abs err {s['max_abs']:.3e} > {BF16_RMS_TOL} x RMS {s['rms_ref']:.3e} ({s})"
+        tol = BF16_RMS_TOL if rms_tol is None else rms_tol
+        assert s["rel_rms"] <= tol, \
+            f"{what}: max abs err {s['max_abs']:.3e} > {tol} x RMS {s['rms_ref']:.3e} ({s})"
     return s

@@ -71,7 +71,7 @@ def test_linear_workspace_query():
 
 def lact(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, out=FAKE,
-             f1=FAKE, f2=FAKE, f3=FAKE, B=1, H=1, Tq=256, Tkv=256, d=64, hid=128, chunk=64, loss=0,
+             f1=FAKE, f2=FAKE, f3=FAKE, B=1, H=1, Tq=512, Tkv=512, d=128, hid=256, chunk=128, loss=0,
              order=0, rownorm=1, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.lact_swiglu_fwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w1"], a["w2"],
@@ -84,8 +84,9 @@ def lact(lib, **kw):
     (dict(w2=None), _lib.TTT_EINVAL), (dict(f3=FAKE + 2), _lib.TTT_EINVAL),
     (dict(rownorm=2), _lib.TTT_EINVAL), (dict(hid=0), _lib.TTT_EINVAL),
     (dict(Tq=100), _lib.TTT_EINVAL), (dict(dtype=0), _lib.TTT_EUNSUPPORTED),
-    (dict(d=48), _lib.TTT_EUNSUPPORTED), (dict(hid=2048), _lib.TTT_EUNSUPPORTED),
-    (dict(chunk=50), _lib.TTT_EUNSUPPORTED), (dict(wsb=0), _lib.TTT_EWORKSPACE),
+    (dict(order=1, Tq=100, chunk=200), _lib.TTT_EUNSUPPORTED),
+    (dict(d=64), _lib.TTT_EUNSUPPORTED), (dict(hid=2048), _lib.TTT_EUNSUPPORTED),
+    (dict(chunk=64), _lib.TTT_EUNSUPPORTED), (dict(wsb=0), _lib.TTT_EWORKSPACE),
 ])
 def test_lact_validation(kw, code):
     assert lact(_lib.load(), **kw) == code

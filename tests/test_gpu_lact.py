@@ -1,0 +1,128 @@
+"""GPU parity of lact_swiglu_fwd against the fp64 oracle (same seeded inputs).
+
+Small shapes go through the token-by-token C oracle; the two full-size
+workloads go through the oracle's chunk-matmul form on sampled heads (all of
+their outputs and final weights).  Row norms of the final weights are checked
+against the initial ones at full size (an invariant of the update rule).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import dense
+import ttt_inputs as ti
+from tests.parity import DELTA_TOL_LACT, assert_close, inputs_to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _cla():
+    import chunked_linear_attention_amd as cla
+    return cla
+
+
+def run_gpu(inp, chunk, loss, order, rownorm):
+    cla = _cla()
+    g = inputs_to_device(inp, "bf16")
+    out, f1, f2, f3 = cla.lact_swiglu_fwd(g["q"], g["k"], g["v"], g["eta"], g["w1"], g["w2"], g["w3"],
+                                          chunk=chunk, loss=loss, order=order, rownorm=rownorm)
+    torch.cuda.synchronize()
+    return to_np(out), to_np(f1), to_np(f2), to_np(f3)
+
+
+def check(gpu, ref, inp, what=""):
+    out, f1, f2, f3 = gpu
+    ro, r1, r2, r3 = ref
+    assert_close(out, ro, "bf16", what + "out")
+    for name, a, b, w0 in (("w1", f1, r1, inp["w1"]), ("w2", f2, r2, inp["w2"]), ("w3", f3, r3, inp["w3"])):
+        assert_close(a, b, "bf16", what + name)
+        assert_close(a - w0, b - w0, "bf16", what + name + " - init", rms_tol=DELTA_TOL_LACT)
+
+
+def case(B, H, Tq, Tkv, d, hid, chunk, loss, order, rownorm=1, seed=0, eta_scale=1.0):
+    print(f"[case] B={B} H={H} Tq={Tq} Tkv={Tkv} d={d} hid={hid} b={chunk} loss={loss} "
+          f"order={order} rownorm={rownorm}", flush=True)
+    inp = ti.gen_lact(B, H, Tq, Tkv, d, hid, seed=seed, eta_scale=eta_scale)
+    gpu = run_gpu(inp, chunk, loss, order, rownorm)
+    ref = oracle.lact_swiglu(inp["q"], inp["k"], inp["v"], inp["eta"], inp["w1"], inp["w2"],
+                             inp["w3"], chunk=chunk, loss=loss, order=order, rownorm=rownorm)
+    check(gpu, ref, inp)
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+def test_causal_multi_chunk(loss):
+    # eta scaled up so the updates move the weights well past bf16 noise
+    case(1, 2, 512, 512, 128, 256, 128, loss, 0, seed=41, eta_scale=20.0)
+
+
+def test_causal_ragged_last_chunk():
+    case(1, 1, 600, 600, 128, 256, 128, 0, 0, seed=42, eta_scale=20.0)
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+def test_noncausal_single_chunk(loss):
+    case(1, 2, 77, 300, 128, 256, 4096, loss, 1, seed=43, eta_scale=20.0)
+
+
+def test_noncausal_multi_chunk_no_rownorm():
+    case(2, 1, 130, 384, 128, 384, 128, 0, 1, rownorm=0, seed=44, eta_scale=20.0)
+
+
+def test_wider_head():
+    case(1, 1, 256, 256, 256, 512, 128, 0, 0, seed=45, eta_scale=20.0)
+
+
+def test_in_place_state():
+    cla = _cla()
+    inp = ti.gen_lact(1, 2, 384, 384, 128, 256, seed=46, eta_scale=20.0)
+    g = inputs_to_device(inp, "bf16")
+    ref = cla.lact_swiglu_fwd(g["q"], g["k"], g["v"], g["eta"], g["w1"], g["w2"], g["w3"], chunk=128)
+    w1, w2, w3 = g["w1"].clone(), g["w2"].clone(), g["w3"].clone()
+    got = cla.lact_swiglu_fwd(g["q"], g["k"], g["v"], g["eta"], w1, w2, w3, chunk=128,
+                              w1_final=w1, w2_final=w2, w3_final=w3)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], ref[0])
+    for a, b in zip((w1, w2, w3), ref[1:]):
+        assert torch.equal(a, b)
+
+
+def test_repeat_runs_bitwise_identical():
+    cla = _cla()
+    inp = ti.gen_lact(1, 2, 512, 512, 128, 256, seed=47)
+    g = inputs_to_device(inp, "bf16")
+    a = cla.lact_swiglu_fwd(g["q"], g["k"], g["v"], g["eta"], g["w1"], g["w2"], g["w3"], chunk=128)
+    b = cla.lact_swiglu_fwd(g["q"], g["k"], g["v"], g["eta"], g["w1"], g["w2"], g["w3"], chunk=128)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def _full(wl, heads):
+    inp = ti.gen_lact_workload(wl)
+    gpu = run_gpu(inp, wl.chunk, wl.loss, wl.order, wl.rownorm)
+    out, f1, f2, f3 = gpu
+    # invariant at any size: row norms of the final weights equal the initial ones
+    for a, w0 in ((f1, inp["w1"]), (f2, inp["w2"]), (f3, inp["w3"])):
+        na, n0 = np.linalg.norm(a, axis=-1), np.linalg.norm(w0.astype(np.float64), axis=-1)
+        assert np.max(np.abs(na - n0) / n0) < 1e-4
+    B, H = wl.B, wl.H
+    for hh in heads:
+        b, h = divmod(hh, H)
+        print(f"[oracle] {wl.name} head {hh}", flush=True)
+        ro, r1, r2, r3 = dense.lact_head(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
+                                         inp["eta"][b, h], inp["w1"][b, h], inp["w2"][b, h],
+                                         inp["w3"][b, h], chunk=wl.chunk, loss=wl.loss,
+                                         order=wl.order, rownorm=wl.rownorm)
+        sub = {k: inp[k][b, h] for k in ("w1", "w2", "w3")}
+        check((out[b, h], f1[b, h], f2[b, h], f3[b, h]), (ro, r1, r2, r3), sub, f"head {hh} ")
+
+
+def test_workload_lact_causal_full_size():
+    """LaCT causal, d=256, hidden 512, b=2048, 4 heads, T=32768 (heads 0 and 3)."""
+    _full(ti.LACT_CAUSAL, [0, 3])
+
+
+def test_workload_lact_noncausal_full_size():
+    """LaCT non-causal, d=384, hidden 768, 65536 update tokens, 16384 queries (head 1)."""
+    _full(ti.LACT_NONCAUSAL, [1])
