@@ -63,7 +63,7 @@ def kernel_source_hash(names):
 def read_traffic(kind: str, workload: str, src_hash: str):
     """HBM bytes per call from a committed rocprofv3 --pmc summary, if it was taken on
     the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -189,7 +189,10 @@ def bench_lact(wl, steps, warmup):
                             chunk=wl.chunk, loss=wl.loss, order=wl.order, rownorm=bool(wl.rownorm),
                             out=outs[0], w1_final=outs[1], w2_final=outs[2], w3_final=outs[3],
                             workspace=ws)
-    ms, wall = time_calls(call, [None], steps, warmup)
+    class _One:
+        def __getitem__(self, i):
+            return None
+    ms, wall = time_calls(call, _One(), steps, warmup)
     NH = wl.B * wl.H
     Tq = s["q"].shape[2]
     flops, byts = lact_alg(NH, Tq, wl.Tkv, wl.d, wl.hid, wl.order)
@@ -212,17 +215,14 @@ def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0):
     eta = inp["eta"].reshape(NH, T)
     w0 = inp["w0"].reshape(NH, d, d)
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.ttt_linear(q[:1][None], k[:1][None], v[:1][None], eta[:1][None], w0[:1][None],
-                      chunk=chunk, loss=loss)
-    first = time.perf_counter() - t0
-    # enough whole heads (run in parallel over the host threads) to fill the budget
-    n = int(max(1, min(NH, (budget_s - first) * threads / max(first, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.ttt_linear(q[:n][None], k[:n][None], v[:n][None], eta[:n][None], w0[:n][None],
-                      chunk=chunk, loss=loss)
-    elapsed = first + (time.perf_counter() - t0)
-    heads_done = 1 + n
+    # whole heads, all host threads (OpenMP over heads), repeated until about
+    # budget_s of wall time has been spent
+    heads_done, elapsed = 0, 0.0
+    while elapsed < budget_s:
+        t0 = time.perf_counter()
+        oracle.ttt_linear(q[None], k[None], v[None], eta[None], w0[None], chunk=chunk, loss=loss)
+        elapsed += time.perf_counter() - t0
+        heads_done += NH
     return {"value": heads_done * T / elapsed, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{heads_done} heads x {T} tokens of the same workload (fp64 token-by-token "
@@ -237,6 +237,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -244,6 +246,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_call": n, "calls": 5}))
+        return
     import chunked_linear_attention_amd as cla
     import ttt_inputs as ti
     cla.load_library()
