@@ -49,17 +49,49 @@ struct LinParams {
     int NH, Tq, Tkv, chunk, seg_tokens, S, Ssum, seg_q, Sq;
 };
 
-// LDS image of one 16-token sub-block.  Feature-major rows are padded to 20
-// elements so the transposing writes of one wave spread over the banks.
+// LDS image of one 16-token sub-block, token-major.  The fragments that need
+// four consecutive tokens of one feature (K^T for the update, V in the
+// accumulator layout) come from the same token-major tiles through gfx950's
+// transposing LDS read for 16-bit data; the fp32 path keeps feature-major
+// copies instead (kt, vt; rows padded to 20 elements).
 template <typename E, int D> struct alignas(16) SubTile {
+    static constexpr bool TR = sizeof(E) == 2;
     static constexpr int RP = D + (sizeof(E) == 2 ? 8 : 4);  // token-major row pitch
     static constexpr int FP = 20;                            // feature-major row pitch
-    E qs[16][RP];   // Q, token-major
-    E ks[16][RP];   // K, token-major
-    E kt[D][FP];    // K, feature-major (tokens 0..15 used)
-    E vt[D][FP];    // V, feature-major
+    E qs[16][RP];
+    E ks[16][RP];
+    E vs[TR ? 16 : 1][RP];
+    E kt[TR ? 1 : D][FP];
+    E vt[TR ? 1 : D][FP];
     float eta[16];
 };
+
+// Transposing read (16-bit elements): within each group of 16 lanes, lane i
+// slot j receives the element that lane 4j + i/4 would read at slot i%4.
+// Lane (m, g) pointing at row 4g + m/4, column c0 + 4(m%4) of a token-major
+// tile therefore receives tile[4g + j][c0 + m], j = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p)
+{
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) v4bf *)((__attribute__((address_space(3))) char *)p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Fragment with k = token (4 consecutive tokens per lane) of column block
+// `blk` of K or V: lane (m, g) gets X[4g + j][16 blk + m].
+template <typename E, int D>
+__device__ __forceinline__ typename Frag<E>::type tok_frag(const SubTile<E, D> &tl, bool from_v, int blk,
+                                                           int m, int g)
+{
+    if constexpr (SubTile<E, D>::TR) {
+        const E(*src)[SubTile<E, D>::RP] = from_v ? tl.vs : tl.ks;
+        return lds_read_tr(&src[4 * g + (m >> 2)][16 * blk + 4 * (m & 3)]);
+    } else {
+        const E(*src)[SubTile<E, D>::FP] = from_v ? tl.vt : tl.kt;
+        return load4<E>(&src[16 * blk + m][4 * g]);
+    }
+}
 
 // Which tensors a kernel stages.
 enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
@@ -67,9 +99,10 @@ enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
 // Cooperative global -> register -> LDS loader with a ring of PD register
 // slots.  Every thread runs the same instruction stream: for each staged
 // tensor it moves CPT pieces of 4 consecutive features of one token (8 bytes
-// bf16, 16 bytes fp32) and one eta value, at clamped addresses (rows past the
-// segment end re-read the last valid row), so there is no branch around a
-// load; rows past the end are zeroed when written to LDS.
+// bf16, 16 bytes fp32) and one eta value, with buffer loads: the per-thread
+// byte offset is fixed, the sub-block's position is the scalar offset, and
+// the buffer's extent ends at the segment's last token, so rows past it read
+// as zero in hardware (no clamps, selects or 64-bit address arithmetic).
 template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
     typedef typename Vec4<E>::type V4;
     static constexpr bool LQ = STAGE & STAGE_Q, LK = STAGE & STAGE_K, LV = STAGE & STAGE_V,
@@ -77,60 +110,73 @@ template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
     static constexpr int CPT = (4 * D) / NT;  // pieces per tensor per thread (16 rows x D/4 pieces)
     static_assert(CPT >= 1 && CPT * NT == 4 * D, "loader shape");
     int row[CPT], col[CPT];
-    const E *q, *k, *v;
-    V4 rq[PD][CPT], rk[PD][CPT], rv[PD][CPT];
-    float re[PD];
+    int voff[CPT];
+    __amdgpu_buffer_rsrc_t rq, rk, rv, re;
+    V4 vq[PD][CPT], vk[PD][CPT], vv[PD][CPT];
+    float ve[PD];
 
-    __device__ void init(int tid, const LinParams &p, int h, int T)
+    __device__ void init(int tid, const LinParams &p, int h, int T, int tend)
     {
         const size_t hoff = (size_t)h * T * D;
-        q = (const E *)p.q + hoff;
-        k = (const E *)p.k + hoff;
-        v = (const E *)p.v + hoff;
+        const int bytes = tend * D * (int)sizeof(E);
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)p.q + hoff), (short)0, LQ ? bytes : 0, 0x00020000);
+        rk = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)p.k + hoff), (short)0, LK ? bytes : 0, 0x00020000);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)p.v + hoff), (short)0, LV ? bytes : 0, 0x00020000);
+        re = __builtin_amdgcn_make_buffer_rsrc((void *)(LE ? p.eta + (size_t)h * T : p.eta), (short)0,
+                                               LE ? tend * 4 : 0, 0x00020000);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int piece = tid + i * NT;
             row[i] = piece / (D / 4);
             col[i] = piece % (D / 4);
+            voff[i] = (row[i] * D + 4 * col[i]) * (int)sizeof(E);
         }
     }
 
-    __device__ __forceinline__ void issue(int s, int tb0, int tend, const float *eta_h)
+    __device__ __forceinline__ V4 bload(__amdgpu_buffer_rsrc_t r, int vo, int so)
     {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const size_t off = (size_t)min(tb0 + row[i], tend - 1) * D + 4 * col[i];
-            if (LQ) rq[s][i] = load4<E>(q + off);
-            if (LK) rk[s][i] = load4<E>(k + off);
-            if (LV) rv[s][i] = load4<E>(v + off);
-        }
-        if (LE) re[s] = eta_h[min(tb0 + (int)(threadIdx.x & 15), tend - 1)];
+        if constexpr (sizeof(E) == 2)
+            return __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
+        else
+            return __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
     }
 
-    // Write slot s (the sub-block starting at token tb0) to LDS.
-    __device__ __forceinline__ void commit(int s, SubTile<E, D> &tl, int tb0, int tend)
+    __device__ __forceinline__ void issue(int s, int tb0)
+    {
+        const int so = tb0 * D * (int)sizeof(E);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            if (LQ) vq[s][i] = bload(rq, voff[i], so);
+            if (LK) vk[s][i] = bload(rk, voff[i], so);
+            if (LV) vv[s][i] = bload(rv, voff[i], so);
+        }
+        if (LE) ve[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, (int)(threadIdx.x & 15) * 4, tb0 * 4, 0));
+    }
+
+    // Write slot s to LDS.
+    __device__ __forceinline__ void commit(int s, SubTile<E, D> &tl)
     {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const bool ok = tb0 + row[i] < tend;
             const int r = row[i], c = 4 * col[i];
-            if (LQ) store4<E>(&tl.qs[r][c], ok ? rq[s][i] : zero_vec4<E>());
+            if (LQ) store4<E>(&tl.qs[r][c], vq[s][i]);
             if (LK) {
-                const V4 x = ok ? rk[s][i] : zero_vec4<E>();
-                store4<E>(&tl.ks[r][c], x);
+                store4<E>(&tl.ks[r][c], vk[s][i]);
+                if constexpr (!SubTile<E, D>::TR) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) tl.kt[c + j][r] = x[j];
+                    for (int j = 0; j < 4; ++j) tl.kt[c + j][r] = vk[s][i][j];
+                }
             }
             if (LV) {
-                const V4 x = ok ? rv[s][i] : zero_vec4<E>();
+                if constexpr (SubTile<E, D>::TR) {
+                    store4<E>(&tl.vs[r][c], vv[s][i]);
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) tl.vt[c + j][r] = x[j];
+                    for (int j = 0; j < 4; ++j) tl.vt[c + j][r] = vv[s][i][j];
+                }
             }
         }
-        if (LE) {
-            const int j = threadIdx.x & 15;
-            tl.eta[j] = (tb0 + j < tend) ? re[s] : 0.f;
-        }
+        if (LE) tl.eta[threadIdx.x & 15] = ve[s];
     }
 };
 
@@ -141,21 +187,21 @@ template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
 // nothing, and bodies mask their stores with t < tend.
 template <typename E, int D, int STAGE, int PD, int NT, typename Body>
 __device__ __forceinline__ void run_subblocks(SubTile<E, D> *tiles, Loader<E, D, STAGE, PD, NT> &ld,
-                                              int t0, int tend, const float *eta_h, Body &&body)
+                                              int t0, int tend, Body &&body)
 {
     static_assert(PD % 2 == 0, "PD must be even");
     const int nsb = (tend - t0 + 15) / 16;
     const int ngroups = (nsb + PD - 1) / PD;
 #pragma unroll
-    for (int s = 0; s < PD; ++s) ld.issue(s, t0 + 16 * s, tend, eta_h);
-    ld.commit(0, tiles[0], t0, tend);
+    for (int s = 0; s < PD; ++s) ld.issue(s, t0 + 16 * s);
+    ld.commit(0, tiles[0]);
     lds_barrier();
     for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
         for (int j = 0; j < PD; ++j) {
             const int sb = gi * PD + j;
-            ld.issue(j, t0 + 16 * (sb + PD), tend, eta_h);
-            ld.commit((j + 1) % PD, tiles[(j + 1) & 1], t0 + 16 * (sb + 1), tend);
+            ld.issue(j, t0 + 16 * (sb + PD));
+            ld.commit((j + 1) % PD, tiles[(j + 1) & 1]);
             body(tiles[j & 1], t0 + 16 * sb);
             lds_barrier();
         }
@@ -217,6 +263,15 @@ __device__ __forceinline__ f32x4 mma_state_a(f32x4 acc, const SplitFrag<E> *S,
     return acc;
 }
 
+// acc += A(16 x D) * B(D x 16) with both operands as D/16 fragments.
+template <typename F, int ND>
+__device__ __forceinline__ f32x4 mma_b(f32x4 acc, const F *A, const F *B)
+{
+#pragma unroll
+    for (int r = 0; r < ND; r += 2) acc = mma32(acc, A[r], A[r + 1], B[r], B[r + 1]);
+    return acc;
+}
+
 // ---------------------------------------------------------------------------
 // summary: P_s (MSE) and B_s of a segment.  The state X = [P | B] starts at 0
 // and follows X <- X + K^T H (R - K X_c) over the segment's chunks, with
@@ -239,21 +294,23 @@ __global__ __launch_bounds__((MSE ? 2 : 1) * (D / 16) / CPW * 64) void lin_summa
     const int tend = min(T, t0 + p.seg_tokens);
 
     Loader<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT> ld;
-    ld.init(threadIdx.x, p, h, T);
+    ld.init(threadIdx.x, p, h, T, tend);
     const float *eta_h = p.eta + (size_t)h * T;
 
+    // X starts at 0 and stays moderate, so one bf16 rounding per element is
+    // enough for the residual product.
     f32x4 X[CPW][ND];
-    SplitFrag<E> Xr[CPW][ND], Xs[SNAP ? CPW : 1][ND];
+    F Xr[CPW][ND], Xs[SNAP ? CPW : 1][ND];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
         for (int r = 0; r < ND; ++r) {
             X[c][r] = zero4();
-            Xr[c][r].set(zero4());
+            Xr[c][r] = to_frag<E>(zero4());
             if (SNAP) Xs[c][r] = Xr[c][r];
         }
 
-    run_subblocks<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend, eta_h,
+    run_subblocks<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend,
         [&](SubTile<E, D> &tl, int tg) {
             if (SNAP && MSE && (tg % p.chunk) == 0) {
 #pragma unroll
@@ -273,20 +330,19 @@ __global__ __launch_bounds__((MSE ? 2 : 1) * (D / 16) / CPW * 64) void lin_summa
                 const int x = wave * CPW + c;
                 const bool pcol = MSE && x < ND;
                 const int cb = pcol ? x : x - (MSE ? ND : 0);
-                f32x4 U = frag_to_f32(pcol ? lds_frag<E>(&tl.kt[16 * cb + m][4 * g])
-                                           : lds_frag<E>(&tl.vt[16 * cb + m][4 * g]));
-                if (MSE) U = U - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Xs[c] : Xr[c]);
+                f32x4 U = frag_to_f32(tok_frag<E, D>(tl, !pcol, cb, m, g));
+                if (MSE) U = U - mma_b<F, ND>(zero4(), Ka, SNAP ? Xs[c] : Xr[c]);
                 EU[c] = to_frag<E>(U * et);
             }
             F KtA[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) KtA[r] = lds_frag<E>(&tl.kt[16 * r + m][4 * g]);
+            for (int r = 0; r < ND; ++r) KtA[r] = tok_frag<E, D>(tl, false, r, m, g);
 #pragma unroll
             for (int c = 0; c < CPW; ++c)
 #pragma unroll
                 for (int r = 0; r < ND; ++r) {
                     X[c][r] = mma16(X[c][r], KtA[r], EU[c]);
-                    if (MSE) Xr[c][r].set(X[c][r]);
+                    if (MSE) Xr[c][r] = to_frag<E>(X[c][r]);
                 }
         });
 
@@ -409,32 +465,38 @@ __global__ __launch_bounds__((D / 16) / CPW * 64) void lin_replay(LinParams p)
 
     const float *ws = (p.S > 1) ? p.wsW + ((size_t)h * (p.S + 1) + seg) * D * D
                                 : p.w_init + (size_t)h * D * D;
-    f32x4 W[CPW][ND];
-    SplitFrag<E> Wr[CPW][ND], Ws[SNAP ? CPW : 1][ND];
+    // State = W0 + dW: the start state enters products as a split (hi/lo)
+    // pair computed once; the change dW since the segment start stays small,
+    // so one bf16 rounding of it per sub-block is enough.
+    SplitFrag<E> W0[CPW][ND];
+    f32x4 dW[CPW][ND];
+    F dWr[CPW][ND], dWs[SNAP ? CPW : 1][ND];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
         const int cb = wave * CPW + c;
 #pragma unroll
         for (int r = 0; r < ND; ++r) {
+            f32x4 w;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) W[c][r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
-            Wr[c][r].set(W[c][r]);
-            if (SNAP) Ws[c][r] = Wr[c][r];
+            for (int j = 0; j < 4; ++j) w[j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
+            W0[c][r].set(w);
+            dW[c][r] = zero4();
+            dWr[c][r] = to_frag<E>(zero4());
+            if (SNAP) dWs[c][r] = dWr[c][r];
         }
     }
 
     Loader<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT> ld;
-    ld.init(threadIdx.x, p, h, T);
-    const float *eta_h = p.eta + (size_t)h * T;
+    ld.init(threadIdx.x, p, h, T, tend);
     E *out_h = (E *)p.out + (size_t)h * T * D;
 
-    run_subblocks<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend, eta_h,
+    run_subblocks<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend,
         [&](SubTile<E, D> &tl, int tg) {
             if (SNAP && MSE && (tg % p.chunk) == 0) {
 #pragma unroll
                 for (int c = 0; c < CPW; ++c)
 #pragma unroll
-                    for (int r = 0; r < ND; ++r) Ws[c][r] = Wr[c][r];
+                    for (int r = 0; r < ND; ++r) dWs[c][r] = dWr[c][r];
             }
             F Qa[ND], Ka[ND];
 #pragma unroll
@@ -444,9 +506,7 @@ __global__ __launch_bounds__((D / 16) / CPW * 64) void lin_replay(LinParams p)
             }
             const f32x4 et = *reinterpret_cast<const f32x4 *>(&tl.eta[4 * g]);
             // S^T[i][t] = k_i . q_t, kept for i <= t, times eta_i.
-            f32x4 St = zero4();
-#pragma unroll
-            for (int r = 0; r < ND; r += 2) St = mma32(St, Ka[r], Ka[r + 1], Qa[r], Qa[r + 1]);
+            f32x4 St = mma_b<F, ND>(zero4(), Ka, Qa);
 #pragma unroll
             for (int j = 0; j < 4; ++j) St[j] = (4 * g + j <= m) ? St[j] * et[j] : 0.f;
             const F Sf = to_frag<E>(St);
@@ -455,39 +515,57 @@ __global__ __launch_bounds__((D / 16) / CPW * 64) void lin_replay(LinParams p)
 #pragma unroll
             for (int c = 0; c < CPW; ++c) {
                 const int cb = wave * CPW + c;
-                f32x4 U = frag_to_f32(lds_frag<E>(&tl.vt[16 * cb + m][4 * g]));
-                if (MSE) U = U - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Ws[c] : Wr[c]);
-                // O^T = W_run^T Q^T + U^T S^T.  The two terms use separate
-                // accumulators: no accumulation chain mixes MFMA shapes
-                // (16x16x32 feeding 16x16x16).
+                f32x4 U = frag_to_f32(tok_frag<E, D>(tl, true, cb, m, g));
+                if (MSE) {
+                    f32x4 P = zero4();
+#pragma unroll
+                    for (int r = 0; r < ND; r += 2) P = mma32(P, Ka[r], Ka[r + 1], W0[c][r].hi, W0[c][r + 1].hi);
+                    P = mma_b<F, ND>(P, Ka, SNAP ? dWs[c] : dWr[c]);
+                    U = U - P;
+                }
+                // O^T = W^T Q^T + U^T S^T with W = W0 + dW (running).  The two
+                // terms use separate accumulators: no accumulation chain mixes
+                // MFMA shapes (16x16x32 feeding 16x16x16).
                 const f32x4 Oi = mma16(zero4(), to_frag<E>(U), Sf);
-                const f32x4 O = mma_state_a<E, ND>(zero4(), Wr[c], Qa) + Oi;
+                f32x4 O = mma_state_a<E, ND>(zero4(), W0[c], Qa);
+#pragma unroll
+                for (int r = 0; r < ND; r += 2) O = mma32(O, dWr[c][r], dWr[c][r + 1], Qa[r], Qa[r + 1]);
+                O = O + Oi;
                 if (t < tend) store4<E>(out_h + (size_t)t * D + 16 * cb + 4 * g, out4<E>(O));
                 EU[c] = to_frag<E>(U * et);
             }
-            // W += K^T (eta * U)
+            // dW += K^T (eta * U)
             F KtA[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) KtA[r] = lds_frag<E>(&tl.kt[16 * r + m][4 * g]);
+            for (int r = 0; r < ND; ++r) KtA[r] = tok_frag<E, D>(tl, false, r, m, g);
 #pragma unroll
             for (int c = 0; c < CPW; ++c)
 #pragma unroll
                 for (int r = 0; r < ND; ++r) {
-                    W[c][r] = mma16(W[c][r], KtA[r], EU[c]);
-                    Wr[c][r].set(W[c][r]);
+                    dW[c][r] = mma16(dW[c][r], KtA[r], EU[c]);
+                    dWr[c][r] = to_frag<E>(dW[c][r]);
                 }
         });
 
     if (seg == p.S - 1) {
+        // final state = start state + change; all reads before any write (w_final
+        // may alias w_init when there is a single segment)
         float *wf = p.w_final + (size_t)h * D * D;
+        f32x4 w0f[CPW][ND];
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int cb = wave * CPW + c;
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int r = 0; r < ND; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[c][r][j];
-        }
+                for (int j = 0; j < 4; ++j)
+                    w0f[c][r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * (wave * CPW + c) + m];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    wf[(size_t)(16 * r + 4 * g + j) * D + 16 * (wave * CPW + c) + m] = w0f[c][r][j] + dW[c][r][j];
     }
 }
 
@@ -519,9 +597,9 @@ __global__ __launch_bounds__((D / 16) / CPW * 64) void lin_apply(LinParams p, co
             Wr[c][r].set(w);
         }
     Loader<E, D, STAGE_Q, PD, NT> ld;
-    ld.init(threadIdx.x, p, h, T);
+    ld.init(threadIdx.x, p, h, T, tend);
     E *out_h = (E *)p.out + (size_t)h * T * D;
-    run_subblocks<E, D, STAGE_Q, PD, NT>(tiles, ld, t0, tend, nullptr,
+    run_subblocks<E, D, STAGE_Q, PD, NT>(tiles, ld, t0, tend,
         [&](SubTile<E, D> &tl, int tg) {
             F Qa[ND];
 #pragma unroll
