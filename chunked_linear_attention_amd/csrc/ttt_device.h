@@ -36,17 +36,19 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 __device__ __forceinline__ f32x4 to_f32x4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
 
-// x = hi + lo with hi = x truncated to bf16 (low 16 bits cleared, exact in
-// fp32) and lo = bf16(x - hi): about 16 mantissa bits in two bf16 operands.
+// x = hi + lo with hi = bf16(x) (nearest even) and lo = bf16(x - hi), where
+// x - hi is exact in fp32: about 16 mantissa bits in two bf16 operands, and hi
+// alone is the correctly rounded single operand.
 __device__ __forceinline__ void split_bf16x4(f32x4 x, bf16x4 &hi, bf16x4 &lo)
 {
-    const u32x4 xb = __builtin_bit_cast(u32x4, x);
-    const u32x4 hb = xb & 0xFFFF0000u;
-    lo = to_bf16x4(x - __builtin_bit_cast(f32x4, hb));
-    u32x2 h;
-    h[0] = __builtin_amdgcn_perm(xb[1], xb[0], 0x07060302u);
-    h[1] = __builtin_amdgcn_perm(xb[3], xb[2], 0x07060302u);
-    hi = __builtin_bit_cast(bf16x4, h);
+    hi = to_bf16x4(x);
+    const u32x2 hb = __builtin_bit_cast(u32x2, hi);
+    f32x4 hf;
+    hf[0] = __builtin_bit_cast(float, hb[0] << 16);
+    hf[1] = __builtin_bit_cast(float, hb[0] & 0xFFFF0000u);
+    hf[2] = __builtin_bit_cast(float, hb[1] << 16);
+    hf[3] = __builtin_bit_cast(float, hb[1] & 0xFFFF0000u);
+    lo = to_bf16x4(x - hf);
 }
 template <typename E> __device__ __forceinline__ typename Frag<E>::type to_frag(f32x4 x);
 template <> __device__ __forceinline__ f32x4 to_frag<float>(f32x4 x) { return x; }
@@ -81,6 +83,15 @@ __device__ __forceinline__ f32x4 mma32(f32x4 acc, f32x4 a0, f32x4 a1, f32x4 b0, 
     acc = mma16(acc, a0, b0);
     return mma16(acc, a1, b1);
 }
+// A single 16-deep product issued in the 32-deep shape (second half zero), so
+// an accumulation chain never mixes MFMA shapes; a 16x16x16 bf16 MFMA costs
+// as much as a 16x16x32 one on gfx950.  fp32 has no such shape change.
+__device__ __forceinline__ f32x4 mma32z(f32x4 acc, bf16x4 a0, bf16x4 b0)
+{
+    const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    return mma32(acc, a0, z, b0, z);
+}
+__device__ __forceinline__ f32x4 mma32z(f32x4 acc, f32x4 a0, f32x4 b0) { return mma16(acc, a0, b0); }
 
 // ---- small vector memory helpers --------------------------------------------
 // Four consecutive elements (8 bytes for bf16, 16 bytes for fp32).

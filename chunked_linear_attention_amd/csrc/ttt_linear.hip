@@ -1,4 +1,5 @@
-// TTT-Linear forward on gfx950: segment-parallel chunked gradient descent.
+// TTT-Linear forward on gfx950: segment-parallel chunked gradient descent,
+// walked in super-blocks of up to 64 tokens.
 //
 // What is computed ("Test-Time Training (TTT)" summary page: "TTT definition",
 // examples 1 and 2, "TTT-Linear", "Mini-batch gradient descent"; the parallel
@@ -10,24 +11,33 @@
 //
 // How it is laid out on the chip (not on the pages):
 //  * Column separability.  Column j of W only ever meets column j of V, U
-//    and O, so one wave owns a 16-column block of the state and runs its
-//    chain with the state resident in MFMA accumulators (fp32), never
-//    leaving registers across chunks.  A workgroup = one wave per column
-//    block, sharing the token tiles it stages in LDS.
-//  * Sub-blocks of 16 tokens.  A chunk of b tokens (b a multiple of 16) is
-//    walked 16 tokens at a time: U uses the chunk-start snapshot of the
-//    state, the inter-chunk read uses the running state (which already holds
-//    the chunk's earlier sub-blocks), and the diagonal 16 x 16 block supplies
-//    the rest of the causal intra-chunk term.  This is the same sum as the
-//    b x b masked product, regrouped; work per token is O(d^2) for every b.
+//    and O, so one wave owns a 16-column block of the state and keeps it in
+//    MFMA accumulators (fp32) for a whole segment.  A workgroup = one wave
+//    per column block, sharing the token tiles it stages in LDS.
+//  * Super-blocks.  Tokens are walked in super-blocks of up to 64 tokens (four
+//    16-token tiles), placed so that every token of a super-block takes its
+//    residual from the same state:
+//      b <= 64: a super-block is floor(64/b) whole chunks.  With R the running
+//        state at its start and, for tiles j < i in different chunks,
+//        L_ij = K_i K_j^T diag(eta_j), the chunk rule reads (I + L) U = V - K R.
+//        Block forward substitution applies T = (I + L)^-1 to K and V, which
+//        do not depend on the state: U = Vt - Kt R with Kt = T K, Vt = T V.
+//        (Exact up to rounding; it is the chunk recurrence written for four
+//        tiles at once.)
+//      b > 64: a super-block lies inside one chunk and every residual uses the
+//        chunk-start snapshot S: U = V - K S.
+//    Either way O = Q R + (Q K^T * M_incl * eta^T) U over the super-block (the
+//    running state is the sum of all earlier updates) and R <- R + K^T diag(eta) U.
+//    One super-block is one step of the serial chain, and every product in it
+//    has four independent 16-token tiles.
 //  * Segments.  The chunk update is affine in the state,
 //    W_{c+1} = (I - K_c^T H_c K_c) W_c + K_c^T H_c V_c, so a run of whole
 //    chunks (a segment) is one affine map W -> W - P W + B.  Three kernels:
 //      summary : every segment (but the last, causal) computes P and B from
 //                its keys/values alone, all segments in parallel;
 //      prefix  : per (head, column block), W_start(s+1) = W_s - P_s W_s + B_s;
-//      replay  : every segment replays its chunks from W_start(s) and writes
-//                its outputs; the last segment writes the final state.
+//      replay  : every segment replays its super-blocks from W_start(s) and
+//                writes its outputs; the last segment writes the final state.
 //    For the inner-product loss P = 0 and the prefix is a running sum.
 //  * Non-causal order: summary over all segments, prefix to W_final, then an
 //    apply kernel O = Q W_final.
@@ -45,30 +55,15 @@ struct LinParams {
     float *w_final;
     void *wsP;      // [NH][Ssum][d][d] element type (MSE only)
     float *wsB;     // [NH][Ssum][d][d]
-    float *wsW;     // [NH][S + 1][d][d]: W_start(s); slot S = final state
+    float *wsW0;    // [NH][d][d]: copy of w_init read by the replay (causal, S > 1)
     int NH, Tq, Tkv, chunk, seg_tokens, S, Ssum, seg_q, Sq;
 };
 
-// LDS image of one 16-token sub-block, token-major.  The fragments that need
-// four consecutive tokens of one feature (K^T for the update, V in the
-// accumulator layout) come from the same token-major tiles through gfx950's
-// transposing LDS read for 16-bit data; the fp32 path keeps feature-major
-// copies instead (kt, vt; rows padded to 20 elements).
-template <typename E, int D> struct alignas(16) SubTile {
-    static constexpr bool TR = sizeof(E) == 2;
-    static constexpr int RP = D + (sizeof(E) == 2 ? 8 : 4);  // token-major row pitch
-    static constexpr int FP = 20;                            // feature-major row pitch
-    E qs[16][RP];
-    E ks[16][RP];
-    E vs[TR ? 16 : 1][RP];
-    E kt[TR ? 1 : D][FP];
-    E vt[TR ? 1 : D][FP];
-    float eta[16];
-};
+constexpr int SB = 64;  // tokens per super-block tile (four 16-token tiles)
 
 // Transposing read (16-bit elements): within each group of 16 lanes, lane i
 // slot j receives the element that lane 4j + i/4 would read at slot i%4.
-// Lane (m, g) pointing at row 4g + m/4, column c0 + 4(m%4) of a token-major
+// Lane (m, g) pointing at row 4g + m/4, column c0 + 4(m%4) of a row-major
 // tile therefore receives tile[4g + j][c0 + m], j = 0..3.
 __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p)
 {
@@ -78,67 +73,132 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p)
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Fragment with k = token (4 consecutive tokens per lane) of column block
-// `blk` of K or V: lane (m, g) gets X[4g + j][16 blk + m].
-template <typename E, int D>
-__device__ __forceinline__ typename Frag<E>::type tok_frag(const SubTile<E, D> &tl, bool from_v, int blk,
-                                                           int m, int g)
-{
-    if constexpr (SubTile<E, D>::TR) {
-        const E(*src)[SubTile<E, D>::RP] = from_v ? tl.vs : tl.ks;
-        return lds_read_tr(&src[4 * g + (m >> 2)][16 * blk + 4 * (m & 3)]);
-    } else {
-        const E(*src)[SubTile<E, D>::FP] = from_v ? tl.vt : tl.kt;
-        return load4<E>(&src[16 * blk + m][4 * g]);
-    }
-}
-
 // Which tensors a kernel stages.
 enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
 
+// LDS image of one 64-token super-block.  bf16: token-major tiles; fragments
+// that need four consecutive tokens of one feature come from the transposing
+// read.  fp32: queries token-major, keys and values feature-major (rows
+// padded), so both fragment kinds are plain 16-byte or scalar reads.
+template <typename E, int D, int ST> struct alignas(16) SbTile {
+    static constexpr bool TR = sizeof(E) == 2;
+    static constexpr bool LQ = (ST & STAGE_Q) != 0, LK = (ST & STAGE_K) != 0, LV = (ST & STAGE_V) != 0;
+    static constexpr int RP = D + (TR ? 8 : 4);  // token-major row pitch
+    static constexpr int FP = SB + 4;            // feature-major row pitch (fp32)
+    E qs[LQ ? SB : 1][RP];
+    E ks[(LK && TR) ? SB : 1][RP];
+    E vs[(LV && TR) ? SB : 1][RP];
+    E kt[(LK && !TR) ? D : 1][FP];
+    E vt[(LV && !TR) ? D : 1][FP];
+    float eta[SB];
+};
+
+// Row fragment (rows = tokens of tile i, contraction over features 16r..16r+15):
+// lane (m, g) gets X[16i + m][16r + 4g + j].
+template <typename E, int D, int ST>
+__device__ __forceinline__ typename Frag<E>::type q_row(const SbTile<E, D, ST> &t, int i, int r, int m, int g)
+{
+    return load4<E>(&t.qs[16 * i + m][16 * r + 4 * g]);
+}
+template <typename E, int D, int ST>
+__device__ __forceinline__ typename Frag<E>::type k_row(const SbTile<E, D, ST> &t, int i, int r, int m, int g)
+{
+    if constexpr (SbTile<E, D, ST>::TR) {
+        return load4<E>(&t.ks[16 * i + m][16 * r + 4 * g]);
+    } else {
+        f32x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = t.kt[16 * r + 4 * g + j][16 * i + m];
+        return x;
+    }
+}
+// Token fragment (contraction over the tokens of tile i, features 16c..16c+15):
+// lane (m, g) gets X[16i + 4g + j][16c + m].  As an A operand it is the
+// transposed tile, as a B operand the tile itself, as an accumulator the C layout.
+template <typename E, int D, int ST>
+__device__ __forceinline__ typename Frag<E>::type k_tok(const SbTile<E, D, ST> &t, int i, int c, int m, int g)
+{
+    if constexpr (SbTile<E, D, ST>::TR)
+        return lds_read_tr(&t.ks[16 * i + 4 * g + (m >> 2)][16 * c + 4 * (m & 3)]);
+    else
+        return load4<E>(&t.kt[16 * c + m][16 * i + 4 * g]);
+}
+template <typename E, int D, int ST>
+__device__ __forceinline__ typename Frag<E>::type v_tok(const SbTile<E, D, ST> &t, int i, int c, int m, int g)
+{
+    if constexpr (SbTile<E, D, ST>::TR)
+        return lds_read_tr(&t.vs[16 * i + 4 * g + (m >> 2)][16 * c + 4 * (m & 3)]);
+    else
+        return load4<E>(&t.vt[16 * c + m][16 * i + 4 * g]);
+}
+
+// Transformed keys Kt = T K of one super-block, shared by the waves: each wave
+// writes its column block (accumulator layout), every wave reads row
+// fragments.  bf16: feature-major, 8-byte writes, transposing reads.
+template <typename E, int D> struct alignas(16) KtTile;
+template <int D> struct alignas(16) KtTile<__bf16, D> {
+    __bf16 fm[D][SB + 8];
+    __device__ __forceinline__ void put(int c, int i, f32x4 x, int m, int g)
+    {
+        store4<__bf16>(&fm[16 * c + m][16 * i + 4 * g], to_bf16x4(x));
+    }
+    __device__ __forceinline__ bf16x4 row(int i, int r, int m, int g) const
+    {
+        return lds_read_tr(&fm[16 * r + 4 * g + (m >> 2)][16 * i + 4 * (m & 3)]);
+    }
+};
+template <int D> struct alignas(16) KtTile<float, D> {
+    float tm[SB][D + 4];
+    __device__ __forceinline__ void put(int c, int i, f32x4 x, int m, int g)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tm[16 * i + 4 * g + j][16 * c + m] = x[j];
+    }
+    __device__ __forceinline__ f32x4 row(int i, int r, int m, int g) const
+    {
+        return load4<float>(&tm[16 * i + m][16 * r + 4 * g]);
+    }
+};
+
 // Cooperative global -> register -> LDS loader with a ring of PD register
-// slots.  Every thread runs the same instruction stream: for each staged
-// tensor it moves CPT pieces of 4 consecutive features of one token (8 bytes
-// bf16, 16 bytes fp32) and one eta value, with buffer loads: the per-thread
-// byte offset is fixed, the sub-block's position is the scalar offset, and
-// the buffer's extent ends at the segment's last token, so rows past it read
-// as zero in hardware (no clamps, selects or 64-bit address arithmetic).
-template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
-    typedef typename Vec4<E>::type V4;
-    static constexpr bool LQ = STAGE & STAGE_Q, LK = STAGE & STAGE_K, LV = STAGE & STAGE_V,
-                          LE = STAGE & STAGE_E;
-    static constexpr int CPT = (4 * D) / NT;  // pieces per tensor per thread (16 rows x D/4 pieces)
-    static_assert(CPT >= 1 && CPT * NT == 4 * D, "loader shape");
-    int row[CPT], col[CPT];
-    int voff[CPT];
+// slots.  Every thread moves CPT 16-byte pieces of each staged tensor per
+// super-block and one eta value, with buffer loads: the per-thread byte
+// offset is fixed, the super-block's first token is the scalar offset, and the
+// buffer's extent ends at the segment's last token, so rows past it read as
+// zero in hardware.
+template <typename E, int D, int ST, int PD, int NT> struct SbLoader {
+    typedef SbTile<E, D, ST> Tile;
+    static constexpr bool TR = Tile::TR, LQ = Tile::LQ, LK = Tile::LK, LV = Tile::LV;
+    static constexpr bool LE = (ST & STAGE_E) != 0;
+    static constexpr int PE = 16 / (int)sizeof(E);  // elements per piece
+    static constexpr int PPR = D / PE;              // pieces per token row
+    static constexpr int CPT = SB * PPR / NT;       // pieces per thread per tensor
+    static_assert(CPT >= 1 && CPT * NT == SB * PPR, "loader shape");
+    int row[CPT], col[CPT], voff[CPT];
     __amdgpu_buffer_rsrc_t rq, rk, rv, re;
-    V4 vq[PD][CPT], vk[PD][CPT], vv[PD][CPT];
+    u32x4 vq[PD][CPT], vk[PD][CPT], vv[PD][CPT];
     float ve[PD];
 
-    __device__ void init(int tid, const LinParams &p, int h, int T, int tend)
+    __device__ void init(int tid, const void *q, const void *k, const void *v, const float *eta, int h,
+                         int T, int tend)
     {
         const size_t hoff = (size_t)h * T * D;
         const int bytes = tend * D * (int)sizeof(E);
-        rq = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)p.q + hoff), (short)0, LQ ? bytes : 0, 0x00020000);
-        rk = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)p.k + hoff), (short)0, LK ? bytes : 0, 0x00020000);
-        rv = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)p.v + hoff), (short)0, LV ? bytes : 0, 0x00020000);
-        re = __builtin_amdgcn_make_buffer_rsrc((void *)(LE ? p.eta + (size_t)h * T : p.eta), (short)0,
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)q + (LQ ? hoff : 0)), (short)0,
+                                               LQ ? bytes : 0, 0x00020000);
+        rk = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)k + (LK ? hoff : 0)), (short)0,
+                                               LK ? bytes : 0, 0x00020000);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void *)((const E *)v + (LV ? hoff : 0)), (short)0,
+                                               LV ? bytes : 0, 0x00020000);
+        re = __builtin_amdgcn_make_buffer_rsrc((void *)(eta + (LE ? (size_t)h * T : 0)), (short)0,
                                                LE ? tend * 4 : 0, 0x00020000);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int piece = tid + i * NT;
-            row[i] = piece / (D / 4);
-            col[i] = piece % (D / 4);
-            voff[i] = (row[i] * D + 4 * col[i]) * (int)sizeof(E);
+            row[i] = piece / PPR;
+            col[i] = piece % PPR;
+            voff[i] = (row[i] * D + PE * col[i]) * (int)sizeof(E);
         }
-    }
-
-    __device__ __forceinline__ V4 bload(__amdgpu_buffer_rsrc_t r, int vo, int so)
-    {
-        if constexpr (sizeof(E) == 2)
-            return __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
-        else
-            return __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
     }
 
     __device__ __forceinline__ void issue(int s, int tb0)
@@ -146,77 +206,112 @@ template <typename E, int D, int STAGE, int PD, int NT> struct Loader {
         const int so = tb0 * D * (int)sizeof(E);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            if (LQ) vq[s][i] = bload(rq, voff[i], so);
-            if (LK) vk[s][i] = bload(rk, voff[i], so);
-            if (LV) vv[s][i] = bload(rv, voff[i], so);
+            if (LQ) vq[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff[i], so, 0);
+            if (LK) vk[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], so, 0);
+            if (LV) vv[s][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], so, 0);
         }
-        if (LE) ve[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, (int)(threadIdx.x & 15) * 4, tb0 * 4, 0));
+        if (LE)
+            ve[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  re, (int)(threadIdx.x & (SB - 1)) * 4, tb0 * 4, 0));
     }
 
     // Write slot s to LDS.
-    __device__ __forceinline__ void commit(int s, SubTile<E, D> &tl)
+    __device__ __forceinline__ void commit(int s, Tile &tl)
     {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int r = row[i], c = 4 * col[i];
-            if (LQ) store4<E>(&tl.qs[r][c], vq[s][i]);
+            const int r = row[i], c = PE * col[i];
+            if (LQ) *reinterpret_cast<u32x4 *>(&tl.qs[r][c]) = vq[s][i];
             if (LK) {
-                store4<E>(&tl.ks[r][c], vk[s][i]);
-                if constexpr (!SubTile<E, D>::TR) {
+                if constexpr (TR) {
+                    *reinterpret_cast<u32x4 *>(&tl.ks[r][c]) = vk[s][i];
+                } else {
+                    const f32x4 x = __builtin_bit_cast(f32x4, vk[s][i]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) tl.kt[c + j][r] = vk[s][i][j];
+                    for (int j = 0; j < 4; ++j) tl.kt[c + j][r] = x[j];
                 }
             }
             if (LV) {
-                if constexpr (SubTile<E, D>::TR) {
-                    store4<E>(&tl.vs[r][c], vv[s][i]);
+                if constexpr (TR) {
+                    *reinterpret_cast<u32x4 *>(&tl.vs[r][c]) = vv[s][i];
                 } else {
+                    const f32x4 x = __builtin_bit_cast(f32x4, vv[s][i]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) tl.vt[c + j][r] = vv[s][i][j];
+                    for (int j = 0; j < 4; ++j) tl.vt[c + j][r] = x[j];
                 }
             }
         }
-        if (LE) tl.eta[threadIdx.x & 15] = ve[s];
+        if (LE) tl.eta[threadIdx.x & (SB - 1)] = ve[s];
     }
 };
 
-// Drive the staged loop over the sub-blocks [t0, tend) of one head; `body` is
-// called once per sub-block with the LDS tile and the sub-block's first token.
-// The sub-block count is padded up to a multiple of PD so that the ring runs
-// without branches; padded sub-blocks are all-zero (eta = 0) and change
-// nothing, and bodies mask their stores with t < tend.
-template <typename E, int D, int STAGE, int PD, int NT, typename Body>
-__device__ __forceinline__ void run_subblocks(SubTile<E, D> *tiles, Loader<E, D, STAGE, PD, NT> &ld,
-                                              int t0, int tend, Body &&body)
+// Super-block schedule inside a segment (the segment starts on a chunk
+// boundary).  b <= 64: super-block n covers floor(64/b) whole chunks.  b > 64:
+// each chunk is cut into 64-token pieces plus a shorter last piece.
+struct SbSched {
+    int b, L, per;
+    __device__ explicit SbSched(int chunk) : b(chunk)
+    {
+        if (chunk <= SB) {
+            L = (SB / chunk) * chunk;
+            per = 1;
+        } else {
+            L = SB;
+            per = (chunk + SB - 1) / SB;
+        }
+    }
+    __device__ int start(int n) const { return b <= SB ? n * L : (n / per) * b + SB * (n % per); }
+    __device__ int len(int n) const { return b <= SB ? L : min(SB, b - SB * (n % per)); }
+    __device__ int count(int rem) const
+    {
+        return b <= SB ? (rem + L - 1) / L : (rem / b) * per + (rem % b + SB - 1) / SB;
+    }
+    __device__ bool chunk_start(int n) const { return b <= SB || (n % per) == 0; }
+};
+
+// Drive the staged loop over the super-blocks of [t0, tend); `body(tile, n)`
+// runs once per super-block.  The count is padded up to a multiple of PD so
+// the ring runs without branches: padded super-blocks start past tend, read
+// as zero (eta = 0) and change nothing; bodies mask their stores.
+// NBUF = 2: the next tile is written while the current one is read (one
+// barrier per super-block); NBUF = 1 (large fp32 tiles): write after a barrier.
+template <typename E, int D, int ST, int PD, int NT, int NBUF, typename Body>
+__device__ __forceinline__ void run_sb(SbTile<E, D, ST> *tiles, SbLoader<E, D, ST, PD, NT> &ld,
+                                       const SbSched &sc, int t0, int tend, Body &&body)
 {
-    static_assert(PD % 2 == 0, "PD must be even");
-    const int nsb = (tend - t0 + 15) / 16;
+    static_assert(NBUF == 1 || PD % 2 == 0, "double buffering needs an even ring");
+    const int nsb = sc.count(tend - t0);
     const int ngroups = (nsb + PD - 1) / PD;
 #pragma unroll
-    for (int s = 0; s < PD; ++s) ld.issue(s, t0 + 16 * s);
+    for (int s = 0; s < PD; ++s) {
+        ld.issue(s, t0 + sc.start(s));
+        __builtin_amdgcn_sched_barrier(0);  // same load order as the loop body
+    }
     ld.commit(0, tiles[0]);
     lds_barrier();
     for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
         for (int j = 0; j < PD; ++j) {
-            const int sb = gi * PD + j;
-            ld.issue(j, t0 + 16 * (sb + PD));
-            ld.commit((j + 1) % PD, tiles[(j + 1) & 1]);
-            body(tiles[j & 1], t0 + 16 * sb);
-            lds_barrier();
+            const int n = gi * PD + j;
+            ld.issue(j, t0 + sc.start(n + PD));
+            if constexpr (NBUF == 2) {
+                ld.commit((j + 1) % PD, tiles[(j + 1) & 1]);
+                body(tiles[j & 1], n);
+                lds_barrier();
+            } else {
+                body(tiles[0], n);
+                lds_barrier();
+                ld.commit((j + 1) % PD, tiles[0]);
+                lds_barrier();
+            }
         }
     }
 }
 
-template <typename E> __device__ __forceinline__ typename Frag<E>::type lds_frag(const E *p)
-{
-    return load4<E>(p);
-}
-
-// A state tile as MFMA operand.  bf16: hi = bf16(x), lo = bf16(x - hi), so
-// products with exact bf16 inputs keep ~16 mantissa bits of the state (the
-// state sits near the identity, where a single bf16 would lose the update).
-// fp32: hi = x, lo unused.
+// A state tile as MFMA operand.  bf16: hi = x truncated to bf16, lo =
+// bf16(x - hi), so products with exact bf16 inputs keep ~16 mantissa bits of
+// the state (the state sits near the identity, where a single bf16 would lose
+// the update).  fp32: hi = x, lo unused.
 template <typename E> struct SplitFrag {
     typedef typename Frag<E>::type F;
     static constexpr bool SPLIT = sizeof(E) == 2;
@@ -273,344 +368,545 @@ __device__ __forceinline__ f32x4 mma_b(f32x4 acc, const F *A, const F *B)
 }
 
 // ---------------------------------------------------------------------------
-// summary: P_s (MSE) and B_s of a segment.  The state X = [P | B] starts at 0
-// and follows X <- X + K^T H (R - K X_c) over the segment's chunks, with
-// R = [K | V] (MSE; A = I - P is the product of the chunk transitions) or
-// R = V (inner product, where X_c does not enter).  Column blocks 0..ND-1 of
-// X are P, ND..2ND-1 are B (MSE); each wave owns CPW column blocks.
+// Tile-pair blocks of a super-block, computed once per workgroup and shared
+// in fragment-native layout (lane l keeps lane l's fragment).
+//   index 0..5  : -L_ij, (i, j) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), as the
+//                 A operand of L_ij X_j: lane (m, g) holds
+//                 -(k_{16i+m} . k_{16j+4g+x}) eta_{16j+4g+x}, zero unless tile
+//                 j lies in an earlier chunk than tile i;
+//   index 6..15 : A_ij = (Q_i K_j^T * M * eta_j^T), j <= i, in the layout that
+//                 is the B operand of U_j^T A_ij^T: lane (m, g) holds
+//                 (q_{16i+m} . k_{16j+4g+x}) eta_{16j+4g+x}, causal (key <=
+//                 query) on the diagonal.
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool MSE, int CPW, bool SNAP, int PD>
-__global__ __launch_bounds__((MSE ? 2 : 1) * (D / 16) / CPW * 64) void lin_summary(LinParams p)
+__host__ __device__ constexpr int lblk(int i, int j) { return i * (i - 1) / 2 + j; }
+__host__ __device__ constexpr int ablk(int i, int j) { return 6 + i * (i + 1) / 2 + j; }
+__host__ __device__ constexpr int blk_i(int b) { return b < 6 ? (b < 1 ? 1 : b < 3 ? 2 : 3) : (b < 7 ? 0 : b < 9 ? 1 : b < 12 ? 2 : 3); }
+__host__ __device__ constexpr int blk_j(int b) { return b < 6 ? b - lblk(blk_i(b), 0) : b - ablk(blk_i(b), 0); }
+
+template <typename E, int D, int ST, int NW, bool WANT_L, bool WANT_A>
+__device__ __forceinline__ void pair_blocks(const SbTile<E, D, ST> &t, typename Frag<E>::type (*gb)[64],
+                                            const f32x4 *et, int chunk, int wave, int lane, int m, int g)
 {
     typedef typename Frag<E>::type F;
     constexpr int ND = D / 16;
-    constexpr int NW = (MSE ? 2 : 1) * ND / CPW;
-    constexpr int NT = NW * 64;
-    __shared__ SubTile<E, D> tiles[2];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const bool isL = b < 6;
+        if (isL && !WANT_L) continue;
+        if (!isL && !WANT_A) continue;
+        if (b % NW != wave) continue;
+        const int i = blk_i(b), j = blk_j(b);
+        if (isL && !((16 * j) / chunk < (16 * i) / chunk)) {
+            gb[b][lane] = to_frag<E>(zero4());
+            continue;
+        }
+        F Kj[ND], Xi[ND];
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            Kj[r] = k_row(t, j, r, m, g);
+            if constexpr (SbTile<E, D, ST>::LQ)
+                Xi[r] = isL ? k_row(t, i, r, m, g) : q_row(t, i, r, m, g);
+            else
+                Xi[r] = k_row(t, i, r, m, g);
+        }
+        f32x4 acc = mma_b<F, ND>(zero4(), Kj, Xi);
+        if (isL) {
+            acc = acc * (-et[j]);
+        } else {
+            acc = acc * et[j];
+            if (i == j) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[x] = (4 * g + x <= m) ? acc[x] : 0.f;
+            }
+        }
+        gb[b][lane] = to_frag<E>(acc);
+    }
+}
+
+// Kt = T K and Vt = T V for one column block c by block forward substitution:
+// X~_i = X_i - sum_{j<i} L_ij X~_j (the -L_ij are the shared blocks 0..5).
+template <typename E>
+__device__ __forceinline__ void substitute(f32x4 *X, const typename Frag<E>::type *Ln)
+{
+    typedef typename Frag<E>::type F;
+    const F x0 = to_frag<E>(X[0]);
+    X[1] = mma32z(X[1], Ln[lblk(1, 0)], x0);
+    const F x1 = to_frag<E>(X[1]);
+    X[2] = mma32(X[2], Ln[lblk(2, 0)], Ln[lblk(2, 1)], x0, x1);
+    const F x2 = to_frag<E>(X[2]);
+    X[3] = mma32(X[3], Ln[lblk(3, 0)], Ln[lblk(3, 1)], x0, x1);
+    X[3] = mma32z(X[3], Ln[lblk(3, 2)], x2);
+}
+
+// eta of the tokens a lane's accumulator rows cover, masked to the super-block.
+template <typename E, int D, int ST>
+__device__ __forceinline__ void load_eta(const SbTile<E, D, ST> &t, int len, int g, f32x4 *et)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) et[i] = *reinterpret_cast<const f32x4 *>(&t.eta[16 * i + 4 * g]);
+    if (len < SB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) et[i][x] = (16 * i + 4 * g + x < len) ? et[i][x] : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// summary: P_s (MSE) and B_s of a segment.  The state X = [P | B] starts at 0
+// and follows the chunk rule with residual R - K X_c, R = [K | V] (MSE; A = I -
+// P is the product of the chunk transitions) or R = V (inner product, where
+// X_c does not enter).  Wave c owns column block c of P and of B.
+// LT: b < 64 (transform by T); SNAP: b > 64 (chunk-start snapshots).
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool MSE, bool LT, bool SNAP, int PD>
+__global__ __launch_bounds__((D / 16) * 64) void lin_summary(LinParams p)
+{
+    typedef typename Frag<E>::type F;
+    constexpr int ND = D / 16;
+    constexpr int NT = ND * 64;
+    constexpr int NBUF = sizeof(E) == 2 ? 2 : 1;
+    constexpr int ST = STAGE_K | STAGE_V | STAGE_E;
+    __shared__ SbTile<E, D, ST> tiles[NBUF];
+    __shared__ KtTile<E, LT ? D : 16> kts;
+    __shared__ F gb[LT ? 16 : 1][64];
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // column block
     const int seg = blockIdx.x % p.Ssum, h = blockIdx.x / p.Ssum;
     const int T = p.Tkv;
     const int t0 = seg * p.seg_tokens;
     const int tend = min(T, t0 + p.seg_tokens);
+    const SbSched sc(p.chunk);
 
-    Loader<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT> ld;
-    ld.init(threadIdx.x, p, h, T, tend);
-    const float *eta_h = p.eta + (size_t)h * T;
+    if (seg == 0 && p.wsW0) {
+        // copy of w_init for the replay (w_final may alias w_init)
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(p.w_init + (size_t)h * D * D);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(p.wsW0 + (size_t)h * D * D);
+        for (int i = threadIdx.x; i < D * D / 4; i += NT) dst[i] = src[i];
+    }
+
+    SbLoader<E, D, ST, PD, NT> ld;
+    ld.init(threadIdx.x, nullptr, p.k, p.v, p.eta, h, T, tend);
 
     // X starts at 0 and stays moderate, so one bf16 rounding per element is
     // enough for the residual product.
-    f32x4 X[CPW][ND];
-    F Xr[CPW][ND], Xs[SNAP ? CPW : 1][ND];
+    f32x4 Xp[ND], Xb[ND];
+    F Xpr[ND], Xbr[ND], Xps[SNAP ? ND : 1], Xbs[SNAP ? ND : 1];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
+    for (int r = 0; r < ND; ++r) {
+        Xp[r] = zero4();
+        Xb[r] = zero4();
+        Xpr[r] = to_frag<E>(zero4());
+        Xbr[r] = Xpr[r];
+    }
+
+    run_sb<E, D, ST, PD, NT, NBUF>(tiles, ld, sc, t0, tend, [&](SbTile<E, D, ST> &t, int n) {
+        f32x4 et[4];
+        load_eta(t, sc.len(n), g, et);
+        if (!MSE) {
+            // B += K^T diag(eta) V
+            F EV[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) EV[i] = to_frag<E>(frag_to_f32(v_tok(t, i, c, m, g)) * et[i]);
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; i += 2)
+                    Xb[r] = mma32(Xb[r], k_tok(t, i, r, m, g), k_tok(t, i + 1, r, m, g), EV[i], EV[i + 1]);
+            return;
+        }
+        if (SNAP && sc.chunk_start(n)) {
+#pragma unroll
+            for (int r = 0; r < ND; ++r) {
+                Xps[r] = Xpr[r];
+                Xbs[r] = Xbr[r];
+            }
+        }
+        f32x4 Kc[4], Vc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Kc[i] = frag_to_f32(k_tok(t, i, c, m, g));
+            Vc[i] = frag_to_f32(v_tok(t, i, c, m, g));
+        }
+        if constexpr (LT) {
+            pair_blocks<E, D, ST, ND, true, false>(t, gb, et, p.chunk, c, lane, m, g);
+            lds_barrier();
+            F Ln[6];
+#pragma unroll
+            for (int x = 0; x < 6; ++x) Ln[x] = gb[x][lane];
+            substitute<E>(Kc, Ln);
+            substitute<E>(Vc, Ln);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kts.put(c, i, Kc[i], m, g);
+            lds_barrier();
+        }
+        // U = [Kt | Vt] - Kt X_base, then X += K^T diag(eta) U
+        F EUp[4], EUb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            F Ka[ND];
+#pragma unroll
+            for (int r = 0; r < ND; ++r) {
+                if constexpr (LT)
+                    Ka[r] = kts.row(i, r, m, g);
+                else
+                    Ka[r] = k_row(t, i, r, m, g);
+            }
+            const f32x4 Up = Kc[i] - mma_b<F, ND>(zero4(), Ka, SNAP ? Xps : Xpr);
+            const f32x4 Ub = Vc[i] - mma_b<F, ND>(zero4(), Ka, SNAP ? Xbs : Xbr);
+            EUp[i] = to_frag<E>(Up * et[i]);
+            EUb[i] = to_frag<E>(Ub * et[i]);
+        }
 #pragma unroll
         for (int r = 0; r < ND; ++r) {
-            X[c][r] = zero4();
-            Xr[c][r] = to_frag<E>(zero4());
-            if (SNAP) Xs[c][r] = Xr[c][r];
+            const F k0 = k_tok(t, 0, r, m, g), k1 = k_tok(t, 1, r, m, g);
+            const F k2 = k_tok(t, 2, r, m, g), k3 = k_tok(t, 3, r, m, g);
+            Xp[r] = mma32(Xp[r], k0, k1, EUp[0], EUp[1]);
+            Xp[r] = mma32(Xp[r], k2, k3, EUp[2], EUp[3]);
+            Xb[r] = mma32(Xb[r], k0, k1, EUb[0], EUb[1]);
+            Xb[r] = mma32(Xb[r], k2, k3, EUb[2], EUb[3]);
+            Xpr[r] = to_frag<E>(Xp[r]);
+            Xbr[r] = to_frag<E>(Xb[r]);
         }
-
-    run_subblocks<E, D, STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend,
-        [&](SubTile<E, D> &tl, int tg) {
-            if (SNAP && MSE && (tg % p.chunk) == 0) {
-#pragma unroll
-                for (int c = 0; c < CPW; ++c)
-#pragma unroll
-                    for (int r = 0; r < ND; ++r) Xs[c][r] = Xr[c][r];
-            }
-            F Ka[ND];
-            if (MSE) {
-#pragma unroll
-                for (int r = 0; r < ND; ++r) Ka[r] = lds_frag<E>(&tl.ks[m][16 * r + 4 * g]);
-            }
-            const f32x4 et = *reinterpret_cast<const f32x4 *>(&tl.eta[4 * g]);
-            F EU[CPW];
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-                const int x = wave * CPW + c;
-                const bool pcol = MSE && x < ND;
-                const int cb = pcol ? x : x - (MSE ? ND : 0);
-                f32x4 U = frag_to_f32(tok_frag<E, D>(tl, !pcol, cb, m, g));
-                if (MSE) U = U - mma_b<F, ND>(zero4(), Ka, SNAP ? Xs[c] : Xr[c]);
-                EU[c] = to_frag<E>(U * et);
-            }
-            F KtA[ND];
-#pragma unroll
-            for (int r = 0; r < ND; ++r) KtA[r] = tok_frag<E, D>(tl, false, r, m, g);
-#pragma unroll
-            for (int c = 0; c < CPW; ++c)
-#pragma unroll
-                for (int r = 0; r < ND; ++r) {
-                    X[c][r] = mma16(X[c][r], KtA[r], EU[c]);
-                    if (MSE) Xr[c][r] = to_frag<E>(X[c][r]);
-                }
-        });
+    });
 
     const size_t base = ((size_t)h * p.Ssum + seg) * D * D;
+    if (MSE) {
+        E *dst = (E *)p.wsP + base;
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        const int x = wave * CPW + c;
-        const bool pcol = MSE && x < ND;
-        const int cb = pcol ? x : x - (MSE ? ND : 0);
-        if (pcol) {
-            E *dst = (E *)p.wsP + base;
+        for (int r = 0; r < ND; ++r)
 #pragma unroll
-            for (int r = 0; r < ND; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = (E)X[c][r][j];
-        } else {
-            float *dst = p.wsB + base;
-#pragma unroll
-            for (int r = 0; r < ND; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = X[c][r][j];
-        }
+            for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = (E)Xp[r][j];
     }
+    float *dst = p.wsB + base;
+#pragma unroll
+    for (int r = 0; r < ND; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = Xb[r][j];
 }
 
 // ---------------------------------------------------------------------------
-// prefix: per (head, column block), one wave per 16-row tile of the state.
-// W_start(0) = w_init; W_start(s+1) = W_start(s) - P_s W_start(s) + B_s.
-// Writes every W_start(s) (slot s of wsW); with WRITE_FINAL also the state
-// after the last summarised segment into slot S and into w_final.
+// Segment-start chain.  R holds column block c of a state (accumulator
+// layout); apply the affine maps of segments 0..nsteps-1 of head h to it:
+// R <- R - P_s R + B_s.  P_s (D x D, element type) is staged through LDS by
+// the whole workgroup, two steps ahead in registers; each wave reads the P
+// rows it needs as A fragments and its column block of B_s into the
+// accumulator layout.  NPB = 2: double-buffered LDS (one barrier a step).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool MSE, bool WRITE_FINAL>
-__global__ __launch_bounds__((D / 16) * 64) void lin_prefix(LinParams p)
+template <typename E, int D> struct alignas(16) PStage {
+    E m[D][D + (sizeof(E) == 2 ? 8 : 4)];
+};
+
+template <typename E, int D, int NT> struct PLoader {
+    static constexpr int PE = 16 / (int)sizeof(E);
+    static constexpr int PPR = D / PE;
+    static constexpr int CPT = D * PPR / NT;
+    static_assert(CPT >= 1 && CPT * NT == D * PPR, "P loader shape");
+    int row[CPT], col[CPT];
+    u32x4 v[2][CPT];
+    const E *base;
+    __device__ void init(int tid, const E *b)
+    {
+        base = b;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int piece = tid + i * NT;
+            row[i] = piece / PPR;
+            col[i] = piece % PPR;
+        }
+    }
+    __device__ __forceinline__ void issue(int slot, int step)
+    {
+        const E *P = base + (size_t)step * D * D;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            v[slot][i] = *reinterpret_cast<const u32x4 *>(P + (size_t)row[i] * D + PE * col[i]);
+    }
+    __device__ __forceinline__ void commit(int slot, PStage<E, D> &st)
+    {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4 *>(&st.m[row[i]][PE * col[i]]) = v[slot][i];
+    }
+};
+
+template <typename E, int D, bool MSE, int NT, int NPB>
+__device__ __forceinline__ void chain_maps(f32x4 *R, const LinParams &p, int h, int nsteps,
+                                           PStage<E, D> *pst, int c, int m, int g)
 {
     typedef typename Frag<E>::type F;
     constexpr int ND = D / 16;
-    constexpr int PP = (D == 64) ? 8 : 4;  // steps of P/B prefetched ahead (memory latency)
-    __shared__ SplitFrag<E> xch[2][ND][64];
-    const int lane = threadIdx.x & 63, r = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
-    const int cb = blockIdx.x % ND, h = blockIdx.x / ND;
-    const float *w0 = p.w_init + (size_t)h * D * D;
-    float *wsW = p.wsW + (size_t)h * (p.S + 1) * D * D;
-
-    f32x4 W;
+    const size_t hb = (size_t)h * p.Ssum * D * D;
+    const float *Bh = p.wsB + hb;
+    f32x4 Bt[2][ND];
+    auto loadB = [&](int slot, int step) {
+        const float *Bs = Bh + (size_t)step * D * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) W[j] = w0[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
+        for (int r = 0; r < ND; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wsW[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
-
-    // Steps are padded up to a multiple of PP so the prefetch ring runs
-    // without branches: padded steps read the last valid step's data, add
-    // nothing (masked to zero at use) and rewrite the last slot unchanged.
-    const int nst = p.Ssum;
-    const int ngroups = (nst + PP - 1) / PP;
-    F PA[PP][ND];
-    f32x4 BB[PP];
-    auto issue = [&](int slot, int s) {
-        const size_t base = ((size_t)h * p.Ssum + min(s, nst - 1)) * D * D;
-        if (MSE) {
-            const E *P = (const E *)p.wsP + base;
-#pragma unroll
-            for (int q = 0; q < ND; ++q) PA[slot][q] = load4<E>(P + (size_t)(16 * r + m) * D + 16 * q + 4 * g);
-        }
-        const float *Bm = p.wsB + base;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) BB[slot][j] = Bm[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
+            for (int j = 0; j < 4; ++j) Bt[slot][r][j] = Bs[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
     };
-#pragma unroll
-    for (int s = 0; s < PP; ++s) issue(s, s);
-    for (int gi = 0; gi < ngroups; ++gi) {
-#pragma unroll
-        for (int jj = 0; jj < PP; ++jj) {
-            const int s = gi * PP + jj;
-            const bool live = s < nst;
-            f32x4 upd = BB[jj];
-            if (MSE) {
-                SplitFrag<E> mine;
-                mine.set(W);
-                xch[jj & 1][r][lane] = mine;
-                lds_barrier();
-                SplitFrag<E> Wb[ND];
-#pragma unroll
-                for (int q = 0; q < ND; ++q) Wb[q] = xch[jj & 1][q][lane];
-                upd = upd - mma_state_b<E, ND>(zero4(), PA[jj], Wb);
-            }
-            W = W + (live ? upd : zero4());
-            issue(jj, s + PP);
-            float *dst = wsW + (size_t)min(s + 1, nst) * D * D;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
-        }
+    const int last = nsteps - 1;
+    PLoader<E, D, NT> pl;
+    if (MSE) {
+        pl.init(threadIdx.x, (const E *)p.wsP + hb);
+        pl.issue(0, 0);
+        pl.issue(1, min(1, last));
     }
-    if (WRITE_FINAL) {
-        float *wf = p.w_final + (size_t)h * D * D;
+    loadB(0, 0);
+    loadB(1, min(1, last));
+    if (MSE) {
+        pl.commit(0, pst[0]);
+        pl.issue(0, min(2, last));
+        lds_barrier();
+    }
+    // Steps run in pairs so ring slots are compile-time; a padded last step
+    // changes nothing.  Step s: register slot s%2 holds B_s and, after the
+    // commit of step s-1, the P of step s+2; LDS buffer s%NPB holds P_s.
+    const int npairs = (nsteps + 1) / 2;
+    for (int pi = 0; pi < npairs; ++pi) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m] = W[j];
+        for (int j = 0; j < 2; ++j) {
+            const int s = 2 * pi + j;
+            if (s < nsteps) {
+                if (MSE) {
+                    SplitFrag<E> Ws[ND];
+#pragma unroll
+                    for (int r = 0; r < ND; ++r) Ws[r].set(R[r]);
+                    const PStage<E, D> &P = pst[NPB == 2 ? j : 0];
+#pragma unroll
+                    for (int r = 0; r < ND; ++r) {
+                        F PA[ND];
+#pragma unroll
+                        for (int q = 0; q < ND; ++q) PA[q] = load4<E>(&P.m[16 * r + m][16 * q + 4 * g]);
+                        R[r] = R[r] + Bt[j][r] - mma_state_b<E, ND>(zero4(), PA, Ws);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < ND; ++r) R[r] = R[r] + Bt[j][r];
+                }
+            }
+            loadB(j, min(s + 2, last));
+            if (MSE) {
+                if (NPB == 1) lds_barrier();
+                pl.commit(1 - j, pst[NPB == 2 ? 1 - j : 0]);
+                pl.issue(1 - j, min(s + 3, last));
+                lds_barrier();
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// replay (causal): outputs of one segment from its start state.  Each wave
-// owns CPW column blocks; the query/key fragments and the masked Q K^T block
-// are shared by them.  SNAP: chunks longer than one sub-block need a separate
-// chunk-start snapshot of the state for the residual.
+// final state (non-causal): W_final = the maps of all segments applied to
+// w_init, one workgroup per head (wave c owns column block c).  Reads all of
+// w_init before writing w_final (they may alias).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool MSE, int CPW, bool SNAP, int PD>
-__global__ __launch_bounds__((D / 16) / CPW * 64) void lin_replay(LinParams p)
+template <typename E, int D, bool MSE>
+__global__ __launch_bounds__((D / 16) * 64) void lin_final(LinParams p)
+{
+    constexpr int ND = D / 16;
+    constexpr int NT = ND * 64;
+    constexpr int NPB = (sizeof(E) == 4 && D == 128) ? 1 : 2;
+    __shared__ PStage<E, D> pst[MSE ? NPB : 1];
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int h = blockIdx.x;
+    (void)lane;
+    const float *w0 = p.w_init + (size_t)h * D * D;
+    f32x4 R[ND];
+#pragma unroll
+    for (int r = 0; r < ND; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[r][j] = w0[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
+    chain_maps<E, D, MSE, NT, NPB>(R, p, h, p.Ssum, pst, c, m, g);
+    float *wf = p.w_final + (size_t)h * D * D;
+#pragma unroll
+    for (int r = 0; r < ND; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = R[r][j];
+}
+
+// ---------------------------------------------------------------------------
+// replay (causal): outputs of one segment.  The workgroup first builds its
+// start state from w_init and the summaries of the segments before it, then
+// walks its super-blocks.  Wave c owns column block c of the running state R
+// (fp32 accumulators, re-split into hi/lo operands after every update) and of
+// the outputs.
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool MSE, bool LT, bool SNAP, int PD>
+__global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
 {
     typedef typename Frag<E>::type F;
     constexpr int ND = D / 16;
-    constexpr int NW = ND / CPW;
-    constexpr int NT = NW * 64;
-    __shared__ SubTile<E, D> tiles[2];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+    constexpr int NT = ND * 64;
+    constexpr int NBUF = sizeof(E) == 2 ? 2 : 1;
+    constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E;
+    constexpr int NPB = (sizeof(E) == 4 && D == 128) ? 1 : 2;
+    // The super-block tiles and the staged P of the segment-start chain are
+    // never live at the same time.
+    __shared__ union {
+        SbTile<E, D, ST> tiles[NBUF];
+        PStage<E, D> pst[MSE ? NPB : 1];
+    } lds;
+    SbTile<E, D, ST> *tiles = lds.tiles;
+    __shared__ KtTile<E, LT ? D : 16> kts;
+    __shared__ F gb[16][64];
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // column block
     const int seg = blockIdx.x % p.S, h = blockIdx.x / p.S;
     const int T = p.Tkv;
     const int t0 = seg * p.seg_tokens;
     const int tend = min(T, t0 + p.seg_tokens);
+    const SbSched sc(p.chunk);
 
-    const float *ws = (p.S > 1) ? p.wsW + ((size_t)h * (p.S + 1) + seg) * D * D
-                                : p.w_init + (size_t)h * D * D;
-    // State = W0 + dW: the start state enters products as a split (hi/lo)
-    // pair computed once; the change dW since the segment start stays small,
-    // so one bf16 rounding of it per sub-block is enough.
-    SplitFrag<E> W0[CPW][ND];
-    f32x4 dW[CPW][ND];
-    F dWr[CPW][ND], dWs[SNAP ? CPW : 1][ND];
+    // w_init itself when this head has one segment; otherwise the summary's
+    // copy (w_final may alias w_init, and the last segment writes it).
+    const float *ws = ((p.S > 1) ? p.wsW0 : p.w_init) + (size_t)h * D * D;
+    f32x4 R[ND];
+    SplitFrag<E> Rs[ND], Ss[SNAP ? ND : 1];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        const int cb = wave * CPW + c;
+    for (int r = 0; r < ND; ++r)
 #pragma unroll
-        for (int r = 0; r < ND; ++r) {
-            f32x4 w;
+        for (int j = 0; j < 4; ++j) R[r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
+    if (seg > 0) chain_maps<E, D, MSE, NT, NPB>(R, p, h, seg, lds.pst, c, m, g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * cb + m];
-            W0[c][r].set(w);
-            dW[c][r] = zero4();
-            dWr[c][r] = to_frag<E>(zero4());
-            if (SNAP) dWs[c][r] = dWr[c][r];
-        }
-    }
+    for (int r = 0; r < ND; ++r) Rs[r].set(R[r]);
 
-    Loader<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT> ld;
-    ld.init(threadIdx.x, p, h, T, tend);
+    SbLoader<E, D, ST, PD, NT> ld;
+    ld.init(threadIdx.x, p.q, p.k, p.v, p.eta, h, T, tend);
     E *out_h = (E *)p.out + (size_t)h * T * D;
 
-    run_subblocks<E, D, STAGE_Q | STAGE_K | STAGE_V | STAGE_E, PD, NT>(tiles, ld, t0, tend,
-        [&](SubTile<E, D> &tl, int tg) {
-            if (SNAP && MSE && (tg % p.chunk) == 0) {
+    run_sb<E, D, ST, PD, NT, NBUF>(tiles, ld, sc, t0, tend, [&](SbTile<E, D, ST> &t, int n) {
+        const int s = t0 + sc.start(n), len = sc.len(n);
+        const int lim = min(tend, s + len);
+        f32x4 et[4];
+        load_eta(t, len, g, et);
+        if (SNAP && sc.chunk_start(n)) {
 #pragma unroll
-                for (int c = 0; c < CPW; ++c)
+            for (int r = 0; r < ND; ++r) Ss[r] = Rs[r];
+        }
+        pair_blocks<E, D, ST, ND, LT, true>(t, gb, et, p.chunk, c, lane, m, g);
+        lds_barrier();
+        // residuals U of the four tiles (column block c)
+        f32x4 U[4];
 #pragma unroll
-                    for (int r = 0; r < ND; ++r) dWs[c][r] = dWr[c][r];
+        for (int i = 0; i < 4; ++i) U[i] = frag_to_f32(v_tok(t, i, c, m, g));
+        if (MSE) {
+            if constexpr (LT) {
+                F Ln[6];
+#pragma unroll
+                for (int x = 0; x < 6; ++x) Ln[x] = gb[x][lane];
+                f32x4 Kc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Kc[i] = frag_to_f32(k_tok(t, i, c, m, g));
+                substitute<E>(Kc, Ln);
+                substitute<E>(U, Ln);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kts.put(c, i, Kc[i], m, g);
+                lds_barrier();
             }
-            F Qa[ND], Ka[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) {
-                Qa[r] = lds_frag<E>(&tl.qs[m][16 * r + 4 * g]);
-                Ka[r] = lds_frag<E>(&tl.ks[m][16 * r + 4 * g]);
-            }
-            const f32x4 et = *reinterpret_cast<const f32x4 *>(&tl.eta[4 * g]);
-            // S^T[i][t] = k_i . q_t, kept for i <= t, times eta_i.
-            f32x4 St = mma_b<F, ND>(zero4(), Ka, Qa);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) St[j] = (4 * g + j <= m) ? St[j] * et[j] : 0.f;
-            const F Sf = to_frag<E>(St);
-            const int t = tg + m;
-            F EU[CPW];
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-                const int cb = wave * CPW + c;
-                f32x4 U = frag_to_f32(tok_frag<E, D>(tl, true, cb, m, g));
-                if (MSE) {
-                    f32x4 P = zero4();
-#pragma unroll
-                    for (int r = 0; r < ND; r += 2) P = mma32(P, Ka[r], Ka[r + 1], W0[c][r].hi, W0[c][r + 1].hi);
-                    P = mma_b<F, ND>(P, Ka, SNAP ? dWs[c] : dWr[c]);
-                    U = U - P;
-                }
-                // O^T = W^T Q^T + U^T S^T with W = W0 + dW (running).  The two
-                // terms use separate accumulators: no accumulation chain mixes
-                // MFMA shapes (16x16x32 feeding 16x16x16).
-                const f32x4 Oi = mma16(zero4(), to_frag<E>(U), Sf);
-                f32x4 O = mma_state_a<E, ND>(zero4(), W0[c], Qa);
-#pragma unroll
-                for (int r = 0; r < ND; r += 2) O = mma32(O, dWr[c][r], dWr[c][r + 1], Qa[r], Qa[r + 1]);
-                O = O + Oi;
-                if (t < tend) store4<E>(out_h + (size_t)t * D + 16 * cb + 4 * g, out4<E>(O));
-                EU[c] = to_frag<E>(U * et);
-            }
-            // dW += K^T (eta * U)
-            F KtA[ND];
-#pragma unroll
-            for (int r = 0; r < ND; ++r) KtA[r] = tok_frag<E, D>(tl, false, r, m, g);
-#pragma unroll
-            for (int c = 0; c < CPW; ++c)
+            for (int i = 0; i < 4; ++i) {
+                F Ka[ND];
 #pragma unroll
                 for (int r = 0; r < ND; ++r) {
-                    dW[c][r] = mma16(dW[c][r], KtA[r], EU[c]);
-                    dWr[c][r] = to_frag<E>(dW[c][r]);
+                    if constexpr (LT)
+                        Ka[r] = kts.row(i, r, m, g);
+                    else
+                        Ka[r] = k_row(t, i, r, m, g);
                 }
-        });
+                U[i] = U[i] - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Ss : Rs);
+            }
+        }
+        F Uf[4], EU[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Uf[i] = to_frag<E>(U[i]);
+            EU[i] = to_frag<E>(U[i] * et[i]);
+        }
+        // O^T_i = R^T Q_i^T + sum_{j<=i} U_j^T A_ij^T (transposed so each lane
+        // stores four consecutive columns of one token); key tiles are paired
+        // into 32-deep products.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (16 * i >= len) break;
+            F Qa[ND];
+#pragma unroll
+            for (int r = 0; r < ND; ++r) Qa[r] = q_row(t, i, r, m, g);
+            f32x4 O = mma_state_a<E, ND>(zero4(), Rs, Qa);
+#pragma unroll
+            for (int j = 0; j <= i; j += 2) {
+                if (j + 1 <= i)
+                    O = mma32(O, Uf[j], Uf[j + 1], gb[ablk(i, j)][lane], gb[ablk(i, j + 1)][lane]);
+                else
+                    O = mma32z(O, Uf[j], gb[ablk(i, j)][lane]);
+            }
+            const int tk = s + 16 * i + m;
+            if (tk < lim) store4<E>(out_h + (size_t)tk * D + 16 * c + 4 * g, out4<E>(O));
+        }
+        // R += K^T diag(eta) U
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            R[r] = mma32(R[r], k_tok(t, 0, r, m, g), k_tok(t, 1, r, m, g), EU[0], EU[1]);
+            R[r] = mma32(R[r], k_tok(t, 2, r, m, g), k_tok(t, 3, r, m, g), EU[2], EU[3]);
+            Rs[r].set(R[r]);
+        }
+    });
 
     if (seg == p.S - 1) {
-        // final state = start state + change; all reads before any write (w_final
-        // may alias w_init when there is a single segment)
         float *wf = p.w_final + (size_t)h * D * D;
-        f32x4 w0f[CPW][ND];
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+        for (int r = 0; r < ND; ++r)
 #pragma unroll
-            for (int r = 0; r < ND; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    w0f[c][r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * (wave * CPW + c) + m];
-#pragma unroll
-        for (int c = 0; c < CPW; ++c)
-#pragma unroll
-            for (int r = 0; r < ND; ++r)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    wf[(size_t)(16 * r + 4 * g + j) * D + 16 * (wave * CPW + c) + m] = w0f[c][r][j] + dW[c][r][j];
+            for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = R[r][j];
     }
 }
 
 // ---------------------------------------------------------------------------
 // apply (non-causal): O = Q W_final over query segments.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int CPW, int PD>
-__global__ __launch_bounds__((D / 16) / CPW * 64) void lin_apply(LinParams p, const float *wsrc,
-                                                                 size_t wsrc_head_stride)
+template <typename E, int D, int PD>
+__global__ __launch_bounds__((D / 16) * 64) void lin_apply(LinParams p, const float *wsrc,
+                                                           size_t wsrc_head_stride)
 {
     typedef typename Frag<E>::type F;
     constexpr int ND = D / 16;
-    constexpr int NT = ND / CPW * 64;
-    __shared__ SubTile<E, D> tiles[2];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, m = lane & 15;
+    constexpr int NT = ND * 64;
+    constexpr int ST = STAGE_Q;
+    __shared__ SbTile<E, D, ST> tiles[2];
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // column block
+    (void)lane;
     const int seg = blockIdx.x % p.Sq, h = blockIdx.x / p.Sq;
     const int T = p.Tq;
     const int t0 = seg * p.seg_q;
     const int tend = min(T, t0 + p.seg_q);
     const float *ws = wsrc + (size_t)h * wsrc_head_stride;
-    SplitFrag<E> Wr[CPW][ND];
+    SplitFrag<E> Wr[ND];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
+    for (int r = 0; r < ND; ++r) {
+        f32x4 w;
 #pragma unroll
-        for (int r = 0; r < ND; ++r) {
-            f32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * (wave * CPW + c) + m];
-            Wr[c][r].set(w);
-        }
-    Loader<E, D, STAGE_Q, PD, NT> ld;
-    ld.init(threadIdx.x, p, h, T, tend);
+        for (int j = 0; j < 4; ++j) w[j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
+        Wr[r].set(w);
+    }
+    SbLoader<E, D, ST, PD, NT> ld;
+    ld.init(threadIdx.x, p.q, nullptr, nullptr, nullptr, h, T, tend);
     E *out_h = (E *)p.out + (size_t)h * T * D;
-    run_subblocks<E, D, STAGE_Q, PD, NT>(tiles, ld, t0, tend,
-        [&](SubTile<E, D> &tl, int tg) {
+    const SbSched sc(SB);
+    run_sb<E, D, ST, PD, NT, 2>(tiles, ld, sc, t0, tend, [&](SbTile<E, D, ST> &t, int n) {
+        const int s = t0 + sc.start(n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             F Qa[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) Qa[r] = lds_frag<E>(&tl.qs[m][16 * r + 4 * g]);
-            const int t = tg + m;
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-                const f32x4 O = mma_state_a<E, ND>(zero4(), Wr[c], Qa);
-                if (t < tend) store4<E>(out_h + (size_t)t * D + 16 * (wave * CPW + c) + 4 * g, out4<E>(O));
-            }
-        });
+            for (int r = 0; r < ND; ++r) Qa[r] = q_row(t, i, r, m, g);
+            const f32x4 O = mma_state_a<E, ND>(zero4(), Wr, Qa);
+            const int tk = s + 16 * i + m;
+            if (tk < tend) store4<E>(out_h + (size_t)tk * D + 16 * c + 4 * g, out4<E>(O));
+        }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -629,21 +925,22 @@ LinearPlan linear_plan(const LinearShape &s)
 {
     LinearPlan pl{};
     const int T = s.Tkv;
-    // Segment length: whole chunks, enough segments to give every CU a few
-    // workgroups, at least 64 tokens.
+    // Segment length: whole super-block periods (whole chunks), enough
+    // segments to give every CU a workgroup or two, at least 64 tokens.
+    const long long period = (s.chunk <= SB) ? (long long)(SB / s.chunk) * s.chunk : s.chunk;
     const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 512);
-    long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : s.chunk;
-    if (seg < 64) seg = 64;
+    long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : period;
+    if (seg < SB) seg = SB;
     const int forced = env_int("TTT_LINEAR_SEG_TOKENS", 0);
     if (forced > 0) seg = forced;
-    seg = (seg + s.chunk - 1) / s.chunk * s.chunk;
-    if (T > 0 && seg > T) seg = (T + s.chunk - 1) / s.chunk * s.chunk;
+    seg = (seg + period - 1) / period * period;
+    if (T > 0 && seg > T) seg = (T + period - 1) / period * period;
     pl.seg_tokens = (int)seg;
     pl.S = (T > 0) ? (int)((T + seg - 1) / seg) : 0;
     pl.Ssum = (s.order == 0) ? (pl.S > 0 ? pl.S - 1 : 0) : pl.S;
-    long long segq = (s.Tq > 0) ? ((long long)s.NH * s.Tq + target_wg - 1) / target_wg : 16;
-    if (segq < 64) segq = 64;
-    segq = (segq + 15) / 16 * 16;
+    long long segq = (s.Tq > 0) ? ((long long)s.NH * s.Tq + target_wg - 1) / target_wg : SB;
+    if (segq < SB) segq = SB;
+    segq = (segq + SB - 1) / SB * SB;
     pl.seg_q = (int)segq;
     pl.Sq = (s.Tq > 0) ? (int)((s.Tq + segq - 1) / segq) : 0;
     const size_t esz = s.bf16 ? 2 : 4;
@@ -653,34 +950,27 @@ LinearPlan linear_plan(const LinearShape &s)
     if (s.loss == 1) off = align_up(off + (size_t)s.NH * pl.Ssum * dd * esz, 256);
     pl.offB = off;
     off = align_up(off + (size_t)s.NH * pl.Ssum * dd * 4, 256);
-    pl.offW = off;
-    off = align_up(off + (size_t)s.NH * (pl.S + 1) * dd * 4, 256);
+    pl.offW = off;  // copy of w_init (causal, more than one segment)
+    if (s.order == 0 && pl.S > 1) off = align_up(off + (size_t)s.NH * dd * 4, 256);
     pl.bytes = off;
     return pl;
 }
 
-template <typename E, int D, bool MSE, bool SNAP>
+template <typename E, int D, bool MSE, bool LT, bool SNAP>
 static hipError_t launch_typed(const LinearShape &s, const LinearPlan &pl, LinParams p,
                                hipStream_t st)
 {
     constexpr int ND = D / 16;
-    constexpr int PD = (D == 64) ? 8 : 4;  // sub-blocks in flight; even (LDS buffer = slot parity)
-    constexpr int CPW_R = (D == 128) ? 2 : 1;             // replay / apply
-    constexpr int CPW_S = (MSE || D == 128) ? 2 : 1;      // summary
-    constexpr int NW_S = (MSE ? 2 : 1) * ND / CPW_S;
+    constexpr int PD = 2;  // super-blocks in flight
+    const dim3 block(ND * 64);
     if (s.Tkv > 0) {
-        if (pl.Ssum > 0) {
-            lin_summary<E, D, MSE, CPW_S, SNAP, PD><<<dim3(s.NH * pl.Ssum), dim3(NW_S * 64), 0, st>>>(p);
-            if (s.order == 0)
-                lin_prefix<E, D, MSE, false><<<dim3(s.NH * ND), dim3(ND * 64), 0, st>>>(p);
-            else
-                lin_prefix<E, D, MSE, true><<<dim3(s.NH * ND), dim3(ND * 64), 0, st>>>(p);
-        }
+        if (pl.Ssum > 0) lin_summary<E, D, MSE, LT, SNAP, PD><<<dim3(s.NH * pl.Ssum), block, 0, st>>>(p);
         if (s.order == 0) {
-            lin_replay<E, D, MSE, CPW_R, SNAP, PD><<<dim3(s.NH * pl.S), dim3(ND / CPW_R * 64), 0, st>>>(p);
-        } else if (pl.Sq > 0) {
-            lin_apply<E, D, CPW_R, PD><<<dim3(s.NH * pl.Sq), dim3(ND / CPW_R * 64), 0, st>>>(
-                p, p.wsW + (size_t)pl.S * D * D, (size_t)(pl.S + 1) * D * D);
+            lin_replay<E, D, MSE, LT, SNAP, PD><<<dim3(s.NH * pl.S), block, 0, st>>>(p);
+        } else {
+            lin_final<E, D, MSE><<<dim3(s.NH), block, 0, st>>>(p);
+            if (pl.Sq > 0)
+                lin_apply<E, D, PD><<<dim3(s.NH * pl.Sq), block, 0, st>>>(p, p.w_final, (size_t)D * D);
         }
     } else {
         // No key/value tokens: the state is unchanged.
@@ -690,8 +980,7 @@ static hipError_t launch_typed(const LinearShape &s, const LinearPlan &pl, LinPa
             if (e != hipSuccess) return e;
         }
         if (s.order == 1 && pl.Sq > 0)
-            lin_apply<E, D, CPW_R, PD><<<dim3(s.NH * pl.Sq), dim3(ND / CPW_R * 64), 0, st>>>(
-                p, p.w_init, (size_t)D * D);
+            lin_apply<E, D, PD><<<dim3(s.NH * pl.Sq), block, 0, st>>>(p, p.w_init, (size_t)D * D);
     }
     return hipGetLastError();
 }
@@ -710,7 +999,7 @@ hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void 
     p.w_final = w_final;
     p.wsP = (char *)ws + pl.offP;
     p.wsB = (float *)((char *)ws + pl.offB);
-    p.wsW = (float *)((char *)ws + pl.offW);
+    p.wsW0 = (s.order == 0 && pl.S > 1) ? (float *)((char *)ws + pl.offW) : nullptr;
     p.NH = s.NH;
     p.Tq = s.Tq;
     p.Tkv = s.Tkv;
@@ -721,11 +1010,15 @@ hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void 
     p.seg_q = pl.seg_q;
     p.Sq = pl.Sq;
     const bool mse = s.loss == 1;
-    const bool snap = s.chunk > 16;
-#define TTT_DISPATCH(E, D)                                                            \
-    if (mse) return snap ? launch_typed<E, D, true, true>(s, pl, p, stream)           \
-                         : launch_typed<E, D, true, false>(s, pl, p, stream);         \
-    return launch_typed<E, D, false, false>(s, pl, p, stream);
+    // b < 64: transform by T; b > 64: chunk-start snapshots; b = 64: neither.
+    const bool lt = s.chunk < SB, snap = s.chunk > SB;
+#define TTT_DISPATCH(E, D)                                                                  \
+    if (mse) {                                                                              \
+        if (lt) return launch_typed<E, D, true, true, false>(s, pl, p, stream);             \
+        if (snap) return launch_typed<E, D, true, false, true>(s, pl, p, stream);           \
+        return launch_typed<E, D, true, false, false>(s, pl, p, stream);                    \
+    }                                                                                       \
+    return launch_typed<E, D, false, false, false>(s, pl, p, stream);
     if (s.bf16) {
         if (s.d == 64) { TTT_DISPATCH(__bf16, 64) }
         if (s.d == 128) { TTT_DISPATCH(__bf16, 128) }

@@ -52,7 +52,9 @@ def lin(lib, **kw):
     (dict(Tq=32), _lib.TTT_EINVAL), (dict(Tkv=-1, Tq=-1), _lib.TTT_EINVAL),
     (dict(d=32), _lib.TTT_EUNSUPPORTED), (dict(d=96), _lib.TTT_EUNSUPPORTED),
     (dict(chunk=8), _lib.TTT_EUNSUPPORTED), (dict(chunk=24), _lib.TTT_EUNSUPPORTED),
-    (dict(wsb=16), _lib.TTT_EWORKSPACE), (dict(ws=None), _lib.TTT_EINVAL),
+    # several segments, so a workspace is needed (one causal segment needs none)
+    (dict(wsb=16, Tq=4096, Tkv=4096), _lib.TTT_EWORKSPACE),
+    (dict(ws=None, Tq=4096, Tkv=4096), _lib.TTT_EINVAL),
 ])
 def test_linear_validation(kw, code):
     assert lin(_lib.load(), **kw) == code

@@ -133,9 +133,12 @@ def test_in_place_state_and_resume():
     o2, _ = cla.ttt_linear_fwd(s2(g["q"]), s2(g["k"]), s2(g["v"]), s2(g["eta"]), w, chunk=b, loss=1,
                                w_final=w)
     torch.cuda.synchronize()
-    o = torch.cat([o1, o2], dim=2)
-    assert (o.float() - full_o.float()).abs().max().item() <= 2e-2 * full_o.float().pow(2).mean().sqrt().item()
-    assert (w - full_w).abs().max().item() <= 2e-2 * full_w.pow(2).mean().sqrt().item()
+    # Both runs are held to the oracle's one-call result at the parity bar (two
+    # bf16-rounded GPU results may each sit up to the bar from it, on either side).
+    ro, rw = oracle.ttt_linear(inp["q"], inp["k"], inp["v"], inp["eta"], inp["w0"], chunk=b, loss=1)
+    for o, wf in ((full_o, full_w), (torch.cat([o1, o2], dim=2), w)):
+        assert_close(to_np(o), ro, "bf16", "out")
+        assert_close(to_np(wf), rw, "bf16", "w_final")
 
 
 def test_repeat_runs_are_bitwise_identical():
