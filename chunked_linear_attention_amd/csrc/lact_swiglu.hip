@@ -57,23 +57,34 @@ __device__ __forceinline__ f32x4 mfma32(f32x4 acc, bf16x8 a, bf16x8 b)
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
 
+// Workgroups are dealt to the 8 XCDs round-robin (XCD = block index mod 8),
+// and each XCD has its own L2.  Renumber blocks so that logical blocks
+// [x * n/8, (x + 1) * n/8) all run on XCD x: kernels order their logical
+// index so that tiles sharing an operand are consecutive, and the operand is
+// then fetched into one L2 instead of eight.
+__device__ __forceinline__ int xcd_block(int b, int n)
+{
+    return (n % 8) ? b : (b % 8) * (n / 8) + b / 8;
+}
+
 // ---------------------------------------------------------------------------
 // Generic NT GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16, k contiguous),
-// block tile 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 32, K a multiple
-// of 32.  Rows of A past M and rows of B past N read as zero.  The epilogue
-// gets the wave's 4 x 4 accumulator tiles: tile (i, q) holds C at rows
-// mbase + 16 i + 4 g + (0..3), column nbase + 16 q + (lane & 15).
+// block tile 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 64 (a full
+// 128-byte row of each operand per stage), K a multiple of 64.  Rows of A
+// past M and rows of B past N read as zero.  The epilogue gets the wave's
+// 4 x 4 accumulator tiles: tile (i, q) holds C at rows mbase + 16 i + 4 g +
+// (0..3), column nbase + 16 q + (lane & 15).
 // ---------------------------------------------------------------------------
-constexpr int GBK = 32;
-constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): conflict-free 16-byte fragment reads
-constexpr int GPD = 4;           // register stages in flight (even: LDS buffer = stage parity)
+constexpr int GBK = 64;
+constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): 16-byte fragment reads hit distinct banks per 8 lanes
+constexpr int GPD = 2;           // register stages in flight (even: LDS buffer = stage parity)
 
 struct GemmLds {
     bf16 a[2][128][GPITCH];
     bf16 b[2][128][GPITCH];
 };
 
-// K is cut into nseg segments of kseg (a multiple of 32); segment s reads A
+// K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
 // from As[s] and B from Bs[s] (same leading dimensions).  This sums products
 // of split operands (hi and lo bf16 parts) in one accumulation.
 template <typename Epi>
@@ -85,31 +96,31 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
-    int lrow[2], lcol[2];
+    // 4 pieces of 16 bytes per thread and operand: rows tid/8 + 32 i, 8 columns each
+    int lrow[4], lcol;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pc = tid + 256 * i;
-        lrow[i] = pc >> 2;
-        lcol[i] = (pc & 3) * 8;
-    }
+    for (int i = 0; i < 4; ++i) lrow[i] = (tid >> 3) + 32 * i;
+    lcol = (tid & 7) * 8;
+    const bool aok[4] = {m0 + lrow[0] < M, m0 + lrow[1] < M, m0 + lrow[2] < M, m0 + lrow[3] < M};
+    const bool bok[4] = {n0 + lrow[0] < N, n0 + lrow[1] < N, n0 + lrow[2] < N, n0 + lrow[3] < N};
     const int nst = K / GBK;
     const int ngroups = (nst + GPD - 1) / GPD;
-    B8 ra[GPD][2], rb[GPD][2];
+    B8 ra[GPD][4], rb[GPD][4];
     auto issue = [&](int s, int st) {
         const int kk = min(st, nst - 1) * GBK;
         const int sg = kk / kseg, kin = kk - sg * kseg;
         const bf16 *A = As[sg], *B = Bs[sg];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol[i]);
-            rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol[i]);
+        for (int i = 0; i < 4; ++i) {
+            ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
+            rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
         }
     };
     auto commit = [&](int s, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            st16(&L.a[buf][lrow[i]][lcol[i]], (m0 + lrow[i] < M) ? ra[s][i] : zero16());
-            st16(&L.b[buf][lrow[i]][lcol[i]], (n0 + lrow[i] < N) ? rb[s][i] : zero16());
+        for (int i = 0; i < 4; ++i) {
+            st16(&L.a[buf][lrow[i]][lcol], aok[i] ? ra[s][i] : zero16());
+            st16(&L.b[buf][lrow[i]][lcol], bok[i] ? rb[s][i] : zero16());
         }
     };
     f32x4 acc[4][4];
@@ -119,7 +130,10 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
         for (int q = 0; q < 4; ++q) acc[i][q] = zero4();
 
 #pragma unroll
-    for (int s = 0; s < GPD; ++s) issue(s, s);
+    for (int s = 0; s < GPD; ++s) {
+        issue(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     commit(0, 0);
     lds_barrier();
     for (int gi = 0; gi < ngroups; ++gi) {
@@ -129,17 +143,20 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
             issue(j, st + GPD);
             commit((j + 1) % GPD, (j + 1) & 1);
             const int buf = j & 1;
-            bf16x8 af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = as_bf8(ld16(&L.a[buf][wm * 64 + 16 * i + mm][8 * g]));
-                bfr[i] = as_bf8(ld16(&L.b[buf][wn * 64 + 16 * i + mm][8 * g]));
-            }
             if (st < nst) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int kh = 0; kh < 2; ++kh) {
+                    bf16x8 af[4], bfr[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
+                    for (int i = 0; i < 4; ++i) {
+                        af[i] = as_bf8(ld16(&L.a[buf][wm * 64 + 16 * i + mm][32 * kh + 8 * g]));
+                        bfr[i] = as_bf8(ld16(&L.b[buf][wn * 64 + 16 * i + mm][32 * kh + 8 * g]));
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
+                }
             }
             lds_barrier();
         }
@@ -269,12 +286,14 @@ __global__ __launch_bounds__(256) void lact_prep_weights(LactParams p)
 // ---------------------------------------------------------------------------
 // fwdgrad: per (head, 128-token tile, 64-wide hidden slice) of chunk c.
 // ---------------------------------------------------------------------------
+constexpr int FBK = 32, FPITCH = FBK + 8, FPD = 4;  // k step, LDS pitch, register stages
+
 struct FwdGradLds {
-    bf16 ak[2][128][GPITCH];   // K tile
-    bf16 ay[2][128][GPITCH];   // dY tile
-    bf16 b1[2][64][GPITCH];    // W1 rows of the slice
-    bf16 b3[2][64][GPITCH];    // W3 rows of the slice
-    bf16 b2[2][64][GPITCH];    // W2 columns of the slice (transposed on the way in)
+    bf16 ak[2][128][FPITCH];   // K tile
+    bf16 ay[2][128][FPITCH];   // dY tile
+    bf16 b1[2][64][FPITCH];    // W1 rows of the slice
+    bf16 b3[2][64][FPITCH];    // W3 rows of the slice
+    bf16 b2[2][64][FPITCH];    // W2 columns of the slice (transposed on the way in)
 };
 
 __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slot)
@@ -284,7 +303,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     const int g = lane >> 4, mm = lane & 15;
     const int nslice = p.hid / 64;
     const int ntile = p.cpad / 128;
-    int bid = blockIdx.x;
+    int bid = xcd_block(blockIdx.x, gridDim.x);
     const int sl = bid % nslice;
     bid /= nslice;
     const int tt = bid % ntile;
@@ -317,11 +336,11 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
         const int t = r0 + arow[i];
         erow[i] = (t < clen) ? (dot ? -eh[t] : 1.f) : 0.f;
     }
-    const int nst = d / GBK;
-    const int ngroups = (nst + GPD - 1) / GPD;
-    B8 rk[GPD][2], ry[GPD][2], r1[GPD], r3[GPD], r2[GPD];
+    const int nst = d / FBK;
+    const int ngroups = (nst + FPD - 1) / FPD;
+    B8 rk[FPD][2], ry[FPD][2], r1[FPD], r3[FPD], r2[FPD];
     auto issue = [&](int s, int st) {
-        const int kk = min(st, nst - 1) * GBK;
+        const int kk = min(st, nst - 1) * FBK;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int t = min(r0 + arow[i], clen - 1);
@@ -357,15 +376,15 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
         for (int q = 0; q < 4; ++q) a1[i][q] = a3[i][q] = a2[i][q] = zero4();
 
 #pragma unroll
-    for (int s = 0; s < GPD; ++s) issue(s, s);
+    for (int s = 0; s < FPD; ++s) issue(s, s);
     commit(0, 0);
     lds_barrier();
     for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
-        for (int j = 0; j < GPD; ++j) {
-            const int st = gi * GPD + j;
-            issue(j, st + GPD);
-            commit((j + 1) % GPD, (j + 1) & 1);
+        for (int j = 0; j < FPD; ++j) {
+            const int st = gi * FPD + j;
+            issue(j, st + FPD);
+            commit((j + 1) % FPD, (j + 1) & 1);
             const int buf = j & 1;
             bf16x8 fk[2], fy[2], f1[4], f3[4], f2[4];
 #pragma unroll
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
 //   which 1: dW3 likewise with dH3^T
 //   which 2: dW2[o][h] = sum_t dY^T[o][t] G^T[h][t]     as GEMM (M = h, N = o)
 // A lane's four consecutive M indices are the contiguous dimension of the
-// stored gradient.  Token ranges are whole 32-token steps: past the chunk end
+// stored gradient.  Token ranges are whole 64-token steps: past the chunk end
 // dH^T, G^T are zero (and dY^T too), so no guard is needed on k.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
@@ -432,17 +451,17 @@ __global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
     __shared__ GemmLds L;
     const int d = p.d, hid = p.hid;
     const int t13 = (d / 128) * (hid / 128);
-    int bid = blockIdx.x;
+    int bid = xcd_block(blockIdx.x, gridDim.x);
     const int tile = bid % (3 * t13);
     bid /= 3 * t13;
     const int sk = bid % p.splitk;
     const int h = bid / p.splitk;
     const int which = tile / t13, ti = tile % t13;
     const int cstart = c * p.chunk;
-    const int clen32 = (min(p.chunk, p.Tkv - cstart) + 31) / 32 * 32;
-    const int kper = ((clen32 + p.splitk - 1) / p.splitk + 31) / 32 * 32;
-    const int k0 = min(clen32, sk * kper);
-    const int k1 = min(clen32, k0 + kper);
+    const int clen64 = (min(p.chunk, p.Tkv - cstart) + 63) / 64 * 64;
+    const int kper = ((clen64 + p.splitk - 1) / p.splitk + 63) / 64 * 64;
+    const int k0 = min(clen64, sk * kper);
+    const int k1 = min(clen64, k0 + kper);
     float *part = p.part + (((long)sk * p.NH + h) * 3 + which) * (long)hid * d;
     const int Mdim = (which < 2) ? d : hid, Ndim = (which < 2) ? hid : d;
     const int tm = ti / (Ndim / 128), tn = ti % (Ndim / 128);
@@ -556,7 +575,7 @@ __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, 
 {
     __shared__ GemmLds L;
     const int mt = (2 * p.hid) / 128, nt = (T + 127) / 128;
-    int bid = blockIdx.x;
+    int bid = xcd_block(blockIdx.x, gridDim.x);
     const int tm = bid % mt;
     bid /= mt;
     const int tn = bid % nt;
@@ -599,7 +618,7 @@ __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot
 {
     __shared__ GemmLds L;
     const int mt = p.d / 128, nt = (T + 127) / 128;
-    int bid = blockIdx.x;
+    int bid = xcd_block(blockIdx.x, gridDim.x);
     const int tm = bid % mt;
     bid /= mt;
     const int tn = bid % nt;
@@ -651,8 +670,11 @@ static int lact_splitk(const LactShape &s, int clen)
 {
     const int t13 = (s.d / 128) * (s.hid / 128);
     const int tiles = s.NH * 3 * t13;
-    int sk = (768 + tiles - 1) / tiles;            // aim at ~3 workgroups per CU
-    const int maxsk = (clen + 255) / 256;          // at least 256 tokens per split
+    // Each split adds a 3 x hid x d fp32 partial per head that the update reads
+    // back; two splits balance that traffic against filling the CUs.
+    int sk = (256 + tiles - 1) / tiles;
+    if (sk > 2) sk = 2;
+    const int maxsk = (clen + 511) / 512;          // at least 512 tokens per split
     if (sk > maxsk) sk = maxsk;
     return sk < 1 ? 1 : sk;
 }
