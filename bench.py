@@ -237,6 +237,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--lact-only", action="store_true",
+                    help="only time the two LaCT workloads (for profiling them alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (scales HBM counters)")
     args = ap.parse_args()
@@ -261,6 +263,10 @@ def main():
     import ttt_inputs as ti
     cla.load_library()
     torch.cuda.set_device(0)
+    if args.lact_only:
+        print(json.dumps({"lact": [bench_lact(lw, args.steps, args.warmup)
+                                   for lw in (ti.LACT_CAUSAL, ti.LACT_NONCAUSAL)]}), flush=True)
+        return
 
     wl = ti.MSE_D64
     seed = ti.WORKLOAD_SEEDS[wl.name]
@@ -289,7 +295,7 @@ def main():
                    "state": "fp32", "input_copies_rotated": r["copies"]},
         "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
-                     "unit_of_launch": "one ttt_linear_fwd call (summary, prefix and replay kernels)",
+                     "unit_of_launch": "one ttt_linear_fwd call (summary and replay kernels)",
                      "alg_bytes_per_launch": r["alg_bytes"],
                      "kernel_source_sha256_16": src_hash},
     }

@@ -925,10 +925,12 @@ LinearPlan linear_plan(const LinearShape &s)
 {
     LinearPlan pl{};
     const int T = s.Tkv;
-    // Segment length: whole super-block periods (whole chunks), enough
-    // segments to give every CU a workgroup or two, at least 64 tokens.
+    // Segment length: whole super-block periods (whole chunks), about one
+    // workgroup per CU (longer segments lengthen the serial walk, shorter ones
+    // the segment-start chain; 256 measured best on the d = 64 and d = 128
+    // workloads), at least 64 tokens.
     const long long period = (s.chunk <= SB) ? (long long)(SB / s.chunk) * s.chunk : s.chunk;
-    const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 512);
+    const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 256);
     long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : period;
     if (seg < SB) seg = SB;
     const int forced = env_int("TTT_LINEAR_SEG_TOKENS", 0);
