@@ -80,6 +80,15 @@ def test_bf16_multi_segment(d, loss, chunk):
     run_case(2, 2, 1000, d, chunk, loss, "bf16", seed=4)
 
 
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [32, 80, 96, 112, 160, 192])
+def test_bf16_chunk_schedules(chunk, loss):
+    """Chunks that put several chunks in a 64-token super-block (32), cut a
+    chunk into 64-token pieces with a short last piece (80, 96, 112, 160,
+    192), across several segments and a ragged tail."""
+    run_case(1, 3, 777, 64, chunk, loss, "bf16", seed=11)
+
+
 @pytest.mark.parametrize("seg", [16, 32, 160, 4096])
 def test_bf16_segment_sizes(seg):
     """Results must not depend on how the sequence is cut into segments."""
