@@ -57,15 +57,6 @@ __device__ __forceinline__ f32x4 mfma32(f32x4 acc, bf16x8 a, bf16x8 b)
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
 
-// Workgroups are dealt to the 8 XCDs round-robin (XCD = block index mod 8),
-// and each XCD has its own L2.  Renumber blocks so that logical blocks
-// [x * n/8, (x + 1) * n/8) all run on XCD x: kernels order their logical
-// index so that tiles sharing an operand are consecutive, and the operand is
-// then fetched into one L2 instead of eight.
-__device__ __forceinline__ int xcd_block(int b, int n)
-{
-    return (n % 8) ? b : (b % 8) * (n / 8) + b / 8;
-}
 
 // ---------------------------------------------------------------------------
 // Generic NT GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16, k contiguous),

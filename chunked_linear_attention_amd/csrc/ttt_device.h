@@ -93,6 +93,17 @@ __device__ __forceinline__ f32x4 mma32z(f32x4 acc, bf16x4 a0, bf16x4 b0)
 }
 __device__ __forceinline__ f32x4 mma32z(f32x4 acc, f32x4 a0, f32x4 b0) { return mma16(acc, a0, b0); }
 
+// ---- workgroup placement ------------------------------------------------------
+// Workgroups are dealt to the 8 XCDs round-robin (XCD = block index mod 8),
+// and each XCD has its own L2.  Renumber blocks so that logical blocks
+// [x * n/8, (x + 1) * n/8) all run on XCD x: kernels order their logical
+// index so that blocks sharing data are consecutive, and the data is then
+// fetched into one L2 instead of eight.
+__device__ __forceinline__ int xcd_block(int b, int n)
+{
+    return (n % 8) ? b : (b % 8) * (n / 8) + b / 8;
+}
+
 // ---- small vector memory helpers --------------------------------------------
 // Four consecutive elements (8 bytes for bf16, 16 bytes for fp32).
 template <typename E> struct Vec4;

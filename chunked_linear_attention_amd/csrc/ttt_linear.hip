@@ -32,15 +32,20 @@
 //    has four independent 16-token tiles.
 //  * Segments.  The chunk update is affine in the state,
 //    W_{c+1} = (I - K_c^T H_c K_c) W_c + K_c^T H_c V_c, so a run of whole
-//    chunks (a segment) is one affine map W -> W - P W + B.  Three kernels:
+//    chunks (a segment) is one affine map W -> W - P W + B.  Two kernels:
 //      summary : every segment (but the last, causal) computes P and B from
 //                its keys/values alone, all segments in parallel;
-//      prefix  : per (head, column block), W_start(s+1) = W_s - P_s W_s + B_s;
-//      replay  : every segment replays its super-blocks from W_start(s) and
-//                writes its outputs; the last segment writes the final state.
-//    For the inner-product loss P = 0 and the prefix is a running sum.
-//  * Non-causal order: summary over all segments, prefix to W_final, then an
-//    apply kernel O = Q W_final.
+//      replay  : every segment first builds its start state by applying the
+//                maps of the segments before it to w_init (the chain),
+//                W_start(s+1) = W_s - P_s W_s + B_s, then replays its
+//                super-blocks and writes its outputs; the last segment writes
+//                the final state.
+//    For the inner-product loss P = 0 and the chain is a running sum.
+//  * Non-causal order: summary over all segments, the chain to W_final (one
+//    workgroup per head), then an apply kernel O = Q W_final.
+//  * bf16 with d = 64 and b <= 64 runs producer/consumer versions of summary
+//    and replay (eight waves; see the section that defines them); the other
+//    shapes run the four-wave versions.
 #include "ttt_device.h"
 #include "ttt_internal.h"
 
@@ -54,8 +59,9 @@ struct LinParams {
     void *out;
     float *w_final;
     void *wsP;      // [NH][Ssum][d][d] element type (MSE only)
-    float *wsB;     // [NH][Ssum][d][d]
-    float *wsW0;    // [NH][d][d]: copy of w_init read by the replay (causal, S > 1)
+    float *wsB;     // [NH][Ssum][d/16 col blocks][d/16 row blocks][64 lanes][4] fp32
+    float *wsW0;    // [NH][d][d]: copy of w_init for the replay (causal, S > 1,
+                    // w_final == w_init); null otherwise
     int NH, Tq, Tkv, chunk, seg_tokens, S, Ssum, seg_q, Sq;
 };
 
@@ -579,20 +585,20 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_summary(LinParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = (E)Xp[r][j];
     }
-    float *dst = p.wsB + base;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(p.wsB + base) + c * ND * 64;
 #pragma unroll
-    for (int r = 0; r < ND; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = Xb[r][j];
+    for (int r = 0; r < ND; ++r) dst[r * 64 + lane] = Xb[r];
 }
 
 // ---------------------------------------------------------------------------
 // Segment-start chain.  R holds column block c of a state (accumulator
 // layout); apply the affine maps of segments 0..nsteps-1 of head h to it:
-// R <- R - P_s R + B_s.  P_s (D x D, element type) is staged through LDS by
-// the whole workgroup, two steps ahead in registers; each wave reads the P
-// rows it needs as A fragments and its column block of B_s into the
-// accumulator layout.  NPB = 2: double-buffered LDS (one barrier a step).
+// R <- R - P_s R + B_s.  P_s (D x D row-major, element type) is staged
+// through LDS by the whole workgroup, two steps ahead in registers; each wave
+// reads the P rows it needs as A fragments.  B_s is stored in accumulator
+// order (column block, row block, lane, 4 rows), so a wave's column block is
+// one 16-byte read per row block.  NPB = 2: double-buffered LDS (one barrier a
+// step).
 // ---------------------------------------------------------------------------
 template <typename E, int D> struct alignas(16) PStage {
     E m[D][D + (sizeof(E) == 2 ? 8 : 4)];
@@ -639,12 +645,11 @@ __device__ __forceinline__ void chain_maps(f32x4 *R, const LinParams &p, int h, 
     const size_t hb = (size_t)h * p.Ssum * D * D;
     const float *Bh = p.wsB + hb;
     f32x4 Bt[2][ND];
+    const int lane = 16 * g + m;
     auto loadB = [&](int slot, int step) {
-        const float *Bs = Bh + (size_t)step * D * D;
+        const f32x4 *Bs = reinterpret_cast<const f32x4 *>(Bh + (size_t)step * D * D) + c * ND * 64;
 #pragma unroll
-        for (int r = 0; r < ND; ++r)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Bt[slot][r][j] = Bs[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
+        for (int r = 0; r < ND; ++r) Bt[slot][r] = Bs[r * 64 + lane];
     };
     const int last = nsteps - 1;
     PLoader<E, D, NT> pl;
@@ -760,9 +765,9 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
     const int tend = min(T, t0 + p.seg_tokens);
     const SbSched sc(p.chunk);
 
-    // w_init itself when this head has one segment; otherwise the summary's
-    // copy (w_final may alias w_init, and the last segment writes it).
-    const float *ws = ((p.S > 1) ? p.wsW0 : p.w_init) + (size_t)h * D * D;
+    // w_init itself, or the summary's copy of it when w_final is the same
+    // buffer (the last segment writes it while earlier ones may still read).
+    const float *ws = (p.wsW0 ? p.wsW0 : p.w_init) + (size_t)h * D * D;
     f32x4 R[ND];
     SplitFrag<E> Rs[ND], Ss[SNAP ? ND : 1];
 #pragma unroll
@@ -855,6 +860,695 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
     });
 
     if (seg == p.S - 1) {
+        float *wf = p.w_final + (size_t)h * D * D;
+#pragma unroll
+        for (int r = 0; r < ND; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wf[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = R[r][j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Producer/consumer kernels (bf16, d = 64, b <= 64).  Eight waves per
+// workgroup.  Waves 0-3 (consumers) own column block c of the running state
+// (replay) or of [P | B] (summary) exactly as above.  Waves 4-7 (producers)
+// move the token tiles from HBM into a three-deep LDS ring and compute, one
+// super-block ahead, everything that does not depend on the state: the
+// transformed keys and values (T K, T V, each producer one column block) and,
+// for the replay, the query-key blocks A_ij.  Each SIMD then runs one wave of
+// each kind, so the serial state chain issues beside the independent work
+// instead of after it.  One workgroup barrier per super-block.
+// ---------------------------------------------------------------------------
+constexpr int PC_NR = 3;  // LDS ring of raw super-block tiles
+// Producer wave k (0..3) alone loads super-blocks n = k (mod 4) and chain
+// steps s = k (mod 4): when it commits one, the only loads it has in flight
+// are that item's, issued four iterations earlier, so the wait before the
+// commit (which the compiler places conservatively inside loops) costs nothing.
+template <int ST> using PcLoader = SbLoader<__bf16, 64, ST, 1, 64>;
+
+// Producer results for one super-block (replay).
+template <bool LT> struct alignas(16) PcRepDer {
+    KtTile<__bf16, LT ? 64 : 16> kt;  // T K, feature-major
+    bf16x4 ab[10][64];                // A_ij (pair-block indices 6..15)
+};
+// Producer results for one super-block (summary, b < 64 only).
+template <bool LT> struct alignas(16) PcSumDer {
+    KtTile<__bf16, LT ? 64 : 16> kt;
+    f32x4 kc[LT ? 4 : 1][4][64];  // T K by column block, accumulator order
+};
+
+// Tokens per super-block for chunk CH <= 64, and whether T is needed: only
+// when the super-block holds several chunks (b = 48 holds one chunk of three
+// tiles; its fourth tile is masked).
+template <int CH> struct PcCfg {
+    static constexpr int L = (SB / CH) * CH;
+    static constexpr bool MULTI = (SB / CH) > 1;
+};
+
+template <int ST>
+__device__ __forceinline__ void pc_krows(const SbTile<__bf16, 64, ST> &t, bf16x4 (&Kr)[4][4], int m, int g)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Kr[i][r] = k_row(t, i, r, m, g);
+}
+
+// The A_ij blocks producer wave PC computes: indices 6 + PC + 4k.
+template <int PC, int ST, typename Der>
+__device__ __forceinline__ void pc_ablocks(const SbTile<__bf16, 64, ST> &t, const bf16x4 (&Kr)[4][4],
+                                           const f32x4 *et, Der &dv, int lane, int m, int g)
+{
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int b = 6 + PC + 4 * k;
+        if (b > 15) break;
+        const int i = blk_i(b), j = blk_j(b);
+        bf16x4 Qi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Qi[r] = q_row(t, i, r, m, g);
+        f32x4 acc = mma_b<bf16x4, 4>(zero4(), Kr[j], Qi) * et[j];
+        if (i == j) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[x] = (4 * g + x <= m) ? acc[x] : 0.f;
+        }
+        dv.ab[b - 6][lane] = to_bf16x4(acc);
+    }
+}
+
+// Shared -L_ij blocks (b < 64 with several chunks per super-block).  Producer
+// wave K computes the nonzero blocks among indices K and K + 4, writes them to
+// LDS and counts itself in; the others wait for all four before the forward
+// substitution of T K.  Every producer wave reaches its count before it waits,
+// so the wait ends.  Two buffers by super-block parity: the consumers apply
+// the blocks of their super-block to V (T V) while the producers fill the
+// next one's.
+struct alignas(16) PcLShare {
+    bf16x4 blk[2][6][64];
+    unsigned count;
+};
+
+template <int CH> __host__ __device__ constexpr bool l_nonzero(int b)
+{
+    return (16 * blk_j(b)) / CH < (16 * blk_i(b)) / CH;
+}
+
+template <int K, int CH, int ST>
+__device__ __forceinline__ void pc_lshare_put(const SbTile<__bf16, 64, ST> &t, const f32x4 *et, PcLShare &ls,
+                                              int n, int lane, int m, int g)
+{
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int b = K + 4 * q;
+        if (b >= 6 || !l_nonzero<CH>(b)) continue;
+        const int i = blk_i(b), j = blk_j(b);
+        bf16x4 Ki[4], Kj[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            Ki[r] = k_row(t, i, r, m, g);
+            Kj[r] = k_row(t, j, r, m, g);
+        }
+        ls.blk[n & 1][b][lane] = to_bf16x4(mma_b<bf16x4, 4>(zero4(), Kj, Ki) * (-et[j]));
+    }
+    if (lane == 0) __hip_atomic_fetch_add(&ls.count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <int CH>
+__device__ __forceinline__ void pc_lshare_read(const PcLShare &ls, int n, bf16x4 *Ln, int lane)
+{
+#pragma unroll
+    for (int b = 0; b < 6; ++b)
+        if (l_nonzero<CH>(b)) Ln[b] = ls.blk[n & 1][b][lane];
+}
+template <int CH>
+__device__ __forceinline__ void pc_lshare_get(PcLShare &ls, int n, bf16x4 *Ln, int lane)
+{
+    const unsigned target = 4u * (n + 1);
+    while (__builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(&ls.count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < target)
+        __builtin_amdgcn_s_sleep(1);
+    pc_lshare_read<CH>(ls, n, Ln, lane);
+}
+
+// Block forward substitution with the blocks that are zero for CH skipped.
+template <int CH>
+__device__ __forceinline__ void substitute_ch(f32x4 *X, const bf16x4 *Ln)
+{
+    static_assert(l_nonzero<CH>(1) && l_nonzero<CH>(2) && l_nonzero<CH>(3) && l_nonzero<CH>(4), "chunk shape");
+    const bf16x4 x0 = to_bf16x4(X[0]);
+    if constexpr (l_nonzero<CH>(0)) X[1] = mma32z(X[1], Ln[lblk(1, 0)], x0);
+    const bf16x4 x1 = to_bf16x4(X[1]);
+    X[2] = mma32(X[2], Ln[lblk(2, 0)], Ln[lblk(2, 1)], x0, x1);
+    const bf16x4 x2 = to_bf16x4(X[2]);
+    X[3] = mma32(X[3], Ln[lblk(3, 0)], Ln[lblk(3, 1)], x0, x1);
+    if constexpr (l_nonzero<CH>(5)) X[3] = mma32z(X[3], Ln[lblk(3, 2)], x2);
+}
+
+// Producer wave K's share of one super-block (replay): its A_ij blocks and,
+// for b < 64 with several chunks, its column block of T K.
+template <int K, bool LT, int CH, int ST, typename Der>
+__device__ __forceinline__ void pc_derive_rep(const SbTile<__bf16, 64, ST> &t, Der &dv, PcLShare &ls, int n,
+                                              int len, int lane, int m, int g)
+{
+    f32x4 et[4];
+    load_eta(t, len, g, et);
+    if constexpr (LT) pc_lshare_put<K, CH>(t, et, ls, n, lane, m, g);
+    bf16x4 Kr[4][4];
+    pc_krows(t, Kr, m, g);
+    pc_ablocks<K>(t, Kr, et, dv, lane, m, g);
+    if constexpr (LT) {
+        f32x4 Kc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Kc[i] = to_f32x4(k_tok(t, i, K, m, g));
+        bf16x4 Ln[6];
+        pc_lshare_get<CH>(ls, n, Ln, lane);
+        substitute_ch<CH>(Kc, Ln);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv.kt.put(K, i, Kc[i], m, g);
+    }
+}
+
+// Producer wave K's share of one super-block (summary, b < 64 with several
+// chunks): its column block of T K (bf16 feature-major and fp32).
+template <int K, int CH, int ST, typename Der>
+__device__ __forceinline__ void pc_derive_sum(const SbTile<__bf16, 64, ST> &t, Der &dv, PcLShare &ls, int n,
+                                              int len, int lane, int m, int g)
+{
+    f32x4 et[4];
+    load_eta(t, len, g, et);
+    pc_lshare_put<K, CH>(t, et, ls, n, lane, m, g);
+    f32x4 Kc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Kc[i] = to_f32x4(k_tok(t, i, K, m, g));
+    bf16x4 Ln[6];
+    pc_lshare_get<CH>(ls, n, Ln, lane);
+    substitute_ch<CH>(Kc, Ln);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dv.kt.put(K, i, Kc[i], m, g);
+        dv.kc[K][i][lane] = Kc[i];
+    }
+}
+
+// Segment-start chain for consumer wave c, reading the summaries from global
+// memory two steps ahead (no LDS, no barrier): R <- R - P_s R + B_s.
+template <bool MSE, typename Step>
+__device__ __forceinline__ void pc_chain(f32x4 (&R)[4], const LinParams &p, int h, int nsteps, int c, int lane,
+                                         int m, int g, Step &&step)
+{
+    const size_t hb = (size_t)h * p.Ssum * 64 * 64;
+    const __bf16 *Ph = (const __bf16 *)p.wsP + hb + m * 64 + 4 * g;
+    const f32x4 *Bh = reinterpret_cast<const f32x4 *>(p.wsB + hb) + c * 4 * 64 + lane;
+    bf16x4 PA[2][4][4];
+    f32x4 Bt[2][4];
+    auto load = [&](int slot, int step) {
+        if (MSE) {
+            const __bf16 *P = Ph + (size_t)step * 64 * 64;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) PA[slot][r][q] = load4<__bf16>(P + 16 * r * 64 + 16 * q);
+        }
+        const f32x4 *B = Bh + (size_t)step * 1024;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Bt[slot][r] = B[r * 64];
+    };
+    const int last = nsteps - 1;
+    load(0, 0);
+    load(1, min(1, last));
+    for (int s0 = 0; s0 < nsteps; s0 += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int s = s0 + j;
+            if (s >= nsteps) break;
+            if (MSE) {
+                SplitFrag<__bf16> Ws[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ws[r].set(R[r]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    R[r] = R[r] + Bt[j][r] - mma_state_b<__bf16, 4>(zero4(), PA[j][r], Ws);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) R[r] = R[r] + Bt[j][r];
+            }
+            step(s);
+            load(j, min(s + 2, last));
+        }
+    }
+}
+
+// Segment-start chain staged through LDS (MSE): the producers load P_s
+// (row-major) and B_s (accumulator order) four steps ahead into a two-entry
+// ring; the consumers apply R <- R - P_s R + B_s.  One barrier per step on
+// both sides.
+struct alignas(16) PcChainStage {
+    __bf16 P[2][64][72];
+    f32x4 B[2][4][4][64];
+};
+
+template <typename Mid>
+__device__ __forceinline__ void pc_chain_stage(const LinParams &p, int h, int nsteps, PcChainStage &cs, int k,
+                                               int lane, Mid &&mid)
+{
+    const size_t hb = (size_t)h * p.Ssum * 64 * 64;
+    const __bf16 *Ph = (const __bf16 *)p.wsP + hb;
+    const f32x4 *Bh = reinterpret_cast<const f32x4 *>(p.wsB + hb);
+    u32x4 vp[8];
+    f32x4 vb[16];
+    auto issue = [&](int step) {
+        const __bf16 *P = Ph + (size_t)step * 64 * 64;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = lane + 64 * i;
+            vp[i] = *reinterpret_cast<const u32x4 *>(P + (piece >> 3) * 64 + (piece & 7) * 8);
+        }
+        const f32x4 *B = Bh + (size_t)step * 1024;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vb[i] = B[lane + 64 * i];
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = lane + 64 * i;
+            *reinterpret_cast<u32x4 *>(&cs.P[buf][piece >> 3][(piece & 7) * 8]) = vp[i];
+        }
+        f32x4 *Bd = &cs.B[buf][0][0][0];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Bd[lane + 64 * i] = vb[i];
+    };
+    // mid() (the wave's first super-block load) follows the wave's last chain
+    // load: the chain's own loads are not queued behind it, and the wave's
+    // next wait (four steps later) finds it landed
+    if (k < nsteps) {
+        issue(k);
+        if (k + 4 >= nsteps) mid();
+    } else {
+        mid();
+    }
+    if (k == 0) {
+        commit(0);
+        if (4 < nsteps) {
+            issue(4);
+            if (8 >= nsteps) mid();
+        }
+    }
+    lds_barrier();
+    for (int s = 0; s < nsteps; ++s) {
+        // stage step s + 1 into buffer (s + 1) & 1, then load step s + 5
+        if (((s + 1) & 3) == k && s + 1 < nsteps) {
+            commit((s + 1) & 1);
+            if (s + 5 < nsteps) {
+                issue(s + 5);
+                if (s + 9 >= nsteps) mid();
+            }
+        }
+        lds_barrier();
+    }
+}
+
+template <typename Step>
+__device__ __forceinline__ void pc_chain_lds(f32x4 (&R)[4], int nsteps, const PcChainStage &cs, int c, int lane,
+                                             int m, int g, Step &&step)
+{
+    lds_barrier();  // step 0 staged
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        SplitFrag<__bf16> Ws[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ws[r].set(R[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bf16x4 PA[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) PA[q] = load4<__bf16>(&cs.P[buf][16 * r + m][16 * q + 4 * g]);
+            R[r] = R[r] + cs.B[buf][c][r][lane] - mma_state_b<__bf16, 4>(zero4(), PA, Ws);
+        }
+        step(s);
+        lds_barrier();
+    }
+}
+
+// Producer waves 0 and 1 commit super-blocks 0 and 1 before the walk; the
+// loads of 2..5 start with the walk (pc_walk), so that the first two are not
+// queued behind them.
+template <int ST, int L>
+__device__ __forceinline__ void pc_first_commit(SbTile<__bf16, 64, ST> *raw, PcLoader<ST> &ld, int k)
+{
+    if (k < 2) ld.commit(0, raw[k]);
+}
+
+// Main walk: iteration n, consumers run super-block n, producers prepare n + 1
+// and producer wave (n + 2) mod 4 commits super-block n + 2 into the ring and
+// loads n + 6.  The caller has committed super-blocks 0 and 1 (producer waves
+// 0 and 1) and made them visible with a barrier; waves 2 and 3 have issued
+// super-blocks 2 and 3 unless late23.  The two roles run separate loops with
+// the same barrier count, so neither keeps the other's registers.
+template <int ST, int L, typename Cons, typename Prod>
+__device__ __forceinline__ void pc_walk(SbTile<__bf16, 64, ST> *raw, PcLoader<ST> &ld, bool producer, int k,
+                                        bool late23, int t0, int nsb, Cons &&cons, Prod &&prod)
+{
+    const int ngroups = (nsb + PC_NR - 1) / PC_NR;
+    if (producer) {
+        if (k >= 2) {
+            if (late23) ld.issue(0, t0 + k * L);
+        } else {
+            ld.issue(0, t0 + (k + 4) * L);
+        }
+        if (nsb > 0) prod(raw[0], 0);
+        lds_barrier();
+        for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+            for (int j = 0; j < PC_NR; ++j) {
+                const int n = PC_NR * gi + j;
+                if (n >= nsb) break;  // uniform: every wave leaves at the same n
+                if (n + 1 < nsb) prod(raw[(j + 1) % PC_NR], n + 1);
+                if (((n + 2) & 3) == k) {
+                    ld.commit(0, raw[(j + 2) % PC_NR]);
+                    ld.issue(0, t0 + (n + 6) * L);
+                }
+                lds_barrier();
+            }
+        }
+    } else {
+        lds_barrier();
+        for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+            for (int j = 0; j < PC_NR; ++j) {
+                const int n = PC_NR * gi + j;
+                if (n >= nsb) break;
+                cons(raw[j], n);
+                lds_barrier();
+            }
+        }
+    }
+}
+
+template <bool MSE, int CH>
+__global__ __launch_bounds__(512) void lin_summary_pc(LinParams p)
+{
+    typedef __bf16 E;
+    typedef bf16x4 F;
+    constexpr int D = 64, ND = 4, L = PcCfg<CH>::L;
+    constexpr bool LT = MSE && PcCfg<CH>::MULTI;
+    constexpr int ST = STAGE_K | STAGE_V | STAGE_E;
+    __shared__ SbTile<E, D, ST> raw[PC_NR];
+    __shared__ PcSumDer<LT> der[LT ? 2 : 1];
+    __shared__ PcLShare ls;
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool producer = wave >= 4;
+    const int c = wave & 3;  // consumer column block / producer column block
+    // a head's segments on one XCD: the replay's chain then reads the
+    // summaries from the L2 they were written to
+    const int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int seg = bid % p.Ssum, h = bid / p.Ssum;
+    const int T = p.Tkv;
+    const int t0 = seg * p.seg_tokens;
+    const int tend = min(T, t0 + p.seg_tokens);
+    const int nsb = (tend - t0 + L - 1) / L;
+
+    PcLoader<ST> ld;
+    if (threadIdx.x == 0) ls.count = 0;
+    if (producer) {
+        ld.init(lane, nullptr, p.k, p.v, p.eta, h, T, tend);
+        if (c < 2) ld.issue(0, t0 + c * L);
+        pc_first_commit<ST, L>(raw, ld, c);
+    }
+    lds_barrier();
+
+    f32x4 Xp[ND], Xb[ND];
+    F Xpr[ND], Xbr[ND];
+#pragma unroll
+    for (int r = 0; r < ND; ++r) {
+        Xp[r] = zero4();
+        Xb[r] = zero4();
+        Xpr[r] = to_frag<E>(zero4());
+        Xbr[r] = Xpr[r];
+    }
+    auto prod = [&](const SbTile<E, D, ST> &t, int n) {
+        if constexpr (LT) {
+            PcSumDer<LT> &dv = der[n & 1];
+            switch (c) {
+            case 0: pc_derive_sum<0, CH>(t, dv, ls, n, L, lane, m, g); break;
+            case 1: pc_derive_sum<1, CH>(t, dv, ls, n, L, lane, m, g); break;
+            case 2: pc_derive_sum<2, CH>(t, dv, ls, n, L, lane, m, g); break;
+            default: pc_derive_sum<3, CH>(t, dv, ls, n, L, lane, m, g); break;
+            }
+        }
+    };
+    auto cons = [&](const SbTile<E, D, ST> &t, int n) {
+        f32x4 et[4];
+        load_eta(t, L, g, et);
+        if (!MSE) {
+            F EV[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) EV[i] = to_bf16x4(to_f32x4(v_tok(t, i, c, m, g)) * et[i]);
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; i += 2)
+                    Xb[r] = mma32(Xb[r], k_tok(t, i, r, m, g), k_tok(t, i + 1, r, m, g), EV[i], EV[i + 1]);
+            return;
+        }
+        // tiles (and the P and B halves) side by side: consecutive MFMAs are
+        // independent
+        f32x4 Kc[4], Vc[4];
+        F Ka[4][ND];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (LT) {
+                const PcSumDer<LT> &dv = der[n & 1];
+                Kc[i] = dv.kc[c][i][lane];
+                Vc[i] = to_f32x4(v_tok(t, i, c, m, g));
+#pragma unroll
+                for (int r = 0; r < ND; ++r) Ka[i][r] = dv.kt.row(i, r, m, g);
+            } else {
+                Kc[i] = to_f32x4(k_tok(t, i, c, m, g));
+                Vc[i] = to_f32x4(v_tok(t, i, c, m, g));
+#pragma unroll
+                for (int r = 0; r < ND; ++r) Ka[i][r] = k_row(t, i, r, m, g);
+            }
+        }
+        if constexpr (LT) {
+            // T V for this column block, from the super-block's shared blocks
+            bf16x4 Ln[6];
+            pc_lshare_read<CH>(ls, n, Ln, lane);
+            substitute_ch<CH>(Vc, Ln);
+        }
+        f32x4 Ap[4] = {zero4(), zero4(), zero4(), zero4()}, Ab[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int r = 0; r < ND; r += 2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Ap[i] = mma32(Ap[i], Ka[i][r], Ka[i][r + 1], Xpr[r], Xpr[r + 1]);
+                Ab[i] = mma32(Ab[i], Ka[i][r], Ka[i][r + 1], Xbr[r], Xbr[r + 1]);
+            }
+        F EUp[4], EUb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            EUp[i] = to_bf16x4((Kc[i] - Ap[i]) * et[i]);
+            EUb[i] = to_bf16x4((Vc[i] - Ab[i]) * et[i]);
+        }
+        F kt[4][ND];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < ND; ++r) kt[i][r] = k_tok(t, i, r, m, g);
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            Xp[r] = mma32(Xp[r], kt[0][r], kt[1][r], EUp[0], EUp[1]);
+            Xb[r] = mma32(Xb[r], kt[0][r], kt[1][r], EUb[0], EUb[1]);
+        }
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            Xp[r] = mma32(Xp[r], kt[2][r], kt[3][r], EUp[2], EUp[3]);
+            Xb[r] = mma32(Xb[r], kt[2][r], kt[3][r], EUb[2], EUb[3]);
+            Xpr[r] = to_bf16x4(Xp[r]);
+            Xbr[r] = to_bf16x4(Xb[r]);
+        }
+    };
+    pc_walk<ST, L>(raw, ld, producer, c, true, t0, nsb, cons, prod);
+
+    const size_t base = ((size_t)h * p.Ssum + seg) * D * D;
+    if (!producer) {
+        if (MSE) {
+            E *dst = (E *)p.wsP + base;
+#pragma unroll
+            for (int r = 0; r < ND; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m] = (E)Xp[r][j];
+        }
+        f32x4 *dst = reinterpret_cast<f32x4 *>(p.wsB + base) + c * ND * 64;
+#pragma unroll
+        for (int r = 0; r < ND; ++r) dst[r * 64 + lane] = Xb[r];
+    } else if (seg == 0 && p.wsW0) {
+        // copy of w_init for the replay when w_final is the same buffer
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(p.w_init + (size_t)h * D * D);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(p.wsW0 + (size_t)h * D * D);
+        for (int i = threadIdx.x - 256; i < D * D / 4; i += 256) dst[i] = src[i];
+    }
+}
+
+template <bool MSE, int CH>
+__global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
+{
+    typedef __bf16 E;
+    typedef bf16x4 F;
+    constexpr int D = 64, ND = 4, L = PcCfg<CH>::L;
+    constexpr bool LT = MSE && PcCfg<CH>::MULTI;
+    constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E;
+    __shared__ SbTile<E, D, ST> raw[PC_NR];
+    // the chain's staging and the producers' results are never live together
+    __shared__ union {
+        PcRepDer<LT> der[2];
+        PcChainStage cs;
+    } u;
+    __shared__ PcLShare ls;
+    PcRepDer<LT> *der = u.der;
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool producer = wave >= 4;
+    const int c = wave & 3;
+    const int bid = xcd_block(blockIdx.x, gridDim.x);  // a head's segments on one XCD
+    const int seg = bid % p.S, h = bid / p.S;
+    const int T = p.Tkv;
+    const int t0 = seg * p.seg_tokens;
+    const int tend = min(T, t0 + p.seg_tokens);
+    const int nsb = (tend - t0 + L - 1) / L;
+
+    PcLoader<ST> ld;
+    f32x4 R[ND];
+    SplitFrag<E> Rs[ND];
+    const bool chain_lds = MSE && seg > 0;
+    if (threadIdx.x == 0) ls.count = 0;
+    if (producer) {
+        ld.init(lane, p.q, p.k, p.v, p.eta, h, T, tend);
+        // the chain's loads go first; each wave's first super-block load
+        // follows its last chain load
+        if (chain_lds)
+            pc_chain_stage(p, h, seg, u.cs, c, lane, [&] { ld.issue(0, t0 + c * L); });
+        else if (c < 2)
+            ld.issue(0, t0 + c * L);
+        pc_first_commit<ST, L>(raw, ld, c);
+    } else {
+        // w_init itself, or the summary's copy of it when w_final is the same
+        // buffer (the last segment writes it while earlier ones may still read)
+        const float *ws = (p.wsW0 ? p.wsW0 : p.w_init) + (size_t)h * D * D;
+#pragma unroll
+        for (int r = 0; r < ND; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) R[r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
+        if (seg > 0) {
+            if (MSE)
+                pc_chain_lds(R, seg, u.cs, c, lane, m, g, [](int) {});
+            else
+                pc_chain<false>(R, p, h, seg, c, lane, m, g, [](int) {});
+        }
+#pragma unroll
+        for (int r = 0; r < ND; ++r) Rs[r].set(R[r]);
+    }
+    lds_barrier();
+
+    E *out_h = (E *)p.out + (size_t)h * T * D;
+    auto prod = [&](const SbTile<E, D, ST> &t, int n) {
+        PcRepDer<LT> &dv = der[n & 1];
+        switch (c) {
+        case 0: pc_derive_rep<0, LT, CH>(t, dv, ls, n, L, lane, m, g); break;
+        case 1: pc_derive_rep<1, LT, CH>(t, dv, ls, n, L, lane, m, g); break;
+        case 2: pc_derive_rep<2, LT, CH>(t, dv, ls, n, L, lane, m, g); break;
+        default: pc_derive_rep<3, LT, CH>(t, dv, ls, n, L, lane, m, g); break;
+        }
+    };
+    auto cons = [&](const SbTile<E, D, ST> &t, int n) {
+        const PcRepDer<LT> &dv = der[n & 1];
+        const int s = t0 + n * L;
+        const int lim = min(tend, s + L);
+        f32x4 et[4];
+        load_eta(t, L, g, et);
+        // The four tiles' products are issued side by side (tile index
+        // innermost) so that consecutive MFMAs are independent.
+        f32x4 U[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[i] = to_f32x4(v_tok(t, i, c, m, g));
+        if constexpr (LT) {
+            // T V for this column block, from the super-block's shared blocks
+            bf16x4 Ln[6];
+            pc_lshare_read<CH>(ls, n, Ln, lane);
+            substitute_ch<CH>(U, Ln);
+        }
+        if (MSE) {
+            F Ka[4][ND];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < ND; ++r) {
+                    if constexpr (LT)
+                        Ka[i][r] = dv.kt.row(i, r, m, g);
+                    else
+                        Ka[i][r] = k_row(t, i, r, m, g);
+                }
+            f32x4 KR[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+            for (int r = 0; r < ND; r += 2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) KR[i] = mma32(KR[i], Ka[i][r], Ka[i][r + 1], Rs[r].hi, Rs[r + 1].hi);
+#pragma unroll
+            for (int r = 0; r < ND; r += 2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) KR[i] = mma32(KR[i], Ka[i][r], Ka[i][r + 1], Rs[r].lo, Rs[r + 1].lo);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) U[i] = U[i] - KR[i];
+        }
+        F Uf[4], EU[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Uf[i] = to_bf16x4(U[i]);
+            EU[i] = to_bf16x4(U[i] * et[i]);
+        }
+        // O^T_i = R^T Q_i^T + sum_{j<=i} U_j^T A_ij^T (transposed so each lane
+        // stores four consecutive columns of one token)
+        constexpr int NTI = (L + 15) / 16;  // tiles holding outputs
+        F Qa[4][ND];
+#pragma unroll
+        for (int i = 0; i < NTI; ++i)
+#pragma unroll
+            for (int r = 0; r < ND; ++r) Qa[i][r] = q_row(t, i, r, m, g);
+        f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int r = 0; r < ND; r += 2)
+#pragma unroll
+            for (int i = 0; i < NTI; ++i) O[i] = mma32(O[i], Rs[r].hi, Rs[r + 1].hi, Qa[i][r], Qa[i][r + 1]);
+#pragma unroll
+        for (int r = 0; r < ND; r += 2)
+#pragma unroll
+            for (int i = 0; i < NTI; ++i) O[i] = mma32(O[i], Rs[r].lo, Rs[r + 1].lo, Qa[i][r], Qa[i][r + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; j += 2)
+#pragma unroll
+            for (int i = j; i < NTI; ++i) {
+                if (j + 1 <= i)
+                    O[i] = mma32(O[i], Uf[j], Uf[j + 1], dv.ab[ablk(i, j) - 6][lane], dv.ab[ablk(i, j + 1) - 6][lane]);
+                else
+                    O[i] = mma32z(O[i], Uf[j], dv.ab[ablk(i, j) - 6][lane]);
+            }
+#pragma unroll
+        for (int i = 0; i < NTI; ++i) {
+            const int tk = s + 16 * i + m;
+            if (tk < lim) store4<E>(out_h + (size_t)tk * D + 16 * c + 4 * g, out4<E>(O[i]));
+        }
+        // R += K^T diag(eta) U
+#pragma unroll
+        for (int r = 0; r < ND; ++r) R[r] = mma32(R[r], k_tok(t, 0, r, m, g), k_tok(t, 1, r, m, g), EU[0], EU[1]);
+#pragma unroll
+        for (int r = 0; r < ND; ++r) {
+            R[r] = mma32(R[r], k_tok(t, 2, r, m, g), k_tok(t, 3, r, m, g), EU[2], EU[3]);
+            Rs[r].set(R[r]);
+        }
+    };
+    pc_walk<ST, L>(raw, ld, producer, c, !chain_lds, t0, nsb, cons, prod);
+
+    if (!producer && seg == p.S - 1) {
         float *wf = p.w_final + (size_t)h * D * D;
 #pragma unroll
         for (int r = 0; r < ND; ++r)
@@ -987,6 +1681,20 @@ static hipError_t launch_typed(const LinearShape &s, const LinearPlan &pl, LinPa
     return hipGetLastError();
 }
 
+template <bool MSE, int CH>
+static hipError_t launch_pc(const LinearShape &s, const LinearPlan &pl, LinParams p, hipStream_t st)
+{
+    const dim3 block(512);
+    if (pl.Ssum > 0) lin_summary_pc<MSE, CH><<<dim3(s.NH * pl.Ssum), block, 0, st>>>(p);
+    if (s.order == 0) {
+        lin_replay_pc<MSE, CH><<<dim3(s.NH * pl.S), block, 0, st>>>(p);
+    } else {
+        lin_final<__bf16, 64, MSE><<<dim3(s.NH), dim3(256), 0, st>>>(p);
+        if (pl.Sq > 0) lin_apply<__bf16, 64, 2><<<dim3(s.NH * pl.Sq), dim3(256), 0, st>>>(p, p.w_final, 64 * 64);
+    }
+    return hipGetLastError();
+}
+
 hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void *q, const void *k,
                          const void *v, const float *eta, const float *w_init, void *out,
                          float *w_final, void *ws, hipStream_t stream)
@@ -1001,7 +1709,11 @@ hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void 
     p.w_final = w_final;
     p.wsP = (char *)ws + pl.offP;
     p.wsB = (float *)((char *)ws + pl.offB);
-    p.wsW0 = (s.order == 0 && pl.S > 1) ? (float *)((char *)ws + pl.offW) : nullptr;
+    // The replay reads w_init at its start while the last segment writes
+    // w_final at its end: a copy is needed only when the two are one buffer.
+    p.wsW0 = (s.order == 0 && pl.S > 1 && (const void *)w_final == (const void *)w_init)
+                 ? (float *)((char *)ws + pl.offW)
+                 : nullptr;
     p.NH = s.NH;
     p.Tq = s.Tq;
     p.Tkv = s.Tkv;
@@ -1014,6 +1726,17 @@ hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void 
     const bool mse = s.loss == 1;
     // b < 64: transform by T; b > 64: chunk-start snapshots; b = 64: neither.
     const bool lt = s.chunk < SB, snap = s.chunk > SB;
+    if (s.bf16 && s.d == 64 && !snap && s.Tkv > 0) {
+        // producer/consumer kernels; the inner-product loss only needs the
+        // super-block length (64, or 48 for b = 48)
+        if (!mse) return s.chunk == 48 ? launch_pc<false, 48>(s, pl, p, stream) : launch_pc<false, 64>(s, pl, p, stream);
+        switch (s.chunk) {
+        case 16: return launch_pc<true, 16>(s, pl, p, stream);
+        case 32: return launch_pc<true, 32>(s, pl, p, stream);
+        case 48: return launch_pc<true, 48>(s, pl, p, stream);
+        default: return launch_pc<true, 64>(s, pl, p, stream);
+        }
+    }
 #define TTT_DISPATCH(E, D)                                                                  \
     if (mse) {                                                                              \
         if (lt) return launch_typed<E, D, true, true, false>(s, pl, p, stream);             \

@@ -81,11 +81,12 @@ def test_bf16_multi_segment(d, loss, chunk):
 
 
 @pytest.mark.parametrize("loss", [0, 1])
-@pytest.mark.parametrize("chunk", [32, 80, 96, 112, 160, 192])
+@pytest.mark.parametrize("chunk", [32, 48, 64, 80, 96, 112, 160, 192])
 def test_bf16_chunk_schedules(chunk, loss):
-    """Chunks that put several chunks in a 64-token super-block (32), cut a
-    chunk into 64-token pieces with a short last piece (80, 96, 112, 160,
-    192), across several segments and a ragged tail."""
+    """Chunks that put several chunks in a 64-token super-block (32), fill a
+    48-token super-block (48) or a whole one (64), cut a chunk into 64-token
+    pieces with a short last piece (80, 96, 112, 160, 192), across several
+    segments and a ragged tail."""
     run_case(1, 3, 777, 64, chunk, loss, "bf16", seed=11)
 
 
