@@ -880,11 +880,13 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
 // instead of after it.  One workgroup barrier per super-block.
 // ---------------------------------------------------------------------------
 constexpr int PC_NR = 3;  // LDS ring of raw super-block tiles
-// Producer wave k (0..3) alone loads super-blocks n = k (mod 4) and chain
-// steps s = k (mod 4): when it commits one, the only loads it has in flight
-// are that item's, issued four iterations earlier, so the wait before the
-// commit (which the compiler places conservatively inside loops) costs nothing.
-template <int ST> using PcLoader = SbLoader<__bf16, 64, ST, 1, 64>;
+// Producer waves 2p and 2p + 1 (p = k >> 1) load super-blocks n = p (mod 2),
+// half the rows each, and producer wave k alone stages chain steps
+// s = k (mod 4): when a wave commits one, the only loads it has in flight are
+// that item's, issued two (super-blocks) or four (chain steps) iterations
+// earlier, so the wait before the commit (which the compiler places
+// conservatively inside loops) costs nothing.
+template <int ST> using PcLoader = SbLoader<__bf16, 64, ST, 1, 128>;
 
 // Producer results for one super-block (replay).
 template <bool LT> struct alignas(16) PcRepDer {
@@ -1138,30 +1140,30 @@ __device__ __forceinline__ void pc_chain_stage(const LinParams &p, int h, int ns
         for (int i = 0; i < 16; ++i) Bd[lane + 64 * i] = vb[i];
     };
     // mid() (the wave's first super-block load) follows the wave's last chain
-    // load: the chain's own loads are not queued behind it, and the wave's
-    // next wait (four steps later) finds it landed
-    if (k < nsteps) {
+    // commit: the chain's loads are not queued behind super-block loads, the
+    // wave has no chain wait left that would cover it, and the super-blocks
+    // are requested during the chain's last four steps, when they are next
+    // needed
+    if (k < nsteps)
         issue(k);
-        if (k + 4 >= nsteps) mid();
-    } else {
+    else
         mid();
-    }
     if (k == 0) {
         commit(0);
-        if (4 < nsteps) {
+        if (4 < nsteps)
             issue(4);
-            if (8 >= nsteps) mid();
-        }
+        else
+            mid();
     }
     lds_barrier();
     for (int s = 0; s < nsteps; ++s) {
         // stage step s + 1 into buffer (s + 1) & 1, then load step s + 5
         if (((s + 1) & 3) == k && s + 1 < nsteps) {
             commit((s + 1) & 1);
-            if (s + 5 < nsteps) {
+            if (s + 5 < nsteps)
                 issue(s + 5);
-                if (s + 9 >= nsteps) mid();
-            }
+            else
+                mid();
         }
         lds_barrier();
     }
@@ -1189,32 +1191,27 @@ __device__ __forceinline__ void pc_chain_lds(f32x4 (&R)[4], int nsteps, const Pc
     }
 }
 
-// Producer waves 0 and 1 commit super-blocks 0 and 1 before the walk; the
-// loads of 2..5 start with the walk (pc_walk), so that the first two are not
-// queued behind them.
+// Producer pair p commits super-block p before the walk; the loads of 2 and
+// 3 start with the walk (pc_walk), so that the first two are not queued
+// behind them.
 template <int ST, int L>
 __device__ __forceinline__ void pc_first_commit(SbTile<__bf16, 64, ST> *raw, PcLoader<ST> &ld, int k)
 {
-    if (k < 2) ld.commit(0, raw[k]);
+    ld.commit(0, raw[k >> 1]);
 }
 
 // Main walk: iteration n, consumers run super-block n, producers prepare n + 1
-// and producer wave (n + 2) mod 4 commits super-block n + 2 into the ring and
-// loads n + 6.  The caller has committed super-blocks 0 and 1 (producer waves
-// 0 and 1) and made them visible with a barrier; waves 2 and 3 have issued
-// super-blocks 2 and 3 unless late23.  The two roles run separate loops with
-// the same barrier count, so neither keeps the other's registers.
+// and producer pair (n + 2) mod 2 commits super-block n + 2 into the ring and
+// loads n + 4.  The caller has committed super-blocks 0 and 1 and made them
+// visible with a barrier.  The two roles run separate loops with the same
+// barrier count, so neither keeps the other's registers.
 template <int ST, int L, typename Cons, typename Prod>
 __device__ __forceinline__ void pc_walk(SbTile<__bf16, 64, ST> *raw, PcLoader<ST> &ld, bool producer, int k,
-                                        bool late23, int t0, int nsb, Cons &&cons, Prod &&prod)
+                                        int t0, int nsb, Cons &&cons, Prod &&prod)
 {
     const int ngroups = (nsb + PC_NR - 1) / PC_NR;
     if (producer) {
-        if (k >= 2) {
-            if (late23) ld.issue(0, t0 + k * L);
-        } else {
-            ld.issue(0, t0 + (k + 4) * L);
-        }
+        ld.issue(0, t0 + ((k >> 1) + 2) * L);
         if (nsb > 0) prod(raw[0], 0);
         lds_barrier();
         for (int gi = 0; gi < ngroups; ++gi) {
@@ -1223,9 +1220,9 @@ __device__ __forceinline__ void pc_walk(SbTile<__bf16, 64, ST> *raw, PcLoader<ST
                 const int n = PC_NR * gi + j;
                 if (n >= nsb) break;  // uniform: every wave leaves at the same n
                 if (n + 1 < nsb) prod(raw[(j + 1) % PC_NR], n + 1);
-                if (((n + 2) & 3) == k) {
+                if ((n & 1) == (k >> 1)) {
                     ld.commit(0, raw[(j + 2) % PC_NR]);
-                    ld.issue(0, t0 + (n + 6) * L);
+                    ld.issue(0, t0 + (n + 4) * L);
                 }
                 lds_barrier();
             }
@@ -1271,8 +1268,8 @@ __global__ __launch_bounds__(512) void lin_summary_pc(LinParams p)
     PcLoader<ST> ld;
     if (threadIdx.x == 0) ls.count = 0;
     if (producer) {
-        ld.init(lane, nullptr, p.k, p.v, p.eta, h, T, tend);
-        if (c < 2) ld.issue(0, t0 + c * L);
+        ld.init((c & 1) * 64 + lane, nullptr, p.k, p.v, p.eta, h, T, tend);
+        ld.issue(0, t0 + (c >> 1) * L);
         pc_first_commit<ST, L>(raw, ld, c);
     }
     lds_barrier();
@@ -1368,7 +1365,7 @@ __global__ __launch_bounds__(512) void lin_summary_pc(LinParams p)
             Xbr[r] = to_bf16x4(Xb[r]);
         }
     };
-    pc_walk<ST, L>(raw, ld, producer, c, true, t0, nsb, cons, prod);
+    pc_walk<ST, L>(raw, ld, producer, c, t0, nsb, cons, prod);
 
     const size_t base = ((size_t)h * p.Ssum + seg) * D * D;
     if (!producer) {
@@ -1423,13 +1420,13 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
     const bool chain_lds = MSE && seg > 0;
     if (threadIdx.x == 0) ls.count = 0;
     if (producer) {
-        ld.init(lane, p.q, p.k, p.v, p.eta, h, T, tend);
+        ld.init((c & 1) * 64 + lane, p.q, p.k, p.v, p.eta, h, T, tend);
         // the chain's loads go first; each wave's first super-block load
         // follows its last chain load
         if (chain_lds)
-            pc_chain_stage(p, h, seg, u.cs, c, lane, [&] { ld.issue(0, t0 + c * L); });
-        else if (c < 2)
-            ld.issue(0, t0 + c * L);
+            pc_chain_stage(p, h, seg, u.cs, c, lane, [&] { ld.issue(0, t0 + (c >> 1) * L); });
+        else
+            ld.issue(0, t0 + (c >> 1) * L);
         pc_first_commit<ST, L>(raw, ld, c);
     } else {
         // w_init itself, or the summary's copy of it when w_final is the same
@@ -1546,7 +1543,7 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
             Rs[r].set(R[r]);
         }
     };
-    pc_walk<ST, L>(raw, ld, producer, c, !chain_lds, t0, nsb, cons, prod);
+    pc_walk<ST, L>(raw, ld, producer, c, t0, nsb, cons, prod);
 
     if (!producer && seg == p.S - 1) {
         float *wf = p.w_final + (size_t)h * D * D;
@@ -1622,11 +1619,13 @@ LinearPlan linear_plan(const LinearShape &s)
     // Segment length: whole super-block periods (whole chunks), about one
     // workgroup per CU (longer segments lengthen the serial walk, shorter ones
     // the segment-start chain; 256 measured best on the d = 64 and d = 128
-    // workloads), at least 64 tokens.
+    // workloads), at least four super-blocks: with few heads, more and
+    // shorter segments would fill the chip but the chain, which grows with
+    // the number of segments, costs more than they save.
     const long long period = (s.chunk <= SB) ? (long long)(SB / s.chunk) * s.chunk : s.chunk;
     const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 256);
     long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : period;
-    if (seg < SB) seg = SB;
+    if (seg < 4 * SB) seg = 4 * SB;
     const int forced = env_int("TTT_LINEAR_SEG_TOKENS", 0);
     if (forced > 0) seg = forced;
     seg = (seg + period - 1) / period * period;
