@@ -79,8 +79,22 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p)
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Which tensors a kernel stages.
-enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
+// Which tensors a kernel stages; STAGE_SWZ: bf16 tiles use the swizzled
+// layout below instead of padded rows.
+enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8, STAGE_SWZ = 16 };
+
+// Swizzled position of the 4-column group starting at column col (a multiple
+// of 4) in row row of an unpadded bf16 tile: inside each 64-column group the
+// 8-column chunk index is XORed with a 3-bit function of row bits 0-2 and the
+// two 4-column halves are exchanged on row bit 3.  The row fragments (16 rows,
+// 4 columns each), the transposing reads (4 rows x 16 columns per 16 lanes)
+// and the 16-byte stores then spread over the banks.  A 4-column group is
+// never split, so every 8-byte access stays contiguous.
+__device__ __forceinline__ int swz(int row, int col)
+{
+    const int v = ((row & 3) << 1) | ((row >> 2) & 1), hs = (row >> 3) & 1;
+    return (col & ~63) | ((((col >> 3) & 7) ^ v) << 3) | ((((col >> 2) & 1) ^ hs) << 2);
+}
 
 // LDS image of one 64-token super-block.  bf16: token-major tiles; fragments
 // that need four consecutive tokens of one feature come from the transposing
@@ -89,7 +103,8 @@ enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8 };
 template <typename E, int D, int ST> struct alignas(16) SbTile {
     static constexpr bool TR = sizeof(E) == 2;
     static constexpr bool LQ = (ST & STAGE_Q) != 0, LK = (ST & STAGE_K) != 0, LV = (ST & STAGE_V) != 0;
-    static constexpr int RP = D + (TR ? 8 : 4);  // token-major row pitch
+    static constexpr bool SW = TR && (ST & STAGE_SWZ) != 0;
+    static constexpr int RP = SW ? D : D + (TR ? 8 : 4);  // token-major row pitch
     static constexpr int FP = SB + 4;            // feature-major row pitch (fp32)
     E qs[LQ ? SB : 1][RP];
     E ks[(LK && TR) ? SB : 1][RP];
@@ -101,16 +116,21 @@ template <typename E, int D, int ST> struct alignas(16) SbTile {
 
 // Row fragment (rows = tokens of tile i, contraction over features 16r..16r+15):
 // lane (m, g) gets X[16i + m][16r + 4g + j].
+// column of the 4-column group at col in row row of a token-major tile
+template <bool SW> __device__ __forceinline__ int tcol(int row, int col) { return SW ? swz(row, col) : col; }
+
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type q_row(const SbTile<E, D, ST> &t, int i, int r, int m, int g)
 {
-    return load4<E>(&t.qs[16 * i + m][16 * r + 4 * g]);
+    constexpr bool SW = SbTile<E, D, ST>::SW;
+    return load4<E>(&t.qs[16 * i + m][tcol<SW>(16 * i + m, 16 * r + 4 * g)]);
 }
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type k_row(const SbTile<E, D, ST> &t, int i, int r, int m, int g)
 {
+    constexpr bool SW = SbTile<E, D, ST>::SW;
     if constexpr (SbTile<E, D, ST>::TR) {
-        return load4<E>(&t.ks[16 * i + m][16 * r + 4 * g]);
+        return load4<E>(&t.ks[16 * i + m][tcol<SW>(16 * i + m, 16 * r + 4 * g)]);
     } else {
         f32x4 x;
 #pragma unroll
@@ -124,16 +144,20 @@ __device__ __forceinline__ typename Frag<E>::type k_row(const SbTile<E, D, ST> &
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type k_tok(const SbTile<E, D, ST> &t, int i, int c, int m, int g)
 {
+    constexpr bool SW = SbTile<E, D, ST>::SW;
+    const int row = 16 * i + 4 * g + (m >> 2);
     if constexpr (SbTile<E, D, ST>::TR)
-        return lds_read_tr(&t.ks[16 * i + 4 * g + (m >> 2)][16 * c + 4 * (m & 3)]);
+        return lds_read_tr(&t.ks[row][tcol<SW>(row, 16 * c + 4 * (m & 3))]);
     else
         return load4<E>(&t.kt[16 * c + m][16 * i + 4 * g]);
 }
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type v_tok(const SbTile<E, D, ST> &t, int i, int c, int m, int g)
 {
+    constexpr bool SW = SbTile<E, D, ST>::SW;
+    const int row = 16 * i + 4 * g + (m >> 2);
     if constexpr (SbTile<E, D, ST>::TR)
-        return lds_read_tr(&t.vs[16 * i + 4 * g + (m >> 2)][16 * c + 4 * (m & 3)]);
+        return lds_read_tr(&t.vs[row][tcol<SW>(row, 16 * c + 4 * (m & 3))]);
     else
         return load4<E>(&t.vt[16 * c + m][16 * i + 4 * g]);
 }
@@ -141,19 +165,21 @@ __device__ __forceinline__ typename Frag<E>::type v_tok(const SbTile<E, D, ST> &
 // Transformed keys Kt = T K of one super-block, shared by the waves: each wave
 // writes its column block (accumulator layout), every wave reads row
 // fragments.  bf16: feature-major, 8-byte writes, transposing reads.
-template <typename E, int D> struct alignas(16) KtTile;
-template <int D> struct alignas(16) KtTile<__bf16, D> {
-    __bf16 fm[D][SB + 8];
+template <typename E, int D, bool SW = false> struct alignas(16) KtTile;
+template <int D, bool SW> struct alignas(16) KtTile<__bf16, D, SW> {
+    __bf16 fm[D][SW ? SB : SB + 8];
     __device__ __forceinline__ void put(int c, int i, f32x4 x, int m, int g)
     {
-        store4<__bf16>(&fm[16 * c + m][16 * i + 4 * g], to_bf16x4(x));
+        const int row = 16 * c + m;
+        store4<__bf16>(&fm[row][tcol<SW>(row, 16 * i + 4 * g)], to_bf16x4(x));
     }
     __device__ __forceinline__ bf16x4 row(int i, int r, int m, int g) const
     {
-        return lds_read_tr(&fm[16 * r + 4 * g + (m >> 2)][16 * i + 4 * (m & 3)]);
+        const int rr = 16 * r + 4 * g + (m >> 2);
+        return lds_read_tr(&fm[rr][tcol<SW>(rr, 16 * i + 4 * (m & 3))]);
     }
 };
-template <int D> struct alignas(16) KtTile<float, D> {
+template <int D, bool SW> struct alignas(16) KtTile<float, D, SW> {
     float tm[SB][D + 4];
     __device__ __forceinline__ void put(int c, int i, f32x4 x, int m, int g)
     {
@@ -221,16 +247,24 @@ template <typename E, int D, int ST, int PD, int NT> struct SbLoader {
                                                   re, (int)(threadIdx.x & (SB - 1)) * 4, tb0 * 4, 0));
     }
 
+    // A 16-byte piece (8 columns) in the swizzled layout: its chunk moves and
+    // its two 4-column halves swap on row bit 3.
+    static __device__ __forceinline__ u32x4 halves(u32x4 x, int r)
+    {
+        return ((r >> 3) & 1) ? u32x4{x[2], x[3], x[0], x[1]} : x;
+    }
     // Write slot s to LDS.
     __device__ __forceinline__ void commit(int s, Tile &tl)
     {
+        constexpr bool SW = Tile::SW;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int r = row[i], c = PE * col[i];
-            if (LQ) *reinterpret_cast<u32x4 *>(&tl.qs[r][c]) = vq[s][i];
+            const int r = row[i], c0 = PE * col[i];
+            const int c = SW ? (swz(r, c0) & ~7) : c0;
+            if (LQ) *reinterpret_cast<u32x4 *>(&tl.qs[r][c]) = SW ? halves(vq[s][i], r) : vq[s][i];
             if (LK) {
                 if constexpr (TR) {
-                    *reinterpret_cast<u32x4 *>(&tl.ks[r][c]) = vk[s][i];
+                    *reinterpret_cast<u32x4 *>(&tl.ks[r][c]) = SW ? halves(vk[s][i], r) : vk[s][i];
                 } else {
                     const f32x4 x = __builtin_bit_cast(f32x4, vk[s][i]);
 #pragma unroll
@@ -239,7 +273,7 @@ template <typename E, int D, int ST, int PD, int NT> struct SbLoader {
             }
             if (LV) {
                 if constexpr (TR) {
-                    *reinterpret_cast<u32x4 *>(&tl.vs[r][c]) = vv[s][i];
+                    *reinterpret_cast<u32x4 *>(&tl.vs[r][c]) = SW ? halves(vv[s][i], r) : vv[s][i];
                 } else {
                     const f32x4 x = __builtin_bit_cast(f32x4, vv[s][i]);
 #pragma unroll
@@ -890,12 +924,12 @@ template <int ST> using PcLoader = SbLoader<__bf16, 64, ST, 1, 128>;
 
 // Producer results for one super-block (replay).
 template <bool LT> struct alignas(16) PcRepDer {
-    KtTile<__bf16, LT ? 64 : 16> kt;  // T K, feature-major
+    KtTile<__bf16, LT ? 64 : 16, true> kt;  // T K, feature-major (swizzled)
     bf16x4 ab[10][64];                // A_ij (pair-block indices 6..15)
 };
 // Producer results for one super-block (summary, b < 64 only).
 template <bool LT> struct alignas(16) PcSumDer {
-    KtTile<__bf16, LT ? 64 : 16> kt;
+    KtTile<__bf16, LT ? 64 : 16, true> kt;
     f32x4 kc[LT ? 4 : 1][4][64];  // T K by column block, accumulator order
 };
 
@@ -1105,7 +1139,7 @@ __device__ __forceinline__ void pc_chain(f32x4 (&R)[4], const LinParams &p, int 
 // ring; the consumers apply R <- R - P_s R + B_s.  One barrier per step on
 // both sides.
 struct alignas(16) PcChainStage {
-    __bf16 P[2][64][72];
+    __bf16 P[2][64][64];  // swizzled rows
     f32x4 B[2][4][4][64];
 };
 
@@ -1132,8 +1166,10 @@ __device__ __forceinline__ void pc_chain_stage(const LinParams &p, int h, int ns
     auto commit = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int piece = lane + 64 * i;
-            *reinterpret_cast<u32x4 *>(&cs.P[buf][piece >> 3][(piece & 7) * 8]) = vp[i];
+            const int piece = lane + 64 * i, r = piece >> 3;
+            const u32x4 x = vp[i];
+            *reinterpret_cast<u32x4 *>(&cs.P[buf][r][swz(r, (piece & 7) * 8) & ~7]) =
+                ((r >> 3) & 1) ? u32x4{x[2], x[3], x[0], x[1]} : x;
         }
         f32x4 *Bd = &cs.B[buf][0][0][0];
 #pragma unroll
@@ -1183,7 +1219,7 @@ __device__ __forceinline__ void pc_chain_lds(f32x4 (&R)[4], int nsteps, const Pc
         for (int r = 0; r < 4; ++r) {
             bf16x4 PA[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) PA[q] = load4<__bf16>(&cs.P[buf][16 * r + m][16 * q + 4 * g]);
+            for (int q = 0; q < 4; ++q) PA[q] = load4<__bf16>(&cs.P[buf][16 * r + m][swz(16 * r + m, 16 * q + 4 * g)]);
             R[r] = R[r] + cs.B[buf][c][r][lane] - mma_state_b<__bf16, 4>(zero4(), PA, Ws);
         }
         step(s);
@@ -1248,7 +1284,7 @@ __global__ __launch_bounds__(512) void lin_summary_pc(LinParams p)
     typedef bf16x4 F;
     constexpr int D = 64, ND = 4, L = PcCfg<CH>::L;
     constexpr bool LT = MSE && PcCfg<CH>::MULTI;
-    constexpr int ST = STAGE_K | STAGE_V | STAGE_E;
+    constexpr int ST = STAGE_K | STAGE_V | STAGE_E | STAGE_SWZ;
     __shared__ SbTile<E, D, ST> raw[PC_NR];
     __shared__ PcSumDer<LT> der[LT ? 2 : 1];
     __shared__ PcLShare ls;
@@ -1394,7 +1430,7 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
     typedef bf16x4 F;
     constexpr int D = 64, ND = 4, L = PcCfg<CH>::L;
     constexpr bool LT = MSE && PcCfg<CH>::MULTI;
-    constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E;
+    constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E | STAGE_SWZ;
     __shared__ SbTile<E, D, ST> raw[PC_NR];
     // the chain's staging and the producers' results are never live together
     __shared__ union {
