@@ -989,23 +989,22 @@ template <int CH> __host__ __device__ constexpr bool l_nonzero(int b)
     return (16 * blk_j(b)) / CH < (16 * blk_i(b)) / CH;
 }
 
-template <int K, int CH, int ST>
-__device__ __forceinline__ void pc_lshare_put(const SbTile<__bf16, 64, ST> &t, const f32x4 *et, PcLShare &ls,
-                                              int n, int lane, int m, int g)
+// Producer wave K's nonzero blocks among K and K + 4, from the key rows.
+template <int K, int CH>
+__device__ __forceinline__ void pc_lshare_put(const bf16x4 (&Kr)[4][4], const f32x4 *et, PcLShare &ls, int n,
+                                              int lane)
 {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int b = K + 4 * q;
         if (b >= 6 || !l_nonzero<CH>(b)) continue;
         const int i = blk_i(b), j = blk_j(b);
-        bf16x4 Ki[4], Kj[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Ki[r] = k_row(t, i, r, m, g);
-            Kj[r] = k_row(t, j, r, m, g);
-        }
-        ls.blk[n & 1][b][lane] = to_bf16x4(mma_b<bf16x4, 4>(zero4(), Kj, Ki) * (-et[j]));
+        ls.blk[n & 1][b][lane] = to_bf16x4(mma_b<bf16x4, 4>(zero4(), Kr[j], Kr[i]) * (-et[j]));
     }
+}
+// Count the wave in once its LDS writes are done.
+__device__ __forceinline__ void pc_lshare_signal(PcLShare &ls, int lane)
+{
     if (lane == 0) __hip_atomic_fetch_add(&ls.count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
@@ -1041,21 +1040,26 @@ __device__ __forceinline__ void substitute_ch(f32x4 *X, const bf16x4 *Ln)
 }
 
 // Producer wave K's share of one super-block (replay): its A_ij blocks and,
-// for b < 64 with several chunks, its column block of T K.
+// for b < 64 with several chunks, its column block of T K.  All reads and the
+// independent products come first; the one wait (for the other producers'
+// blocks) comes last.
 template <int K, bool LT, int CH, int ST, typename Der>
 __device__ __forceinline__ void pc_derive_rep(const SbTile<__bf16, 64, ST> &t, Der &dv, PcLShare &ls, int n,
                                               int len, int lane, int m, int g)
 {
     f32x4 et[4];
     load_eta(t, len, g, et);
-    if constexpr (LT) pc_lshare_put<K, CH>(t, et, ls, n, lane, m, g);
     bf16x4 Kr[4][4];
     pc_krows(t, Kr, m, g);
-    pc_ablocks<K>(t, Kr, et, dv, lane, m, g);
+    f32x4 Kc[4];
     if constexpr (LT) {
-        f32x4 Kc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) Kc[i] = to_f32x4(k_tok(t, i, K, m, g));
+        pc_lshare_put<K, CH>(Kr, et, ls, n, lane);
+    }
+    pc_ablocks<K>(t, Kr, et, dv, lane, m, g);
+    if constexpr (LT) {
+        pc_lshare_signal(ls, lane);
         bf16x4 Ln[6];
         pc_lshare_get<CH>(ls, n, Ln, lane);
         substitute_ch<CH>(Kc, Ln);
@@ -1072,10 +1076,13 @@ __device__ __forceinline__ void pc_derive_sum(const SbTile<__bf16, 64, ST> &t, D
 {
     f32x4 et[4];
     load_eta(t, len, g, et);
-    pc_lshare_put<K, CH>(t, et, ls, n, lane, m, g);
+    bf16x4 Kr[4][4];
+    pc_krows(t, Kr, m, g);
     f32x4 Kc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) Kc[i] = to_f32x4(k_tok(t, i, K, m, g));
+    pc_lshare_put<K, CH>(Kr, et, ls, n, lane);
+    pc_lshare_signal(ls, lane);
     bf16x4 Ln[6];
     pc_lshare_get<CH>(ls, n, Ln, lane);
     substitute_ch<CH>(Kc, Ln);
