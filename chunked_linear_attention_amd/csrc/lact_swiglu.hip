@@ -279,12 +279,14 @@ __global__ __launch_bounds__(256) void lact_prep_weights(LactParams p)
 // ---------------------------------------------------------------------------
 constexpr int FBK = 32, FPITCH = FBK + 8, FPD = 4;  // k step, LDS pitch, register stages
 
+constexpr int F2PITCH = 64 + 16;  // W2 slice rows: the transposing reads of 16 lanes hit distinct banks
+
 struct FwdGradLds {
     bf16 ak[2][128][FPITCH];   // K tile
     bf16 ay[2][128][FPITCH];   // dY tile
     bf16 b1[2][64][FPITCH];    // W1 rows of the slice
     bf16 b3[2][64][FPITCH];    // W3 rows of the slice
-    bf16 b2[2][64][FPITCH];    // W2 columns of the slice (transposed on the way in)
+    bf16 b2[2][FBK][F2PITCH];  // W2 rows (k) of the slice, as stored
 };
 
 __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slot)
@@ -355,9 +357,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
         }
         st16(&L.b1[buf][brow][bcol], r1[s]);
         st16(&L.b3[buf][brow][bcol], r3[s]);
-        const bf16x8 w = as_bf8(r2[s]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) L.b2[buf][hcol + j][orow] = w[j];
+        st16(&L.b2[buf][orow][hcol], r2[s]);
     };
     // wave w: tokens 32 w .. 32 w + 31 (2 m-tiles), hidden 0..63 of the slice (4 n-tiles)
     f32x4 a1[2][4], a3[2][4], a2[2][4];
@@ -377,17 +377,25 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
             issue(j, st + FPD);
             commit((j + 1) % FPD, (j + 1) & 1);
             const int buf = j & 1;
+            // K x W1/W3: natural k order (8 consecutive k per lane).  dY x W2:
+            // W2's fragments come from the transposing read (k = 4g + j and
+            // 16 + 4g + j), and dY's use the same k order.
             bf16x8 fk[2], fy[2], f1[4], f3[4], f2[4];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                fk[i] = as_bf8(ld16(&L.ak[buf][wave * 32 + 16 * i + mm][8 * g]));
-                fy[i] = as_bf8(ld16(&L.ay[buf][wave * 32 + 16 * i + mm][8 * g]));
+                const int row = wave * 32 + 16 * i + mm;
+                fk[i] = as_bf8(ld16(&L.ak[buf][row][8 * g]));
+                const bf16x4 y0 = load4<bf16>(&L.ay[buf][row][4 * g]);
+                const bf16x4 y1 = load4<bf16>(&L.ay[buf][row][16 + 4 * g]);
+                fy[i] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 f1[q] = as_bf8(ld16(&L.b1[buf][16 * q + mm][8 * g]));
                 f3[q] = as_bf8(ld16(&L.b3[buf][16 * q + mm][8 * g]));
-                f2[q] = as_bf8(ld16(&L.b2[buf][16 * q + mm][8 * g]));
+                const bf16x4 w0 = lds_read_tr(&L.b2[buf][4 * g + (mm >> 2)][16 * q + 4 * (mm & 3)]);
+                const bf16x4 w1 = lds_read_tr(&L.b2[buf][16 + 4 * g + (mm >> 2)][16 * q + 4 * (mm & 3)]);
+                f2[q] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             if (st < nst) {
 #pragma unroll

@@ -93,6 +93,18 @@ __device__ __forceinline__ f32x4 mma32z(f32x4 acc, bf16x4 a0, bf16x4 b0)
 }
 __device__ __forceinline__ f32x4 mma32z(f32x4 acc, f32x4 a0, f32x4 b0) { return mma16(acc, a0, b0); }
 
+// Transposing read (16-bit elements): within each group of 16 lanes, lane i
+// slot j receives the element that lane 4j + i/4 would read at slot i%4.
+// Lane (m, g) pointing at row 4g + m/4, column c0 + 4(m%4) of a row-major
+// tile therefore receives tile[4g + j][c0 + m], j = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p)
+{
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
+    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) v4bf *)((__attribute__((address_space(3))) char *)p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // ---- workgroup placement ------------------------------------------------------
 // Workgroups are dealt to the 8 XCDs round-robin (XCD = block index mod 8),
 // and each XCD has its own L2.  Renumber blocks so that logical blocks

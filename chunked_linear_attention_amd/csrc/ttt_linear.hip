@@ -67,18 +67,6 @@ struct LinParams {
 
 constexpr int SB = 64;  // tokens per super-block tile (four 16-token tiles)
 
-// Transposing read (16-bit elements): within each group of 16 lanes, lane i
-// slot j receives the element that lane 4j + i/4 would read at slot i%4.
-// Lane (m, g) pointing at row 4g + m/4, column c0 + 4(m%4) of a row-major
-// tile therefore receives tile[4g + j][c0 + m], j = 0..3.
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p)
-{
-    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf;
-    const v4bf r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) v4bf *)((__attribute__((address_space(3))) char *)p));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
 // Which tensors a kernel stages; STAGE_SWZ: bf16 tiles use the swizzled
 // layout below instead of padded rows.
 enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8, STAGE_SWZ = 16 };
