@@ -1129,14 +1129,32 @@ __device__ __forceinline__ void pc_chain(f32x4 (&R)[4], const LinParams &p, int 
     }
 }
 
-// Segment-start chain staged through LDS (MSE): the producers load P_s
-// (row-major) and B_s (accumulator order) four steps ahead into a two-entry
-// ring; the consumers apply R <- R - P_s R + B_s.  One barrier per step on
-// both sides.
+// Segment-start chain staged through LDS (MSE): producer wave k loads P_s
+// (row-major) and B_s (accumulator order) of the steps s = k (mod 4), four
+// steps ahead in registers, and commits each into a four-entry LDS ring as
+// soon as the consumers are done with that entry's previous step; the
+// consumers apply R <- R - P_s R + B_s.  The two sides meet through LDS
+// counters, not workgroup barriers: ready[e] holds 1 + the step last
+// committed into entry e, done[e] counts the consumer waves' reads of that
+// entry.  Entry e only ever holds the steps s = e (mod 4), so the commit of
+// step s waits for 4 * (s / 4) reads of its entry, which are the reads of
+// the steps before it in that entry; those steps were fed by the same wave's
+// earlier commits, and a consumer step waits only on its own commit, so
+// every wait ends.
 struct alignas(16) PcChainStage {
-    __bf16 P[2][64][64];  // swizzled rows
-    f32x4 B[2][4][4][64];
+    __bf16 P[4][64][64];  // swizzled rows
+    f32x4 B[4][4][4][64];
+    unsigned ready[4];
+    unsigned done[4];
 };
+
+__device__ __forceinline__ void pc_chain_init(PcChainStage &cs)
+{
+    if (threadIdx.x < 4) {
+        cs.ready[threadIdx.x] = 0u;
+        cs.done[threadIdx.x] = 0u;
+    }
+}
 
 template <typename Mid>
 __device__ __forceinline__ void pc_chain_stage(const LinParams &p, int h, int nsteps, PcChainStage &cs, int k,
@@ -1158,67 +1176,83 @@ __device__ __forceinline__ void pc_chain_stage(const LinParams &p, int h, int ns
 #pragma unroll
         for (int i = 0; i < 16; ++i) vb[i] = B[lane + 64 * i];
     };
-    auto commit = [&](int buf) {
+    auto commit = [&](int e) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int piece = lane + 64 * i, r = piece >> 3;
             const u32x4 x = vp[i];
-            *reinterpret_cast<u32x4 *>(&cs.P[buf][r][swz(r, (piece & 7) * 8) & ~7]) =
+            *reinterpret_cast<u32x4 *>(&cs.P[e][r][swz(r, (piece & 7) * 8) & ~7]) =
                 ((r >> 3) & 1) ? u32x4{x[2], x[3], x[0], x[1]} : x;
         }
-        f32x4 *Bd = &cs.B[buf][0][0][0];
+        f32x4 *Bd = &cs.B[e][0][0][0];
 #pragma unroll
         for (int i = 0; i < 16; ++i) Bd[lane + 64 * i] = vb[i];
     };
+    lds_barrier();  // counters initialised
     // mid() (the wave's first super-block load) follows the wave's last chain
     // commit: the chain's loads are not queued behind super-block loads, the
     // wave has no chain wait left that would cover it, and the super-blocks
-    // are requested during the chain's last four steps, when they are next
-    // needed
+    // are requested during the chain's last steps, when they are next needed
     if (k < nsteps)
         issue(k);
     else
         mid();
-    if (k == 0) {
-        commit(0);
-        if (4 < nsteps)
-            issue(4);
+    for (int s = k; s < nsteps; s += 4) {
+        // entry s % 4 is free once all four consumers are done with step s - 4
+        if (s >= 4)
+            while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&cs.done[s & 3], __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_WORKGROUP)) <
+                   4u * (unsigned)(s >> 2))
+                __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        commit(s & 3);
+        if (lane == 0)
+            __hip_atomic_store(&cs.ready[s & 3], (unsigned)(s + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (s + 4 < nsteps)
+            issue(s + 4);
         else
             mid();
-    }
-    lds_barrier();
-    for (int s = 0; s < nsteps; ++s) {
-        // stage step s + 1 into buffer (s + 1) & 1, then load step s + 5
-        if (((s + 1) & 3) == k && s + 1 < nsteps) {
-            commit((s + 1) & 1);
-            if (s + 5 < nsteps)
-                issue(s + 5);
-            else
-                mid();
-        }
-        lds_barrier();
     }
 }
 
 template <typename Step>
-__device__ __forceinline__ void pc_chain_lds(f32x4 (&R)[4], int nsteps, const PcChainStage &cs, int c, int lane,
+__device__ __forceinline__ void pc_chain_lds(f32x4 (&R)[4], int nsteps, PcChainStage &cs, int c, int lane,
                                              int m, int g, Step &&step)
 {
-    lds_barrier();  // step 0 staged
+    lds_barrier();  // counters initialised
     for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
+        const int e = s & 3;
+        while (__builtin_amdgcn_readfirstlane(
+                   __hip_atomic_load(&cs.ready[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) !=
+               (unsigned)(s + 1))
+            __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // the four row blocks side by side: consecutive MFMAs are independent
+        bf16x4 PA[4][4];
+        f32x4 Bs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) PA[r][q] = load4<__bf16>(&cs.P[e][16 * r + m][swz(16 * r + m, 16 * q + 4 * g)]);
+            Bs[r] = cs.B[e][c][r][lane];
+        }
         SplitFrag<__bf16> Ws[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ws[r].set(R[r]);
+        f32x4 PR[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            bf16x4 PA[4];
+        for (int q = 0; q < 4; q += 2)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) PA[q] = load4<__bf16>(&cs.P[buf][16 * r + m][swz(16 * r + m, 16 * q + 4 * g)]);
-            R[r] = R[r] + cs.B[buf][c][r][lane] - mma_state_b<__bf16, 4>(zero4(), PA, Ws);
-        }
+            for (int r = 0; r < 4; ++r) PR[r] = mma32(PR[r], PA[r][q], PA[r][q + 1], Ws[q].hi, Ws[q + 1].hi);
+#pragma unroll
+        for (int q = 0; q < 4; q += 2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) PR[r] = mma32(PR[r], PA[r][q], PA[r][q + 1], Ws[q].lo, Ws[q + 1].lo);
+        // this wave's reads of entry e are complete: release it
+        if (lane == 0) __hip_atomic_fetch_add(&cs.done[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[r] = R[r] + Bs[r] - PR[r];
         step(s);
-        lds_barrier();
     }
 }
 
@@ -1426,14 +1460,17 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
     constexpr int D = 64, ND = 4, L = PcCfg<CH>::L;
     constexpr bool LT = MSE && PcCfg<CH>::MULTI;
     constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E | STAGE_SWZ;
-    __shared__ SbTile<E, D, ST> raw[PC_NR];
-    // the chain's staging and the producers' results are never live together
+    // the chain's staging and the walk's tiles are never live together
     __shared__ union {
-        PcRepDer<LT> der[2];
+        struct {
+            SbTile<E, D, ST> raw[PC_NR];
+            PcRepDer<LT> der[2];
+        } w;
         PcChainStage cs;
     } u;
     __shared__ PcLShare ls;
-    PcRepDer<LT> *der = u.der;
+    SbTile<E, D, ST> *raw = u.w.raw;
+    PcRepDer<LT> *der = u.w.der;
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const bool producer = wave >= 4;
@@ -1450,14 +1487,17 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
     SplitFrag<E> Rs[ND];
     const bool chain_lds = MSE && seg > 0;
     if (threadIdx.x == 0) ls.count = 0;
+    if (chain_lds) pc_chain_init(u.cs);
     if (producer) {
         ld.init((c & 1) * 64 + lane, p.q, p.k, p.v, p.eta, h, T, tend);
         // the chain's loads go first; each wave's first super-block load
-        // follows its last chain load
-        if (chain_lds)
+        // follows its last chain commit
+        if (chain_lds) {
             pc_chain_stage(p, h, seg, u.cs, c, lane, [&] { ld.issue(0, t0 + (c >> 1) * L); });
-        else
+            lds_barrier();  // the consumers are done with the staging, which the tiles overlay
+        } else {
             ld.issue(0, t0 + (c >> 1) * L);
+        }
         pc_first_commit<ST, L>(raw, ld, c);
     } else {
         // w_init itself, or the summary's copy of it when w_final is the same
@@ -1468,10 +1508,12 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) R[r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
         if (seg > 0) {
-            if (MSE)
+            if (MSE) {
                 pc_chain_lds(R, seg, u.cs, c, lane, m, g, [](int) {});
-            else
+                lds_barrier();  // pairs with the producers' barrier after their staging
+            } else {
                 pc_chain<false>(R, p, h, seg, c, lane, m, g, [](int) {});
+            }
         }
 #pragma unroll
         for (int r = 0; r < ND; ++r) Rs[r].set(R[r]);
