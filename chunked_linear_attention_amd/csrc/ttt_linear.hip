@@ -938,38 +938,52 @@ __device__ __forceinline__ void pc_krows(const SbTile<__bf16, 64, ST> &t, bf16x4
         for (int r = 0; r < 4; ++r) Kr[i][r] = k_row(t, i, r, m, g);
 }
 
-// The A_ij blocks producer wave PC computes: indices 6 + PC + 4k.
-template <int PC, int ST, typename Der>
+// Producer wave owning A_ij block b (6..15).  Blocks of one row block i go
+// to one wave where possible, so its query rows are read once; with the six
+// shared L_ij blocks of b = 16 (waves 0 and 1 compute two of them, waves 2
+// and 3 one) every wave ends up with four blocks, otherwise with three or two.
+template <bool ALL_L> __host__ __device__ constexpr int a_owner(int b)
+{
+    if (ALL_L) return (b == 7 || b == 8) ? 0 : (b == 6 || b == 15) ? 1 : (b >= 12) ? 2 : 3;
+    return (b >= 12 && b <= 14) ? 0 : (b >= 9 && b <= 11) ? 1 : (b == 6 || b == 15) ? 2 : 3;
+}
+
+template <int PC, bool ALL_L, int ST, typename Der>
 __device__ __forceinline__ void pc_ablocks(const SbTile<__bf16, 64, ST> &t, const bf16x4 (&Kr)[4][4],
                                            const f32x4 *et, Der &dv, int lane, int m, int g)
 {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const int b = 6 + PC + 4 * k;
-        if (b > 15) break;
-        const int i = blk_i(b), j = blk_j(b);
+    for (int i = 0; i < 4; ++i) {
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j <= i; ++j) any |= a_owner<ALL_L>(ablk(i, j)) == PC;
+        if (!any) continue;
         bf16x4 Qi[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) Qi[r] = q_row(t, i, r, m, g);
-        f32x4 acc = mma_b<bf16x4, 4>(zero4(), Kr[j], Qi) * et[j];
-        if (i == j) {
 #pragma unroll
-            for (int x = 0; x < 4; ++x) acc[x] = (4 * g + x <= m) ? acc[x] : 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const int b = ablk(i, j);
+            if (a_owner<ALL_L>(b) != PC) continue;
+            f32x4 acc = mma_b<bf16x4, 4>(zero4(), Kr[j], Qi) * et[j];
+            if (i == j) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[x] = (4 * g + x <= m) ? acc[x] : 0.f;
+            }
+            dv.ab[b - 6][lane] = to_bf16x4(acc);
         }
-        dv.ab[b - 6][lane] = to_bf16x4(acc);
     }
 }
 
-// Shared -L_ij blocks (b < 64 with several chunks per super-block).  Producer
-// wave K computes the nonzero blocks among indices K and K + 4, writes them to
-// LDS and counts itself in; the others wait for all four before the forward
-// substitution of T K.  Every producer wave reaches its count before it waits,
-// so the wait ends.  Two buffers by super-block parity: the consumers apply
-// the blocks of their super-block to V (T V) while the producers fill the
-// next one's.
+// -L_ij blocks (b < 64 with several chunks per super-block).  Every producer
+// wave computes all nonzero blocks in registers for its own substitution (a
+// few extra MFMAs instead of an exchange through LDS and a wait on the other
+// producers), and wave K writes blocks K and K + 4 to LDS for the consumers,
+// which apply them to V (T V).  Two buffers by super-block parity: the
+// consumers read the blocks of their super-block while the producers write
+// the next one's.
 struct alignas(16) PcLShare {
     bf16x4 blk[2][6][64];
-    unsigned count;
 };
 
 template <int CH> __host__ __device__ constexpr bool l_nonzero(int b)
@@ -977,23 +991,17 @@ template <int CH> __host__ __device__ constexpr bool l_nonzero(int b)
     return (16 * blk_j(b)) / CH < (16 * blk_i(b)) / CH;
 }
 
-// Producer wave K's nonzero blocks among K and K + 4, from the key rows.
 template <int K, int CH>
-__device__ __forceinline__ void pc_lshare_put(const bf16x4 (&Kr)[4][4], const f32x4 *et, PcLShare &ls, int n,
-                                              int lane)
+__device__ __forceinline__ void pc_lblocks(const bf16x4 (&Kr)[4][4], const f32x4 *et, PcLShare &ls, int n,
+                                           bf16x4 *Ln, int lane)
 {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int b = K + 4 * q;
-        if (b >= 6 || !l_nonzero<CH>(b)) continue;
+    for (int b = 0; b < 6; ++b) {
+        if (!l_nonzero<CH>(b)) continue;
         const int i = blk_i(b), j = blk_j(b);
-        ls.blk[n & 1][b][lane] = to_bf16x4(mma_b<bf16x4, 4>(zero4(), Kr[j], Kr[i]) * (-et[j]));
+        Ln[b] = to_bf16x4(mma_b<bf16x4, 4>(zero4(), Kr[j], Kr[i]) * (-et[j]));
+        if ((b & 3) == K) ls.blk[n & 1][b][lane] = Ln[b];
     }
-}
-// Count the wave in once its LDS writes are done.
-__device__ __forceinline__ void pc_lshare_signal(PcLShare &ls, int lane)
-{
-    if (lane == 0) __hip_atomic_fetch_add(&ls.count, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 template <int CH>
@@ -1002,15 +1010,6 @@ __device__ __forceinline__ void pc_lshare_read(const PcLShare &ls, int n, bf16x4
 #pragma unroll
     for (int b = 0; b < 6; ++b)
         if (l_nonzero<CH>(b)) Ln[b] = ls.blk[n & 1][b][lane];
-}
-template <int CH>
-__device__ __forceinline__ void pc_lshare_get(PcLShare &ls, int n, bf16x4 *Ln, int lane)
-{
-    const unsigned target = 4u * (n + 1);
-    while (__builtin_amdgcn_readfirstlane(
-               __hip_atomic_load(&ls.count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < target)
-        __builtin_amdgcn_s_sleep(1);
-    pc_lshare_read<CH>(ls, n, Ln, lane);
 }
 
 // Block forward substitution with the blocks that are zero for CH skipped.
@@ -1028,9 +1027,7 @@ __device__ __forceinline__ void substitute_ch(f32x4 *X, const bf16x4 *Ln)
 }
 
 // Producer wave K's share of one super-block (replay): its A_ij blocks and,
-// for b < 64 with several chunks, its column block of T K.  All reads and the
-// independent products come first; the one wait (for the other producers'
-// blocks) comes last.
+// for b < 64 with several chunks, its column block of T K.
 template <int K, bool LT, int CH, int ST, typename Der>
 __device__ __forceinline__ void pc_derive_rep(const SbTile<__bf16, 64, ST> &t, Der &dv, PcLShare &ls, int n,
                                               int len, int lane, int m, int g)
@@ -1040,16 +1037,14 @@ __device__ __forceinline__ void pc_derive_rep(const SbTile<__bf16, 64, ST> &t, D
     bf16x4 Kr[4][4];
     pc_krows(t, Kr, m, g);
     f32x4 Kc[4];
+    bf16x4 Ln[6];
     if constexpr (LT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Kc[i] = to_f32x4(k_tok(t, i, K, m, g));
-        pc_lshare_put<K, CH>(Kr, et, ls, n, lane);
+        pc_lblocks<K, CH>(Kr, et, ls, n, Ln, lane);
     }
-    pc_ablocks<K>(t, Kr, et, dv, lane, m, g);
+    pc_ablocks<K, LT && l_nonzero<CH>(0) && l_nonzero<CH>(5)>(t, Kr, et, dv, lane, m, g);
     if constexpr (LT) {
-        pc_lshare_signal(ls, lane);
-        bf16x4 Ln[6];
-        pc_lshare_get<CH>(ls, n, Ln, lane);
         substitute_ch<CH>(Kc, Ln);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dv.kt.put(K, i, Kc[i], m, g);
@@ -1069,10 +1064,8 @@ __device__ __forceinline__ void pc_derive_sum(const SbTile<__bf16, 64, ST> &t, D
     f32x4 Kc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) Kc[i] = to_f32x4(k_tok(t, i, K, m, g));
-    pc_lshare_put<K, CH>(Kr, et, ls, n, lane);
-    pc_lshare_signal(ls, lane);
     bf16x4 Ln[6];
-    pc_lshare_get<CH>(ls, n, Ln, lane);
+    pc_lblocks<K, CH>(Kr, et, ls, n, Ln, lane);
     substitute_ch<CH>(Kc, Ln);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1331,7 +1324,6 @@ __global__ __launch_bounds__(512) void lin_summary_pc(LinParams p)
     const int nsb = (tend - t0 + L - 1) / L;
 
     PcLoader<ST> ld;
-    if (threadIdx.x == 0) ls.count = 0;
     if (producer) {
         ld.init((c & 1) * 64 + lane, nullptr, p.k, p.v, p.eta, h, T, tend);
         ld.issue(0, t0 + (c >> 1) * L);
@@ -1486,7 +1478,6 @@ __global__ __launch_bounds__(512) void lin_replay_pc(LinParams p)
     f32x4 R[ND];
     SplitFrag<E> Rs[ND];
     const bool chain_lds = MSE && seg > 0;
-    if (threadIdx.x == 0) ls.count = 0;
     if (chain_lds) pc_chain_init(u.cs);
     if (producer) {
         ld.init((c & 1) * 64 + lane, p.q, p.k, p.v, p.eta, h, T, tend);
