@@ -23,15 +23,17 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           # keep packed fp32 instructions out of the generated code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the VALU work
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Per-source flags.  TTT-Linear: MFMA accumulators in VGPRs (no AGPR<->VGPR
+# copies around the VALU work on the state).  LaCT's GEMM tiles keep their
+# accumulators in AGPRs, which leaves the VGPRs to the load stages.
+FLAGS = {"ttt_linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -16,7 +16,7 @@
 // Kernels (one launch each):
 //   lact_prep     K^T and (-eta V)^T for all tokens; fp32 masters; bf16
 //                 weight copies for chunk 0.
-//   lact_fwdgrad  per (head, 128-token tile, 64-wide hidden slice): the three
+//   lact_fwdgrad  per (head, 128-token tile, 128-wide hidden slice): the three
 //                 products K W1^T, K W3^T, dY W2 share the d-long contraction;
 //                 the epilogue does the SwiGLU backward and writes G^T, dH1^T,
 //                 dH3^T (hidden-major, token-contiguous: the next GEMM's k).
@@ -55,7 +55,9 @@ __device__ __forceinline__ f32x4 mfma32(f32x4 acc, bf16x8 a, bf16x8 b)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
+// logistic function with the hardware reciprocal (about 1 ulp; the results are
+// rounded to bf16): 1 + e^-z = inf gives 0, e^-z = 0 gives 1
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 
 // ---------------------------------------------------------------------------
@@ -275,17 +277,19 @@ __global__ __launch_bounds__(256) void lact_prep_weights(LactParams p)
 }
 
 // ---------------------------------------------------------------------------
-// fwdgrad: per (head, 128-token tile, 64-wide hidden slice) of chunk c.
+// fwdgrad: per (head, 128-token tile, 128-wide hidden slice) of chunk c.  Four
+// waves as 2 x 2 tiles of 64 tokens x 64 hidden units, each holding all three
+// products (K W1^T, K W3^T, dY W2) of its tile: 48 MFMAs per 32-wide k step
+// for 20 fragment reads.
 // ---------------------------------------------------------------------------
-constexpr int FBK = 32, FPITCH = FBK + 8, FPD = 4;  // k step, LDS pitch, register stages
-
-constexpr int F2PITCH = 64 + 16;  // W2 slice rows: the transposing reads of 16 lanes hit distinct banks
+constexpr int FBK = 32, FPITCH = FBK + 8, FPD = 2;  // k step, LDS pitch, register stages (even, divides d / FBK)
+constexpr int F2PITCH = 128 + 16;  // W2 slice rows: transposing reads of 8 rows hit distinct banks
 
 struct FwdGradLds {
     bf16 ak[2][128][FPITCH];   // K tile
     bf16 ay[2][128][FPITCH];   // dY tile
-    bf16 b1[2][64][FPITCH];    // W1 rows of the slice
-    bf16 b3[2][64][FPITCH];    // W3 rows of the slice
+    bf16 b1[2][128][FPITCH];   // W1 rows of the slice
+    bf16 b3[2][128][FPITCH];   // W3 rows of the slice
     bf16 b2[2][FBK][F2PITCH];  // W2 rows (k) of the slice, as stored
 };
 
@@ -294,7 +298,8 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     __shared__ FwdGradLds L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
-    const int nslice = p.hid / 64;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nslice = p.hid / 128;
     const int ntile = p.cpad / 128;
     int bid = xcd_block(blockIdx.x, gridDim.x);
     const int sl = bid % nslice;
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     const int cstart = c * p.chunk;
     const int clen = min(p.chunk, p.Tkv - cstart);
     const int r0 = tt * 128;
-    const int h0 = sl * 64;
+    const int h0 = sl * 128;
     const int d = p.d;
     const bf16 *kh = p.k + ((long)h * p.Tkv + cstart) * d;
     const bf16 *vh = p.v + ((long)h * p.Tkv + cstart) * d;
@@ -314,55 +319,55 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     const bf16 *w2 = p.w2b + slot_off2(p, slot, h);
     const bool dot = (p.loss == 0);
 
-    int arow[2], acol[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pc = tid + 256 * i;
-        arow[i] = pc >> 2;
-        acol[i] = (pc & 3) * 8;
-    }
-    const int brow = tid >> 2, bcol = (tid & 3) * 8;  // W1/W3 slice rows
-    const int orow = tid >> 3, hcol = (tid & 7) * 8;  // W2: o row 0..31, 8 hidden columns
+    // 128 rows x 32 columns per operand and stage: rows tid/4 and 64 + tid/4,
+    // 8 columns each.  W2: k rows tid/16 and 16 + tid/16, 8 hidden columns.
+    const int lrow = tid >> 2, lcol = (tid & 3) * 8;
+    const int orow = tid >> 4, hcol = (tid & 15) * 8;
     float erow[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int t = r0 + arow[i];
+        const int t = r0 + lrow + 64 * i;
         erow[i] = (t < clen) ? (dot ? -eh[t] : 1.f) : 0.f;
     }
+    // d is a multiple of 128, so the k steps fill whole groups of FPD and
+    // every step computes: the loads, LDS writes and MFMAs of a step form one
+    // basic block and interleave
     const int nst = d / FBK;
-    const int ngroups = (nst + FPD - 1) / FPD;
-    B8 rk[FPD][2], ry[FPD][2], r1[FPD], r3[FPD], r2[FPD];
+    const int ngroups = nst / FPD;
+    B8 rk[FPD][2], ry[FPD][2], r1[FPD][2], r3[FPD][2], r2[FPD][2];
     auto issue = [&](int s, int st) {
         const int kk = min(st, nst - 1) * FBK;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int t = min(r0 + arow[i], clen - 1);
-            rk[s][i] = ld16(kh + (long)t * d + kk + acol[i]);
-            ry[s][i] = ld16((dot ? vh : dyh) + (long)t * d + kk + acol[i]);
+            const int t = min(r0 + lrow + 64 * i, clen - 1);
+            rk[s][i] = ld16(kh + (long)t * d + kk + lcol);
+            ry[s][i] = ld16((dot ? vh : dyh) + (long)t * d + kk + lcol);
+            r1[s][i] = ld16(w13 + (long)packed_row(h0 + lrow + 64 * i, 0) * d + kk + lcol);
+            r3[s][i] = ld16(w13 + (long)packed_row(h0 + lrow + 64 * i, 1) * d + kk + lcol);
+            r2[s][i] = ld16(w2 + (long)(kk + orow + 16 * i) * p.hid + h0 + hcol);
         }
-        r1[s] = ld16(w13 + (long)packed_row(h0 + brow, 0) * d + kk + bcol);
-        r3[s] = ld16(w13 + (long)packed_row(h0 + brow, 1) * d + kk + bcol);
-        r2[s] = ld16(w2 + (long)(kk + orow) * p.hid + h0 + hcol);
     };
     auto commit = [&](int s, int buf) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const bool ok = r0 + arow[i] < clen;
-            st16(&L.ak[buf][arow[i]][acol[i]], ok ? rk[s][i] : zero16());
+            const int row = lrow + 64 * i;
+            const bool ok = r0 + row < clen;
+            st16(&L.ak[buf][row][lcol], ok ? rk[s][i] : zero16());
             const bf16x8 vb = as_bf8(ry[s][i]);
             bf16x8 o;
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[j] = dot ? (bf16)((float)vb[j] * erow[i]) : (ok ? vb[j] : (bf16)0.f);
-            st16(&L.ay[buf][arow[i]][acol[i]], B8{__builtin_bit_cast(u32x4v, o)});
+            st16(&L.ay[buf][row][lcol], B8{__builtin_bit_cast(u32x4v, o)});
+            st16(&L.b1[buf][row][lcol], r1[s][i]);
+            st16(&L.b3[buf][row][lcol], r3[s][i]);
+            st16(&L.b2[buf][orow + 16 * i][hcol], r2[s][i]);
         }
-        st16(&L.b1[buf][brow][bcol], r1[s]);
-        st16(&L.b3[buf][brow][bcol], r3[s]);
-        st16(&L.b2[buf][orow][hcol], r2[s]);
     };
-    // wave w: tokens 32 w .. 32 w + 31 (2 m-tiles), hidden 0..63 of the slice (4 n-tiles)
-    f32x4 a1[2][4], a3[2][4], a2[2][4];
+    // wave (wm, wn): tokens 64 wm .. 64 wm + 63 (4 m-tiles), hidden 64 wn ..
+    // 64 wn + 63 of the slice (4 n-tiles)
+    f32x4 a1[4][4], a3[4][4], a2[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) a1[i][q] = a3[i][q] = a2[i][q] = zero4();
 
@@ -374,16 +379,15 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
 #pragma unroll
         for (int j = 0; j < FPD; ++j) {
             const int st = gi * FPD + j;
-            issue(j, st + FPD);
-            commit((j + 1) % FPD, (j + 1) & 1);
-            const int buf = j & 1;
-            // K x W1/W3: natural k order (8 consecutive k per lane).  dY x W2:
-            // W2's fragments come from the transposing read (k = 4g + j and
-            // 16 + 4g + j), and dY's use the same k order.
-            bf16x8 fk[2], fy[2], f1[4], f3[4], f2[4];
+            const int buf = j & 1;  // FPD is even: the LDS buffer is the k-step parity
+            // All fragments of the step first.  K x W1/W3: natural k order (8
+            // consecutive k per lane).  dY x W2: W2's fragments come from the
+            // transposing read (k = 4g + j and 16 + 4g + j), and dY's use the
+            // same k order.
+            bf16x8 fk[4], fy[4], f1[4], f3[4], f2[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = wave * 32 + 16 * i + mm;
+            for (int i = 0; i < 4; ++i) {
+                const int row = wm * 64 + 16 * i + mm;
                 fk[i] = as_bf8(ld16(&L.ak[buf][row][8 * g]));
                 const bf16x4 y0 = load4<bf16>(&L.ay[buf][row][4 * g]);
                 const bf16x4 y1 = load4<bf16>(&L.ay[buf][row][16 + 4 * g]);
@@ -391,32 +395,48 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                f1[q] = as_bf8(ld16(&L.b1[buf][16 * q + mm][8 * g]));
-                f3[q] = as_bf8(ld16(&L.b3[buf][16 * q + mm][8 * g]));
-                const bf16x4 w0 = lds_read_tr(&L.b2[buf][4 * g + (mm >> 2)][16 * q + 4 * (mm & 3)]);
-                const bf16x4 w1 = lds_read_tr(&L.b2[buf][16 + 4 * g + (mm >> 2)][16 * q + 4 * (mm & 3)]);
+                const int col = wn * 64 + 16 * q;
+                f1[q] = as_bf8(ld16(&L.b1[buf][col + mm][8 * g]));
+                f3[q] = as_bf8(ld16(&L.b3[buf][col + mm][8 * g]));
+                const bf16x4 w0 = lds_read_tr(&L.b2[buf][4 * g + (mm >> 2)][col + 4 * (mm & 3)]);
+                const bf16x4 w1 = lds_read_tr(&L.b2[buf][16 + 4 * g + (mm >> 2)][col + 4 * (mm & 3)]);
                 f2[q] = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            if (st < nst) {
+            // the loads and LDS writes of later steps go into the MFMAs' shadow
+            issue(j, st + FPD);
+            commit((j + 1) % FPD, (j + 1) & 1);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        a1[i][q] = mfma32(a1[i][q], fk[i], f1[q]);
-                        a3[i][q] = mfma32(a3[i][q], fk[i], f3[q]);
-                        a2[i][q] = mfma32(a2[i][q], fy[i], f2[q]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    a1[i][q] = mfma32(a1[i][q], fk[i], f1[q]);
+                    a3[i][q] = mfma32(a3[i][q], fk[i], f3[q]);
+                    a2[i][q] = mfma32(a2[i][q], fy[i], f2[q]);
+                }
+            // schedule: the fragment reads, then the 48 MFMAs with a global
+            // load or an LDS write after every second one
+            __builtin_amdgcn_sched_group_barrier(0x100, 28, 0);
+#pragma unroll
+            for (int x = 0; x < 10; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
+#pragma unroll
+            for (int x = 0; x < 10; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             lds_barrier();
         }
     }
-    // lane: tokens r0 + 32 wave + 16 i + 4 g + (0..3), hidden h0 + 16 q + mm.
+    // lane: tokens r0 + 64 wm + 16 i + 4 g + (0..3), hidden h0 + 64 wn + 16 q + mm.
     // Rows past the chunk have K = dY = 0, so every output there is 0.
     bf16 *gt = p.gt + (long)h * p.hid * p.cpad;
     bf16 *d1 = p.dh1t + (long)h * p.hid * p.cpad;
     bf16 *d3 = p.dh3t + (long)h * p.hid * p.cpad;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             f32x4 gv, v1, v3;
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
                 v3[j] = dg * act;
                 v1[j] = dg * z3 * (sg * (1.f + z1 * (1.f - sg)));
             }
-            const long off = (long)(h0 + 16 * q + mm) * p.cpad + r0 + wave * 32 + 16 * i + 4 * g;
+            const long off = (long)(h0 + wn * 64 + 16 * q + mm) * p.cpad + r0 + wm * 64 + 16 * i + 4 * g;
             store4<bf16>(gt + off, to_bf16x4(gv));
             store4<bf16>(d1 + off, to_bf16x4(v1));
             store4<bf16>(d3 + off, to_bf16x4(v3));
@@ -777,7 +797,7 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
             lact_apply2<<<dim3(s.NH * (s.d / 128) * ((clen + 127) / 128)), dim3(256), 0, st>>>(
                 p, clen, slot, 1, c);
         }
-        lact_fwdgrad<<<dim3(s.NH * (p.cpad / 128) * (s.hid / 64)), dim3(256), 0, st>>>(p, c, slot);
+        lact_fwdgrad<<<dim3(s.NH * (p.cpad / 128) * (s.hid / 128)), dim3(256), 0, st>>>(p, c, slot);
         lact_wgrad<<<dim3(s.NH * p.splitk * 3 * t13), dim3(256), 0, st>>>(p, c);
         lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst);
     }
