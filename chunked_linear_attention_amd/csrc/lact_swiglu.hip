@@ -109,11 +109,14 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
             rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
         }
     };
-    auto commit = [&](int s, int buf) {
+    // Past the last k step the stage holds zeros, so every step computes (the
+    // loads, LDS writes and MFMAs of a step stay in one basic block).
+    auto commit = [&](int s, int buf, int st) {
+        const bool live = st < nst;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            st16(&L.a[buf][lrow[i]][lcol], aok[i] ? ra[s][i] : zero16());
-            st16(&L.b[buf][lrow[i]][lcol], bok[i] ? rb[s][i] : zero16());
+            st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
+            st16(&L.b[buf][lrow[i]][lcol], (live && bok[i]) ? rb[s][i] : zero16());
         }
     };
     f32x4 acc[4][4];
@@ -127,28 +130,39 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
         issue(s, s);
         __builtin_amdgcn_sched_barrier(0);
     }
-    commit(0, 0);
+    commit(0, 0, 0);
     lds_barrier();
     for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
         for (int j = 0; j < GPD; ++j) {
             const int st = gi * GPD + j;
-            issue(j, st + GPD);
-            commit((j + 1) % GPD, (j + 1) & 1);
             const int buf = j & 1;
-            if (st < nst) {
+            // per 32-wide half: its fragments, then its MFMAs with the next
+            // steps' loads (first half) or LDS writes (second half) between them
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    bf16x8 af[4], bfr[4];
+            for (int kh = 0; kh < 2; ++kh) {
+                bf16x8 af[4], bfr[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        af[i] = as_bf8(ld16(&L.a[buf][wm * 64 + 16 * i + mm][32 * kh + 8 * g]));
-                        bfr[i] = as_bf8(ld16(&L.b[buf][wn * 64 + 16 * i + mm][32 * kh + 8 * g]));
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    af[i] = as_bf8(ld16(&L.a[buf][wm * 64 + 16 * i + mm][32 * kh + 8 * g]));
+                    bfr[i] = as_bf8(ld16(&L.b[buf][wn * 64 + 16 * i + mm][32 * kh + 8 * g]));
+                }
+                if (kh == 0)
+                    issue(j, st + GPD);
+                else
+                    commit((j + 1) % GPD, (j + 1) & 1, st + 1);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
+                    for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (kh == 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    else
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
                 }
             }
             lds_barrier();
@@ -689,10 +703,15 @@ static int lact_splitk(const LactShape &s, int clen)
 {
     const int t13 = (s.d / 128) * (s.hid / 128);
     const int tiles = s.NH * 3 * t13;
-    // Each split adds a 3 x hid x d fp32 partial per head that the update reads
-    // back; two splits balance that traffic against filling the CUs.
-    int sk = (256 + tiles - 1) / tiles;
-    if (sk > 2) sk = 2;
+    // Up to two workgroups per CU.  Each split adds a 3 x hid x d fp32 partial
+    // per head, written here and read back by the update: beyond two splits
+    // only while that stays within a tenth of the chunk's own token traffic
+    // (K and V read, G^T, dH1^T and dH3^T written and read).
+    int sk = 512 / tiles;
+    const long tok_bytes = (long)clen * (4L * s.d + 6L * s.hid);
+    const long split_bytes = 24L * s.hid * s.d;
+    const long cap = tok_bytes / (10 * split_bytes);
+    if (sk > (cap > 2 ? cap : 2)) sk = (int)(cap > 2 ? cap : 2);
     const int maxsk = (clen + 511) / 512;          // at least 512 tokens per split
     if (sk > maxsk) sk = maxsk;
     return sk < 1 ? 1 : sk;
