@@ -306,10 +306,19 @@ struct FwdGradLds {
     bf16 b3[2][128][FPITCH];   // W3 rows of the slice
     bf16 b2[2][FBK][F2PITCH];  // W2 rows (k) of the slice, as stored
 };
+// After the k loop: each wave's three 64 x 64 output tiles, hidden-major, rows
+// padded to 68 (34 dwords: the 16 rows a fragment write touches and the two
+// rows of a 16-lane read fall on distinct banks)
+constexpr int FOPITCH = 64 + 4;
+union FwdGradLdsAll {
+    FwdGradLds k;
+    bf16 out[4][3][64][FOPITCH];
+};
 
 __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slot)
 {
-    __shared__ FwdGradLds L;
+    __shared__ FwdGradLdsAll LA;
+    FwdGradLds &L = LA.k;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
@@ -444,11 +453,12 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
             lds_barrier();
         }
     }
-    // lane: tokens r0 + 64 wm + 16 i + 4 g + (0..3), hidden h0 + 64 wn + 16 q + mm.
-    // Rows past the chunk have K = dY = 0, so every output there is 0.
-    bf16 *gt = p.gt + (long)h * p.hid * p.cpad;
-    bf16 *d1 = p.dh1t + (long)h * p.hid * p.cpad;
-    bf16 *d3 = p.dh3t + (long)h * p.hid * p.cpad;
+    // lane: tokens 64 wm + 16 i + 4 g + (0..3), hidden 64 wn + 16 q + mm of the
+    // tile.  Rows past the chunk have K = dY = 0, so every output there is 0.
+    // The three outputs go through the wave's own LDS tiles (the k loop ended
+    // with a barrier, so the operand buffers are free) and leave as whole
+    // 128-byte rows of 64 tokens.
+    bf16(*st)[64][FOPITCH] = LA.out[wave];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -463,10 +473,23 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
                 v3[j] = dg * act;
                 v1[j] = dg * z3 * (sg * (1.f + z1 * (1.f - sg)));
             }
-            const long off = (long)(h0 + wn * 64 + 16 * q + mm) * p.cpad + r0 + wm * 64 + 16 * i + 4 * g;
-            store4<bf16>(gt + off, to_bf16x4(gv));
-            store4<bf16>(d1 + off, to_bf16x4(v1));
-            store4<bf16>(d3 + off, to_bf16x4(v3));
+            store4<bf16>(&st[0][16 * q + mm][16 * i + 4 * g], to_bf16x4(gv));
+            store4<bf16>(&st[1][16 * q + mm][16 * i + 4 * g], to_bf16x4(v1));
+            store4<bf16>(&st[2][16 * q + mm][16 * i + 4 * g], to_bf16x4(v3));
+        }
+    bf16 *const outs[3] = {p.gt + (long)h * p.hid * p.cpad, p.dh1t + (long)h * p.hid * p.cpad,
+                           p.dh3t + (long)h * p.hid * p.cpad};
+    const int orow8 = lane >> 3, ocol = (lane & 7) * 8;
+#pragma unroll
+    for (int o = 0; o < 3; ++o)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int row = 8 * r + orow8;
+            const bf16x4 x0 = load4<bf16>(&st[o][row][ocol]);
+            const bf16x4 x1 = load4<bf16>(&st[o][row][ocol + 4]);
+            const bf16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            st16(outs[o] + (long)(h0 + wn * 64 + row) * p.cpad + r0 + wm * 64 + ocol,
+                 B8{__builtin_bit_cast(u32x4v, x)});
         }
 }
 
