@@ -645,24 +645,45 @@ __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, 
     bf16 *Glo = G + (long)p.qpad * p.hid;
     gemm_nt_tile(L, as, p.d, bs, p.d, 2 * p.hid, T, p.d, 2, tm * 128, tn * 128,
                  [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+                     // G of the tile's 128 tokens x 64 hidden units, hi and lo,
+                     // staged token-major in the GEMM's LDS (free after its last
+                     // barrier; rows padded to 34 dwords) and written as whole
+                     // 128-byte rows
+                     bf16(*sh)[68] = reinterpret_cast<bf16(*)[68]>(&L);
+                     bf16(*sl)[68] = sh + 128;
+                     const int ml = mb - tm * 128, nl = nb - tn * 128;
 #pragma unroll
                      for (int i = 0; i < 4; i += 2)
 #pragma unroll
                          for (int q = 0; q < 4; ++q) {
-                             const int t = nb + 16 * q + mm;
-                             const int hh = (mb + 16 * i) / 2 + 4 * g;
+                             const int tl = nl + 16 * q + mm;
+                             const int hl = (ml + 16 * i) / 2 + 4 * g;
                              f32x4 gv;
 #pragma unroll
                              for (int j = 0; j < 4; ++j) {
                                  const float z1 = acc[i][q][j], z3 = acc[i + 1][q][j];
                                  gv[j] = z1 * sigmoidf_(z1) * z3;
                              }
-                             if (t < T) {
-                                 const bf16x4 hi = to_bf16x4(gv);
-                                 store4<bf16>(G + (long)t * p.hid + hh, hi);
-                                 store4<bf16>(Glo + (long)t * p.hid + hh, to_bf16x4(gv - to_f32x4(hi)));
-                             }
+                             const bf16x4 hi = to_bf16x4(gv);
+                             store4<bf16>(&sh[tl][hl], hi);
+                             store4<bf16>(&sl[tl][hl], to_bf16x4(gv - to_f32x4(hi)));
                          }
+                     lds_barrier();
+#pragma unroll
+                     for (int r = 0; r < 4; ++r) {
+                         const int piece = threadIdx.x + 256 * r;  // 128 rows x 8 pieces of 16 bytes
+                         const int row = piece >> 3, ch = 8 * (piece & 7);
+                         const int t = tn * 128 + row;
+                         if (t < T) {
+                             const long off = (long)t * p.hid + tm * 64 + ch;
+                             st16(G + off, B8{__builtin_bit_cast(u32x4v, __builtin_shufflevector(
+                                                  load4<bf16>(&sh[row][ch]), load4<bf16>(&sh[row][ch + 4]),
+                                                  0, 1, 2, 3, 4, 5, 6, 7))});
+                             st16(Glo + off, B8{__builtin_bit_cast(u32x4v, __builtin_shufflevector(
+                                                    load4<bf16>(&sl[row][ch]), load4<bf16>(&sl[row][ch + 4]),
+                                                    0, 1, 2, 3, 4, 5, 6, 7))});
+                         }
+                     }
                  });
 }
 
@@ -687,6 +708,31 @@ __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot
     const int cstart = c * p.chunk;
     gemm_nt_tile(L, as, p.hid, bs, p.hid, p.d, T, p.hid, 3, tm * 128, tn * 128,
                  [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+                     if (mode == 0) {
+                         // O of the tile's 128 tokens x 128 outputs staged
+                         // token-major in the GEMM's LDS (rows padded to 66
+                         // dwords) and written as whole 256-byte rows
+                         bf16(*so)[132] = reinterpret_cast<bf16(*)[132]>(&L);
+                         const int ml = mb - tm * 128, nl = nb - tn * 128;
+#pragma unroll
+                         for (int i = 0; i < 4; ++i)
+#pragma unroll
+                             for (int q = 0; q < 4; ++q)
+                                 store4<bf16>(&so[nl + 16 * q + mm][ml + 16 * i + 4 * g], to_bf16x4(acc[i][q]));
+                         lds_barrier();
+#pragma unroll
+                         for (int r = 0; r < 8; ++r) {
+                             const int piece = threadIdx.x + 256 * r;  // 128 rows x 16 pieces of 16 bytes
+                             const int row = piece >> 4, ch = 8 * (piece & 15);
+                             const int t = tn * 128 + row;
+                             if (t < T)
+                                 st16(p.out + ((long)h * p.Tq + t) * p.d + tm * 128 + ch,
+                                      B8{__builtin_bit_cast(u32x4v, __builtin_shufflevector(
+                                                            load4<bf16>(&so[row][ch]), load4<bf16>(&so[row][ch + 4]),
+                                                            0, 1, 2, 3, 4, 5, 6, 7))});
+                         }
+                         return;
+                     }
 #pragma unroll
                      for (int i = 0; i < 4; ++i)
 #pragma unroll
