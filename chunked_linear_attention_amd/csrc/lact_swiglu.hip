@@ -542,11 +542,23 @@ __global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
     const bf16 *as[1] = {A}, *bs[1] = {B};
     gemm_nt_tile(L, as, lda, bs, ldb, Mdim, Ndim, k1 - k0, 1, tm * 128, tn * 128,
                  [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+                     // the 128 x 128 partial staged in the GEMM's LDS (rows
+                     // padded to 132 floats) and written as whole 512-byte rows
+                     float(*sp)[132] = reinterpret_cast<float(*)[132]>(&L);
+                     const int ml = mb - tm * 128, nl = nb - tn * 128;
 #pragma unroll
                      for (int i = 0; i < 4; ++i)
 #pragma unroll
                          for (int q = 0; q < 4; ++q)
-                             *reinterpret_cast<f32x4 *>(part + (long)(nb + 16 * q + mm) * Mdim + mb + 16 * i + 4 * g) = acc[i][q];
+                             *reinterpret_cast<f32x4 *>(&sp[nl + 16 * q + mm][ml + 16 * i + 4 * g]) = acc[i][q];
+                     lds_barrier();
+#pragma unroll
+                     for (int r = 0; r < 16; ++r) {
+                         const int piece = threadIdx.x + 256 * r;  // 128 rows x 32 pieces of 16 bytes
+                         const int row = piece >> 5, ch = 4 * (piece & 31);
+                         *reinterpret_cast<f32x4 *>(part + (long)(tn * 128 + row) * Mdim + tm * 128 + ch) =
+                             *reinterpret_cast<const f32x4 *>(&sp[row][ch]);
+                     }
                  });
 }
 
