@@ -501,7 +501,10 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_summary(LinParams p)
     __shared__ F gb[LT ? 16 : 1][64];
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
     const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // column block
-    const int seg = blockIdx.x % p.Ssum, h = blockIdx.x / p.Ssum;
+    // a head's segments on one XCD: the replay's chain then reads the
+    // summaries from the L2 they were written to
+    const int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int seg = bid % p.Ssum, h = bid / p.Ssum;
     const int T = p.Tkv;
     const int t0 = seg * p.seg_tokens;
     const int tend = min(T, t0 + p.seg_tokens);
@@ -781,7 +784,8 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
     __shared__ F gb[16][64];
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
     const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // column block
-    const int seg = blockIdx.x % p.S, h = blockIdx.x / p.S;
+    const int bid = xcd_block(blockIdx.x, gridDim.x);  // a head's segments on one XCD
+    const int seg = bid % p.S, h = bid / p.S;
     const int T = p.Tkv;
     const int t0 = seg * p.seg_tokens;
     const int tend = min(T, t0 + p.seg_tokens);
