@@ -35,6 +35,8 @@
 #include "ttt_device.h"
 #include "ttt_internal.h"
 
+#include <mutex>
+
 namespace tttk {
 
 typedef __bf16 bf16;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot
                              const int row = piece >> 4, ch = 8 * (piece & 15);
                              const int t = tn * 128 + row;
                              if (t < T)
-                                 st16(p.out + ((long)h * p.Tq + t) * p.d + tm * 128 + ch,
+                                 st16(p.out + ((long)h * p.Tq + cstart + t) * p.d + tm * 128 + ch,
                                       B8{__builtin_bit_cast(u32x4v, __builtin_shufflevector(
                                                             load4<bf16>(&so[row][ch]), load4<bf16>(&so[row][ch + 4]),
                                                             0, 1, 2, 3, 4, 5, 6, 7))});
@@ -836,6 +838,35 @@ LactPlan lact_plan(const LactShape &s)
     return pl;
 }
 
+// A second stream per device (default priority) and two events, created on
+// first use and kept for the life of the process; the mutex is held while a
+// call enqueues its work, so calls from several host threads do not interleave
+// their event records.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t ready = nullptr, done = nullptr;
+    bool ok = false;
+};
+
+static SideStream *side_stream()
+{
+    constexpr int MAXDEV = 64;
+    static SideStream sides[MAXDEV];
+    static std::mutex init_mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV) return nullptr;
+    std::lock_guard<std::mutex> lk(init_mu);
+    SideStream &ss = sides[dev];
+    if (!ss.ok) {
+        if (!ss.s && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (!ss.ready && hipEventCreateWithFlags(&ss.ready, hipEventDisableTiming) != hipSuccess) return nullptr;
+        if (!ss.done && hipEventCreateWithFlags(&ss.done, hipEventDisableTiming) != hipSuccess) return nullptr;
+        ss.ok = true;
+    }
+    return &ss;
+}
+
 hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
                        const void *v, const float *eta, const float *w1, const float *w2,
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
@@ -886,6 +917,27 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     if (s.Tkv > 0) lact_prep_tokens<<<dim3(s.NH * (p.tpad / 64)), dim3(256), 0, st>>>(p);
     const int t13 = (s.d / 128) * (s.hid / 128);
     const int urows = s.NH * (2 * s.hid + s.d);
+    // Causal, inner-product loss: the queries of chunk c read the weights the
+    // chunk starts with, so their two apply GEMMs run on a side stream as soon
+    // as those weights exist, beside the (latency-bound) update chain of the
+    // later chunks; the caller's stream waits for them at the end.
+    SideStream *side = (s.order == 0 && s.loss == 0 && s.Tq > 0) ? side_stream() : nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    if (side) side_lock = std::unique_lock<std::mutex>(side->mu);
+    hipError_t serr = hipSuccess;  // first failure of an event call: the result is then invalid
+    auto chk = [&](hipError_t e) {
+        if (e != hipSuccess && serr == hipSuccess) serr = e;
+    };
+    auto apply_chunk = [&](int c) {
+        chk(hipEventRecord(side->ready, st));
+        chk(hipStreamWaitEvent(side->s, side->ready, 0));
+        const int qlen = (c + 1) * p.chunk <= s.Tq ? p.chunk : s.Tq - c * p.chunk;
+        lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((qlen + 127) / 128)), dim3(256), 0, side->s>>>(
+            p, p.q + (long)c * p.chunk * s.d, (long)s.Tq * s.d, qlen, c);
+        lact_apply2<<<dim3(s.NH * (s.d / 128) * ((qlen + 127) / 128)), dim3(256), 0, side->s>>>(p, qlen, c, 0,
+                                                                                               c);
+    };
+    if (side) apply_chunk(0);
     for (int c = 0; c < pl.nchunks; ++c) {
         const int slot = (s.order == 0) ? c : 0;
         const int dst = (s.order == 0) ? c + 1 : 0;
@@ -900,14 +952,19 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
         lact_fwdgrad<<<dim3(s.NH * (p.cpad / 128) * (s.hid / 128)), dim3(256), 0, st>>>(p, c, slot);
         lact_wgrad<<<dim3(s.NH * p.splitk * 3 * t13), dim3(256), 0, st>>>(p, c);
         lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst);
+        if (side && (c + 1) * p.chunk < s.Tq) apply_chunk(c + 1);
     }
-    if (s.Tq > 0) {
+    if (side) {
+        chk(hipEventRecord(side->done, side->s));
+        chk(hipStreamWaitEvent(st, side->done, 0));
+    } else if (s.Tq > 0) {
         const int fixed = (s.order == 0) ? -1 : 0;
         lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(
             p, p.q, (long)s.Tq * s.d, s.Tq, fixed);
         lact_apply2<<<dim3(s.NH * (s.d / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(
             p, s.Tq, fixed, 0, 0);
     }
+    if (serr != hipSuccess) return serr;
     return hipGetLastError();
 }
 
