@@ -27,10 +27,12 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are HIP device pointers owned by the caller.  The
- *     library never allocates device memory and keeps no state between calls;
- *     scratch space is the caller's `workspace` (size from the matching
- *     *_workspace_bytes query).  Calls on different streams with distinct
- *     workspaces and outputs may run concurrently.
+ *     library never allocates device memory; scratch space is the caller's
+ *     `workspace` (size from the matching *_workspace_bytes query).  The only
+ *     state kept between calls is, per device, one extra stream (default
+ *     priority) and two events that lact_swiglu_fwd creates on first use and
+ *     keeps until the process ends (see there).  Calls on different streams
+ *     with distinct workspaces and outputs may run concurrently.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronising.  Buffers must stay alive
  *     until the stream has passed the call.
@@ -127,6 +129,14 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
  * There is no intra-chunk term (causality inside a chunk belongs to the
  * window attention beside the layer, [LaCT] section 4).
  * Finals may alias the matching inits exactly.
+ * Causal order with the inner-product loss: the apply of each chunk's
+ * queries runs on a library-owned stream of the current device, after an
+ * event recorded on `stream` once that chunk's weights are written, and
+ * `stream` waits for it before the call's last operation, so on `stream`
+ * the call is ordered as a whole (also under graph capture, which the two
+ * event waits carry over to that stream).  Calls that take this path
+ * enqueue one at a time per device (a host-side lock) and share that
+ * stream, so their applies run in call order.
  * Supported: dtype TTT_BF16; d and hidden multiples of 128, each <= 1024;
  * chunk a positive multiple of 128, or >= Tkv (one chunk of any length);
  * any loss and order.  Other shapes return TTT_EUNSUPPORTED.
