@@ -921,7 +921,12 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     // chunk starts with, so their two apply GEMMs run on a side stream as soon
     // as those weights exist, beside the (latency-bound) update chain of the
     // later chunks; the caller's stream waits for them at the end.
-    SideStream *side = (s.order == 0 && s.loss == 0 && s.Tq > 0) ? side_stream() : nullptr;
+    // (Not under stream capture: there every launch stays on the caller's stream.)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
+    SideStream *side = (s.order == 0 && s.loss == 0 && s.Tq > 0 && cap == hipStreamCaptureStatusNone)
+                           ? side_stream()
+                           : nullptr;
     std::unique_lock<std::mutex> side_lock;
     if (side) side_lock = std::unique_lock<std::mutex>(side->mu);
     hipError_t serr = hipSuccess;  // first failure of an event call: the result is then invalid

@@ -133,10 +133,10 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
  * queries runs on a library-owned stream of the current device, after an
  * event recorded on `stream` once that chunk's weights are written, and
  * `stream` waits for it before the call's last operation, so on `stream`
- * the call is ordered as a whole (also under graph capture, which the two
- * event waits carry over to that stream).  Calls that take this path
- * enqueue one at a time per device (a host-side lock) and share that
- * stream, so their applies run in call order.
+ * the call is ordered as a whole.  While `stream` is being captured into a
+ * graph, every launch stays on `stream`.  Calls that take this path enqueue
+ * one at a time per device (a host-side lock) and share that stream, so
+ * their applies run in call order.
  * Supported: dtype TTT_BF16; d and hidden multiples of 128, each <= 1024;
  * chunk a positive multiple of 128, or >= Tkv (one chunk of any length);
  * any loss and order.  Other shapes return TTT_EUNSUPPORTED.

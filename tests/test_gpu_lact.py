@@ -126,3 +126,63 @@ def test_workload_lact_causal_full_size():
 def test_workload_lact_noncausal_full_size():
     """LaCT non-causal, d=384, hidden 768, 65536 update tokens, 16384 queries (head 1)."""
     _full(ti.LACT_NONCAUSAL, [1])
+
+
+def _causal_dot_inputs(seed):
+    inp = ti.gen_lact(1, 2, 512, 512, 128, 256, seed=seed, eta_scale=20.0)
+    return inputs_to_device(inp, "bf16")
+
+
+def _call(g):
+    cla = _cla()
+    return cla.lact_swiglu_fwd(g["q"], g["k"], g["v"], g["eta"], g["w1"], g["w2"], g["w3"],
+                               chunk=128, loss=0, order=0, rownorm=1)
+
+
+def test_causal_concurrent_streams():
+    """Two causal inner-product calls on two streams at once (their chunk
+    applies share the library's side stream) give the results of the same
+    calls made one at a time."""
+    ga, gb = _causal_dot_inputs(61), _causal_dot_inputs(62)
+    ref_a = [to_np(x) for x in _call(ga)]
+    ref_b = [to_np(x) for x in _call(gb)]
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sa):
+        ra = _call(ga)
+    with torch.cuda.stream(sb):
+        rb = _call(gb)
+    torch.cuda.synchronize()
+    for x, y in zip(ra, ref_a):
+        assert np.array_equal(to_np(x), y)
+    for x, y in zip(rb, ref_b):
+        assert np.array_equal(to_np(x), y)
+
+
+def test_causal_graph_replays():
+    """A causal inner-product call captured into a graph (every launch on the
+    capturing stream) matches the eager call on every replay, with eager work
+    and synchronisations between the replays."""
+    g = _causal_dot_inputs(63)
+    ref = [to_np(x) for x in _call(g)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _call(g)  # warm-up on the side stream, as torch advises before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = _call(g)
+    for _ in range(3):
+        for t in outs:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs, ref):
+            assert np.array_equal(to_np(x), y)
+        _call(g)  # eager work between replays
+        torch.cuda.synchronize()
