@@ -63,39 +63,51 @@ __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rc
 
 
 // ---------------------------------------------------------------------------
-// Generic NT GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16, k contiguous),
-// block tile 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 64 (a full
-// 128-byte row of each operand per stage), K a multiple of 64.  Rows of A
-// past M and rows of B past N read as zero.  The epilogue gets the wave's
-// 4 x 4 accumulator tiles: tile (i, q) holds C at rows mbase + 16 i + 4 g +
-// (0..3), column nbase + 16 q + (lane & 15).
+// Generic GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16), block tile
+// 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 64, K a multiple of 64.  An
+// operand is stored either k-contiguous (row m of A at A + m * lda, 128-byte
+// rows per stage) or, with AT / BT, k-major (row k at A + k * lda, holding
+// M contiguous elements: a token-major tensor read as its transpose), whose
+// fragments come from the transposing LDS read.  Rows of A past M and rows of
+// B past N read as zero, and so do rows k >= kvalid of a k-major operand.  The
+// epilogue gets the wave's 4 x 4 accumulator tiles: tile (i, q) holds C at
+// rows mbase + 16 i + 4 g + (0..3), column nbase + 16 q + (lane & 15).
 // ---------------------------------------------------------------------------
 constexpr int GBK = 64;
 constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): 16-byte fragment reads hit distinct banks per 8 lanes
+constexpr int GTPITCH = 128 + 16;  // k-major stage rows: transposing reads of 8 rows hit distinct banks
 constexpr int GPD = 2;           // register stages in flight (even: LDS buffer = stage parity)
 
 struct GemmLds {
     bf16 a[2][128][GPITCH];
     bf16 b[2][128][GPITCH];
 };
+static_assert(sizeof(bf16[GBK][GTPITCH]) <= sizeof(bf16[128][GPITCH]), "k-major stage fits the buffer");
 
 // K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
 // from As[s] and B from Bs[s] (same leading dimensions).  This sums products
 // of split operands (hi and lo bf16 parts) in one accumulation.
-template <typename Epi>
+template <bool AT = false, bool BT = false, typename Epi>
 __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, long lda,
                                              const bf16 *const *Bs, long ldb, int M, int N,
-                                             int kseg, int nseg, int m0, int n0, Epi &&epi)
+                                             int kseg, int nseg, int m0, int n0, int kvalid, Epi &&epi)
 {
+    constexpr bool TR = AT || BT;  // fragments in the transposing read's k order
     const int K = kseg * nseg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
-    // 4 pieces of 16 bytes per thread and operand: rows tid/8 + 32 i, 8 columns each
-    int lrow[4], lcol;
+    // 4 pieces of 16 bytes per thread and operand.  k-contiguous: rows
+    // tid/8 + 32 i, 8 columns each.  k-major: k rows tid/16 + 16 i, 8 of the
+    // 128 row elements each.
+    int lrow[4], lcol, krow[4], kcol;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lrow[i] = (tid >> 3) + 32 * i;
+    for (int i = 0; i < 4; ++i) {
+        lrow[i] = (tid >> 3) + 32 * i;
+        krow[i] = (tid >> 4) + 16 * i;
+    }
     lcol = (tid & 7) * 8;
+    kcol = (tid & 15) * 8;
     const bool aok[4] = {m0 + lrow[0] < M, m0 + lrow[1] < M, m0 + lrow[2] < M, m0 + lrow[3] < M};
     const bool bok[4] = {n0 + lrow[0] < N, n0 + lrow[1] < N, n0 + lrow[2] < N, n0 + lrow[3] < N};
     const int nst = K / GBK;
@@ -107,19 +119,52 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
         const bf16 *A = As[sg], *B = Bs[sg];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
-            rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
+            if constexpr (AT)
+                ra[s][i] = ld16(A + (long)min(kin + krow[i], kvalid - 1) * lda + m0 + kcol);
+            else
+                ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
+            if constexpr (BT)
+                rb[s][i] = ld16(B + (long)min(kin + krow[i], kvalid - 1) * ldb + n0 + kcol);
+            else
+                rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
         }
     };
     // Past the last k step the stage holds zeros, so every step computes (the
     // loads, LDS writes and MFMAs of a step stay in one basic block).
     auto commit = [&](int s, int buf, int st) {
         const bool live = st < nst;
+        const int kin = (min(st, nst - 1) * GBK) % kseg;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
-            st16(&L.b[buf][lrow[i]][lcol], (live && bok[i]) ? rb[s][i] : zero16());
+            if constexpr (AT) {
+                bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.a[buf][0][0]);
+                st16(&T[krow[i]][kcol], (live && kin + krow[i] < kvalid) ? ra[s][i] : zero16());
+            } else {
+                st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
+            }
+            if constexpr (BT) {
+                bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.b[buf][0][0]);
+                st16(&T[krow[i]][kcol], (live && kin + krow[i] < kvalid) ? rb[s][i] : zero16());
+            } else {
+                st16(&L.b[buf][lrow[i]][lcol], (live && bok[i]) ? rb[s][i] : zero16());
+            }
         }
+    };
+    // fragment of row r (m or n) for the 32-wide half kh: natural k order
+    // (8 consecutive k per lane) or, when an operand is k-major, k = 4g + j
+    // and 16 + 4g + j on both sides
+    auto frag = [&](const bf16 (*X)[GPITCH], bool kmajor, int r, int kh) {
+        if (!TR) return as_bf8(ld16(&X[r][32 * kh + 8 * g]));
+        if (kmajor) {
+            const bf16(*T)[GTPITCH] = reinterpret_cast<const bf16(*)[GTPITCH]>(&X[0][0]);
+            const int rb0 = r - mm;  // first row of the 16-row block
+            const bf16x4 x0 = lds_read_tr(&T[32 * kh + 4 * g + (mm >> 2)][rb0 + 4 * (mm & 3)]);
+            const bf16x4 x1 = lds_read_tr(&T[32 * kh + 16 + 4 * g + (mm >> 2)][rb0 + 4 * (mm & 3)]);
+            return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        const bf16x4 x0 = load4<bf16>(&X[r][32 * kh + 4 * g]);
+        const bf16x4 x1 = load4<bf16>(&X[r][32 * kh + 16 + 4 * g]);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     f32x4 acc[4][4];
 #pragma unroll
@@ -146,8 +191,8 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
                 bf16x8 af[4], bfr[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    af[i] = as_bf8(ld16(&L.a[buf][wm * 64 + 16 * i + mm][32 * kh + 8 * g]));
-                    bfr[i] = as_bf8(ld16(&L.b[buf][wn * 64 + 16 * i + mm][32 * kh + 8 * g]));
+                    af[i] = frag(L.a[buf], AT, wm * 64 + 16 * i + mm, kh);
+                    bfr[i] = frag(L.b[buf], BT, wn * 64 + 16 * i + mm, kh);
                 }
                 if (kh == 0)
                     issue(j, st + GPD);
@@ -157,7 +202,7 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, TR ? 16 : 8, 0);
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -182,9 +227,7 @@ struct LactParams {
     const float *w1i, *w2i, *w3i;
     bf16 *out;
     float *w1, *w2, *w3;        // fp32 masters (the final-state buffers)
-    int NH, Tq, Tkv, d, hid, chunk, nchunks, cpad, tpad, qpad, loss, order, rownorm, splitk;
-    bf16 *kt;      // [NH][d][tpad]    K^T
-    bf16 *dyt;     // [NH][d][tpad]    dY^T: (-eta V)^T for all tokens (inner product); per chunk (MSE)
+    int NH, Tq, Tkv, d, hid, chunk, nchunks, cpad, qpad, loss, order, rownorm, splitk;
     bf16 *dy;      // [NH][cpad][d]    dY token-major (MSE)
     bf16 *w13b;    // [nslots][NH][2 parts][2 hid][d]  W1/W3 rows interleaved by 16; part 0 =
                    //   bf16(W) (nearest), part 1 = bf16(W - part 0)
@@ -219,48 +262,9 @@ __device__ __forceinline__ void split1(float w, bf16 &hi, bf16 &lo)
 }
 
 // ---------------------------------------------------------------------------
-// prep: K^T and (inner product) (-eta V)^T for all key tokens, through LDS.
-// One block = 64 tokens of one head; zero rows up to tpad.
+// prep: fp32 masters from the inits (skipped where they alias) and the bf16
+// copies of slot 0.  Grid-stride over NH * 3 * hid * d elements.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void lact_prep_tokens(LactParams p)
-{
-    __shared__ bf16 tk[64][72];
-    __shared__ bf16 tv[64][72];
-    const int nb = p.tpad / 64;
-    const int h = blockIdx.x / nb, tb = blockIdx.x % nb;
-    const int t0 = tb * 64;
-    const bf16 *k = p.k + (long)h * p.Tkv * p.d;
-    const bf16 *v = p.v + (long)h * p.Tkv * p.d;
-    const float *eta = p.eta + (long)h * p.Tkv;
-    const bool dot = (p.loss == 0);
-    for (int f0 = 0; f0 < p.d; f0 += 64) {
-        for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-            const int r = i >> 3, c = (i & 7) * 8;
-            const int t = t0 + r;
-            const bool ok = t < p.Tkv;
-            const int tc = ok ? t : 0;
-            const B8 kx = ok ? ld16(k + (long)tc * p.d + f0 + c) : zero16();
-            const B8 vx = ok ? ld16(v + (long)tc * p.d + f0 + c) : zero16();
-            const float e = ok ? -eta[tc] : 0.f;
-            const bf16x8 kb = as_bf8(kx), vb = as_bf8(vx);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                tk[c + j][r] = kb[j];
-                tv[c + j][r] = (bf16)((float)vb[j] * e);
-            }
-        }
-        lds_barrier();
-        for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-            const int f = i >> 3, c = (i & 7) * 8;
-            st16(p.kt + ((long)h * p.d + f0 + f) * p.tpad + t0 + c, ld16(&tk[f][c]));
-            if (dot) st16(p.dyt + ((long)h * p.d + f0 + f) * p.tpad + t0 + c, ld16(&tv[f][c]));
-        }
-        lds_barrier();
-    }
-}
-
-// fp32 masters from the inits (skipped where they alias) and the bf16 copies
-// of slot 0.  Grid-stride over NH * 3 * hid * d elements.
 __global__ __launch_bounds__(256) void lact_prep_weights(LactParams p)
 {
     const long n13 = (long)p.hid * p.d;
@@ -460,9 +464,17 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     // The three outputs go through the wave's own LDS tiles (the k loop ended
     // with a barrier, so the operand buffers are free) and leave as whole
     // 128-byte rows of 64 tokens.
+    // Inner product: G^T is written with each token's -eta folded in, so the
+    // weight gradient of W2 (sum over tokens of dY^T G, dY = -eta V) reads V.
     bf16(*st)[64][FOPITCH] = LA.out[wave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        f32x4 ge;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = r0 + wm * 64 + 16 * i + 4 * g + j;
+            ge[j] = dot ? ((t < clen) ? -eh[t] : 0.f) : 1.f;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             f32x4 gv, v1, v3;
@@ -471,7 +483,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
                 const float z1 = a1[i][q][j], z3 = a3[i][q][j], dg = a2[i][q][j];
                 const float sg = sigmoidf_(z1);
                 const float act = z1 * sg;
-                gv[j] = act * z3;
+                gv[j] = act * z3 * ge[j];
                 v3[j] = dg * act;
                 v1[j] = dg * z3 * (sg * (1.f + z1 * (1.f - sg)));
             }
@@ -479,6 +491,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
             store4<bf16>(&st[1][16 * q + mm][16 * i + 4 * g], to_bf16x4(v1));
             store4<bf16>(&st[2][16 * q + mm][16 * i + 4 * g], to_bf16x4(v3));
         }
+    }
     bf16 *const outs[3] = {p.gt + (long)h * p.hid * p.cpad, p.dh1t + (long)h * p.hid * p.cpad,
                            p.dh3t + (long)h * p.hid * p.cpad};
     const int orow8 = lane >> 3, ocol = (lane & 7) * 8;
@@ -528,22 +541,11 @@ __global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
             part[(long)(tn * 128 + (e >> 7)) * Mdim + tm * 128 + (e & 127)] = 0.f;
         return;
     }
-    const bf16 *A, *B;
-    long lda, ldb;
-    if (which < 2) {
-        A = p.kt + (long)h * d * p.tpad + cstart + k0;
-        lda = p.tpad;
-        B = (which == 0 ? p.dh1t : p.dh3t) + (long)h * hid * p.cpad + k0;
-        ldb = p.cpad;
-    } else {
-        A = p.gt + (long)h * hid * p.cpad + k0;
-        lda = p.cpad;
-        B = p.dyt + (long)h * d * p.tpad + (p.loss == 0 ? cstart : 0) + k0;
-        ldb = p.tpad;
-    }
-    const bf16 *as[1] = {A}, *bs[1] = {B};
-    gemm_nt_tile(L, as, lda, bs, ldb, Mdim, Ndim, k1 - k0, 1, tm * 128, tn * 128,
-                 [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+    // K and V (inner product) or dY (MSE) are read token-major straight from
+    // their tensors, as k-major operands; rows past the chunk read as zero.
+    const int clen = min(p.chunk, p.Tkv - cstart);
+    const int kvalid = clen - k0;
+    auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
                      // the 128 x 128 partial staged in the GEMM's LDS (rows
                      // padded to 132 floats) and written as whole 512-byte rows
                      float(*sp)[132] = reinterpret_cast<float(*)[132]>(&L);
@@ -561,7 +563,19 @@ __global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
                          *reinterpret_cast<f32x4 *>(part + (long)(tn * 128 + row) * Mdim + tm * 128 + ch) =
                              *reinterpret_cast<const f32x4 *>(&sp[row][ch]);
                      }
-                 });
+                 };
+    if (which < 2) {
+        const bf16 *as[1] = {p.k + ((long)h * p.Tkv + cstart + k0) * d};
+        const bf16 *bs[1] = {(which == 0 ? p.dh1t : p.dh3t) + (long)h * hid * p.cpad + k0};
+        gemm_nt_tile<true, false>(L, as, d, bs, p.cpad, Mdim, Ndim, k1 - k0, 1, tm * 128, tn * 128, kvalid, epi);
+    } else {
+        // dW2 = sum_t dY_t^T G_t.  Inner product: dY = -eta V, and G^T already
+        // carries the -eta, so B is V itself.
+        const bf16 *as[1] = {p.gt + (long)h * hid * p.cpad + k0};
+        const bf16 *bs[1] = {p.loss == 0 ? p.v + ((long)h * p.Tkv + cstart + k0) * d
+                                         : p.dy + ((long)h * p.cpad + k0) * d};
+        gemm_nt_tile<false, true>(L, as, p.cpad, bs, d, Mdim, Ndim, k1 - k0, 1, tm * 128, tn * 128, kvalid, epi);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -657,7 +671,7 @@ __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, 
     const bf16 *bs[2] = {B, B};
     bf16 *G = p.gq + (long)h * 2 * p.qpad * p.hid;
     bf16 *Glo = G + (long)p.qpad * p.hid;
-    gemm_nt_tile(L, as, p.d, bs, p.d, 2 * p.hid, T, p.d, 2, tm * 128, tn * 128,
+    gemm_nt_tile(L, as, p.d, bs, p.d, 2 * p.hid, T, p.d, 2, tm * 128, tn * 128, 1 << 30,
                  [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
                      // G of the tile's 128 tokens x 64 hidden units, hi and lo,
                      // staged token-major in the GEMM's LDS (free after its last
@@ -703,7 +717,7 @@ __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, 
 
 // apply2: Y[t][o] = G[t] . W2[o], as the GEMM W2 G^T (4 consecutive outputs of
 // one token per lane).  mode 0: out = Y (bf16).  mode 1 (MSE): dY = eta (Y - V)
-// token-major into p.dy and transposed into p.dyt (chunk-local tokens).
+// token-major into p.dy (chunk-local tokens).
 __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot_fixed, int mode,
                                                    int c)
 {
@@ -720,7 +734,7 @@ __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot
     const bf16 *ghi = p.gq + (long)h * 2 * p.qpad * p.hid, *glo = ghi + (long)p.qpad * p.hid;
     const bf16 *as[3] = {whi, wlo, whi}, *bs[3] = {ghi, ghi, glo};
     const int cstart = c * p.chunk;
-    gemm_nt_tile(L, as, p.hid, bs, p.hid, p.d, T, p.hid, 3, tm * 128, tn * 128,
+    gemm_nt_tile(L, as, p.hid, bs, p.hid, p.d, T, p.hid, 3, tm * 128, tn * 128, 1 << 30,
                  [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
                      if (mode == 0) {
                          // O of the tile's 128 tokens x 128 outputs staged
@@ -753,26 +767,11 @@ __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot
                          for (int q = 0; q < 4; ++q) {
                              const int t = nb + 16 * q + mm;
                              const int o = mb + 16 * i + 4 * g;
-                             if (mode == 1 && t >= T) {
-                                 // zero the rest of the chunk's padded columns: the weight
-                                 // gradient reads them (against zero partners)
-#pragma unroll
-                                 for (int j = 0; j < 4; ++j) p.dyt[((long)h * p.d + o + j) * p.tpad + t] = (bf16)0.f;
-                                 continue;
-                             }
-                             if (t >= T) continue;
-                             if (mode == 0) {
-                                 store4<bf16>(p.out + ((long)h * p.Tq + t) * p.d + o, to_bf16x4(acc[i][q]));
-                             } else {
-                                 const long tk = (long)h * p.Tkv + cstart + t;
-                                 const float e = p.eta[tk];
-                                 const f32x4 vv = to_f32x4(load4<bf16>(p.v + tk * p.d + o));
-                                 const f32x4 dyv = (acc[i][q] - vv) * e;
-                                 const bf16x4 db = to_bf16x4(dyv);
-                                 store4<bf16>(p.dy + ((long)h * p.cpad + t) * p.d + o, db);
-#pragma unroll
-                                 for (int j = 0; j < 4; ++j) p.dyt[((long)h * p.d + o + j) * p.tpad + t] = db[j];
-                             }
+                             if (t >= T) continue;  // the readers treat rows past the chunk as zero
+                             const long tk = (long)h * p.Tkv + cstart + t;
+                             const float e = p.eta[tk];
+                             const f32x4 vv = to_f32x4(load4<bf16>(p.v + tk * p.d + o));
+                             store4<bf16>(p.dy + ((long)h * p.cpad + t) * p.d + o, to_bf16x4((acc[i][q] - vv) * e));
                          }
                  });
 }
@@ -807,7 +806,6 @@ LactPlan lact_plan(const LactShape &s)
     pl.nchunks = (s.Tkv > 0) ? (s.Tkv + chunk - 1) / chunk : 0;
     const int clen = (s.Tkv > 0) ? (chunk < s.Tkv ? chunk : s.Tkv) : 0;
     const size_t cpad = (size_t)((clen + 127) / 128 * 128);
-    const size_t tpad = (size_t)((s.Tkv + 127) / 128 * 128);
     const size_t qpad = (size_t)(((s.Tq > (int)cpad ? s.Tq : (int)cpad) + 127) / 128 * 128);
     pl.maxc = (int)cpad;
     const int nslots = (s.order == 0) ? pl.nchunks + 1 : 1;
@@ -818,8 +816,7 @@ LactPlan lact_plan(const LactShape &s)
         pl.off[idx] = off;
         off = al256(off + bytes);
     };
-    take(0, NH * d * tpad * 2);                 // kt
-    take(1, NH * d * tpad * 2);                 // dyt
+    // slots 0, 1 and 13 are not used
     take(2, s.loss == 1 ? NH * cpad * d * 2 : 0);  // dy
     take(3, (size_t)nslots * NH * 2 * 2 * hid * d * 2);  // w13b (hi, lo)
     take(4, (size_t)nslots * NH * 2 * d * hid * 2);      // w2b (hi, lo)
@@ -831,7 +828,6 @@ LactPlan lact_plan(const LactShape &s)
     pl.off[10] = (size_t)splitk;
     pl.off[11] = (size_t)nslots;
     pl.off[12] = cpad;
-    pl.off[13] = tpad;
     pl.off[14] = qpad;
     pl.off[15] = (size_t)chunk;
     pl.bytes = off;
@@ -893,15 +889,12 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     p.chunk = (int)pl.off[15];
     p.nchunks = pl.nchunks;
     p.cpad = (int)pl.off[12];
-    p.tpad = (int)pl.off[13];
     p.qpad = (int)pl.off[14];
     p.loss = s.loss;
     p.order = s.order;
     p.rownorm = s.rownorm;
     p.splitk = (int)pl.off[10];
     p.nslots = (int)pl.off[11];
-    p.kt = (bf16 *)(base + pl.off[0]);
-    p.dyt = (bf16 *)(base + pl.off[1]);
     p.dy = (bf16 *)(base + pl.off[2]);
     p.w13b = (bf16 *)(base + pl.off[3]);
     p.w2b = (bf16 *)(base + pl.off[4]);
@@ -914,7 +907,6 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     const long n3 = (long)s.NH * 3 * s.hid * s.d;
     const int wblocks = (int)((n3 + 255) / 256 < 4096 ? (n3 + 255) / 256 : 4096);
     lact_prep_weights<<<dim3(wblocks), dim3(256), 0, st>>>(p);
-    if (s.Tkv > 0) lact_prep_tokens<<<dim3(s.NH * (p.tpad / 64)), dim3(256), 0, st>>>(p);
     const int t13 = (s.d / 128) * (s.hid / 128);
     const int urows = s.NH * (2 * s.hid + s.d);
     // Causal, inner-product loss: the queries of chunk c read the weights the
