@@ -9,6 +9,8 @@ for the page sections it follows and the readings it takes); this module
 builds it with gcc and wraps it with ctypes.  ``dense.py`` restates the same
 definitions with each chunk's sum over tokens done by a numpy matmul, for
 sizes where the token loop is too slow; it is pinned against the token loop.
+``decode.py`` is the single-token decode step of TTT-Linear (one gradient step
+per token on a carried state, optionally anchored at the chunk-start state).
 """
 from __future__ import annotations
 
