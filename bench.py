@@ -202,6 +202,96 @@ def bench_lact(wl, steps, warmup):
             "alg_flops": flops, "alg_bytes": byts}
 
 
+# ----------------------------------------------------------------------------
+# Decode steps (one token per sequence and head; the state is read -- and for
+# TTT-Linear rewritten -- once per token).  Algorithmic bytes per head-token:
+#   TTT-Linear: state read + write 8 d^2, the chunk-start anchor read 4 d^2
+#               (MSE, chunk > 1), the anchor write 4 d^2 once per chunk, q k v
+#               and out 4 d s_in, eta 4;
+#   LaCT apply: the three weight matrices 12 d hid, q and out 2 d s_in.
+# State sets are rotated (>= 1 GiB) so the last-level cache cannot hold them.
+def linear_decode_bytes(NH, d, esz, loss, chunk):
+    anchored = loss == 1 and chunk > 1
+    per = 8 * d * d + (4 * d * d if anchored else 0) + 4 * d * esz + 4
+    if chunk > 1:
+        per += 4 * d * d / chunk
+    return NH * per
+
+
+def bench_linear_decode(B, H, d, loss, chunk, dtype, steps, warmup, seed=41):
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_linear(B, H, 1, 1, d, seed=seed, dtype=dtype, w0="normal")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if dtype == "bf16":
+        up = lambda n: torch.from_numpy(inp[n + "16"][:, :, 0].copy().view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        up = lambda n: torch.from_numpy(inp[n][:, :, 0].copy()).cuda()
+    q, k, v = up("q"), up("k"), up("v")
+    eta = torch.from_numpy(inp["eta"][:, :, 0].copy()).cuda()
+    w0 = torch.from_numpy(inp["w0"]).cuda()
+    anchored = chunk > 1
+    per = w0.numel() * 4 * (2 if anchored else 1)
+    sets = Rotated(lambda i: {"w": w0.clone(), "a": w0.clone() if anchored else None}, per,
+                   1 << 30, 32)
+    out = torch.empty_like(q)
+    step = [0]
+
+    def call(s):
+        i = step[0]
+        step[0] += 1
+        cla.ttt_linear_decode(q, k, v, eta, s["w"], loss=loss, w_anchor=s["a"],
+                              anchor_update=anchored and i % chunk == chunk - 1, out=out)
+    ms, _ = time_calls(call, sets, steps, warmup)
+    esz = 2 if dtype == "bf16" else 4
+    byts = linear_decode_bytes(B * H, d, esz, loss, chunk)
+    name = (f"ttt_linear_decode_{'mse' if loss else 'dot'}_B{B}_H{H}_d{d}_"
+            f"{'b' + str(chunk) if chunk > 1 else 'recurrent'}_{dtype}")
+    return {"workload": name, "us_per_step": ms * 1e3, "tokens_per_s": B / (ms * 1e-3),
+            "alg_bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
+            "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "state_copies": sets.n}
+
+
+def bench_lact_decode(B, H, d, hid, steps, warmup, seed=43):
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_lact(B, H, 1, 1, d, hid, seed=seed)
+    q = torch.from_numpy(inp["q16"][:, :, 0].copy().view(np.int16)).view(torch.bfloat16).cuda()
+    ws0 = [torch.from_numpy(inp[n]).cuda() for n in ("w1", "w2", "w3")]
+    per = sum(t.numel() * 4 for t in ws0)
+    sets = Rotated(lambda i: ws0 if i == 0 else [t.clone() for t in ws0], per, 1 << 30, 32)
+    out = torch.empty_like(q)
+    nb = cla.lact_swiglu_decode_workspace_bytes(B, H, d, hid, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def call(s):
+        cla.lact_swiglu_decode(q, *s, out=out, workspace=ws)
+    ms, _ = time_calls(call, sets, steps, warmup)
+    byts = B * H * (12 * d * hid + 2 * d * 2)
+    return {"workload": f"lact_swiglu_decode_B{B}_H{H}_d{d}_h{hid}_bf16", "us_per_step": ms * 1e3,
+            "tokens_per_s": B / (ms * 1e-3), "alg_bytes": byts,
+            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "state_copies": sets.n}
+
+
+def bench_decode(steps, warmup):
+    """The decode-step workloads: the headline head shape (d = 64, H = 8, MSE,
+    chunk-16 anchor) at the headline batch and at a serving batch of 256
+    sequences, the recurrent rule, d = 128, and the two LaCT head shapes."""
+    res = []
+    for args in ((256, 8, 64, 1, 16), (4, 8, 64, 1, 16), (256, 8, 64, 1, 1), (64, 16, 128, 1, 16)):
+        log(f"[bench] timing decode {args}")
+        res.append(bench_linear_decode(*args, "bf16", steps, warmup))
+    for args in ((64, 4, 256, 512), (64, 2, 384, 768)):
+        log(f"[bench] timing LaCT decode {args}")
+        res.append(bench_lact_decode(*args, steps, warmup))
+    return res
+
+
 def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0):
     """The oracle as it stands, on the host cores, over whole heads of the workload
     until about `budget_s` of CPU time has been spent (at least one head)."""
@@ -239,6 +329,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--lact-only", action="store_true",
                     help="only time the two LaCT workloads (for profiling them alone)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the decode-step workloads (for profiling them alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (scales HBM counters)")
     args = ap.parse_args()
@@ -266,6 +358,10 @@ def main():
     if args.lact_only:
         print(json.dumps({"lact": [bench_lact(lw, args.steps, args.warmup)
                                    for lw in (ti.LACT_CAUSAL, ti.LACT_NONCAUSAL)]}), flush=True)
+        return
+
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(args.steps, args.warmup)}), flush=True)
         return
 
     wl = ti.MSE_D64
@@ -323,6 +419,7 @@ def main():
             except Exception as e:  # reported, never hidden
                 lact.append({"workload": lw.name, "error": str(e)})
         line["lact"] = lact
+        line["decode"] = bench_decode(max(50, args.steps), args.warmup)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline_linear(inp, wl.chunk, wl.loss, args.cpu_budget)

@@ -40,6 +40,13 @@ bool lact_supported(int dtype, int d, int hid, int chunk, int Tkv)
     return true;
 }
 
+// [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,6 +131,52 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
     if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
     hipError_t e = tttk::lact_launch(s, pl, q, k, v, eta, w1_init, w2_init, w3_init, out, w1_final,
                                      w2_final, w3_final, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
+ttt_status ttt_linear_decode(const void *q, const void *k, const void *v, int dtype,
+                             const float *eta, float *w, float *w_anchor, int anchor_update,
+                             void *out, int B, int H, int d, int loss, void *stream)
+{
+    if (!valid_enums(dtype, loss, TTT_CAUSAL)) return TTT_EINVAL;
+    if (B < 1 || H < 1 || d < 1 || (anchor_update != 0 && anchor_update != 1)) return TTT_EINVAL;
+    if ((long long)B * H > (1LL << 24)) return TTT_EUNSUPPORTED;
+    const void *req[6] = {q, k, v, eta, w, out};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return TTT_EINVAL;
+    if (anchor_update && !w_anchor) return TTT_EINVAL;
+    if (d != 64 && d != 128) return TTT_EUNSUPPORTED;
+    const size_t sbytes = (size_t)B * H * d * d * sizeof(float);
+    if (w_anchor && (!aligned16(w_anchor) || overlaps(w, sbytes, w_anchor, sbytes)))
+        return TTT_EINVAL;
+    hipError_t e = tttk::linear_decode_launch(B * H, d, dtype == TTT_BF16 ? 1 : 0, loss, q, k, v,
+                                              eta, w, w_anchor, anchor_update, out,
+                                              (hipStream_t)stream);
+    return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
+size_t lact_swiglu_decode_workspace_bytes(int B, int H, int d, int hidden, int dtype)
+{
+    if ((dtype != TTT_F32 && dtype != TTT_BF16) || B < 1 || H < 1 || d < 1 || hidden < 1) return 0;
+    if ((long long)B * H > (1LL << 24) || d % 64 || hidden % 64 || d > 1024 || hidden > 1024)
+        return 0;
+    return tttk::lact_decode_workspace(B * H, hidden);
+}
+
+ttt_status lact_swiglu_decode(const void *q, int dtype, const float *w1, const float *w2,
+                              const float *w3, void *out, int B, int H, int d, int hidden,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_EINVAL;
+    if (B < 1 || H < 1 || d < 1 || hidden < 1) return TTT_EINVAL;
+    const void *req[6] = {q, w1, w2, w3, out, workspace};
+    for (const void *p : req)
+        if (!p || !aligned16(p)) return TTT_EINVAL;
+    if ((long long)B * H > (1LL << 24)) return TTT_EUNSUPPORTED;
+    if (d % 64 || hidden % 64 || d > 1024 || hidden > 1024) return TTT_EUNSUPPORTED;
+    if (workspace_bytes < tttk::lact_decode_workspace(B * H, hidden)) return TTT_EWORKSPACE;
+    hipError_t e = tttk::lact_decode_launch(B * H, d, hidden, dtype == TTT_BF16 ? 1 : 0, q, w1, w2,
+                                            w3, out, workspace, (hipStream_t)stream);
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 

@@ -48,4 +48,13 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
                        hipStream_t stream);
 
+// ---- decode steps (one token per head) ---------------------------------------------
+hipError_t linear_decode_launch(int NH, int d, int bf16, int loss, const void *q, const void *k,
+                                const void *v, const float *eta, float *w, float *anchor,
+                                int anchor_update, void *out, hipStream_t stream);
+size_t lact_decode_workspace(int NH, int hid);
+hipError_t lact_decode_launch(int NH, int d, int hid, int bf16, const void *q, const float *w1,
+                              const float *w2, const float *w3, void *out, void *ws,
+                              hipStream_t stream);
+
 }  // namespace tttk

@@ -106,3 +106,56 @@ def lact_swiglu_fwd(q, k, v, eta, w1, w2, w3, *, chunk: int, loss="dot", order="
     if rc != TTT_OK:
         raise TTTError(rc, "lact_swiglu_fwd")
     return out, w1_final, w2_final, w3_final
+
+
+def ttt_linear_decode(q, k, v, eta, w, *, loss="mse", w_anchor=None, anchor_update=False,
+                      out=None, stream=None):
+    """One decode step: q, k, v [B,H,d], eta [B,H]; w [B,H,d,d] fp32 is updated in
+    place; w_anchor (optional, [B,H,d,d] fp32) is the chunk-start state, moved to
+    the new state when anchor_update is set.  Returns out [B,H,d]."""
+    lib = load()
+    B, H, d = q.shape
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dt)
+    _check(eta, "eta", torch.float32)
+    _check(w, "w", torch.float32)
+    if w_anchor is not None:
+        _check(w_anchor, "w_anchor", torch.float32)
+    if tuple(k.shape) != (B, H, d) or tuple(v.shape) != (B, H, d) or tuple(eta.shape) != (B, H) \
+            or tuple(w.shape) != (B, H, d, d) or (w_anchor is not None and w_anchor.shape != w.shape):
+        raise ValueError("ttt_linear_decode: inconsistent shapes")
+    out = torch.empty_like(q) if out is None else out
+    rc = lib.ttt_linear_decode(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(eta), _ptr(w),
+                               _ptr(w_anchor), int(bool(anchor_update)), _ptr(out), B, H, d,
+                               _LOSS[loss], _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "ttt_linear_decode")
+    return out
+
+
+def lact_swiglu_decode_workspace_bytes(B, H, d, hidden, dtype) -> int:
+    return int(load().lact_swiglu_decode_workspace_bytes(B, H, d, hidden, _DT[dtype]))
+
+
+def lact_swiglu_decode(q, w1, w2, w3, *, out=None, workspace=None, stream=None):
+    """LaCT decode apply: q [B,H,d] -> W2 (silu(W1 q) * (W3 q)) [B,H,d] with the
+    weights as they stand (w1, w3 [B,H,hid,d], w2 [B,H,d,hid] fp32)."""
+    lib = load()
+    B, H, d = q.shape
+    hid = w1.shape[2]
+    dt = q.dtype
+    _check(q, "q", dt)
+    for t, n in ((w1, "w1"), (w2, "w2"), (w3, "w3")):
+        _check(t, n, torch.float32)
+    if tuple(w1.shape) != (B, H, hid, d) or w3.shape != w1.shape or tuple(w2.shape) != (B, H, d, hid):
+        raise ValueError("lact_swiglu_decode: inconsistent shapes")
+    out = torch.empty_like(q) if out is None else out
+    nbytes = lib.lact_swiglu_decode_workspace_bytes(B, H, d, hid, _DT[dt])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.lact_swiglu_decode(_ptr(q), _DT[dt], _ptr(w1), _ptr(w2), _ptr(w3), _ptr(out), B, H, d,
+                                hid, _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "lact_swiglu_decode")
+    return out

@@ -151,6 +151,56 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
                            int chunk, int loss, int order, int rownorm, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Decode steps: one token per (batch, head) on a carried state.
+ *
+ * TTT-Linear ([TTT] "TTT definition": one gradient step per token on the
+ * state carried from the previous token, the output read after the step;
+ * examples 1 and 2 for the gradients; "Mini-batch gradient descent" for the
+ * chunk-start anchor).  Per (batch, head), with A the state the gradient is
+ * taken at:
+ *   u = v - k A   (MSE)   or   v   (DOT)
+ *   W <- W + eta k^T u
+ *   y = q W       (after the step)
+ * q, k, v [B][H][d] in `dtype`; eta [B][H] fp32; out [B][H][d] in `dtype`.
+ * w [B][H][d][d] fp32: the carried state, read and rewritten in place.
+ * w_anchor == NULL: A = W (the recurrent rule, chunk size 1).
+ * w_anchor != NULL: [B][H][d][d] fp32, the state at the start of the current
+ *   chunk (A = w_anchor); anchor_update = 1 (the token closes its chunk) also
+ *   writes the new W to w_anchor, anchor_update = 0 leaves it as it is.  It
+ *   must not overlap w.  The inner-product loss never reads it.
+ * Stepping a sequence through this call, with the anchor moved at the last
+ * token of every chunk, gives the causal ttt_linear_fwd result for that chunk
+ * size.  Arithmetic: fp32 FMA (the state is read once per token; the step is
+ * bound by memory bandwidth).  No workspace.
+ * Supported: d in {64, 128}; dtype TTT_F32 or TTT_BF16; 16-byte aligned
+ * pointers.  Other d: TTT_EUNSUPPORTED.  anchor_update other than 0 or 1, or 1
+ * without an anchor: TTT_EINVAL.
+ * ------------------------------------------------------------------------ */
+ttt_status ttt_linear_decode(const void *q, const void *k, const void *v, int dtype,
+                             const float *eta, float *w, float *w_anchor, int anchor_update,
+                             void *out, int B, int H, int d, int loss, void *stream);
+
+/* LaCT decode apply ([LaCT] sections 3.2 and 4): out = W2 (silu(W1 q) * (W3 q))
+ * for one query per (batch, head), with the weights as they stand (in the
+ * causal order, the start-of-chunk weights of the chunk being decoded).  The
+ * chunk's keys, values and learning rates are kept by the caller; once the
+ * chunk is complete, lact_swiglu_fwd with TTT_NONCAUSAL and Tq = 0 applies
+ * its update.  Stepping a sequence this way gives the causal lact_swiglu_fwd
+ * result.
+ * q [B][H][d] in `dtype`; w1, w3 [B][H][hidden][d], w2 [B][H][d][hidden]
+ * fp32, read only; out [B][H][d] in `dtype`.  Arithmetic: fp32 FMA.
+ * workspace: at least lact_swiglu_decode_workspace_bytes (it holds the hidden
+ * activations between the two launches).
+ * Supported: dtype TTT_F32 or TTT_BF16; d and hidden multiples of 64, each
+ * <= 1024; 16-byte aligned pointers.  The workspace query returns 0 for
+ * anything unsupported. */
+size_t lact_swiglu_decode_workspace_bytes(int B, int H, int d, int hidden, int dtype);
+
+ttt_status lact_swiglu_decode(const void *q, int dtype, const float *w1, const float *w2,
+                              const float *w3, void *out, int B, int H, int d, int hidden,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

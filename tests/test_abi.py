@@ -93,3 +93,51 @@ def lact(lib, **kw):
 ])
 def test_lact_validation(kw, code):
     assert lact(_lib.load(), **kw) == code
+
+
+def dec(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w=FAKE, anchor=None, upd=0, out=FAKE, B=1,
+             H=1, d=64, loss=1, stream=None)
+    a.update(kw)
+    return lib.ttt_linear_decode(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w"], a["anchor"],
+                                 a["upd"], a["out"], a["B"], a["H"], a["d"], a["loss"], a["stream"])
+
+
+# every case fails validation before a launch
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.TTT_EINVAL), (dict(eta=None), _lib.TTT_EINVAL), (dict(w=None), _lib.TTT_EINVAL),
+    (dict(out=None), _lib.TTT_EINVAL), (dict(w=FAKE + 4), _lib.TTT_EINVAL),
+    (dict(dtype=3), _lib.TTT_EINVAL), (dict(loss=2), _lib.TTT_EINVAL), (dict(B=0), _lib.TTT_EINVAL),
+    (dict(H=-1), _lib.TTT_EINVAL), (dict(upd=2), _lib.TTT_EINVAL), (dict(upd=1), _lib.TTT_EINVAL),
+    (dict(d=32), _lib.TTT_EUNSUPPORTED), (dict(d=96), _lib.TTT_EUNSUPPORTED),
+    # the anchor may not overlap the running state
+    (dict(anchor=FAKE), _lib.TTT_EINVAL), (dict(anchor=FAKE + 64 * 64 * 4 - 16), _lib.TTT_EINVAL),
+    (dict(anchor=FAKE + 64 * 64 * 4 + 8), _lib.TTT_EINVAL),
+])
+def test_linear_decode_validation(kw, code):
+    assert dec(_lib.load(), **kw) == code
+
+
+def lact_dec(lib, **kw):
+    a = dict(q=FAKE, dtype=1, w1=FAKE, w2=FAKE, w3=FAKE, out=FAKE, B=1, H=1, d=256, hid=512, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.lact_swiglu_decode(a["q"], a["dtype"], a["w1"], a["w2"], a["w3"], a["out"], a["B"],
+                                  a["H"], a["d"], a["hid"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.TTT_EINVAL), (dict(w2=None), _lib.TTT_EINVAL), (dict(ws=None), _lib.TTT_EINVAL),
+    (dict(out=FAKE + 2), _lib.TTT_EINVAL), (dict(dtype=2), _lib.TTT_EINVAL), (dict(B=0), _lib.TTT_EINVAL),
+    (dict(d=96), _lib.TTT_EUNSUPPORTED), (dict(hid=2048), _lib.TTT_EUNSUPPORTED),
+    (dict(wsb=512 * 4 - 1), _lib.TTT_EWORKSPACE),
+])
+def test_lact_decode_validation(kw, code):
+    assert lact_dec(_lib.load(), **kw) == code
+
+
+def test_lact_decode_workspace_query():
+    lib = _lib.load()
+    assert lib.lact_swiglu_decode_workspace_bytes(64, 4, 256, 512, 1) == 64 * 4 * 512 * 4
+    assert lib.lact_swiglu_decode_workspace_bytes(1, 1, 96, 512, 1) == 0
+    assert lib.lact_swiglu_decode_workspace_bytes(1, 1, 256, 512, 5) == 0
