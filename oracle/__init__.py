@@ -32,6 +32,9 @@ LOSS_DOT = 0
 LOSS_MSE = 1
 CAUSAL = 0
 NONCAUSAL = 1
+RULE_GD = 0
+RULE_MOMENTUM = 1
+RULE_MUON = 2
 
 
 def build(force: bool = False) -> str:
@@ -57,6 +60,9 @@ def _load():
             lib.oracle_ttt_linear.restype = i
             lib.oracle_lact_swiglu.argtypes = [dp] * 11 + [i] * 11
             lib.oracle_lact_swiglu.restype = i
+            f = ctypes.c_double
+            lib.oracle_lact_swiglu_rule.argtypes = [dp] * 11 + [i] * 11 + [f, i, f] + [dp] * 3 + [i]
+            lib.oracle_lact_swiglu_rule.restype = i
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = i
             _lib = lib
@@ -114,3 +120,33 @@ def lact_swiglu(q, k, v, eta, w1, w2, w3, *, chunk: int, loss: int = LOSS_DOT,
     if rc != 0:
         raise ValueError(f"oracle_lact_swiglu failed with {rc}")
     return out, f1, f2, f3
+
+
+def lact_swiglu_rule(q, k, v, eta, w1, w2, w3, *, chunk: int, loss: int = LOSS_DOT,
+                     order: int = CAUSAL, rownorm: int = 1, rule: int = RULE_GD,
+                     beta: float = 0.0, ns_steps: int = 5, lr: float = 1.0, m=None,
+                     nthreads: int = 0):
+    """LaCT SwiGLU forward in fp64 with an update rule: RULE_GD, RULE_MOMENTUM
+    (M <- beta M + G, step M) or RULE_MUON (step lr * NS_k(M), M = G when beta is
+    0).  m = (m1, m2, m3) momentum buffers shaped like the weights (zeros when
+    None).  Returns (out, w1_final, w2_final, w3_final, (m1, m2, m3) after)."""
+    lib = _load()
+    q, k, v, eta = _d(q), _d(k), _d(v), _d(eta)
+    w1, w2, w3 = _d(w1), _d(w2), _d(w3)
+    B, H, Tq, d = q.shape
+    Tkv = k.shape[2]
+    hid = w1.shape[2]
+    assert w1.shape == (B, H, hid, d) and w3.shape == w1.shape and w2.shape == (B, H, d, hid)
+    assert k.shape == (B, H, Tkv, d) and v.shape == k.shape and eta.shape == (B, H, Tkv)
+    if m is None:
+        m = (np.zeros_like(w1), np.zeros_like(w2), np.zeros_like(w3))
+    m = tuple(np.array(a, dtype=np.float64) for a in m)
+    out = np.zeros((B, H, Tq, d))
+    f1, f2, f3 = np.zeros_like(w1), np.zeros_like(w2), np.zeros_like(w3)
+    rc = lib.oracle_lact_swiglu_rule(_p(q), _p(k), _p(v), _p(eta), _p(w1), _p(w2), _p(w3),
+                                     _p(out), _p(f1), _p(f2), _p(f3), B, H, Tq, Tkv, d, hid, chunk,
+                                     loss, order, rownorm, rule, float(beta), ns_steps, float(lr),
+                                     _p(m[0]), _p(m[1]), _p(m[2]), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_lact_swiglu_rule failed with {rc}")
+    return out, f1, f2, f3, m

@@ -51,6 +51,12 @@
  *     is left as is.  Off when rownorm == 0.
  *  R9 LaCT MSE variant (not used by the workloads): L = 1/2 ||f(k) - v||^2.
  *  R10 silu(z) = z * sigmoid(z); silu'(z) = s (1 + z (1 - s)), s = sigmoid(z).
+ *  R11 LaCT update rules (section 3.3 names gradient descent, momentum and
+ *     Muon, which maps the matrix gradient through a Newton-Schulz iteration,
+ *     and gives no coefficients): momentum M <- beta M + G with step M; Muon
+ *     steps lr * NS_k(M) with the textbook cubic Newton-Schulz iteration for
+ *     the orthogonal polar factor started from M / ||M||_F; beta, k and lr
+ *     are parameters; the row rescale of R8 follows every rule.
  *
  * Parity: every function here is pinned by tests against closed forms and
  * brute force (causal linear attention, the delta rule, one-chunk dense
@@ -278,9 +284,69 @@ static void lact_chunk_grad(const double *w1, const double *w2, const double *w3
     }
 }
 
-/* Plain gradient-descent step W <- W - G on the three matrices, then R8. */
+/* Update rules (R11).  rule 0: plain gradient descent.  rule 1:
+ * momentum, M <- beta M + G, step M.  rule 2: Muon, M as for momentum (M = G
+ * when beta == 0), step lr * NS_k(M), where NS_k is k steps of the cubic
+ * Newton-Schulz iteration for the orthogonal polar factor,
+ *     X_0 = M / ||M||_F,   X_{j+1} = 1.5 X_j - 0.5 X_j (X_j^T X_j),
+ * and the zero matrix maps to zero. */
+typedef struct {
+    int rule;
+    double beta;
+    int ns_steps;
+    double lr;
+    double *m1, *m2, *m3;   /* momentum buffers of this head (rules 1, 2 with beta != 0) */
+    double *x, *gram, *prod;   /* Newton-Schulz scratch */
+} lact_rule;
+
+static void newton_schulz(double *dst, int rows, int cols, int steps, lact_rule *u)
+{
+    const size_t n = (size_t)rows * cols;
+    double ss = 0.0;
+    for (size_t i = 0; i < n; ++i) ss += dst[i] * dst[i];
+    if (ss == 0.0) return;
+    const double inv = 1.0 / sqrt(ss);
+    for (size_t i = 0; i < n; ++i) u->x[i] = dst[i] * inv;
+    for (int it = 0; it < steps; ++it) {
+        /* gram = X^T X  (cols x cols) */
+        for (int i = 0; i < cols; ++i)
+            for (int j = 0; j < cols; ++j) {
+                double acc = 0.0;
+                for (int r = 0; r < rows; ++r) acc += u->x[(size_t)r * cols + i] * u->x[(size_t)r * cols + j];
+                u->gram[(size_t)i * cols + j] = acc;
+            }
+        /* prod = X gram */
+        for (int r = 0; r < rows; ++r)
+            for (int j = 0; j < cols; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < cols; ++i) acc += u->x[(size_t)r * cols + i] * u->gram[(size_t)i * cols + j];
+                u->prod[(size_t)r * cols + j] = acc;
+            }
+        for (size_t i = 0; i < n; ++i) u->x[i] = 1.5 * u->x[i] - 0.5 * u->prod[i];
+    }
+    for (size_t i = 0; i < n; ++i) dst[i] = u->x[i];
+}
+
+/* The step direction of one matrix (in place over its gradient g). */
+static void rule_direction(double *g, double *m, int rows, int cols, lact_rule *u)
+{
+    const size_t n = (size_t)rows * cols;
+    if (u->rule == 0) return;
+    if (m) {
+        for (size_t i = 0; i < n; ++i) {
+            m[i] = u->beta * m[i] + g[i];
+            g[i] = m[i];
+        }
+    }
+    if (u->rule == 2) {
+        newton_schulz(g, rows, cols, u->ns_steps, u);
+        for (size_t i = 0; i < n; ++i) g[i] *= u->lr;
+    }
+}
+
+/* Step W <- W - direction on the three matrices, then R8. */
 static void lact_update(double *w1, double *w2, double *w3, int d, int hid, int rownorm,
-                        lact_scratch *s)
+                        lact_scratch *s, lact_rule *u)
 {
     const size_t n13 = (size_t)hid * d, n2 = (size_t)d * hid;
     if (rownorm) {
@@ -288,6 +354,9 @@ static void lact_update(double *w1, double *w2, double *w3, int d, int hid, int 
         row_norms(w2, s->n2, d, hid);
         row_norms(w3, s->n3, hid, d);
     }
+    rule_direction(s->g1, u->m1, hid, d, u);
+    rule_direction(s->g2, u->m2, d, hid, u);
+    rule_direction(s->g3, u->m3, hid, d, u);
     for (size_t i = 0; i < n13; ++i) w1[i] -= s->g1[i];
     for (size_t i = 0; i < n2; ++i) w2[i] -= s->g2[i];
     for (size_t i = 0; i < n13; ++i) w3[i] -= s->g3[i];
@@ -300,7 +369,8 @@ static void lact_update(double *w1, double *w2, double *w3, int d, int hid, int 
 
 static void lact_head(const double *q, const double *k, const double *v, const double *eta,
                       double *w1, double *w2, double *w3, double *out, int Tq, int Tkv, int d,
-                      int hid, int chunk, int loss, int order, int rownorm, lact_scratch *s)
+                      int hid, int chunk, int loss, int order, int rownorm, lact_scratch *s,
+                      lact_rule *u)
 {
     const size_t n13 = (size_t)hid * d, n2 = (size_t)d * hid;
     const int causal = (order == 0);
@@ -315,7 +385,7 @@ static void lact_head(const double *q, const double *k, const double *v, const d
         memset(s->g2, 0, sizeof(double) * n2);
         memset(s->g3, 0, sizeof(double) * n13);
         lact_chunk_grad(w1, w2, w3, k, v, eta, c0, c1, d, hid, loss, s);
-        lact_update(w1, w2, w3, d, hid, rownorm, s);
+        lact_update(w1, w2, w3, d, hid, rownorm, s, u);
     }
     if (!causal) {
         for (int t = 0; t < Tq; ++t)
@@ -326,17 +396,24 @@ static void lact_head(const double *q, const double *k, const double *v, const d
 /* q [B,H,Tq,d]; k, v [B,H,Tkv,d]; eta [B,H,Tkv];
  * w1_init, w3_init [B,H,hid,d]; w2_init [B,H,d,hid]; out [B,H,Tq,d];
  * w*_final like the inits.  loss: 0 inner product, 1 MSE.  order: 0 causal
- * (Tq == Tkv), 1 non-causal.  rownorm: 1 = R8 on, 0 = off. */
-int oracle_lact_swiglu(const double *q, const double *k, const double *v, const double *eta,
-                       const double *w1_init, const double *w2_init, const double *w3_init,
-                       double *out, double *w1_final, double *w2_final, double *w3_final, int B,
-                       int H, int Tq, int Tkv, int d, int hid, int chunk, int loss, int order,
-                       int rownorm, int nthreads)
+ * (Tq == Tkv), 1 non-causal.  rownorm: 1 = R8 on, 0 = off.
+ * rule: 0 gradient descent, 1 momentum, 2 Muon (see lact_rule); m1, m2, m3
+ * (like w1, w2, w3) are the momentum buffers, read and updated in place, used
+ * by rule 1 and by rule 2 when beta != 0 (may be NULL otherwise). */
+int oracle_lact_swiglu_rule(const double *q, const double *k, const double *v, const double *eta,
+                            const double *w1_init, const double *w2_init, const double *w3_init,
+                            double *out, double *w1_final, double *w2_final, double *w3_final,
+                            int B, int H, int Tq, int Tkv, int d, int hid, int chunk, int loss,
+                            int order, int rownorm, int rule, double beta, int ns_steps, double lr,
+                            double *m1, double *m2, double *m3, int nthreads)
 {
     if (B < 1 || H < 1 || Tq < 0 || Tkv < 0 || d < 1 || hid < 1 || chunk < 1) return ORACLE_EINVAL;
     if (loss != 0 && loss != 1) return ORACLE_EINVAL;
     if (order != 0 && order != 1) return ORACLE_EINVAL;
     if (order == 0 && Tq != Tkv) return ORACLE_EINVAL;
+    if (rule < 0 || rule > 2 || (rule == 2 && ns_steps < 0)) return ORACLE_EINVAL;
+    const int use_m = rule == 1 || (rule == 2 && beta != 0.0);
+    if (use_m && (!m1 || !m2 || !m3)) return ORACLE_EINVAL;
     const int NH = B * H;
     const size_t n13 = (size_t)hid * d, n2 = (size_t)d * hid;
     int err = ORACLE_OK;
@@ -345,7 +422,9 @@ int oracle_lact_swiglu(const double *q, const double *k, const double *v, const 
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
     for (int h = 0; h < NH; ++h) {
-        const size_t nscr = 2 * n13 + n2 + 6 * (size_t)hid + 3 * (size_t)d + 2 * (size_t)hid + (size_t)d;
+        const size_t big = (size_t)(hid > d ? hid : d);
+        const size_t nns = (rule == 2) ? 2 * n13 + big * big : 0;
+        const size_t nscr = 2 * n13 + n2 + 6 * (size_t)hid + 3 * (size_t)d + 2 * (size_t)hid + (size_t)d + nns;
         double *buf = (double *)malloc(sizeof(double) * nscr);
         if (!buf) {
             err = ORACLE_ENOMEM;
@@ -366,6 +445,17 @@ int oracle_lact_swiglu(const double *q, const double *k, const double *v, const 
         s.n2 = p; p += d;
         s.dy = p; p += d;
         s.y = p; p += d;
+        lact_rule u;
+        u.rule = rule;
+        u.beta = beta;
+        u.ns_steps = ns_steps;
+        u.lr = lr;
+        u.m1 = use_m ? m1 + (size_t)h * n13 : NULL;
+        u.m2 = use_m ? m2 + (size_t)h * n2 : NULL;
+        u.m3 = use_m ? m3 + (size_t)h * n13 : NULL;
+        u.x = p; p += (rule == 2) ? n13 : 0;
+        u.prod = p; p += (rule == 2) ? n13 : 0;
+        u.gram = p;
         double *w1 = w1_final + (size_t)h * n13, *w3 = w3_final + (size_t)h * n13;
         double *w2 = w2_final + (size_t)h * n2;
         memcpy(w1, w1_init + (size_t)h * n13, sizeof(double) * n13);
@@ -373,10 +463,21 @@ int oracle_lact_swiglu(const double *q, const double *k, const double *v, const 
         memcpy(w3, w3_init + (size_t)h * n13, sizeof(double) * n13);
         lact_head(q + (size_t)h * Tq * d, k + (size_t)h * Tkv * d, v + (size_t)h * Tkv * d,
                   eta + (size_t)h * Tkv, w1, w2, w3, out + (size_t)h * Tq * d, Tq, Tkv, d, hid,
-                  chunk, loss, order, rownorm, &s);
+                  chunk, loss, order, rownorm, &s, &u);
         free(buf);
     }
     return err;
+}
+
+int oracle_lact_swiglu(const double *q, const double *k, const double *v, const double *eta,
+                       const double *w1_init, const double *w2_init, const double *w3_init,
+                       double *out, double *w1_final, double *w2_final, double *w3_final, int B,
+                       int H, int Tq, int Tkv, int d, int hid, int chunk, int loss, int order,
+                       int rownorm, int nthreads)
+{
+    return oracle_lact_swiglu_rule(q, k, v, eta, w1_init, w2_init, w3_init, out, w1_final,
+                                   w2_final, w3_final, B, H, Tq, Tkv, d, hid, chunk, loss, order,
+                                   rownorm, 0, 0.0, 0, 0.0, NULL, NULL, NULL, nthreads);
 }
 
 /* Number of threads an OpenMP region would use (1 without OpenMP). */

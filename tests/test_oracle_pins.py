@@ -450,3 +450,160 @@ def test_handworked_lact_two_chunks():
     np.testing.assert_allclose(f1[0, 0, 0], w1n, rtol=0, atol=1e-15)
     np.testing.assert_allclose(f3[0, 0, 0], w3n, rtol=0, atol=1e-15)
     np.testing.assert_allclose(f2[0, 0, :, 0], [1.0, 0.0], rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# LaCT update rules: momentum and Muon ("LaCT" section 3.3 names gradient
+# descent, momentum and Muon -- a Newton-Schulz map of the matrix gradient --
+# without coefficients; the readings are beta, k steps of the cubic iteration
+# from M / ||M||_F, and a step size lr).
+# --------------------------------------------------------------------------
+def _ns_by_svd(m, steps):
+    """Closed form of k Newton-Schulz steps: X_k = U f^k(S / ||M||_F) V^T with
+    f(s) = 1.5 s - 0.5 s^3, from numpy's SVD."""
+    u, sv, vt = np.linalg.svd(m, full_matrices=False)
+    s = sv / np.sqrt(np.sum(m * m))
+    for _ in range(steps):
+        s = 1.5 * s - 0.5 * s ** 3
+    return (u * s) @ vt
+
+
+@pytest.mark.parametrize("shape", [(12, 5), (5, 12), (9, 9)])
+@pytest.mark.parametrize("steps", [1, 3, 5])
+def test_newton_schulz_matches_svd_closed_form(shape, steps):
+    rng = np.random.default_rng(51)
+    m = rng.standard_normal(shape)
+    assert rel(dense.newton_schulz(m, steps), _ns_by_svd(m, steps)) < 1e-12
+
+
+def test_newton_schulz_fixed_points():
+    """A rank-one matrix s u v^T maps to u v^T after any number of steps; the
+    iteration converges to the polar factor; zero maps to zero."""
+    rng = np.random.default_rng(52)
+    u = rng.standard_normal(7)
+    u /= np.linalg.norm(u)
+    v = rng.standard_normal(4)
+    v /= np.linalg.norm(v)
+    assert rel(dense.newton_schulz(3.7 * np.outer(u, v), 5), np.outer(u, v)) < 1e-14
+    m = rng.standard_normal((6, 3))
+    uu, _, vt = np.linalg.svd(m, full_matrices=False)
+    assert rel(dense.newton_schulz(m, 40), uu @ vt) < 1e-10
+    assert np.array_equal(dense.newton_schulz(np.zeros((3, 2)), 5), np.zeros((3, 2)))
+
+
+def _lact_small(seed, T=24, d=6, hid=10, B=1, H=2):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, T, d)) / np.sqrt(d)
+    k = rng.standard_normal((B, H, T, d)) / np.sqrt(d)
+    v = rng.standard_normal((B, H, T, d))
+    eta = rng.uniform(0.05, 0.3, (B, H, T))
+    w1 = rng.standard_normal((B, H, hid, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((B, H, d, hid)) / np.sqrt(hid)
+    w3 = rng.standard_normal((B, H, hid, d)) / np.sqrt(d)
+    return q, k, v, eta, w1, w2, w3
+
+
+def _gd_gradient(k, v, eta, w1, w2, w3, loss):
+    """Chunk gradients extracted from the (pinned) gradient-descent oracle: one
+    chunk without the row rescale moves each W by exactly minus its gradient."""
+    _, f1, f2, f3 = oracle.lact_swiglu(k[:, :, :1] * 0, k, v, eta, w1, w2, w3, chunk=k.shape[2],
+                                       loss=loss, order=oracle.NONCAUSAL, rownorm=0)
+    return w1 - f1, w2 - f2, w3 - f3
+
+
+def test_lact_rule_gd_and_beta_zero_momentum_equal_plain_gd():
+    q, k, v, eta, w1, w2, w3 = _lact_small(53)
+    ref = oracle.lact_swiglu(q, k, v, eta, w1, w2, w3, chunk=8, loss=0, order=0, rownorm=1)
+    for rule in (oracle.RULE_GD, oracle.RULE_MOMENTUM):
+        got = oracle.lact_swiglu_rule(q, k, v, eta, w1, w2, w3, chunk=8, loss=0, order=0,
+                                      rownorm=1, rule=rule, beta=0.0)
+        for a, b in zip(got[:4], ref):
+            assert rel(a, b) < 1e-13
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+def test_lact_momentum_composes_gd_gradients(loss):
+    """Three chunks of momentum: M_c = beta M_{c-1} + G_c(W_c), W_{c+1} = W_c - M_c,
+    with every G_c taken from the gradient-descent oracle at the current weights;
+    the final momentum buffers are M_2."""
+    q, k, v, eta, w1, w2, w3 = _lact_small(54, T=24)
+    beta, chunk = 0.6, 8
+    out, f1, f2, f3, m = oracle.lact_swiglu_rule(q, k, v, eta, w1, w2, w3, chunk=chunk, loss=loss,
+                                                 order=0, rownorm=0, rule=oracle.RULE_MOMENTUM,
+                                                 beta=beta)
+    W = [w1.copy(), w2.copy(), w3.copy()]
+    M = [np.zeros_like(w1), np.zeros_like(w2), np.zeros_like(w3)]
+    outs = []
+    for c0 in range(0, 24, chunk):
+        sl = slice(c0, c0 + chunk)
+        outs.append(oracle.lact_swiglu(q[:, :, sl], k[:, :, :0], v[:, :, :0], eta[:, :, :0], *W,
+                                       chunk=chunk, loss=loss, order=oracle.NONCAUSAL,
+                                       rownorm=0)[0])
+        G = _gd_gradient(k[:, :, sl], v[:, :, sl], eta[:, :, sl], *W, loss)
+        M = [beta * a + g for a, g in zip(M, G)]
+        W = [w - a for w, a in zip(W, M)]
+    assert rel(out, np.concatenate(outs, axis=2)) < 1e-12
+    for a, b in zip((f1, f2, f3), W):
+        assert rel(a, b) < 1e-12
+    for a, b in zip(m, M):
+        assert rel(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_lact_muon_step_is_lr_times_svd_polar_map(beta):
+    """Two chunks of Muon without the row rescale: W <- W - lr * U f^k(S/||M||) V^T
+    of the momentum, with gradients from the gradient-descent oracle and the
+    Newton-Schulz map from numpy's SVD."""
+    q, k, v, eta, w1, w2, w3 = _lact_small(55, T=16)
+    lr, steps, chunk = 0.03, 5, 8
+    _, f1, f2, f3, m = oracle.lact_swiglu_rule(q, k, v, eta, w1, w2, w3, chunk=chunk, loss=0,
+                                               order=0, rownorm=0, rule=oracle.RULE_MUON,
+                                               beta=beta, ns_steps=steps, lr=lr)
+    W = [w1.copy(), w2.copy(), w3.copy()]
+    M = [np.zeros_like(w1), np.zeros_like(w2), np.zeros_like(w3)]
+    for c0 in range(0, 16, chunk):
+        sl = slice(c0, c0 + chunk)
+        G = _gd_gradient(k[:, :, sl], v[:, :, sl], eta[:, :, sl], *W, 0)
+        M = [beta * a + g for a, g in zip(M, G)]
+        for i in range(3):
+            for h in range(2):
+                W[i][0, h] = W[i][0, h] - lr * _ns_by_svd(M[i][0, h], steps)
+    for a, b in zip((f1, f2, f3), W):
+        assert rel(a, b) < 1e-11
+    if beta:
+        for a, b in zip(m, M):
+            assert rel(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("rule,beta", [(1, 0.7), (2, 0.0), (2, 0.8)])
+@pytest.mark.parametrize("order", [0, 1])
+def test_lact_rule_dense_form_matches_token_loop(rule, beta, order):
+    q, k, v, eta, w1, w2, w3 = _lact_small(56, T=20)
+    kw = dict(chunk=8, loss=1, order=order, rownorm=1, rule=rule, beta=beta, ns_steps=3, lr=0.05)
+    out, f1, f2, f3, m = oracle.lact_swiglu_rule(q, k, v, eta, w1, w2, w3, **kw)
+    for h in range(2):
+        mm = [np.zeros_like(w1[0, h]), np.zeros_like(w2[0, h]), np.zeros_like(w3[0, h])]
+        o, a1, a2, a3 = dense.lact_head(q[0, h], k[0, h], v[0, h], eta[0, h], w1[0, h], w2[0, h],
+                                        w3[0, h], m=mm, **kw)
+        assert rel(o, out[0, h]) < 1e-11
+        for a, b in zip((a1, a2, a3), (f1, f2, f3)):
+            assert rel(a, b[0, h]) < 1e-11
+        if rule == 1 or beta:
+            for a, b in zip(mm, m):
+                assert rel(a, b[0, h]) < 1e-11
+
+
+def test_lact_momentum_state_carry():
+    """Two calls carrying weights and momentum buffers = one call (chunk-aligned split)."""
+    q, k, v, eta, w1, w2, w3 = _lact_small(57, T=24)
+    kw = dict(chunk=8, loss=0, rownorm=1, rule=oracle.RULE_MUON, beta=0.9, ns_steps=2, lr=0.02)
+    o, f1, f2, f3, m = oracle.lact_swiglu_rule(q, k, v, eta, w1, w2, w3, order=0, **kw)
+    a = slice(0, 16)
+    b = slice(16, 24)
+    oa, g1, g2, g3, ma = oracle.lact_swiglu_rule(q[:, :, a], k[:, :, a], v[:, :, a], eta[:, :, a],
+                                                 w1, w2, w3, order=0, **kw)
+    ob, h1, h2, h3, mb = oracle.lact_swiglu_rule(q[:, :, b], k[:, :, b], v[:, :, b], eta[:, :, b],
+                                                 g1, g2, g3, order=0, m=ma, **kw)
+    assert rel(np.concatenate([oa, ob], axis=2), o) < 1e-13
+    for x, y in zip((h1, h2, h3) + tuple(mb), (f1, f2, f3) + tuple(m)):
+        assert rel(x, y) < 1e-13
