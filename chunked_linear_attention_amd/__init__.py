@@ -5,13 +5,15 @@ a C ABI, declared in include/ttt.h).  This package is a thin binding: it
 checks tensors, allocates outputs and the workspace with torch (device memory
 and the current stream only) and calls the library.  Nothing here computes.
 """
-from .ops import (CAUSAL, NONCAUSAL, LOSS_DOT, LOSS_MSE, lact_swiglu_decode,
-                  lact_swiglu_decode_workspace_bytes, lact_swiglu_fwd,
+from .ops import (CAUSAL, NONCAUSAL, LOSS_DOT, LOSS_MSE, RULE_GD, RULE_MOMENTUM, RULE_MUON,
+                  lact_swiglu_decode, lact_swiglu_decode_workspace_bytes, lact_swiglu_fwd,
+                  lact_swiglu_fwd_rule, lact_swiglu_rule_workspace_bytes,
                   lact_swiglu_workspace_bytes, ttt_linear_decode, ttt_linear_fwd,
                   ttt_linear_workspace_bytes)
 from ._lib import TTTError, load as load_library, status_string
 
 __all__ = ["ttt_linear_fwd", "lact_swiglu_fwd", "ttt_linear_workspace_bytes",
            "lact_swiglu_workspace_bytes", "ttt_linear_decode", "lact_swiglu_decode",
-           "lact_swiglu_decode_workspace_bytes", "TTTError", "load_library", "status_string",
+           "lact_swiglu_decode_workspace_bytes", "lact_swiglu_fwd_rule",
+           "lact_swiglu_rule_workspace_bytes", "RULE_GD", "RULE_MOMENTUM", "RULE_MUON", "TTTError", "load_library", "status_string",
            "CAUSAL", "NONCAUSAL", "LOSS_DOT", "LOSS_MSE"]

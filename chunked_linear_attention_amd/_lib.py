@@ -16,7 +16,8 @@ TTT_EHIP = -4
 
 EXPORTS = ("ttt_status_string", "ttt_abi_version", "ttt_linear_workspace_bytes", "ttt_linear_fwd",
            "lact_swiglu_workspace_bytes", "lact_swiglu_fwd", "ttt_linear_decode",
-           "lact_swiglu_decode_workspace_bytes", "lact_swiglu_decode")
+           "lact_swiglu_decode_workspace_bytes", "lact_swiglu_decode",
+           "lact_swiglu_rule_workspace_bytes", "lact_swiglu_fwd_rule")
 
 _lock = threading.Lock()
 _lib = None
@@ -52,6 +53,12 @@ def load() -> ctypes.CDLL:
         lib.lact_swiglu_fwd.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp] + [i] * 10 + \
             [vp, sz, vp]
         lib.lact_swiglu_fwd.restype = i
+        f = ctypes.c_float
+        lib.lact_swiglu_rule_workspace_bytes.argtypes = [i] * 11
+        lib.lact_swiglu_rule_workspace_bytes.restype = sz
+        lib.lact_swiglu_fwd_rule.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp] + \
+            [i] * 11 + [f, i, f, vp, vp, vp, vp, sz, vp]
+        lib.lact_swiglu_fwd_rule.restype = i
         lib.ttt_linear_decode.argtypes = [vp, vp, vp, i, vp, vp, vp, i, vp, i, i, i, i, vp]
         lib.ttt_linear_decode.restype = i
         lib.lact_swiglu_decode_workspace_bytes.argtypes = [i] * 5

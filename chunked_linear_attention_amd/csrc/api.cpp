@@ -97,22 +97,31 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 
-size_t lact_swiglu_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden, int chunk,
-                                   int loss, int order, int dtype)
+size_t lact_swiglu_rule_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden,
+                                        int chunk, int loss, int order, int dtype, int rule)
 {
-    if (!valid_enums(dtype, loss, order)) return 0;
+    if (!valid_enums(dtype, loss, order) || rule < TTT_RULE_GD || rule > TTT_RULE_MUON) return 0;
     if (check_dims(B, H, Tq, Tkv, d, chunk, order) != TTT_OK || hidden < 1) return 0;
     if (!lact_supported(dtype, d, hidden, chunk, Tkv)) return 0;
     tttk::LactShape s{B * H, Tq, Tkv, d, hidden, chunk, loss, order, 1};
+    s.rule = rule;
     return tttk::lact_plan(s).bytes;
 }
 
-ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtype,
-                           const float *eta, const float *w1_init, const float *w2_init,
-                           const float *w3_init, void *out, float *w1_final, float *w2_final,
-                           float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
-                           int chunk, int loss, int order, int rownorm, void *workspace,
-                           size_t workspace_bytes, void *stream)
+size_t lact_swiglu_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden, int chunk,
+                                   int loss, int order, int dtype)
+{
+    return lact_swiglu_rule_workspace_bytes(B, H, Tq, Tkv, d, hidden, chunk, loss, order, dtype,
+                                            TTT_RULE_GD);
+}
+
+ttt_status lact_swiglu_fwd_rule(const void *q, const void *k, const void *v, int dtype,
+                                const float *eta, const float *w1_init, const float *w2_init,
+                                const float *w3_init, void *out, float *w1_final, float *w2_final,
+                                float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
+                                int chunk, int loss, int order, int rownorm, int rule, float beta,
+                                int ns_steps, float muon_lr, float *m1, float *m2, float *m3,
+                                void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
     ttt_status st = check_dims(B, H, Tq, Tkv, d, chunk, order);
@@ -124,14 +133,46 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
     if (Tq > 0 && (!q || !out || !aligned16(q) || !aligned16(out))) return TTT_EINVAL;
     if (Tkv > 0 && (!k || !v || !eta || !aligned16(k) || !aligned16(v) || !aligned16(eta)))
         return TTT_EINVAL;
+    // update rule: the momentum coefficient lies in [0, 1]; Muon takes 1..16
+    // Newton-Schulz steps and a finite step size >= 0
+    if (rule < TTT_RULE_GD || rule > TTT_RULE_MUON) return TTT_EINVAL;
+    if (rule != TTT_RULE_GD && !(beta >= 0.f && beta <= 1.f)) return TTT_EINVAL;
+    if (rule == TTT_RULE_MUON && (ns_steps < 1 || ns_steps > 16 || !(muon_lr >= 0.f) ||
+                                  muon_lr > 3.0e38f))
+        return TTT_EINVAL;
+    const bool use_m = rule == TTT_RULE_MOMENTUM || (rule == TTT_RULE_MUON && beta != 0.f);
+    if (use_m) {
+        const float *ms[3] = {m1, m2, m3};
+        for (const float *p : ms)
+            if (!p || !aligned16(p)) return TTT_EINVAL;
+    }
     if (!lact_supported(dtype, d, hidden, chunk, Tkv)) return TTT_EUNSUPPORTED;
     tttk::LactShape s{B * H, Tq, Tkv, d, hidden, chunk, loss, order, rownorm};
+    s.rule = rule;
+    s.beta = rule == TTT_RULE_GD ? 0.f : beta;
+    s.ns_steps = rule == TTT_RULE_MUON ? ns_steps : 0;
+    s.lr = rule == TTT_RULE_MUON ? muon_lr : 0.f;
     tttk::LactPlan pl = tttk::lact_plan(s);
     if (pl.bytes > 0 && (!workspace || !aligned16(workspace))) return TTT_EINVAL;
     if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
     hipError_t e = tttk::lact_launch(s, pl, q, k, v, eta, w1_init, w2_init, w3_init, out, w1_final,
-                                     w2_final, w3_final, workspace, (hipStream_t)stream);
+                                     w2_final, w3_final, workspace, (hipStream_t)stream,
+                                     use_m ? m1 : nullptr, use_m ? m2 : nullptr,
+                                     use_m ? m3 : nullptr);
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
+ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtype,
+                           const float *eta, const float *w1_init, const float *w2_init,
+                           const float *w3_init, void *out, float *w1_final, float *w2_final,
+                           float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
+                           int chunk, int loss, int order, int rownorm, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    return lact_swiglu_fwd_rule(q, k, v, dtype, eta, w1_init, w2_init, w3_init, out, w1_final,
+                                w2_final, w3_final, B, H, Tq, Tkv, d, hidden, chunk, loss, order,
+                                rownorm, TTT_RULE_GD, 0.f, 0, 0.f, nullptr, nullptr, nullptr,
+                                workspace, workspace_bytes, stream);
 }
 
 ttt_status ttt_linear_decode(const void *q, const void *k, const void *v, int dtype,

@@ -236,8 +236,15 @@ struct LactParams {
     bf16 *dh1t;    // [NH][hid][cpad]
     bf16 *dh3t;    // [NH][hid][cpad]
     bf16 *gq;      // [NH][2 parts][qpad][hid]  G of the queries (or of the keys, MSE), hi/lo
-    float *part;   // [splitk][NH][3][hid * d] gradient partials
+    float *part;   // [splitk][NH][3][hid * d] gradient partials; under Muon split 0 then
+                   //   holds the momentum-step direction and the Newton-Schulz iterate (fp32)
     int nslots;
+    int rule;      // 0 gradient descent, 1 momentum, 2 Muon
+    float beta, lr;
+    float *m1, *m2, *m3;   // momentum buffers (like w1, w2, w3), or null
+    bf16 *nsb;     // [2][NH][3][hid * d] bf16 copies of the iterate (ping-pong)
+    bf16 *gram;    // [NH][3][d][d] bf16 Gram matrix of the iterate
+    float *diag;   // [NH][3][d] fp32 diagonal of the first Gram matrix
 };
 
 // Row of W1 (which = 0) or W3 (which = 1) hidden unit h inside the packed
@@ -579,9 +586,13 @@ __global__ __launch_bounds__(256) void lact_wgrad(LactParams p, int c)
 }
 
 // ---------------------------------------------------------------------------
-// update: one wave per row of W1, W3 (length d) or W2 (length hid):
-// W <- W - sum of the split partials, then the row back to its old L2 norm;
-// writes the fp32 master and the bf16 copy of slot `dst_slot`.
+// update: one wave per row of W1, W3 (length d) or W2 (length hid).
+// phase 0: W <- W - D, then the row back to its old L2 norm; writes the fp32
+//   master and the bf16 copy of slot `dst_slot`.  D = the summed gradient G
+//   (gradient descent), M = beta M + G (momentum, M written back), or lr X_k
+//   (Muon: the Newton-Schulz iterate left in partial split 0).
+// phase 1 (Muon, before the iteration): D = G or M = beta M + G, written in
+//   place over partial split 0 (fp32) and as bf16 into the first iterate copy.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -590,7 +601,7 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-__global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot)
+__global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot, int phase)
 {
     const int lane = threadIdx.x & 63;
     const int rows_per_head = 2 * p.hid + p.d;
@@ -603,6 +614,23 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot)
     else { which = 2; row = r - 2 * p.hid; len = p.hid; }
     const long n13 = (long)p.hid * p.d;
     float *w = (which == 0 ? p.w1 : which == 1 ? p.w3 : p.w2) + (long)h * n13 + (long)row * len;
+    const long eoff = ((long)h * 3 + which) * n13 + (long)row * len;  // element 0 of the row
+    float *mrow = nullptr;
+    if (p.rule == 1 || (p.rule == 2 && p.beta != 0.f))
+        mrow = (which == 0 ? p.m1 : which == 1 ? p.m3 : p.m2) + (long)h * n13 + (long)row * len;
+    if (phase == 1) {
+        for (int col = lane; col < len; col += 64) {
+            float gsum = 0.f;
+            for (int s = 0; s < p.splitk; ++s) gsum += p.part[(long)s * p.NH * 3 * n13 + eoff + col];
+            if (mrow) {
+                gsum += p.beta * mrow[col];
+                mrow[col] = gsum;
+            }
+            p.part[eoff + col] = gsum;
+            p.nsb[eoff + col] = (bf16)gsum;
+        }
+        return;
+    }
     constexpr int MAXE = 16;  // len <= 1024 = 16 x 64
     float nv[MAXE];
     float so = 0.f, sn = 0.f;
@@ -612,10 +640,18 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot)
         nv[e] = 0.f;
         if (col < len) {
             const float old = w[col];
-            float gsum = 0.f;
-            for (int s = 0; s < p.splitk; ++s)
-                gsum += p.part[(((long)s * p.NH + h) * 3 + which) * n13 + (long)row * len + col];
-            const float x = old - gsum;
+            float dir;
+            if (p.rule == 2) {
+                dir = p.lr * p.part[eoff + col];
+            } else {
+                dir = 0.f;
+                for (int s = 0; s < p.splitk; ++s) dir += p.part[(long)s * p.NH * 3 * n13 + eoff + col];
+                if (mrow) {
+                    dir += p.beta * mrow[col];
+                    mrow[col] = dir;
+                }
+            }
+            const float x = old - dir;
             so += old * old;
             sn += x * x;
             nv[e] = x;
@@ -631,6 +667,10 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot)
     for (int e = 0; e < MAXE; ++e) {
         const int col = lane + 64 * e;
         if (col < len) {
+            // rounded once: the bf16 pair below must encode exactly the stored
+            // master (a product fused into the split would give a different lo
+            // part than a later call rebuilding the pair from the master)
+#pragma clang fp contract(off)
             const float x = nv[e] * scale;
             w[col] = x;
             bf16 hi, lo;
@@ -645,6 +685,108 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot)
                 p.w2b[slot_off2(p, dst_slot, h, 1) + o] = lo;
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Muon: k steps of the cubic Newton-Schulz iteration for the orthogonal polar
+// factor of each matrix's step direction D ("LaCT" section 3.3 names Muon's
+// Newton-Schulz map without coefficients; the textbook cubic form is used):
+//     X_0 = D / ||D||_F,   X_{j+1} = 1.5 X_j - 0.5 X_j (X_j^T X_j).
+// With T the tall view of a matrix (W1, W3 gradients [hid][d] as they are,
+// W2's [d][hid] transposed) the Gram matrix T^T T is d x d for all three, and
+// the product is written as T (T^T T) for W1 and W3 and (T^T T) T^T for W2,
+// so every launch covers the three matrices of all heads.  Step 0 runs on the
+// unscaled D: its Gram diagonal (fp32) gives ||D||_F^2, and the apply scales
+// by it.  Operands are bf16 copies of the iterate; the iterate itself and all
+// accumulations are fp32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
+{
+    __shared__ GemmLds L;
+    const int d = p.d, hid = p.hid;
+    const int tpm = d / 128;
+    int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int tile = bid % (tpm * tpm);
+    bid /= tpm * tpm;
+    const int which = bid % 3, h = bid / 3;
+    const int tm = tile / tpm, tn = tile % tpm;
+    const long n13 = (long)hid * d;
+    const bf16 *x = p.nsb + (long)(step & 1) * p.NH * 3 * n13 + ((long)h * 3 + which) * n13;
+    bf16 *gr = p.gram + ((long)h * 3 + which) * d * d;
+    float *dg = p.diag + ((long)h * 3 + which) * d;
+    auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int m = mb + 16 * i + 4 * g + j, n = nb + 16 * q + mm;
+                    gr[(long)m * d + n] = (bf16)acc[i][q][j];
+                    if (step == 0 && m == n) dg[m] = acc[i][q][j];
+                }
+    };
+    const bf16 *as[1] = {x};
+    if (which < 2)  // T = X [hid][d]: T^T T, both operands k-major
+        gemm_nt_tile<true, true>(L, as, d, as, d, d, d, hid, 1, tm * 128, tn * 128, hid, epi);
+    else            // T = X^T, X [d][hid]: X X^T
+        gemm_nt_tile<false, false>(L, as, hid, as, hid, d, d, hid, 1, tm * 128, tn * 128, 1 << 30, epi);
+}
+
+__global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
+{
+    __shared__ GemmLds L;
+    __shared__ float red[4];
+    const int d = p.d, hid = p.hid;
+    const int tpm = (hid / 128) * (d / 128);
+    int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int tile = bid % tpm;
+    bid /= tpm;
+    const int which = bid % 3, h = bid / 3;
+    const long n13 = (long)hid * d;
+    const long moff = ((long)h * 3 + which) * n13;
+    const bf16 *x = p.nsb + (long)(step & 1) * p.NH * 3 * n13 + moff;
+    bf16 *xn = p.nsb + (long)((step + 1) & 1) * p.NH * 3 * n13 + moff;
+    float *xf = p.part + moff;
+    const bf16 *gr = p.gram + ((long)h * 3 + which) * d * d;
+    // step 0: the iterate is D itself; X_1 = (1.5 D - 0.5 D (D^T D) / s^2) / s, s = ||D||_F
+    float a = 1.5f, b = -0.5f;
+    if (step == 0) {
+        float ss = 0.f;
+        for (int e = threadIdx.x; e < d; e += 256) ss += p.diag[((long)h * 3 + which) * d + e];
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        ss = red[0] + red[1] + red[2] + red[3];
+        const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+        a = 1.5f * inv;
+        b = ss > 0.f ? -0.5f * inv / ss : 0.f;
+    }
+    const int N = (which < 2) ? d : hid;
+    auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const long e = (long)(mb + 16 * i + 4 * g + j) * N + nb + 16 * q + mm;
+                    const float v = a * xf[e] + b * acc[i][q][j];
+                    xf[e] = v;
+                    xn[e] = (bf16)v;
+                }
+    };
+    if (which < 2) {  // X [hid][d]: X G, G symmetric (row-major = its own transpose)
+        const int tm = tile / (d / 128), tn = tile % (d / 128);
+        const bf16 *as[1] = {x};
+        const bf16 *bs[1] = {gr};
+        gemm_nt_tile<false, false>(L, as, d, bs, d, hid, d, d, 1, tm * 128, tn * 128, 1 << 30, epi);
+    } else {          // X [d][hid]: G X, X read k-major
+        const int tm = tile / (hid / 128), tn = tile % (hid / 128);
+        const bf16 *as[1] = {gr};
+        const bf16 *bs[1] = {x};
+        gemm_nt_tile<false, true>(L, as, d, bs, hid, d, hid, d, 1, tm * 128, tn * 128, d, epi);
     }
 }
 
@@ -816,7 +958,10 @@ LactPlan lact_plan(const LactShape &s)
         pl.off[idx] = off;
         off = al256(off + bytes);
     };
-    // slots 0, 1 and 13 are not used
+    const bool muon = s.rule == 2;
+    take(0, muon ? 2 * NH * 3 * hid * d * 2 : 0);   // Newton-Schulz iterate, bf16 ping-pong
+    take(1, muon ? NH * 3 * d * d * 2 : 0);         // Gram matrices, bf16
+    take(13, muon ? NH * 3 * d * 4 : 0);            // first Gram diagonal, fp32
     take(2, s.loss == 1 ? NH * cpad * d * 2 : 0);  // dy
     take(3, (size_t)nslots * NH * 2 * 2 * hid * d * 2);  // w13b (hi, lo)
     take(4, (size_t)nslots * NH * 2 * d * hid * 2);      // w2b (hi, lo)
@@ -866,7 +1011,7 @@ static SideStream *side_stream()
 hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
                        const void *v, const float *eta, const float *w1, const float *w2,
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
-                       hipStream_t st)
+                       hipStream_t st, float *m1, float *m2, float *m3)
 {
     LactParams p;
     char *base = (char *)ws;
@@ -903,6 +1048,15 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     p.dh3t = (bf16 *)(base + pl.off[7]);
     p.gq = (bf16 *)(base + pl.off[8]);
     p.part = (float *)(base + pl.off[9]);
+    p.rule = s.rule;
+    p.beta = s.beta;
+    p.lr = s.lr;
+    p.m1 = m1;
+    p.m2 = m2;
+    p.m3 = m3;
+    p.nsb = (bf16 *)(base + pl.off[0]);
+    p.gram = (bf16 *)(base + pl.off[1]);
+    p.diag = (float *)(base + pl.off[13]);
 
     const long n3 = (long)s.NH * 3 * s.hid * s.d;
     const int wblocks = (int)((n3 + 255) / 256 < 4096 ? (n3 + 255) / 256 : 4096);
@@ -948,7 +1102,14 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
         }
         lact_fwdgrad<<<dim3(s.NH * (p.cpad / 128) * (s.hid / 128)), dim3(256), 0, st>>>(p, c, slot);
         lact_wgrad<<<dim3(s.NH * p.splitk * 3 * t13), dim3(256), 0, st>>>(p, c);
-        lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst);
+        if (s.rule == 2) {
+            lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst, 1);
+            for (int j = 0; j < s.ns_steps; ++j) {
+                lact_ns_gram<<<dim3(s.NH * 3 * (s.d / 128) * (s.d / 128)), dim3(256), 0, st>>>(p, j);
+                lact_ns_apply<<<dim3(s.NH * 3 * t13), dim3(256), 0, st>>>(p, j);
+            }
+        }
+        lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst, 0);
         if (side && (c + 1) * p.chunk < s.Tq) apply_chunk(c + 1);
     }
     if (side) {

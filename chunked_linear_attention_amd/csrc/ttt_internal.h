@@ -35,6 +35,10 @@ hipError_t linear_launch(const LinearShape &s, const LinearPlan &pl, const void 
 // ---- LaCT SwiGLU ---------------------------------------------------------------
 struct LactShape {
     int NH, Tq, Tkv, d, hid, chunk, loss, order, rownorm;
+    int rule = 0;        // 0 gradient descent, 1 momentum, 2 Muon
+    float beta = 0.f;    // momentum coefficient (rules 1, 2)
+    int ns_steps = 0;    // Newton-Schulz steps (rule 2)
+    float lr = 0.f;      // Muon step size (rule 2)
 };
 struct LactPlan {
     int nchunks;
@@ -46,7 +50,8 @@ LactPlan lact_plan(const LactShape &s);
 hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
                        const void *v, const float *eta, const float *w1, const float *w2,
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
-                       hipStream_t stream);
+                       hipStream_t stream, float *m1 = nullptr, float *m2 = nullptr,
+                       float *m3 = nullptr);
 
 // ---- decode steps (one token per head) ---------------------------------------------
 hipError_t linear_decode_launch(int NH, int d, int bf16, int loss, const void *q, const void *k,

@@ -77,6 +77,61 @@ def lact_swiglu_workspace_bytes(B, H, Tq, Tkv, d, hidden, chunk, loss, order, dt
                                                   _ORDER[order], _DT[dtype]))
 
 
+RULE_GD, RULE_MOMENTUM, RULE_MUON = 0, 1, 2
+_RULE = {"gd": RULE_GD, "momentum": RULE_MOMENTUM, "muon": RULE_MUON, RULE_GD: RULE_GD,
+         RULE_MOMENTUM: RULE_MOMENTUM, RULE_MUON: RULE_MUON}
+
+
+def lact_swiglu_rule_workspace_bytes(B, H, Tq, Tkv, d, hidden, chunk, loss, order, dtype,
+                                     rule) -> int:
+    return int(load().lact_swiglu_rule_workspace_bytes(B, H, Tq, Tkv, d, hidden, chunk,
+                                                       _LOSS[loss], _ORDER[order], _DT[dtype],
+                                                       _RULE[rule]))
+
+
+def lact_swiglu_fwd_rule(q, k, v, eta, w1, w2, w3, *, chunk: int, rule="gd", beta: float = 0.0,
+                         ns_steps: int = 5, muon_lr: float = 0.0, momentum=None, loss="dot",
+                         order="causal", rownorm: bool = True, out=None, w1_final=None,
+                         w2_final=None, w3_final=None, workspace=None, stream=None):
+    """LaCT SwiGLU forward with an update rule ("gd", "momentum", "muon").
+    ``momentum`` = (m1, m2, m3) fp32 buffers shaped like the weights, updated in
+    place (needed by "momentum", and by "muon" when beta != 0).
+    Returns (out, w1_final, w2_final, w3_final)."""
+    lib = load()
+    B, H, Tq, d = q.shape
+    Tkv = k.shape[2]
+    hid = w1.shape[2]
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dt)
+    _check(eta, "eta", torch.float32)
+    for t, n in ((w1, "w1"), (w2, "w2"), (w3, "w3")):
+        _check(t, n, torch.float32)
+    ms = (None, None, None) if momentum is None else tuple(momentum)
+    for t, w, n in zip(ms, (w1, w2, w3), ("m1", "m2", "m3")):
+        if t is not None:
+            _check(t, n, torch.float32)
+            if t.shape != w.shape:
+                raise ValueError(f"{n} must be shaped like its weight")
+    out = torch.empty_like(q) if out is None else out
+    w1_final = torch.empty_like(w1) if w1_final is None else w1_final
+    w2_final = torch.empty_like(w2) if w2_final is None else w2_final
+    w3_final = torch.empty_like(w3) if w3_final is None else w3_final
+    ls, od, ru = _LOSS[loss], _ORDER[order], _RULE[rule]
+    nbytes = lib.lact_swiglu_rule_workspace_bytes(B, H, Tq, Tkv, d, hid, chunk, ls, od, _DT[dt], ru)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.lact_swiglu_fwd_rule(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(eta), _ptr(w1),
+                                  _ptr(w2), _ptr(w3), _ptr(out), _ptr(w1_final), _ptr(w2_final),
+                                  _ptr(w3_final), B, H, Tq, Tkv, d, hid, chunk, ls, od,
+                                  int(bool(rownorm)), ru, float(beta), int(ns_steps),
+                                  float(muon_lr), _ptr(ms[0]), _ptr(ms[1]), _ptr(ms[2]),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "lact_swiglu_fwd_rule")
+    return out, w1_final, w2_final, w3_final
+
+
 def lact_swiglu_fwd(q, k, v, eta, w1, w2, w3, *, chunk: int, loss="dot", order="causal",
                     rownorm: bool = True, out=None, w1_final=None, w2_final=None, w3_final=None,
                     workspace=None, stream=None):

@@ -152,6 +152,42 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
                            size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * LaCT update rules ([LaCT] section 3.3 compares gradient descent, momentum
+ * and Muon, which maps the matrix-shaped gradient through a Newton-Schulz
+ * iteration; the pages give no coefficients).  With G the chunk's summed
+ * gradient of each matrix:
+ *   TTT_RULE_GD:       W <- W - G                         (lact_swiglu_fwd)
+ *   TTT_RULE_MOMENTUM: M <- beta M + G;  W <- W - M
+ *   TTT_RULE_MUON:     M <- beta M + G (M = G when beta == 0);
+ *                      W <- W - muon_lr * NS_k(M), where NS_k is k steps of the
+ *                      cubic Newton-Schulz iteration for the orthogonal polar
+ *                      factor, X_0 = M / ||M||_F, X <- 1.5 X - 0.5 X (X^T X),
+ *                      and the zero matrix maps to zero
+ * each followed by the row rescale when rownorm != 0.
+ * m1, m2, m3: momentum buffers shaped like w1, w2, w3 (fp32), read and
+ * updated in place across the call's chunks (pass zeros to start; carry them
+ * between calls like the weights).  Required by TTT_RULE_MOMENTUM and by
+ * TTT_RULE_MUON with beta != 0; ignored (may be NULL) otherwise.  They must
+ * not overlap any other argument.
+ * Limits: 0 <= beta <= 1; TTT_RULE_MUON takes 1 <= ns_steps <= 16 and a
+ * finite muon_lr >= 0; otherwise TTT_EINVAL.  The Newton-Schulz products run
+ * on bf16 matrix cores with fp32 accumulation and an fp32 iterate.  Everything
+ * else is as for lact_swiglu_fwd, whose workspace query this one extends.
+ * ------------------------------------------------------------------------ */
+typedef enum { TTT_RULE_GD = 0, TTT_RULE_MOMENTUM = 1, TTT_RULE_MUON = 2 } ttt_rule;
+
+size_t lact_swiglu_rule_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden,
+                                        int chunk, int loss, int order, int dtype, int rule);
+
+ttt_status lact_swiglu_fwd_rule(const void *q, const void *k, const void *v, int dtype,
+                                const float *eta, const float *w1_init, const float *w2_init,
+                                const float *w3_init, void *out, float *w1_final, float *w2_final,
+                                float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
+                                int chunk, int loss, int order, int rownorm, int rule, float beta,
+                                int ns_steps, float muon_lr, float *m1, float *m2, float *m3,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Decode steps: one token per (batch, head) on a carried state.
  *
  * TTT-Linear ([TTT] "TTT definition": one gradient step per token on the

@@ -141,3 +141,48 @@ def test_lact_decode_workspace_query():
     assert lib.lact_swiglu_decode_workspace_bytes(64, 4, 256, 512, 1) == 64 * 4 * 512 * 4
     assert lib.lact_swiglu_decode_workspace_bytes(1, 1, 96, 512, 1) == 0
     assert lib.lact_swiglu_decode_workspace_bytes(1, 1, 256, 512, 5) == 0
+
+
+def lact_rule(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, out=FAKE,
+             f1=FAKE, f2=FAKE, f3=FAKE, B=1, H=1, Tq=512, Tkv=512, d=128, hid=256, chunk=128, loss=0,
+             order=0, rownorm=1, rule=1, beta=0.9, ns=5, lr=0.02, m1=FAKE, m2=FAKE, m3=FAKE, ws=FAKE,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.lact_swiglu_fwd_rule(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w1"], a["w2"],
+                                    a["w3"], a["out"], a["f1"], a["f2"], a["f3"], a["B"], a["H"],
+                                    a["Tq"], a["Tkv"], a["d"], a["hid"], a["chunk"], a["loss"],
+                                    a["order"], a["rownorm"], a["rule"], a["beta"], a["ns"], a["lr"],
+                                    a["m1"], a["m2"], a["m3"], a["ws"], a["wsb"], a["stream"])
+
+
+# every case fails validation before a launch (wsb = 0 ends the valid ones with EWORKSPACE)
+@pytest.mark.parametrize("kw,code", [
+    (dict(), _lib.TTT_EWORKSPACE),
+    (dict(rule=3), _lib.TTT_EINVAL), (dict(rule=-1), _lib.TTT_EINVAL),
+    (dict(beta=-0.1), _lib.TTT_EINVAL), (dict(beta=1.5), _lib.TTT_EINVAL),
+    (dict(beta=float("nan")), _lib.TTT_EINVAL),
+    (dict(m2=None), _lib.TTT_EINVAL), (dict(m3=FAKE + 4), _lib.TTT_EINVAL),
+    (dict(rule=2, ns=0), _lib.TTT_EINVAL), (dict(rule=2, ns=17), _lib.TTT_EINVAL),
+    (dict(rule=2, lr=-1.0), _lib.TTT_EINVAL), (dict(rule=2, lr=float("inf")), _lib.TTT_EINVAL),
+    (dict(rule=2, lr=float("nan")), _lib.TTT_EINVAL),
+    # Muon without momentum needs no buffers; gradient descent ignores beta and the buffers
+    (dict(rule=2, beta=0.0, m1=None, m2=None, m3=None), _lib.TTT_EWORKSPACE),
+    (dict(rule=2, beta=0.5, m1=None), _lib.TTT_EINVAL),
+    (dict(rule=0, beta=7.0, m1=None, m2=None, m3=None), _lib.TTT_EWORKSPACE),
+    (dict(d=64), _lib.TTT_EUNSUPPORTED),
+])
+def test_lact_rule_validation(kw, code):
+    assert lact_rule(_lib.load(), **kw) == code
+
+
+def test_lact_rule_workspace_query():
+    lib = _lib.load()
+    args = (1, 4, 4096, 4096, 256, 512, 2048, 0, 0, 1)
+    gd = lib.lact_swiglu_rule_workspace_bytes(*args, 0)
+    assert gd == lib.lact_swiglu_workspace_bytes(*args)
+    assert lib.lact_swiglu_rule_workspace_bytes(*args, 1) == gd
+    # Muon adds two bf16 iterate copies, the Gram matrices and their diagonal
+    extra = 2 * 4 * 3 * 512 * 256 * 2 + 4 * 3 * 256 * 256 * 2 + 4 * 3 * 256 * 4
+    assert extra <= lib.lact_swiglu_rule_workspace_bytes(*args, 2) - gd <= extra + 3 * 256
+    assert lib.lact_swiglu_rule_workspace_bytes(*args, 3) == 0
