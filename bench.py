@@ -168,7 +168,10 @@ def lact_alg(NH, Tq, Tkv, d, hid, order):
     return flops, byts
 
 
-def bench_lact(wl, steps, warmup):
+def bench_lact(wl, steps, warmup, rule=None):
+    """One LaCT workload.  rule = None (gradient descent through lact_swiglu_fwd)
+    or a dict of lact_swiglu_fwd_rule arguments (rule, beta, ns_steps, muon_lr);
+    Muon's flops add 4 hid d^2 per matrix and Newton-Schulz step per chunk."""
     import numpy as np
     import torch
     import chunked_linear_attention_amd as cla
@@ -184,11 +187,25 @@ def bench_lact(wl, steps, warmup):
                                              wl.chunk, wl.loss, wl.order, torch.bfloat16)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
+    if rule is not None:
+        nbytes = cla.lact_swiglu_rule_workspace_bytes(wl.B, wl.H, s["q"].shape[2], wl.Tkv, wl.d,
+                                                      wl.hid, wl.chunk, wl.loss, wl.order,
+                                                      torch.bfloat16, rule["rule"])
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        mom = [torch.zeros_like(s[n]) for n in ("w1", "w2", "w3")]
+
     def call(_):
-        cla.lact_swiglu_fwd(s["q"], s["k"], s["v"], s["eta"], s["w1"], s["w2"], s["w3"],
-                            chunk=wl.chunk, loss=wl.loss, order=wl.order, rownorm=bool(wl.rownorm),
-                            out=outs[0], w1_final=outs[1], w2_final=outs[2], w3_final=outs[3],
-                            workspace=ws)
+        if rule is None:
+            cla.lact_swiglu_fwd(s["q"], s["k"], s["v"], s["eta"], s["w1"], s["w2"], s["w3"],
+                                chunk=wl.chunk, loss=wl.loss, order=wl.order,
+                                rownorm=bool(wl.rownorm), out=outs[0], w1_final=outs[1],
+                                w2_final=outs[2], w3_final=outs[3], workspace=ws)
+        else:
+            cla.lact_swiglu_fwd_rule(s["q"], s["k"], s["v"], s["eta"], s["w1"], s["w2"], s["w3"],
+                                     chunk=wl.chunk, loss=wl.loss, order=wl.order,
+                                     rownorm=bool(wl.rownorm), out=outs[0], w1_final=outs[1],
+                                     w2_final=outs[2], w3_final=outs[3], workspace=ws,
+                                     momentum=mom, **rule)
     class _One:
         def __getitem__(self, i):
             return None
@@ -196,8 +213,14 @@ def bench_lact(wl, steps, warmup):
     NH = wl.B * wl.H
     Tq = s["q"].shape[2]
     flops, byts = lact_alg(NH, Tq, wl.Tkv, wl.d, wl.hid, wl.order)
+    name = wl.name
+    if rule is not None:
+        nchunks = -(-wl.Tkv // wl.chunk)
+        if rule["rule"] == "muon":
+            flops += NH * nchunks * 3 * rule["ns_steps"] * 4 * wl.hid * wl.d * wl.d
+        name += "_" + "_".join(f"{k}{v}" for k, v in rule.items() if k != "rule") + "_" + rule["rule"]
     tok = wl.B * (wl.Tkv if wl.order == 0 else wl.Tkv + Tq)
-    return {"workload": wl.name, "ms": ms, "tokens_per_s": tok / (ms * 1e-3),
+    return {"workload": name, "ms": ms, "tokens_per_s": tok / (ms * 1e-3),
             "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "alg_flops": flops, "alg_bytes": byts}
 
@@ -292,6 +315,19 @@ def bench_decode(steps, warmup):
     return res
 
 
+LACT_RULES = ({"rule": "momentum", "beta": 0.9},
+              {"rule": "muon", "beta": 0.9, "ns_steps": 5, "muon_lr": 0.02})
+
+
+def bench_lact_rules(steps, warmup):
+    """The causal LaCT workload under the momentum and Muon update rules."""
+    out = []
+    for r in LACT_RULES:
+        log(f"[bench] timing LaCT causal, rule {r}")
+        out.append(bench_lact(__import__("ttt_inputs").LACT_CAUSAL, steps, warmup, rule=r))
+    return out
+
+
 def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0):
     """The oracle as it stands, on the host cores, over whole heads of the workload
     until about `budget_s` of CPU time has been spent (at least one head)."""
@@ -357,7 +393,8 @@ def main():
     torch.cuda.set_device(0)
     if args.lact_only:
         print(json.dumps({"lact": [bench_lact(lw, args.steps, args.warmup)
-                                   for lw in (ti.LACT_CAUSAL, ti.LACT_NONCAUSAL)]}), flush=True)
+                                   for lw in (ti.LACT_CAUSAL, ti.LACT_NONCAUSAL)],
+                          "lact_rules": bench_lact_rules(args.steps, args.warmup)}), flush=True)
         return
 
     if args.decode_only:
@@ -419,6 +456,10 @@ def main():
             except Exception as e:  # reported, never hidden
                 lact.append({"workload": lw.name, "error": str(e)})
         line["lact"] = lact
+        try:
+            line["lact_rules"] = bench_lact_rules(max(5, args.steps // 10), 2)
+        except Exception as e:  # reported, never hidden
+            line["lact_rules"] = [{"error": str(e)}]
         line["decode"] = bench_decode(max(50, args.steps), args.warmup)
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
