@@ -315,6 +315,35 @@ def bench_decode(steps, warmup):
     return res
 
 
+def window_attn_flops(NH, T, d, W):
+    """2 d flops for each score and 2 d for each value accumulation, per (query,
+    key in its window): sum_t min(t + 1, W) keys."""
+    pairs = W * (W + 1) // 2 + (T - W) * W if T >= W else T * (T + 1) // 2
+    return NH * pairs * 4 * d
+
+
+def bench_window_attention(B, H, T, d, W, steps, warmup, seed=95):
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_lact(B, H, T, T, d, 128, seed=seed)
+    up = lambda n: torch.from_numpy(inp[n + "16"].view(np.int16).copy()).view(torch.bfloat16).cuda()
+    q, k, v = up("q"), up("k"), up("v")
+    out = torch.empty_like(q)
+
+    class _One:
+        def __getitem__(self, i):
+            return None
+
+    ms, _ = time_calls(lambda _: cla.window_attention_fwd(q, k, v, window=W, out=out), _One(),
+                       steps, warmup)
+    fl = window_attn_flops(B * H, T, d, W)
+    return {"workload": f"window_attention_B{B}_H{H}_T{T}_d{d}_W{W}_bf16", "ms": ms,
+            "tokens_per_s": B * T / (ms * 1e-3), "alg_flops": fl,
+            "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 LACT_RULES = ({"rule": "momentum", "beta": 0.9},
               {"rule": "muon", "beta": 0.9, "ns_steps": 5, "muon_lr": 0.02})
 
@@ -365,6 +394,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--lact-only", action="store_true",
                     help="only time the two LaCT workloads (for profiling them alone)")
+    ap.add_argument("--window-only", action="store_true",
+                    help="only time the sliding-window attention workload")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode-step workloads (for profiling them alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -397,6 +428,11 @@ def main():
                           "lact_rules": bench_lact_rules(args.steps, args.warmup)}), flush=True)
         return
 
+    if args.window_only:
+        print(json.dumps({"window_attention": [bench_window_attention(1, 4, 32768, 256, 2048,
+                                                                      args.steps, args.warmup)]}),
+              flush=True)
+        return
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(args.steps, args.warmup)}), flush=True)
         return
@@ -461,6 +497,9 @@ def main():
         except Exception as e:  # reported, never hidden
             line["lact_rules"] = [{"error": str(e)}]
         line["decode"] = bench_decode(max(50, args.steps), args.warmup)
+        log("[bench] timing the sliding-window attention (LaCT LM shape)")
+        line["window_attention"] = [bench_window_attention(1, 4, 32768, 256, 2048,
+                                                           max(10, args.steps // 5), 3)]
     if not args.no_cpu:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline_linear(inp, wl.chunk, wl.loss, args.cpu_budget)

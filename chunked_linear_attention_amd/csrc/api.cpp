@@ -221,4 +221,26 @@ ttt_status lact_swiglu_decode(const void *q, int dtype, const float *w1, const f
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 
+ttt_status window_attention_fwd(const void *q, const void *k, const void *v, int dtype, void *out,
+                                int B, int H, int T, int d, int window, float scale,
+                                int accumulate, void *stream)
+{
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_EINVAL;
+    if (B < 1 || H < 1 || T < 0 || d < 1 || window < 1) return TTT_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return TTT_EINVAL;
+    if (!(scale > 0.f) || scale > 3.0e38f) return TTT_EINVAL;
+    if (T > 0) {
+        const void *req[4] = {q, k, v, out};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return TTT_EINVAL;
+    }
+    if ((long long)B * H > (1LL << 24) || (long long)T > (1LL << 30)) return TTT_EUNSUPPORTED;
+    if (dtype != TTT_BF16 || (d != 64 && d != 128 && d != 256)) return TTT_EUNSUPPORTED;
+    if (T == 0) return TTT_OK;
+    if ((long long)B * H * ((T + 127) / 128) > 0x7fffffffLL) return TTT_EUNSUPPORTED;
+    hipError_t e = tttk::window_attn_launch(B * H, T, d, window, scale, accumulate, q, k, v, out,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
 }  // extern "C"

@@ -62,4 +62,9 @@ hipError_t lact_decode_launch(int NH, int d, int hid, int bf16, const void *q, c
                               const float *w2, const float *w3, void *out, void *ws,
                               hipStream_t stream);
 
+// ---- sliding-window attention beside LaCT ------------------------------------------
+hipError_t window_attn_launch(int NH, int T, int d, int window, float scale, int accumulate,
+                              const void *q, const void *k, const void *v, void *out,
+                              hipStream_t stream);
+
 }  // namespace tttk

@@ -214,3 +214,28 @@ def lact_swiglu_decode(q, w1, w2, w3, *, out=None, workspace=None, stream=None):
     if rc != TTT_OK:
         raise TTTError(rc, "lact_swiglu_decode")
     return out
+
+
+def window_attention_fwd(q, k, v, *, window: int, scale=None, out=None, accumulate=False,
+                         stream=None):
+    """Causal sliding-window softmax attention over q, k, v [B,H,T,d] (bf16): query t
+    attends to keys t - window < s <= t with scores scale * q.k (scale 1/sqrt(d) by
+    default).  With accumulate, adds into ``out`` (e.g. the LaCT output).  Returns out."""
+    lib = load()
+    B, H, T, d = q.shape
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dt)
+        if tuple(t.shape) != (B, H, T, d):
+            raise ValueError(f"{n} must be shaped like q")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out")
+        out = torch.empty_like(q)
+    _check(out, "out", dt)
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    rc = lib.window_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(out), B, H, T, d,
+                                  int(window), sc, int(bool(accumulate)), _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "window_attention_fwd")
+    return out

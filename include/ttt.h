@@ -237,6 +237,24 @@ ttt_status lact_swiglu_decode(const void *q, int dtype, const float *w1, const f
                               const float *w3, void *out, int B, int H, int d, int hidden,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Sliding-window attention beside LaCT ([LaCT] section 3.1: a window attention
+ * reads the relations of nearby tokens; section 4: it shares Q, K, V with the
+ * fast weight, the two outputs are combined, and its causal sliding window
+ * supplies causality inside a chunk).  Per (batch, head) and query t:
+ *   out_t (+)= sum_{t - window < s <= t} softmax_s(scale * q_t . k_s) v_s
+ * q, k, v, out [B][H][T][d] in `dtype` (the same tensors the fast weight
+ * reads).  accumulate = 1 adds the attention to what out holds (out may then
+ * be the output of lact_swiglu_fwd), in fp32 with one rounding; 0 overwrites.
+ * out must not overlap q, k or v.  scale: a finite value > 0 (1/sqrt(d) is
+ * the usual choice).  Scores, the softmax and the output accumulate in fp32;
+ * Q K^T and P V run on bf16 matrix cores.  No workspace.
+ * Supported: dtype TTT_BF16; d in {64, 128, 256}; any T >= 0 and window >= 1.
+ * ------------------------------------------------------------------------ */
+ttt_status window_attention_fwd(const void *q, const void *k, const void *v, int dtype, void *out,
+                                int B, int H, int T, int d, int window, float scale,
+                                int accumulate, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -186,3 +186,25 @@ def test_lact_rule_workspace_query():
     extra = 2 * 4 * 3 * 512 * 256 * 2 + 4 * 3 * 256 * 256 * 2 + 4 * 3 * 256 * 4
     assert extra <= lib.lact_swiglu_rule_workspace_bytes(*args, 2) - gd <= extra + 3 * 256
     assert lib.lact_swiglu_rule_workspace_bytes(*args, 3) == 0
+
+
+def win(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, out=FAKE, B=1, H=1, T=100, d=128, window=16,
+             scale=0.1, acc=0, stream=None)
+    a.update(kw)
+    return lib.window_attention_fwd(a["q"], a["k"], a["v"], a["dtype"], a["out"], a["B"], a["H"],
+                                    a["T"], a["d"], a["window"], a["scale"], a["acc"], a["stream"])
+
+
+# every case fails validation before a launch (T = 0 returns before any launch)
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.TTT_EINVAL), (dict(out=FAKE + 2), _lib.TTT_EINVAL),
+    (dict(dtype=4), _lib.TTT_EINVAL), (dict(B=0), _lib.TTT_EINVAL), (dict(T=-1), _lib.TTT_EINVAL),
+    (dict(window=0), _lib.TTT_EINVAL), (dict(scale=0.0), _lib.TTT_EINVAL),
+    (dict(scale=float("nan")), _lib.TTT_EINVAL), (dict(scale=float("inf")), _lib.TTT_EINVAL),
+    (dict(acc=2), _lib.TTT_EINVAL), (dict(dtype=0), _lib.TTT_EUNSUPPORTED),
+    (dict(d=96), _lib.TTT_EUNSUPPORTED), (dict(d=512), _lib.TTT_EUNSUPPORTED),
+    (dict(T=0, q=None, k=None, v=None, out=None), _lib.TTT_OK),
+])
+def test_window_attention_validation(kw, code):
+    assert win(_lib.load(), **kw) == code
