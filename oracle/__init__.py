@@ -12,7 +12,8 @@ sizes where the token loop is too slow; it is pinned against the token loop.
 ``decode.py`` is the single-token decode step of TTT-Linear (one gradient step
 per token on a carried state, optionally anchored at the chunk-start state).
 ``window_attention.py`` is the causal sliding-window softmax attention that
-sits beside LaCT's fast weight on the same Q, K, V.
+sits beside LaCT's fast weight on the same Q, K, V.  ``backward.py`` is the
+reverse-mode differentiation of the causal TTT-Linear token loop.
 """
 from __future__ import annotations
 
