@@ -344,6 +344,43 @@ def bench_window_attention(B, H, T, d, W, steps, warmup, seed=95):
             "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+def linear_bwd_flops(NH, T, d, b, loss):
+    """Per chunk of n tokens: the chunk-start states' forward pass 2nd^2 (MSE:
+    +2nd^2) and the adjoints 2nd^2 x (5 inner product | 8 MSE) + 2dn^2 x 4."""
+    full, rem = divmod(T, b)
+    f = 0
+    for n, cnt in ((b, full), (rem, 1 if rem else 0)):
+        f += cnt * (2 * n * d * d * ((2 if loss == 1 else 1) + (8 if loss == 1 else 5))
+                    + 8 * d * n * n)
+    return NH * f
+
+
+def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_linear(B, H, T, T, d, seed=seed, dtype="bf16", w0="identity")
+    up = lambda a: torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    q, k, v = (up(inp[n + "16"]) for n in ("q", "k", "v"))
+    eta, w0 = torch.from_numpy(inp["eta"]).cuda(), torch.from_numpy(inp["w0"]).cuda()
+    dy = up(ti.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32)))
+    import chunked_linear_attention_amd._lib as L
+    nb = L.load().ttt_linear_bwd_workspace_bytes(B, H, T, d, chunk, loss, 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    class _One:
+        def __getitem__(self, i):
+            return None
+
+    ms, _ = time_calls(lambda _: cla.ttt_linear_bwd(q, k, v, eta, w0, dy, chunk=chunk, loss=loss,
+                                                     workspace=ws), _One(), steps, warmup)
+    fl = linear_bwd_flops(B * H, T, d, chunk, loss)
+    return {"workload": f"ttt_linear_bwd_{'mse' if loss else 'dot'}_B{B}_H{H}_T{T}_d{d}_b{chunk}_bf16",
+            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "alg_flops": fl,
+            "tflops": fl / (ms * 1e-3) / 1e12, "fp32_frac": fl / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
+
+
 LACT_RULES = ({"rule": "momentum", "beta": 0.9},
               {"rule": "muon", "beta": 0.9, "ns_steps": 5, "muon_lr": 0.02})
 
@@ -394,6 +431,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--lact-only", action="store_true",
                     help="only time the two LaCT workloads (for profiling them alone)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="only time the TTT-Linear backward on the headline shape")
     ap.add_argument("--window-only", action="store_true",
                     help="only time the sliding-window attention workload")
     ap.add_argument("--decode-only", action="store_true",
@@ -428,6 +467,10 @@ def main():
                           "lact_rules": bench_lact_rules(args.steps, args.warmup)}), flush=True)
         return
 
+    if args.bwd_only:
+        print(json.dumps({"backward": [bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps,
+                                                        args.warmup)]}), flush=True)
+        return
     if args.window_only:
         print(json.dumps({"window_attention": [bench_window_attention(1, 4, 32768, 256, 2048,
                                                                       args.steps, args.warmup)]}),
@@ -497,6 +540,8 @@ def main():
         except Exception as e:  # reported, never hidden
             line["lact_rules"] = [{"error": str(e)}]
         line["decode"] = bench_decode(max(50, args.steps), args.warmup)
+        log("[bench] timing the TTT-Linear backward (headline shape)")
+        line["backward"] = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, max(5, args.steps // 10), 2)]
         log("[bench] timing the sliding-window attention (LaCT LM shape)")
         line["window_attention"] = [bench_window_attention(1, 4, 32768, 256, 2048,
                                                            max(10, args.steps // 5), 3)]

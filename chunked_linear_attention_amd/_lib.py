@@ -17,7 +17,8 @@ TTT_EHIP = -4
 EXPORTS = ("ttt_status_string", "ttt_abi_version", "ttt_linear_workspace_bytes", "ttt_linear_fwd",
            "lact_swiglu_workspace_bytes", "lact_swiglu_fwd", "ttt_linear_decode",
            "lact_swiglu_decode_workspace_bytes", "lact_swiglu_decode",
-           "lact_swiglu_rule_workspace_bytes", "lact_swiglu_fwd_rule", "window_attention_fwd")
+           "lact_swiglu_rule_workspace_bytes", "lact_swiglu_fwd_rule", "window_attention_fwd",
+           "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +60,11 @@ def load() -> ctypes.CDLL:
         lib.lact_swiglu_fwd_rule.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp] + \
             [i] * 11 + [f, i, f, vp, vp, vp, vp, sz, vp]
         lib.lact_swiglu_fwd_rule.restype = i
+        lib.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 7
+        lib.ttt_linear_bwd_workspace_bytes.restype = sz
+        lib.ttt_linear_bwd.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp] + \
+            [i] * 6 + [vp, sz, vp]
+        lib.ttt_linear_bwd.restype = i
         lib.window_attention_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, f, i, vp]
         lib.window_attention_fwd.restype = i
         lib.ttt_linear_decode.argtypes = [vp, vp, vp, i, vp, vp, vp, i, vp, i, i, i, i, vp]

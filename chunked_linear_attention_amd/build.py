@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libttt_mi355x.so")
-SOURCES = ["api.cpp", "ttt_linear.hip", "lact_swiglu.hip", "decode.hip", "window_attn.hip"]
+SOURCES = ["api.cpp", "ttt_linear.hip", "lact_swiglu.hip", "decode.hip", "window_attn.hip",
+           "ttt_linear_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

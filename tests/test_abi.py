@@ -208,3 +208,34 @@ def win(lib, **kw):
 ])
 def test_window_attention_validation(kw, code):
     assert win(_lib.load(), **kw) == code
+
+
+def lin_bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w0=FAKE, do=FAKE, dwf=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, de=FAKE, dw0=FAKE, B=1, H=1, T=100, d=64, chunk=16, loss=1, ws=FAKE, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.ttt_linear_bwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w0"], a["do"],
+                              a["dwf"], a["dq"], a["dk"], a["dv"], a["de"], a["dw0"], a["B"], a["H"],
+                              a["T"], a["d"], a["chunk"], a["loss"], a["ws"], a["wsb"], a["stream"])
+
+
+# every case fails validation before a launch (wsb = 0 ends the valid ones with EWORKSPACE)
+@pytest.mark.parametrize("kw,code", [
+    (dict(), _lib.TTT_EWORKSPACE), (dict(dwf=FAKE), _lib.TTT_EWORKSPACE),
+    (dict(dwf=FAKE + 4), _lib.TTT_EINVAL), (dict(do=None), _lib.TTT_EINVAL),
+    (dict(de=None), _lib.TTT_EINVAL), (dict(dw0=FAKE + 8), _lib.TTT_EINVAL),
+    (dict(ws=None), _lib.TTT_EINVAL), (dict(T=0), _lib.TTT_EINVAL), (dict(loss=3), _lib.TTT_EINVAL),
+    (dict(dtype=5), _lib.TTT_EINVAL), (dict(d=128), _lib.TTT_EUNSUPPORTED),
+    (dict(chunk=64), _lib.TTT_EUNSUPPORTED), (dict(chunk=8), _lib.TTT_EUNSUPPORTED),
+])
+def test_linear_bwd_validation(kw, code):
+    assert lin_bwd(_lib.load(), **kw) == code
+
+
+def test_linear_bwd_workspace_query():
+    lib = _lib.load()
+    # one fp32 d x d chunk-start state per chunk and head
+    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 64, 16, 1, 1) == 32 * 256 * 64 * 64 * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 64, 32, 0, 0) == 2 * 64 * 64 * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 128, 16, 0, 0) == 0
