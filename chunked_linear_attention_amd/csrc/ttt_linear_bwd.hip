@@ -13,10 +13,16 @@
 //     dK   = dA^T Q + H U G^T  [- dU W_c^T  (MSE)]
 //     dV   = dU
 //     dL/dW_c = G + Q^T dO  [- K^T dU  (MSE)]
-// and the sweep runs over the chunks in reverse, one workgroup per (batch,
-// head), with the chunk-start states written by a forward pass of the same
-// recursion.  Everything is fp32 FMA in LDS: the chain over chunks is serial
-// per head, so this version parallelises over heads only.
+// Only two recursions are serial over the chunks, and neither mixes the
+// columns of its d x d matrix: the forward one for the chunk-start states,
+//     W_{c+1} = W_c + K^T H (V - K W_c),
+// and the backward one for G,
+//     G_c = G_{c+1} + R_c [- K^T H K G_{c+1}],   R_c = Q^T dO [- K^T S~],  S~ = S^T dO.
+// So the work runs in four launches: the state recursion and the G recursion
+// with one workgroup per (head, 16 columns), and between and after them two
+// launches with one workgroup per (head, chunk) for everything else (the
+// G-free terms and R_c first, then the terms that need G_{c+1}), exchanging
+// per-chunk matrices through the workspace.  Everything is fp32 FMA in LDS.
 #include "ttt_device.h"
 #include "ttt_internal.h"
 
@@ -30,7 +36,12 @@ struct LinBwdParams {
     const float *eta, *w0, *dwf;
     void *dq, *dk, *dv;
     float *deta, *dw0;
-    float *states;  // [NH][nchunks][D][D]
+    float *states;  // [NH][nchunks][D][D]  chunk-start states W_c
+    float *gnext;   // [NH][nchunks][D][D]  G_{c+1} = dL/dW_{c+1}
+    float *rc;      // [NH][nchunks][D][D]  R_c = Q^T dO [- K^T S~]
+    float *ub;      // [NH][nchunks * B][D] U (MSE residuals)
+    float *st;      // [NH][nchunks * B][D] S~ = S^T dO
+    float *dkl;     // [NH][nchunks * B][D] dA^T Q [- S~ W_c^T]
     int T, nchunks, loss;
 };
 
@@ -43,200 +54,373 @@ template <typename E> __device__ __forceinline__ void stf(void *p, long i, float
     static_cast<E *>(p)[i] = (E)x;
 }
 
-// forward recursion over the chunks, writing each chunk-start state
+constexpr int CB = 16;  // state columns per workgroup in the serial passes
+
+// Serial pass 1 (one workgroup per (head, 16 state columns); columns of the
+// state never mix in the recursion W_{c+1} = W_c + K^T H (V - K W_c)):
+// writes every chunk-start state.  The next chunk's K, V columns and eta are
+// loaded into registers while the current chunk computes.
 template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lin_bwd_states(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 {
-    __shared__ float W[D][D + 1];
-    __shared__ float Ks[B][D + 1], Us[B][D + 1];
+    __shared__ float W[D][CB + 1];
+    __shared__ float Ks[B][D + 1], Us[B][CB + 1];
     __shared__ float et[B];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    constexpr int NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
+    const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
-    for (int e = tid; e < D * D; e += 256) W[e / D][e % D] = p.w0[(long)h * D * D + e];
+    float pk[NK], pv[NV], pe = 0.f;
+    auto fetch = [&](int c) {
+        const int c0 = c * B, n = min(B, p.T - c0);
+#pragma unroll
+        for (int r = 0; r < NK; ++r) {
+            const int e = tid + 256 * r, i = e / D, a = e % D;
+            pk[r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < NV; ++r) {
+            const int e = tid + 256 * r, i = e / CB, j = e % CB;
+            pv[r] = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j0 + j) : 0.f;
+        }
+        pe = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int r = 0; r < NK; ++r) Ks[(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[r];
+#pragma unroll
+        for (int r = 0; r < NV; ++r) Us[(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pv[r];
+        if (tid < B) et[tid] = pe;
+    };
+    for (int e = tid; e < D * CB; e += 256) W[e / CB][e % CB] = p.w0[(long)h * D * D + (e / CB) * D + j0 + e % CB];
+    fetch(0);
+    commit();
     __syncthreads();
     for (int c = 0; c < p.nchunks; ++c) {
-        const int c0 = c * B, n = min(B, p.T - c0);
+        // loads first: a later wait for them then does not also wait for the stores
+        if (c + 1 < p.nchunks) fetch(c + 1);
         float *dst = p.states + ((long)h * p.nchunks + c) * D * D;
-        for (int e = tid; e < D * D; e += 256) dst[e] = W[e / D][e % D];
-        for (int e = tid; e < B * D; e += 256) {
-            const int i = e / D, j = e % D;
-            Ks[i][j] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + j) : 0.f;
-            Us[i][j] = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f;
-        }
-        if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
-        __syncthreads();
+        for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
         if (p.loss == 1) {
-            float u[(B * D + 255) / 256];
+            float u[NV];
 #pragma unroll
-            for (int r = 0; r < (B * D + 255) / 256; ++r) {
-                const int e = tid + 256 * r;
-                u[r] = 0.f;
-                if (e < B * D) {
-                    const int i = e / D, j = e % D;
-                    float s = 0.f;
-                    for (int a = 0; a < D; ++a) s += Ks[i][a] * W[a][j];
-                    u[r] = Us[i][j] - s;
-                }
+            for (int r = 0; r < NV; ++r) {
+                const int e = tid + 256 * r, i = e / CB, j = e % CB;
+                float s = 0.f;
+                for (int a = 0; a < D; ++a) s += Ks[i][a] * W[a][j];
+                u[r] = Us[i][j] - s;
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
-            for (int r = 0; r < (B * D + 255) / 256; ++r) {
-                const int e = tid + 256 * r;
-                if (e < B * D) Us[e / D][e % D] = u[r];
-            }
-            __syncthreads();
+            for (int r = 0; r < NV; ++r) Us[(tid + 256 * r) / CB][(tid + 256 * r) % CB] = u[r];
+            lds_barrier();
         }
-        for (int e = tid; e < D * D; e += 256) {
-            const int a = e / D, j = e % D;
+        for (int e = tid; e < D * CB; e += 256) {
+            const int a = e / CB, j = e % CB;
             float s = 0.f;
             for (int i = 0; i < B; ++i) s += Ks[i][a] * et[i] * Us[i][j];
             W[a][j] += s;
         }
-        __syncthreads();
+        lds_barrier();
+        if (c + 1 < p.nchunks) {
+            commit();
+            lds_barrier();
+        }
     }
 }
 
+// Parallel pass 2, one workgroup per (head, chunk): every term that does not
+// need G.  Writes dQ, d_eta's first part and the chunk's U, S~, dK part, R_c.
 template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lin_bwd_sweep(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
 {
-    __shared__ float Wc[D][D + 1], G[D][D + 1];
-    __shared__ float Qs[B][D + 1], Ks[B][D + 1], dOs[B][D + 1], Us[B][D + 1], dUs[B][D + 1],
-        KGs[B][D + 1];
+    __shared__ float Wc[D][D + 1];
+    __shared__ float Qs[B][D + 1], Ks[B][D + 1], dOs[B][D + 1], Us[B][D + 1], Ss[B][D + 1];
     __shared__ float As[B][B + 1], dAs[B][B + 1];
     __shared__ float et[B];
-    constexpr int NBD = (B * D + 255) / 256;
-    const int h = blockIdx.x, tid = threadIdx.x;
+    constexpr int NBD = B * D / 256;
+    const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
-    for (int e = tid; e < D * D; e += 256)
-        G[e / D][e % D] = p.dwf ? p.dwf[(long)h * D * D + e] : 0.f;
-    for (int c = p.nchunks - 1; c >= 0; --c) {
+    const int c0 = c * B, n = min(B, p.T - c0);
+    const long cb = ((long)h * p.nchunks + c);
+    const float *src = p.states + cb * D * D;
+    for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
+    for (int e = tid; e < B * D; e += 256) {
+        const int i = e / D, j = e % D;
+        const bool ok = i < n;
+        const long g = (tok0 + c0 + i) * D + j;
+        Qs[i][j] = ok ? ldf<E>(p.q, g) : 0.f;
+        Ks[i][j] = ok ? ldf<E>(p.k, g) : 0.f;
+        Us[i][j] = ok ? ldf<E>(p.v, g) : 0.f;
+        dOs[i][j] = ok ? ldf<E>(p.dout, g) : 0.f;
+    }
+    if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
+    __syncthreads();
+    const long row0 = (long)h * p.nchunks * B + (long)c * B;  // this chunk's rows in the per-token buffers
+    if (p.loss == 1) {
+        float u[NBD];
+        {
+            const int i0 = tid / D, j = tid % D;  // outputs (i0 + 4 r, j)
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) u[r] = 0.f;
+            for (int a = 0; a < D; ++a) {
+                const float w = Wc[a][j];
+#pragma unroll
+                for (int r = 0; r < NBD; ++r) u[r] += Ks[i0 + 4 * r][a] * w;
+            }
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) u[r] = Us[i0 + 4 * r][j] - u[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) {
+            const int e = tid + 256 * r;
+            Us[e / D][e % D] = u[r];
+            p.ub[(row0 + e / D) * D + e % D] = u[r];
+        }
+    }
+    for (int e = tid; e < B * B; e += 256) {
+        const int t = e / B, i = e % B;
+        float s = 0.f;
+        if (i <= t)
+            for (int a = 0; a < D; ++a) s += Qs[t][a] * Ks[i][a];
+        As[t][i] = s;
+    }
+    __syncthreads();
+    // S~ = S^T dO (S = A H);  dS = (dO U^T) * M
+    {
+        const int i0 = tid / D, j = tid % D;
+        float sv[NBD];
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) sv[r] = 0.f;
+        for (int t = 0; t < B; ++t) {
+            const float x = dOs[t][j];
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) sv[r] += As[t][i0 + 4 * r] * x;  // A is zero for t < i
+        }
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) {
+            const int i = i0 + 4 * r;
+            Ss[i][j] = et[i] * sv[r];
+            p.st[(row0 + i) * D + j] = et[i] * sv[r];
+        }
+    }
+    for (int e = tid; e < B * B; e += 256) {
+        const int t = e / B, i = e % B;
+        float s = 0.f;
+        if (i <= t)
+            for (int a = 0; a < D; ++a) s += dOs[t][a] * Us[i][a];
+        dAs[t][i] = s;
+    }
+    __syncthreads();
+    if (tid < 64) {  // d_eta, the G-free part: sum_t dS[t][i] A[t][i]
+        for (int i = 0; i < B; ++i) {
+            float s = 0.f;
+            for (int t = tid; t < B; t += 64) s += dAs[t][i] * As[t][i];
+            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+            if (tid == 0 && i < n) p.deta[tok0 + c0 + i] = s;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < B * B; e += 256) dAs[e / B][e % B] *= et[e % B];
+    __syncthreads();
+    // dQ = dO Wc^T + dA K;  dK part = dA^T Q [- S~ Wc^T]
+    {
+        const int i0 = tid / D, a = tid % D;  // outputs (i0 + 4 r, a)
+        float sq[NBD], sk[NBD];
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) sq[r] = sk[r] = 0.f;
+        for (int j = 0; j < D; ++j) {
+            const float w = Wc[a][j];
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) {
+                sq[r] += dOs[i0 + 4 * r][j] * w;
+                if (p.loss == 1) sk[r] -= Ss[i0 + 4 * r][j] * w;
+            }
+        }
+        for (int t = 0; t < B; ++t) {
+            const float kk = Ks[t][a], qq = Qs[t][a];
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) {
+                sq[r] += dAs[i0 + 4 * r][t] * kk;
+                sk[r] += dAs[t][i0 + 4 * r] * qq;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) {
+            const int i = i0 + 4 * r;
+            if (i < n) stf<E>(p.dq, (tok0 + c0 + i) * D + a, sq[r]);
+            p.dkl[(row0 + i) * D + a] = sk[r];
+        }
+    }
+    // R_c = Q^T dO [- K^T S~]
+    float *R = p.rc + cb * D * D;
+    {
+        constexpr int NR = D * D / 256;
+        const int a0 = tid / D, j = tid % D;  // outputs (a0 + 4 r, j)
+        float sr[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) sr[r] = 0.f;
+        for (int i = 0; i < B; ++i) {
+            const float x = dOs[i][j], y = Ss[i][j];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                sr[r] += Qs[i][a0 + 4 * r] * x;
+                if (p.loss == 1) sr[r] -= Ks[i][a0 + 4 * r] * y;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) R[(long)(a0 + 4 * r) * D + j] = sr[r];
+    }
+}
+
+// Serial pass 3 (one workgroup per (head, 16 columns of G); G's columns never
+// mix either): G_c = G_{c+1} + R_c [- K^T H K G_{c+1}], storing every G_{c+1};
+// the last G is d_w_init.  The next chunk's K, eta and R_c columns are loaded
+// into registers while the current chunk computes.
+template <int D, int B, typename E>
+__global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
+{
+    __shared__ float G[D][CB + 1], Rs[D][CB + 1];
+    __shared__ float Ks[B][D + 1], KG[B][CB + 1];
+    __shared__ float et[B];
+    constexpr int NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
+    const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
+    const long tok0 = (long)h * p.T;
+    float pk[NK], pr[NR], pe = 0.f;
+    auto fetch = [&](int c) {
         const int c0 = c * B, n = min(B, p.T - c0);
-        const float *src = p.states + ((long)h * p.nchunks + c) * D * D;
-        for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
-        for (int e = tid; e < B * D; e += 256) {
-            const int i = e / D, j = e % D;
-            const bool ok = i < n;
-            const long g = (tok0 + c0 + i) * D + j;
-            Qs[i][j] = ok ? ldf<E>(p.q, g) : 0.f;
-            Ks[i][j] = ok ? ldf<E>(p.k, g) : 0.f;
-            Us[i][j] = ok ? ldf<E>(p.v, g) : 0.f;
-            dOs[i][j] = ok ? ldf<E>(p.dout, g) : 0.f;
-        }
-        if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
-        __syncthreads();
-        // U (MSE), K G, A
-        float u[NBD], kg[NBD];
+        const float *R = p.rc + ((long)h * p.nchunks + c) * D * D;
 #pragma unroll
-        for (int r = 0; r < NBD; ++r) {
+        for (int r = 0; r < NR; ++r) {
             const int e = tid + 256 * r;
-            u[r] = kg[r] = 0.f;
-            if (e < B * D) {
-                const int i = e / D, j = e % D;
-                float s = 0.f, t = 0.f;
-                for (int a = 0; a < D; ++a) {
-                    s += Ks[i][a] * Wc[a][j];
-                    t += Ks[i][a] * G[a][j];
-                }
-                u[r] = Us[i][j] - s;
-                kg[r] = t;
+            pr[r] = R[(long)(e / CB) * D + j0 + e % CB];
+        }
+        if (p.loss == 1) {
+#pragma unroll
+            for (int r = 0; r < NK; ++r) {
+                const int e = tid + 256 * r, i = e / D, a = e % D;
+                pk[r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
             }
+            pe = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
         }
-        for (int e = tid; e < B * B; e += 256) {
-            const int t = e / B, i = e % B;
-            float s = 0.f;
-            if (i <= t)
-                for (int a = 0; a < D; ++a) s += Qs[t][a] * Ks[i][a];
-            As[t][i] = s;
-        }
-        __syncthreads();
+    };
+    auto commit = [&]() {
 #pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int e = tid + 256 * r;
-            if (e < B * D) {
-                if (p.loss == 1) Us[e / D][e % D] = u[r];
-                KGs[e / D][e % D] = kg[r];
-            }
-        }
-        __syncthreads();
-        // dU = S^T dO + H (K G);  dS = (dO U^T) * M,  dA = dS H
+        for (int r = 0; r < NR; ++r) Rs[(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pr[r];
+        if (p.loss == 1) {
 #pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int e = tid + 256 * r;
-            if (e < B * D) {
-                const int i = e / D, j = e % D;
+            for (int r = 0; r < NK; ++r) Ks[(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[r];
+            if (tid < B) et[tid] = pe;
+        }
+    };
+    for (int e = tid; e < D * CB; e += 256)
+        G[e / CB][e % CB] = p.dwf ? p.dwf[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
+    fetch(p.nchunks - 1);
+    commit();
+    __syncthreads();
+    for (int c = p.nchunks - 1; c >= 0; --c) {
+        // loads first: a later wait for them then does not also wait for the stores
+        if (c > 0) fetch(c - 1);
+        float *gdst = p.gnext + ((long)h * p.nchunks + c) * D * D;
+        for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+        if (p.loss == 1) {
+            for (int e = tid; e < B * CB; e += 256) {
+                const int i = e / CB, j = e % CB;
                 float s = 0.f;
-                for (int t = i; t < B; ++t) s += As[t][i] * dOs[t][j];
-                dUs[i][j] = et[i] * (s + KGs[i][j]);
+                for (int a = 0; a < D; ++a) s += Ks[i][a] * G[a][j];
+                KG[i][j] = et[i] * s;
             }
+            lds_barrier();
         }
-        for (int e = tid; e < B * B; e += 256) {
-            const int t = e / B, i = e % B;
-            float s = 0.f;
-            if (i <= t)
-                for (int a = 0; a < D; ++a) s += dOs[t][a] * Us[i][a];
-            dAs[t][i] = s;  // dS for now
-        }
-        __syncthreads();
-        // deta (one wave): sum_t dS[t][i] A[t][i] + (K G)_i . U_i
-        if (tid < 64) {
-            for (int i = 0; i < B; ++i) {
-                float s = 0.f;
-                for (int t = tid; t < B; t += 64) s += dAs[t][i] * As[t][i];
-                for (int a = tid; a < D; a += 64) s += KGs[i][a] * Us[i][a];
-                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-                if (tid == 0 && i < n) p.deta[tok0 + c0 + i] = s;
-            }
-        }
-        __syncthreads();
-        for (int e = tid; e < B * B; e += 256) dAs[e / B][e % B] *= et[e % B];
-        __syncthreads();
-        // dQ = dO Wc^T + dA K;  dK = dA^T Q + H U G^T - dU Wc^T (MSE);  dV = dU
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int e = tid + 256 * r;
-            if (e < B * D) {
-                const int i = e / D, a = e % D;
-                float sq = 0.f, sk = 0.f, ug = 0.f;
-                for (int j = 0; j < D; ++j) {
-                    sq += dOs[i][j] * Wc[a][j];
-                    ug += Us[i][j] * G[a][j];
-                    if (p.loss == 1) sk -= dUs[i][j] * Wc[a][j];
-                }
-                for (int t = 0; t < B; ++t) {
-                    sq += dAs[i][t] * Ks[t][a];
-                    sk += dAs[t][i] * Qs[t][a];
-                }
-                sk += et[i] * ug;
-                if (i < n) {
-                    const long g = (tok0 + c0 + i) * D + a;
-                    stf<E>(p.dq, g, sq);
-                    stf<E>(p.dk, g, sk);
-                    stf<E>(p.dv, g, dUs[i][a]);
-                }
-            }
-        }
-        __syncthreads();
-        // G <- G + Q^T dO - K^T dU (MSE)
-        for (int e = tid; e < D * D; e += 256) {
-            const int a = e / D, j = e % D;
-            float s = 0.f;
-            for (int i = 0; i < B; ++i) {
-                s += Qs[i][a] * dOs[i][j];
-                if (p.loss == 1) s -= Ks[i][a] * dUs[i][j];
-            }
+        for (int e = tid; e < D * CB; e += 256) {
+            const int a = e / CB, j = e % CB;
+            float s = Rs[a][j];
+            if (p.loss == 1)
+                for (int i = 0; i < B; ++i) s -= Ks[i][a] * KG[i][j];
             G[a][j] += s;
         }
-        __syncthreads();
+        lds_barrier();
+        if (c > 0) {
+            commit();
+            lds_barrier();
+        }
     }
-    for (int e = tid; e < D * D; e += 256) p.dw0[(long)h * D * D + e] = G[e / D][e % D];
+    for (int e = tid; e < D * CB; e += 256) p.dw0[(long)h * D * D + (e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+}
+
+// Parallel pass 4, one workgroup per (head, chunk): the terms that need
+// G = G_{c+1}:  KG = K G,  dV = dU = S~ + H KG,
+// dK = part + H (U G^T [- KG Wc^T]),  d_eta += rowsum(KG * U).
+template <int D, int B, typename E>
+__global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
+{
+    __shared__ float Gn[D][D + 1], Wc[D][D + 1];
+    __shared__ float Ks[B][D + 1], Us[B][D + 1], KGs[B][D + 1];
+    __shared__ float et[B];
+    constexpr int NBD = B * D / 256;
+    const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks, tid = threadIdx.x;
+    const long tok0 = (long)h * p.T;
+    const int c0 = c * B, n = min(B, p.T - c0);
+    const long cb = ((long)h * p.nchunks + c);
+    const long row0 = (long)h * p.nchunks * B + (long)c * B;
+    for (int e = tid; e < D * D; e += 256) {
+        Gn[e / D][e % D] = p.gnext[cb * D * D + e];
+        if (p.loss == 1) Wc[e / D][e % D] = p.states[cb * D * D + e];
+    }
+    for (int e = tid; e < B * D; e += 256) {
+        const int i = e / D, j = e % D;
+        const bool ok = i < n;
+        Ks[i][j] = ok ? ldf<E>(p.k, (tok0 + c0 + i) * D + j) : 0.f;
+        Us[i][j] = p.loss == 1 ? p.ub[(row0 + i) * D + j] : (ok ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f);
+    }
+    if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NBD; ++r) {
+        const int e = tid + 256 * r, i = e / D, j = e % D;
+        float s = 0.f;
+        for (int a = 0; a < D; ++a) s += Ks[i][a] * Gn[a][j];
+        KGs[i][j] = s;
+        if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + j, p.st[(row0 + i) * D + j] + et[i] * s);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        for (int i = 0; i < n; ++i) {
+            float s = 0.f;
+            for (int a = tid; a < D; a += 64) s += KGs[i][a] * Us[i][a];
+            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+            if (tid == 0) p.deta[tok0 + c0 + i] += s;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NBD; ++r) {
+        const int e = tid + 256 * r, i = e / D, a = e % D;
+        float s = 0.f;
+        for (int j = 0; j < D; ++j) {
+            s += Us[i][j] * Gn[a][j];
+            if (p.loss == 1) s -= KGs[i][j] * Wc[a][j];
+        }
+        if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, p.dkl[(row0 + i) * D + a] + et[i] * s);
+    }
 }
 
 }  // namespace
 
 size_t linear_bwd_workspace(int NH, int T, int d, int chunk)
 {
-    const long nchunks = (T + chunk - 1) / chunk;
-    return (size_t)NH * nchunks * d * d * sizeof(float);
+    const size_t nch = (T + chunk - 1) / chunk;
+    // states, G_{c+1}, R_c (d x d per chunk) and U, S~, dK part (chunk x d per chunk), fp32
+    return (size_t)NH * nch * (3 * (size_t)d * d + 3 * (size_t)chunk * d) * sizeof(float);
+}
+
+template <int B, typename E>
+static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
+{
+    const dim3 b(256);
+    lbw_states<64, B, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
+    lbw_local<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+    lbw_grad<64, B, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
+    lbw_dep<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
 }
 
 hipError_t linear_bwd_launch(int NH, int T, int d, int chunk, int loss, int bf16, const void *q,
@@ -244,25 +428,18 @@ hipError_t linear_bwd_launch(int NH, int T, int d, int chunk, int loss, int bf16
                              const void *dout, const float *dwf, void *dq, void *dk, void *dv,
                              float *deta, float *dw0, void *ws, hipStream_t st)
 {
-    LinBwdParams p{q, k, v, dout, eta, w0, dwf, dq, dk, dv, deta, dw0, static_cast<float *>(ws),
-                   T, (T + chunk - 1) / chunk, loss};
-    const dim3 g(NH), b(256);
+    const int nch = (T + chunk - 1) / chunk;
+    float *base = static_cast<float *>(ws);
+    const size_t dd = (size_t)NH * nch * d * d, bd = (size_t)NH * nch * chunk * d;
+    LinBwdParams p{q, k, v, dout, eta, w0, dwf, dq, dk, dv, deta, dw0, base, base + dd,
+                   base + 2 * dd, base + 3 * dd, base + 3 * dd + bd, base + 3 * dd + 2 * bd, T,
+                   nch, loss};
     if (chunk == 16) {
-        if (bf16) {
-            lin_bwd_states<64, 16, __bf16><<<g, b, 0, st>>>(p);
-            lin_bwd_sweep<64, 16, __bf16><<<g, b, 0, st>>>(p);
-        } else {
-            lin_bwd_states<64, 16, float><<<g, b, 0, st>>>(p);
-            lin_bwd_sweep<64, 16, float><<<g, b, 0, st>>>(p);
-        }
+        if (bf16) lbw_run<16, __bf16>(p, NH, st);
+        else lbw_run<16, float>(p, NH, st);
     } else {
-        if (bf16) {
-            lin_bwd_states<64, 32, __bf16><<<g, b, 0, st>>>(p);
-            lin_bwd_sweep<64, 32, __bf16><<<g, b, 0, st>>>(p);
-        } else {
-            lin_bwd_states<64, 32, float><<<g, b, 0, st>>>(p);
-            lin_bwd_sweep<64, 32, float><<<g, b, 0, st>>>(p);
-        }
+        if (bf16) lbw_run<32, __bf16>(p, NH, st);
+        else lbw_run<32, float>(p, NH, st);
     }
     return hipGetLastError();
 }

@@ -235,7 +235,8 @@ def test_linear_bwd_validation(kw, code):
 
 def test_linear_bwd_workspace_query():
     lib = _lib.load()
-    # one fp32 d x d chunk-start state per chunk and head
-    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 64, 16, 1, 1) == 32 * 256 * 64 * 64 * 4
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 64, 32, 0, 0) == 2 * 64 * 64 * 4
+    # per chunk and head: three fp32 d x d matrices (state, G, R) and three chunk x d ones
+    per = lambda b: (3 * 64 * 64 + 3 * b * 64) * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 64, 16, 1, 1) == 32 * 256 * per(16)
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 64, 32, 0, 0) == 2 * per(32)
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 128, 16, 0, 0) == 0
