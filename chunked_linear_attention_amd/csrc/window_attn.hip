@@ -165,7 +165,12 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
                     }
                 mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mnew = fmaxf(mrun[u], mx);
+                // The running max moves only when a score exceeds it by more
+                // than 2^8 (base 2): numerator and denominator share the stale
+                // max, so the result is unchanged, the probabilities stay below
+                // 256, and most blocks skip rescaling the output accumulators.
+                const bool grow = mx > mrun[u] + 8.f;
+                const float mnew = grow ? mx : mrun[u];
                 const float alpha = __builtin_amdgcn_exp2f(mrun[u] - mnew);
                 mrun[u] = mnew;
                 float ls = 0.f;
@@ -178,8 +183,10 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
                         ls += e;
                     }
                 lrun[u] = lrun[u] * alpha + ls;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) o[dt][u] *= alpha;
+                    for (int dt = 0; dt < NDT; ++dt) o[dt][u] *= alpha;
+                }
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp)
                     pf[pp][u] = __builtin_shufflevector(to_bf16x4(s[2 * pp][u]), to_bf16x4(s[2 * pp + 1][u]),
