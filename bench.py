@@ -277,6 +277,46 @@ def bench_linear_decode(B, H, d, loss, chunk, dtype, steps, warmup, seed=41):
             "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "state_copies": sets.n}
 
 
+def bench_linear_decode_graph(B, H, d, loss, chunk, replays, seed=41):
+    """One chunk of anchored decode steps captured into a HIP graph and replayed:
+    the per-step time without host launch overhead.  The state buffers are fixed
+    by the capture, so a small batch's state stays in the last-level cache."""
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_linear(B, H, chunk, chunk, d, seed=seed, dtype="bf16", w0="normal")
+    up = lambda n, t: torch.from_numpy(inp[n + "16"][:, :, t].copy().view(np.int16)).view(torch.bfloat16).cuda()
+    toks = [(up("q", t), up("k", t), up("v", t), torch.from_numpy(inp["eta"][:, :, t].copy()).cuda())
+            for t in range(chunk)]
+    w = torch.from_numpy(inp["w0"]).cuda()
+    a = w.clone()
+    outs = [torch.empty_like(toks[0][0]) for _ in range(chunk)]
+
+    def run():
+        for t in range(chunk):
+            cla.ttt_linear_decode(*toks[t], w, loss=loss, w_anchor=a, anchor_update=t == chunk - 1,
+                                  out=outs[t])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+
+    class _One:
+        def __getitem__(self, i):
+            return None
+    ms, _ = time_calls(lambda _: graph.replay(), _One(), replays, 3)
+    per = ms / chunk
+    return {"workload": f"ttt_linear_decode_{'mse' if loss else 'dot'}_B{B}_H{H}_d{d}_b{chunk}_bf16_graph",
+            "us_per_step": per * 1e3, "tokens_per_s": B / (per * 1e-3),
+            "note": f"{chunk} steps per graph replay; state resident in the last-level cache"}
+
+
 def bench_lact_decode(B, H, d, hid, steps, warmup, seed=43):
     import numpy as np
     import torch
@@ -309,6 +349,8 @@ def bench_decode(steps, warmup):
     for args in ((256, 8, 64, 1, 16), (4, 8, 64, 1, 16), (256, 8, 64, 1, 1), (64, 16, 128, 1, 16)):
         log(f"[bench] timing decode {args}")
         res.append(bench_linear_decode(*args, "bf16", steps, warmup))
+    log("[bench] timing decode (4, 8, 64, 1, 16) replayed from a graph")
+    res.append(bench_linear_decode_graph(4, 8, 64, 1, 16, max(20, steps // 5)))
     for args in ((64, 4, 256, 512), (64, 2, 384, 768)):
         log(f"[bench] timing LaCT decode {args}")
         res.append(bench_lact_decode(*args, steps, warmup))

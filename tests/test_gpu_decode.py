@@ -187,3 +187,50 @@ def test_lact_decode_sequence_matches_causal_forward():
                                  ("w1", "w2", "w3")):
         assert_close(to_np(got), ref, "bf16", n)
         assert_close(to_np(got) - init, ref - init, "bf16", n + " change", rms_tol=DELTA_TOL_LACT)
+
+
+def test_linear_decode_graph_replays():
+    """Sixteen chunk-anchored decode steps (one 16-token chunk, closed at its last
+    token) captured into a graph: every replay, from the same initial state and
+    with eager work between replays, equals the eager steps bit for bit."""
+    cla = _cla()
+    B, H, T, d, chunk = 4, 8, 16, 64, 16
+    inp, g = _linear_inputs(B, H, T, d, "bf16", seed=150)
+    toks = [(_tok(g, "q", t), _tok(g, "k", t), _tok(g, "v", t), g["eta"][:, :, t].contiguous())
+            for t in range(T)]
+    w0 = g["w0"]
+    print("[case] decode graph, 16 anchored steps, B=4 H=8 d=64 bf16", flush=True)
+
+    def run(w, anchor, outs):
+        for t in range(T):
+            cla.ttt_linear_decode(*toks[t], w, loss=1, w_anchor=anchor,
+                                  anchor_update=t == T - 1, out=outs[t])
+
+    w_e, a_e = w0.clone(), w0.clone()
+    outs_e = [torch.empty_like(toks[0][0]) for _ in range(T)]
+    run(w_e, a_e, outs_e)
+    torch.cuda.synchronize()
+    w_g, a_g = w0.clone(), w0.clone()
+    outs_g = [torch.empty_like(toks[0][0]) for _ in range(T)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(w_g, a_g, outs_g)  # warm-up before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(w_g, a_g, outs_g)
+    for _ in range(3):
+        w_g.copy_(w0)
+        a_g.copy_(w0)
+        for o in outs_g:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs_g, outs_e):
+            assert torch.equal(x, y)
+        assert torch.equal(w_g, w_e) and torch.equal(a_g, a_e)
+        run(w0.clone(), w0.clone(), [torch.empty_like(o) for o in outs_g])  # eager work between
+        torch.cuda.synchronize()
