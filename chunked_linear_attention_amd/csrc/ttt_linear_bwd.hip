@@ -19,7 +19,8 @@
 // and the backward one for G,
 //     G_c = G_{c+1} + R_c [- K^T H K G_{c+1}],   R_c = Q^T dO [- K^T S~],  S~ = S^T dO.
 // So the work runs in four launches: the state recursion and the G recursion
-// with one workgroup per (head, 16 columns), and between and after them two
+// with one workgroup per (head, 16 columns) and their operands staged in LDS
+// a batch of chunks at a time, and between and after them two
 // launches with one workgroup per (head, chunk) for everything else (the
 // G-free terms and R_c first, then the terms that need G_{c+1}), exchanging
 // per-chunk matrices through the workspace.  Everything is fp32 FMA in LDS.
@@ -56,74 +57,94 @@ template <typename E> __device__ __forceinline__ void stf(void *p, long i, float
 
 constexpr int CB = 16;  // state columns per workgroup in the serial passes
 
+// Serial passes: the operands of NB chunks at a time are loaded into registers
+// while the previous NB chunks compute out of LDS, and written to LDS once per
+// batch, so no chunk step waits for memory (a step only reads LDS and stores).
+template <int B> struct Batch {
+    static constexpr int NB = B <= 16 ? 8 : 4;
+};
+
 // Serial pass 1 (one workgroup per (head, 16 state columns); columns of the
 // state never mix in the recursion W_{c+1} = W_c + K^T H (V - K W_c)):
-// writes every chunk-start state.  The next chunk's K, V columns and eta are
-// loaded into registers while the current chunk computes.
+// writes every chunk-start state.
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 {
+    constexpr int NB = Batch<B>::NB, NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
     __shared__ float W[D][CB + 1];
-    __shared__ float Ks[B][D + 1], Us[B][CB + 1];
-    __shared__ float et[B];
-    constexpr int NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
+    __shared__ float Ks[2][NB][B][D + 1], Us[2][NB][B][CB + 1];
+    __shared__ float et[2][NB][B];
+    __shared__ float Ut[B][CB + 1];
     const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
-    float pk[NK], pv[NV], pe = 0.f;
-    auto fetch = [&](int c) {
-        const int c0 = c * B, n = min(B, p.T - c0);
+    const int nbat = (p.nchunks + NB - 1) / NB;
+    float pk[NB][NK], pv[NB][NV], pe[NB];
+    auto load = [&](int k) {
 #pragma unroll
-        for (int r = 0; r < NK; ++r) {
-            const int e = tid + 256 * r, i = e / D, a = e % D;
-            pk[r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
-        }
+        for (int m = 0; m < NB; ++m) {
+            const int c = k * NB + m;
+            const int c0 = c * B, n = c < p.nchunks ? min(B, p.T - c0) : 0;
 #pragma unroll
-        for (int r = 0; r < NV; ++r) {
-            const int e = tid + 256 * r, i = e / CB, j = e % CB;
-            pv[r] = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j0 + j) : 0.f;
-        }
-        pe = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
-    };
-    auto commit = [&]() {
-#pragma unroll
-        for (int r = 0; r < NK; ++r) Ks[(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[r];
-#pragma unroll
-        for (int r = 0; r < NV; ++r) Us[(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pv[r];
-        if (tid < B) et[tid] = pe;
-    };
-    for (int e = tid; e < D * CB; e += 256) W[e / CB][e % CB] = p.w0[(long)h * D * D + (e / CB) * D + j0 + e % CB];
-    fetch(0);
-    commit();
-    __syncthreads();
-    for (int c = 0; c < p.nchunks; ++c) {
-        // loads first: a later wait for them then does not also wait for the stores
-        if (c + 1 < p.nchunks) fetch(c + 1);
-        float *dst = p.states + ((long)h * p.nchunks + c) * D * D;
-        for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
-        if (p.loss == 1) {
-            float u[NV];
+            for (int r = 0; r < NK; ++r) {
+                const int e = tid + 256 * r, i = e / D, a = e % D;
+                pk[m][r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
+            }
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
                 const int e = tid + 256 * r, i = e / CB, j = e % CB;
-                float s = 0.f;
-                for (int a = 0; a < D; ++a) s += Ks[i][a] * W[a][j];
-                u[r] = Us[i][j] - s;
+                pv[m][r] = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j0 + j) : 0.f;
+            }
+            pe[m] = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+#pragma unroll
+            for (int r = 0; r < NK; ++r) Ks[buf][m][(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[m][r];
+#pragma unroll
+            for (int r = 0; r < NV; ++r) Us[buf][m][(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pv[m][r];
+            if (tid < B) et[buf][m][tid] = pe[m];
+        }
+    };
+    for (int e = tid; e < D * CB; e += 256) W[e / CB][e % CB] = p.w0[(long)h * D * D + (e / CB) * D + j0 + e % CB];
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int k = 0; k < nbat; ++k) {
+        const int buf = k & 1;
+        if (k + 1 < nbat) load(k + 1);
+        for (int m = 0; m < NB; ++m) {
+            const int c = k * NB + m;
+            if (c >= p.nchunks) break;
+            float *dst = p.states + ((long)h * p.nchunks + c) * D * D;
+            for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
+            const float(*Kc)[D + 1] = Ks[buf][m];
+            const float(*Vc)[CB + 1] = Us[buf][m];
+            const float(*Uc)[CB + 1] = Vc;
+            if (p.loss == 1) {  // U = V - K W
+                for (int e = tid; e < B * CB; e += 256) {
+                    const int i = e / CB, j = e % CB;
+                    float sacc = 0.f;
+#pragma unroll
+                    for (int a = 0; a < D; ++a) sacc += Kc[i][a] * W[a][j];
+                    Ut[i][j] = Vc[i][j] - sacc;
+                }
+                lds_barrier();
+                Uc = Ut;
+            }
+            for (int e = tid; e < D * CB; e += 256) {
+                const int a = e / CB, j = e % CB;
+                float sacc = 0.f;
+#pragma unroll
+                for (int i = 0; i < B; ++i) sacc += Kc[i][a] * et[buf][m][i] * Uc[i][j];
+                W[a][j] += sacc;
             }
             lds_barrier();
-#pragma unroll
-            for (int r = 0; r < NV; ++r) Us[(tid + 256 * r) / CB][(tid + 256 * r) % CB] = u[r];
-            lds_barrier();
         }
-        for (int e = tid; e < D * CB; e += 256) {
-            const int a = e / CB, j = e % CB;
-            float s = 0.f;
-            for (int i = 0; i < B; ++i) s += Ks[i][a] * et[i] * Us[i][j];
-            W[a][j] += s;
-        }
-        lds_barrier();
-        if (c + 1 < p.nchunks) {
-            commit();
-            lds_barrier();
+        if (k + 1 < nbat) {
+            store(buf ^ 1);
+            __syncthreads();
         }
     }
 }
@@ -275,76 +296,94 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
 
 // Serial pass 3 (one workgroup per (head, 16 columns of G); G's columns never
 // mix either): G_c = G_{c+1} + R_c [- K^T H K G_{c+1}], storing every G_{c+1};
-// the last G is d_w_init.  The next chunk's K, eta and R_c columns are loaded
-// into registers while the current chunk computes.
+// the last G is d_w_init.  Chunks run last to first, in batches as above.
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
 {
-    __shared__ float G[D][CB + 1], Rs[D][CB + 1];
-    __shared__ float Ks[B][D + 1], KG[B][CB + 1];
-    __shared__ float et[B];
-    constexpr int NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
+    constexpr int NB = Batch<B>::NB, NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
+    __shared__ float G[D][CB + 1], KG[B][CB + 1];
+    __shared__ float Rs[2][NB][D][CB + 1], Ks[2][NB][B][D + 1];
+    __shared__ float et[2][NB][B];
     const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
-    float pk[NK], pr[NR], pe = 0.f;
-    auto fetch = [&](int c) {
-        const int c0 = c * B, n = min(B, p.T - c0);
-        const float *R = p.rc + ((long)h * p.nchunks + c) * D * D;
+    const int last = p.nchunks - 1;
+    const int nbat = (p.nchunks + NB - 1) / NB;
+    float pk[NB][NK], pr[NB][NR], pe[NB];
+    auto load = [&](int k) {  // batch k = chunks last - k NB - m, m < NB
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int e = tid + 256 * r;
-            pr[r] = R[(long)(e / CB) * D + j0 + e % CB];
-        }
-        if (p.loss == 1) {
+        for (int m = 0; m < NB; ++m) {
+            const int c = last - (k * NB + m);
+            const bool ok = c >= 0;
+            const int c0 = c * B, n = ok ? min(B, p.T - c0) : 0;
+            const float *R = p.rc + ((long)h * p.nchunks + (ok ? c : 0)) * D * D;
 #pragma unroll
-            for (int r = 0; r < NK; ++r) {
-                const int e = tid + 256 * r, i = e / D, a = e % D;
-                pk[r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
+            for (int r = 0; r < NR; ++r) {
+                const int e = tid + 256 * r;
+                pr[m][r] = ok ? R[(long)(e / CB) * D + j0 + e % CB] : 0.f;
             }
-            pe = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
+            if (p.loss == 1) {
+#pragma unroll
+                for (int r = 0; r < NK; ++r) {
+                    const int e = tid + 256 * r, i = e / D, a = e % D;
+                    pk[m][r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
+                }
+                pe[m] = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
+            }
         }
     };
-    auto commit = [&]() {
+    auto store = [&](int buf) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) Rs[(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pr[r];
-        if (p.loss == 1) {
+        for (int m = 0; m < NB; ++m) {
 #pragma unroll
-            for (int r = 0; r < NK; ++r) Ks[(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[r];
-            if (tid < B) et[tid] = pe;
+            for (int r = 0; r < NR; ++r) Rs[buf][m][(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pr[m][r];
+            if (p.loss == 1) {
+#pragma unroll
+                for (int r = 0; r < NK; ++r) Ks[buf][m][(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[m][r];
+                if (tid < B) et[buf][m][tid] = pe[m];
+            }
         }
     };
     for (int e = tid; e < D * CB; e += 256)
         G[e / CB][e % CB] = p.dwf ? p.dwf[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
-    fetch(p.nchunks - 1);
-    commit();
+    load(0);
+    store(0);
     __syncthreads();
-    for (int c = p.nchunks - 1; c >= 0; --c) {
-        // loads first: a later wait for them then does not also wait for the stores
-        if (c > 0) fetch(c - 1);
-        float *gdst = p.gnext + ((long)h * p.nchunks + c) * D * D;
-        for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
-        if (p.loss == 1) {
-            for (int e = tid; e < B * CB; e += 256) {
-                const int i = e / CB, j = e % CB;
-                float s = 0.f;
-                for (int a = 0; a < D; ++a) s += Ks[i][a] * G[a][j];
-                KG[i][j] = et[i] * s;
+    for (int k = 0; k < nbat; ++k) {
+        const int buf = k & 1;
+        if (k + 1 < nbat) load(k + 1);
+        for (int m = 0; m < NB; ++m) {
+            const int c = last - (k * NB + m);
+            if (c < 0) break;
+            float *gdst = p.gnext + ((long)h * p.nchunks + c) * D * D;
+            for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+            const float(*Kc)[D + 1] = Ks[buf][m];
+            if (p.loss == 1) {
+                for (int e = tid; e < B * CB; e += 256) {
+                    const int i = e / CB, j = e % CB;
+                    float sacc = 0.f;
+#pragma unroll
+                    for (int a = 0; a < D; ++a) sacc += Kc[i][a] * G[a][j];
+                    KG[i][j] = et[buf][m][i] * sacc;
+                }
+                lds_barrier();
+            }
+            for (int e = tid; e < D * CB; e += 256) {
+                const int a = e / CB, j = e % CB;
+                float sacc = Rs[buf][m][a][j];
+                if (p.loss == 1) {
+#pragma unroll
+                    for (int i = 0; i < B; ++i) sacc -= Kc[i][a] * KG[i][j];
+                }
+                G[a][j] += sacc;
             }
             lds_barrier();
         }
-        for (int e = tid; e < D * CB; e += 256) {
-            const int a = e / CB, j = e % CB;
-            float s = Rs[a][j];
-            if (p.loss == 1)
-                for (int i = 0; i < B; ++i) s -= Ks[i][a] * KG[i][j];
-            G[a][j] += s;
-        }
-        lds_barrier();
-        if (c > 0) {
-            commit();
-            lds_barrier();
+        if (k + 1 < nbat) {
+            store(buf ^ 1);
+            __syncthreads();
         }
     }
+    __syncthreads();
     for (int e = tid; e < D * CB; e += 256) p.dw0[(long)h * D * D + (e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
 }
 
