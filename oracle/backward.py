@@ -27,7 +27,9 @@ steps, token by token in reverse, each step's adjoint written out:
 
 and at a chunk start the gradient reaching W_c (the running state before the
 chunk's first token) adds the residual contributions dW_c.  The running states
-W_t of a chunk are recomputed forward from W_c before its reverse sweep.
+W_t of a chunk are recomputed forward from W_c before its reverse sweep.  The
+update-then-apply order (all key/value chunks update, then every query reads
+the final state) is differentiated the same way, its apply first.
 """
 from __future__ import annotations
 
@@ -37,8 +39,28 @@ LOSS_DOT = 0
 LOSS_MSE = 1
 
 
+def _head_bwd_noncausal(q, k, v, eta, w0, dy, dwf, chunk, loss):
+    """Update-then-apply order: the chunked updates run over all key/value tokens
+    (no outputs), then y_j = q_j W_final for every query.  Adjoint of the apply:
+    dq_j = dy_j W_final^T and dW_final += sum_j q_j^T dy_j; then the same reverse
+    sweep over the key/value chunks with no output terms."""
+    Tkv, d = k.shape
+    W = w0.copy()
+    for c0 in range(0, Tkv, chunk):
+        Wc = W.copy()
+        for t in range(c0, min(c0 + chunk, Tkv)):
+            r = k[t] @ Wc - v[t] if loss == LOSS_MSE else -v[t]
+            W = W - eta[t] * np.outer(k[t], r)
+    dq = dy @ W.T
+    G = dwf + q.T @ dy
+    dk, dv, deta = np.zeros_like(k), np.zeros_like(v), np.zeros_like(eta)
+    zero_q = np.zeros((Tkv, d))
+    _, dk, dv, deta, G = _head_bwd(zero_q, k, v, eta, w0, zero_q, G, chunk, loss)
+    return dq, dk, dv, deta, G
+
+
 def _head_bwd(q, k, v, eta, w0, dy, dwf, chunk, loss):
-    T, d = q.shape
+    T, d = k.shape
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -83,18 +105,20 @@ def _head_bwd(q, k, v, eta, w0, dy, dwf, chunk, loss):
     return dq, dk, dv, deta, G
 
 
-def ttt_linear_bwd(q, k, v, eta, w0, dy, dwf=None, *, chunk: int, loss: int):
-    """q, k, v, dy [B,H,T,d]; eta [B,H,T]; w0, dwf [B,H,d,d] (dwf None = zero).
-    Returns (dq, dk, dv, deta, dw0)."""
+def ttt_linear_bwd(q, k, v, eta, w0, dy, dwf=None, *, chunk: int, loss: int, order: int = 0):
+    """q, dy [B,H,Tq,d]; k, v [B,H,Tkv,d]; eta [B,H,Tkv]; w0, dwf [B,H,d,d] (dwf None
+    = zero).  order 0: causal (Tq == Tkv); 1: update over all keys, then apply to
+    every query.  Returns (dq, dk, dv, deta, dw0)."""
     q, k, v, eta, w0, dy = (np.asarray(a, dtype=np.float64) for a in (q, k, v, eta, w0, dy))
-    B, H, T, d = q.shape
+    B, H, Tq, d = q.shape
     dwf = np.zeros((B, H, d, d)) if dwf is None else np.asarray(dwf, dtype=np.float64)
     outs = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(eta),
             np.zeros_like(w0)]
+    fn = _head_bwd if order == 0 else _head_bwd_noncausal
     for b in range(B):
         for h in range(H):
-            r = _head_bwd(q[b, h], k[b, h], v[b, h], eta[b, h], w0[b, h], dy[b, h], dwf[b, h],
-                          chunk, loss)
+            r = fn(q[b, h], k[b, h], v[b, h], eta[b, h], w0[b, h], dy[b, h], dwf[b, h],
+                   chunk, loss)
             for o, x in zip(outs, r):
                 o[b, h] = x
     return tuple(outs)

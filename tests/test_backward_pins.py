@@ -106,3 +106,37 @@ def test_dot_zero_state_closed_form():
                                              for t in range(i, T))) < 1e-12
     # dW0 = sum_t q_t^T dy_t
     assert rel(dw0[0, 0], q[0, 0].T @ dy[0, 0]) < 1e-12
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [1, 4, 20])
+def test_noncausal_backward_matches_finite_differences(loss, chunk):
+    """Update over all key/value chunks, then every query reads the final state."""
+    rng = np.random.default_rng(400 + chunk + loss)
+    B, H, Tq, Tkv, d = 1, 2, 5, 9, 3
+    q = rng.standard_normal((B, H, Tq, d)) / np.sqrt(d)
+    k = rng.standard_normal((B, H, Tkv, d)) / np.sqrt(d)
+    v = rng.standard_normal((B, H, Tkv, d))
+    eta = rng.uniform(0.05, 0.4, (B, H, Tkv))
+    w0 = rng.standard_normal((B, H, d, d)) / np.sqrt(d)
+    dy = rng.standard_normal((B, H, Tq, d))
+    dwf = rng.standard_normal((B, H, d, d))
+    grads = ttt_linear_bwd(q, k, v, eta, w0, dy, dwf, chunk=chunk, loss=loss, order=1)
+
+    def L(args):
+        y, wf = oracle.ttt_linear(*args, chunk=chunk, loss=loss, order=oracle.NONCAUSAL)
+        return float(np.sum(y * dy) + np.sum(wf * dwf))
+
+    base = [q, k, v, eta, w0]
+    h = 1e-6
+    for idx, g in enumerate(grads):
+        fd = np.zeros_like(base[idx])
+        it = np.nditer(base[idx], flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            plus = [a.copy() for a in base]
+            minus = [a.copy() for a in base]
+            plus[idx][mi] += h
+            minus[idx][mi] -= h
+            fd[mi] = (L(plus) - L(minus)) / (2 * h)
+        assert rel(g, fd) < 1e-7, ("q", "k", "v", "eta", "w0")[idx]
