@@ -408,7 +408,7 @@ def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
     eta, w0 = torch.from_numpy(inp["eta"]).cuda(), torch.from_numpy(inp["w0"]).cuda()
     dy = up(ti.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32)))
     import chunked_linear_attention_amd._lib as L
-    nb = L.load().ttt_linear_bwd_workspace_bytes(B, H, T, d, chunk, loss, 1)
+    nb = L.load().ttt_linear_bwd_workspace_bytes(B, H, T, T, d, chunk, loss, 0, 1)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
 
     class _One:

@@ -60,10 +60,10 @@ def load() -> ctypes.CDLL:
         lib.lact_swiglu_fwd_rule.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp] + \
             [i] * 11 + [f, i, f, vp, vp, vp, vp, sz, vp]
         lib.lact_swiglu_fwd_rule.restype = i
-        lib.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 7
+        lib.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 9
         lib.ttt_linear_bwd_workspace_bytes.restype = sz
         lib.ttt_linear_bwd.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp] + \
-            [i] * 6 + [vp, sz, vp]
+            [i] * 8 + [vp, sz, vp]
         lib.ttt_linear_bwd.restype = i
         lib.window_attention_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, f, i, vp]
         lib.window_attention_fwd.restype = i

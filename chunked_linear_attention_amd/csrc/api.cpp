@@ -63,7 +63,7 @@ const char *ttt_status_string(int status)
     }
 }
 
-int ttt_abi_version(void) { return 1; }
+int ttt_abi_version(void) { return 2; }
 
 size_t ttt_linear_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
                                   int order, int dtype)
@@ -243,34 +243,45 @@ ttt_status window_attention_fwd(const void *q, const void *k, const void *v, int
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 
-size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int loss, int dtype)
+size_t ttt_linear_bwd_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
+                                      int order, int dtype)
 {
-    if (!valid_enums(dtype, loss, TTT_CAUSAL) || B < 1 || H < 1 || T < 1) return 0;
-    if ((long long)B * H > (1LL << 24) || (long long)T > (1LL << 30)) return 0;
+    if (!valid_enums(dtype, loss, order) || B < 1 || H < 1 || Tq < 0 || Tkv < 1) return 0;
+    if (order == TTT_CAUSAL && Tq != Tkv) return 0;
+    if ((long long)B * H > (1LL << 24) || (long long)Tq > (1LL << 30) || (long long)Tkv > (1LL << 30))
+        return 0;
     if (d != 64 || (chunk != 16 && chunk != 32)) return 0;
-    return tttk::linear_bwd_workspace(B * H, T, d, chunk);
+    return tttk::linear_bwd_workspace(B * H, Tkv, d, chunk);
 }
 
 ttt_status ttt_linear_bwd(const void *q, const void *k, const void *v, int dtype, const float *eta,
                           const float *w_init, const void *d_out, const float *d_w_final,
                           void *d_q, void *d_k, void *d_v, float *d_eta, float *d_w_init, int B,
-                          int H, int T, int d, int chunk, int loss, void *workspace,
-                          size_t workspace_bytes, void *stream)
+                          int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                          void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!valid_enums(dtype, loss, TTT_CAUSAL)) return TTT_EINVAL;
-    if (B < 1 || H < 1 || T < 1 || d < 1 || chunk < 1) return TTT_EINVAL;
-    const void *req[11] = {q, k, v, eta, w_init, d_out, d_q, d_k, d_v, d_eta, d_w_init};
+    if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
+    if (B < 1 || H < 1 || Tq < 0 || Tkv < 1 || d < 1 || chunk < 1) return TTT_EINVAL;
+    if (order == TTT_CAUSAL && Tq != Tkv) return TTT_EINVAL;
+    const void *req[8] = {k, v, eta, w_init, d_k, d_v, d_eta, d_w_init};
     for (const void *p : req)
         if (!p || !aligned16(p)) return TTT_EINVAL;
+    if (Tq > 0) {
+        const void *qs[3] = {q, d_out, d_q};
+        for (const void *p : qs)
+            if (!p || !aligned16(p)) return TTT_EINVAL;
+    }
     if (d_w_final && !aligned16(d_w_final)) return TTT_EINVAL;
-    if ((long long)B * H > (1LL << 24) || (long long)T > (1LL << 30)) return TTT_EUNSUPPORTED;
+    if ((long long)B * H > (1LL << 24) || (long long)Tq > (1LL << 30) || (long long)Tkv > (1LL << 30))
+        return TTT_EUNSUPPORTED;
     if (d != 64 || (chunk != 16 && chunk != 32)) return TTT_EUNSUPPORTED;
-    const size_t need = tttk::linear_bwd_workspace(B * H, T, d, chunk);
+    const size_t need = tttk::linear_bwd_workspace(B * H, Tkv, d, chunk);
     if (!workspace || !aligned16(workspace)) return TTT_EINVAL;
     if (workspace_bytes < need) return TTT_EWORKSPACE;
-    hipError_t e = tttk::linear_bwd_launch(B * H, T, d, chunk, loss, dtype == TTT_BF16 ? 1 : 0, q,
-                                           k, v, eta, w_init, d_out, d_w_final, d_q, d_k, d_v,
-                                           d_eta, d_w_init, workspace, (hipStream_t)stream);
+    hipError_t e = tttk::linear_bwd_launch(B * H, Tq, Tkv, d, chunk, loss, order,
+                                           dtype == TTT_BF16 ? 1 : 0, q, k, v, eta, w_init, d_out,
+                                           d_w_final, d_q, d_k, d_v, d_eta, d_w_init, workspace,
+                                           (hipStream_t)stream);
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 

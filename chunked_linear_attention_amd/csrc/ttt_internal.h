@@ -68,10 +68,11 @@ hipError_t window_attn_launch(int NH, int T, int d, int window, float scale, int
                               hipStream_t stream);
 
 // ---- TTT-Linear backward (causal) -----------------------------------------------------
-size_t linear_bwd_workspace(int NH, int T, int d, int chunk);
-hipError_t linear_bwd_launch(int NH, int T, int d, int chunk, int loss, int bf16, const void *q,
-                             const void *k, const void *v, const float *eta, const float *w0,
-                             const void *dout, const float *dwf, void *dq, void *dk, void *dv,
-                             float *deta, float *dw0, void *ws, hipStream_t stream);
+size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk);
+hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                             int bf16, const void *q, const void *k, const void *v,
+                             const float *eta, const float *w0, const void *dout, const float *dwf,
+                             void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
+                             hipStream_t stream);
 
 }  // namespace tttk

@@ -43,7 +43,10 @@ struct LinBwdParams {
     float *ub;      // [NH][nchunks * B][D] U (MSE residuals)
     float *st;      // [NH][nchunks * B][D] S~ = S^T dO
     float *dkl;     // [NH][nchunks * B][D] dA^T Q [- S~ W_c^T]
-    int T, nchunks, loss;
+    int T, nchunks, loss;  // T: key/value tokens (= queries in the causal order)
+    int order, Tq;         // order 1: update over all key/value chunks, then apply to Tq queries
+    float *wfinal;         // [NH][D][D] (order 1) final state
+    float *ginit;          // [NH][D][D] (order 1) dL/dW_final incl. the apply's Q^T dO
 };
 
 template <typename E> __device__ __forceinline__ float ldf(const void *p, long i)
@@ -147,6 +150,8 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
             __syncthreads();
         }
     }
+    if (p.order == 1)
+        for (int e = tid; e < D * CB; e += 256) p.wfinal[(long)h * D * D + (e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
 }
 
 // Parallel pass 2, one workgroup per (head, chunk): every term that does not
@@ -316,10 +321,11 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
             const bool ok = c >= 0;
             const int c0 = c * B, n = ok ? min(B, p.T - c0) : 0;
             const float *R = p.rc + ((long)h * p.nchunks + (ok ? c : 0)) * D * D;
+            const bool hasr = ok && p.order == 0;  // the update-then-apply order has no R_c
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const int e = tid + 256 * r;
-                pr[m][r] = ok ? R[(long)(e / CB) * D + j0 + e % CB] : 0.f;
+                pr[m][r] = hasr ? R[(long)(e / CB) * D + j0 + e % CB] : 0.f;
             }
             if (p.loss == 1) {
 #pragma unroll
@@ -343,8 +349,9 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
             }
         }
     };
+    const float *g0 = p.order == 1 ? p.ginit : p.dwf;
     for (int e = tid; e < D * CB; e += 256)
-        G[e / CB][e % CB] = p.dwf ? p.dwf[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
+        G[e / CB][e % CB] = g0 ? g0[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
     load(0);
     store(0);
     __syncthreads();
@@ -406,21 +413,37 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
         Gn[e / D][e % D] = p.gnext[cb * D * D + e];
         if (p.loss == 1) Wc[e / D][e % D] = p.states[cb * D * D + e];
     }
+    const bool nc = p.order == 1;  // no outputs per chunk: U from here, no G-free parts
     for (int e = tid; e < B * D; e += 256) {
         const int i = e / D, j = e % D;
         const bool ok = i < n;
         Ks[i][j] = ok ? ldf<E>(p.k, (tok0 + c0 + i) * D + j) : 0.f;
-        Us[i][j] = p.loss == 1 ? p.ub[(row0 + i) * D + j] : (ok ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f);
+        Us[i][j] = (p.loss == 1 && !nc) ? p.ub[(row0 + i) * D + j]
+                                        : (ok ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f);
     }
     if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
     __syncthreads();
+    if (nc && p.loss == 1) {  // U = V - K W_c
+        float u[NBD];
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) {
+            const int e = tid + 256 * r, i = e / D, j = e % D;
+            float sacc = 0.f;
+            for (int a = 0; a < D; ++a) sacc += Ks[i][a] * Wc[a][j];
+            u[r] = Us[i][j] - sacc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) Us[(tid + 256 * r) / D][(tid + 256 * r) % D] = u[r];
+        __syncthreads();
+    }
 #pragma unroll
     for (int r = 0; r < NBD; ++r) {
         const int e = tid + 256 * r, i = e / D, j = e % D;
         float s = 0.f;
         for (int a = 0; a < D; ++a) s += Ks[i][a] * Gn[a][j];
         KGs[i][j] = s;
-        if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + j, p.st[(row0 + i) * D + j] + et[i] * s);
+        if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + j, (nc ? 0.f : p.st[(row0 + i) * D + j]) + et[i] * s);
     }
     __syncthreads();
     if (tid < 64) {
@@ -428,7 +451,7 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
             float s = 0.f;
             for (int a = tid; a < D; a += 64) s += KGs[i][a] * Us[i][a];
             for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-            if (tid == 0) p.deta[tok0 + c0 + i] += s;
+            if (tid == 0) p.deta[tok0 + c0 + i] = (nc ? 0.f : p.deta[tok0 + c0 + i]) + s;
         }
     }
 #pragma unroll
@@ -439,17 +462,84 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
             s += Us[i][j] * Gn[a][j];
             if (p.loss == 1) s -= KGs[i][j] * Wc[a][j];
         }
-        if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, p.dkl[(row0 + i) * D + a] + et[i] * s);
+        if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, (nc ? 0.f : p.dkl[(row0 + i) * D + a]) + et[i] * s);
+    }
+}
+
+// Update-then-apply order, the apply's adjoint: G_final = dW_final + Q^T dO
+// (one workgroup per (head, 16 columns), queries in tiles of 64) ...
+template <int D, typename E>
+__global__ __launch_bounds__(256) void lbw_nc_g(LinBwdParams p)
+{
+    __shared__ float Qs[64][D + 1], dOs[64][CB + 1];
+    constexpr int NCB = D / CB;
+    const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
+    const long q0 = (long)h * p.Tq;
+    float acc[D * CB / 256];
+#pragma unroll
+    for (int r = 0; r < D * CB / 256; ++r) {
+        const int e = tid + 256 * r;
+        acc[r] = p.dwf ? p.dwf[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
+    }
+    for (int t0 = 0; t0 < p.Tq; t0 += 64) {
+        const int n = min(64, p.Tq - t0);
+        for (int e = tid; e < 64 * D; e += 256) {
+            const int t = e / D, a = e % D;
+            Qs[t][a] = t < n ? ldf<E>(p.q, (q0 + t0 + t) * D + a) : 0.f;
+        }
+        for (int e = tid; e < 64 * CB; e += 256) {
+            const int t = e / CB, j = e % CB;
+            dOs[t][j] = t < n ? ldf<E>(p.dout, (q0 + t0 + t) * D + j0 + j) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < D * CB / 256; ++r) {
+            const int e = tid + 256 * r, a = e / CB, j = e % CB;
+            float sacc = 0.f;
+            for (int t = 0; t < 64; ++t) sacc += Qs[t][a] * dOs[t][j];
+            acc[r] += sacc;
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < D * CB / 256; ++r) {
+        const int e = tid + 256 * r;
+        p.ginit[(long)h * D * D + (e / CB) * D + j0 + e % CB] = acc[r];
+    }
+}
+
+// ... and dQ = dO W_final^T (one workgroup per (head, 64 queries)).
+template <int D, typename E>
+__global__ __launch_bounds__(256) void lbw_nc_dq(LinBwdParams p)
+{
+    __shared__ float Wf[D][D + 1], dOs[64][D + 1];
+    const int nqt = (p.Tq + 63) / 64;
+    const int h = blockIdx.x / nqt, t0 = (blockIdx.x % nqt) * 64, tid = threadIdx.x;
+    const long q0 = (long)h * p.Tq;
+    const int n = min(64, p.Tq - t0);
+    for (int e = tid; e < D * D; e += 256) Wf[e / D][e % D] = p.wfinal[(long)h * D * D + e];
+    for (int e = tid; e < 64 * D; e += 256) {
+        const int t = e / D, j = e % D;
+        dOs[t][j] = t < n ? ldf<E>(p.dout, (q0 + t0 + t) * D + j) : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * D; e += 256) {
+        const int t = e / D, a = e % D;
+        float sacc = 0.f;
+        for (int j = 0; j < D; ++j) sacc += dOs[t][j] * Wf[a][j];
+        if (t < n) stf<E>(p.dq, (q0 + t0 + t) * D + a, sacc);
     }
 }
 
 }  // namespace
 
-size_t linear_bwd_workspace(int NH, int T, int d, int chunk)
+size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
 {
-    const size_t nch = (T + chunk - 1) / chunk;
-    // states, G_{c+1}, R_c (d x d per chunk) and U, S~, dK part (chunk x d per chunk), fp32
-    return (size_t)NH * nch * (3 * (size_t)d * d + 3 * (size_t)chunk * d) * sizeof(float);
+    const size_t nch = (Tkv + chunk - 1) / chunk;
+    // states, G_{c+1}, R_c (d x d per chunk) and U, S~, dK part (chunk x d per chunk), plus
+    // the final state and dL/dW_final (update-then-apply order), fp32
+    return (size_t)NH * (nch * (3 * (size_t)d * d + 3 * (size_t)chunk * d) + 2 * (size_t)d * d) *
+           sizeof(float);
 }
 
 template <int B, typename E>
@@ -457,22 +547,29 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
     lbw_states<64, B, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
-    lbw_local<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+    if (p.order == 0) {
+        lbw_local<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+    } else {
+        lbw_nc_g<64, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
+        if (p.Tq > 0) lbw_nc_dq<64, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
+    }
     lbw_grad<64, B, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
     lbw_dep<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
 }
 
-hipError_t linear_bwd_launch(int NH, int T, int d, int chunk, int loss, int bf16, const void *q,
-                             const void *k, const void *v, const float *eta, const float *w0,
-                             const void *dout, const float *dwf, void *dq, void *dk, void *dv,
-                             float *deta, float *dw0, void *ws, hipStream_t st)
+hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                             int bf16, const void *q, const void *k, const void *v,
+                             const float *eta, const float *w0, const void *dout, const float *dwf,
+                             void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
+                             hipStream_t st)
 {
-    const int nch = (T + chunk - 1) / chunk;
+    const int nch = (Tkv + chunk - 1) / chunk;
     float *base = static_cast<float *>(ws);
     const size_t dd = (size_t)NH * nch * d * d, bd = (size_t)NH * nch * chunk * d;
+    float *tail = base + 3 * dd + 3 * bd;
     LinBwdParams p{q, k, v, dout, eta, w0, dwf, dq, dk, dv, deta, dw0, base, base + dd,
-                   base + 2 * dd, base + 3 * dd, base + 3 * dd + bd, base + 3 * dd + 2 * bd, T,
-                   nch, loss};
+                   base + 2 * dd, base + 3 * dd, base + 3 * dd + bd, base + 3 * dd + 2 * bd, Tkv,
+                   nch, loss, order, Tq, tail, tail + (size_t)NH * d * d};
     if (chunk == 16) {
         if (bf16) lbw_run<16, __bf16>(p, NH, st);
         else lbw_run<16, float>(p, NH, st);

@@ -242,31 +242,32 @@ def window_attention_fwd(q, k, v, *, window: int, scale=None, out=None, accumula
 
 
 def ttt_linear_bwd(q, k, v, eta, w_init, d_out, d_w_final=None, *, chunk: int, loss="mse",
-                   workspace=None, stream=None):
-    """Backward of the causal ttt_linear_fwd: returns (d_q, d_k, d_v, d_eta, d_w_init)
-    for upstream gradients d_out [B,H,T,d] (q's dtype) and d_w_final [B,H,d,d] fp32
+                   order="causal", workspace=None, stream=None):
+    """Backward of ttt_linear_fwd: returns (d_q, d_k, d_v, d_eta, d_w_init) for
+    upstream gradients d_out [B,H,Tq,d] (q's dtype) and d_w_final [B,H,d,d] fp32
     (None = zero)."""
     lib = load()
-    B, H, T, d = q.shape
+    B, H, Tq, d = q.shape
+    Tkv = k.shape[2]
     dt = q.dtype
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_out, "d_out")):
+    for t, n, T in ((q, "q", Tq), (k, "k", Tkv), (v, "v", Tkv), (d_out, "d_out", Tq)):
         _check(t, n, dt)
         if tuple(t.shape) != (B, H, T, d):
-            raise ValueError(f"{n} must be shaped like q")
+            raise ValueError(f"{n} has the wrong shape")
     _check(eta, "eta", torch.float32)
     _check(w_init, "w_init", torch.float32)
     if d_w_final is not None:
         _check(d_w_final, "d_w_final", torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     deta, dw0 = torch.empty_like(eta), torch.empty_like(w_init)
-    ls = _LOSS[loss]
-    nbytes = lib.ttt_linear_bwd_workspace_bytes(B, H, T, d, chunk, ls, _DT[dt])
+    ls, od = _LOSS[loss], _ORDER[order]
+    nbytes = lib.ttt_linear_bwd_workspace_bytes(B, H, Tq, Tkv, d, chunk, ls, od, _DT[dt])
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     rc = lib.ttt_linear_bwd(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(eta), _ptr(w_init),
                             _ptr(d_out), _ptr(d_w_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
-                            _ptr(dw0), B, H, T, d, chunk, ls, _ptr(workspace), workspace.numel(),
-                            _stream(stream))
+                            _ptr(dw0), B, H, Tq, Tkv, d, chunk, ls, od, _ptr(workspace),
+                            workspace.numel(), _stream(stream))
     if rc != TTT_OK:
         raise TTTError(rc, "ttt_linear_bwd")
     return dq, dk, dv, deta, dw0

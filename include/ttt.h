@@ -218,30 +218,34 @@ ttt_status ttt_linear_decode(const void *q, const void *k, const void *v, int dt
                              void *out, int B, int H, int d, int loss, void *stream);
 
 /* ------------------------------------------------------------------------
- * TTT-Linear backward, causal order: the gradients of a scalar loss through
- * ttt_linear_fwd (TTT_CAUSAL, Tq = Tkv = T), given its upstream gradients.
- * Reverse-mode differentiation of the per-chunk rule documented above (the
- * token-by-token definition), per chunk in reverse with G = dL/dW_{c+1}:
+ * TTT-Linear backward: the gradients of a scalar loss through ttt_linear_fwd
+ * with the same arguments, given its upstream gradients.  Reverse-mode
+ * differentiation of the per-chunk rule documented above (the token-by-token
+ * definition).  Causal order, per chunk in reverse with G = dL/dW_{c+1}:
  *   dU = S^T dO + H K G,  dS = (dO U^T) * M,  dA = dS H,
  *   d_eta = rowsum_t(dS * A) + rowsum(K G * U),  dQ = dO W_c^T + dA K,
  *   dK = dA^T Q + H U G^T [- dU W_c^T],  dV = dU,  G <- G + Q^T dO [- K^T dU]
  * (A = (Q K^T) * M, S = A H; bracketed terms for the MSE loss only).
- * Inputs: q, k, v, eta, w_init as given to the forward; d_out [B][H][T][d] in
- * `dtype`; d_w_final [B][H][d][d] fp32 or NULL (zero).
- * Outputs: d_q, d_k, d_v [B][H][T][d] in `dtype`; d_eta [B][H][T] fp32;
- * d_w_init [B][H][d][d] fp32.  Arithmetic: fp32 throughout (the chunk-start
- * states are recomputed by a forward pass into the workspace).
- * Supported: d = 64; chunk 16 or 32 (any T >= 1, ragged tails included);
- * dtype TTT_F32 or TTT_BF16.  Others: TTT_EUNSUPPORTED.  Outputs must not
- * overlap the inputs.
+ * Non-causal order: dQ = dO W_final^T, G starts at d_w_final + Q^T dO, and the
+ * same sweep runs over the key/value chunks without the output terms.
+ * Inputs: q, k, v, eta, w_init as given to the forward; d_out [B][H][Tq][d]
+ * in `dtype`; d_w_final [B][H][d][d] fp32 or NULL (zero).
+ * Outputs: d_q [B][H][Tq][d] and d_k, d_v [B][H][Tkv][d] in `dtype`; d_eta
+ * [B][H][Tkv] fp32; d_w_init [B][H][d][d] fp32.  Arithmetic: fp32 throughout
+ * (the chunk-start states are recomputed by a forward pass into the
+ * workspace).  Tq == Tkv for TTT_CAUSAL; Tkv >= 1; Tq may be 0 (q, d_out and
+ * d_q are then not read and may be NULL) in the non-causal order.
+ * Supported: d = 64; chunk 16 or 32 (ragged tails included); dtype TTT_F32 or
+ * TTT_BF16.  Others: TTT_EUNSUPPORTED.  Outputs must not overlap the inputs.
  * ------------------------------------------------------------------------ */
-size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int loss, int dtype);
+size_t ttt_linear_bwd_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
+                                      int order, int dtype);
 
 ttt_status ttt_linear_bwd(const void *q, const void *k, const void *v, int dtype, const float *eta,
                           const float *w_init, const void *d_out, const float *d_w_final,
                           void *d_q, void *d_k, void *d_v, float *d_eta, float *d_w_init, int B,
-                          int H, int T, int d, int chunk, int loss, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* LaCT decode apply ([LaCT] sections 3.2 and 4): out = W2 (silu(W1 q) * (W3 q))
  * for one query per (batch, head), with the weights as they stand (in the

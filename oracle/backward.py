@@ -1,4 +1,4 @@
-"""Backward pass of the causal TTT-Linear forward in fp64 -- test infrastructure.
+"""Backward pass of the TTT-Linear forward in fp64 -- test infrastructure.
 
 Like the rest of ``oracle/``, only tests, the smoke check and the benchmark's
 CPU leg may use this module; the library never does.

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ttt_abi_version() == 1
+    assert lib.ttt_abi_version() == 2
 
 
 def test_status_strings():
@@ -212,12 +212,14 @@ def test_window_attention_validation(kw, code):
 
 def lin_bwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w0=FAKE, do=FAKE, dwf=None, dq=FAKE, dk=FAKE,
-             dv=FAKE, de=FAKE, dw0=FAKE, B=1, H=1, T=100, d=64, chunk=16, loss=1, ws=FAKE, wsb=0,
-             stream=None)
+             dv=FAKE, de=FAKE, dw0=FAKE, B=1, H=1, T=100, Tkv=None, d=64, chunk=16, loss=1, order=0,
+             ws=FAKE, wsb=0, stream=None)
     a.update(kw)
+    tkv = a["T"] if a["Tkv"] is None else a["Tkv"]
     return lib.ttt_linear_bwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w0"], a["do"],
                               a["dwf"], a["dq"], a["dk"], a["dv"], a["de"], a["dw0"], a["B"], a["H"],
-                              a["T"], a["d"], a["chunk"], a["loss"], a["ws"], a["wsb"], a["stream"])
+                              a["T"], tkv, a["d"], a["chunk"], a["loss"], a["order"], a["ws"],
+                              a["wsb"], a["stream"])
 
 
 # every case fails validation before a launch (wsb = 0 ends the valid ones with EWORKSPACE)
@@ -228,6 +230,10 @@ def lin_bwd(lib, **kw):
     (dict(ws=None), _lib.TTT_EINVAL), (dict(T=0), _lib.TTT_EINVAL), (dict(loss=3), _lib.TTT_EINVAL),
     (dict(dtype=5), _lib.TTT_EINVAL), (dict(d=128), _lib.TTT_EUNSUPPORTED),
     (dict(chunk=64), _lib.TTT_EUNSUPPORTED), (dict(chunk=8), _lib.TTT_EUNSUPPORTED),
+    (dict(order=2), _lib.TTT_EINVAL), (dict(Tkv=50), _lib.TTT_EINVAL),
+    (dict(order=1, Tkv=50), _lib.TTT_EWORKSPACE), (dict(order=1, Tkv=0), _lib.TTT_EINVAL),
+    (dict(order=1, T=0, Tkv=50, q=None, do=None, dq=None), _lib.TTT_EWORKSPACE),
+    (dict(order=1, T=3, q=None), _lib.TTT_EINVAL),
 ])
 def test_linear_bwd_validation(kw, code):
     assert lin_bwd(_lib.load(), **kw) == code
@@ -236,7 +242,12 @@ def test_linear_bwd_validation(kw, code):
 def test_linear_bwd_workspace_query():
     lib = _lib.load()
     # per chunk and head: three fp32 d x d matrices (state, G, R) and three chunk x d ones
+    # plus the final state and dL/dW_final per head
     per = lambda b: (3 * 64 * 64 + 3 * b * 64) * 4
-    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 64, 16, 1, 1) == 32 * 256 * per(16)
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 64, 32, 0, 0) == 2 * per(32)
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 128, 16, 0, 0) == 0
+    tail = 2 * 64 * 64 * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 4096, 64, 16, 1, 0, 1) == \
+        32 * (256 * per(16) + tail)
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 64, 32, 0, 0, 0) == 2 * per(32) + tail
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 1, 0) == 2 * per(32) + tail
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 0, 0) == 0
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 16, 0, 0, 0) == 0

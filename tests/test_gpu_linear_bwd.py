@@ -22,12 +22,13 @@ def _cla():
     return cla
 
 
-def run_case(B, H, T, chunk, loss, dtype, seed, with_dwf=True, heads=None):
+def run_case(B, H, T, chunk, loss, dtype, seed, with_dwf=True, heads=None, order=0, Tq=None):
     cla = _cla()
     d = 64
-    inp = ti.gen_linear(B, H, T, T, d, seed=seed, dtype=dtype, w0="normal")
+    Tq = T if Tq is None else Tq
+    inp = ti.gen_linear(B, H, Tq, T, d, seed=seed, dtype=dtype, w0="normal")
     rng = np.random.default_rng(seed + 1)
-    dy = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    dy = rng.standard_normal((B, H, Tq, d)).astype(np.float32)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     if dtype == "bf16":
         dy = ti.round_bf16(dy)
@@ -36,16 +37,18 @@ def run_case(B, H, T, chunk, loss, dtype, seed, with_dwf=True, heads=None):
         g_dy = dev(dy)
     dwf = rng.standard_normal((B, H, d, d)).astype(np.float32) if with_dwf else None
     g = {n: dev(inp[n], inp.get(n + "16"), tdt) for n in ("q", "k", "v")}
-    print(f"[case] bwd B={B} H={H} T={T} b={chunk} loss={loss} {dtype} dwf={with_dwf}", flush=True)
+    print(f"[case] bwd B={B} H={H} T={T} Tq={Tq} b={chunk} loss={loss} {dtype} order={order} "
+          f"dwf={with_dwf}", flush=True)
     out = cla.ttt_linear_bwd(g["q"], g["k"], g["v"], dev(inp["eta"]), dev(inp["w0"]), g_dy,
-                             None if dwf is None else dev(dwf), chunk=chunk, loss=loss)
+                             None if dwf is None else dev(dwf), chunk=chunk, loss=loss,
+                             order=order)
     torch.cuda.synchronize()
     got = [to_np(t) for t in out]
     sl = slice(None) if heads is None else heads
     flat = lambda a: a.reshape((B * H,) + a.shape[2:])[sl][None]
     ref = oracle_bwd(flat(inp["q"]), flat(inp["k"]), flat(inp["v"]), flat(inp["eta"]),
                      flat(inp["w0"]), flat(dy), None if dwf is None else flat(dwf), chunk=chunk,
-                     loss=loss)
+                     loss=loss, order=order)
     for name, a, r in zip(("d_q", "d_k", "d_v", "d_eta", "d_w_init"), got, ref):
         a = flat(a)
         if dtype == "f32" or name in ("d_eta", "d_w_init"):
@@ -70,3 +73,15 @@ def test_bwd_headline_shape_sampled_heads():
     """B4 H8 T4096 d64 chunk 16, MSE, bf16 (the forward's headline workload
     shape), heads 0 and 31 against the oracle."""
     run_case(4, 8, 4096, 16, 1, "bf16", seed=140, heads=[0, 31])
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_noncausal(loss, chunk, dtype):
+    """Update over 200 key/value tokens, then 77 queries read the final state."""
+    run_case(1, 2, 200, chunk, loss, dtype, seed=160 + chunk + loss, order=1, Tq=77)
+
+
+def test_bwd_noncausal_many_queries_no_dwf():
+    run_case(2, 1, 50, 16, 1, "f32", seed=170, with_dwf=False, order=1, Tq=300)
