@@ -250,7 +250,7 @@ size_t ttt_linear_bwd_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int 
     if (order == TTT_CAUSAL && Tq != Tkv) return 0;
     if ((long long)B * H > (1LL << 24) || (long long)Tq > (1LL << 30) || (long long)Tkv > (1LL << 30))
         return 0;
-    if (d != 64 || (chunk != 16 && chunk != 32)) return 0;
+    if (!((d == 64 && (chunk == 16 || chunk == 32)) || (d == 128 && chunk == 16))) return 0;
     return tttk::linear_bwd_workspace(B * H, Tkv, d, chunk);
 }
 
@@ -274,7 +274,8 @@ ttt_status ttt_linear_bwd(const void *q, const void *k, const void *v, int dtype
     if (d_w_final && !aligned16(d_w_final)) return TTT_EINVAL;
     if ((long long)B * H > (1LL << 24) || (long long)Tq > (1LL << 30) || (long long)Tkv > (1LL << 30))
         return TTT_EUNSUPPORTED;
-    if (d != 64 || (chunk != 16 && chunk != 32)) return TTT_EUNSUPPORTED;
+    if (!((d == 64 && (chunk == 16 || chunk == 32)) || (d == 128 && chunk == 16)))
+        return TTT_EUNSUPPORTED;
     const size_t need = tttk::linear_bwd_workspace(B * H, Tkv, d, chunk);
     if (!workspace || !aligned16(workspace)) return TTT_EINVAL;
     if (workspace_bytes < need) return TTT_EWORKSPACE;

@@ -63,8 +63,8 @@ constexpr int CB = 16;  // state columns per workgroup in the serial passes
 // Serial passes: the operands of NB chunks at a time are loaded into registers
 // while the previous NB chunks compute out of LDS, and written to LDS once per
 // batch, so no chunk step waits for memory (a step only reads LDS and stores).
-template <int B> struct Batch {
-    static constexpr int NB = B <= 16 ? 8 : 4;
+template <int D, int B> struct Batch {
+    static constexpr int NB = (B <= 16 ? 8 : 4) * 64 / D;  // LDS: two batches of K and V / R_c
 };
 
 // Serial pass 1 (one workgroup per (head, 16 state columns); columns of the
@@ -73,7 +73,7 @@ template <int B> struct Batch {
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 {
-    constexpr int NB = Batch<B>::NB, NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
+    constexpr int NB = Batch<D, B>::NB, NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
     __shared__ float W[D][CB + 1];
     __shared__ float Ks[2][NB][B][D + 1], Us[2][NB][B][CB + 1];
     __shared__ float et[2][NB][B];
@@ -164,6 +164,7 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
     __shared__ float As[B][B + 1], dAs[B][B + 1];
     __shared__ float et[B];
     constexpr int NBD = B * D / 256;
+    constexpr int RS = 256 / D;  // row stride of one thread's outputs (rows i0 + RS r)
     const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
     const int c0 = c * B, n = min(B, p.T - c0);
@@ -185,16 +186,16 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
     if (p.loss == 1) {
         float u[NBD];
         {
-            const int i0 = tid / D, j = tid % D;  // outputs (i0 + 4 r, j)
+            const int i0 = tid / D, j = tid % D;  // outputs (i0 + RS r, j)
 #pragma unroll
             for (int r = 0; r < NBD; ++r) u[r] = 0.f;
             for (int a = 0; a < D; ++a) {
                 const float w = Wc[a][j];
 #pragma unroll
-                for (int r = 0; r < NBD; ++r) u[r] += Ks[i0 + 4 * r][a] * w;
+                for (int r = 0; r < NBD; ++r) u[r] += Ks[i0 + RS * r][a] * w;
             }
 #pragma unroll
-            for (int r = 0; r < NBD; ++r) u[r] = Us[i0 + 4 * r][j] - u[r];
+            for (int r = 0; r < NBD; ++r) u[r] = Us[i0 + RS * r][j] - u[r];
         }
         __syncthreads();
 #pragma unroll
@@ -221,11 +222,11 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
         for (int t = 0; t < B; ++t) {
             const float x = dOs[t][j];
 #pragma unroll
-            for (int r = 0; r < NBD; ++r) sv[r] += As[t][i0 + 4 * r] * x;  // A is zero for t < i
+            for (int r = 0; r < NBD; ++r) sv[r] += As[t][i0 + RS * r] * x;  // A is zero for t < i
         }
 #pragma unroll
         for (int r = 0; r < NBD; ++r) {
-            const int i = i0 + 4 * r;
+            const int i = i0 + RS * r;
             Ss[i][j] = et[i] * sv[r];
             p.st[(row0 + i) * D + j] = et[i] * sv[r];
         }
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
     __syncthreads();
     // dQ = dO Wc^T + dA K;  dK part = dA^T Q [- S~ Wc^T]
     {
-        const int i0 = tid / D, a = tid % D;  // outputs (i0 + 4 r, a)
+        const int i0 = tid / D, a = tid % D;  // outputs (i0 + RS r, a)
         float sq[NBD], sk[NBD];
 #pragma unroll
         for (int r = 0; r < NBD; ++r) sq[r] = sk[r] = 0.f;
@@ -259,21 +260,21 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
             const float w = Wc[a][j];
 #pragma unroll
             for (int r = 0; r < NBD; ++r) {
-                sq[r] += dOs[i0 + 4 * r][j] * w;
-                if (p.loss == 1) sk[r] -= Ss[i0 + 4 * r][j] * w;
+                sq[r] += dOs[i0 + RS * r][j] * w;
+                if (p.loss == 1) sk[r] -= Ss[i0 + RS * r][j] * w;
             }
         }
         for (int t = 0; t < B; ++t) {
             const float kk = Ks[t][a], qq = Qs[t][a];
 #pragma unroll
             for (int r = 0; r < NBD; ++r) {
-                sq[r] += dAs[i0 + 4 * r][t] * kk;
-                sk[r] += dAs[t][i0 + 4 * r] * qq;
+                sq[r] += dAs[i0 + RS * r][t] * kk;
+                sk[r] += dAs[t][i0 + RS * r] * qq;
             }
         }
 #pragma unroll
         for (int r = 0; r < NBD; ++r) {
-            const int i = i0 + 4 * r;
+            const int i = i0 + RS * r;
             if (i < n) stf<E>(p.dq, (tok0 + c0 + i) * D + a, sq[r]);
             p.dkl[(row0 + i) * D + a] = sk[r];
         }
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
     float *R = p.rc + cb * D * D;
     {
         constexpr int NR = D * D / 256;
-        const int a0 = tid / D, j = tid % D;  // outputs (a0 + 4 r, j)
+        const int a0 = tid / D, j = tid % D;  // outputs (a0 + RS r, j)
         float sr[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) sr[r] = 0.f;
@@ -290,12 +291,12 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
             const float x = dOs[i][j], y = Ss[i][j];
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                sr[r] += Qs[i][a0 + 4 * r] * x;
-                if (p.loss == 1) sr[r] -= Ks[i][a0 + 4 * r] * y;
+                sr[r] += Qs[i][a0 + RS * r] * x;
+                if (p.loss == 1) sr[r] -= Ks[i][a0 + RS * r] * y;
             }
         }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) R[(long)(a0 + 4 * r) * D + j] = sr[r];
+        for (int r = 0; r < NR; ++r) R[(long)(a0 + RS * r) * D + j] = sr[r];
     }
 }
 
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
 {
-    constexpr int NB = Batch<B>::NB, NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
+    constexpr int NB = Batch<D, B>::NB, NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
     __shared__ float G[D][CB + 1], KG[B][CB + 1];
     __shared__ float Rs[2][NB][D][CB + 1], Ks[2][NB][B][D + 1];
     __shared__ float et[2][NB][B];
@@ -542,19 +543,19 @@ size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
            sizeof(float);
 }
 
-template <int B, typename E>
+template <int D, int B, typename E>
 static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
-    lbw_states<64, B, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
+    lbw_states<D, B, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
     if (p.order == 0) {
-        lbw_local<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        lbw_local<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
     } else {
-        lbw_nc_g<64, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
-        if (p.Tq > 0) lbw_nc_dq<64, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
+        lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+        if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
-    lbw_grad<64, B, E><<<dim3(NH * (64 / CB)), b, 0, st>>>(p);
-    lbw_dep<64, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+    lbw_grad<D, B, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    lbw_dep<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
 }
 
 hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
@@ -570,12 +571,15 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
     LinBwdParams p{q, k, v, dout, eta, w0, dwf, dq, dk, dv, deta, dw0, base, base + dd,
                    base + 2 * dd, base + 3 * dd, base + 3 * dd + bd, base + 3 * dd + 2 * bd, Tkv,
                    nch, loss, order, Tq, tail, tail + (size_t)NH * d * d};
-    if (chunk == 16) {
-        if (bf16) lbw_run<16, __bf16>(p, NH, st);
-        else lbw_run<16, float>(p, NH, st);
+    if (d == 128) {  // chunk 16 only (LDS of the dependent pass)
+        if (bf16) lbw_run<128, 16, __bf16>(p, NH, st);
+        else lbw_run<128, 16, float>(p, NH, st);
+    } else if (chunk == 16) {
+        if (bf16) lbw_run<64, 16, __bf16>(p, NH, st);
+        else lbw_run<64, 16, float>(p, NH, st);
     } else {
-        if (bf16) lbw_run<32, __bf16>(p, NH, st);
-        else lbw_run<32, float>(p, NH, st);
+        if (bf16) lbw_run<64, 32, __bf16>(p, NH, st);
+        else lbw_run<64, 32, float>(p, NH, st);
     }
     return hipGetLastError();
 }

@@ -228,7 +228,8 @@ def lin_bwd(lib, **kw):
     (dict(dwf=FAKE + 4), _lib.TTT_EINVAL), (dict(do=None), _lib.TTT_EINVAL),
     (dict(de=None), _lib.TTT_EINVAL), (dict(dw0=FAKE + 8), _lib.TTT_EINVAL),
     (dict(ws=None), _lib.TTT_EINVAL), (dict(T=0), _lib.TTT_EINVAL), (dict(loss=3), _lib.TTT_EINVAL),
-    (dict(dtype=5), _lib.TTT_EINVAL), (dict(d=128), _lib.TTT_EUNSUPPORTED),
+    (dict(dtype=5), _lib.TTT_EINVAL), (dict(d=128), _lib.TTT_EWORKSPACE),
+    (dict(d=128, chunk=32), _lib.TTT_EUNSUPPORTED), (dict(d=96), _lib.TTT_EUNSUPPORTED),
     (dict(chunk=64), _lib.TTT_EUNSUPPORTED), (dict(chunk=8), _lib.TTT_EUNSUPPORTED),
     (dict(order=2), _lib.TTT_EINVAL), (dict(Tkv=50), _lib.TTT_EINVAL),
     (dict(order=1, Tkv=50), _lib.TTT_EWORKSPACE), (dict(order=1, Tkv=0), _lib.TTT_EINVAL),
@@ -250,4 +251,7 @@ def test_linear_bwd_workspace_query():
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 64, 32, 0, 0, 0) == 2 * per(32) + tail
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 1, 0) == 2 * per(32) + tail
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 0, 0) == 0
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 16, 0, 0, 0) == 0
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 32, 0, 0, 0) == 0
+    per128 = (3 * 128 * 128 + 3 * 16 * 128) * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 16, 0, 0, 0) == \
+        4 * per128 + 2 * 128 * 128 * 4

@@ -22,9 +22,9 @@ def _cla():
     return cla
 
 
-def run_case(B, H, T, chunk, loss, dtype, seed, with_dwf=True, heads=None, order=0, Tq=None):
+def run_case(B, H, T, chunk, loss, dtype, seed, with_dwf=True, heads=None, order=0, Tq=None,
+             d=64):
     cla = _cla()
-    d = 64
     Tq = T if Tq is None else Tq
     inp = ti.gen_linear(B, H, Tq, T, d, seed=seed, dtype=dtype, w0="normal")
     rng = np.random.default_rng(seed + 1)
@@ -85,3 +85,11 @@ def test_bwd_noncausal(loss, chunk, dtype):
 
 def test_bwd_noncausal_many_queries_no_dwf():
     run_case(2, 1, 50, 16, 1, "f32", seed=170, with_dwf=False, order=1, Tq=300)
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("order", [0, 1])
+def test_bwd_d128(loss, order):
+    """Head dim 128 (chunk 16), both orders, ragged key/value length."""
+    run_case(1, 2, 150, 16, loss, "bf16", seed=180 + loss + order, order=order,
+             Tq=150 if order == 0 else 40, d=128)
