@@ -7,7 +7,10 @@
 //     o_t = sum_{t - W < s <= t} softmax_s(scale * q_t . k_s) v_s
 // optionally added to what `out` already holds.
 //
-// One workgroup = 128 queries of one head, four waves of 32.  Key/value blocks
+// One workgroup = 128 queries of one head, eight waves of 16 (at head dim 256
+// a wave then needs about 200 registers, so two waves share each SIMD and one
+// wave's softmax and barrier latency hides behind the other's matrix work;
+// four waves of 32 need nearly 500 and run one per SIMD).  Key/value blocks
 // of 64 tokens are staged in LDS (double-buffered, the next block's global
 // loads in flight during the current block's math).  Each wave computes the
 // transposed scores S^T = K Q^T (rows = keys, columns = its queries), so the
@@ -43,8 +46,7 @@ struct WinParams {
     float scale_log2;  // scale * log2(e)
 };
 
-constexpr int WQ = 32;        // queries per wave
-constexpr int QB = 4 * WQ;    // queries per workgroup
+constexpr int QB = 128;       // queries per workgroup
 constexpr int KB = 64;        // keys per block
 
 template <int D> struct WinLds {
@@ -54,12 +56,16 @@ template <int D> struct WinLds {
     bf16 v[2][KB][VP];
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
+// NW waves per workgroup, each owning QB / NW queries (NU query tiles of 16).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void window_attn_fwd(WinParams p)
 {
+    constexpr int NT = 64 * NW;
+    constexpr int WQ = QB / NW;   // queries per wave
+    constexpr int NU = WQ / 16;   // 16-query tiles per wave
     constexpr int NKS = D / 32;   // 32-deep k steps over the head dim
     constexpr int NDT = D / 16;   // 16-row output tiles over the head dim
-    constexpr int LPT = KB * D / 8 / 256;  // 16-byte pieces per thread per operand and block
+    constexpr int LPT = KB * D / 8 / NT;  // 16-byte pieces per thread per operand and block
     __shared__ WinLds<D> L;
     const int nqb = (p.T + QB - 1) / QB;
     const int bid = xcd_block(blockIdx.x, gridDim.x);
@@ -78,22 +84,22 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
     const int nblk = (khi - kb0 + KB - 1) / KB;
 
     // Q^T fragments (B operand, column = query): 8 consecutive head-dim elements
-    bf16x8 qf[2][NKS];
+    bf16x8 qf[NU][NKS];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
         const int t = min(qw0 + 16 * u + mm, p.T - 1);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
             qf[u][ks] = __builtin_bit_cast(bf16x8, ldg16(p.q + hoff + (long)t * D + 32 * ks + 8 * g));
     }
 
-    // block loader: piece i * 256 + tid covers row piece / (D / 8), 8 columns, so
-    // each load instruction of the workgroup reads 4 KiB of consecutive rows
+    // block loader: piece i * NT + tid covers row piece / (D / 8), 8 columns, so
+    // each load instruction of the workgroup reads NT x 16 bytes of consecutive rows
     u32x4w rk[LPT], rv[LPT];
     auto issue = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            const int piece = i * 256 + tid;
+            const int piece = i * NT + tid;
             const int r = piece / (D / 8), c = (piece % (D / 8)) * 8;
             const long row = min(kb + r, p.T - 1);
             rk[i] = ldg16(K + row * D + c);
@@ -103,20 +109,22 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
     auto commit = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            const int piece = i * 256 + tid;
+            const int piece = i * NT + tid;
             const int r = piece / (D / 8), c = (piece % (D / 8)) * 8;
             sts16(&L.k[buf][r][c], rk[i]);
             sts16(&L.v[buf][r][c], rv[i]);
         }
     };
 
-    f32x4 o[NDT][2];
+    f32x4 o[NDT][NU];
+    float mrun[NU], lrun[NU];   // running max (base-2 scaled scores) and this lane's share of the sum
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int u = 0; u < NU; ++u) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) o[dt][u] = zero4();
-    float mrun[2] = {-1e30f, -1e30f};   // running max (base-2 scaled scores) per query column
-    float lrun[2] = {0.f, 0.f};         // this lane's share of the running sum
+        for (int dt = 0; dt < NDT; ++dt) o[dt][u] = zero4();
+        mrun[u] = -1e30f;
+        lrun[u] = 0.f;
+    }
 
     issue(kb0);
     commit(0);
@@ -130,11 +138,11 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
         const bool live = qw0 < p.T && kb <= qlast && kb + KB - 1 > qw0 - p.window;
         const bool full = kb + KB - 1 <= qw0 && kb > qlast - p.window && kb + KB <= p.T;
         if (live) {
-            f32x4 s[4][2];
+            f32x4 s[4][NU];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) s[kt][u] = zero4();
+                for (int u = 0; u < NU; ++u) s[kt][u] = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -142,13 +150,13 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
                     const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4w *>(
                                                                     &L.k[buf][16 * kt + mm][32 * ks + 8 * g]));
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) s[kt][u] = mfma32b(s[kt][u], a, qf[u][ks]);
+                    for (int u = 0; u < NU; ++u) s[kt][u] = mfma32b(s[kt][u], a, qf[u][ks]);
                 }
             }
             // s[kt][u][j] = score of key kb + 16 kt + 4 g + j for query qw0 + 16 u + mm
-            bf16x8 pf[2][2];
+            bf16x8 pf[2][NU];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 const int qi = qw0 + 16 * u + mm;
                 float mx = -1e30f;
 #pragma unroll
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
                     const bf16x4 x1 = lds_read_tr(&L.v[buf][32 * pp + 16 + 4 * g + (mm >> 2)][16 * dt + 4 * (mm & 3)]);
                     const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) o[dt][u] = mfma32b(o[dt][u], a, pf[pp][u]);
+                    for (int u = 0; u < NU; ++u) o[dt][u] = mfma32b(o[dt][u], a, pf[pp][u]);
                 }
             }
         }
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
 
     // finish: divide by the row sums (the four g lanes of a column hold shares)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
         float l = lrun[u];
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
@@ -231,6 +239,10 @@ __global__ __launch_bounds__(256) void window_attn_fwd(WinParams p)
 
 }  // namespace
 
+#ifndef WIN_NW
+#define WIN_NW 8  // waves per workgroup: 8 waves of 16 queries (two waves per SIMD)
+#endif
+
 hipError_t window_attn_launch(int NH, int T, int d, int window, float scale, int accumulate,
                               const void *q, const void *k, const void *v, void *out,
                               hipStream_t st)
@@ -238,11 +250,11 @@ hipError_t window_attn_launch(int NH, int T, int d, int window, float scale, int
     WinParams p{static_cast<const bf16 *>(q), static_cast<const bf16 *>(k),
                 static_cast<const bf16 *>(v), static_cast<bf16 *>(out), NH, T, window, accumulate,
                 scale * 1.4426950408889634f};
-    const dim3 grid(NH * ((T + QB - 1) / QB)), block(256);
+    const dim3 grid(NH * ((T + QB - 1) / QB));
     switch (d) {
-    case 64: window_attn_fwd<64><<<grid, block, 0, st>>>(p); break;
-    case 128: window_attn_fwd<128><<<grid, block, 0, st>>>(p); break;
-    default: window_attn_fwd<256><<<grid, block, 0, st>>>(p); break;
+    case 64: window_attn_fwd<64, WIN_NW><<<grid, dim3(64 * WIN_NW), 0, st>>>(p); break;
+    case 128: window_attn_fwd<128, WIN_NW><<<grid, dim3(64 * WIN_NW), 0, st>>>(p); break;
+    default: window_attn_fwd<256, WIN_NW><<<grid, dim3(64 * WIN_NW), 0, st>>>(p); break;
     }
     return hipGetLastError();
 }
