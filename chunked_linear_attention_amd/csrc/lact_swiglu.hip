@@ -319,18 +319,33 @@ struct FwdGradLds {
     bf16 b3[2][128][FPITCH];   // W3 rows of the slice
     bf16 b2[2][FBK][F2PITCH];  // W2 rows (k) of the slice, as stored
 };
-// After the k loop: each wave's three 64 x 64 output tiles, hidden-major, rows
-// padded to 68 (34 dwords: the 16 rows a fragment write touches and the two
-// rows of a 16-lane read fall on distinct banks)
-constexpr int FOPITCH = 64 + 4;
-union FwdGradLdsAll {
+// Waves per workgroup: 8 (4 x 2 waves of 32 tokens x 64 hidden units; 96
+// accumulator registers per wave, so two waves fit on each SIMD and one wave's
+// MFMAs cover the other's loads) or 4 (2 x 2 waves of 64 tokens x 64 hidden
+// units, one wave per SIMD; about 2% slower on the LaCT layer shapes).
+#ifndef FWD_NW
+#define FWD_NW 8
+#endif
+// After the k loop: each wave's three output tiles (its hidden units x its
+// tokens), hidden-major, rows padded by 4 (the 16 rows a fragment write
+// touches and the rows of a 16-lane read fall on distinct banks)
+template <int NW> struct FwdGradOut {
+    static constexpr int TOK = 128 / (NW / 2);  // tokens per wave
+    static constexpr int PITCH = TOK + 4;
+};
+template <int NW> union FwdGradLdsAllT {
     FwdGradLds k;
-    bf16 out[4][3][64][FOPITCH];
+    bf16 out[NW][3][64][FwdGradOut<NW>::PITCH];
 };
 
-__global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slot)
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void lact_fwdgrad(LactParams p, int c, int slot)
 {
-    __shared__ FwdGradLdsAll LA;
+    constexpr int NT = 64 * NW;
+    constexpr int MI = 4 / (NW / 4);      // 16-token m-tiles per wave (4 or 2)
+    constexpr int TOKW = 16 * MI;         // tokens per wave
+    constexpr int NI = 2 / (NW / 4);      // loader passes over the 128 tile rows (2 or 1)
+    __shared__ FwdGradLdsAllT<NW> LA;
     FwdGradLds &L = LA.k;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
@@ -355,13 +370,13 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     const bf16 *w2 = p.w2b + slot_off2(p, slot, h);
     const bool dot = (p.loss == 0);
 
-    // 128 rows x 32 columns per operand and stage: rows tid/4 and 64 + tid/4,
-    // 8 columns each.  W2: k rows tid/16 and 16 + tid/16, 8 hidden columns.
+    // 128 rows x 32 columns per operand and stage: rows tid/4 (+ 64 with four
+    // waves), 8 columns each.  W2: k rows tid/16 (+ 16), 8 hidden columns.
     const int lrow = tid >> 2, lcol = (tid & 3) * 8;
     const int orow = tid >> 4, hcol = (tid & 15) * 8;
-    float erow[2];
+    float erow[NI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int t = r0 + lrow + 64 * i;
         erow[i] = (t < clen) ? (dot ? -eh[t] : 1.f) : 0.f;
     }
@@ -370,11 +385,11 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     // basic block and interleave
     const int nst = d / FBK;
     const int ngroups = nst / FPD;
-    B8 rk[FPD][2], ry[FPD][2], r1[FPD][2], r3[FPD][2], r2[FPD][2];
+    B8 rk[FPD][NI], ry[FPD][NI], r1[FPD][NI], r3[FPD][NI], r2[FPD][NI];
     auto issue = [&](int s, int st) {
         const int kk = min(st, nst - 1) * FBK;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NI; ++i) {
             const int t = min(r0 + lrow + 64 * i, clen - 1);
             rk[s][i] = ld16(kh + (long)t * d + kk + lcol);
             ry[s][i] = ld16((dot ? vh : dyh) + (long)t * d + kk + lcol);
@@ -385,7 +400,7 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     };
     auto commit = [&](int s, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NI; ++i) {
             const int row = lrow + 64 * i;
             const bool ok = r0 + row < clen;
             st16(&L.ak[buf][row][lcol], ok ? rk[s][i] : zero16());
@@ -399,11 +414,11 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
             st16(&L.b2[buf][orow + 16 * i][hcol], r2[s][i]);
         }
     };
-    // wave (wm, wn): tokens 64 wm .. 64 wm + 63 (4 m-tiles), hidden 64 wn ..
-    // 64 wn + 63 of the slice (4 n-tiles)
-    f32x4 a1[4][4], a3[4][4], a2[4][4];
+    // wave (wm, wn): tokens TOKW wm .. TOKW wm + TOKW - 1 (MI m-tiles), hidden
+    // 64 wn .. 64 wn + 63 of the slice (4 n-tiles)
+    f32x4 a1[MI][4], a3[MI][4], a2[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) a1[i][q] = a3[i][q] = a2[i][q] = zero4();
 
@@ -420,10 +435,10 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
             // consecutive k per lane).  dY x W2: W2's fragments come from the
             // transposing read (k = 4g + j and 16 + 4g + j), and dY's use the
             // same k order.
-            bf16x8 fk[4], fy[4], f1[4], f3[4], f2[4];
+            bf16x8 fk[MI], fy[MI], f1[4], f3[4], f2[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 64 + 16 * i + mm;
+            for (int i = 0; i < MI; ++i) {
+                const int row = wm * TOKW + 16 * i + mm;
                 fk[i] = as_bf8(ld16(&L.ak[buf][row][8 * g]));
                 const bf16x4 y0 = load4<bf16>(&L.ay[buf][row][4 * g]);
                 const bf16x4 y1 = load4<bf16>(&L.ay[buf][row][16 + 4 * g]);
@@ -444,42 +459,43 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < MI; ++i) {
                     a1[i][q] = mfma32(a1[i][q], fk[i], f1[q]);
                     a3[i][q] = mfma32(a3[i][q], fk[i], f3[q]);
                     a2[i][q] = mfma32(a2[i][q], fy[i], f2[q]);
                 }
-            // schedule: the fragment reads, then the 48 MFMAs with a global
-            // load or an LDS write after every second one
-            __builtin_amdgcn_sched_group_barrier(0x100, 28, 0);
+            // schedule: the fragment reads, then the MFMAs with a global load
+            // or an LDS write after every second one
+            __builtin_amdgcn_sched_group_barrier(0x100, 3 * MI + 16, 0);
 #pragma unroll
-            for (int x = 0; x < 10; ++x) {
+            for (int x = 0; x < 5 * NI; ++x) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
 #pragma unroll
-            for (int x = 0; x < 10; ++x) {
+            for (int x = 0; x < 5 * NI; ++x) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 12 * MI - 20 * NI, 0);
             lds_barrier();
         }
     }
-    // lane: tokens 64 wm + 16 i + 4 g + (0..3), hidden 64 wn + 16 q + mm of the
-    // tile.  Rows past the chunk have K = dY = 0, so every output there is 0.
-    // The three outputs go through the wave's own LDS tiles (the k loop ended
-    // with a barrier, so the operand buffers are free) and leave as whole
-    // 128-byte rows of 64 tokens.
+    // lane: tokens TOKW wm + 16 i + 4 g + (0..3), hidden 64 wn + 16 q + mm of
+    // the tile.  Rows past the chunk have K = dY = 0, so every output there is
+    // 0.  The three outputs go through the wave's own LDS tiles (the k loop
+    // ended with a barrier, so the operand buffers are free) and leave as whole
+    // rows of the wave's tokens.
     // Inner product: G^T is written with each token's -eta folded in, so the
     // weight gradient of W2 (sum over tokens of dY^T G, dY = -eta V) reads V.
-    bf16(*st)[64][FOPITCH] = LA.out[wave];
+    constexpr int OP = FwdGradOut<NW>::PITCH;
+    bf16(*st)[64][OP] = LA.out[wave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
         f32x4 ge;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int t = r0 + wm * 64 + 16 * i + 4 * g + j;
+            const int t = r0 + wm * TOKW + 16 * i + 4 * g + j;
             ge[j] = dot ? ((t < clen) ? -eh[t] : 0.f) : 1.f;
         }
 #pragma unroll
@@ -501,16 +517,17 @@ __global__ __launch_bounds__(256) void lact_fwdgrad(LactParams p, int c, int slo
     }
     bf16 *const outs[3] = {p.gt + (long)h * p.hid * p.cpad, p.dh1t + (long)h * p.hid * p.cpad,
                            p.dh3t + (long)h * p.hid * p.cpad};
-    const int orow8 = lane >> 3, ocol = (lane & 7) * 8;
+    constexpr int LPR = TOKW / 8;             // lanes per output row (16 bytes each)
+    const int orowl = lane / LPR, ocol = (lane % LPR) * 8;
 #pragma unroll
     for (int o = 0; o < 3; ++o)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int row = 8 * r + orow8;
+        for (int r = 0; r < 64 / (64 / LPR); ++r) {
+            const int row = (64 / LPR) * r + orowl;
             const bf16x4 x0 = load4<bf16>(&st[o][row][ocol]);
             const bf16x4 x1 = load4<bf16>(&st[o][row][ocol + 4]);
             const bf16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-            st16(outs[o] + (long)(h0 + wn * 64 + row) * p.cpad + r0 + wm * 64 + ocol,
+            st16(outs[o] + (long)(h0 + wn * 64 + row) * p.cpad + r0 + wm * TOKW + ocol,
                  B8{__builtin_bit_cast(u32x4v, x)});
         }
 }
@@ -1100,7 +1117,7 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
             lact_apply2<<<dim3(s.NH * (s.d / 128) * ((clen + 127) / 128)), dim3(256), 0, st>>>(
                 p, clen, slot, 1, c);
         }
-        lact_fwdgrad<<<dim3(s.NH * (p.cpad / 128) * (s.hid / 128)), dim3(256), 0, st>>>(p, c, slot);
+        lact_fwdgrad<FWD_NW><<<dim3(s.NH * (p.cpad / 128) * (s.hid / 128)), dim3(64 * FWD_NW), 0, st>>>(p, c, slot);
         lact_wgrad<<<dim3(s.NH * p.splitk * 3 * t13), dim3(256), 0, st>>>(p, c);
         if (s.rule == 2) {
             lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst, 1);
