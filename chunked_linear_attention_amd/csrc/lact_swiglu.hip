@@ -718,6 +718,11 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot, i
 // by it.  Operands are bf16 copies of the iterate; the iterate itself and all
 // accumulations are fp32.
 // ---------------------------------------------------------------------------
+// fp32 staging of a 128 x 128 product tile in the GEMM's LDS (rows padded by
+// 4: a fragment write's 4 row groups fall 16 banks apart)
+constexpr int NSPITCH = 128 + 4;
+static_assert(sizeof(float[128][NSPITCH]) <= sizeof(GemmLds), "staged tile fits the GEMM's LDS");
+
 __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
 {
     __shared__ GemmLds L;
@@ -732,7 +737,11 @@ __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
     const bf16 *x = p.nsb + (long)(step & 1) * p.NH * 3 * n13 + ((long)h * 3 + which) * n13;
     bf16 *gr = p.gram + ((long)h * 3 + which) * d * d;
     float *dg = p.diag + ((long)h * 3 + which) * d;
+    const int m0 = tm * 128, n0 = tn * 128;
     auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+        // the tile goes through LDS (free after the k loop's last barrier) and
+        // leaves as whole rows, 16 bytes per lane
+        float(*S)[NSPITCH] = reinterpret_cast<float(*)[NSPITCH]>(&L);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -740,9 +749,19 @@ __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int m = mb + 16 * i + 4 * g + j, n = nb + 16 * q + mm;
-                    gr[(long)m * d + n] = (bf16)acc[i][q][j];
+                    S[m - m0][n - n0] = acc[i][q][j];
                     if (step == 0 && m == n) dg[m] = acc[i][q][j];
                 }
+        __syncthreads();
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = (t >> 4) + 16 * it, c = (t & 15) * 8;
+            const bf16x4 x0 = to_bf16x4(load4<float>(&S[r][c]));
+            const bf16x4 x1 = to_bf16x4(load4<float>(&S[r][c + 4]));
+            const bf16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            st16(gr + (long)(m0 + r) * d + n0 + c, B8{__builtin_bit_cast(u32x4v, x)});
+        }
     };
     const bf16 *as[1] = {x};
     if (which < 2)  // T = X [hid][d]: T^T T, both operands k-major
@@ -781,26 +800,44 @@ __global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
         b = ss > 0.f ? -0.5f * inv / ss : 0.f;
     }
     const int N = (which < 2) ? d : hid;
+    const int tm = (which < 2) ? tile / (d / 128) : tile / (hid / 128);
+    const int tn = (which < 2) ? tile % (d / 128) : tile % (hid / 128);
+    const int m0 = tm * 128, n0 = tn * 128;
     auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+        // the product tile goes through LDS (free after the k loop's last
+        // barrier); the iterate is then read and written as whole rows
+        float(*S)[NSPITCH] = reinterpret_cast<float(*)[NSPITCH]>(&L);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const long e = (long)(mb + 16 * i + 4 * g + j) * N + nb + 16 * q + mm;
-                    const float v = a * xf[e] + b * acc[i][q][j];
-                    xf[e] = v;
-                    xn[e] = (bf16)v;
-                }
+                for (int j = 0; j < 4; ++j)
+                    S[mb - m0 + 16 * i + 4 * g + j][nb - n0 + 16 * q + mm] = acc[i][q][j];
+        __syncthreads();
+        const int t = threadIdx.x;
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int r = (t >> 5) + 8 * it, c = (t & 31) * 4;
+            const long e = (long)(m0 + r) * N + n0 + c;
+            const f32x4 xo = load4<float>(xf + e);
+            const f32x4 pr = load4<float>(&S[r][c]);
+            f32x4 v;
+            bf16x4 vb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = a * xo[j] + b * pr[j];
+                vb[j] = (bf16)v[j];
+            }
+            store4<float>(xf + e, v);
+            store4<bf16>(xn + e, vb);
+        }
     };
     if (which < 2) {  // X [hid][d]: X G, G symmetric (row-major = its own transpose)
-        const int tm = tile / (d / 128), tn = tile % (d / 128);
         const bf16 *as[1] = {x};
         const bf16 *bs[1] = {gr};
         gemm_nt_tile<false, false>(L, as, d, bs, d, hid, d, d, 1, tm * 128, tn * 128, 1 << 30, epi);
     } else {          // X [d][hid]: G X, X read k-major
-        const int tm = tile / (hid / 128), tn = tile % (hid / 128);
         const bf16 *as[1] = {gr};
         const bf16 *bs[1] = {x};
         gemm_nt_tile<false, true>(L, as, d, bs, hid, d, hid, d, 1, tm * 128, tn * 128, d, epi);
