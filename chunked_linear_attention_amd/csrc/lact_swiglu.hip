@@ -737,11 +737,8 @@ __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
     const bf16 *x = p.nsb + (long)(step & 1) * p.NH * 3 * n13 + ((long)h * 3 + which) * n13;
     bf16 *gr = p.gram + ((long)h * 3 + which) * d * d;
     float *dg = p.diag + ((long)h * 3 + which) * d;
-    const int m0 = tm * 128, n0 = tn * 128;
+    // direct stores: staging this small bf16 tile through LDS measured ~1% slower
     auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
-        // the tile goes through LDS (free after the k loop's last barrier) and
-        // leaves as whole rows, 16 bytes per lane
-        float(*S)[NSPITCH] = reinterpret_cast<float(*)[NSPITCH]>(&L);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -749,19 +746,9 @@ __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int m = mb + 16 * i + 4 * g + j, n = nb + 16 * q + mm;
-                    S[m - m0][n - n0] = acc[i][q][j];
+                    gr[(long)m * d + n] = (bf16)acc[i][q][j];
                     if (step == 0 && m == n) dg[m] = acc[i][q][j];
                 }
-        __syncthreads();
-        const int t = threadIdx.x;
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = (t >> 4) + 16 * it, c = (t & 15) * 8;
-            const bf16x4 x0 = to_bf16x4(load4<float>(&S[r][c]));
-            const bf16x4 x1 = to_bf16x4(load4<float>(&S[r][c + 4]));
-            const bf16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-            st16(gr + (long)(m0 + r) * d + n0 + c, B8{__builtin_bit_cast(u32x4v, x)});
-        }
     };
     const bf16 *as[1] = {x};
     if (which < 2)  // T = X [hid][d]: T^T T, both operands k-major
