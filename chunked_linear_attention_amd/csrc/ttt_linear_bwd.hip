@@ -156,11 +156,17 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 
 // Parallel pass 2, one workgroup per (head, chunk): every term that does not
 // need G.  Writes dQ, d_eta's first part and the chunk's U, S~, dK part, R_c.
+// four consecutive floats of an LDS row (16-byte aligned)
+__device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast<const f32x4 *>(x); }
+
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
 {
     __shared__ float Wc[D][D + 1];
-    __shared__ float Qs[B][D + 1], Ks[B][D + 1], dOs[B][D + 1], Us[B][D + 1], Ss[B][D + 1];
+    // token rows padded to D + 4 floats: 16-byte aligned, so the loops below read
+    // four consecutive elements of a row (the same row for the whole wave) at once
+    constexpr int P = D + 4;
+    __shared__ __align__(16) float Qs[B][P], Ks[B][P], dOs[B][P], Us[B][P], Ss[B][P];
     __shared__ float As[B][B + 1], dAs[B][B + 1];
     __shared__ float et[B];
     constexpr int NBD = B * D / 256;
@@ -189,10 +195,17 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
             const int i0 = tid / D, j = tid % D;  // outputs (i0 + RS r, j)
 #pragma unroll
             for (int r = 0; r < NBD; ++r) u[r] = 0.f;
-            for (int a = 0; a < D; ++a) {
-                const float w = Wc[a][j];
+            #pragma unroll 2
+            for (int a = 0; a < D; a += 4) {
+                const float w0 = Wc[a][j], w1 = Wc[a + 1][j], w2 = Wc[a + 2][j], w3 = Wc[a + 3][j];
 #pragma unroll
-                for (int r = 0; r < NBD; ++r) u[r] += Ks[i0 + RS * r][a] * w;
+                for (int r = 0; r < NBD; ++r) {
+                    const f32x4 kv = lds4(&Ks[i0 + RS * r][a]);
+                    u[r] += kv[0] * w0;
+                    u[r] += kv[1] * w1;
+                    u[r] += kv[2] * w2;
+                    u[r] += kv[3] * w3;
+                }
             }
 #pragma unroll
             for (int r = 0; r < NBD; ++r) u[r] = Us[i0 + RS * r][j] - u[r];
@@ -256,12 +269,19 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
         float sq[NBD], sk[NBD];
 #pragma unroll
         for (int r = 0; r < NBD; ++r) sq[r] = sk[r] = 0.f;
-        for (int j = 0; j < D; ++j) {
-            const float w = Wc[a][j];
+        #pragma unroll 2
+        for (int j = 0; j < D; j += 4) {
+            const float w[4] = {Wc[a][j], Wc[a][j + 1], Wc[a][j + 2], Wc[a][j + 3]};
 #pragma unroll
             for (int r = 0; r < NBD; ++r) {
-                sq[r] += dOs[i0 + RS * r][j] * w;
-                if (p.loss == 1) sk[r] -= Ss[i0 + RS * r][j] * w;
+                const f32x4 ov = lds4(&dOs[i0 + RS * r][j]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) sq[r] += ov[x] * w[x];
+                if (p.loss == 1) {
+                    const f32x4 sv4 = lds4(&Ss[i0 + RS * r][j]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) sk[r] -= sv4[x] * w[x];
+                }
             }
         }
         for (int t = 0; t < B; ++t) {
@@ -283,20 +303,27 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
     float *R = p.rc + cb * D * D;
     {
         constexpr int NR = D * D / 256;
-        const int a0 = tid / D, j = tid % D;  // outputs (a0 + RS r, j)
+        const int a0 = (tid / D) * NR, j = tid % D;  // outputs (a0 + r, j)
         float sr[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) sr[r] = 0.f;
+        #pragma unroll 2
         for (int i = 0; i < B; ++i) {
             const float x = dOs[i][j], y = Ss[i][j];
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                sr[r] += Qs[i][a0 + RS * r] * x;
-                if (p.loss == 1) sr[r] -= Ks[i][a0 + RS * r] * y;
+            for (int r = 0; r < NR; r += 4) {
+                const f32x4 qv = lds4(&Qs[i][a0 + r]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sr[r + e] += qv[e] * x;
+                if (p.loss == 1) {
+                    const f32x4 kv = lds4(&Ks[i][a0 + r]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sr[r + e] -= kv[e] * y;
+                }
             }
         }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) R[(long)(a0 + RS * r) * D + j] = sr[r];
+        for (int r = 0; r < NR; ++r) R[(long)(a0 + r) * D + j] = sr[r];
     }
 }
 
