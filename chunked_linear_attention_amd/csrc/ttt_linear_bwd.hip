@@ -429,7 +429,9 @@ template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
 {
     __shared__ float Gn[D][D + 1], Wc[D][D + 1];
-    __shared__ float Ks[B][D + 1], Us[B][D + 1], KGs[B][D + 1];
+    // token rows padded to D + 4 floats (16-byte aligned: four elements per read)
+    constexpr int P = D + 4;
+    __shared__ __align__(16) float Ks[B][P], Us[B][P], KGs[B][P];
     __shared__ float et[B];
     constexpr int NBD = B * D / 256;
     const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks, tid = threadIdx.x;
@@ -465,13 +467,32 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
         for (int r = 0; r < NBD; ++r) Us[(tid + 256 * r) / D][(tid + 256 * r) % D] = u[r];
         __syncthreads();
     }
+    // thread outputs (i0 + RS r, j): the wave shares its rows, so row reads are
+    // broadcasts and each column element of G is read once for all rows
+    constexpr int RS = 256 / D;
+    const int i0 = tid / D, jl = tid % D;
+    {
+        float sg[NBD];
 #pragma unroll
-    for (int r = 0; r < NBD; ++r) {
-        const int e = tid + 256 * r, i = e / D, j = e % D;
-        float s = 0.f;
-        for (int a = 0; a < D; ++a) s += Ks[i][a] * Gn[a][j];
-        KGs[i][j] = s;
-        if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + j, (nc ? 0.f : p.st[(row0 + i) * D + j]) + et[i] * s);
+        for (int r = 0; r < NBD; ++r) sg[r] = 0.f;
+#pragma unroll 2
+        for (int a = 0; a < D; a += 4) {
+            const float g0 = Gn[a][jl], g1 = Gn[a + 1][jl], g2 = Gn[a + 2][jl], g3 = Gn[a + 3][jl];
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) {
+                const f32x4 kv = lds4(&Ks[i0 + RS * r][a]);
+                sg[r] += kv[0] * g0;
+                sg[r] += kv[1] * g1;
+                sg[r] += kv[2] * g2;
+                sg[r] += kv[3] * g3;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) {
+            const int i = i0 + RS * r;
+            KGs[i][jl] = sg[r];
+            if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + jl, (nc ? 0.f : p.st[(row0 + i) * D + jl]) + et[i] * sg[r]);
+        }
     }
     __syncthreads();
     if (tid < 64) {
@@ -482,15 +503,40 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
             if (tid == 0) p.deta[tok0 + c0 + i] = (nc ? 0.f : p.deta[tok0 + c0 + i]) + s;
         }
     }
+    {
+        const int a = jl;  // outputs (i0 + RS r, a)
+        float sk[NBD];
 #pragma unroll
-    for (int r = 0; r < NBD; ++r) {
-        const int e = tid + 256 * r, i = e / D, a = e % D;
-        float s = 0.f;
-        for (int j = 0; j < D; ++j) {
-            s += Us[i][j] * Gn[a][j];
-            if (p.loss == 1) s -= KGs[i][j] * Wc[a][j];
+        for (int r = 0; r < NBD; ++r) sk[r] = 0.f;
+#pragma unroll 2
+        for (int j = 0; j < D; j += 4) {
+            const float g[4] = {Gn[a][j], Gn[a][j + 1], Gn[a][j + 2], Gn[a][j + 3]};
+            float w[4] = {0.f, 0.f, 0.f, 0.f};
+            if (p.loss == 1) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = Wc[a][j + x];
+            }
+#pragma unroll
+            for (int r = 0; r < NBD; ++r) {
+                const f32x4 uv = lds4(&Us[i0 + RS * r][j]);
+                if (p.loss == 1) {
+                    const f32x4 kg = lds4(&KGs[i0 + RS * r][j]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        sk[r] += uv[x] * g[x];
+                        sk[r] -= kg[x] * w[x];
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) sk[r] += uv[x] * g[x];
+                }
+            }
         }
-        if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, (nc ? 0.f : p.dkl[(row0 + i) * D + a]) + et[i] * s);
+#pragma unroll
+        for (int r = 0; r < NBD; ++r) {
+            const int i = i0 + RS * r;
+            if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, (nc ? 0.f : p.dkl[(row0 + i) * D + a]) + et[i] * sk[r]);
+        }
     }
 }
 
