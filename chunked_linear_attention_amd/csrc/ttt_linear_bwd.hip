@@ -334,8 +334,13 @@ template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
 {
     constexpr int NB = Batch<D, B>::NB, NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
-    __shared__ float G[D][CB + 1], KG[B][CB + 1];
-    __shared__ float Rs[2][NB][D][CB + 1], Ks[2][NB][B][D + 1];
+    // K rows padded to D + 4 floats and (H K G) stored transposed, rows padded
+    // to B + 4: both dot products read four consecutive elements at a time
+    constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
+    __shared__ float G[D][CB + 1];
+    __shared__ __align__(16) float KGt[CB][TP];
+    __shared__ float Rs[2][NB][D][CB + 1];
+    __shared__ __align__(16) float Ks[2][NB][B][KP];
     __shared__ float et[2][NB][B];
     const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
@@ -391,25 +396,40 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
             if (c < 0) break;
             float *gdst = p.gnext + ((long)h * p.nchunks + c) * D * D;
             for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
-            const float(*Kc)[D + 1] = Ks[buf][m];
+            const float(*Kc)[KP] = Ks[buf][m];
             if (p.loss == 1) {
                 for (int e = tid; e < B * CB; e += 256) {
                     const int i = e / CB, j = e % CB;
                     float sacc = 0.f;
 #pragma unroll
-                    for (int a = 0; a < D; ++a) sacc += Kc[i][a] * G[a][j];
-                    KG[i][j] = et[buf][m][i] * sacc;
+                    for (int a = 0; a < D; a += 4) {
+                        const f32x4 kv = lds4(&Kc[i][a]);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) sacc += kv[x] * G[a + x][j];
+                    }
+                    KGt[j][i] = et[buf][m][i] * sacc;
                 }
                 lds_barrier();
             }
-            for (int e = tid; e < D * CB; e += 256) {
-                const int a = e / CB, j = e % CB;
-                float sacc = Rs[buf][m][a][j];
+            {
+                // thread elements (tid / CB + (256 / CB) r, tid % CB): one column j,
+                // so each read of (H K G)^T serves all of them
+                const int j = tid % CB, ab = tid / CB;
+                float sacc[NE];
+#pragma unroll
+                for (int r = 0; r < NE; ++r) sacc[r] = Rs[buf][m][ab + (256 / CB) * r][j];
                 if (p.loss == 1) {
 #pragma unroll
-                    for (int i = 0; i < B; ++i) sacc -= Kc[i][a] * KG[i][j];
+                    for (int i = 0; i < B; i += 4) {
+                        const f32x4 kg = lds4(&KGt[j][i]);
+#pragma unroll
+                        for (int r = 0; r < NE; ++r)
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) sacc[r] -= Kc[i + x][ab + (256 / CB) * r] * kg[x];
+                    }
                 }
-                G[a][j] += sacc;
+#pragma unroll
+                for (int r = 0; r < NE; ++r) G[ab + (256 / CB) * r][j] += sacc[r];
             }
             lds_barrier();
         }
