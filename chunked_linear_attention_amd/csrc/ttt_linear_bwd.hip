@@ -60,6 +60,9 @@ template <typename E> __device__ __forceinline__ void stf(void *p, long i, float
 
 constexpr int CB = 16;  // state columns per workgroup in the serial passes
 
+// four consecutive floats of an LDS row (16-byte aligned)
+__device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast<const f32x4 *>(x); }
+
 // Serial passes: the operands of NB chunks at a time are loaded into registers
 // while the previous NB chunks compute out of LDS, and written to LDS once per
 // batch, so no chunk step waits for memory (a step only reads LDS and stores).
@@ -74,10 +77,14 @@ template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 {
     constexpr int NB = Batch<D, B>::NB, NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
+    // K rows padded to D + 4 floats; V and U stored transposed (token index
+    // last), rows padded to B + 4: the dot products read four elements at a time
+    constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
     __shared__ float W[D][CB + 1];
-    __shared__ float Ks[2][NB][B][D + 1], Us[2][NB][B][CB + 1];
-    __shared__ float et[2][NB][B];
-    __shared__ float Ut[B][CB + 1];
+    __shared__ __align__(16) float Ks[2][NB][B][KP];
+    __shared__ __align__(16) float Vt[2][NB][CB][TP];
+    __shared__ __align__(16) float et[2][NB][B];
+    __shared__ __align__(16) float Ut[CB][TP];
     const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
     const int nbat = (p.nchunks + NB - 1) / NB;
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 #pragma unroll
             for (int r = 0; r < NK; ++r) Ks[buf][m][(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[m][r];
 #pragma unroll
-            for (int r = 0; r < NV; ++r) Us[buf][m][(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pv[m][r];
+            for (int r = 0; r < NV; ++r) Vt[buf][m][(tid + 256 * r) % CB][(tid + 256 * r) / CB] = pv[m][r];
             if (tid < B) et[buf][m][tid] = pe[m];
         }
     };
@@ -122,26 +129,42 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
             if (c >= p.nchunks) break;
             float *dst = p.states + ((long)h * p.nchunks + c) * D * D;
             for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
-            const float(*Kc)[D + 1] = Ks[buf][m];
-            const float(*Vc)[CB + 1] = Us[buf][m];
-            const float(*Uc)[CB + 1] = Vc;
+            const float(*Kc)[KP] = Ks[buf][m];
+            const float(*Vc)[TP] = Vt[buf][m];
+            const float(*Uc)[TP] = Vc;
             if (p.loss == 1) {  // U = V - K W
                 for (int e = tid; e < B * CB; e += 256) {
                     const int i = e / CB, j = e % CB;
                     float sacc = 0.f;
 #pragma unroll
-                    for (int a = 0; a < D; ++a) sacc += Kc[i][a] * W[a][j];
-                    Ut[i][j] = Vc[i][j] - sacc;
+                    for (int a = 0; a < D; a += 4) {
+                        const f32x4 kv = lds4(&Kc[i][a]);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) sacc += kv[x] * W[a + x][j];
+                    }
+                    Ut[j][i] = Vc[j][i] - sacc;
                 }
                 lds_barrier();
                 Uc = Ut;
             }
-            for (int e = tid; e < D * CB; e += 256) {
-                const int a = e / CB, j = e % CB;
-                float sacc = 0.f;
+            {
+                // thread elements (tid / CB + (256 / CB) r, tid % CB): one column j,
+                // so each read of U^T and eta serves all of them
+                const int j = tid % CB, ab = tid / CB;
+                float sacc[NE];
 #pragma unroll
-                for (int i = 0; i < B; ++i) sacc += Kc[i][a] * et[buf][m][i] * Uc[i][j];
-                W[a][j] += sacc;
+                for (int r = 0; r < NE; ++r) sacc[r] = 0.f;
+#pragma unroll
+                for (int i = 0; i < B; i += 4) {
+                    const f32x4 uv = lds4(&Uc[j][i]);
+                    const f32x4 ev = lds4(&et[buf][m][i]);
+#pragma unroll
+                    for (int r = 0; r < NE; ++r)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) sacc[r] += Kc[i + x][ab + (256 / CB) * r] * ev[x] * uv[x];
+                }
+#pragma unroll
+                for (int r = 0; r < NE; ++r) W[ab + (256 / CB) * r][j] += sacc[r];
             }
             lds_barrier();
         }
@@ -156,9 +179,6 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 
 // Parallel pass 2, one workgroup per (head, chunk): every term that does not
 // need G.  Writes dQ, d_eta's first part and the chunk's U, S~, dK part, R_c.
-// four consecutive floats of an LDS row (16-byte aligned)
-__device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast<const f32x4 *>(x); }
-
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
 {
