@@ -93,22 +93,78 @@ class Rotated:
 
 def time_calls(fn, sets, steps, warmup):
     """Warm up, then time exactly `steps` calls between two device syncs with
-    HIP events recorded on the current stream (the one the library launches on)."""
+    HIP events recorded on the current stream (the one the library launches on).
+    An event is also recorded between consecutive calls, so every call's own
+    duration is known.  Returns (mean ms per call over the bracketed region,
+    median ms per call, wall seconds of the timed region)."""
     import torch
     for i in range(warmup):
         fn(sets[i])
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(st)
+    ev[0].record(st)
     for i in range(steps):
         fn(sets[i])
-    e1.record(st)
+        ev[i + 1].record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return ev[0].elapsed_time(ev[steps]) / steps, median, wall
+
+
+# The pages' benchmark method: 10 warm-up calls, then 100 timed calls with the
+# device synchronised on both sides.  Every workload besides the headline (whose
+# step count the caller sets) is timed that way.
+EXTRA_WARMUP, EXTRA_STEPS = 10, 100
+
+
+def measured_peaks():
+    """Peaks measured in this process: HBM bandwidth of a plain 1 GiB device copy
+    (torch's copy kernel; bytes read + written over the copy's time, best of 5)
+    and the dense bf16 rate of an MFMA loop (ttt_probe_mfma_bf16: 2048
+    workgroups of four waves, four independent 32x32x16 products per wave and
+    round, best of 5)."""
+    import torch
+    import chunked_linear_attention_amd._lib as L
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    st = torch.cuda.current_stream()
+    best = None
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        dst.copy_(src)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    copy_gbs = 2 * n / (best * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 2048, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    lib = L.load()
+    best = None
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        rc = lib.ttt_probe_mfma_bf16(out.data_ptr(), blocks, iters, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"ttt_probe_mfma_bf16 failed ({rc})")
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    mfma_tflops = blocks * 4 * iters * 4 * 32768 / (best * 1e-3) / 1e12
+    return {"hbm_copy_gbs": copy_gbs, "bf16_mfma_tflops": mfma_tflops,
+            "method": "best of 6: 1 GiB device copy (read + write bytes); bf16 32x32x16 MFMA loop, "
+                      "2048 workgroups x 4 waves x 2048 rounds x 4 products"}
 
 
 # ----------------------------------------------------------------------------
@@ -152,12 +208,13 @@ def bench_linear(B, H, T, d, chunk, loss, dtype, seed, steps, warmup, inp=None, 
     def call(s):
         cla.ttt_linear_fwd(s["q"], s["k"], s["v"], s["eta"], s["w0"], chunk=chunk, loss=loss,
                            out=s["out"], w_final=s["wf"], workspace=ws)
-    ms, wall = time_calls(call, sets, steps, warmup)
+    ms, med, wall = time_calls(call, sets, steps, warmup)
     esz = 2 if dtype == "bf16" else 4
     NH = B * H
     alg_b = linear_alg_bytes(NH, T, T, d, esz)
     alg_f = linear_alg_flops(NH, T, d, chunk, loss)
-    return {"ms": ms, "wall_s": wall, "tokens_per_s": B * T / (ms * 1e-3), "alg_bytes": alg_b,
+    return {"ms": ms, "ms_median": med, "wall_s": wall, "tokens_per_s": B * T / (ms * 1e-3),
+            "alg_bytes": alg_b,
             "alg_flops": alg_f, "gbs": alg_b / (ms * 1e-3) / 1e9,
             "tflops": alg_f / (ms * 1e-3) / 1e12, "copies": sets.n}
 
@@ -209,7 +266,7 @@ def bench_lact(wl, steps, warmup, rule=None):
     class _One:
         def __getitem__(self, i):
             return None
-    ms, wall = time_calls(call, _One(), steps, warmup)
+    ms, med, wall = time_calls(call, _One(), steps, warmup)
     NH = wl.B * wl.H
     Tq = s["q"].shape[2]
     flops, byts = lact_alg(NH, Tq, wl.Tkv, wl.d, wl.hid, wl.order)
@@ -220,7 +277,8 @@ def bench_lact(wl, steps, warmup, rule=None):
             flops += NH * nchunks * 3 * rule["ns_steps"] * 4 * wl.hid * wl.d * wl.d
         name += "_" + "_".join(f"{k}{v}" for k, v in rule.items() if k != "rule") + "_" + rule["rule"]
     tok = wl.B * (wl.Tkv if wl.order == 0 else wl.Tkv + Tq)
-    return {"workload": name, "ms": ms, "tokens_per_s": tok / (ms * 1e-3),
+    return {"workload": name, "ms": ms, "ms_median": med, "steps": steps, "warmup": warmup,
+            "tokens_per_s": tok / (ms * 1e-3),
             "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "alg_flops": flops, "alg_bytes": byts}
 
@@ -267,13 +325,13 @@ def bench_linear_decode(B, H, d, loss, chunk, dtype, steps, warmup, seed=41):
         step[0] += 1
         cla.ttt_linear_decode(q, k, v, eta, s["w"], loss=loss, w_anchor=s["a"],
                               anchor_update=anchored and i % chunk == chunk - 1, out=out)
-    ms, _ = time_calls(call, sets, steps, warmup)
+    ms, med, _ = time_calls(call, sets, steps, warmup)
     esz = 2 if dtype == "bf16" else 4
     byts = linear_decode_bytes(B * H, d, esz, loss, chunk)
     name = (f"ttt_linear_decode_{'mse' if loss else 'dot'}_B{B}_H{H}_d{d}_"
             f"{'b' + str(chunk) if chunk > 1 else 'recurrent'}_{dtype}")
-    return {"workload": name, "us_per_step": ms * 1e3, "tokens_per_s": B / (ms * 1e-3),
-            "alg_bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
+    return {"workload": name, "us_per_step": ms * 1e3, "us_median": med * 1e3,
+            "tokens_per_s": B / (ms * 1e-3), "alg_bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
             "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "state_copies": sets.n}
 
 
@@ -310,7 +368,7 @@ def bench_linear_decode_graph(B, H, d, loss, chunk, replays, seed=41):
     class _One:
         def __getitem__(self, i):
             return None
-    ms, _ = time_calls(lambda _: graph.replay(), _One(), replays, 3)
+    ms, _, _ = time_calls(lambda _: graph.replay(), _One(), replays, 3)
     per = ms / chunk
     return {"workload": f"ttt_linear_decode_{'mse' if loss else 'dot'}_B{B}_H{H}_d{d}_b{chunk}_bf16_graph",
             "us_per_step": per * 1e3, "tokens_per_s": B / (per * 1e-3),
@@ -333,9 +391,10 @@ def bench_lact_decode(B, H, d, hid, steps, warmup, seed=43):
 
     def call(s):
         cla.lact_swiglu_decode(q, *s, out=out, workspace=ws)
-    ms, _ = time_calls(call, sets, steps, warmup)
+    ms, med, _ = time_calls(call, sets, steps, warmup)
     byts = B * H * (12 * d * hid + 2 * d * 2)
     return {"workload": f"lact_swiglu_decode_B{B}_H{H}_d{d}_h{hid}_bf16", "us_per_step": ms * 1e3,
+            "us_median": med * 1e3,
             "tokens_per_s": B / (ms * 1e-3), "alg_bytes": byts,
             "hbm_gbs": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "state_copies": sets.n}
@@ -378,10 +437,10 @@ def bench_window_attention(B, H, T, d, W, steps, warmup, seed=95):
         def __getitem__(self, i):
             return None
 
-    ms, _ = time_calls(lambda _: cla.window_attention_fwd(q, k, v, window=W, out=out), _One(),
-                       steps, warmup)
+    ms, med, _ = time_calls(lambda _: cla.window_attention_fwd(q, k, v, window=W, out=out), _One(),
+                            steps, warmup)
     fl = window_attn_flops(B * H, T, d, W)
-    return {"workload": f"window_attention_B{B}_H{H}_T{T}_d{d}_W{W}_bf16", "ms": ms,
+    return {"workload": f"window_attention_B{B}_H{H}_T{T}_d{d}_W{W}_bf16", "ms": ms, "ms_median": med,
             "tokens_per_s": B * T / (ms * 1e-3), "alg_flops": fl,
             "tflops": fl / (ms * 1e-3) / 1e12, "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
@@ -415,11 +474,12 @@ def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
         def __getitem__(self, i):
             return None
 
-    ms, _ = time_calls(lambda _: cla.ttt_linear_bwd(q, k, v, eta, w0, dy, chunk=chunk, loss=loss,
-                                                     workspace=ws), _One(), steps, warmup)
+    ms, med, _ = time_calls(lambda _: cla.ttt_linear_bwd(q, k, v, eta, w0, dy, chunk=chunk,
+                                                          loss=loss, workspace=ws),
+                            _One(), steps, warmup)
     fl = linear_bwd_flops(B * H, T, d, chunk, loss)
     return {"workload": f"ttt_linear_bwd_{'mse' if loss else 'dot'}_B{B}_H{H}_T{T}_d{d}_b{chunk}_bf16",
-            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "alg_flops": fl,
+            "ms": ms, "ms_median": med, "tokens_per_s": B * T / (ms * 1e-3), "alg_flops": fl,
             "tflops": fl / (ms * 1e-3) / 1e12, "fp32_frac": fl / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
 
 
@@ -436,10 +496,11 @@ def bench_lact_rules(steps, warmup):
     return out
 
 
-def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0):
+def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0, nthreads=0):
     """The oracle as it stands, on the host cores, over whole heads of the workload
-    until about `budget_s` of CPU time has been spent (at least one head)."""
-    import numpy as np
+    until about `budget_s` of wall time has been spent (at least one call).
+    nthreads = 0: every host thread (OpenMP over heads); 1: a single core, on
+    as many heads as fit the budget (one head at a time)."""
     import oracle
     B, H, T, d = inp["q"].shape
     NH = B * H
@@ -448,19 +509,45 @@ def cpu_baseline_linear(inp, chunk, loss, budget_s=10.0):
     v = inp["v"].reshape(NH, T, d)
     eta = inp["eta"].reshape(NH, T)
     w0 = inp["w0"].reshape(NH, d, d)
-    threads = oracle.max_threads()
-    # whole heads, all host threads (OpenMP over heads), repeated until about
-    # budget_s of wall time has been spent
-    heads_done, elapsed = 0, 0.0
+    threads = oracle.max_threads() if nthreads <= 0 else nthreads
+    per = NH if threads > 1 else 1   # heads per oracle call
+    heads_done, elapsed, h0 = 0, 0.0, 0
     while elapsed < budget_s:
+        sl = slice(h0, h0 + per)
         t0 = time.perf_counter()
-        oracle.ttt_linear(q[None], k[None], v[None], eta[None], w0[None], chunk=chunk, loss=loss)
+        oracle.ttt_linear(q[None, sl], k[None, sl], v[None, sl], eta[None, sl], w0[None, sl],
+                          chunk=chunk, loss=loss, nthreads=threads)
         elapsed += time.perf_counter() - t0
-        heads_done += NH
+        heads_done += per
+        h0 = (h0 + per) % NH
+    how = "OpenMP over heads" if threads > 1 else "one core"
     return {"value": heads_done * T / elapsed, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{heads_done} heads x {T} tokens of the same workload (fp64 token-by-token "
-                      f"C oracle, OpenMP over heads), {elapsed:.1f} s"}
+                      f"C oracle, {how}), {elapsed:.1f} s"}
+
+
+def cpu_baseline_lact(wl, tkv, tq, nthreads=1):
+    """The C oracle (fp64 token loop) on a bounded sample of a LaCT workload: one
+    head, the first `tkv` update tokens (whole chunks of the workload's chunk size,
+    or one chunk of all of them for the non-causal workload) and `tq` queries;
+    tokens/s counted like the GPU's (causal: B*T; non-causal: update + query tokens)."""
+    import oracle
+    import ttt_inputs as ti
+    inp = ti.gen_lact_workload(wl, Tkv=tkv, Tq=tq)
+    sub = {n: inp[n][:, :1] for n in ("q", "k", "v", "eta", "w1", "w2", "w3")}
+    chunk = wl.chunk if wl.order == 0 else tkv
+    t0 = time.perf_counter()
+    oracle.lact_swiglu(sub["q"], sub["k"], sub["v"], sub["eta"], sub["w1"], sub["w2"], sub["w3"],
+                       chunk=chunk, loss=wl.loss, order=wl.order, rownorm=wl.rownorm,
+                       nthreads=nthreads)
+    el = time.perf_counter() - t0
+    tok = tkv if wl.order == 0 else tkv + tq
+    return {"workload": wl.name, "value": tok / el, "unit": "tokens/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"1 head, {tkv} update tokens" + (f" + {tq} queries" if wl.order else "")
+                      + f" (chunk {chunk}) of the same workload, fp64 token-by-token C oracle on "
+                        f"{nthreads} core(s), {el:.1f} s"}
 
 
 def main():
@@ -531,6 +618,8 @@ def main():
                      args.warmup, inp=inp)
     src_hash = kernel_source_hash(["ttt_linear.hip", "ttt_device.h"])
     traffic = read_traffic("ttt_linear", wl.name, src_hash)
+    log("[bench] measuring the copy bandwidth and the MFMA-loop rate")
+    peaks = measured_peaks()
     line = {
         "metric": METRIC,
         "value": r["tokens_per_s"],
@@ -551,7 +640,11 @@ def main():
                      "frac": r["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "unit_of_launch": "one ttt_linear_fwd call (summary and replay kernels)",
                      "alg_bytes_per_launch": r["alg_bytes"],
-                     "kernel_source_sha256_16": src_hash},
+                     "kernel_source_sha256_16": src_hash,
+                     "ms_median": r["ms_median"],
+                     "measured_peak": peaks["hbm_copy_gbs"],
+                     "frac_of_measured_peak": r["gbs"] / peaks["hbm_copy_gbs"]},
+        "measured_peaks": peaks,
     }
     if not args.no_extras:
         curve = []
@@ -560,11 +653,12 @@ def main():
         for b in (16, 64, 256, 1024):
             w3 = ti.mse_d128(b)
             log(f"[bench] timing {w3.name}")
-            c = bench_linear(w3.B, w3.H, w3.T, w3.d, b, w3.loss, w3.dtype, 3, max(20, args.steps // 2),
-                             args.warmup, inp=inp3)
+            c = bench_linear(w3.B, w3.H, w3.T, w3.d, b, w3.loss, w3.dtype, 3, EXTRA_STEPS,
+                             EXTRA_WARMUP, inp=inp3)
             pages_r = b / (1 + 2 * b / w3.d)
             curve.append({"workload": w3.name, "chunk": b, "tokens_per_s": c["tokens_per_s"],
-                          "ms": c["ms"], "hbm_gbs": c["gbs"], "hbm_frac": c["gbs"] / HBM_PEAK_GBS,
+                          "ms": c["ms"], "ms_median": c["ms_median"], "hbm_gbs": c["gbs"],
+                          "hbm_frac": c["gbs"] / HBM_PEAK_GBS,
                           "dual_form_tflops": c["tflops"],
                           "pages_intensity_r_elements": pages_r})
         del inp3
@@ -573,23 +667,39 @@ def main():
         for lw in (ti.LACT_CAUSAL, ti.LACT_NONCAUSAL):
             try:
                 log(f"[bench] timing {lw.name}")
-                lact.append(bench_lact(lw, max(5, args.steps // 10), 2))
+                lact.append(bench_lact(lw, EXTRA_STEPS, EXTRA_WARMUP))
             except Exception as e:  # reported, never hidden
                 lact.append({"workload": lw.name, "error": str(e)})
         line["lact"] = lact
         try:
-            line["lact_rules"] = bench_lact_rules(max(5, args.steps // 10), 2)
+            line["lact_rules"] = bench_lact_rules(EXTRA_STEPS, EXTRA_WARMUP)
         except Exception as e:  # reported, never hidden
             line["lact_rules"] = [{"error": str(e)}]
-        line["decode"] = bench_decode(max(50, args.steps), args.warmup)
+        line["decode"] = bench_decode(EXTRA_STEPS, EXTRA_WARMUP)
         log("[bench] timing the TTT-Linear backward (headline shape)")
-        line["backward"] = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, max(5, args.steps // 10), 2)]
+        line["backward"] = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, EXTRA_STEPS, EXTRA_WARMUP)]
         log("[bench] timing the sliding-window attention (LaCT LM shape)")
-        line["window_attention"] = [bench_window_attention(1, 4, 32768, 256, 2048,
-                                                           max(10, args.steps // 5), 3)]
+        line["window_attention"] = [bench_window_attention(1, 4, 32768, 256, 2048, EXTRA_STEPS,
+                                                           EXTRA_WARMUP)]
+    # every fraction also against the peaks measured in this process
+    for c in line.get("chunk_curve", []):
+        c["hbm_frac_of_measured"] = c["hbm_gbs"] / peaks["hbm_copy_gbs"]
+    for key in ("lact", "lact_rules", "window_attention"):
+        for e in line.get(key, []):
+            if "tflops" in e:
+                e["mfma_frac_of_measured"] = e["tflops"] / peaks["bf16_mfma_tflops"]
+    for e in line.get("decode", []):
+        if "hbm_gbs" in e:
+            e["hbm_frac_of_measured"] = e["hbm_gbs"] / peaks["hbm_copy_gbs"]
     if not args.no_cpu:
-        log("[bench] timing the CPU oracle")
+        log("[bench] timing the CPU oracle (all host threads, then one core)")
         line["cpu_baseline"] = cpu_baseline_linear(inp, wl.chunk, wl.loss, args.cpu_budget)
+        line["cpu_baseline_single_core"] = cpu_baseline_linear(inp, wl.chunk, wl.loss,
+                                                               args.cpu_budget, nthreads=1)
+        if not args.no_extras:
+            log("[bench] timing the CPU oracle on samples of the LaCT workloads (one core)")
+            line["cpu_baseline_lact"] = [cpu_baseline_lact(ti.LACT_CAUSAL, 4096, 4096),
+                                         cpu_baseline_lact(ti.LACT_NONCAUSAL, 4096, 1024)]
     print(json.dumps(line), flush=True)
 
 

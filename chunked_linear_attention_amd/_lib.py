@@ -15,10 +15,11 @@ TTT_EWORKSPACE = -3
 TTT_EHIP = -4
 
 EXPORTS = ("ttt_status_string", "ttt_abi_version", "ttt_linear_workspace_bytes", "ttt_linear_fwd",
+           "ttt_linear_workspace_bytes_seg", "ttt_linear_fwd_seg",
            "lact_swiglu_workspace_bytes", "lact_swiglu_fwd", "ttt_linear_decode",
            "lact_swiglu_decode_workspace_bytes", "lact_swiglu_decode",
            "lact_swiglu_rule_workspace_bytes", "lact_swiglu_fwd_rule", "window_attention_fwd",
-           "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd")
+           "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd", "ttt_probe_mfma_bf16")
 
 _lock = threading.Lock()
 _lib = None
@@ -49,16 +50,20 @@ def load() -> ctypes.CDLL:
         lib.ttt_linear_workspace_bytes.restype = sz
         lib.ttt_linear_fwd.argtypes = [vp, vp, vp, i, vp, vp, vp, vp] + [i] * 8 + [vp, sz, vp]
         lib.ttt_linear_fwd.restype = i
+        lib.ttt_linear_workspace_bytes_seg.argtypes = [i] * 10
+        lib.ttt_linear_workspace_bytes_seg.restype = sz
+        lib.ttt_linear_fwd_seg.argtypes = [vp, vp, vp, i, vp, vp, vp, vp] + [i] * 9 + [vp, sz, vp]
+        lib.ttt_linear_fwd_seg.restype = i
         lib.lact_swiglu_workspace_bytes.argtypes = [i] * 10
         lib.lact_swiglu_workspace_bytes.restype = sz
         lib.lact_swiglu_fwd.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp] + [i] * 10 + \
-            [vp, sz, vp]
+            [vp, sz, vp, vp]
         lib.lact_swiglu_fwd.restype = i
         f = ctypes.c_float
         lib.lact_swiglu_rule_workspace_bytes.argtypes = [i] * 11
         lib.lact_swiglu_rule_workspace_bytes.restype = sz
         lib.lact_swiglu_fwd_rule.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp] + \
-            [i] * 11 + [f, i, f, vp, vp, vp, vp, sz, vp]
+            [i] * 11 + [f, i, f, vp, vp, vp, vp, sz, vp, vp]
         lib.lact_swiglu_fwd_rule.restype = i
         lib.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 9
         lib.ttt_linear_bwd_workspace_bytes.restype = sz
@@ -73,6 +78,8 @@ def load() -> ctypes.CDLL:
         lib.lact_swiglu_decode_workspace_bytes.restype = sz
         lib.lact_swiglu_decode.argtypes = [vp, i, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
         lib.lact_swiglu_decode.restype = i
+        lib.ttt_probe_mfma_bf16.argtypes = [vp, i, i, vp]
+        lib.ttt_probe_mfma_bf16.restype = i
         _lib = lib
         return lib
 

@@ -63,24 +63,30 @@ const char *ttt_status_string(int status)
     }
 }
 
-int ttt_abi_version(void) { return 2; }
+int ttt_abi_version(void) { return 3; }
+
+size_t ttt_linear_workspace_bytes_seg(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
+                                      int order, int dtype, int seg_tokens)
+{
+    if (!valid_enums(dtype, loss, order) || seg_tokens < 0) return 0;
+    if (check_dims(B, H, Tq, Tkv, d, chunk, order) != TTT_OK) return 0;
+    if (!linear_supported(d, chunk)) return 0;
+    tttk::LinearShape s{B * H, Tq, Tkv, d, chunk, loss, order, dtype == TTT_BF16 ? 1 : 0, seg_tokens};
+    return tttk::linear_plan(s).bytes;
+}
 
 size_t ttt_linear_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
                                   int order, int dtype)
 {
-    if (!valid_enums(dtype, loss, order)) return 0;
-    if (check_dims(B, H, Tq, Tkv, d, chunk, order) != TTT_OK) return 0;
-    if (!linear_supported(d, chunk)) return 0;
-    tttk::LinearShape s{B * H, Tq, Tkv, d, chunk, loss, order, dtype == TTT_BF16 ? 1 : 0};
-    return tttk::linear_plan(s).bytes;
+    return ttt_linear_workspace_bytes_seg(B, H, Tq, Tkv, d, chunk, loss, order, dtype, 0);
 }
 
-ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype, const float *eta,
-                          const float *w_init, void *out, float *w_final, int B, int H, int Tq,
-                          int Tkv, int d, int chunk, int loss, int order, void *workspace,
-                          size_t workspace_bytes, void *stream)
+ttt_status ttt_linear_fwd_seg(const void *q, const void *k, const void *v, int dtype,
+                              const float *eta, const float *w_init, void *out, float *w_final,
+                              int B, int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                              int seg_tokens, void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
+    if (!valid_enums(dtype, loss, order) || seg_tokens < 0) return TTT_EINVAL;
     ttt_status st = check_dims(B, H, Tq, Tkv, d, chunk, order);
     if (st != TTT_OK) return st;
     if (!w_init || !w_final || !aligned16(w_init) || !aligned16(w_final)) return TTT_EINVAL;
@@ -88,13 +94,22 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
     if (Tkv > 0 && (!k || !v || !eta || !aligned16(k) || !aligned16(v) || !aligned16(eta)))
         return TTT_EINVAL;
     if (!linear_supported(d, chunk)) return TTT_EUNSUPPORTED;
-    tttk::LinearShape s{B * H, Tq, Tkv, d, chunk, loss, order, dtype == TTT_BF16 ? 1 : 0};
+    tttk::LinearShape s{B * H, Tq, Tkv, d, chunk, loss, order, dtype == TTT_BF16 ? 1 : 0, seg_tokens};
     tttk::LinearPlan pl = tttk::linear_plan(s);
     if (pl.bytes > 0 && (!workspace || !aligned16(workspace))) return TTT_EINVAL;
     if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
     hipError_t e = tttk::linear_launch(s, pl, q, k, v, eta, w_init, out, w_final, workspace,
                                        (hipStream_t)stream);
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
+ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype, const float *eta,
+                          const float *w_init, void *out, float *w_final, int B, int H, int Tq,
+                          int Tkv, int d, int chunk, int loss, int order, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    return ttt_linear_fwd_seg(q, k, v, dtype, eta, w_init, out, w_final, B, H, Tq, Tkv, d, chunk,
+                              loss, order, 0, workspace, workspace_bytes, stream);
 }
 
 size_t lact_swiglu_rule_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden,
@@ -121,7 +136,8 @@ ttt_status lact_swiglu_fwd_rule(const void *q, const void *k, const void *v, int
                                 float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
                                 int chunk, int loss, int order, int rownorm, int rule, float beta,
                                 int ns_steps, float muon_lr, float *m1, float *m2, float *m3,
-                                void *workspace, size_t workspace_bytes, void *stream)
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                void *aux_stream)
 {
     if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
     ttt_status st = check_dims(B, H, Tq, Tkv, d, chunk, order);
@@ -157,8 +173,8 @@ ttt_status lact_swiglu_fwd_rule(const void *q, const void *k, const void *v, int
     if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
     hipError_t e = tttk::lact_launch(s, pl, q, k, v, eta, w1_init, w2_init, w3_init, out, w1_final,
                                      w2_final, w3_final, workspace, (hipStream_t)stream,
-                                     use_m ? m1 : nullptr, use_m ? m2 : nullptr,
-                                     use_m ? m3 : nullptr);
+                                     (hipStream_t)aux_stream, use_m ? m1 : nullptr,
+                                     use_m ? m2 : nullptr, use_m ? m3 : nullptr);
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 
@@ -167,12 +183,12 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
                            const float *w3_init, void *out, float *w1_final, float *w2_final,
                            float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
                            int chunk, int loss, int order, int rownorm, void *workspace,
-                           size_t workspace_bytes, void *stream)
+                           size_t workspace_bytes, void *stream, void *aux_stream)
 {
     return lact_swiglu_fwd_rule(q, k, v, dtype, eta, w1_init, w2_init, w3_init, out, w1_final,
                                 w2_final, w3_final, B, H, Tq, Tkv, d, hidden, chunk, loss, order,
                                 rownorm, TTT_RULE_GD, 0.f, 0, 0.f, nullptr, nullptr, nullptr,
-                                workspace, workspace_bytes, stream);
+                                workspace, workspace_bytes, stream, aux_stream);
 }
 
 ttt_status ttt_linear_decode(const void *q, const void *k, const void *v, int dtype,

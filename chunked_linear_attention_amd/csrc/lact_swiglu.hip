@@ -14,16 +14,21 @@
 // Non-causal: every query reads the final weights.
 //
 // Kernels (one launch each):
-//   lact_prep     K^T and (-eta V)^T for all tokens; fp32 masters; bf16
-//                 weight copies for chunk 0.
+//   lact_prep_weights  fp32 masters from the inits (where they do not alias)
+//                 and the bf16 hi/lo weight copies of the first chunk.
 //   lact_fwdgrad  per (head, 128-token tile, 128-wide hidden slice): the three
-//                 products K W1^T, K W3^T, dY W2 share the d-long contraction;
-//                 the epilogue does the SwiGLU backward and writes G^T, dH1^T,
-//                 dH3^T (hidden-major, token-contiguous: the next GEMM's k).
-//   lact_wgrad    the three weight gradients as NT GEMMs over the chunk's
-//                 tokens, split over tokens, fp32 partials.
-//   lact_update   sums the partials, GD step, row norms, fp32 masters, bf16
-//                 copies of the new weights.
+//                 products K W1^T, K W3^T, dY W2 share the d-long contraction
+//                 (K and V read token-major as stored); the epilogue does the
+//                 SwiGLU backward and writes G^T, dH1^T, dH3^T (hidden-major,
+//                 token-contiguous: the next GEMM's k).
+//   lact_wgrad    the three weight gradients as GEMMs over the chunk's tokens,
+//                 split over tokens, fp32 partials; K and V (or dY) are read
+//                 token-major as k-major operands through the transposing LDS
+//                 read.
+//   lact_update   sums the partials, takes the step (gradient descent,
+//                 momentum, or Muon's Newton-Schulz direction), row norms, fp32
+//                 masters, bf16 copies of the new weights.
+//   lact_ns_gram, lact_ns_apply  Muon's Newton-Schulz iteration.
 //   lact_apply1   G_q = silu(Q W1^T) * (Q W3^T) for every query, each with its
 //                 chunk's weights (computed transposed so G_q lands
 //                 token-major).
@@ -34,8 +39,6 @@
 // barriers.
 #include "ttt_device.h"
 #include "ttt_internal.h"
-
-#include <mutex>
 
 namespace tttk {
 
@@ -1020,39 +1023,10 @@ LactPlan lact_plan(const LactShape &s)
     return pl;
 }
 
-// A second stream per device (default priority) and two events, created on
-// first use and kept for the life of the process; the mutex is held while a
-// call enqueues its work, so calls from several host threads do not interleave
-// their event records.
-struct SideStream {
-    std::mutex mu;
-    hipStream_t s = nullptr;
-    hipEvent_t ready = nullptr, done = nullptr;
-    bool ok = false;
-};
-
-static SideStream *side_stream()
-{
-    constexpr int MAXDEV = 64;
-    static SideStream sides[MAXDEV];
-    static std::mutex init_mu;
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV) return nullptr;
-    std::lock_guard<std::mutex> lk(init_mu);
-    SideStream &ss = sides[dev];
-    if (!ss.ok) {
-        if (!ss.s && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (!ss.ready && hipEventCreateWithFlags(&ss.ready, hipEventDisableTiming) != hipSuccess) return nullptr;
-        if (!ss.done && hipEventCreateWithFlags(&ss.done, hipEventDisableTiming) != hipSuccess) return nullptr;
-        ss.ok = true;
-    }
-    return &ss;
-}
-
 hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
                        const void *v, const float *eta, const float *w1, const float *w2,
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
-                       hipStream_t st, float *m1, float *m2, float *m3)
+                       hipStream_t st, hipStream_t aux, float *m1, float *m2, float *m3)
 {
     LactParams p;
     char *base = (char *)ws;
@@ -1105,31 +1079,39 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     const int t13 = (s.d / 128) * (s.hid / 128);
     const int urows = s.NH * (2 * s.hid + s.d);
     // Causal, inner-product loss: the queries of chunk c read the weights the
-    // chunk starts with, so their two apply GEMMs run on a side stream as soon
-    // as those weights exist, beside the (latency-bound) update chain of the
-    // later chunks; the caller's stream waits for them at the end.
-    // (Not under stream capture: there every launch stays on the caller's stream.)
+    // chunk starts with, so their two apply GEMMs can run on the caller's
+    // second stream `aux` as soon as those weights exist, beside the
+    // (latency-bound) update chain of the later chunks; `st` waits for them at
+    // the end.  Two events, made for this call and released at its end, order
+    // the streams.  Without `aux`, or while `st` is being captured into a
+    // graph, every launch stays on `st` and the applies run after the chain.
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
-    SideStream *side = (s.order == 0 && s.loss == 0 && s.Tq > 0 && cap == hipStreamCaptureStatusNone)
-                           ? side_stream()
-                           : nullptr;
-    std::unique_lock<std::mutex> side_lock;
-    if (side) side_lock = std::unique_lock<std::mutex>(side->mu);
+    bool use_aux = aux && aux != st && s.order == 0 && s.loss == 0 && s.Tq > 0 &&
+                   cap == hipStreamCaptureStatusNone;
+    hipEvent_t ready = nullptr, done = nullptr;
+    if (use_aux) {
+        hipError_t e = hipEventCreateWithFlags(&ready, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (ready) (void)hipEventDestroy(ready);
+            return e;
+        }
+    }
     hipError_t serr = hipSuccess;  // first failure of an event call: the result is then invalid
     auto chk = [&](hipError_t e) {
         if (e != hipSuccess && serr == hipSuccess) serr = e;
     };
     auto apply_chunk = [&](int c) {
-        chk(hipEventRecord(side->ready, st));
-        chk(hipStreamWaitEvent(side->s, side->ready, 0));
+        chk(hipEventRecord(ready, st));
+        chk(hipStreamWaitEvent(aux, ready, 0));
         const int qlen = (c + 1) * p.chunk <= s.Tq ? p.chunk : s.Tq - c * p.chunk;
-        lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((qlen + 127) / 128)), dim3(256), 0, side->s>>>(
+        lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((qlen + 127) / 128)), dim3(256), 0, aux>>>(
             p, p.q + (long)c * p.chunk * s.d, (long)s.Tq * s.d, qlen, c);
-        lact_apply2<<<dim3(s.NH * (s.d / 128) * ((qlen + 127) / 128)), dim3(256), 0, side->s>>>(p, qlen, c, 0,
-                                                                                               c);
+        lact_apply2<<<dim3(s.NH * (s.d / 128) * ((qlen + 127) / 128)), dim3(256), 0, aux>>>(p, qlen, c, 0,
+                                                                                          c);
     };
-    if (side) apply_chunk(0);
+    if (use_aux) apply_chunk(0);
     for (int c = 0; c < pl.nchunks; ++c) {
         const int slot = (s.order == 0) ? c : 0;
         const int dst = (s.order == 0) ? c + 1 : 0;
@@ -1151,11 +1133,14 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
             }
         }
         lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst, 0);
-        if (side && (c + 1) * p.chunk < s.Tq) apply_chunk(c + 1);
+        if (use_aux && (c + 1) * p.chunk < s.Tq) apply_chunk(c + 1);
     }
-    if (side) {
-        chk(hipEventRecord(side->done, side->s));
-        chk(hipStreamWaitEvent(st, side->done, 0));
+    if (use_aux) {
+        chk(hipEventRecord(done, aux));
+        chk(hipStreamWaitEvent(st, done, 0));
+        // released once the device has passed them (the waits stay enqueued)
+        chk(hipEventDestroy(ready));
+        chk(hipEventDestroy(done));
     } else if (s.Tq > 0) {
         const int fixed = (s.order == 0) ? -1 : 0;
         lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(

@@ -16,6 +16,7 @@ struct LinearShape {
     int loss;     // 0 inner product, 1 MSE
     int order;    // 0 causal, 1 non-causal
     int bf16;     // 1 bf16 inputs/outputs, 0 fp32
+    int seg_tokens = 0;  // segment length chosen by the caller (0: the plan's own choice)
 };
 
 struct LinearPlan {
@@ -50,8 +51,8 @@ LactPlan lact_plan(const LactShape &s);
 hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, const void *k,
                        const void *v, const float *eta, const float *w1, const float *w2,
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
-                       hipStream_t stream, float *m1 = nullptr, float *m2 = nullptr,
-                       float *m3 = nullptr);
+                       hipStream_t stream, hipStream_t aux, float *m1 = nullptr,
+                       float *m2 = nullptr, float *m3 = nullptr);
 
 // ---- decode steps (one token per head) ---------------------------------------------
 hipError_t linear_decode_launch(int NH, int d, int bf16, int loss, const void *q, const void *k,

@@ -1673,13 +1673,6 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_apply(LinParams p, const fl
 // ---------------------------------------------------------------------------
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static int env_int(const char *name, int dflt)
-{
-    const char *s = getenv(name);
-    if (!s || !*s) return dflt;
-    return atoi(s);
-}
-
 LinearPlan linear_plan(const LinearShape &s)
 {
     LinearPlan pl{};
@@ -1689,13 +1682,14 @@ LinearPlan linear_plan(const LinearShape &s)
     // the segment-start chain; 256 measured best on the d = 64 and d = 128
     // workloads), at least four super-blocks: with few heads, more and
     // shorter segments would fill the chip but the chain, which grows with
-    // the number of segments, costs more than they save.
+    // the number of segments, costs more than they save.  A caller-chosen
+    // length (seg_tokens > 0) replaces that choice and is rounded up to whole
+    // periods.
     const long long period = (s.chunk <= SB) ? (long long)(SB / s.chunk) * s.chunk : s.chunk;
-    const long long target_wg = env_int("TTT_LINEAR_TARGET_WG", 256);
+    constexpr long long target_wg = 256;
     long long seg = (T > 0) ? ((long long)s.NH * T + target_wg - 1) / target_wg : period;
     if (seg < 4 * SB) seg = 4 * SB;
-    const int forced = env_int("TTT_LINEAR_SEG_TOKENS", 0);
-    if (forced > 0) seg = forced;
+    if (s.seg_tokens > 0) seg = s.seg_tokens;
     seg = (seg + period - 1) / period * period;
     if (T > 0 && seg > T) seg = (T + period - 1) / period * period;
     pl.seg_tokens = (int)seg;

@@ -28,11 +28,9 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are HIP device pointers owned by the caller.  The
  *     library never allocates device memory; scratch space is the caller's
- *     `workspace` (size from the matching *_workspace_bytes query).  The only
- *     state kept between calls is, per device, one extra stream (default
- *     priority) and two events that lact_swiglu_fwd creates on first use and
- *     keeps until the process ends (see there).  Calls on different streams
- *     with distinct workspaces and outputs may run concurrently.
+ *     `workspace` (size from the matching *_workspace_bytes query).  It keeps
+ *     no state between calls.  Calls on different streams with distinct
+ *     workspaces and outputs may run concurrently.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronising.  Buffers must stay alive
  *     until the stream has passed the call.
@@ -115,6 +113,26 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
                           int B, int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* ttt_linear_fwd with the segment length chosen by the caller.  The chunk
+ * update is affine in the state, so the library cuts the key/value sequence
+ * into segments of whole chunks, summarises each as one affine map and chains
+ * the maps ([TTT] "Mini-batch gradient descent": the per-chunk rule
+ * W <- W + K^T H (V - K W) is affine in W).  ttt_linear_fwd picks the length
+ * itself (about one workgroup per compute unit); here seg_tokens > 0 is the
+ * requested number of key tokens per segment, rounded up to whole chunks and
+ * whole 64-token blocks, and 0 means the library's own choice.  The result is
+ * the same for every length up to rounding.  seg_tokens < 0: TTT_EINVAL.  The
+ * workspace comes from ttt_linear_workspace_bytes_seg with the same
+ * seg_tokens. */
+size_t ttt_linear_workspace_bytes_seg(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
+                                      int order, int dtype, int seg_tokens);
+
+ttt_status ttt_linear_fwd_seg(const void *q, const void *k, const void *v, int dtype,
+                              const float *eta, const float *w_init, void *out, float *w_final,
+                              int B, int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                              int seg_tokens, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* ------------------------------------------------------------------------
  * LaCT SwiGLU ([LaCT] section 3.2): f(x) = W2 (silu(W1 x) * (W3 x)) per
  * (batch, head), column convention, silu(z) = z * sigmoid(z).
@@ -129,14 +147,16 @@ ttt_status ttt_linear_fwd(const void *q, const void *k, const void *v, int dtype
  * There is no intra-chunk term (causality inside a chunk belongs to the
  * window attention beside the layer, [LaCT] section 4).
  * Finals may alias the matching inits exactly.
- * Causal order with the inner-product loss: the apply of each chunk's
- * queries runs on a library-owned stream of the current device, after an
- * event recorded on `stream` once that chunk's weights are written, and
- * `stream` waits for it before the call's last operation, so on `stream`
- * the call is ordered as a whole.  While `stream` is being captured into a
- * graph, every launch stays on `stream`.  Calls that take this path enqueue
- * one at a time per device (a host-side lock) and share that stream, so
- * their applies run in call order.
+ * aux_stream (may be NULL): a second stream of the caller's on the same
+ * device.  In the causal order with the inner-product loss the apply of each
+ * chunk's queries does not lie on the chain of chunk updates, so when
+ * aux_stream is given (and differs from `stream`) those applies run on it,
+ * each after an event recorded on `stream` once its chunk's weights are
+ * written, and `stream` waits for the last of them before the call returns:
+ * on `stream` the call is still ordered as a whole.  The two events are made
+ * for the call and released at its end.  With NULL, for other orders or
+ * losses, or while `stream` is being captured into a graph, every launch stays
+ * on `stream`.  Work already queued on aux_stream runs before the applies.
  * Supported: dtype TTT_BF16; d and hidden multiples of 128, each <= 1024;
  * chunk a positive multiple of 128, or >= Tkv (one chunk of any length);
  * any loss and order.  Other shapes return TTT_EUNSUPPORTED.
@@ -149,7 +169,7 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
                            const float *w3_init, void *out, float *w1_final, float *w2_final,
                            float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
                            int chunk, int loss, int order, int rownorm, void *workspace,
-                           size_t workspace_bytes, void *stream);
+                           size_t workspace_bytes, void *stream, void *aux_stream);
 
 /* ------------------------------------------------------------------------
  * LaCT update rules ([LaCT] section 3.3 compares gradient descent, momentum
@@ -172,7 +192,8 @@ ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtyp
  * Limits: 0 <= beta <= 1; TTT_RULE_MUON takes 1 <= ns_steps <= 16 and a
  * finite muon_lr >= 0; otherwise TTT_EINVAL.  The Newton-Schulz products run
  * on bf16 matrix cores with fp32 accumulation and an fp32 iterate.  Everything
- * else is as for lact_swiglu_fwd, whose workspace query this one extends.
+ * else (aux_stream included) is as for lact_swiglu_fwd, whose workspace
+ * query this one extends.
  * ------------------------------------------------------------------------ */
 typedef enum { TTT_RULE_GD = 0, TTT_RULE_MOMENTUM = 1, TTT_RULE_MUON = 2 } ttt_rule;
 
@@ -185,7 +206,8 @@ ttt_status lact_swiglu_fwd_rule(const void *q, const void *k, const void *v, int
                                 float *w3_final, int B, int H, int Tq, int Tkv, int d, int hidden,
                                 int chunk, int loss, int order, int rownorm, int rule, float beta,
                                 int ns_steps, float muon_lr, float *m1, float *m2, float *m3,
-                                void *workspace, size_t workspace_bytes, void *stream);
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                void *aux_stream);
 
 /* ------------------------------------------------------------------------
  * Decode steps: one token per (batch, head) on a carried state.
@@ -285,6 +307,16 @@ ttt_status lact_swiglu_decode(const void *q, int dtype, const float *w1, const f
 ttt_status window_attention_fwd(const void *q, const void *k, const void *v, int dtype, void *out,
                                 int B, int H, int T, int d, int window, float scale,
                                 int accumulate, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement helper (not part of the layer): `blocks` workgroups of four
+ * waves, each wave running `iters` rounds of four independent bf16 32x32x16
+ * matrix-core products (32768 flops each), so the dense bf16 rate this part
+ * reaches is blocks * 4 * iters * 4 * 32768 flops over the launch's duration.
+ * out: device buffer of blocks * 256 floats (written with the accumulators'
+ * sums).  blocks in [1, 2^20], iters >= 1, else TTT_EINVAL.
+ * ------------------------------------------------------------------------ */
+ttt_status ttt_probe_mfma_bf16(float *out, int blocks, int iters, void *stream);
 
 #ifdef __cplusplus
 }

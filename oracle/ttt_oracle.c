@@ -155,8 +155,9 @@ int oracle_ttt_linear(const double *q, const double *k, const double *v, const d
     const int NH = B * H;
     int err = ORACLE_OK;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+    /* a thread count for this loop only (the process-wide default is left as is) */
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nth)
 #endif
     for (int h = 0; h < NH; ++h) {
         double *scratch = (double *)malloc(sizeof(double) * ((size_t)d * d + 2 * (size_t)d));
@@ -418,8 +419,9 @@ int oracle_lact_swiglu_rule(const double *q, const double *k, const double *v, c
     const size_t n13 = (size_t)hid * d, n2 = (size_t)d * hid;
     int err = ORACLE_OK;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+    /* a thread count for this loop only (the process-wide default is left as is) */
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nth)
 #endif
     for (int h = 0; h < NH; ++h) {
         const size_t big = (size_t)(hid > d ? hid : d);

@@ -4,14 +4,25 @@ the library, run the oracle on the same (rounded) values, compare.
 Tolerances (written out here, used by every test):
   fp32 path : max|gpu - oracle| / max|oracle| <= 1e-4        (normwise relative)
   bf16 path : max|gpu - oracle| <= 2e-2 * RMS(oracle)
-The same rule is applied to the state change W_final - W_init (against the
-oracle's change), so that a mis-scaled update cannot hide inside the state.
-For LaCT that change check uses 5e-2 x RMS(change) (DELTA_TOL_LACT): the
-change is a sum of products of bf16 operands (dY, G, dH, the bf16 weights) and
-its max/RMS ratio is about 5, so one bf16 rounding (relative error up to 2^-8)
-per operand already reaches ~2-3% of its RMS at the largest element; a
-mis-scaled update, which this check is there to catch, is off by tens of
-percent.  W_final itself is held to the 2e-2 x RMS rule.
+for outputs and final states.  On top of that the change a call makes is
+checked against the oracle's change, so that a mis-scaled update cannot hide
+inside the state: W_final - W_init for every path, and for LaCT also
+O - f(Q; W_init) (the outputs minus those of the initial weights).
+
+LaCT change bar.  The change is small against the state (about 1-2% of the
+weights' RMS per chunk at the workloads' learning rates), and the kernels
+hand it bf16 operands (the chunk-start weights, dY, G, dH1, dH3, the
+Newton-Schulz iterate and Gram matrix), so bf16 rounding alone moves its
+largest element by 1.3-4.2% of its RMS: more than 2e-2 on some inputs, for
+any implementation that rounds at these points.  tests/lact_rounding_model.py
+computes exactly that floor on the CPU (the method with bf16 roundings at the
+kernels' operand points, fp64 elsewhere); on every case measured the GPU's
+error equals the model's to two or three digits.  So each LaCT change must
+satisfy  error <= max(2e-2, 1.5 x model error)  x RMS(oracle change), the
+model error being taken on the same inputs.  For O - f(Q; W_init) each
+element is first allowed its own bf16 output rounding (2^-8 |O|), which the
+output check already covers and which alone exceeds 2e-2 of the change's RMS
+at full size (the change is 7-11% of the outputs' RMS there).
 """
 from __future__ import annotations
 
@@ -20,7 +31,7 @@ import torch
 
 FP32_RTOL = 1e-4
 BF16_RMS_TOL = 2e-2
-DELTA_TOL_LACT = 5e-2
+FLOOR_MARGIN = 1.5     # LaCT change bar: max(BF16_RMS_TOL, FLOOR_MARGIN x rounding-model error)
 
 
 def dev(x: np.ndarray, bits: np.ndarray | None = None, dtype=torch.float32) -> torch.Tensor:
@@ -87,3 +98,40 @@ def assert_close_bf16_rounded(got: np.ndarray, ref: np.ndarray, what: str, rms_t
     assert worst <= rms_tol * s["rms_ref"], \
         f"{what}: error beyond output rounding {worst:.3e} > {rms_tol} x RMS {s['rms_ref']:.3e} ({s})"
     return s
+
+
+def lact_change_errors(got, ref, base, output: bool) -> float:
+    """max |got - ref| / RMS(ref - base); for outputs (bf16) each element first
+    loses its own rounding allowance 2^-8 |ref|."""
+    got, ref, base = (np.asarray(a, dtype=np.float64) for a in (got, ref, base))
+    drms = float(np.sqrt(np.mean((ref - base) ** 2)))
+    d = np.abs(got - ref)
+    if output:
+        d = d - np.abs(ref) * 2.0 ** -8
+    return float(np.max(d)) / drms if drms > 0 else float(np.max(d))
+
+
+def assert_lact_change(got, ref, model, base, what: str, output: bool = False):
+    """The change check of a LaCT result (see the module docstring).  ``model``
+    is the rounding model's result for the same inputs."""
+    err = lact_change_errors(got, ref, base, output)
+    floor = lact_change_errors(model, ref, base, output)
+    bar = max(BF16_RMS_TOL, FLOOR_MARGIN * floor)
+    print(f"    {what}: change error {err:.4f}, rounding-model floor {floor:.4f}, bar {bar:.4f}",
+          flush=True)
+    assert err <= bar, f"{what}: change error {err:.4e} > {bar:.4e} (rounding-model floor {floor:.4e})"
+
+
+def assert_close_floor(got, ref, model, what: str):
+    """2e-2 x RMS like assert_close, unless the rounding model's own error on the
+    same inputs exceeds it: then 1.5 x that error.  For LaCT momentum buffers,
+    which hold sums of gradients formed from bf16 operands (their value, not
+    only their change, sits at the floor the module docstring describes)."""
+    got, ref, model = (np.asarray(a, dtype=np.float64) for a in (got, ref, model))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = float(np.max(np.abs(got - ref))) / rms
+    floor = float(np.max(np.abs(model - ref))) / rms
+    bar = max(BF16_RMS_TOL, FLOOR_MARGIN * floor)
+    print(f"    {what}: error {err:.4f}, rounding-model floor {floor:.4f}, bar {bar:.4f}", flush=True)
+    assert err <= bar, f"{what}: error {err:.4e} > {bar:.4e} x RMS (rounding-model floor {floor:.4e})"

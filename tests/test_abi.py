@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_lib.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ttt_abi_version() == 2
+    assert lib.ttt_abi_version() == 3
 
 
 def test_status_strings():
@@ -75,12 +75,12 @@ def test_linear_workspace_query():
 def lact(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, out=FAKE,
              f1=FAKE, f2=FAKE, f3=FAKE, B=1, H=1, Tq=512, Tkv=512, d=128, hid=256, chunk=128, loss=0,
-             order=0, rownorm=1, ws=FAKE, wsb=1 << 40, stream=None)
+             order=0, rownorm=1, ws=FAKE, wsb=1 << 40, stream=None, aux=None)
     a.update(kw)
     return lib.lact_swiglu_fwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w1"], a["w2"],
                                a["w3"], a["out"], a["f1"], a["f2"], a["f3"], a["B"], a["H"],
                                a["Tq"], a["Tkv"], a["d"], a["hid"], a["chunk"], a["loss"],
-                               a["order"], a["rownorm"], a["ws"], a["wsb"], a["stream"])
+                               a["order"], a["rownorm"], a["ws"], a["wsb"], a["stream"], a["aux"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -90,6 +90,8 @@ def lact(lib, **kw):
     (dict(order=1, Tq=100, chunk=200), _lib.TTT_EUNSUPPORTED),
     (dict(d=64), _lib.TTT_EUNSUPPORTED), (dict(hid=2048), _lib.TTT_EUNSUPPORTED),
     (dict(chunk=64), _lib.TTT_EUNSUPPORTED), (dict(wsb=0), _lib.TTT_EWORKSPACE),
+    # a second stream changes nothing about validation
+    (dict(wsb=0, aux=FAKE), _lib.TTT_EWORKSPACE), (dict(w1=None, aux=FAKE), _lib.TTT_EINVAL),
 ])
 def test_lact_validation(kw, code):
     assert lact(_lib.load(), **kw) == code
@@ -147,13 +149,14 @@ def lact_rule(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, out=FAKE,
              f1=FAKE, f2=FAKE, f3=FAKE, B=1, H=1, Tq=512, Tkv=512, d=128, hid=256, chunk=128, loss=0,
              order=0, rownorm=1, rule=1, beta=0.9, ns=5, lr=0.02, m1=FAKE, m2=FAKE, m3=FAKE, ws=FAKE,
-             wsb=0, stream=None)
+             wsb=0, stream=None, aux=None)
     a.update(kw)
     return lib.lact_swiglu_fwd_rule(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w1"], a["w2"],
                                     a["w3"], a["out"], a["f1"], a["f2"], a["f3"], a["B"], a["H"],
                                     a["Tq"], a["Tkv"], a["d"], a["hid"], a["chunk"], a["loss"],
                                     a["order"], a["rownorm"], a["rule"], a["beta"], a["ns"], a["lr"],
-                                    a["m1"], a["m2"], a["m3"], a["ws"], a["wsb"], a["stream"])
+                                    a["m1"], a["m2"], a["m3"], a["ws"], a["wsb"], a["stream"],
+                                    a["aux"])
 
 
 # every case fails validation before a launch (wsb = 0 ends the valid ones with EWORKSPACE)
@@ -255,3 +258,18 @@ def test_linear_bwd_workspace_query():
     per128 = (3 * 128 * 128 + 3 * 16 * 128) * 4
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 16, 0, 0, 0) == \
         4 * per128 + 2 * 128 * 128 * 4
+
+
+def test_linear_segment_length_argument():
+    """ttt_linear_fwd_seg: a negative length is rejected before any launch; the
+    workspace query follows the requested length (fewer, longer segments need
+    fewer summaries), and 0 is the library's own choice."""
+    lib = _lib.load()
+    a = (FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1, 1, 4096, 4096, 64, 16, 1, 0)
+    assert lib.ttt_linear_fwd_seg(*a, -1, FAKE, 1 << 40, None) == _lib.TTT_EINVAL
+    assert lib.ttt_linear_fwd_seg(*a, 256, FAKE, 16, None) == _lib.TTT_EWORKSPACE
+    q = lambda seg: lib.ttt_linear_workspace_bytes_seg(4, 8, 4096, 4096, 64, 16, 1, 0, 1, seg)
+    assert q(0) == lib.ttt_linear_workspace_bytes(4, 8, 4096, 4096, 64, 16, 1, 0, 1)
+    assert q(-5) == 0
+    assert q(2048) < q(256) < q(64)
+    assert q(4096) == 0   # one segment per head: no summaries

@@ -2,8 +2,9 @@
 against the fp64 oracle on the same seeded inputs.
 
 Tolerances are those of the gradient-descent path (tests/parity.py): outputs
-and final weights within 2e-2 x RMS, the weight change and the momentum
-buffers (sums of bf16-operand gradients) within 5e-2 x RMS.
+and final weights within 2e-2 x RMS; the changes W_final - W_init,
+O - f(Q; W_init) and M_final - M_init (momentum buffers) against the
+oracle's, with the bar the bf16 rounding model sets on the same inputs.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,9 @@ import torch
 import oracle
 import ttt_inputs as ti
 from oracle import dense
-from tests.parity import DELTA_TOL_LACT, assert_close, inputs_to_device, to_np
+from tests.lact_rounding_model import lact_head_bf16_model
+from tests.parity import (assert_close, assert_close_floor, assert_lact_change,
+                          inputs_to_device, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,16 +39,21 @@ def run(inp, m0, *, chunk, loss, order, rule, beta, ns_steps, lr, rownorm=1):
     return [to_np(t) for t in (out, f1, f2, f3)], (None if mom is None else [to_np(t) for t in mom])
 
 
-def check(gpu, gm, ref, rm, w0, what=""):
+def check_head(gpu, gm, ref, rm, model, mm, w0, m0, q, what=""):
+    """One (batch, head).  gpu/ref/model: (out, w1, w2, w3); gm/rm/mm: the momentum
+    buffers after the call (or None); w0/m0 their initial values; q the queries."""
     out, f1, f2, f3 = gpu
     ro, r1, r2, r3 = ref
     assert_close(out, ro, "bf16", what + "out")
-    for n, a, b, w in (("w1", f1, r1, w0[0]), ("w2", f2, r2, w0[1]), ("w3", f3, r3, w0[2])):
+    base = dense.swiglu_apply(np.asarray(q, np.float64), *(np.asarray(w, np.float64) for w in w0))
+    assert_lact_change(out, ro, model[0], base, what + "out - f(Q; W_init)", output=True)
+    for i, (n, a, b) in enumerate((("w1", f1, r1), ("w2", f2, r2), ("w3", f3, r3))):
         assert_close(a, b, "bf16", what + n)
-        assert_close(a - w, b - w, "bf16", what + n + " - init", rms_tol=DELTA_TOL_LACT)
+        assert_lact_change(a, b, model[i + 1], w0[i], what + n + " - init")
     if gm is not None:
-        for n, a, b in zip(("m1", "m2", "m3"), gm, rm):
-            assert_close(a, b, "bf16", what + n, rms_tol=DELTA_TOL_LACT)
+        for i, (n, a, b) in enumerate(zip(("m1", "m2", "m3"), gm, rm)):
+            assert_close_floor(a, b, mm[i], what + n)
+            assert_lact_change(a, b, mm[i], m0[i], what + n + " - init")
 
 
 def case(rule, beta, loss, order, *, B=1, H=2, Tq=512, Tkv=512, d=128, hid=256, chunk=128,
@@ -65,7 +73,18 @@ def case(rule, beta, loss, order, *, B=1, H=2, Tq=512, Tkv=512, d=128, hid=256, 
         inp["q"], inp["k"], inp["v"], inp["eta"], *w0, chunk=chunk, loss=loss, order=order,
         rownorm=rownorm, rule=RULES[rule], beta=beta, ns_steps=ns_steps, lr=lr,
         m=None if m0 is None else [a.astype(np.float32) for a in m0])
-    check(gpu, gm, (ro, r1, r2, r3), rm if uses_m else None, w0)
+    for b in range(B):
+        for h in range(H):
+            sub = [inp[n][b, h] for n in ("q", "k", "v", "eta", "w1", "w2", "w3")]
+            mh0 = None if m0 is None else [a[b, h].astype(np.float32) for a in m0]
+            mm = None if m0 is None else [a.copy() for a in mh0]
+            model = lact_head_bf16_model(*sub, chunk=chunk, loss=loss, order=order,
+                                         rownorm=rownorm, rule=RULES[rule], beta=beta,
+                                         ns_steps=ns_steps, lr=lr, m=mm)
+            check_head([a[b, h] for a in gpu], None if gm is None else [a[b, h] for a in gm],
+                       [a[b, h] for a in (ro, r1, r2, r3)],
+                       None if rm is None else [a[b, h] for a in rm], model, mm, sub[4:],
+                       mh0, sub[0], f"[{b},{h}] ")
 
 
 @pytest.mark.parametrize("loss", [0, 1])
@@ -137,7 +156,7 @@ def test_gd_rule_equals_plain_entry_point():
 
 def test_workload_lact_causal_full_size_muon():
     """The causal LM workload (H4 T32768 d256 h512 b2048) under Muon with
-    momentum 0.9, 5 Newton-Schulz steps: heads 0 and 2 against the oracle's
+    momentum 0.9, 5 Newton-Schulz steps: every head against the oracle's
     chunk-matmul form; row norms of the final weights equal the initial ones."""
     wl = ti.LACT_CAUSAL
     inp = ti.gen_lact_workload(wl)
@@ -149,15 +168,15 @@ def test_workload_lact_causal_full_size_muon():
     for a, w0 in ((f1, inp["w1"]), (f2, inp["w2"]), (f3, inp["w3"])):
         na, n0 = np.linalg.norm(a, axis=-1), np.linalg.norm(w0.astype(np.float64), axis=-1)
         assert np.max(np.abs(na - n0) / n0) < 1e-4
-    for hh in (0, 2):
+    for hh in (0, 1, 2, 3):
         print(f"[oracle] {wl.name} muon head {hh}", flush=True)
-        mm = [np.zeros_like(inp[n][0, hh], dtype=np.float64) for n in ("w1", "w2", "w3")]
-        ro, r1, r2, r3 = dense.lact_head(inp["q"][0, hh], inp["k"][0, hh], inp["v"][0, hh],
-                                         inp["eta"][0, hh], inp["w1"][0, hh], inp["w2"][0, hh],
-                                         inp["w3"][0, hh], chunk=wl.chunk, loss=wl.loss,
-                                         order=wl.order, rownorm=wl.rownorm, rule=2,
-                                         beta=kw["beta"], ns_steps=kw["ns_steps"], lr=kw["lr"],
-                                         m=mm)
-        w0 = [inp[n][0, hh] for n in ("w1", "w2", "w3")]
-        check((out[0, hh], f1[0, hh], f2[0, hh], f3[0, hh]), [a[0, hh] for a in gm],
-              (ro, r1, r2, r3), mm, w0, f"head {hh} ")
+        sub = [inp[n][0, hh] for n in ("q", "k", "v", "eta", "w1", "w2", "w3")]
+        kw2 = dict(chunk=wl.chunk, loss=wl.loss, order=wl.order, rownorm=wl.rownorm, rule=2,
+                   beta=kw["beta"], ns_steps=kw["ns_steps"], lr=kw["lr"])
+        rmh = [np.zeros_like(a, dtype=np.float64) for a in sub[4:]]
+        ref = dense.lact_head(*sub, m=rmh, **kw2)
+        mmh = [np.zeros(a.shape, np.float32) for a in sub[4:]]
+        model = lact_head_bf16_model(*sub, m=mmh, **kw2)
+        check_head((out[0, hh], f1[0, hh], f2[0, hh], f3[0, hh]), [a[0, hh] for a in gm], ref,
+                   rmh, model, mmh, sub[4:], [np.zeros_like(a) for a in sub[4:]], sub[0],
+                   f"head {hh} ")

@@ -4,8 +4,6 @@ Shapes span several 16-token sub-blocks, several chunks and several segments
 plus ragged tails; the full-size workloads are checked on all heads (d = 64)
 or on sampled heads (d = 128, every chunk size of the sweep).
 """
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -29,21 +27,11 @@ def run_case(B, H, T, d, chunk, loss, dtype, order=0, Tq=None, seed=0, seg_token
     inp = ti.gen_linear(B, H, Tq, T, d, seed=seed, dtype=dtype, qk_dist=qk_dist, v_dist=v_dist,
                         w0=w0, eta_scale=eta_scale)
     g = inputs_to_device(inp, dtype)
-    old = os.environ.get("TTT_LINEAR_SEG_TOKENS")
-    if seg_tokens is not None:
-        os.environ["TTT_LINEAR_SEG_TOKENS"] = str(seg_tokens)
-    try:
-        print(f"[case] B={B} H={H} T={T} Tq={Tq} d={d} b={chunk} loss={loss} {dtype} "
-              f"order={order} seg={seg_tokens}", flush=True)
-        out, wf = cla.ttt_linear_fwd(g["q"], g["k"], g["v"], g["eta"], g["w0"], chunk=chunk,
-                                     loss=loss, order=order)
-        torch.cuda.synchronize()
-    finally:
-        if seg_tokens is not None:
-            if old is None:
-                del os.environ["TTT_LINEAR_SEG_TOKENS"]
-            else:
-                os.environ["TTT_LINEAR_SEG_TOKENS"] = old
+    print(f"[case] B={B} H={H} T={T} Tq={Tq} d={d} b={chunk} loss={loss} {dtype} "
+          f"order={order} seg={seg_tokens}", flush=True)
+    out, wf = cla.ttt_linear_fwd(g["q"], g["k"], g["v"], g["eta"], g["w0"], chunk=chunk,
+                                 loss=loss, order=order, seg_tokens=seg_tokens or 0)
+    torch.cuda.synchronize()
     out, wf = to_np(out), to_np(wf)
     sl = slice(None) if heads is None else heads
     q = inp["q"].reshape(B * H, Tq, d)[sl][None]
