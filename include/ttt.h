@@ -309,6 +309,30 @@ ttt_status window_attention_fwd(const void *q, const void *k, const void *v, int
                                 int accumulate, void *stream);
 
 /* ------------------------------------------------------------------------
+ * ttt_linear_fwd for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, kernels and results as ttt_linear_fwd, minus
+ * the workspace: the scratch the state scan needs (segment summaries, and a
+ * copy of w_init for in-place calls) lives in one static device array per
+ * GPU of ttt_linear_noalloc_max_scratch_bytes() bytes (64 MiB), held from the
+ * first call on that GPU until the process ends.  No allocation is made by
+ * the call.  A problem whose scratch (ttt_linear_workspace_bytes) exceeds the
+ * array returns TTT_EWORKSPACE before anything is enqueued; with the
+ * library's own segment length every causal call fits, and an
+ * update-then-apply call fits while heads * d * d * (2 or 4 + 4) bytes does.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, not ordered with each other) race on it and must not
+ * be issued.  Nothing needs clearing between calls (each call writes all the
+ * scratch it reads).
+ * ------------------------------------------------------------------------ */
+size_t ttt_linear_noalloc_max_scratch_bytes(void);
+
+ttt_status ttt_linear_fwd_noalloc(const void *q, const void *k, const void *v, int dtype,
+                                  const float *eta, const float *w_init, void *out,
+                                  float *w_final, int B, int H, int Tq, int Tkv, int d, int chunk,
+                                  int loss, int order, void *stream);
+
+/* ------------------------------------------------------------------------
  * Measurement helper (not part of the layer): `blocks` workgroups of four
  * waves, each wave running `iters` rounds of four independent bf16 32x32x16
  * matrix-core products (32768 flops each), so the dense bf16 rate this part
