@@ -483,6 +483,55 @@ def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
             "tflops": fl / (ms * 1e-3) / 1e12, "fp32_frac": fl / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}
 
 
+def lact_bwd_flops(NH, Tq, Tkv, d, hid):
+    """Dense products of the LaCT backward, one per product (the bf16 hi/lo
+    pairs multiply the executed count by about 2.5): per key token the replayed
+    chunk gradient 12 d hid and the chunk gradient's reverse 30 d hid (H1, H3,
+    dG and the three adjoint products over d; three weight adjoints over
+    tokens; the key and value adjoints over hidden); per query token the
+    apply's reverse 16 d hid."""
+    return NH * (Tkv * 42 * d * hid + Tq * 16 * d * hid)
+
+
+def bench_lact_bwd(wl, steps, warmup, seed=4004):
+    """lact_swiglu_bwd on a LaCT workload (upstream gradients of the outputs and
+    of the final weights)."""
+    import numpy as np
+    import torch
+    import chunked_linear_attention_amd as cla
+    import ttt_inputs as ti
+    inp = ti.gen_lact_workload(wl)
+    up = lambda a: torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    s = {n: up(inp[n + "16"]) for n in ("q", "k", "v")}
+    for n in ("eta", "w1", "w2", "w3"):
+        s[n] = torch.from_numpy(inp[n]).cuda()
+    rng = np.random.default_rng(seed)
+    do = up(ti.f32_to_bf16_bits(rng.standard_normal(inp["q"].shape).astype(np.float32)))
+    dw = [torch.from_numpy((0.1 * rng.standard_normal(inp[n].shape)).astype(np.float32)).cuda()
+          for n in ("w1", "w2", "w3")]
+    Tq = s["q"].shape[2]
+    nb = cla.load_library().lact_swiglu_bwd_workspace_bytes(wl.B, wl.H, Tq, wl.Tkv, wl.d, wl.hid,
+                                                        wl.chunk, wl.loss, wl.order, 1)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    class _One:
+        def __getitem__(self, i):
+            return None
+
+    ms, med, _ = time_calls(lambda _: cla.lact_swiglu_bwd(s["q"], s["k"], s["v"], s["eta"], s["w1"],
+                                                          s["w2"], s["w3"], do, dw, chunk=wl.chunk,
+                                                          order=wl.order, rownorm=bool(wl.rownorm),
+                                                          workspace=ws),
+                            _One(), steps, warmup)
+    NH = wl.B * wl.H
+    fl = lact_bwd_flops(NH, Tq, wl.Tkv, wl.d, wl.hid)
+    tok = wl.B * (wl.Tkv if wl.order == 0 else wl.Tkv + Tq)
+    return {"workload": wl.name + "_bwd", "ms": ms, "ms_median": med, "steps": steps,
+            "warmup": warmup, "tokens_per_s": tok / (ms * 1e-3), "alg_flops": fl,
+            "tflops": fl / (ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 LACT_RULES = ({"rule": "momentum", "beta": 0.9},
               {"rule": "muon", "beta": 0.9, "ns_steps": 5, "muon_lr": 0.02})
 
@@ -598,7 +647,9 @@ def main():
 
     if args.bwd_only:
         print(json.dumps({"backward": [bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps,
-                                                        args.warmup)]}), flush=True)
+                                                        args.warmup),
+                                       bench_lact_bwd(ti.LACT_CAUSAL, args.steps, args.warmup)]}),
+              flush=True)
         return
     if args.window_only:
         print(json.dumps({"window_attention": [bench_window_attention(1, 4, 32768, 256, 2048,
@@ -678,13 +729,18 @@ def main():
         line["decode"] = bench_decode(EXTRA_STEPS, EXTRA_WARMUP)
         log("[bench] timing the TTT-Linear backward (headline shape)")
         line["backward"] = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, EXTRA_STEPS, EXTRA_WARMUP)]
+        log("[bench] timing the LaCT backward (causal LM workload)")
+        try:
+            line["backward"].append(bench_lact_bwd(ti.LACT_CAUSAL, 20, 3))
+        except Exception as e:  # reported, never hidden
+            line["backward"].append({"workload": ti.LACT_CAUSAL.name + "_bwd", "error": str(e)})
         log("[bench] timing the sliding-window attention (LaCT LM shape)")
         line["window_attention"] = [bench_window_attention(1, 4, 32768, 256, 2048, EXTRA_STEPS,
                                                            EXTRA_WARMUP)]
     # every fraction also against the peaks measured in this process
     for c in line.get("chunk_curve", []):
         c["hbm_frac_of_measured"] = c["hbm_gbs"] / peaks["hbm_copy_gbs"]
-    for key in ("lact", "lact_rules", "window_attention"):
+    for key in ("lact", "lact_rules", "window_attention", "backward"):
         for e in line.get(key, []):
             if "tflops" in e:
                 e["mfma_frac_of_measured"] = e["tflops"] / peaks["bf16_mfma_tflops"]

@@ -20,7 +20,8 @@ EXPORTS = ("ttt_status_string", "ttt_abi_version", "ttt_linear_workspace_bytes",
            "lact_swiglu_decode_workspace_bytes", "lact_swiglu_decode",
            "lact_swiglu_rule_workspace_bytes", "lact_swiglu_fwd_rule", "window_attention_fwd",
            "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd", "ttt_probe_mfma_bf16",
-           "ttt_linear_noalloc_max_scratch_bytes", "ttt_linear_fwd_noalloc")
+           "ttt_linear_noalloc_max_scratch_bytes", "ttt_linear_fwd_noalloc",
+           "lact_swiglu_bwd_workspace_bytes", "lact_swiglu_bwd")
 
 _lock = threading.Lock()
 _lib = None
@@ -85,6 +86,10 @@ def load() -> ctypes.CDLL:
         lib.ttt_linear_noalloc_max_scratch_bytes.restype = sz
         lib.ttt_linear_fwd_noalloc.argtypes = [vp, vp, vp, i, vp, vp, vp, vp] + [i] * 8 + [vp]
         lib.ttt_linear_fwd_noalloc.restype = i
+        lib.lact_swiglu_bwd_workspace_bytes.argtypes = [i] * 10
+        lib.lact_swiglu_bwd_workspace_bytes.restype = sz
+        lib.lact_swiglu_bwd.argtypes = [vp, vp, vp, i] + [vp] * 15 + [i] * 10 + [vp, sz, vp]
+        lib.lact_swiglu_bwd.restype = i
         _lib = lib
         return lib
 

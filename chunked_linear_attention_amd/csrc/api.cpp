@@ -178,6 +178,65 @@ ttt_status lact_swiglu_fwd_rule(const void *q, const void *k, const void *v, int
     return e == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 
+size_t lact_swiglu_bwd_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden, int chunk,
+                                       int loss, int order, int dtype)
+{
+    if (!valid_enums(dtype, loss, order)) return 0;
+    if (check_dims(B, H, Tq, Tkv, d, chunk, order) != TTT_OK || hidden < 1 || Tkv < 1) return 0;
+    if (!lact_supported(dtype, d, hidden, chunk, Tkv) || loss != TTT_LOSS_DOT) return 0;
+    tttk::LactShape s{B * H, Tq, Tkv, d, hidden, chunk, loss, order, 1};
+    return tttk::lact_bwd_plan(s).bytes;
+}
+
+ttt_status lact_swiglu_bwd(const void *q, const void *k, const void *v, int dtype, const float *eta,
+                           const float *w1_init, const float *w2_init, const float *w3_init,
+                           const void *d_out, const float *d_w1_final, const float *d_w2_final,
+                           const float *d_w3_final, void *d_q, void *d_k, void *d_v, float *d_eta,
+                           float *d_w1_init, float *d_w2_init, float *d_w3_init, int B, int H,
+                           int Tq, int Tkv, int d, int hidden, int chunk, int loss, int order,
+                           int rownorm, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!valid_enums(dtype, loss, order)) return TTT_EINVAL;
+    ttt_status st = check_dims(B, H, Tq, Tkv, d, chunk, order);
+    if (st != TTT_OK) return st;
+    if (hidden < 1 || Tkv < 1 || (rownorm != 0 && rownorm != 1)) return TTT_EINVAL;
+    const void *need[10] = {k, v, eta, w1_init, w2_init, w3_init, d_k, d_v, d_eta, d_w1_init};
+    for (const void *p : need)
+        if (!p || !aligned16(p)) return TTT_EINVAL;
+    if (!d_w2_init || !d_w3_init || !aligned16(d_w2_init) || !aligned16(d_w3_init)) return TTT_EINVAL;
+    if (Tq > 0 && (!q || !d_out || !d_q || !aligned16(q) || !aligned16(d_out) || !aligned16(d_q)))
+        return TTT_EINVAL;
+    // the upstream weight gradients come as all three or none
+    const int ndw = (d_w1_final != nullptr) + (d_w2_final != nullptr) + (d_w3_final != nullptr);
+    if (ndw != 0 && ndw != 3) return TTT_EINVAL;
+    if (ndw == 3 && (!aligned16(d_w1_final) || !aligned16(d_w2_final) || !aligned16(d_w3_final)))
+        return TTT_EINVAL;
+    if (!lact_supported(dtype, d, hidden, chunk, Tkv) || loss != TTT_LOSS_DOT) return TTT_EUNSUPPORTED;
+    // outputs must not overlap the inputs or each other
+    const size_t NH = (size_t)B * H, n13 = (size_t)hidden * d;
+    const size_t tk = NH * Tkv * d * 2, tq = NH * (size_t)Tq * d * 2, te = NH * Tkv * 4, tw = NH * n13 * 4;
+    const void *outs[7] = {d_q, d_k, d_v, d_eta, d_w1_init, d_w2_init, d_w3_init};
+    const size_t osz[7] = {tq, tk, tk, te, tw, tw, tw};
+    const void *ins[11] = {q, k, v, eta, w1_init, w2_init, w3_init, d_out, d_w1_final, d_w2_final, d_w3_final};
+    const size_t isz[11] = {tq, tk, tk, te, tw, tw, tw, tq, tw, tw, tw};
+    for (int a = 0; a < 7; ++a) {
+        if (!outs[a] || osz[a] == 0) continue;
+        for (int b = 0; b < 11; ++b)
+            if (ins[b] && isz[b] && overlaps(outs[a], osz[a], ins[b], isz[b])) return TTT_EINVAL;
+        for (int b = a + 1; b < 7; ++b)
+            if (outs[b] && osz[b] && overlaps(outs[a], osz[a], outs[b], osz[b])) return TTT_EINVAL;
+    }
+    tttk::LactShape s{B * H, Tq, Tkv, d, hidden, chunk, loss, order, rownorm};
+    tttk::LactBwdPlan pl = tttk::lact_bwd_plan(s);
+    if (!workspace || !aligned16(workspace)) return TTT_EINVAL;
+    if (workspace_bytes < pl.bytes) return TTT_EWORKSPACE;
+    hipError_t e = tttk::lact_bwd_launch(s, pl, q, k, v, eta, w1_init, w2_init, w3_init, d_out,
+                                         d_w1_final, d_w2_final, d_w3_final, d_q, d_k, d_v, d_eta,
+                                         d_w1_init, d_w2_init, d_w3_init, workspace,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? TTT_OK : TTT_EHIP;
+}
+
 ttt_status lact_swiglu_fwd(const void *q, const void *k, const void *v, int dtype,
                            const float *eta, const float *w1_init, const float *w2_init,
                            const float *w3_init, void *out, float *w1_final, float *w2_final,

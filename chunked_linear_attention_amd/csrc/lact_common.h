@@ -1,0 +1,244 @@
+// Pieces shared by the LaCT SwiGLU forward (lact_swiglu.hip) and backward
+// (lact_swiglu_bwd.hip) kernels: 16-byte vector helpers, the bf16 MFMA wrapper,
+// the generic GEMM tile and the parameter block of a LaCT call.
+#pragma once
+
+#include "ttt_device.h"
+
+namespace tttk {
+
+typedef __bf16 bf16;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// 16 bytes = 8 bf16
+struct alignas(16) B8 {
+    u32x4v v;
+};
+
+__device__ __forceinline__ B8 ld16(const bf16 *p) { return B8{*reinterpret_cast<const u32x4v *>(p)}; }
+__device__ __forceinline__ void st16(bf16 *p, B8 x) { *reinterpret_cast<u32x4v *>(p) = x.v; }
+__device__ __forceinline__ B8 zero16() { return B8{u32x4v{0u, 0u, 0u, 0u}}; }
+__device__ __forceinline__ bf16x8 as_bf8(B8 x) { return __builtin_bit_cast(bf16x8, x.v); }
+
+__device__ __forceinline__ f32x4 mfma32(f32x4 acc, bf16x8 a, bf16x8 b)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+// logistic function with the hardware reciprocal (about 1 ulp; the results are
+// rounded to bf16): 1 + e^-z = inf gives 0, e^-z = 0 gives 1
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
+
+// ---------------------------------------------------------------------------
+// Generic GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16), block tile
+// 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 64, K a multiple of 64.  An
+// operand is stored either k-contiguous (row m of A at A + m * lda, 128-byte
+// rows per stage) or, with AT / BT, k-major (row k at A + k * lda, holding
+// M contiguous elements: a token-major tensor read as its transpose), whose
+// fragments come from the transposing LDS read.  Rows of A past M and rows of
+// B past N read as zero, and so do rows k >= kvalid of a k-major operand.  The
+// epilogue gets the wave's 4 x 4 accumulator tiles: tile (i, q) holds C at
+// rows mbase + 16 i + 4 g + (0..3), column nbase + 16 q + (lane & 15).
+// ---------------------------------------------------------------------------
+constexpr int GBK = 64;
+constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): 16-byte fragment reads hit distinct banks per 8 lanes
+constexpr int GTPITCH = 128 + 16;  // k-major stage rows: transposing reads of 8 rows hit distinct banks
+constexpr int GPD = 2;           // register stages in flight (even: LDS buffer = stage parity)
+
+struct GemmLds {
+    bf16 a[2][128][GPITCH];
+    bf16 b[2][128][GPITCH];
+};
+static_assert(sizeof(bf16[GBK][GTPITCH]) <= sizeof(bf16[128][GPITCH]), "k-major stage fits the buffer");
+
+// K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
+// from As[s] and B from Bs[s] (same leading dimensions).  This sums products
+// of split operands (hi and lo bf16 parts) in one accumulation.
+template <bool AT = false, bool BT = false, typename Epi>
+__device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, long lda,
+                                             const bf16 *const *Bs, long ldb, int M, int N,
+                                             int kseg, int nseg, int m0, int n0, int kvalid, Epi &&epi)
+{
+    constexpr bool TR = AT || BT;  // fragments in the transposing read's k order
+    const int K = kseg * nseg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, mm = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    // 4 pieces of 16 bytes per thread and operand.  k-contiguous: rows
+    // tid/8 + 32 i, 8 columns each.  k-major: k rows tid/16 + 16 i, 8 of the
+    // 128 row elements each.
+    int lrow[4], lcol, krow[4], kcol;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lrow[i] = (tid >> 3) + 32 * i;
+        krow[i] = (tid >> 4) + 16 * i;
+    }
+    lcol = (tid & 7) * 8;
+    kcol = (tid & 15) * 8;
+    const bool aok[4] = {m0 + lrow[0] < M, m0 + lrow[1] < M, m0 + lrow[2] < M, m0 + lrow[3] < M};
+    const bool bok[4] = {n0 + lrow[0] < N, n0 + lrow[1] < N, n0 + lrow[2] < N, n0 + lrow[3] < N};
+    const int nst = K / GBK;
+    const int ngroups = (nst + GPD - 1) / GPD;
+    B8 ra[GPD][4], rb[GPD][4];
+    auto issue = [&](int s, int st) {
+        const int kk = min(st, nst - 1) * GBK;
+        const int sg = kk / kseg, kin = kk - sg * kseg;
+        const bf16 *A = As[sg], *B = Bs[sg];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (AT)
+                ra[s][i] = ld16(A + (long)min(kin + krow[i], kvalid - 1) * lda + m0 + kcol);
+            else
+                ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
+            if constexpr (BT)
+                rb[s][i] = ld16(B + (long)min(kin + krow[i], kvalid - 1) * ldb + n0 + kcol);
+            else
+                rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
+        }
+    };
+    // Past the last k step the stage holds zeros, so every step computes (the
+    // loads, LDS writes and MFMAs of a step stay in one basic block).
+    auto commit = [&](int s, int buf, int st) {
+        const bool live = st < nst;
+        const int kin = (min(st, nst - 1) * GBK) % kseg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (AT) {
+                bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.a[buf][0][0]);
+                st16(&T[krow[i]][kcol], (live && kin + krow[i] < kvalid) ? ra[s][i] : zero16());
+            } else {
+                st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
+            }
+            if constexpr (BT) {
+                bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.b[buf][0][0]);
+                st16(&T[krow[i]][kcol], (live && kin + krow[i] < kvalid) ? rb[s][i] : zero16());
+            } else {
+                st16(&L.b[buf][lrow[i]][lcol], (live && bok[i]) ? rb[s][i] : zero16());
+            }
+        }
+    };
+    // fragment of row r (m or n) for the 32-wide half kh: natural k order
+    // (8 consecutive k per lane) or, when an operand is k-major, k = 4g + j
+    // and 16 + 4g + j on both sides
+    auto frag = [&](const bf16 (*X)[GPITCH], bool kmajor, int r, int kh) {
+        if (!TR) return as_bf8(ld16(&X[r][32 * kh + 8 * g]));
+        if (kmajor) {
+            const bf16(*T)[GTPITCH] = reinterpret_cast<const bf16(*)[GTPITCH]>(&X[0][0]);
+            const int rb0 = r - mm;  // first row of the 16-row block
+            const bf16x4 x0 = lds_read_tr(&T[32 * kh + 4 * g + (mm >> 2)][rb0 + 4 * (mm & 3)]);
+            const bf16x4 x1 = lds_read_tr(&T[32 * kh + 16 + 4 * g + (mm >> 2)][rb0 + 4 * (mm & 3)]);
+            return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        const bf16x4 x0 = load4<bf16>(&X[r][32 * kh + 4 * g]);
+        const bf16x4 x1 = load4<bf16>(&X[r][32 * kh + 16 + 4 * g]);
+        return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = zero4();
+
+#pragma unroll
+    for (int s = 0; s < GPD; ++s) {
+        issue(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    commit(0, 0, 0);
+    lds_barrier();
+    for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+        for (int j = 0; j < GPD; ++j) {
+            const int st = gi * GPD + j;
+            const int buf = j & 1;
+            // per 32-wide half: its fragments, then its MFMAs with the next
+            // steps' loads (first half) or LDS writes (second half) between them
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                bf16x8 af[4], bfr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    af[i] = frag(L.a[buf], AT, wm * 64 + 16 * i + mm, kh);
+                    bfr[i] = frag(L.b[buf], BT, wn * 64 + 16 * i + mm, kh);
+                }
+                if (kh == 0)
+                    issue(j, st + GPD);
+                else
+                    commit((j + 1) % GPD, (j + 1) & 1, st + 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
+                __builtin_amdgcn_sched_group_barrier(0x100, TR ? 16 : 8, 0);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (kh == 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    else
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                }
+            }
+            lds_barrier();
+        }
+    }
+    epi(acc, m0 + wm * 64, n0 + wn * 64, g, mm);
+}
+
+// ---------------------------------------------------------------------------
+// parameters shared by the kernels
+// ---------------------------------------------------------------------------
+struct LactParams {
+    const bf16 *q, *k, *v;
+    const float *eta;
+    const float *w1i, *w2i, *w3i;
+    bf16 *out;
+    float *w1, *w2, *w3;        // fp32 masters (the final-state buffers)
+    int NH, Tq, Tkv, d, hid, chunk, nchunks, cpad, qpad, loss, order, rownorm, splitk;
+    bf16 *dy;      // [NH][cpad][d]    dY token-major (MSE)
+    bf16 *w13b;    // [nslots][NH][2 parts][2 hid][d]  W1/W3 rows interleaved by 16; part 0 =
+                   //   bf16(W) (nearest), part 1 = bf16(W - part 0)
+    bf16 *w2b;     // [nslots][NH][2 parts][d][hid]
+    bf16 *gt;      // [NH][hid][cpad]  G^T of the current chunk
+    bf16 *dh1t;    // [NH][hid][cpad]
+    bf16 *dh3t;    // [NH][hid][cpad]
+    bf16 *gq;      // [NH][2 parts][qpad][hid]  G of the queries (or of the keys, MSE), hi/lo
+    float *part;   // [splitk][NH][3][hid * d] gradient partials; under Muon split 0 then
+                   //   holds the momentum-step direction and the Newton-Schulz iterate (fp32)
+    int nslots;
+    int rule;      // 0 gradient descent, 1 momentum, 2 Muon
+    float beta, lr;
+    float *m1, *m2, *m3;   // momentum buffers (like w1, w2, w3), or null
+    bf16 *nsb;     // [2][NH][3][hid * d] bf16 copies of the iterate (ping-pong)
+    bf16 *gram;    // [NH][3][d][d] bf16 Gram matrix of the iterate
+    float *diag;   // [NH][3][d] fp32 diagonal of the first Gram matrix
+    // Backward's forward replay: when set, the update of chunk save_c also
+    // writes the chunk-start weights and the step direction it subtracts,
+    // [chunk][NH][3][hid * d] fp32 each (W1, W3 as [hid][d], W2 as [d][hid]).
+    float *save_w = nullptr, *save_d = nullptr;
+    int save_c = 0;
+};
+
+// Row of W1 (which = 0) or W3 (which = 1) hidden unit h inside the packed
+// [2 hid][d] copy: blocks of 16 W1 rows and 16 W3 rows alternate, so one
+// wave's 64-row tile of a product with the packed copy holds matching
+// W1 and W3 rows.
+__device__ __forceinline__ int packed_row(int h, int which) { return 32 * (h >> 4) + 16 * which + (h & 15); }
+
+__device__ __forceinline__ long slot_off13(const LactParams &p, int slot, int h, int part = 0)
+{
+    return (((long)slot * p.NH + h) * 2 + part) * 2 * p.hid * p.d;
+}
+__device__ __forceinline__ long slot_off2(const LactParams &p, int slot, int h, int part = 0)
+{
+    return (((long)slot * p.NH + h) * 2 + part) * (long)p.d * p.hid;
+}
+// w = hi + lo: hi = bf16(w) (nearest), lo = bf16(w - hi) (w - hi is exact in fp32).
+__device__ __forceinline__ void split1(float w, bf16 &hi, bf16 &lo)
+{
+    hi = (bf16)w;
+    lo = (bf16)(w - (float)hi);
+}
+
+}  // namespace tttk

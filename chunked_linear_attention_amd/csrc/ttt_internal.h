@@ -40,6 +40,9 @@ struct LactShape {
     float beta = 0.f;    // momentum coefficient (rules 1, 2)
     int ns_steps = 0;    // Newton-Schulz steps (rule 2)
     float lr = 0.f;      // Muon step size (rule 2)
+    // backward's forward replay: per chunk, the chunk-start weights and the
+    // step direction ([chunk][NH][3][hid * d] fp32 each), or null
+    float *save_w = nullptr, *save_d = nullptr;
 };
 struct LactPlan {
     int nchunks;
@@ -53,6 +56,20 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
                        const float *w3, void *out, float *w1f, float *w2f, float *w3f, void *ws,
                        hipStream_t stream, hipStream_t aux, float *m1 = nullptr,
                        float *m2 = nullptr, float *m3 = nullptr);
+
+// ---- LaCT SwiGLU backward (inner-product loss, gradient descent) --------------------
+struct LactBwdPlan {
+    LactPlan fwd;        // the replay's own workspace (at offset 0)
+    int chunk, rpad;     // chunk length; rows of the per-token planes
+    size_t o_save_w, o_save_d, o_wfin, o_lam, o_gam, o_wcb, o_f, o_e, o_dy, o_bdy;
+    size_t bytes;
+};
+LactBwdPlan lact_bwd_plan(const LactShape &s);
+hipError_t lact_bwd_launch(const LactShape &s, const LactBwdPlan &pl, const void *q, const void *k,
+                           const void *v, const float *eta, const float *w1, const float *w2,
+                           const float *w3, const void *dout, const float *dw1f, const float *dw2f,
+                           const float *dw3f, void *dq, void *dk, void *dv, float *deta, float *dw1,
+                           float *dw2, float *dw3, void *ws, hipStream_t stream);
 
 // ---- decode steps (one token per head) ---------------------------------------------
 hipError_t linear_decode_launch(int NH, int d, int bf16, int loss, const void *q, const void *k,

@@ -333,3 +333,38 @@ def ttt_linear_bwd(q, k, v, eta, w_init, d_out, d_w_final=None, *, chunk: int, l
     if rc != TTT_OK:
         raise TTTError(rc, "ttt_linear_bwd")
     return dq, dk, dv, deta, dw0
+
+
+def lact_swiglu_bwd(q, k, v, eta, w1, w2, w3, d_out, d_w_final=None, *, chunk: int, loss="dot",
+                    order="causal", rownorm: bool = True, workspace=None, stream=None):
+    """Backward of lact_swiglu_fwd (inner-product loss, gradient descent): returns
+    (d_q, d_k, d_v, d_eta, d_w1, d_w2, d_w3) for upstream gradients d_out
+    [B,H,Tq,d] (q's dtype) and d_w_final = (d_w1, d_w2, d_w3) fp32 shaped like the
+    weights (None = zero)."""
+    lib = load()
+    B, H, Tq, d, Tkv, hid, dt, dev = _lact_dims(q, k, v, eta, w1, w2, w3)
+    specs = list(_lact_specs(B, H, Tq, d, Tkv, hid, dt, q, k, v, eta, w1, w2, w3, q, w1, w2,
+                             w3))[:7]
+    specs.append((d_out, "d_out", (B, H, Tq, d), dt))
+    if d_w_final is not None:
+        if len(d_w_final) != 3:
+            raise ValueError("d_w_final must be (d_w1, d_w2, d_w3)")
+        specs += [(t, n, tuple(w.shape), torch.float32)
+                  for t, w, n in zip(d_w_final, (w1, w2, w3), ("d_w1_final", "d_w2_final",
+                                                               "d_w3_final"))]
+    _validate(dev, *specs)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    deta = torch.empty_like(eta)
+    dw1, dw2, dw3 = torch.empty_like(w1), torch.empty_like(w2), torch.empty_like(w3)
+    ls, od = _LOSS[loss], _ORDER[order]
+    nbytes = lib.lact_swiglu_bwd_workspace_bytes(B, H, Tq, Tkv, d, hid, chunk, ls, od, _DT[dt])
+    workspace = _workspace(workspace, nbytes, dev)
+    dwf = (None, None, None) if d_w_final is None else tuple(d_w_final)
+    rc = lib.lact_swiglu_bwd(_ptr(q), _ptr(k), _ptr(v), _DT[dt], _ptr(eta), _ptr(w1), _ptr(w2),
+                             _ptr(w3), _ptr(d_out), _ptr(dwf[0]), _ptr(dwf[1]), _ptr(dwf[2]),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw1), _ptr(dw2),
+                             _ptr(dw3), B, H, Tq, Tkv, d, hid, chunk, ls, od, int(bool(rownorm)),
+                             _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != TTT_OK:
+        raise TTTError(rc, "lact_swiglu_bwd")
+    return dq, dk, dv, deta, dw1, dw2, dw3

@@ -270,6 +270,46 @@ ttt_status ttt_linear_bwd(const void *q, const void *k, const void *v, int dtype
                           int H, int Tq, int Tkv, int d, int chunk, int loss, int order,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * LaCT SwiGLU backward: the gradients of a scalar loss through
+ * lact_swiglu_fwd with the same arguments (inner-product loss, gradient
+ * descent), given the upstream gradients of the outputs and of the final
+ * weights.  The pages train the layer end to end ([LaCT] section 6, Table 3:
+ * training throughputs) but give no backward; this is reverse-mode
+ * differentiation of the forward's steps ([LaCT] 3.2-3.3, 4): per chunk in
+ * reverse, the row rescale's adjoint (with n = |W_c[r]|, m = |U[r]|,
+ * U = W_c - D_c: bar_U = (n/m) Lam - (U . Lam) n U / m^3 and
+ * bar_W_c = bar_U + (U . Lam) W_c[r] / (m n)), the adjoint of the chunk
+ * gradient D_c (second derivatives of the SwiGLU: silu'' included) with
+ * respect to the weights, keys, values and learning rates, and, for the
+ * chunk's queries, the apply's adjoint at W_c (causal) or at the final
+ * weights (non-causal).
+ * Inputs as lact_swiglu_fwd, plus d_out [B][H][Tq][d] in `dtype` and
+ * d_w1_final, d_w3_final [B][H][hid][d], d_w2_final [B][H][d][hid] fp32 (all
+ * three, or all NULL for zero).  Outputs: d_q [B][H][Tq][d], d_k, d_v
+ * [B][H][Tkv][d] in `dtype`; d_eta [B][H][Tkv] fp32; d_w1_init, d_w3_init
+ * [B][H][hid][d], d_w2_init [B][H][d][hid] fp32.  Outputs must not overlap
+ * the inputs or each other (TTT_EINVAL).
+ * Arithmetic: a replay of the forward (into the workspace) recovers every
+ * chunk's start weights and step; products run on bf16 matrix cores with fp32
+ * accumulation, the weight adjoints accumulate in fp32.
+ * Supported: dtype TTT_BF16, loss TTT_LOSS_DOT, the forward's shapes (d and
+ * hidden multiples of 128 up to 1024, chunk a multiple of 128 or >= Tkv),
+ * Tkv >= 1; Tq may be 0 in the non-causal order (q, d_out, d_q unused then).
+ * The MSE loss returns TTT_EUNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+size_t lact_swiglu_bwd_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int hidden,
+                                       int chunk, int loss, int order, int dtype);
+
+ttt_status lact_swiglu_bwd(const void *q, const void *k, const void *v, int dtype,
+                           const float *eta, const float *w1_init, const float *w2_init,
+                           const float *w3_init, const void *d_out, const float *d_w1_final,
+                           const float *d_w2_final, const float *d_w3_final, void *d_q, void *d_k,
+                           void *d_v, float *d_eta, float *d_w1_init, float *d_w2_init,
+                           float *d_w3_init, int B, int H, int Tq, int Tkv, int d, int hidden,
+                           int chunk, int loss, int order, int rownorm, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* LaCT decode apply ([LaCT] sections 3.2 and 4): out = W2 (silu(W1 q) * (W3 q))
  * for one query per (batch, head), with the weights as they stand (in the
  * causal order, the start-of-chunk weights of the chunk being decoded).  The

@@ -273,3 +273,40 @@ def test_linear_segment_length_argument():
     assert q(-5) == 0
     assert q(2048) < q(256) < q(64)
     assert q(4096) == 0   # one segment per head: no summaries
+
+
+def lact_bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, eta=FAKE, w1=FAKE, w2=FAKE, w3=FAKE, do=FAKE,
+             dw1=None, dw2=None, dw3=None, dq=FAKE + (1 << 24), dk=FAKE + (2 << 24),
+             dv=FAKE + (3 << 24), de=FAKE + (4 << 24), g1=FAKE + (5 << 24), g2=FAKE + (6 << 24),
+             g3=FAKE + (7 << 24), B=1, H=1, Tq=512, Tkv=512, d=128, hid=256, chunk=128, loss=0,
+             order=0, rownorm=1, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return lib.lact_swiglu_bwd(a["q"], a["k"], a["v"], a["dtype"], a["eta"], a["w1"], a["w2"],
+                               a["w3"], a["do"], a["dw1"], a["dw2"], a["dw3"], a["dq"], a["dk"],
+                               a["dv"], a["de"], a["g1"], a["g2"], a["g3"], a["B"], a["H"],
+                               a["Tq"], a["Tkv"], a["d"], a["hid"], a["chunk"], a["loss"],
+                               a["order"], a["rownorm"], a["ws"], a["wsb"], a["stream"])
+
+
+# every case fails validation before a launch (wsb = 0 ends the valid ones with EWORKSPACE)
+@pytest.mark.parametrize("kw,code", [
+    (dict(), _lib.TTT_EWORKSPACE),
+    (dict(dw1=FAKE), _lib.TTT_EINVAL),          # upstream weight gradients: all three or none
+    (dict(dw1=FAKE, dw2=FAKE, dw3=FAKE + 4), _lib.TTT_EINVAL),
+    (dict(dk=None), _lib.TTT_EINVAL), (dict(g2=FAKE + 8), _lib.TTT_EINVAL),
+    (dict(loss=1), _lib.TTT_EUNSUPPORTED), (dict(dtype=0), _lib.TTT_EUNSUPPORTED),
+    (dict(d=64), _lib.TTT_EUNSUPPORTED), (dict(Tq=100), _lib.TTT_EINVAL),
+    (dict(Tkv=0, Tq=0), _lib.TTT_EINVAL), (dict(rownorm=3), _lib.TTT_EINVAL),
+    (dict(dq=FAKE), _lib.TTT_EINVAL),           # d_q would overlap q
+    (dict(order=1, Tq=0, q=None, do=None, dq=None), _lib.TTT_EWORKSPACE),
+])
+def test_lact_bwd_validation(kw, code):
+    assert lact_bwd(_lib.load(), **kw) == code
+
+
+def test_lact_bwd_workspace_query():
+    lib = _lib.load()
+    n = lib.lact_swiglu_bwd_workspace_bytes(1, 4, 32768, 32768, 256, 512, 2048, 0, 0, 1)
+    assert n > lib.lact_swiglu_workspace_bytes(1, 4, 32768, 32768, 256, 512, 2048, 0, 0, 1)
+    assert lib.lact_swiglu_bwd_workspace_bytes(1, 4, 32768, 32768, 256, 512, 2048, 1, 0, 1) == 0
