@@ -422,35 +422,60 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot, i
         }
         return;
     }
-    constexpr int MAXE = 16;  // len <= 1024 = 16 x 64
-    float nv[MAXE];
+    // Each lane owns four consecutive columns per 256-column step (rows are
+    // multiples of 128 long, at most 1024), and every load of the row is issued
+    // before the first use: the kernel is one round of latency, not of issue.
+    constexpr int MAXE = 4;
+    f32x4 ov[MAXE], dv[MAXE];
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        ov[e] = dv[e] = zero4();
+        const int col = 4 * lane + 256 * e;
+        if (col < len) ov[e] = load4<float>(w + col);
+    }
+    if (p.rule == 2) {
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) {
+            const int col = 4 * lane + 256 * e;
+            if (col < len) dv[e] = p.lr * load4<float>(p.part + eoff + col);
+        }
+    } else {
+        for (int sp = 0; sp < p.splitk; ++sp) {
+            const float *ps = p.part + (long)sp * p.NH * 3 * n13 + eoff;
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e) {
+                const int col = 4 * lane + 256 * e;
+                if (col < len) dv[e] += load4<float>(ps + col);
+            }
+        }
+        if (mrow) {
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e) {
+                const int col = 4 * lane + 256 * e;
+                if (col < len) {
+                    dv[e] += p.beta * load4<float>(mrow + col);
+                    store4<float>(mrow + col, dv[e]);
+                }
+            }
+        }
+    }
     float so = 0.f, sn = 0.f;
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) {
-        const int col = lane + 64 * e;
-        nv[e] = 0.f;
+        const int col = 4 * lane + 256 * e;
         if (col < len) {
-            const float old = w[col];
-            float dir;
-            if (p.rule == 2) {
-                dir = p.lr * p.part[eoff + col];
-            } else {
-                dir = 0.f;
-                for (int s = 0; s < p.splitk; ++s) dir += p.part[(long)s * p.NH * 3 * n13 + eoff + col];
-                if (mrow) {
-                    dir += p.beta * mrow[col];
-                    mrow[col] = dir;
-                }
+            const f32x4 x = ov[e] - dv[e];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                so += ov[e][j] * ov[e][j];
+                sn += x[j] * x[j];
             }
-            const float x = old - dir;
-            so += old * old;
-            sn += x * x;
-            nv[e] = x;
             if (p.save_w) {
                 const long so_off = (long)p.save_c * p.NH * 3 * n13 + eoff + col;
-                p.save_w[so_off] = old;
-                p.save_d[so_off] = dir;
+                store4<float>(p.save_w + so_off, ov[e]);
+                store4<float>(p.save_d + so_off, dv[e]);
             }
+            ov[e] = x;
         }
     }
     float scale = 1.f;
@@ -461,24 +486,31 @@ __global__ __launch_bounds__(256) void lact_update(LactParams p, int dst_slot, i
     }
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) {
-        const int col = lane + 64 * e;
+        const int col = 4 * lane + 256 * e;
         if (col < len) {
             // rounded once: the bf16 pair below must encode exactly the stored
             // master (a product fused into the split would give a different lo
             // part than a later call rebuilding the pair from the master)
+            f32x4 x;
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
 #pragma clang fp contract(off)
-            const float x = nv[e] * scale;
-            w[col] = x;
-            bf16 hi, lo;
-            split1(x, hi, lo);
+                x[j] = ov[e][j] * scale;
+                bf16 h1, l1;
+                split1(x[j], h1, l1);
+                hi[j] = h1;
+                lo[j] = l1;
+            }
+            store4<float>(w + col, x);
             if (which < 2) {
                 const long o = (long)packed_row(row, which) * p.d + col;
-                p.w13b[slot_off13(p, dst_slot, h, 0) + o] = hi;
-                p.w13b[slot_off13(p, dst_slot, h, 1) + o] = lo;
+                store4<bf16>(p.w13b + slot_off13(p, dst_slot, h, 0) + o, hi);
+                store4<bf16>(p.w13b + slot_off13(p, dst_slot, h, 1) + o, lo);
             } else {
                 const long o = (long)row * p.hid + col;
-                p.w2b[slot_off2(p, dst_slot, h, 0) + o] = hi;
-                p.w2b[slot_off2(p, dst_slot, h, 1) + o] = lo;
+                store4<bf16>(p.w2b + slot_off2(p, dst_slot, h, 0) + o, hi);
+                store4<bf16>(p.w2b + slot_off2(p, dst_slot, h, 1) + o, lo);
             }
         }
     }
@@ -617,7 +649,7 @@ __global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
 // Token tiles never straddle chunks (chunk % 128 == 0 or one chunk).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, long x_head_stride,
-                                                   int T, int slot_fixed)
+                                                   int T, int slot_fixed, int slot0)
 {
     __shared__ GemmLds L;
     const int mt = (2 * p.hid) / 128, nt = (T + 127) / 128;
@@ -626,7 +658,7 @@ __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, 
     bid /= mt;
     const int tn = bid % nt;
     const int h = bid / nt;
-    const int slot = (slot_fixed >= 0) ? slot_fixed : (tn * 128) / p.chunk;
+    const int slot = (slot_fixed >= 0) ? slot_fixed : slot0 + (tn * 128) / p.chunk;
     // X (W_hi + W_lo)^T: two K segments over the same X rows
     const bf16 *as[2] = {p.w13b + slot_off13(p, slot, h, 0), p.w13b + slot_off13(p, slot, h, 1)};
     const bf16 *B = X + (long)h * x_head_stride;
@@ -681,7 +713,7 @@ __global__ __launch_bounds__(256) void lact_apply1(LactParams p, const bf16 *X, 
 // one token per lane).  mode 0: out = Y (bf16).  mode 1 (MSE): dY = eta (Y - V)
 // token-major into p.dy (chunk-local tokens).
 __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot_fixed, int mode,
-                                                   int c)
+                                                   int c, int slot0)
 {
     __shared__ GemmLds L;
     const int mt = p.d / 128, nt = (T + 127) / 128;
@@ -690,7 +722,7 @@ __global__ __launch_bounds__(256) void lact_apply2(LactParams p, int T, int slot
     bid /= mt;
     const int tn = bid % nt;
     const int h = bid / nt;
-    const int slot = (slot_fixed >= 0) ? slot_fixed : (tn * 128) / p.chunk;
+    const int slot = (slot_fixed >= 0) ? slot_fixed : slot0 + (tn * 128) / p.chunk;
     // (W2_hi G_hi + W2_lo G_hi + W2_hi G_lo): three K segments
     const bf16 *whi = p.w2b + slot_off2(p, slot, h, 0), *wlo = p.w2b + slot_off2(p, slot, h, 1);
     const bf16 *ghi = p.gq + (long)h * 2 * p.qpad * p.hid, *glo = ghi + (long)p.qpad * p.hid;
@@ -880,16 +912,31 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     auto chk = [&](hipError_t e) {
         if (e != hipSuccess && serr == hipSuccess) serr = e;
     };
-    auto apply_chunk = [&](int c) {
-        chk(hipEventRecord(ready, st));
-        chk(hipStreamWaitEvent(aux, ready, 0));
-        const int qlen = (c + 1) * p.chunk <= s.Tq ? p.chunk : s.Tq - c * p.chunk;
-        lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((qlen + 127) / 128)), dim3(256), 0, aux>>>(
-            p, p.q + (long)c * p.chunk * s.d, (long)s.Tq * s.d, qlen, c);
-        lact_apply2<<<dim3(s.NH * (s.d / 128) * ((qlen + 127) / 128)), dim3(256), 0, aux>>>(p, qlen, c, 0,
-                                                                                          c);
+    // The queries of chunks [c0, c0 + n) in one pair of launches (each tile
+    // reads its own chunk's weights), as soon as the last of those weights
+    // exist.  One chunk per group: grouping two (twice the workgroups per
+    // launch) measured slower on the causal LM workload (1.14 -> 1.27 ms), the
+    // larger launches taking compute units from the update chain, which is the
+    // critical path.
+    constexpr int APPLY_GROUP = 1;
+    const int nq = use_aux ? (s.Tq + p.chunk - 1) / p.chunk : 0;
+    int next_q = 0;  // first chunk whose queries are not yet enqueued
+    auto apply_ready = [&](int slots_ready) {
+        while (next_q < nq) {
+            const int n = (next_q + APPLY_GROUP <= nq) ? APPLY_GROUP : nq - next_q;
+            if (next_q + n - 1 > slots_ready) break;
+            chk(hipEventRecord(ready, st));
+            chk(hipStreamWaitEvent(aux, ready, 0));
+            const int q0 = next_q * p.chunk;
+            const int qlen = ((next_q + n) * p.chunk <= s.Tq ? n * p.chunk : s.Tq - q0);
+            lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((qlen + 127) / 128)), dim3(256), 0, aux>>>(
+                p, p.q + (long)q0 * s.d, (long)s.Tq * s.d, qlen, -1, next_q);
+            lact_apply2<<<dim3(s.NH * (s.d / 128) * ((qlen + 127) / 128)), dim3(256), 0, aux>>>(
+                p, qlen, -1, 0, next_q, next_q);
+            next_q += n;
+        }
     };
-    if (use_aux) apply_chunk(0);
+    apply_ready(0);
     for (int c = 0; c < pl.nchunks; ++c) {
         const int slot = (s.order == 0) ? c : 0;
         const int dst = (s.order == 0) ? c + 1 : 0;
@@ -897,9 +944,9 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
         if (s.loss == 1) {
             // dY = eta (f(K_c) - V_c): G of the chunk's keys, then W2.
             lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((clen + 127) / 128)), dim3(256), 0, st>>>(
-                p, p.k + (long)c * p.chunk * s.d, (long)s.Tkv * s.d, clen, slot);
+                p, p.k + (long)c * p.chunk * s.d, (long)s.Tkv * s.d, clen, slot, 0);
             lact_apply2<<<dim3(s.NH * (s.d / 128) * ((clen + 127) / 128)), dim3(256), 0, st>>>(
-                p, clen, slot, 1, c);
+                p, clen, slot, 1, c, 0);
         }
         lact_fwdgrad<FWD_NW><<<dim3(s.NH * (p.cpad / 128) * (s.hid / 128)), dim3(64 * FWD_NW), 0, st>>>(p, c, slot);
         lact_wgrad<<<dim3(s.NH * p.splitk * 3 * t13), dim3(256), 0, st>>>(p, c);
@@ -912,7 +959,7 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
         }
         p.save_c = c;
         lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst, 0);
-        if (use_aux && (c + 1) * p.chunk < s.Tq) apply_chunk(c + 1);
+        apply_ready(c + 1);
     }
     if (use_aux) {
         chk(hipEventRecord(done, aux));
@@ -923,9 +970,9 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
     } else if (s.Tq > 0) {
         const int fixed = (s.order == 0) ? -1 : 0;
         lact_apply1<<<dim3(s.NH * ((2 * s.hid) / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(
-            p, p.q, (long)s.Tq * s.d, s.Tq, fixed);
+            p, p.q, (long)s.Tq * s.d, s.Tq, fixed, 0);
         lact_apply2<<<dim3(s.NH * (s.d / 128) * ((s.Tq + 127) / 128)), dim3(256), 0, st>>>(
-            p, s.Tq, fixed, 0, 0);
+            p, s.Tq, fixed, 0, 0, 0);
     }
     if (serr != hipSuccess) return serr;
     return hipGetLastError();

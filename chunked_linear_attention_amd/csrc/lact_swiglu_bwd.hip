@@ -48,7 +48,12 @@ namespace tttk {
 //   C_h[m][n] (op)= sum_s sum_k A_s,h[m][k] B_s,h[n][k]
 // with the operand layouts of gemm_nt_tile (AT / BT: k-major).  out: 0 store
 // fp32, 1 add into fp32, 2 store bf16.  Rows m >= M and columns n >= N are not
-// written.
+// written.  With P set the output goes to fp32 partials instead.  Split-K
+// (ksplit > 1, P set): workgroup ks takes either the k rows
+// [ks kper, (ks + 1) kper) of every segment (split_rows, both operands
+// k-major) or the segments [ks nseg/ksplit, (ks + 1) nseg/ksplit), and stores
+// its fp32 partial at P + ks p_ss + h p_hs + m ldc + n; a reduction kernel
+// sums the partials in split order (the result does not depend on timing).
 // ---------------------------------------------------------------------------
 constexpr int BWD_MAXSEG = 12;
 struct BwdGemm {
@@ -60,6 +65,9 @@ struct BwdGemm {
     bf16 *Cb;
     long c_hs, ldc;
     int out;
+    int ksplit, split_rows, kper;
+    float *P;
+    long p_ss, p_hs;
 };
 
 template <bool AT, bool BT>
@@ -68,19 +76,44 @@ __global__ __launch_bounds__(256) void lbk_gemm(BwdGemm j)
     __shared__ GemmLds L;
     const int tm_n = (j.M + 127) / 128, tn_n = (j.N + 127) / 128;
     int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int ks = bid % j.ksplit;
+    bid /= j.ksplit;
     const int tn = bid % tn_n;
     bid /= tn_n;
     const int tm = bid % tm_n;
     const int h = bid / tm_n;
+    int s0 = 0, ns = j.nseg, kseg = j.kseg, kvalid = j.kvalid;
+    long koff_a = 0, koff_b = 0;
+    if (j.ksplit > 1) {
+        if (j.split_rows) {
+            const int k0 = ks * j.kper;
+            kseg = j.kper;
+            kvalid = min(j.kper, j.kvalid - k0);
+            koff_a = (long)k0 * j.lda;
+            koff_b = (long)k0 * j.ldb;
+        } else {
+            ns = j.nseg / j.ksplit;
+            s0 = ks * ns;
+        }
+    }
     const bf16 *as[BWD_MAXSEG], *bs[BWD_MAXSEG];
 #pragma unroll
     for (int s = 0; s < BWD_MAXSEG; ++s) {
-        as[s] = (s < j.nseg) ? j.A[s] + (long)h * j.a_hs : nullptr;
-        bs[s] = (s < j.nseg) ? j.B[s] + (long)h * j.b_hs : nullptr;
+        as[s] = (s < ns) ? j.A[s0 + s] + (long)h * j.a_hs + koff_a : nullptr;
+        bs[s] = (s < ns) ? j.B[s0 + s] + (long)h * j.b_hs + koff_b : nullptr;
     }
+    float *P = j.P ? j.P + (long)ks * j.p_ss + (long)h * j.p_hs : nullptr;
     float *C = j.C ? j.C + (long)h * j.c_hs : nullptr;
     bf16 *Cb = j.Cb ? j.Cb + (long)h * j.c_hs : nullptr;
-    gemm_nt_tile<AT, BT>(L, as, j.lda, bs, j.ldb, j.M, j.N, j.kseg, j.nseg, tm * 128, tn * 128, j.kvalid,
+    if (P && kvalid <= 0) {
+        // an empty k range contributes zero (the partial is still written)
+        for (int e = threadIdx.x; e < 128 * 128; e += 256) {
+            const int m = tm * 128 + (e >> 7), n = tn * 128 + (e & 127);
+            if (m < j.M && n < j.N) P[(long)m * j.ldc + n] = 0.f;
+        }
+        return;
+    }
+    gemm_nt_tile<AT, BT>(L, as, j.lda, bs, j.ldb, j.M, j.N, kseg, ns, tm * 128, tn * 128, kvalid,
                          [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
 #pragma unroll
                              for (int i = 0; i < 4; ++i)
@@ -93,7 +126,9 @@ __global__ __launch_bounds__(256) void lbk_gemm(BwdGemm j)
                                          const int m = mb + 16 * i + 4 * g + r;
                                          if (m >= j.M) continue;
                                          const long o = (long)m * j.ldc + n;
-                                         if (j.out == 0)
+                                         if (P)
+                                             P[o] = acc[i][q][r];
+                                         else if (j.out == 0)
                                              C[o] = acc[i][q][r];
                                          else if (j.out == 1)
                                              C[o] += acc[i][q][r];
@@ -102,6 +137,35 @@ __global__ __launch_bounds__(256) void lbk_gemm(BwdGemm j)
                                      }
                                  }
                          });
+}
+
+// lam[i] += sum_ks P[ks stride + i], in split order
+__global__ __launch_bounds__(256) void lbk_red_add(const float *P, int ksplit, long stride, float *lam, long n)
+{
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        float x = 0.f;
+        for (int k = 0; k < ksplit; ++k) x += P[(long)k * stride + i];
+        lam[i] += x;
+    }
+}
+
+// out[h][t][i] = sum_ks P[ks stride + (h rpad + t) d + i] for t < rows; out as
+// bf16 (ob, head stride o_hs) or fp32 (of, same layout as the partials)
+__global__ __launch_bounds__(256) void lbk_red_rows(const float *P, int ksplit, long stride, int NH, int rows,
+                                                    int rpad, int d, bf16 *ob, long o_hs, float *of)
+{
+    const long n = (long)NH * rows * d;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        const int h = (int)(i / ((long)rows * d));
+        const long r = i % ((long)rows * d);
+        const long src = (long)h * rpad * d + r;
+        float x = 0.f;
+        for (int k = 0; k < ksplit; ++k) x += P[(long)k * stride + src];
+        if (ob)
+            ob[(long)h * o_hs + r] = (bf16)x;
+        else
+            of[src] = x;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -333,6 +397,11 @@ __global__ __launch_bounds__(256) void lbk_tok(const float *bdy, const bf16 *v, 
 // ---------------------------------------------------------------------------
 static size_t al256b(size_t x) { return (x + 255) / 256 * 256; }
 
+// split-K limits: contractions over tokens (the weight adjoints) into at most
+// 16 token ranges, the ones over the hidden units (token-side adjoints) into
+// at most 4 groups of segments
+constexpr int BWD_KS_W = 16, BWD_KS_T = 4;
+
 LactBwdPlan lact_bwd_plan(const LactShape &s)
 {
     LactBwdPlan pl{};
@@ -359,7 +428,9 @@ LactBwdPlan lact_bwd_plan(const LactShape &s)
     take(pl.o_f, 6 * NH * (size_t)pl.rpad * s.hid * 4);
     take(pl.o_e, 12 * NH * (size_t)pl.rpad * s.hid * 2);       // 6 planes, hi then lo
     take(pl.o_dy, 2 * NH * cpad * s.d * 2);                    // hi, lo
-    take(pl.o_bdy, NH * cpad * s.d * 4);
+    take(pl.o_bdy, NH * (size_t)pl.rpad * s.d * 4);
+    const size_t pw = (size_t)BWD_KS_W * NH * 3 * n13, pt = (size_t)BWD_KS_T * NH * pl.rpad * s.d;
+    take(pl.o_part, 4 * (pw > pt ? pw : pt));
     pl.bytes = off;
     return pl;
 }
@@ -367,9 +438,26 @@ LactBwdPlan lact_bwd_plan(const LactShape &s)
 template <bool AT, bool BT>
 static void run_gemm(const BwdGemm &j, int NH, hipStream_t st)
 {
-    const int grid = NH * ((j.M + 127) / 128) * ((j.N + 127) / 128);
+    const int grid = NH * ((j.M + 127) / 128) * ((j.N + 127) / 128) * j.ksplit;
     if (grid > 0 && j.nseg > 0) lbk_gemm<AT, BT><<<dim3(grid), dim3(256), 0, st>>>(j);
 }
+
+// Token-range split of a contraction over ntok tokens (both operands
+// k-major): enough splits to give about one workgroup per compute unit, each
+// a whole number of 64-token steps, at most BWD_KS_W.  Returns the split count.
+static int split_tokens(BwdGemm &j, int NH, int ntok)
+{
+    const int tiles = NH * ((j.M + 127) / 128) * ((j.N + 127) / 128);
+    int ks = 256 / (tiles > 0 ? tiles : 1);
+    ks = ks < 1 ? 1 : (ks > BWD_KS_W ? BWD_KS_W : ks);
+    const int kper = ((ntok + ks - 1) / ks + 63) / 64 * 64;
+    j.ksplit = (ntok + kper - 1) / kper;
+    j.split_rows = 1;
+    j.kper = kper;
+    return j.ksplit;
+}
+
+static unsigned ew_grid(long n) { return (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192); }
 
 static BwdGemm gemm_job(int M, int N, int kseg, int kvalid, long lda, long a_hs, long ldb, long b_hs)
 {
@@ -378,6 +466,7 @@ static BwdGemm gemm_job(int M, int N, int kseg, int kvalid, long lda, long a_hs,
     j.N = N;
     j.kseg = kseg;
     j.nseg = 0;
+    j.ksplit = 1;
     j.kvalid = kvalid;
     j.lda = lda;
     j.a_hs = a_hs;
@@ -407,7 +496,53 @@ struct BwdBufs {
     float *lam, *F;
     bf16 *E;                    // 6 planes hi, then 6 planes lo
     long plane;
+    float *part;                // split-K partials
 };
+
+// The three weight-adjoint GEMMs of a phase (W1, W3: hid x d; W2: d x hid) add
+// into lam: split over token ranges when that fills the chip (partials, then
+// one ordered reduction for all three), else added directly.
+static void weight_adjoints(BwdGemm (&jobs)[3], const BwdBufs &b, int NH, long n13, int ntok, hipStream_t st)
+{
+    int ks = 1;
+    for (int x = 0; x < 3; ++x) ks = split_tokens(jobs[x], NH, ntok);
+    for (int x = 0; x < 3; ++x) {
+        BwdGemm &j = jobs[x];
+        if (ks > 1) {
+            j.P = b.part + (x == 2 ? 2 : x) * n13;
+            j.p_ss = (long)NH * 3 * n13;
+            j.p_hs = 3 * n13;
+        } else {
+            j.ksplit = 1;
+        }
+        run_gemm<true, true>(j, NH, st);
+    }
+    if (ks > 1) {
+        const long n = (long)NH * 3 * n13;
+        lbk_red_add<<<dim3(ew_grid(n)), dim3(256), 0, st>>>(b.part, ks, n, b.lam, n);
+    }
+}
+
+// A token-side product over the hidden units (its segments in groups of three,
+// one group per product), split into one group per workgroup; the ordered sum
+// goes to bf16 rows of an output [NH][.][d] (ob, head stride o_hs) or to fp32
+// rows [NH][rpad][d] (of).
+template <bool BT>
+static void token_side(BwdGemm &j, const BwdBufs &b, const LactBwdPlan &pl, int NH, int rows, int d, bf16 *ob,
+                       long o_hs, float *of, hipStream_t st)
+{
+    // every product here has two bf16-pair operands: three segments each
+    j.ksplit = (j.nseg % 3 == 0 && j.nseg / 3 <= BWD_KS_T) ? j.nseg / 3 : 1;
+    j.split_rows = 0;
+    j.P = b.part;
+    j.p_hs = (long)pl.rpad * d;
+    j.p_ss = (long)NH * pl.rpad * d;
+    j.ldc = d;
+    run_gemm<false, BT>(j, NH, st);
+    const long n = (long)NH * rows * d;
+    lbk_red_rows<<<dim3(ew_grid(n)), dim3(256), 0, st>>>(b.part, j.ksplit, j.p_ss, NH, rows, pl.rpad, d, ob, o_hs,
+                                                         of);
+}
 
 // The apply's reverse for rows X (x0 .. x0 + rows of q, upstream dout) at the
 // weights whose bf16 pairs are in b.wcb: d_q rows, and the weight adjoints
@@ -437,10 +572,12 @@ static void apply_bwd(const LactShape &s, const LactBwdPlan &pl, const BwdBufs &
         b.F, b.E, plane, pl.rpad, hid, rows, tot);
     const int kseg = (rows + 63) / 64 * 64;
     // lam_W1 += bar_H1^T X, lam_W3 += bar_H3^T X, lam_W2 += dO^T G
+    BwdGemm wj[3];
     for (int k = 0; k < 3; ++k) {
         const bool w2 = k == 2;
-        BwdGemm j = gemm_job(w2 ? d : hid, w2 ? hid : d, kseg, rows, w2 ? d : hid, w2 ? x_hs : f_hs,
-                             w2 ? hid : d, w2 ? f_hs : x_hs);
+        BwdGemm &j = wj[k];
+        j = gemm_job(w2 ? d : hid, w2 ? hid : d, kseg, rows, w2 ? d : hid, w2 ? x_hs : f_hs, w2 ? hid : d,
+                     w2 ? f_hs : x_hs);
         if (w2)
             add_prod(j, DO, nullptr, E + 2 * plane, El + 2 * plane);
         else
@@ -449,17 +586,13 @@ static void apply_bwd(const LactShape &s, const LactBwdPlan &pl, const BwdBufs &
         j.c_hs = w_hs;
         j.ldc = w2 ? hid : d;
         j.out = 1;
-        run_gemm<true, true>(j, NH, st);
     }
+    weight_adjoints(wj, b, NH, n13, rows, st);
     // d_q = bar_H1 W1 + bar_H3 W3
     BwdGemm j = gemm_job(rows, d, hid, hid, hid, f_hs, d, w_hs);
     add_prod(j, E + 4 * plane, El + 4 * plane, b.wcb, b.wcb_lo);
     add_prod(j, E + 5 * plane, El + 5 * plane, b.wcb + n13, b.wcb_lo + n13);
-    j.Cb = dq + (long)x0 * d;
-    j.c_hs = x_hs;
-    j.ldc = d;
-    j.out = 2;
-    run_gemm<false, true>(j, NH, st);
+    token_side<true>(j, b, pl, NH, rows, d, dq + (long)x0 * d, x_hs, nullptr, st);
 }
 
 hipError_t lact_bwd_launch(const LactShape &s, const LactBwdPlan &pl, const void *q, const void *k,
@@ -485,7 +618,7 @@ hipError_t lact_bwd_launch(const LactShape &s, const LactBwdPlan &pl, const void
     const bf16 *El = E + 6 * plane;
     const int cpad = (int)pl.fwd.off[12];
     const unsigned wgrid = (unsigned)((wtot + 255) / 256 < 4096 ? (wtot + 255) / 256 : 4096);
-    const BwdBufs bufs{wcb, wcb_lo, lam, F, E, plane};
+    const BwdBufs bufs{wcb, wcb_lo, lam, F, E, plane, (float *)(base + pl.o_part)};
 
     // 1. the forward again (no applies), saving W_c and D_c of every chunk;
     //    its final weights land in wfin ([W1 all heads][W3 all heads][W2 all heads])
@@ -540,10 +673,12 @@ hipError_t lact_bwd_launch(const LactShape &s, const LactBwdPlan &pl, const void
             F, E, plane, pl.rpad, hid, clen, tot);
         // lam_W1 += bar_H1^T K, lam_W3 += bar_H3^T K, lam_W2 += dY^T bar_dG
         const int kseg = (clen + 63) / 64 * 64;
+        BwdGemm wj[3];
         for (int x = 0; x < 3; ++x) {
             const bool w2m = x == 2;
-            BwdGemm j = gemm_job(w2m ? d : hid, w2m ? hid : d, kseg, clen, w2m ? d : hid, w2m ? dy_hs : f_hs,
-                                 w2m ? hid : d, w2m ? f_hs : k_hs);
+            BwdGemm &j = wj[x];
+            j = gemm_job(w2m ? d : hid, w2m ? hid : d, kseg, clen, w2m ? d : hid, w2m ? dy_hs : f_hs,
+                         w2m ? hid : d, w2m ? f_hs : k_hs);
             if (w2m)
                 add_prod(j, DY, DYl, E + 3 * plane, El + 3 * plane);
             else
@@ -552,8 +687,8 @@ hipError_t lact_bwd_launch(const LactShape &s, const LactBwdPlan &pl, const void
             j.c_hs = w_hs;
             j.ldc = w2m ? hid : d;
             j.out = 1;
-            run_gemm<true, true>(j, NH, st);
         }
+        weight_adjoints(wj, bufs, NH, n13, clen, st);
         // d_k = dH1 Gam1 + dH3 Gam3 + bar_H1 W1 + bar_H3 W3 (this chunk's rows)
         {
             BwdGemm j = gemm_job(clen, d, hid, hid, hid, f_hs, d, w_hs);
@@ -561,24 +696,16 @@ hipError_t lact_bwd_launch(const LactShape &s, const LactBwdPlan &pl, const void
             add_prod(j, E + plane, El + plane, gam + n13, gam_lo + n13);
             add_prod(j, E + 4 * plane, El + 4 * plane, wcb, wcb_lo);
             add_prod(j, E + 5 * plane, El + 5 * plane, wcb + n13, wcb_lo + n13);
-            j.Cb = (bf16 *)dk + (long)c0 * d;
-            j.c_hs = k_hs;
-            j.ldc = d;
-            j.out = 2;
-            run_gemm<false, true>(j, NH, st);
+            token_side<true>(j, bufs, pl, NH, clen, d, (bf16 *)dk + (long)c0 * d, k_hs, nullptr, st);
         }
         // bar_dY = G Gam2^T + bar_dG W2^T, then d_v and d_eta
         {
             BwdGemm j = gemm_job(clen, d, hid, hid, hid, f_hs, hid, w_hs);
             add_prod(j, E + 2 * plane, El + 2 * plane, gam + 2 * n13, gam_lo + 2 * n13);
             add_prod(j, E + 3 * plane, El + 3 * plane, wcb + 2 * n13, wcb_lo + 2 * n13);
-            j.C = BDY;
-            j.c_hs = dy_hs;
-            j.ldc = d;
-            j.out = 0;
-            run_gemm<false, false>(j, NH, st);
+            token_side<false>(j, bufs, pl, NH, clen, d, nullptr, 0, BDY, st);
             lbk_tok<<<dim3((NH * clen + 3) / 4), dim3(256), 0, st>>>(BDY, V, eta, (bf16 *)dv, deta, NH, s.Tkv, c0,
-                                                                     clen, cpad, d);
+                                                                     clen, pl.rpad, d);
         }
         // causal: the chunk's queries read W_c
         if (s.order == 0 && c0 < s.Tq) {

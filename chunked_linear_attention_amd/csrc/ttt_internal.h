@@ -61,7 +61,7 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
 struct LactBwdPlan {
     LactPlan fwd;        // the replay's own workspace (at offset 0)
     int chunk, rpad;     // chunk length; rows of the per-token planes
-    size_t o_save_w, o_save_d, o_wfin, o_lam, o_gam, o_wcb, o_f, o_e, o_dy, o_bdy;
+    size_t o_save_w, o_save_d, o_wfin, o_lam, o_gam, o_wcb, o_f, o_e, o_dy, o_bdy, o_part;
     size_t bytes;
 };
 LactBwdPlan lact_bwd_plan(const LactShape &s);
