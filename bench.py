@@ -646,10 +646,13 @@ def main():
         return
 
     if args.bwd_only:
-        print(json.dumps({"backward": [bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps,
-                                                        args.warmup),
-                                       bench_lact_bwd(ti.LACT_CAUSAL, args.steps, args.warmup)]}),
-              flush=True)
+        # the headline shape, the d = 128 chunk-size sweep's shape, then LaCT
+        bwd = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps, args.warmup)]
+        for b in (16, 64, 256, 1024):
+            log(f"[bench] TTT-Linear backward B2 H16 T16384 d128 b{b}")
+            bwd.append(bench_linear_bwd(2, 16, 16384, 128, b, 1, max(5, args.steps // 10), 2))
+        bwd.append(bench_lact_bwd(ti.LACT_CAUSAL, args.steps, args.warmup))
+        print(json.dumps({"backward": bwd}), flush=True)
         return
     if args.window_only:
         print(json.dumps({"window_attention": [bench_window_attention(1, 4, 32768, 256, 2048,

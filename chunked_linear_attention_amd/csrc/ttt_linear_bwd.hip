@@ -47,6 +47,12 @@ struct LinBwdParams {
     int order, Tq;         // order 1: update over all key/value chunks, then apply to Tq queries
     float *wfinal;         // [NH][D][D] (order 1) final state
     float *ginit;          // [NH][D][D] (order 1) dL/dW_final incl. the apply's Q^T dO
+    // The serial passes and the dependent pass step over `ntiles` tiles of the
+    // kernels' B tokens; a chunk is `sub` tiles (sub = 1: a tile is a chunk;
+    // sub > 1 only with B = 16).  The per-token buffers have head stride
+    // rstride = nchunks * chunk rows.
+    int sub, ntiles;
+    long rstride;
 };
 
 template <typename E> __device__ __forceinline__ float ldf(const void *p, long i)
@@ -85,15 +91,16 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
     __shared__ __align__(16) float Vt[2][NB][CB][TP];
     __shared__ __align__(16) float et[2][NB][B];
     __shared__ __align__(16) float Ut[CB][TP];
+    __shared__ float S[D][CB + 1];  // chunk-start state (sub > 1): the residuals' snapshot
     const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
-    const int nbat = (p.nchunks + NB - 1) / NB;
+    const int nbat = (p.ntiles + NB - 1) / NB;
     float pk[NB][NK], pv[NB][NV], pe[NB];
     auto load = [&](int k) {
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
             const int c = k * NB + m;
-            const int c0 = c * B, n = c < p.nchunks ? min(B, p.T - c0) : 0;
+            const int c0 = c * B, n = c < p.ntiles ? min(B, p.T - c0) : 0;
 #pragma unroll
             for (int r = 0; r < NK; ++r) {
                 const int e = tid + 256 * r, i = e / D, a = e % D;
@@ -126,13 +133,20 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
         if (k + 1 < nbat) load(k + 1);
         for (int m = 0; m < NB; ++m) {
             const int c = k * NB + m;
-            if (c >= p.nchunks) break;
-            float *dst = p.states + ((long)h * p.nchunks + c) * D * D;
-            for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
+            if (c >= p.ntiles) break;
+            if (c % p.sub == 0) {  // a chunk starts: store its state (and snapshot it)
+                float *dst = p.states + ((long)h * p.nchunks + c / p.sub) * D * D;
+                for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
+                if (p.sub > 1 && p.loss == 1) {
+                    for (int e = tid; e < D * CB; e += 256) S[e / CB][e % CB] = W[e / CB][e % CB];
+                    lds_barrier();
+                }
+            }
+            const float(*Sm)[CB + 1] = p.sub > 1 ? S : W;  // the residuals read the chunk-start state
             const float(*Kc)[KP] = Ks[buf][m];
             const float(*Vc)[TP] = Vt[buf][m];
             const float(*Uc)[TP] = Vc;
-            if (p.loss == 1) {  // U = V - K W
+            if (p.loss == 1) {  // U = V - K W_c
                 for (int e = tid; e < B * CB; e += 256) {
                     const int i = e / CB, j = e % CB;
                     float sacc = 0.f;
@@ -140,7 +154,7 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
                     for (int a = 0; a < D; a += 4) {
                         const f32x4 kv = lds4(&Kc[i][a]);
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) sacc += kv[x] * W[a + x][j];
+                        for (int x = 0; x < 4; ++x) sacc += kv[x] * Sm[a + x][j];
                     }
                     Ut[j][i] = Vc[j][i] - sacc;
                 }
@@ -180,10 +194,7 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 // Parallel pass 2, one workgroup per (head, chunk): every term that does not
 // need G.  Writes dQ, d_eta's first part and the chunk's U, S~, dK part, R_c.
 template <int D, int B, typename E>
-// Three waves per SIMD (three workgroups per CU at d = 64, chunk 16; the LDS
-// allows it): the register cap costs a few spilled values and still measured
-// ~3.5% faster on the whole backward than two waves per SIMD.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void lbw_local(LinBwdParams p)
+__device__ __forceinline__ void lbw_local_body(const LinBwdParams &p)
 {
     __shared__ float Wc[D][D + 1];
     // token rows padded to D + 4 floats: 16-byte aligned, so the loops below read
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     }
     if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
     __syncthreads();
-    const long row0 = (long)h * p.nchunks * B + (long)c * B;  // this chunk's rows in the per-token buffers
+    const long row0 = (long)h * p.rstride + (long)c * B;  // this chunk's rows in the per-token buffers
     if (p.loss == 1) {
         float u[NBD];
         {
@@ -350,6 +361,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     }
 }
 
+template <int D, int B, typename E>
+__global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
+{
+    lbw_local_body<D, B, E>(p);
+}
+
+// d = 64, chunk 16: three waves per SIMD (three workgroups per CU; the LDS
+// allows it).  The register cap costs a few spilled values (10 VGPRs) and
+// still measured ~3.5% faster on the whole backward than two waves per SIMD.
+// The other shapes keep the compiler's own occupancy (at d = 128 the LDS
+// allows one workgroup per CU, so a cap would only cost registers).
+template <typename E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void lbw_local_w3(LinBwdParams p)
+{
+    lbw_local_body<64, 16, E>(p);
+}
+
 // Serial pass 3 (one workgroup per (head, 16 columns of G); G's columns never
 // mix either): G_c = G_{c+1} + R_c [- K^T H K G_{c+1}], storing every G_{c+1};
 // the last G is d_w_init.  Chunks run last to first, in batches as above.
@@ -361,23 +389,27 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
     // to B + 4: both dot products read four consecutive elements at a time
     constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
     __shared__ float G[D][CB + 1];
+    __shared__ float Gs[D][CB + 1];  // G at the end of the current chunk (sub > 1)
     __shared__ __align__(16) float KGt[CB][TP];
     __shared__ float Rs[2][NB][D][CB + 1];
     __shared__ __align__(16) float Ks[2][NB][B][KP];
     __shared__ float et[2][NB][B];
     const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
-    const int last = p.nchunks - 1;
-    const int nbat = (p.nchunks + NB - 1) / NB;
+    const int last = p.ntiles - 1;
+    const int nbat = (p.ntiles + NB - 1) / NB;
+    // the first tile of a chunk in this (reverse) order: its last one
+    auto chunk_end = [&](int c) { return c == last || c % p.sub == p.sub - 1; };
     float pk[NB][NK], pr[NB][NR], pe[NB];
-    auto load = [&](int k) {  // batch k = chunks last - k NB - m, m < NB
+    auto load = [&](int k) {  // batch k = tiles last - k NB - m, m < NB
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
             const int c = last - (k * NB + m);
             const bool ok = c >= 0;
             const int c0 = c * B, n = ok ? min(B, p.T - c0) : 0;
-            const float *R = p.rc + ((long)h * p.nchunks + (ok ? c : 0)) * D * D;
-            const bool hasr = ok && p.order == 0;  // the update-then-apply order has no R_c
+            const float *R = p.rc + ((long)h * p.nchunks + (ok ? c / p.sub : 0)) * D * D;
+            // R_c once per chunk; the update-then-apply order has none
+            const bool hasr = ok && p.order == 0 && chunk_end(c);
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const int e = tid + 256 * r;
@@ -417,8 +449,15 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
         for (int m = 0; m < NB; ++m) {
             const int c = last - (k * NB + m);
             if (c < 0) break;
-            float *gdst = p.gnext + ((long)h * p.nchunks + c) * D * D;
-            for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+            if (chunk_end(c)) {  // G = G_{c+1} of this chunk: store it (and snapshot it)
+                float *gdst = p.gnext + ((long)h * p.nchunks + c / p.sub) * D * D;
+                for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+                if (p.sub > 1 && p.loss == 1) {
+                    for (int e = tid; e < D * CB; e += 256) Gs[e / CB][e % CB] = G[e / CB][e % CB];
+                    lds_barrier();
+                }
+            }
+            const float(*Gm)[CB + 1] = p.sub > 1 ? Gs : G;  // every tile of the chunk meets G_{c+1}
             const float(*Kc)[KP] = Ks[buf][m];
             if (p.loss == 1) {
                 for (int e = tid; e < B * CB; e += 256) {
@@ -428,7 +467,7 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
                     for (int a = 0; a < D; a += 4) {
                         const f32x4 kv = lds4(&Kc[i][a]);
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) sacc += kv[x] * G[a + x][j];
+                        for (int x = 0; x < 4; ++x) sacc += kv[x] * Gm[a + x][j];
                     }
                     KGt[j][i] = et[buf][m][i] * sacc;
                 }
@@ -477,11 +516,12 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
     __shared__ __align__(16) float Ks[B][P], Us[B][P], KGs[B][P];
     __shared__ float et[B];
     constexpr int NBD = B * D / 256;
-    const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks, tid = threadIdx.x;
+    // one workgroup per (head, tile); the tile's chunk is c / sub
+    const int h = blockIdx.x / p.ntiles, c = blockIdx.x % p.ntiles, tid = threadIdx.x;
     const long tok0 = (long)h * p.T;
     const int c0 = c * B, n = min(B, p.T - c0);
-    const long cb = ((long)h * p.nchunks + c);
-    const long row0 = (long)h * p.nchunks * B + (long)c * B;
+    const long cb = ((long)h * p.nchunks + c / p.sub);
+    const long row0 = (long)h * p.rstride + c0;
     for (int e = tid; e < D * D; e += 256) {
         Gn[e / D][e % D] = p.gnext[cb * D * D + e];
         if (p.loss == 1) Wc[e / D][e % D] = p.states[cb * D * D + e];
@@ -583,6 +623,232 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Chunks of more than 32 tokens (causal order).  The chunk's B x B products
+// (A = (Q K^T) * M and dS = (dO U^T) * M) are taken 16 x 16 blocks at a time:
+// one workgroup per (head, 16-token tile I) walks the tiles of its chunk after
+// I (for the columns i of A and dS that I owns: S~, d_eta's first part, the
+// dA^T Q part of dK) and before I (for the rows t it owns: dA K in dQ).  The
+// residuals U of every tile come first (they are read by the other tiles'
+// workgroups), R_c last (a sum over the whole chunk).
+// ---------------------------------------------------------------------------
+constexpr int TT = 16;  // tokens per tile
+
+// U = V - K W_c for one tile (MSE), into the per-token buffer.
+template <int D, typename E>
+__global__ __launch_bounds__(256) void lbw_u(LinBwdParams p)
+{
+    __shared__ float Wc[D][D + 1];
+    __shared__ __align__(16) float Ks[TT][D + 4];
+    const int h = blockIdx.x / p.ntiles, t = blockIdx.x % p.ntiles, tid = threadIdx.x;
+    const long tok0 = (long)h * p.T;
+    const int c0 = t * TT, n = min(TT, p.T - c0);
+    const float *src = p.states + ((long)h * p.nchunks + t / p.sub) * D * D;
+    for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
+    for (int e = tid; e < TT * D; e += 256) {
+        const int i = e / D, a = e % D;
+        Ks[i][a] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
+    }
+    __syncthreads();
+    const long row0 = (long)h * p.rstride + c0;
+    for (int e = tid; e < TT * D; e += 256) {
+        const int i = e / D, j = e % D;
+        float sacc = 0.f;
+#pragma unroll 4
+        for (int a = 0; a < D; a += 4) {
+            const f32x4 kv = lds4(&Ks[i][a]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sacc += kv[x] * Wc[a + x][j];
+        }
+        const float v = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f;
+        p.ub[(row0 + i) * D + j] = v - sacc;
+    }
+}
+
+// Everything of tile I that needs no G: dQ, d_eta's first part, S~ and the
+// G-free part of dK (as lbw_local does for a whole chunk).
+template <int D, typename E>
+__global__ __launch_bounds__(256) void lbw_local_tiled(LinBwdParams p)
+{
+    constexpr int P = D + 4, RS = 256 / D, NR = TT / RS;  // thread outputs (i0 + RS r, j)
+    __shared__ float Wc[D][D + 1];
+    __shared__ __align__(16) float QI[TT][P], KI[TT][P], UI[TT][P], dOI[TT][P], XJ[TT][P], YJ[TT][P];
+    __shared__ float Am[TT][TT + 1], dAm[TT][TT + 1];
+    __shared__ float etI[TT], etJ[TT];
+    const int h = blockIdx.x / p.ntiles, I = blockIdx.x % p.ntiles, tid = threadIdx.x;
+    const long tok0 = (long)h * p.T;
+    const int cI = I / p.sub;
+    const int J0 = cI * p.sub, J1 = min(p.ntiles, J0 + p.sub);  // the chunk's tiles [J0, J1)
+    const int c0 = I * TT, n = min(TT, p.T - c0);
+    const long row0 = (long)h * p.rstride;  // the head's rows in the per-token buffers
+    const bool mse = p.loss == 1;
+    const float *src = p.states + ((long)h * p.nchunks + cI) * D * D;
+    for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
+    for (int e = tid; e < TT * D; e += 256) {
+        const int i = e / D, a = e % D;
+        const bool ok = i < n;
+        const long g = (tok0 + c0 + i) * D + a;
+        QI[i][a] = ok ? ldf<E>(p.q, g) : 0.f;
+        KI[i][a] = ok ? ldf<E>(p.k, g) : 0.f;
+        dOI[i][a] = ok ? ldf<E>(p.dout, g) : 0.f;
+        UI[i][a] = mse ? p.ub[(row0 + c0 + i) * D + a] : (ok ? ldf<E>(p.v, g) : 0.f);
+    }
+    if (tid < TT) etI[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
+    const int i0 = tid / D, j = tid % D;
+    float sv[NR], dk[NR], dq[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) sv[r] = dk[r] = dq[r] = 0.f;
+    float de = 0.f;  // d_eta's first part for row tid (< TT)
+    __syncthreads();
+    // the chunk's tiles J >= I: A[t][i] = q_t . k_i, dS[t][i] = dO_t . u_i (t in J, i in I, t >= i)
+    for (int J = I; J < J1; ++J) {
+        const int cj = J * TT, nj = min(TT, p.T - cj);
+        for (int e = tid; e < TT * D; e += 256) {
+            const int t = e / D, a = e % D;
+            const bool ok = t < nj;
+            XJ[t][a] = ok ? ldf<E>(p.q, (tok0 + cj + t) * D + a) : 0.f;
+            YJ[t][a] = ok ? ldf<E>(p.dout, (tok0 + cj + t) * D + a) : 0.f;
+        }
+        __syncthreads();
+        {
+            const int t = tid / TT, i = tid % TT;  // one (t, i) pair per thread
+            float sa = 0.f, sd = 0.f;
+            if (J > I || t >= i) {
+#pragma unroll 4
+                for (int a = 0; a < D; a += 4) {
+                    const f32x4 x = lds4(&XJ[t][a]), y = lds4(&YJ[t][a]);
+                    const f32x4 kk = lds4(&KI[i][a]), u = lds4(&UI[i][a]);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        sa += x[z] * kk[z];
+                        sd += y[z] * u[z];
+                    }
+                }
+            }
+            Am[t][i] = sa;
+            dAm[t][i] = sd;
+        }
+        __syncthreads();
+        if (tid < TT)
+            for (int t = 0; t < TT; ++t) de += dAm[t][tid] * Am[t][tid];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int i = i0 + RS * r;
+            float s1 = 0.f, s2 = 0.f;
+            for (int t = 0; t < TT; ++t) {
+                s1 += Am[t][i] * YJ[t][j];   // S~ (before eta)
+                s2 += dAm[t][i] * XJ[t][j];  // dA^T Q (before eta)
+            }
+            sv[r] += s1;
+            dk[r] += s2;
+        }
+        __syncthreads();
+    }
+    // the chunk's tiles J <= I: dA[t][s] = eta_s dO_t . u_s (t in I, s in J, s <= t)
+    for (int J = J0; J <= I; ++J) {
+        const int cj = J * TT, nj = min(TT, p.T - cj);
+        for (int e = tid; e < TT * D; e += 256) {
+            const int t = e / D, a = e % D;
+            const bool ok = t < nj;
+            XJ[t][a] = mse ? p.ub[(row0 + cj + t) * D + a] : (ok ? ldf<E>(p.v, (tok0 + cj + t) * D + a) : 0.f);
+            YJ[t][a] = ok ? ldf<E>(p.k, (tok0 + cj + t) * D + a) : 0.f;
+        }
+        if (tid < TT) etJ[tid] = tid < nj ? p.eta[tok0 + cj + tid] : 0.f;
+        __syncthreads();
+        {
+            const int t = tid / TT, s2 = tid % TT;
+            float sd = 0.f;
+            if (J < I || s2 <= t) {
+#pragma unroll 4
+                for (int a = 0; a < D; a += 4) {
+                    const f32x4 y = lds4(&dOI[t][a]), u = lds4(&XJ[s2][a]);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) sd += y[z] * u[z];
+                }
+            }
+            dAm[t][s2] = sd * etJ[s2];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int t = i0 + RS * r;
+            float s1 = 0.f;
+            for (int s2 = 0; s2 < TT; ++s2) s1 += dAm[t][s2] * YJ[s2][j];
+            dq[r] += s1;
+        }
+        __syncthreads();
+    }
+    // finish: S~ = eta_i (A^T dO), dK part = eta_i (dS^T Q) [- S~ W_c^T], dQ += dO W_c^T
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int i = i0 + RS * r;
+        sv[r] *= etI[i];
+        XJ[i][j] = sv[r];
+        p.st[(row0 + c0 + i) * D + j] = sv[r];
+    }
+    if (tid < TT && tid < n) p.deta[tok0 + c0 + tid] = de;
+    __syncthreads();
+    const int a = j;  // outputs (i0 + RS r, a)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int i = i0 + RS * r;
+        float sq = 0.f, sk = 0.f;
+        for (int jj = 0; jj < D; ++jj) {
+            const float w = Wc[a][jj];
+            sq += dOI[i][jj] * w;
+            if (mse) sk += XJ[i][jj] * w;
+        }
+        if (i < n) stf<E>(p.dq, (tok0 + c0 + i) * D + a, dq[r] + sq);
+        p.dkl[(row0 + c0 + i) * D + a] = etI[i] * dk[r] - sk;
+    }
+}
+
+// R_c = Q^T dO [- K^T S~] over a whole chunk, one workgroup per (head,
+// chunk, 16 columns), tokens in tiles of 32.
+template <int D, typename E>
+__global__ __launch_bounds__(256) void lbw_rc(LinBwdParams p)
+{
+    constexpr int NCB = D / CB, NR = D * CB / 256, TK = 32;
+    __shared__ float Qs[TK][D + 1], Ks[TK][D + 1], dOs[TK][CB + 1], Ss[TK][CB + 1];
+    const int h = blockIdx.x / (p.nchunks * NCB), rem = blockIdx.x % (p.nchunks * NCB);
+    const int c = rem / NCB, j0 = (rem % NCB) * CB, tid = threadIdx.x;
+    const long tok0 = (long)h * p.T, row0 = (long)h * p.rstride;
+    const int chunk = p.sub * TT;
+    const int t0 = c * chunk, t1 = min(p.T, t0 + chunk);
+    const bool mse = p.loss == 1;
+    const int jj = tid % CB, ab = tid / CB;  // outputs (ab + 16 r, j0 + jj)
+    float acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+    for (int s = t0; s < t1; s += TK) {
+        const int n = min(TK, t1 - s);
+        for (int e = tid; e < TK * D; e += 256) {
+            const int t = e / D, a = e % D;
+            const bool ok = t < n;
+            Qs[t][a] = ok ? ldf<E>(p.q, (tok0 + s + t) * D + a) : 0.f;
+            Ks[t][a] = (ok && mse) ? ldf<E>(p.k, (tok0 + s + t) * D + a) : 0.f;
+        }
+        for (int e = tid; e < TK * CB; e += 256) {
+            const int t = e / CB, q = e % CB;
+            const bool ok = t < n;
+            dOs[t][q] = ok ? ldf<E>(p.dout, (tok0 + s + t) * D + j0 + q) : 0.f;
+            Ss[t][q] = (ok && mse) ? p.st[(row0 + s + t) * D + j0 + q] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int a = ab + (256 / CB) * r;
+            float x = 0.f;
+            for (int t = 0; t < TK; ++t) x += Qs[t][a] * dOs[t][jj] - Ks[t][a] * Ss[t][jj];
+            acc[r] += x;
+        }
+        __syncthreads();
+    }
+    float *R = p.rc + ((long)h * p.nchunks + c) * D * D;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) R[(long)(ab + (256 / CB) * r) * D + j0 + jj] = acc[r];
+}
+
 // Update-then-apply order, the apply's adjoint: G_final = dW_final + Q^T dO
 // (one workgroup per (head, 16 columns), queries in tiles of 64) ...
 template <int D, typename E>
@@ -665,13 +931,36 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
     const dim3 b(256);
     lbw_states<D, B, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
     if (p.order == 0) {
-        lbw_local<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        if constexpr (D == 64 && B == 16)
+            lbw_local_w3<E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        else
+            lbw_local<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
     } else {
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_grad<D, B, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
-    lbw_dep<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+    lbw_dep<D, B, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
+}
+
+// Chunks of 16 k tokens (k > 1, or d = 128 with 32): the serial and dependent
+// passes step over 16-token tiles (snapshotting the chunk-start state and
+// G_{c+1}), the G-free terms run tile against tile.
+template <int D, typename E>
+static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
+{
+    const dim3 b(256);
+    lbw_states<D, TT, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    if (p.order == 0) {
+        if (p.loss == 1) lbw_u<D, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
+        lbw_local_tiled<D, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
+        lbw_rc<D, E><<<dim3(NH * p.nchunks * (D / CB)), b, 0, st>>>(p);
+    } else {
+        lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+        if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
+    }
+    lbw_grad<D, TT, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    lbw_dep<D, TT, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
 }
 
 hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
@@ -687,15 +976,31 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
     LinBwdParams p{q, k, v, dout, eta, w0, dwf, dq, dk, dv, deta, dw0, base, base + dd,
                    base + 2 * dd, base + 3 * dd, base + 3 * dd + bd, base + 3 * dd + 2 * bd, Tkv,
                    nch, loss, order, Tq, tail, tail + (size_t)NH * d * d};
-    if (d == 128) {  // chunk 16 only (LDS of the dependent pass)
-        if (bf16) lbw_run<128, 16, __bf16>(p, NH, st);
-        else lbw_run<128, 16, float>(p, NH, st);
-    } else if (chunk == 16) {
-        if (bf16) lbw_run<64, 16, __bf16>(p, NH, st);
-        else lbw_run<64, 16, float>(p, NH, st);
-    } else {
-        if (bf16) lbw_run<64, 32, __bf16>(p, NH, st);
-        else lbw_run<64, 32, float>(p, NH, st);
+    p.rstride = (long)nch * chunk;
+    const bool whole = (d == 64 && (chunk == 16 || chunk == 32)) || (d == 128 && chunk == 16);
+    if (whole) {  // a chunk is one step of the serial passes
+        p.sub = 1;
+        p.ntiles = nch;
+        if (d == 128) {
+            if (bf16) lbw_run<128, 16, __bf16>(p, NH, st);
+            else lbw_run<128, 16, float>(p, NH, st);
+        } else if (chunk == 16) {
+            if (bf16) lbw_run<64, 16, __bf16>(p, NH, st);
+            else lbw_run<64, 16, float>(p, NH, st);
+        } else {
+            if (bf16) lbw_run<64, 32, __bf16>(p, NH, st);
+            else lbw_run<64, 32, float>(p, NH, st);
+        }
+    } else {  // chunk = 16 sub tokens
+        p.sub = chunk / TT;
+        p.ntiles = (Tkv + TT - 1) / TT;
+        if (d == 128) {
+            if (bf16) lbw_run_tiled<128, __bf16>(p, NH, st);
+            else lbw_run_tiled<128, float>(p, NH, st);
+        } else {
+            if (bf16) lbw_run_tiled<64, __bf16>(p, NH, st);
+            else lbw_run_tiled<64, float>(p, NH, st);
+        }
     }
     return hipGetLastError();
 }

@@ -257,9 +257,9 @@ ttt_status ttt_linear_decode(const void *q, const void *k, const void *v, int dt
  * (the chunk-start states are recomputed by a forward pass into the
  * workspace).  Tq == Tkv for TTT_CAUSAL; Tkv >= 1; Tq may be 0 (q, d_out and
  * d_q are then not read and may be NULL) in the non-causal order.
- * Supported: d = 64 with chunk 16 or 32, d = 128 with chunk 16 (ragged tails
- * included); dtype TTT_F32 or TTT_BF16.  Others: TTT_EUNSUPPORTED.  Outputs
- * must not overlap the inputs.
+ * Supported: the forward's shapes, d = 64 or 128 with chunk a multiple of 16
+ * (ragged tails included); dtype TTT_F32 or TTT_BF16.  Others:
+ * TTT_EUNSUPPORTED.  Outputs must not overlap the inputs.
  * ------------------------------------------------------------------------ */
 size_t ttt_linear_bwd_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int chunk, int loss,
                                       int order, int dtype);

@@ -93,3 +93,39 @@ def test_bwd_d128(loss, order):
     """Head dim 128 (chunk 16), both orders, ragged key/value length."""
     run_case(1, 2, 150, 16, loss, "bf16", seed=180 + loss + order, order=order,
              Tq=150 if order == 0 else 40, d=128)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_d128_f32_and_bf16_chunk16(dtype):
+    """Head dim 128, chunk 16, MSE, ragged key/value length, in fp32 (held to
+    1e-4 normwise) as well as bf16."""
+    run_case(1, 2, 150, 16, 1, dtype, seed=185, d=128)
+
+
+# Chunks of 16 k tokens beyond the whole-chunk kernels: the serial passes step
+# over 16-token tiles against the chunk-start state, the G-free terms run tile
+# against tile.
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [48, 64, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_large_chunks(loss, chunk, dtype):
+    """d = 64, several chunks and a ragged tail (T = 300)."""
+    run_case(1, 2, 300, chunk, loss, dtype, seed=190 + chunk + loss)
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("chunk", [32, 64, 1024])
+def test_bwd_d128_large_chunks(loss, order, chunk):
+    """d = 128 (chunk 32 upward runs the tiled kernels), both orders; chunk
+    1024 over 1100 tokens is one whole chunk and a 76-token tail."""
+    T = 1100 if chunk == 1024 else 200
+    run_case(1, 2, T, chunk, loss, "bf16", seed=200 + chunk + loss + order, order=order,
+             Tq=T if order == 0 else 60, d=128)
+
+
+@pytest.mark.parametrize("chunk", [64, 256, 1024])
+def test_bwd_d128_sweep_shape_sampled_heads(chunk):
+    """The chunk-size sweep's shape (B2 H16 T16384 d128, MSE, bf16) at chunks
+    64, 256 and 1024; heads 0 and 31 against the oracle."""
+    run_case(2, 16, 16384, chunk, 1, "bf16", seed=210 + chunk, heads=[0, 31], d=128)
