@@ -53,6 +53,12 @@ struct LinBwdParams {
     // rstride = nchunks * chunk rows.
     int sub, ntiles;
     long rstride;
+    // Segments of the serial passes: nseg runs of seg_chunks chunks (the last
+    // may be shorter) per head.  ssum: [NH][nseg][D][2D], each segment's affine
+    // map as [linear part | offset]; sstart: [NH][nseg][D][D], each segment's
+    // start state (states) or end adjoint (G).
+    int nseg, seg_chunks;
+    float *ssum, *sstart;
 };
 
 template <typename E> __device__ __forceinline__ float ldf(const void *p, long i)
@@ -72,17 +78,32 @@ __device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast
 // Serial passes: the operands of NB chunks at a time are loaded into registers
 // while the previous NB chunks compute out of LDS, and written to LDS once per
 // batch, so no chunk step waits for memory (a step only reads LDS and stores).
+// Small batches keep the LDS small enough for several workgroups per CU.
 template <int D, int B> struct Batch {
-    static constexpr int NB = (B <= 16 ? 8 : 4) * 64 / D;  // LDS: two batches of K and V / R_c
+    static constexpr int NB = 2;  // LDS: two batches of K and V / R_c
 };
 
-// Serial pass 1 (one workgroup per (head, 16 state columns); columns of the
-// state never mix in the recursion W_{c+1} = W_c + K^T H (V - K W_c)):
-// writes every chunk-start state.
+// Both serial recursions are affine in their d x d matrix, chunk by chunk:
+//   states  W_{c+1} = (I - K^T H K) W_c + K^T H V,
+//   G       G_c     = (I - K^T H K) G_{c+1} + R_c,
+// and neither mixes the matrix's columns.  So a segment of chunks is one
+// affine map X -> L X + F; its two parts come out of the same walk started
+// from the identity without the inputs (L) or from zero with them (F).  Three
+// steps per recursion: the maps of all segments in parallel (mode 1, one
+// workgroup per (head, segment, 16 columns of [L | F])), the chain of the
+// maps per (head, 16 columns) (lbw_chain), and the walk of every segment from
+// its own start (mode 0, per (head, segment, 16 columns)), which stores what
+// the parallel passes read.
+
+// Walk of the state recursion over one segment (one workgroup per (head,
+// segment, 16 columns)).  mode 0: from the segment's start state, storing
+// every chunk-start state (and the final state in the update-then-apply
+// order); mode 1: the segment's map, columns [0, D) the linear part (from the
+// identity, V = 0), [D, 2D) the offset (from zero).
 template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_states(LinBwdParams p, int mode)
 {
-    constexpr int NB = Batch<D, B>::NB, NCB = D / CB, NK = B * D / 256, NV = B * CB / 256;
+    constexpr int NB = Batch<D, B>::NB, NK = B * D / 256, NV = B * CB / 256;
     // K rows padded to D + 4 floats; V and U stored transposed (token index
     // last), rows padded to B + 4: the dot products read four elements at a time
     constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
@@ -92,15 +113,24 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
     __shared__ __align__(16) float et[2][NB][B];
     __shared__ __align__(16) float Ut[CB][TP];
     __shared__ float S[D][CB + 1];  // chunk-start state (sub > 1): the residuals' snapshot
-    const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
+    const int ncol = (mode == 1 ? 2 : 1) * (D / CB);
+    const int nsl = mode == 1 ? p.nseg - 1 : p.nseg;  // the last segment's map is never needed
+    int bid = blockIdx.x;
+    const int cbk = bid % ncol;
+    bid /= ncol;
+    const int seg = bid % nsl, h = bid / nsl, tid = threadIdx.x;
+    const bool lin = mode == 1 && cbk < D / CB;  // the map's linear part: no V
+    const int j0 = (cbk % (D / CB)) * CB;
     const long tok0 = (long)h * p.T;
-    const int nbat = (p.ntiles + NB - 1) / NB;
+    const int ca = seg * p.seg_chunks, cb = min(p.nchunks, ca + p.seg_chunks);
+    const int ta = ca * p.sub, tb = min(cb * p.sub, p.ntiles);  // the segment's tiles
+    const int nbat = (tb - ta + NB - 1) / NB;
     float pk[NB][NK], pv[NB][NV], pe[NB];
     auto load = [&](int k) {
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
-            const int c = k * NB + m;
-            const int c0 = c * B, n = c < p.ntiles ? min(B, p.T - c0) : 0;
+            const int c = ta + k * NB + m;
+            const int c0 = c * B, n = c < tb ? min(B, p.T - c0) : 0;
 #pragma unroll
             for (int r = 0; r < NK; ++r) {
                 const int e = tid + 256 * r, i = e / D, a = e % D;
@@ -109,7 +139,7 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
                 const int e = tid + 256 * r, i = e / CB, j = e % CB;
-                pv[m][r] = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j0 + j) : 0.f;
+                pv[m][r] = (i < n && !lin) ? ldf<E>(p.v, (tok0 + c0 + i) * D + j0 + j) : 0.f;
             }
             pe[m] = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
         }
@@ -124,7 +154,15 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
             if (tid < B) et[buf][m][tid] = pe[m];
         }
     };
-    for (int e = tid; e < D * CB; e += 256) W[e / CB][e % CB] = p.w0[(long)h * D * D + (e / CB) * D + j0 + e % CB];
+    {
+        const float *w = mode == 1 ? nullptr
+                         : seg == 0 ? p.w0 + (long)h * D * D
+                                    : p.sstart + ((long)h * p.nseg + seg) * D * D;
+        for (int e = tid; e < D * CB; e += 256) {
+            const int a = e / CB, j = e % CB;
+            W[a][j] = w ? w[(long)a * D + j0 + j] : (lin && a == j0 + j ? 1.f : 0.f);
+        }
+    }
     load(0);
     store(0);
     __syncthreads();
@@ -132,11 +170,13 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
         const int buf = k & 1;
         if (k + 1 < nbat) load(k + 1);
         for (int m = 0; m < NB; ++m) {
-            const int c = k * NB + m;
-            if (c >= p.ntiles) break;
+            const int c = ta + k * NB + m;
+            if (c >= tb) break;
             if (c % p.sub == 0) {  // a chunk starts: store its state (and snapshot it)
-                float *dst = p.states + ((long)h * p.nchunks + c / p.sub) * D * D;
-                for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
+                if (mode == 0) {
+                    float *dst = p.states + ((long)h * p.nchunks + c / p.sub) * D * D;
+                    for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
+                }
                 if (p.sub > 1 && p.loss == 1) {
                     for (int e = tid; e < D * CB; e += 256) S[e / CB][e % CB] = W[e / CB][e % CB];
                     lds_barrier();
@@ -187,8 +227,54 @@ __global__ __launch_bounds__(256) void lbw_states(LinBwdParams p)
             __syncthreads();
         }
     }
-    if (p.order == 1)
+    if (mode == 1) {
+        float *dst = p.ssum + ((long)h * p.nseg + seg) * D * 2 * D + (lin ? 0 : D) + j0;
+        for (int e = tid; e < D * CB; e += 256) dst[(long)(e / CB) * 2 * D + e % CB] = W[e / CB][e % CB];
+    } else if (p.order == 1 && seg == p.nseg - 1) {
         for (int e = tid; e < D * CB; e += 256) p.wfinal[(long)h * D * D + (e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
+    }
+}
+
+// The chain of the segment maps, one workgroup per (head, 16 columns):
+// dir 0 (states): X_0 = w_init, X_{s+1} = L_s X_s + F_s, storing X_s for s >= 1;
+// dir 1 (G): X_{S-1} = g0 (d_w_final, or the apply's G in the update-then-apply
+// order, or zero), X_{s-1} = L_s X_s + F_s, storing X_s for s <= S - 2.
+template <int D>
+__global__ __launch_bounds__(256) void lbw_chain(LinBwdParams p, int dir)
+{
+    constexpr int NE = D * CB / 256;
+    __shared__ float L[D][D + 1];
+    __shared__ float X[D][CB + 1];
+    const int h = blockIdx.x / (D / CB), j0 = (blockIdx.x % (D / CB)) * CB, tid = threadIdx.x;
+    const int S = p.nseg;
+    const float *x0 = dir == 0 ? p.w0 : (p.order == 1 ? p.ginit : p.dwf);
+    for (int e = tid; e < D * CB; e += 256)
+        X[e / CB][e % CB] = x0 ? x0[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
+    const int j = tid % CB, ab = tid / CB;  // outputs (ab + 16 r, j)
+    for (int t = 0; t < S - 1; ++t) {
+        const int s = dir == 0 ? t : S - 1 - t;       // the map applied
+        const int o = dir == 0 ? s + 1 : s - 1;       // the segment whose start it gives
+        const float *M = p.ssum + ((long)h * S + s) * D * 2 * D;
+        for (int e = tid; e < D * D; e += 256) L[e / D][e % D] = M[(long)(e / D) * 2 * D + e % D];
+        __syncthreads();
+        float acc[NE];
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+            const int a = ab + (256 / CB) * r;
+            float x = M[(long)a * 2 * D + D + j0 + j];
+            for (int q = 0; q < D; ++q) x += L[a][q] * X[q][j];
+            acc[r] = x;
+        }
+        __syncthreads();
+        float *dst = p.sstart + ((long)h * S + o) * D * D;
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+            const int a = ab + (256 / CB) * r;
+            X[a][j] = acc[r];
+            dst[(long)a * D + j0 + j] = acc[r];
+        }
+        __syncthreads();
+    }
 }
 
 // Parallel pass 2, one workgroup per (head, chunk): every term that does not
@@ -378,13 +464,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     lbw_local_body<64, 16, E>(p);
 }
 
-// Serial pass 3 (one workgroup per (head, 16 columns of G); G's columns never
-// mix either): G_c = G_{c+1} + R_c [- K^T H K G_{c+1}], storing every G_{c+1};
-// the last G is d_w_init.  Chunks run last to first, in batches as above.
+// Walk of the G recursion over one segment, last chunk first (one workgroup per
+// (head, segment, 16 columns)): G_c = G_{c+1} + R_c [- K^T H K G_{c+1}].  mode
+// 0: from the segment's end adjoint, storing every G_{c+1} (and d_w_init at
+// the start of the first segment); mode 1: the segment's map (segments 1 ..
+// S-1), columns [0, D) the linear part (from the identity, no R_c), [D, 2D)
+// the offset (from zero).
 template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p, int mode)
 {
-    constexpr int NB = Batch<D, B>::NB, NCB = D / CB, NK = B * D / 256, NR = D * CB / 256;
+    constexpr int NB = Batch<D, B>::NB, NK = B * D / 256, NR = D * CB / 256;
     // K rows padded to D + 4 floats and (H K G) stored transposed, rows padded
     // to B + 4: both dot products read four consecutive elements at a time
     constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
@@ -394,22 +483,30 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
     __shared__ float Rs[2][NB][D][CB + 1];
     __shared__ __align__(16) float Ks[2][NB][B][KP];
     __shared__ float et[2][NB][B];
-    const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
+    const int ncol = (mode == 1 ? 2 : 1) * (D / CB);
+    const int nsl = mode == 1 ? p.nseg - 1 : p.nseg;  // maps of segments 1 .. S-1
+    int bid = blockIdx.x;
+    const int cbk = bid % ncol;
+    bid /= ncol;
+    const int seg = bid % nsl + (mode == 1 ? 1 : 0), h = bid / nsl, tid = threadIdx.x;
+    const bool lin = mode == 1 && cbk < D / CB;  // the map's linear part: no R_c
+    const int j0 = (cbk % (D / CB)) * CB;
     const long tok0 = (long)h * p.T;
-    const int last = p.ntiles - 1;
-    const int nbat = (p.ntiles + NB - 1) / NB;
+    const int ca = seg * p.seg_chunks, cbe = min(p.nchunks, ca + p.seg_chunks);
+    const int ta = ca * p.sub, last = min(cbe * p.sub, p.ntiles) - 1;  // the segment's tiles [ta, last]
+    const int nbat = (last - ta + 1 + NB - 1) / NB;
     // the first tile of a chunk in this (reverse) order: its last one
-    auto chunk_end = [&](int c) { return c == last || c % p.sub == p.sub - 1; };
+    auto chunk_end = [&](int c) { return c == p.ntiles - 1 || c % p.sub == p.sub - 1; };
     float pk[NB][NK], pr[NB][NR], pe[NB];
     auto load = [&](int k) {  // batch k = tiles last - k NB - m, m < NB
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
             const int c = last - (k * NB + m);
-            const bool ok = c >= 0;
+            const bool ok = c >= ta;
             const int c0 = c * B, n = ok ? min(B, p.T - c0) : 0;
             const float *R = p.rc + ((long)h * p.nchunks + (ok ? c / p.sub : 0)) * D * D;
             // R_c once per chunk; the update-then-apply order has none
-            const bool hasr = ok && p.order == 0 && chunk_end(c);
+            const bool hasr = ok && !lin && p.order == 0 && chunk_end(c);
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const int e = tid + 256 * r;
@@ -437,9 +534,16 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
             }
         }
     };
-    const float *g0 = p.order == 1 ? p.ginit : p.dwf;
-    for (int e = tid; e < D * CB; e += 256)
-        G[e / CB][e % CB] = g0 ? g0[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
+    {
+        const float *g0 = p.order == 1 ? p.ginit : p.dwf;  // null: zero
+        const float *g = mode == 1 ? nullptr
+                         : seg == p.nseg - 1 ? (g0 ? g0 + (long)h * D * D : nullptr)
+                                             : p.sstart + ((long)h * p.nseg + seg) * D * D;
+        for (int e = tid; e < D * CB; e += 256) {
+            const int a = e / CB, j = e % CB;
+            G[a][j] = g ? g[(long)a * D + j0 + j] : (lin && a == j0 + j ? 1.f : 0.f);
+        }
+    }
     load(0);
     store(0);
     __syncthreads();
@@ -448,10 +552,12 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
         if (k + 1 < nbat) load(k + 1);
         for (int m = 0; m < NB; ++m) {
             const int c = last - (k * NB + m);
-            if (c < 0) break;
+            if (c < ta) break;
             if (chunk_end(c)) {  // G = G_{c+1} of this chunk: store it (and snapshot it)
-                float *gdst = p.gnext + ((long)h * p.nchunks + c / p.sub) * D * D;
-                for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+                if (mode == 0) {
+                    float *gdst = p.gnext + ((long)h * p.nchunks + c / p.sub) * D * D;
+                    for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+                }
                 if (p.sub > 1 && p.loss == 1) {
                     for (int e = tid; e < D * CB; e += 256) Gs[e / CB][e % CB] = G[e / CB][e % CB];
                     lds_barrier();
@@ -501,7 +607,12 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p)
         }
     }
     __syncthreads();
-    for (int e = tid; e < D * CB; e += 256) p.dw0[(long)h * D * D + (e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+    if (mode == 1) {
+        float *dst = p.ssum + ((long)h * p.nseg + seg) * D * 2 * D + (lin ? 0 : D) + j0;
+        for (int e = tid; e < D * CB; e += 256) dst[(long)(e / CB) * 2 * D + e % CB] = G[e / CB][e % CB];
+    } else if (seg == 0) {
+        for (int e = tid; e < D * CB; e += 256) p.dw0[(long)h * D * D + (e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+    }
 }
 
 // Parallel pass 4, one workgroup per (head, chunk): the terms that need
@@ -916,20 +1027,74 @@ __global__ __launch_bounds__(256) void lbw_nc_dq(LinBwdParams p)
 
 }  // namespace
 
+// Segments of the serial passes.  A walk step costs about the same in every
+// workgroup, and a CU holds three (d = 64) or two (d = 128) of them, so the
+// time goes as the segment length times the rounds of workgroups the maps
+// (2 NH (S - 1) d / 16 workgroups) and the walks (NH S d / 16) take; S = 1 is
+// the plain walk.  The smallest estimate wins (ties: fewer segments), with at
+// least 4 chunks (and 64 tokens) per segment.
+static void seg_plan(int NH, int nch, int chunk, int d, int &nseg, int &seg_chunks)
+{
+    const long slots = 256L * (d == 64 ? 3 : 2);
+    const long cols = (long)NH * (d / CB);
+    const int min_chunks = max(4, 64 / chunk);
+    const int most = max(1, min(64, nch / min_chunks));
+    long best = -1;
+    nseg = 1;
+    seg_chunks = nch;
+    for (int s = 1; s <= most; ++s) {
+        const int sc = (nch + s - 1) / s, ns = (nch + sc - 1) / sc;
+        const long rounds = (2 * cols * (ns - 1) + slots - 1) / slots + (cols * ns + slots - 1) / slots;
+        const long est = (long)sc * rounds + 2L * (ns - 1);
+        if (best < 0 || est < best) {
+            best = est;
+            nseg = ns;
+            seg_chunks = sc;
+        }
+    }
+}
+
 size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
 {
     const size_t nch = (Tkv + chunk - 1) / chunk;
+    int nseg = 1, segc = 1;
+    seg_plan(NH, (int)nch, chunk, d, nseg, segc);
     // states, G_{c+1}, R_c (d x d per chunk) and U, S~, dK part (chunk x d per chunk), plus
-    // the final state and dL/dW_final (update-then-apply order), fp32
-    return (size_t)NH * (nch * (3 * (size_t)d * d + 3 * (size_t)chunk * d) + 2 * (size_t)d * d) *
+    // the final state and dL/dW_final (update-then-apply order), plus the
+    // segment maps (d x 2d) and starts (d x d), fp32
+    return (size_t)NH *
+           (nch * (3 * (size_t)d * d + 3 * (size_t)chunk * d) + 2 * (size_t)d * d + (size_t)nseg * 3 * d * d) *
            sizeof(float);
+}
+
+// The two serial recursions, each as segment maps, chain, walks.
+template <int D, int B, typename E>
+static void lbw_serial_states(const LinBwdParams &p, int NH, hipStream_t st)
+{
+    const dim3 b(256);
+    if (p.nseg > 1) {
+        lbw_states<D, B, E><<<dim3(NH * (p.nseg - 1) * 2 * (D / CB)), b, 0, st>>>(p, 1);
+        lbw_chain<D><<<dim3(NH * (D / CB)), b, 0, st>>>(p, 0);
+    }
+    lbw_states<D, B, E><<<dim3(NH * p.nseg * (D / CB)), b, 0, st>>>(p, 0);
+}
+
+template <int D, int B, typename E>
+static void lbw_serial_grad(const LinBwdParams &p, int NH, hipStream_t st)
+{
+    const dim3 b(256);
+    if (p.nseg > 1) {
+        lbw_grad<D, B, E><<<dim3(NH * (p.nseg - 1) * 2 * (D / CB)), b, 0, st>>>(p, 1);
+        lbw_chain<D><<<dim3(NH * (D / CB)), b, 0, st>>>(p, 1);
+    }
+    lbw_grad<D, B, E><<<dim3(NH * p.nseg * (D / CB)), b, 0, st>>>(p, 0);
 }
 
 template <int D, int B, typename E>
 static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
-    lbw_states<D, B, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    lbw_serial_states<D, B, E>(p, NH, st);
     if (p.order == 0) {
         if constexpr (D == 64 && B == 16)
             lbw_local_w3<E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
@@ -939,7 +1104,7 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
-    lbw_grad<D, B, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    lbw_serial_grad<D, B, E>(p, NH, st);
     lbw_dep<D, B, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
 }
 
@@ -950,7 +1115,7 @@ template <int D, typename E>
 static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
-    lbw_states<D, TT, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    lbw_serial_states<D, TT, E>(p, NH, st);
     if (p.order == 0) {
         if (p.loss == 1) lbw_u<D, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
         lbw_local_tiled<D, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
@@ -959,7 +1124,7 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
-    lbw_grad<D, TT, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+    lbw_serial_grad<D, TT, E>(p, NH, st);
     lbw_dep<D, TT, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
 }
 
@@ -977,6 +1142,9 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
                    base + 2 * dd, base + 3 * dd, base + 3 * dd + bd, base + 3 * dd + 2 * bd, Tkv,
                    nch, loss, order, Tq, tail, tail + (size_t)NH * d * d};
     p.rstride = (long)nch * chunk;
+    seg_plan(NH, nch, chunk, d, p.nseg, p.seg_chunks);
+    p.ssum = tail + 2 * (size_t)NH * d * d;
+    p.sstart = p.ssum + (size_t)NH * p.nseg * 2 * d * d;
     const bool whole = (d == 64 && (chunk == 16 || chunk == 32)) || (d == 128 && chunk == 16);
     if (whole) {  // a chunk is one step of the serial passes
         p.sub = 1;

@@ -244,25 +244,41 @@ def test_linear_bwd_validation(kw, code):
     assert lin_bwd(_lib.load(), **kw) == code
 
 
+def _bwd_nseg(NH, nch, chunk, d):
+    """Segments of the backward's serial passes: the count that minimises
+    segment length x (rounds of the 2 NH (S-1) d/16 map workgroups + rounds
+    of the NH S d/16 walk workgroups, 256 x (3 at d = 64, else 2) at a time)
+    + 2 (S - 1), with at least max(4, 64 / chunk) chunks per segment."""
+    slots, cols = 256 * (3 if d == 64 else 2), NH * (d // 16)
+    best, res = None, 1
+    for s in range(1, max(1, min(64, nch // max(4, 64 // chunk))) + 1):
+        sc = -(-nch // s)
+        ns = -(-nch // sc)
+        est = sc * (-(-(2 * cols * (ns - 1)) // slots) + -(-(cols * ns) // slots)) + 2 * (ns - 1)
+        if best is None or est < best:
+            best, res = est, ns
+    return res
+
+
 def test_linear_bwd_workspace_query():
     lib = _lib.load()
-    # per chunk and head: three fp32 d x d matrices (state, G, R) and three chunk x d ones
-    # plus the final state and dL/dW_final per head
-    per = lambda b: (3 * 64 * 64 + 3 * b * 64) * 4
-    tail = 2 * 64 * 64 * 4
-    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 4096, 64, 16, 1, 0, 1) == \
-        32 * (256 * per(16) + tail)
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 64, 32, 0, 0, 0) == 2 * per(32) + tail
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 1, 0) == 2 * per(32) + tail
+    # per chunk and head: three fp32 d x d matrices (state, G, R) and three chunk x d ones;
+    # per head: the final state and dL/dW_final, and per segment a d x 2d map and a d x d start
+    def size(B, H, T, d, b):
+        nch = -(-T // b)
+        NH = B * H
+        return NH * (nch * (3 * d * d + 3 * b * d) + 2 * d * d + _bwd_nseg(NH, nch, b, d) * 3 * d * d) * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 4096, 64, 16, 1, 0, 1) == size(4, 8, 4096, 64, 16)
+    assert _bwd_nseg(32, 256, 16, 64) == 4 and _bwd_nseg(1, 125, 16, 64) == 9
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 64, 32, 0, 0, 0) == size(1, 1, 50, 64, 32)
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 1, 0) == size(1, 1, 50, 64, 32)
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 0, 0) == 0
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 64, 24, 0, 0, 0) == 0
-    per128 = lambda b: (3 * 128 * 128 + 3 * b * 128) * 4
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 32, 0, 0, 0) == \
-        2 * per128(32) + 2 * 128 * 128 * 4
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 32, 0, 0, 0) == size(1, 1, 50, 128, 32)
     assert lib.ttt_linear_bwd_workspace_bytes(2, 16, 16384, 16384, 128, 1024, 1, 0, 1) == \
-        32 * (16 * per128(1024) + 2 * 128 * 128 * 4)
-    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 16, 0, 0, 0) == \
-        4 * per128(16) + 2 * 128 * 128 * 4
+        size(2, 16, 16384, 128, 1024)
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 128, 16, 0, 0, 0) == size(1, 1, 50, 128, 16)
+    assert lib.ttt_linear_bwd_workspace_bytes(1, 2, 2000, 2000, 64, 16, 1, 0, 0) == size(1, 2, 2000, 64, 16)
 
 
 def test_linear_segment_length_argument():

@@ -129,3 +129,17 @@ def test_bwd_d128_sweep_shape_sampled_heads(chunk):
     """The chunk-size sweep's shape (B2 H16 T16384 d128, MSE, bf16) at chunks
     64, 256 and 1024; heads 0 and 31 against the oracle."""
     run_case(2, 16, 16384, chunk, 1, "bf16", seed=210 + chunk, heads=[0, 31], d=128)
+
+
+# The serial recursions in segments (maps in parallel, chain, walks): shapes
+# long enough for many segments per head.
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_many_segments(loss, chunk, dtype):
+    run_case(1, 2, 2000, chunk, loss, dtype, seed=220 + chunk + loss)
+
+
+@pytest.mark.parametrize("loss", [0, 1])
+def test_bwd_many_segments_noncausal_d128(loss):
+    run_case(1, 2, 2000, 16, loss, "f32", seed=230 + loss, order=1, Tq=90, d=128)
