@@ -167,6 +167,66 @@ def measured_peaks():
                       "2048 workgroups x 4 waves x 2048 rounds x 4 products"}
 
 
+def gemm_probe(steps=20, warmup=3):
+    """The LaCT kernels' shared 128 x 128 GEMM tile on plain bf16 products
+    (ttt_probe_gemm_bf16, fp32 out), beside the vendor GEMM behind torch.matmul
+    on the same shapes (bf16 in and out) for context; each checked against an
+    fp32 product of the same bf16 values on a small shape first."""
+    import torch
+    import chunked_linear_attention_amd._lib as L
+    lib = L.load()
+    st = torch.cuda.current_stream()
+
+    def ours(a, b, c, M, N, K, ak, bk):
+        rc = lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk, st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"ttt_probe_gemm_bf16 failed ({rc})")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    out = []
+    for (M, N, K, ak, bk) in [(512, 384, 320, 0, 0), (512, 384, 320, 1, 1), (512, 384, 320, 0, 1)]:
+        a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
+        b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
+        c = torch.empty(M, N, device="cuda")
+        ours(a, b, c, M, N, K, ak, bk)
+        ref = (a.float().t() if ak else a.float()) @ (b.float() if bk else b.float().t())
+        torch.cuda.synchronize()
+        err = float((c - ref).abs().max() / ref.abs().max())
+        if err > 1e-5:
+            raise RuntimeError(f"GEMM tile probe mismatch {err:.2e} at {M}x{N}x{K} ({ak}, {bk})")
+    for (M, N, K, ak, bk, what) in [(4096, 4096, 4096, 0, 0, "square, both operands k-contiguous"),
+                                    (4096, 4096, 4096, 1, 1, "square, both operands k-major"),
+                                    (8192, 8192, 8192, 0, 0, "square 8192, k-contiguous"),
+                                    (16384, 1024, 256, 0, 0, "LaCT key-forward aspect (tokens x hidden x d)"),
+                                    (1024, 512, 32768, 0, 1, "LaCT weight-gradient aspect (hidden x d x tokens)")]:
+        a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
+        b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
+        c = torch.empty(M, N, device="cuda")
+        ms = timed(lambda: ours(a, b, c, M, N, K, ak, bk))
+        at = a.t() if ak else a
+        bt = b if bk else b.t()
+        at, bt = at.contiguous(), bt.contiguous()
+        vms = timed(lambda: torch.matmul(at, bt))
+        fl = 2.0 * M * N * K
+        out.append({"shape": f"{M}x{N}x{K}", "layout": what, "tile_us": ms * 1e3,
+                    "tile_tflops": fl / (ms * 1e-3) / 1e12, "tile_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "vendor_us": vms * 1e3, "vendor_tflops": fl / (vms * 1e-3) / 1e12})
+        del a, b, c, at, bt
+    return out
+
+
 # ----------------------------------------------------------------------------
 def linear_sets(inp, dtype, R_min_bytes):
     import numpy as np
@@ -615,6 +675,8 @@ def main():
                     help="only time the sliding-window attention workload")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode-step workloads (for profiling them alone)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="time the LaCT kernels' shared GEMM tile and the vendor GEMM on plain products")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (scales HBM counters)")
     args = ap.parse_args()
@@ -645,6 +707,9 @@ def main():
                           "lact_rules": bench_lact_rules(args.steps, args.warmup)}), flush=True)
         return
 
+    if args.gemm_probe:
+        print(json.dumps({"gemm_probe": gemm_probe(args.steps, args.warmup)}), flush=True)
+        return
     if args.bwd_only:
         # the headline shape, the d = 128 chunk-size sweep's shape, then LaCT
         bwd = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps, args.warmup)]

@@ -19,7 +19,7 @@ EXPORTS = ("ttt_status_string", "ttt_abi_version", "ttt_linear_workspace_bytes",
            "lact_swiglu_workspace_bytes", "lact_swiglu_fwd", "ttt_linear_decode",
            "lact_swiglu_decode_workspace_bytes", "lact_swiglu_decode",
            "lact_swiglu_rule_workspace_bytes", "lact_swiglu_fwd_rule", "window_attention_fwd",
-           "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd", "ttt_probe_mfma_bf16",
+           "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd", "ttt_probe_mfma_bf16", "ttt_probe_gemm_bf16",
            "ttt_linear_noalloc_max_scratch_bytes", "ttt_linear_fwd_noalloc",
            "lact_swiglu_bwd_workspace_bytes", "lact_swiglu_bwd")
 
@@ -82,6 +82,8 @@ def load() -> ctypes.CDLL:
         lib.lact_swiglu_decode.restype = i
         lib.ttt_probe_mfma_bf16.argtypes = [vp, i, i, vp]
         lib.ttt_probe_mfma_bf16.restype = i
+        lib.ttt_probe_gemm_bf16.argtypes = [vp, vp, vp] + [i] * 5 + [vp]
+        lib.ttt_probe_gemm_bf16.restype = i
         lib.ttt_linear_noalloc_max_scratch_bytes.argtypes = []
         lib.ttt_linear_noalloc_max_scratch_bytes.restype = sz
         lib.ttt_linear_fwd_noalloc.argtypes = [vp, vp, vp, i, vp, vp, vp, vp] + [i] * 8 + [vp]

@@ -1,9 +1,10 @@
-// Measurement helper (not part of the TTT path): a loop of independent bf16
+// Measurement helpers (not part of the TTT path): a loop of independent bf16
 // matrix-core products, from which a benchmark reads the dense bf16 MFMA
 // rate this part reaches, to quote roofline fractions against a measured peak
-// beside the published one.
+// beside the published one; and the LaCT kernels' shared GEMM tile on its own,
+// so its rate can be measured on plain products.
 #include "../../include/ttt.h"
-#include "ttt_device.h"
+#include "lact_common.h"
 
 namespace tttk {
 
@@ -40,7 +41,48 @@ __global__ __launch_bounds__(256) void probe_mfma_loop(float *out, int iters)
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// C[m][n] = sum_k A[m][k] B[n][k] on the shared 128 x 128 tile, fp32 out;
+// one workgroup per output tile.
+template <bool AT, bool BT>
+__global__ __launch_bounds__(256) void probe_gemm_tile(const bf16 *A, const bf16 *B, float *C, int M, int N, int K)
+{
+    __shared__ GemmLds L;
+    const int tn_n = N / 128;
+    const int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int tm = bid / tn_n, tn = bid % tn_n;
+    const bf16 *as[1] = {A}, *bs[1] = {B};
+    gemm_nt_tile<AT, BT>(L, as, AT ? M : K, bs, BT ? N : K, M, N, K, 1, tm * 128, tn * 128, K,
+                         [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+                             for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                 for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                     for (int r = 0; r < 4; ++r)
+                                         C[(long)(mb + 16 * i + 4 * g + r) * N + nb + 16 * q + mm] = acc[i][q][r];
+                         });
+}
+
 }  // namespace tttk
+
+extern "C" ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c, int M, int N, int K, int a_kmajor,
+                                          int b_kmajor, void *stream)
+{
+    if (!a || !b || !c || M < 128 || N < 128 || K < 64 || M % 128 || N % 128 || K % 64) return TTT_EINVAL;
+    if ((long long)(M / 128) * (N / 128) > (1 << 24)) return TTT_EUNSUPPORTED;
+    const dim3 grid((M / 128) * (N / 128)), block(256);
+    const tttk::bf16 *A = (const tttk::bf16 *)a, *B = (const tttk::bf16 *)b;
+    hipStream_t st = (hipStream_t)stream;
+    if (a_kmajor && b_kmajor)
+        tttk::probe_gemm_tile<true, true><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    else if (a_kmajor)
+        tttk::probe_gemm_tile<true, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    else if (b_kmajor)
+        tttk::probe_gemm_tile<false, true><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    else
+        tttk::probe_gemm_tile<false, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    return hipGetLastError() == hipSuccess ? TTT_OK : TTT_EHIP;
+}
 
 extern "C" ttt_status ttt_probe_mfma_bf16(float *out, int blocks, int iters, void *stream)
 {
