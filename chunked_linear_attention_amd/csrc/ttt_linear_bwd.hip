@@ -71,6 +71,7 @@ template <typename E> __device__ __forceinline__ void stf(void *p, long i, float
 }
 
 constexpr int CB = 16;  // state columns per workgroup in the serial passes
+constexpr int DEP_TPW = 8;  // tiles per workgroup of the dependent pass (chunks of several tiles)
 
 // four consecutive floats of an LDS row (16-byte aligned)
 __device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast<const f32x4 *>(x); }
@@ -615,8 +616,9 @@ __global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p, int mode)
     }
 }
 
-// Parallel pass 4, one workgroup per (head, chunk): the terms that need
-// G = G_{c+1}:  KG = K G,  dV = dU = S~ + H KG,
+// Parallel pass 4, one workgroup per (head, chunk), or per (head, group of up
+// to DEP_TPW tiles of a chunk) when chunks are walked in tiles: the terms that
+// need G = G_{c+1}:  KG = K G,  dV = dU = S~ + H KG,
 // dK = part + H (U G^T [- KG Wc^T]),  d_eta += rowsum(KG * U).
 template <int D, int B, typename E>
 __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
@@ -627,110 +629,117 @@ __global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
     __shared__ __align__(16) float Ks[B][P], Us[B][P], KGs[B][P];
     __shared__ float et[B];
     constexpr int NBD = B * D / 256;
-    // one workgroup per (head, tile); the tile's chunk is c / sub
-    const int h = blockIdx.x / p.ntiles, c = blockIdx.x % p.ntiles, tid = threadIdx.x;
+    // one workgroup per (head, chunk, group of up to DEP_TPW of the chunk's
+    // tiles): the chunk's G_{c+1} and W_c are read once for the group
+    const int gpc = (p.sub + DEP_TPW - 1) / DEP_TPW;
+    const int h = blockIdx.x / (p.nchunks * gpc), rem = blockIdx.x % (p.nchunks * gpc), tid = threadIdx.x;
+    const int ch = rem / gpc, grp = rem % gpc;
+    const int ta = ch * p.sub + grp * DEP_TPW, tb = min(min(ta + DEP_TPW, (ch + 1) * p.sub), p.ntiles);
     const long tok0 = (long)h * p.T;
-    const int c0 = c * B, n = min(B, p.T - c0);
-    const long cb = ((long)h * p.nchunks + c / p.sub);
-    const long row0 = (long)h * p.rstride + c0;
+    const long cb = (long)h * p.nchunks + ch;
     for (int e = tid; e < D * D; e += 256) {
         Gn[e / D][e % D] = p.gnext[cb * D * D + e];
         if (p.loss == 1) Wc[e / D][e % D] = p.states[cb * D * D + e];
     }
     const bool nc = p.order == 1;  // no outputs per chunk: U from here, no G-free parts
-    for (int e = tid; e < B * D; e += 256) {
-        const int i = e / D, j = e % D;
-        const bool ok = i < n;
-        Ks[i][j] = ok ? ldf<E>(p.k, (tok0 + c0 + i) * D + j) : 0.f;
-        Us[i][j] = (p.loss == 1 && !nc) ? p.ub[(row0 + i) * D + j]
-                                        : (ok ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f);
-    }
-    if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
-    __syncthreads();
-    if (nc && p.loss == 1) {  // U = V - K W_c
-        float u[NBD];
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int e = tid + 256 * r, i = e / D, j = e % D;
-            float sacc = 0.f;
-            for (int a = 0; a < D; ++a) sacc += Ks[i][a] * Wc[a][j];
-            u[r] = Us[i][j] - sacc;
+    for (int c = ta; c < tb; ++c) {
+        const int c0 = c * B, n = min(B, p.T - c0);
+        const long row0 = (long)h * p.rstride + c0;
+        for (int e = tid; e < B * D; e += 256) {
+            const int i = e / D, j = e % D;
+            const bool ok = i < n;
+            Ks[i][j] = ok ? ldf<E>(p.k, (tok0 + c0 + i) * D + j) : 0.f;
+            Us[i][j] = (p.loss == 1 && !nc) ? p.ub[(row0 + i) * D + j]
+                                            : (ok ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f);
         }
+        if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
         __syncthreads();
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) Us[(tid + 256 * r) / D][(tid + 256 * r) % D] = u[r];
-        __syncthreads();
-    }
-    // thread outputs (i0 + RS r, j): the wave shares its rows, so row reads are
-    // broadcasts and each column element of G is read once for all rows
-    constexpr int RS = 256 / D;
-    const int i0 = tid / D, jl = tid % D;
-    {
-        float sg[NBD];
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) sg[r] = 0.f;
-#pragma unroll 2
-        for (int a = 0; a < D; a += 4) {
-            const float g0 = Gn[a][jl], g1 = Gn[a + 1][jl], g2 = Gn[a + 2][jl], g3 = Gn[a + 3][jl];
-#pragma unroll
+        if (nc && p.loss == 1) {  // U = V - K W_c
+            float u[NBD];
+    #pragma unroll
             for (int r = 0; r < NBD; ++r) {
-                const f32x4 kv = lds4(&Ks[i0 + RS * r][a]);
-                sg[r] += kv[0] * g0;
-                sg[r] += kv[1] * g1;
-                sg[r] += kv[2] * g2;
-                sg[r] += kv[3] * g3;
+                const int e = tid + 256 * r, i = e / D, j = e % D;
+                float sacc = 0.f;
+                for (int a = 0; a < D; ++a) sacc += Ks[i][a] * Wc[a][j];
+                u[r] = Us[i][j] - sacc;
             }
+            __syncthreads();
+    #pragma unroll
+            for (int r = 0; r < NBD; ++r) Us[(tid + 256 * r) / D][(tid + 256 * r) % D] = u[r];
+            __syncthreads();
         }
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int i = i0 + RS * r;
-            KGs[i][jl] = sg[r];
-            if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + jl, (nc ? 0.f : p.st[(row0 + i) * D + jl]) + et[i] * sg[r]);
-        }
-    }
-    __syncthreads();
-    if (tid < 64) {
-        for (int i = 0; i < n; ++i) {
-            float s = 0.f;
-            for (int a = tid; a < D; a += 64) s += KGs[i][a] * Us[i][a];
-            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-            if (tid == 0) p.deta[tok0 + c0 + i] = (nc ? 0.f : p.deta[tok0 + c0 + i]) + s;
-        }
-    }
-    {
-        const int a = jl;  // outputs (i0 + RS r, a)
-        float sk[NBD];
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) sk[r] = 0.f;
-#pragma unroll 2
-        for (int j = 0; j < D; j += 4) {
-            const float g[4] = {Gn[a][j], Gn[a][j + 1], Gn[a][j + 2], Gn[a][j + 3]};
-            float w[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.loss == 1) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) w[x] = Wc[a][j + x];
-            }
-#pragma unroll
-            for (int r = 0; r < NBD; ++r) {
-                const f32x4 uv = lds4(&Us[i0 + RS * r][j]);
-                if (p.loss == 1) {
-                    const f32x4 kg = lds4(&KGs[i0 + RS * r][j]);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        sk[r] += uv[x] * g[x];
-                        sk[r] -= kg[x] * w[x];
-                    }
-                } else {
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) sk[r] += uv[x] * g[x];
+        // thread outputs (i0 + RS r, j): the wave shares its rows, so row reads are
+        // broadcasts and each column element of G is read once for all rows
+        constexpr int RS = 256 / D;
+        const int i0 = tid / D, jl = tid % D;
+        {
+            float sg[NBD];
+    #pragma unroll
+            for (int r = 0; r < NBD; ++r) sg[r] = 0.f;
+    #pragma unroll 2
+            for (int a = 0; a < D; a += 4) {
+                const float g0 = Gn[a][jl], g1 = Gn[a + 1][jl], g2 = Gn[a + 2][jl], g3 = Gn[a + 3][jl];
+    #pragma unroll
+                for (int r = 0; r < NBD; ++r) {
+                    const f32x4 kv = lds4(&Ks[i0 + RS * r][a]);
+                    sg[r] += kv[0] * g0;
+                    sg[r] += kv[1] * g1;
+                    sg[r] += kv[2] * g2;
+                    sg[r] += kv[3] * g3;
                 }
             }
+    #pragma unroll
+            for (int r = 0; r < NBD; ++r) {
+                const int i = i0 + RS * r;
+                KGs[i][jl] = sg[r];
+                if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + jl, (nc ? 0.f : p.st[(row0 + i) * D + jl]) + et[i] * sg[r]);
+            }
         }
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int i = i0 + RS * r;
-            if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, (nc ? 0.f : p.dkl[(row0 + i) * D + a]) + et[i] * sk[r]);
+        __syncthreads();
+        if (tid < 64) {
+            for (int i = 0; i < n; ++i) {
+                float s = 0.f;
+                for (int a = tid; a < D; a += 64) s += KGs[i][a] * Us[i][a];
+                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+                if (tid == 0) p.deta[tok0 + c0 + i] = (nc ? 0.f : p.deta[tok0 + c0 + i]) + s;
+            }
         }
+        {
+            const int a = jl;  // outputs (i0 + RS r, a)
+            float sk[NBD];
+    #pragma unroll
+            for (int r = 0; r < NBD; ++r) sk[r] = 0.f;
+    #pragma unroll 2
+            for (int j = 0; j < D; j += 4) {
+                const float g[4] = {Gn[a][j], Gn[a][j + 1], Gn[a][j + 2], Gn[a][j + 3]};
+                float w[4] = {0.f, 0.f, 0.f, 0.f};
+                if (p.loss == 1) {
+    #pragma unroll
+                    for (int x = 0; x < 4; ++x) w[x] = Wc[a][j + x];
+                }
+    #pragma unroll
+                for (int r = 0; r < NBD; ++r) {
+                    const f32x4 uv = lds4(&Us[i0 + RS * r][j]);
+                    if (p.loss == 1) {
+                        const f32x4 kg = lds4(&KGs[i0 + RS * r][j]);
+    #pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            sk[r] += uv[x] * g[x];
+                            sk[r] -= kg[x] * w[x];
+                        }
+                    } else {
+    #pragma unroll
+                        for (int x = 0; x < 4; ++x) sk[r] += uv[x] * g[x];
+                    }
+                }
+            }
+    #pragma unroll
+            for (int r = 0; r < NBD; ++r) {
+                const int i = i0 + RS * r;
+                if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, (nc ? 0.f : p.dkl[(row0 + i) * D + a]) + et[i] * sk[r]);
+            }
+        }
+        __syncthreads();  // the next tile overwrites K, U, KG
     }
 }
 
@@ -811,16 +820,46 @@ __global__ __launch_bounds__(256) void lbw_local_tiled(LinBwdParams p)
     for (int r = 0; r < NR; ++r) sv[r] = dk[r] = dq[r] = 0.f;
     float de = 0.f;  // d_eta's first part for row tid (< TT)
     __syncthreads();
-    // the chunk's tiles J >= I: A[t][i] = q_t . k_i, dS[t][i] = dO_t . u_i (t in J, i in I, t >= i)
-    for (int J = I; J < J1; ++J) {
+    // The other tiles' operands go global -> registers one tile ahead.
+    constexpr int NL = TT * D / 256;
+    float xr[NL], yr[NL], er = 0.f;
+    auto load_after = [&](int J) {  // Q and dO of tile J (phase J >= I)
         const int cj = J * TT, nj = min(TT, p.T - cj);
-        for (int e = tid; e < TT * D; e += 256) {
-            const int t = e / D, a = e % D;
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int e = tid + 256 * k, t = e / D, a = e % D;
             const bool ok = t < nj;
-            XJ[t][a] = ok ? ldf<E>(p.q, (tok0 + cj + t) * D + a) : 0.f;
-            YJ[t][a] = ok ? ldf<E>(p.dout, (tok0 + cj + t) * D + a) : 0.f;
+            xr[k] = ok ? ldf<E>(p.q, (tok0 + cj + t) * D + a) : 0.f;
+            yr[k] = ok ? ldf<E>(p.dout, (tok0 + cj + t) * D + a) : 0.f;
         }
+    };
+    auto load_before = [&](int J) {  // U (or V) and K of tile J, and its eta (phase J <= I)
+        const int cj = J * TT, nj = min(TT, p.T - cj);
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int e = tid + 256 * k, t = e / D, a = e % D;
+            const bool ok = t < nj;
+            xr[k] = mse ? p.ub[(row0 + cj + t) * D + a] : (ok ? ldf<E>(p.v, (tok0 + cj + t) * D + a) : 0.f);
+            yr[k] = ok ? ldf<E>(p.k, (tok0 + cj + t) * D + a) : 0.f;
+        }
+        if (tid < TT) er = tid < nj ? p.eta[tok0 + cj + tid] : 0.f;
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int e = tid + 256 * k;
+            XJ[e / D][e % D] = xr[k];
+            YJ[e / D][e % D] = yr[k];
+        }
+        if (tid < TT) etJ[tid] = er;
+    };
+    // the chunk's tiles J >= I: A[t][i] = q_t . k_i, dS[t][i] = dO_t . u_i (t in J, i in I, t >= i)
+    load_after(I);
+    for (int J = I; J < J1; ++J) {
+        put();
         __syncthreads();
+        if (J + 1 < J1) load_after(J + 1);
+        else load_before(J0);
         {
             const int t = tid / TT, i = tid % TT;  // one (t, i) pair per thread
             float sa = 0.f, sd = 0.f;
@@ -857,15 +896,9 @@ __global__ __launch_bounds__(256) void lbw_local_tiled(LinBwdParams p)
     }
     // the chunk's tiles J <= I: dA[t][s] = eta_s dO_t . u_s (t in I, s in J, s <= t)
     for (int J = J0; J <= I; ++J) {
-        const int cj = J * TT, nj = min(TT, p.T - cj);
-        for (int e = tid; e < TT * D; e += 256) {
-            const int t = e / D, a = e % D;
-            const bool ok = t < nj;
-            XJ[t][a] = mse ? p.ub[(row0 + cj + t) * D + a] : (ok ? ldf<E>(p.v, (tok0 + cj + t) * D + a) : 0.f);
-            YJ[t][a] = ok ? ldf<E>(p.k, (tok0 + cj + t) * D + a) : 0.f;
-        }
-        if (tid < TT) etJ[tid] = tid < nj ? p.eta[tok0 + cj + tid] : 0.f;
+        put();
         __syncthreads();
+        if (J + 1 <= I) load_before(J + 1);
         {
             const int t = tid / TT, s2 = tid % TT;
             float sd = 0.f;
@@ -931,21 +964,42 @@ __global__ __launch_bounds__(256) void lbw_rc(LinBwdParams p)
     float acc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-    for (int s = t0; s < t1; s += TK) {
+    // the next 32 tokens' operands go global -> registers while these compute
+    constexpr int NQ = TK * D / 256, NS = TK * CB / 256;
+    float qr[NQ], kr[NQ], orr[NS], sr[NS];
+    auto load = [&](int s) {
         const int n = min(TK, t1 - s);
-        for (int e = tid; e < TK * D; e += 256) {
-            const int t = e / D, a = e % D;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int e = tid + 256 * k, t = e / D, a = e % D;
             const bool ok = t < n;
-            Qs[t][a] = ok ? ldf<E>(p.q, (tok0 + s + t) * D + a) : 0.f;
-            Ks[t][a] = (ok && mse) ? ldf<E>(p.k, (tok0 + s + t) * D + a) : 0.f;
+            qr[k] = ok ? ldf<E>(p.q, (tok0 + s + t) * D + a) : 0.f;
+            kr[k] = (ok && mse) ? ldf<E>(p.k, (tok0 + s + t) * D + a) : 0.f;
         }
-        for (int e = tid; e < TK * CB; e += 256) {
-            const int t = e / CB, q = e % CB;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const int e = tid + 256 * k, t = e / CB, q = e % CB;
             const bool ok = t < n;
-            dOs[t][q] = ok ? ldf<E>(p.dout, (tok0 + s + t) * D + j0 + q) : 0.f;
-            Ss[t][q] = (ok && mse) ? p.st[(row0 + s + t) * D + j0 + q] : 0.f;
+            orr[k] = ok ? ldf<E>(p.dout, (tok0 + s + t) * D + j0 + q) : 0.f;
+            sr[k] = (ok && mse) ? p.st[(row0 + s + t) * D + j0 + q] : 0.f;
+        }
+    };
+    if (t0 < t1) load(t0);
+    for (int s = t0; s < t1; s += TK) {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int e = tid + 256 * k;
+            Qs[e / D][e % D] = qr[k];
+            Ks[e / D][e % D] = kr[k];
+        }
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const int e = tid + 256 * k;
+            dOs[e / CB][e % CB] = orr[k];
+            Ss[e / CB][e % CB] = sr[k];
         }
         __syncthreads();
+        if (s + TK < t1) load(s + TK);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int a = ab + (256 / CB) * r;
@@ -1105,7 +1159,7 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_serial_grad<D, B, E>(p, NH, st);
-    lbw_dep<D, B, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
+    lbw_dep<D, B, E><<<dim3(NH * p.nchunks * ((p.sub + DEP_TPW - 1) / DEP_TPW)), b, 0, st>>>(p);
 }
 
 // Chunks of 16 k tokens (k > 1, or d = 128 with 32): the serial and dependent
@@ -1125,7 +1179,7 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_serial_grad<D, TT, E>(p, NH, st);
-    lbw_dep<D, TT, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
+    lbw_dep<D, TT, E><<<dim3(NH * p.nchunks * ((p.sub + DEP_TPW - 1) / DEP_TPW)), b, 0, st>>>(p);
 }
 
 hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
