@@ -18,12 +18,12 @@
 //     W_{c+1} = W_c + K^T H (V - K W_c),
 // and the backward one for G,
 //     G_c = G_{c+1} + R_c [- K^T H K G_{c+1}],   R_c = Q^T dO [- K^T S~],  S~ = S^T dO.
-// So the work runs in four launches: the state recursion and the G recursion
-// with one workgroup per (head, 16 columns) and their operands staged in LDS
-// a batch of chunks at a time, and between and after them two
-// launches with one workgroup per (head, chunk) for everything else (the
-// G-free terms and R_c first, then the terms that need G_{c+1}), exchanging
-// per-chunk matrices through the workspace.  Everything is fp32 FMA in LDS.
+// So the work runs as the state recursion and the G recursion (segmented:
+// maps, chain, walks; fp32 MFMA, one wave per (head, segment, 16 columns)),
+// and between and after them two passes with one workgroup per (head, chunk)
+// for everything else (the G-free terms and R_c first, then the terms that
+// need G_{c+1}; fp32 FMA in LDS), exchanging per-chunk matrices through the
+// workspace.
 #include "ttt_device.h"
 #include "ttt_internal.h"
 
@@ -59,6 +59,9 @@ struct LinBwdParams {
     // start state (states) or end adjoint (G).
     int nseg, seg_chunks;
     float *ssum, *sstart;
+    // The serial passes on the matrix cores step over 16-token tiles: tpc per
+    // chunk, nwt per head.
+    int tpc, nwt;
 };
 
 template <typename E> __device__ __forceinline__ float ldf(const void *p, long i)
@@ -76,207 +79,20 @@ constexpr int DEP_TPW = 8;  // tiles per workgroup of the dependent pass (chunks
 // four consecutive floats of an LDS row (16-byte aligned)
 __device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast<const f32x4 *>(x); }
 
-// Serial passes: the operands of NB chunks at a time are loaded into registers
-// while the previous NB chunks compute out of LDS, and written to LDS once per
-// batch, so no chunk step waits for memory (a step only reads LDS and stores).
-// Small batches keep the LDS small enough for several workgroups per CU.
-template <int D, int B> struct Batch {
-    static constexpr int NB = 2;  // LDS: two batches of K and V / R_c
-};
-
 // Both serial recursions are affine in their d x d matrix, chunk by chunk:
 //   states  W_{c+1} = (I - K^T H K) W_c + K^T H V,
 //   G       G_c     = (I - K^T H K) G_{c+1} + R_c,
 // and neither mixes the matrix's columns.  So a segment of chunks is one
 // affine map X -> L X + F; its two parts come out of the same walk started
 // from the identity without the inputs (L) or from zero with them (F).  Three
-// steps per recursion: the maps of all segments in parallel (mode 1, one
-// workgroup per (head, segment, 16 columns of [L | F])), the chain of the
-// maps per (head, 16 columns) (lbw_chain), and the walk of every segment from
-// its own start (mode 0, per (head, segment, 16 columns)), which stores what
-// the parallel passes read.
-
-// Walk of the state recursion over one segment (one workgroup per (head,
-// segment, 16 columns)).  mode 0: from the segment's start state, storing
-// every chunk-start state (and the final state in the update-then-apply
-// order); mode 1: the segment's map, columns [0, D) the linear part (from the
-// identity, V = 0), [D, 2D) the offset (from zero).
-template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lbw_states(LinBwdParams p, int mode)
-{
-    constexpr int NB = Batch<D, B>::NB, NK = B * D / 256, NV = B * CB / 256;
-    // K rows padded to D + 4 floats; V and U stored transposed (token index
-    // last), rows padded to B + 4: the dot products read four elements at a time
-    constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
-    __shared__ float W[D][CB + 1];
-    __shared__ __align__(16) float Ks[2][NB][B][KP];
-    __shared__ __align__(16) float Vt[2][NB][CB][TP];
-    __shared__ __align__(16) float et[2][NB][B];
-    __shared__ __align__(16) float Ut[CB][TP];
-    __shared__ float S[D][CB + 1];  // chunk-start state (sub > 1): the residuals' snapshot
-    const int ncol = (mode == 1 ? 2 : 1) * (D / CB);
-    const int nsl = mode == 1 ? p.nseg - 1 : p.nseg;  // the last segment's map is never needed
-    int bid = blockIdx.x;
-    const int cbk = bid % ncol;
-    bid /= ncol;
-    const int seg = bid % nsl, h = bid / nsl, tid = threadIdx.x;
-    const bool lin = mode == 1 && cbk < D / CB;  // the map's linear part: no V
-    const int j0 = (cbk % (D / CB)) * CB;
-    const long tok0 = (long)h * p.T;
-    const int ca = seg * p.seg_chunks, cb = min(p.nchunks, ca + p.seg_chunks);
-    const int ta = ca * p.sub, tb = min(cb * p.sub, p.ntiles);  // the segment's tiles
-    const int nbat = (tb - ta + NB - 1) / NB;
-    float pk[NB][NK], pv[NB][NV], pe[NB];
-    auto load = [&](int k) {
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-            const int c = ta + k * NB + m;
-            const int c0 = c * B, n = c < tb ? min(B, p.T - c0) : 0;
-#pragma unroll
-            for (int r = 0; r < NK; ++r) {
-                const int e = tid + 256 * r, i = e / D, a = e % D;
-                pk[m][r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
-            }
-#pragma unroll
-            for (int r = 0; r < NV; ++r) {
-                const int e = tid + 256 * r, i = e / CB, j = e % CB;
-                pv[m][r] = (i < n && !lin) ? ldf<E>(p.v, (tok0 + c0 + i) * D + j0 + j) : 0.f;
-            }
-            pe[m] = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-#pragma unroll
-            for (int r = 0; r < NK; ++r) Ks[buf][m][(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[m][r];
-#pragma unroll
-            for (int r = 0; r < NV; ++r) Vt[buf][m][(tid + 256 * r) % CB][(tid + 256 * r) / CB] = pv[m][r];
-            if (tid < B) et[buf][m][tid] = pe[m];
-        }
-    };
-    {
-        const float *w = mode == 1 ? nullptr
-                         : seg == 0 ? p.w0 + (long)h * D * D
-                                    : p.sstart + ((long)h * p.nseg + seg) * D * D;
-        for (int e = tid; e < D * CB; e += 256) {
-            const int a = e / CB, j = e % CB;
-            W[a][j] = w ? w[(long)a * D + j0 + j] : (lin && a == j0 + j ? 1.f : 0.f);
-        }
-    }
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int k = 0; k < nbat; ++k) {
-        const int buf = k & 1;
-        if (k + 1 < nbat) load(k + 1);
-        for (int m = 0; m < NB; ++m) {
-            const int c = ta + k * NB + m;
-            if (c >= tb) break;
-            if (c % p.sub == 0) {  // a chunk starts: store its state (and snapshot it)
-                if (mode == 0) {
-                    float *dst = p.states + ((long)h * p.nchunks + c / p.sub) * D * D;
-                    for (int e = tid; e < D * CB; e += 256) dst[(e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
-                }
-                if (p.sub > 1 && p.loss == 1) {
-                    for (int e = tid; e < D * CB; e += 256) S[e / CB][e % CB] = W[e / CB][e % CB];
-                    lds_barrier();
-                }
-            }
-            const float(*Sm)[CB + 1] = p.sub > 1 ? S : W;  // the residuals read the chunk-start state
-            const float(*Kc)[KP] = Ks[buf][m];
-            const float(*Vc)[TP] = Vt[buf][m];
-            const float(*Uc)[TP] = Vc;
-            if (p.loss == 1) {  // U = V - K W_c
-                for (int e = tid; e < B * CB; e += 256) {
-                    const int i = e / CB, j = e % CB;
-                    float sacc = 0.f;
-#pragma unroll
-                    for (int a = 0; a < D; a += 4) {
-                        const f32x4 kv = lds4(&Kc[i][a]);
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) sacc += kv[x] * Sm[a + x][j];
-                    }
-                    Ut[j][i] = Vc[j][i] - sacc;
-                }
-                lds_barrier();
-                Uc = Ut;
-            }
-            {
-                // thread elements (tid / CB + (256 / CB) r, tid % CB): one column j,
-                // so each read of U^T and eta serves all of them
-                const int j = tid % CB, ab = tid / CB;
-                float sacc[NE];
-#pragma unroll
-                for (int r = 0; r < NE; ++r) sacc[r] = 0.f;
-#pragma unroll
-                for (int i = 0; i < B; i += 4) {
-                    const f32x4 uv = lds4(&Uc[j][i]);
-                    const f32x4 ev = lds4(&et[buf][m][i]);
-#pragma unroll
-                    for (int r = 0; r < NE; ++r)
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) sacc[r] += Kc[i + x][ab + (256 / CB) * r] * ev[x] * uv[x];
-                }
-#pragma unroll
-                for (int r = 0; r < NE; ++r) W[ab + (256 / CB) * r][j] += sacc[r];
-            }
-            lds_barrier();
-        }
-        if (k + 1 < nbat) {
-            store(buf ^ 1);
-            __syncthreads();
-        }
-    }
-    if (mode == 1) {
-        float *dst = p.ssum + ((long)h * p.nseg + seg) * D * 2 * D + (lin ? 0 : D) + j0;
-        for (int e = tid; e < D * CB; e += 256) dst[(long)(e / CB) * 2 * D + e % CB] = W[e / CB][e % CB];
-    } else if (p.order == 1 && seg == p.nseg - 1) {
-        for (int e = tid; e < D * CB; e += 256) p.wfinal[(long)h * D * D + (e / CB) * D + j0 + e % CB] = W[e / CB][e % CB];
-    }
-}
-
-// The chain of the segment maps, one workgroup per (head, 16 columns):
+// steps per recursion: the maps of all segments in parallel (mode 1, one wave
+// per (head, segment, 16 columns of [L | F])), the chain of the maps per
+// (head, 16 columns) (lbw_chain_m), and the walk of every segment from its
+// own start (mode 0, per (head, segment, 16 columns)), which stores what the
+// parallel passes read.  The chain, per (head, 16 columns):
 // dir 0 (states): X_0 = w_init, X_{s+1} = L_s X_s + F_s, storing X_s for s >= 1;
 // dir 1 (G): X_{S-1} = g0 (d_w_final, or the apply's G in the update-then-apply
 // order, or zero), X_{s-1} = L_s X_s + F_s, storing X_s for s <= S - 2.
-template <int D>
-__global__ __launch_bounds__(256) void lbw_chain(LinBwdParams p, int dir)
-{
-    constexpr int NE = D * CB / 256;
-    __shared__ float L[D][D + 1];
-    __shared__ float X[D][CB + 1];
-    const int h = blockIdx.x / (D / CB), j0 = (blockIdx.x % (D / CB)) * CB, tid = threadIdx.x;
-    const int S = p.nseg;
-    const float *x0 = dir == 0 ? p.w0 : (p.order == 1 ? p.ginit : p.dwf);
-    for (int e = tid; e < D * CB; e += 256)
-        X[e / CB][e % CB] = x0 ? x0[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
-    const int j = tid % CB, ab = tid / CB;  // outputs (ab + 16 r, j)
-    for (int t = 0; t < S - 1; ++t) {
-        const int s = dir == 0 ? t : S - 1 - t;       // the map applied
-        const int o = dir == 0 ? s + 1 : s - 1;       // the segment whose start it gives
-        const float *M = p.ssum + ((long)h * S + s) * D * 2 * D;
-        for (int e = tid; e < D * D; e += 256) L[e / D][e % D] = M[(long)(e / D) * 2 * D + e % D];
-        __syncthreads();
-        float acc[NE];
-#pragma unroll
-        for (int r = 0; r < NE; ++r) {
-            const int a = ab + (256 / CB) * r;
-            float x = M[(long)a * 2 * D + D + j0 + j];
-            for (int q = 0; q < D; ++q) x += L[a][q] * X[q][j];
-            acc[r] = x;
-        }
-        __syncthreads();
-        float *dst = p.sstart + ((long)h * S + o) * D * D;
-#pragma unroll
-        for (int r = 0; r < NE; ++r) {
-            const int a = ab + (256 / CB) * r;
-            X[a][j] = acc[r];
-            dst[(long)a * D + j0 + j] = acc[r];
-        }
-        __syncthreads();
-    }
-}
 
 // Parallel pass 2, one workgroup per (head, chunk): every term that does not
 // need G.  Writes dQ, d_eta's first part and the chunk's U, S~, dK part, R_c.
@@ -465,154 +281,337 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     lbw_local_body<64, 16, E>(p);
 }
 
-// Walk of the G recursion over one segment, last chunk first (one workgroup per
-// (head, segment, 16 columns)): G_c = G_{c+1} + R_c [- K^T H K G_{c+1}].  mode
-// 0: from the segment's end adjoint, storing every G_{c+1} (and d_w_init at
-// the start of the first segment); mode 1: the segment's map (segments 1 ..
-// S-1), columns [0, D) the linear part (from the identity, no R_c), [D, 2D)
-// the offset (from zero).
-template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lbw_grad(LinBwdParams p, int mode)
-{
-    constexpr int NB = Batch<D, B>::NB, NK = B * D / 256, NR = D * CB / 256;
-    // K rows padded to D + 4 floats and (H K G) stored transposed, rows padded
-    // to B + 4: both dot products read four consecutive elements at a time
-    constexpr int KP = D + 4, TP = B + 4, NE = D * CB / 256;
-    __shared__ float G[D][CB + 1];
-    __shared__ float Gs[D][CB + 1];  // G at the end of the current chunk (sub > 1)
-    __shared__ __align__(16) float KGt[CB][TP];
-    __shared__ float Rs[2][NB][D][CB + 1];
-    __shared__ __align__(16) float Ks[2][NB][B][KP];
-    __shared__ float et[2][NB][B];
-    const int ncol = (mode == 1 ? 2 : 1) * (D / CB);
-    const int nsl = mode == 1 ? p.nseg - 1 : p.nseg;  // maps of segments 1 .. S-1
-    int bid = blockIdx.x;
-    const int cbk = bid % ncol;
-    bid /= ncol;
-    const int seg = bid % nsl + (mode == 1 ? 1 : 0), h = bid / nsl, tid = threadIdx.x;
-    const bool lin = mode == 1 && cbk < D / CB;  // the map's linear part: no R_c
-    const int j0 = (cbk % (D / CB)) * CB;
-    const long tok0 = (long)h * p.T;
-    const int ca = seg * p.seg_chunks, cbe = min(p.nchunks, ca + p.seg_chunks);
-    const int ta = ca * p.sub, last = min(cbe * p.sub, p.ntiles) - 1;  // the segment's tiles [ta, last]
-    const int nbat = (last - ta + 1 + NB - 1) / NB;
-    // the first tile of a chunk in this (reverse) order: its last one
-    auto chunk_end = [&](int c) { return c == p.ntiles - 1 || c % p.sub == p.sub - 1; };
-    float pk[NB][NK], pr[NB][NR], pe[NB];
-    auto load = [&](int k) {  // batch k = tiles last - k NB - m, m < NB
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-            const int c = last - (k * NB + m);
-            const bool ok = c >= ta;
-            const int c0 = c * B, n = ok ? min(B, p.T - c0) : 0;
-            const float *R = p.rc + ((long)h * p.nchunks + (ok ? c / p.sub : 0)) * D * D;
-            // R_c once per chunk; the update-then-apply order has none
-            const bool hasr = ok && !lin && p.order == 0 && chunk_end(c);
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const int e = tid + 256 * r;
-                pr[m][r] = hasr ? R[(long)(e / CB) * D + j0 + e % CB] : 0.f;
-            }
-            if (p.loss == 1) {
-#pragma unroll
-                for (int r = 0; r < NK; ++r) {
-                    const int e = tid + 256 * r, i = e / D, a = e % D;
-                    pk[m][r] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
-                }
-                pe[m] = (tid < n) ? p.eta[tok0 + c0 + tid] : 0.f;
-            }
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) Rs[buf][m][(tid + 256 * r) / CB][(tid + 256 * r) % CB] = pr[m][r];
-            if (p.loss == 1) {
-#pragma unroll
-                for (int r = 0; r < NK; ++r) Ks[buf][m][(tid + 256 * r) / D][(tid + 256 * r) % D] = pk[m][r];
-                if (tid < B) et[buf][m][tid] = pe[m];
-            }
-        }
-    };
+// ---------------------------------------------------------------------------
+// The serial passes on the matrix cores (fp32 16x16x4 MFMA).  One wave per
+// (head, segment, 16 columns) steps over 16-token tiles (a chunk of b tokens
+// is b / 16 tiles: every residual of a chunk reads the chunk-start state and
+// every G-term reads G_{c+1}, kept as a snapshot when a chunk has several
+// tiles).  The wave holds its D x 16 slice of the matrix as D / 16
+// accumulator tiles, lane (g, n) keeping rows 16 s + 4 g + r (r < 4) of
+// column n.  Taking the contraction index of MFMA step j on lane group g as
+// 4 g + j, that accumulator is also the B operand of the next product, and so
+// is the accumulator of Y below; a tile step is
+//     Y = K X                                (A: K rows, 4 features a lane)
+//     X += K^T H (V - Y)   or   G -= K^T H Y  (A: K columns, B: Y itself)
+// with the K tile staged in the wave's own LDS (no barriers).
+// ---------------------------------------------------------------------------
+constexpr int WT = 16;  // tokens per walk tile
+// Walk tiles in flight per wave: a step is a few hundred cycles of MFMA work,
+// short against the latency of its loads.
+template <int D> constexpr int WPF = D == 64 ? 4 : 3;
+
+template <int D> struct WalkTile {
+    float k[WT][D + 4];  // rows padded by 4: row and column fragment reads spread over the banks
+};
+
+// One K tile in registers (16-byte pieces), loaded a step ahead.
+template <int D, typename E> struct WalkK {
+    static constexpr int PE = 16 / (int)sizeof(E);  // elements per piece
+    static constexpr int PPR = D / PE;              // pieces per token row
+    static constexpr int NP = WT * PPR / 64;        // pieces per lane
+    static_assert(NP * 64 == WT * PPR, "walk tile shape");
+    u32x4 v[NP];
+    // Rows past T read the last row (an in-bounds address, no branch around
+    // the load) and are zeroed when the tile is written to LDS.
+    __device__ __forceinline__ void load(const void *k, long tok0, int t0, int T, int lane)
     {
-        const float *g0 = p.order == 1 ? p.ginit : p.dwf;  // null: zero
-        const float *g = mode == 1 ? nullptr
-                         : seg == p.nseg - 1 ? (g0 ? g0 + (long)h * D * D : nullptr)
-                                             : p.sstart + ((long)h * p.nseg + seg) * D * D;
-        for (int e = tid; e < D * CB; e += 256) {
-            const int a = e / CB, j = e % CB;
-            G[a][j] = g ? g[(long)a * D + j0 + j] : (lin && a == j0 + j ? 1.f : 0.f);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int idx = lane + 64 * i, t = min(t0 + idx / PPR, T - 1);
+            v[i] = *reinterpret_cast<const u32x4 *>(static_cast<const E *>(k) + (tok0 + t) * D + PE * (idx % PPR));
         }
     }
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int k = 0; k < nbat; ++k) {
-        const int buf = k & 1;
-        if (k + 1 < nbat) load(k + 1);
-        for (int m = 0; m < NB; ++m) {
-            const int c = last - (k * NB + m);
-            if (c < ta) break;
-            if (chunk_end(c)) {  // G = G_{c+1} of this chunk: store it (and snapshot it)
-                if (mode == 0) {
-                    float *gdst = p.gnext + ((long)h * p.nchunks + c / p.sub) * D * D;
-                    for (int e = tid; e < D * CB; e += 256) gdst[(e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
-                }
-                if (p.sub > 1 && p.loss == 1) {
-                    for (int e = tid; e < D * CB; e += 256) Gs[e / CB][e % CB] = G[e / CB][e % CB];
-                    lds_barrier();
-                }
+    __device__ __forceinline__ void put(WalkTile<D> &w, int lane, int n) const  // n: valid rows
+    {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int idx = lane + 64 * i, row = idx / PPR, c = PE * (idx % PPR);
+            const u32x4 x = row < n ? v[i] : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (sizeof(E) == 2) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, x);
+                *reinterpret_cast<f32x4 *>(&w.k[row][c]) = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+                *reinterpret_cast<f32x4 *>(&w.k[row][c + 4]) = f32x4{(float)b[4], (float)b[5], (float)b[6], (float)b[7]};
+            } else {
+                *reinterpret_cast<f32x4 *>(&w.k[row][c]) = __builtin_bit_cast(f32x4, x);
             }
-            const float(*Gm)[CB + 1] = p.sub > 1 ? Gs : G;  // every tile of the chunk meets G_{c+1}
-            const float(*Kc)[KP] = Ks[buf][m];
-            if (p.loss == 1) {
-                for (int e = tid; e < B * CB; e += 256) {
-                    const int i = e / CB, j = e % CB;
-                    float sacc = 0.f;
-#pragma unroll
-                    for (int a = 0; a < D; a += 4) {
-                        const f32x4 kv = lds4(&Kc[i][a]);
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) sacc += kv[x] * Gm[a + x][j];
-                    }
-                    KGt[j][i] = et[buf][m][i] * sacc;
-                }
-                lds_barrier();
-            }
-            {
-                // thread elements (tid / CB + (256 / CB) r, tid % CB): one column j,
-                // so each read of (H K G)^T serves all of them
-                const int j = tid % CB, ab = tid / CB;
-                float sacc[NE];
-#pragma unroll
-                for (int r = 0; r < NE; ++r) sacc[r] = Rs[buf][m][ab + (256 / CB) * r][j];
-                if (p.loss == 1) {
-#pragma unroll
-                    for (int i = 0; i < B; i += 4) {
-                        const f32x4 kg = lds4(&KGt[j][i]);
-#pragma unroll
-                        for (int r = 0; r < NE; ++r)
-#pragma unroll
-                            for (int x = 0; x < 4; ++x) sacc[r] -= Kc[i + x][ab + (256 / CB) * r] * kg[x];
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < NE; ++r) G[ab + (256 / CB) * r][j] += sacc[r];
-            }
-            lds_barrier();
-        }
-        if (k + 1 < nbat) {
-            store(buf ^ 1);
-            __syncthreads();
         }
     }
-    __syncthreads();
+};
+
+// A operand K[m][16 s + 4 q + j] (contraction over features) ...
+template <int D>
+__device__ __forceinline__ f32x4 walk_rows(const WalkTile<D> &w, int s, int m, int q)
+{
+    return *reinterpret_cast<const f32x4 *>(&w.k[m][16 * s + 4 * q]);
+}
+// ... and K[4 q + j][16 s + m] (contraction over tokens: rows of K^T).
+template <int D>
+__device__ __forceinline__ f32x4 walk_cols(const WalkTile<D> &w, int s, int m, int q)
+{
+    return f32x4{w.k[4 * q][16 * s + m], w.k[4 * q + 1][16 * s + m], w.k[4 * q + 2][16 * s + m],
+                 w.k[4 * q + 3][16 * s + m]};
+}
+
+// Rows 4 g + r of the tile starting at token t0, column col of a token-major
+// [T][D] tensor, and the tokens' eta, as loaded (raw); walk_f32 turns them
+// into floats, zero past T (rows past T read row T - 1: no branch around a
+// load, so its wait can sit at the first use, a step later).
+template <typename E> struct WalkCol {
+    E x[4];
+};
+template <typename E>
+__device__ __forceinline__ WalkCol<E> walk_col4(const void *x, long tok0, int t0, int T, int D, int col, int g)
+{
+    WalkCol<E> r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.x[i] = static_cast<const E *>(x)[(tok0 + min(t0 + 4 * g + i, T - 1)) * D + col];
+    return r;
+}
+__device__ __forceinline__ WalkCol<float> walk_eta4(const float *eta, long tok0, int t0, int T, int g)
+{
+    WalkCol<float> r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.x[i] = eta[tok0 + min(t0 + 4 * g + i, T - 1)];
+    return r;
+}
+template <typename E>
+__device__ __forceinline__ f32x4 walk_f32(const WalkCol<E> &c, int t0, int T, int g)
+{
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = t0 + 4 * g + i < T ? (float)c.x[i] : 0.f;
+    return r;
+}
+
+// A D x 16 column slice of a row-major matrix with row stride ld <-> accumulator tiles.
+template <int NS>
+__device__ __forceinline__ void slice_load(f32x4 *X, const float *src, long ld, int g, int m)
+{
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[s][r] = src[(long)(16 * s + 4 * g + r) * ld + m];
+}
+template <int NS>
+__device__ __forceinline__ void slice_store(float *dst, const f32x4 *X, long ld, int g, int m)
+{
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(long)(16 * s + 4 * g + r) * ld + m] = X[s][r];
+}
+template <int NS>
+__device__ __forceinline__ void slice_identity(f32x4 *X, int j0, int g, int m, bool one)
+{
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[s][r] = (one && 16 * s + 4 * g + r == j0 + m) ? 1.f : 0.f;
+}
+
+// Walk of the state recursion over one segment (mode 0: from its start state,
+// storing every chunk-start state, and the final state in the
+// update-then-apply order; mode 1: the segment's map, wave columns [0, D) the
+// linear part from the identity without V, [D, 2D) the offset from zero).
+template <int D, typename E>
+__global__ __launch_bounds__(256) void lbw_states_m(LinBwdParams p, int mode)
+{
+    constexpr int NS = D / 16;
+    __shared__ WalkTile<D> tiles[4];
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+    const int ncol = (mode == 1 ? 2 : 1) * NS;
+    const int nsl = mode == 1 ? p.nseg - 1 : p.nseg;  // the last segment's map is never needed
+    int w = blockIdx.x * 4 + wv;
+    const int cbk = w % ncol;
+    w /= ncol;
+    const int seg = w % nsl, h = w / nsl;
+    const bool lin = mode == 1 && cbk < NS;
+    const bool mse = p.loss == 1;
+    const int j0 = (cbk % NS) * 16, tpc = p.tpc;
+    const long tok0 = (long)h * p.T;
+    const int ca = seg * p.seg_chunks, cb = min(p.nchunks, ca + p.seg_chunks);
+    const int ta = ca * tpc, tb = min(cb * tpc, p.nwt);
+    WalkTile<D> &kt = tiles[wv];
+    f32x4 X[NS], S[NS];
+    if (mode == 1)
+        slice_identity<NS>(X, j0, g, m, lin);
+    else
+        slice_load<NS>(X, (seg == 0 ? p.w0 + (long)h * D * D : p.sstart + ((long)h * p.nseg + seg) * D * D) + j0,
+                       D, g, m);
+    // WPF tiles in flight, ring slots fixed at compile time by unrolling
+    constexpr int PF = WPF<D>;
+    WalkK<D, E> nk[PF];
+    WalkCol<E> vn[PF];
+    WalkCol<float> en[PF];
+    auto fetch = [&](int j, int t) {
+        nk[j].load(p.k, tok0, t * WT, p.T, lane);
+        vn[j] = walk_col4<E>(p.v, tok0, t * WT, p.T, D, j0 + m, g);
+        en[j] = walk_eta4(p.eta, tok0, t * WT, p.T, g);
+    };
+    // Every slot is refilled unconditionally (tiles past the segment or past T
+    // read in-bounds rows and go unused), so no ring register is ever merged
+    // with an unloaded value and no load needs an early wait.
+#pragma unroll
+    for (int j = 0; j < PF; ++j) fetch(j, ta + j);
+    for (int t0 = ta; t0 < tb; t0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            // slots are staged and refilled past the segment's end too (no exit
+            // from the group: the ring registers stay in place)
+            const int t = t0 + j;
+            nk[j].put(kt, lane, p.T - t * WT);
+            const f32x4 vc = lin ? zero4() : walk_f32(vn[j], t * WT, p.T, g);
+            const f32x4 ec = walk_f32(en[j], t * WT, p.T, g);
+            fetch(j, t + PF);
+            if (t < tb) {
+                if (t % tpc == 0) {  // a chunk starts: store its state (and snapshot it)
+                    if (mode == 0)
+                        slice_store<NS>(p.states + ((long)h * p.nchunks + t / tpc) * D * D + j0, X, D, g, m);
+                    if (tpc > 1 && mse)
+#pragma unroll
+                        for (int s = 0; s < NS; ++s) S[s] = X[s];
+                }
+                f32x4 U = vc;
+                if (mse) {  // U = V - K W_c
+                    f32x4 Y = zero4();
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) Y = mma16(Y, walk_rows<D>(kt, s, m, g), tpc > 1 ? S[s] : X[s]);
+                    U = vc - Y;
+                }
+                const f32x4 HU = U * ec;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) X[s] = mma16(X[s], walk_cols<D>(kt, s, m, g), HU);
+            }
+        }
+    }
+    if (mode == 1)
+        slice_store<NS>(p.ssum + ((long)h * p.nseg + seg) * D * 2 * D + (lin ? 0 : D) + j0, X, 2 * D, g, m);
+    else if (p.order == 1 && seg == p.nseg - 1)
+        slice_store<NS>(p.wfinal + (long)h * D * D + j0, X, D, g, m);
+}
+
+// Walk of the G recursion over one segment, last tile first (mode 0: from the
+// segment's end adjoint, storing every G_{c+1}, and d_w_init at the start of
+// the first segment; mode 1: the map of segments 1 .. S-1, wave columns
+// [0, D) the linear part from the identity without R_c, [D, 2D) the offset
+// from zero).  G_c = G_{c+1} + R_c [- K^T H K G_{c+1}].
+template <int D, typename E, bool MSE>
+__global__ __launch_bounds__(256) void lbw_grad_m(LinBwdParams p, int mode)
+{
+    constexpr int NS = D / 16;
+    __shared__ WalkTile<D> tiles[4];
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+    const int ncol = (mode == 1 ? 2 : 1) * NS;
+    const int nsl = mode == 1 ? p.nseg - 1 : p.nseg;
+    int w = blockIdx.x * 4 + wv;
+    const int cbk = w % ncol;
+    w /= ncol;
+    const int seg = w % nsl + (mode == 1 ? 1 : 0), h = w / nsl;
+    const bool lin = mode == 1 && cbk < NS;
+    const bool addr = !lin && p.order == 0;  // R_c enters (none in the update-then-apply order)
+    const int j0 = (cbk % NS) * 16, tpc = p.tpc;
+    const long tok0 = (long)h * p.T;
+    const int ca = seg * p.seg_chunks, ce = min(p.nchunks, ca + p.seg_chunks);
+    const int ta = ca * tpc, last = min(ce * tpc, p.nwt) - 1;
+    // the first tile of a chunk in this (reverse) order: its last one
+    auto chunk_end = [&](int t) { return t == p.nwt - 1 || t % tpc == tpc - 1; };
+    WalkTile<D> &kt = tiles[wv];
+    f32x4 G[NS], Gs[NS];
     if (mode == 1) {
-        float *dst = p.ssum + ((long)h * p.nseg + seg) * D * 2 * D + (lin ? 0 : D) + j0;
-        for (int e = tid; e < D * CB; e += 256) dst[(long)(e / CB) * 2 * D + e % CB] = G[e / CB][e % CB];
-    } else if (seg == 0) {
-        for (int e = tid; e < D * CB; e += 256) p.dw0[(long)h * D * D + (e / CB) * D + j0 + e % CB] = G[e / CB][e % CB];
+        slice_identity<NS>(G, j0, g, m, lin);
+    } else {
+        const float *g0 = p.order == 1 ? p.ginit : p.dwf;  // null: zero
+        const float *src = seg == p.nseg - 1 ? (g0 ? g0 + (long)h * D * D : nullptr)
+                                             : p.sstart + ((long)h * p.nseg + seg) * D * D;
+        if (src)
+            slice_load<NS>(G, src + j0, D, g, m);
+        else
+            slice_identity<NS>(G, j0, g, m, false);
+    }
+    constexpr int PF = WPF<D>;
+    WalkK<D, E> nk[PF];
+    WalkCol<float> en[PF];
+    auto fetch = [&](int j, int t) {  // unconditional, as in the state walk
+        if constexpr (MSE) {
+            nk[j].load(p.k, tok0, max(t, 0) * WT, p.T, lane);
+            en[j] = walk_eta4(p.eta, tok0, max(t, 0) * WT, p.T, g);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < PF; ++j) fetch(j, last - j);
+    for (int t0 = last; t0 >= ta; t0 -= PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int t = t0 - j;  // below ta: staged, refilled, not computed
+            f32x4 ec = zero4();
+            if constexpr (MSE) {
+                nk[j].put(kt, lane, p.T - max(t, 0) * WT);
+                ec = walk_f32(en[j], max(t, 0) * WT, p.T, g);
+            }
+            fetch(j, t - PF);
+            if (t < ta) continue;
+            const bool ce_t = chunk_end(t);
+            if (ce_t) {  // G = G_{c+1} of this chunk: store it (and snapshot it)
+                if (mode == 0) slice_store<NS>(p.gnext + ((long)h * p.nchunks + t / tpc) * D * D + j0, G, D, g, m);
+                if (tpc > 1 && MSE)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) Gs[s] = G[s];
+            }
+            if constexpr (MSE) {
+                f32x4 Y = zero4();
+#pragma unroll
+                for (int s = 0; s < NS; ++s) Y = mma16(Y, walk_rows<D>(kt, s, m, g), tpc > 1 ? Gs[s] : G[s]);
+                const f32x4 HY = -(Y * ec);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) G[s] = mma16(G[s], walk_cols<D>(kt, s, m, g), HY);
+            }
+            if (ce_t && addr) {
+                f32x4 R[NS];
+                slice_load<NS>(R, p.rc + ((long)h * p.nchunks + t / tpc) * D * D + j0, D, g, m);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) G[s] += R[s];
+            }
+        }
+    }
+    if (mode == 1)
+        slice_store<NS>(p.ssum + ((long)h * p.nseg + seg) * D * 2 * D + (lin ? 0 : D) + j0, G, 2 * D, g, m);
+    else if (seg == 0)
+        slice_store<NS>(p.dw0 + (long)h * D * D + j0, G, D, g, m);
+}
+
+// The chain of the segment maps on the matrix cores, one wave per (head, 16
+// columns): X <- L_s X + F_s in the direction and with the stores above.
+template <int D>
+__global__ __launch_bounds__(256) void lbw_chain_m(LinBwdParams p, int dir)
+{
+    constexpr int NS = D / 16;
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int h = w / NS, j0 = (w % NS) * 16;
+    const int S = p.nseg;
+    const float *x0 = dir == 0 ? p.w0 : (p.order == 1 ? p.ginit : p.dwf);
+    f32x4 X[NS];
+    if (x0)
+        slice_load<NS>(X, x0 + (long)h * D * D + j0, D, g, m);
+    else
+        slice_identity<NS>(X, j0, g, m, false);
+    for (int t = 0; t < S - 1; ++t) {
+        const int s = dir == 0 ? t : S - 1 - t;  // the map applied
+        const int o = dir == 0 ? s + 1 : s - 1;  // the segment whose start it gives
+        const float *M = p.ssum + ((long)h * S + s) * D * 2 * D;
+        f32x4 Xn[NS];
+        slice_load<NS>(Xn, M + D + j0, 2 * D, g, m);  // F_s
+#pragma unroll
+        for (int a = 0; a < NS; ++a)
+#pragma unroll
+            for (int b = 0; b < NS; ++b)
+                Xn[a] = mma16(Xn[a], *reinterpret_cast<const f32x4 *>(M + (long)(16 * a + m) * 2 * D + 16 * b + 4 * g),
+                              X[b]);
+#pragma unroll
+        for (int a = 0; a < NS; ++a) X[a] = Xn[a];
+        slice_store<NS>(p.sstart + ((long)h * S + o) * D * D + j0, X, D, g, m);
     }
 }
 
@@ -1081,17 +1080,18 @@ __global__ __launch_bounds__(256) void lbw_nc_dq(LinBwdParams p)
 
 }  // namespace
 
-// Segments of the serial passes.  A walk step costs about the same in every
-// workgroup, and a CU holds three (d = 64) or two (d = 128) of them, so the
-// time goes as the segment length times the rounds of workgroups the maps
-// (2 NH (S - 1) d / 16 workgroups) and the walks (NH S d / 16) take; S = 1 is
-// the plain walk.  The smallest estimate wins (ties: fewer segments), with at
-// least 4 chunks (and 64 tokens) per segment.
+// Segments of the serial passes.  A walk step (one 16-token tile) costs about
+// the same in every wave, and one wave per SIMD runs at full speed (a second
+// one shares its matrix core), so the time goes as the segment's tiles times
+// the rounds of 1024 waves the maps (2 NH (S - 1) d / 16 waves) and the walks
+// (NH S d / 16) take, plus the chain; S = 1 is the plain walk.  The smallest
+// estimate wins (ties: fewer segments), with at least 64 tokens per segment.
 static void seg_plan(int NH, int nch, int chunk, int d, int &nseg, int &seg_chunks)
 {
-    const long slots = 256L * (d == 64 ? 3 : 2);
+    const long slots = 1024;
     const long cols = (long)NH * (d / CB);
-    const int min_chunks = max(4, 64 / chunk);
+    const int tpc = chunk / 16;
+    const int min_chunks = max(1, 64 / chunk);
     const int most = max(1, min(64, nch / min_chunks));
     long best = -1;
     nseg = 1;
@@ -1099,7 +1099,7 @@ static void seg_plan(int NH, int nch, int chunk, int d, int &nseg, int &seg_chun
     for (int s = 1; s <= most; ++s) {
         const int sc = (nch + s - 1) / s, ns = (nch + sc - 1) / sc;
         const long rounds = (2 * cols * (ns - 1) + slots - 1) / slots + (cols * ns + slots - 1) / slots;
-        const long est = (long)sc * rounds + 2L * (ns - 1);
+        const long est = (long)sc * tpc * rounds + 2L * (ns - 1);
         if (best < 0 || est < best) {
             best = est;
             nseg = ns;
@@ -1122,26 +1122,36 @@ size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
 }
 
 // The two serial recursions, each as segment maps, chain, walks.
+// (one wave per (head, segment, 16 columns), four waves a workgroup: the
+// column counts D / 16 and 2 D / 16 are multiples of four)
 template <int D, int B, typename E>
 static void lbw_serial_states(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
+    constexpr int NC = D / CB / 4;  // workgroups per (head, segment) and D columns
     if (p.nseg > 1) {
-        lbw_states<D, B, E><<<dim3(NH * (p.nseg - 1) * 2 * (D / CB)), b, 0, st>>>(p, 1);
-        lbw_chain<D><<<dim3(NH * (D / CB)), b, 0, st>>>(p, 0);
+        lbw_states_m<D, E><<<dim3(NH * (p.nseg - 1) * 2 * NC), b, 0, st>>>(p, 1);
+        lbw_chain_m<D><<<dim3(NH * NC), b, 0, st>>>(p, 0);
     }
-    lbw_states<D, B, E><<<dim3(NH * p.nseg * (D / CB)), b, 0, st>>>(p, 0);
+    lbw_states_m<D, E><<<dim3(NH * p.nseg * NC), b, 0, st>>>(p, 0);
 }
 
 template <int D, int B, typename E>
 static void lbw_serial_grad(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
+    constexpr int NC = D / CB / 4;
     if (p.nseg > 1) {
-        lbw_grad<D, B, E><<<dim3(NH * (p.nseg - 1) * 2 * (D / CB)), b, 0, st>>>(p, 1);
-        lbw_chain<D><<<dim3(NH * (D / CB)), b, 0, st>>>(p, 1);
+        if (p.loss == 1)
+            lbw_grad_m<D, E, true><<<dim3(NH * (p.nseg - 1) * 2 * NC), b, 0, st>>>(p, 1);
+        else
+            lbw_grad_m<D, E, false><<<dim3(NH * (p.nseg - 1) * 2 * NC), b, 0, st>>>(p, 1);
+        lbw_chain_m<D><<<dim3(NH * NC), b, 0, st>>>(p, 1);
     }
-    lbw_grad<D, B, E><<<dim3(NH * p.nseg * (D / CB)), b, 0, st>>>(p, 0);
+    if (p.loss == 1)
+        lbw_grad_m<D, E, true><<<dim3(NH * p.nseg * NC), b, 0, st>>>(p, 0);
+    else
+        lbw_grad_m<D, E, false><<<dim3(NH * p.nseg * NC), b, 0, st>>>(p, 0);
 }
 
 template <int D, int B, typename E>
@@ -1199,6 +1209,8 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
     seg_plan(NH, nch, chunk, d, p.nseg, p.seg_chunks);
     p.ssum = tail + 2 * (size_t)NH * d * d;
     p.sstart = p.ssum + (size_t)NH * p.nseg * 2 * d * d;
+    p.tpc = chunk / 16;
+    p.nwt = (Tkv + 15) / 16;
     const bool whole = (d == 64 && (chunk == 16 || chunk == 32)) || (d == 128 && chunk == 16);
     if (whole) {  // a chunk is one step of the serial passes
         p.sub = 1;

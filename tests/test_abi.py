@@ -245,16 +245,16 @@ def test_linear_bwd_validation(kw, code):
 
 
 def _bwd_nseg(NH, nch, chunk, d):
-    """Segments of the backward's serial passes: the count that minimises
-    segment length x (rounds of the 2 NH (S-1) d/16 map workgroups + rounds
-    of the NH S d/16 walk workgroups, 256 x (3 at d = 64, else 2) at a time)
-    + 2 (S - 1), with at least max(4, 64 / chunk) chunks per segment."""
-    slots, cols = 256 * (3 if d == 64 else 2), NH * (d // 16)
+    """Segments of the backward's serial passes: the count that minimises the
+    segment's 16-token tiles x (rounds of the 2 NH (S-1) d/16 map waves +
+    rounds of the NH S d/16 walk waves, 1024 at a time) + 2 (S - 1), with at
+    least max(1, 64 / chunk) chunks (64 tokens) per segment."""
+    slots, cols = 1024, NH * (d // 16)
     best, res = None, 1
-    for s in range(1, max(1, min(64, nch // max(4, 64 // chunk))) + 1):
+    for s in range(1, max(1, min(64, nch // max(1, 64 // chunk))) + 1):
         sc = -(-nch // s)
         ns = -(-nch // sc)
-        est = sc * (-(-(2 * cols * (ns - 1)) // slots) + -(-(cols * ns) // slots)) + 2 * (ns - 1)
+        est = sc * (chunk // 16) * (-(-(2 * cols * (ns - 1)) // slots) + -(-(cols * ns) // slots)) + 2 * (ns - 1)
         if best is None or est < best:
             best, res = est, ns
     return res
@@ -269,7 +269,8 @@ def test_linear_bwd_workspace_query():
         NH = B * H
         return NH * (nch * (3 * d * d + 3 * b * d) + 2 * d * d + _bwd_nseg(NH, nch, b, d) * 3 * d * d) * 4
     assert lib.ttt_linear_bwd_workspace_bytes(4, 8, 4096, 4096, 64, 16, 1, 0, 1) == size(4, 8, 4096, 64, 16)
-    assert _bwd_nseg(32, 256, 16, 64) == 4 and _bwd_nseg(1, 125, 16, 64) == 9
+    assert _bwd_nseg(32, 256, 16, 64) == 8 and _bwd_nseg(32, 1024, 16, 128) == 3
+    assert _bwd_nseg(32, 16, 1024, 128) == 3 and _bwd_nseg(1, 125, 16, 64) == 9
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 50, 50, 64, 32, 0, 0, 0) == size(1, 1, 50, 64, 32)
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 1, 0) == size(1, 1, 50, 64, 32)
     assert lib.ttt_linear_bwd_workspace_bytes(1, 1, 7, 50, 64, 32, 0, 0, 0) == 0
