@@ -615,143 +615,157 @@ __global__ __launch_bounds__(256) void lbw_chain_m(LinBwdParams p, int dir)
     }
 }
 
-// Parallel pass 4, one workgroup per (head, chunk), or per (head, group of up
-// to DEP_TPW tiles of a chunk) when chunks are walked in tiles: the terms that
-// need G = G_{c+1}:  KG = K G,  dV = dU = S~ + H KG,
-// dK = part + H (U G^T [- KG Wc^T]),  d_eta += rowsum(KG * U).
-template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lbw_dep(LinBwdParams p)
+// Four consecutive elements of a token-major tensor as floats (i a multiple of 4).
+template <typename E> __device__ __forceinline__ f32x4 ld4f(const void *p, long i)
 {
-    __shared__ float Gn[D][D + 1], Wc[D][D + 1];
-    // token rows padded to D + 4 floats (16-byte aligned: four elements per read)
-    constexpr int P = D + 4;
-    __shared__ __align__(16) float Ks[B][P], Us[B][P], KGs[B][P];
-    __shared__ float et[B];
-    constexpr int NBD = B * D / 256;
-    // one workgroup per (head, chunk, group of up to DEP_TPW of the chunk's
-    // tiles): the chunk's G_{c+1} and W_c are read once for the group
-    const int gpc = (p.sub + DEP_TPW - 1) / DEP_TPW;
-    const int h = blockIdx.x / (p.nchunks * gpc), rem = blockIdx.x % (p.nchunks * gpc), tid = threadIdx.x;
-    const int ch = rem / gpc, grp = rem % gpc;
-    const int ta = ch * p.sub + grp * DEP_TPW, tb = min(min(ta + DEP_TPW, (ch + 1) * p.sub), p.ntiles);
-    const long tok0 = (long)h * p.T;
-    const long cb = (long)h * p.nchunks + ch;
-    for (int e = tid; e < D * D; e += 256) {
-        Gn[e / D][e % D] = p.gnext[cb * D * D + e];
-        if (p.loss == 1) Wc[e / D][e % D] = p.states[cb * D * D + e];
-    }
-    const bool nc = p.order == 1;  // no outputs per chunk: U from here, no G-free parts
-    for (int c = ta; c < tb; ++c) {
-        const int c0 = c * B, n = min(B, p.T - c0);
-        const long row0 = (long)h * p.rstride + c0;
-        for (int e = tid; e < B * D; e += 256) {
-            const int i = e / D, j = e % D;
-            const bool ok = i < n;
-            Ks[i][j] = ok ? ldf<E>(p.k, (tok0 + c0 + i) * D + j) : 0.f;
-            Us[i][j] = (p.loss == 1 && !nc) ? p.ub[(row0 + i) * D + j]
-                                            : (ok ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f);
-        }
-        if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
-        __syncthreads();
-        if (nc && p.loss == 1) {  // U = V - K W_c
-            float u[NBD];
-    #pragma unroll
-            for (int r = 0; r < NBD; ++r) {
-                const int e = tid + 256 * r, i = e / D, j = e % D;
-                float sacc = 0.f;
-                for (int a = 0; a < D; ++a) sacc += Ks[i][a] * Wc[a][j];
-                u[r] = Us[i][j] - sacc;
-            }
-            __syncthreads();
-    #pragma unroll
-            for (int r = 0; r < NBD; ++r) Us[(tid + 256 * r) / D][(tid + 256 * r) % D] = u[r];
-            __syncthreads();
-        }
-        // thread outputs (i0 + RS r, j): the wave shares its rows, so row reads are
-        // broadcasts and each column element of G is read once for all rows
-        constexpr int RS = 256 / D;
-        const int i0 = tid / D, jl = tid % D;
-        {
-            float sg[NBD];
-    #pragma unroll
-            for (int r = 0; r < NBD; ++r) sg[r] = 0.f;
-    #pragma unroll 2
-            for (int a = 0; a < D; a += 4) {
-                const float g0 = Gn[a][jl], g1 = Gn[a + 1][jl], g2 = Gn[a + 2][jl], g3 = Gn[a + 3][jl];
-    #pragma unroll
-                for (int r = 0; r < NBD; ++r) {
-                    const f32x4 kv = lds4(&Ks[i0 + RS * r][a]);
-                    sg[r] += kv[0] * g0;
-                    sg[r] += kv[1] * g1;
-                    sg[r] += kv[2] * g2;
-                    sg[r] += kv[3] * g3;
-                }
-            }
-    #pragma unroll
-            for (int r = 0; r < NBD; ++r) {
-                const int i = i0 + RS * r;
-                KGs[i][jl] = sg[r];
-                if (i < n) stf<E>(p.dv, (tok0 + c0 + i) * D + jl, (nc ? 0.f : p.st[(row0 + i) * D + jl]) + et[i] * sg[r]);
-            }
-        }
-        __syncthreads();
-        if (tid < 64) {
-            for (int i = 0; i < n; ++i) {
-                float s = 0.f;
-                for (int a = tid; a < D; a += 64) s += KGs[i][a] * Us[i][a];
-                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-                if (tid == 0) p.deta[tok0 + c0 + i] = (nc ? 0.f : p.deta[tok0 + c0 + i]) + s;
-            }
-        }
-        {
-            const int a = jl;  // outputs (i0 + RS r, a)
-            float sk[NBD];
-    #pragma unroll
-            for (int r = 0; r < NBD; ++r) sk[r] = 0.f;
-    #pragma unroll 2
-            for (int j = 0; j < D; j += 4) {
-                const float g[4] = {Gn[a][j], Gn[a][j + 1], Gn[a][j + 2], Gn[a][j + 3]};
-                float w[4] = {0.f, 0.f, 0.f, 0.f};
-                if (p.loss == 1) {
-    #pragma unroll
-                    for (int x = 0; x < 4; ++x) w[x] = Wc[a][j + x];
-                }
-    #pragma unroll
-                for (int r = 0; r < NBD; ++r) {
-                    const f32x4 uv = lds4(&Us[i0 + RS * r][j]);
-                    if (p.loss == 1) {
-                        const f32x4 kg = lds4(&KGs[i0 + RS * r][j]);
-    #pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            sk[r] += uv[x] * g[x];
-                            sk[r] -= kg[x] * w[x];
-                        }
-                    } else {
-    #pragma unroll
-                        for (int x = 0; x < 4; ++x) sk[r] += uv[x] * g[x];
-                    }
-                }
-            }
-    #pragma unroll
-            for (int r = 0; r < NBD; ++r) {
-                const int i = i0 + RS * r;
-                if (i < n) stf<E>(p.dk, (tok0 + c0 + i) * D + a, (nc ? 0.f : p.dkl[(row0 + i) * D + a]) + et[i] * sk[r]);
-            }
-        }
-        __syncthreads();  // the next tile overwrites K, U, KG
-    }
+    if constexpr (sizeof(E) == 2)
+        return to_f32x4(*reinterpret_cast<const bf16x4 *>(static_cast<const __bf16 *>(p) + i));
+    else
+        return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + i);
 }
 
-// ---------------------------------------------------------------------------
-// Chunks of more than 32 tokens (causal order).  The chunk's B x B products
-// (A = (Q K^T) * M and dS = (dO U^T) * M) are taken 16 x 16 blocks at a time:
-// one workgroup per (head, 16-token tile I) walks the tiles of its chunk after
-// I (for the columns i of A and dS that I owns: S~, d_eta's first part, the
-// dA^T Q part of dK) and before I (for the rows t it owns: dA K in dQ).  The
-// residuals U of every tile come first (they are read by the other tiles'
-// workgroups), R_c last (a sum over the whole chunk).
-// ---------------------------------------------------------------------------
-constexpr int TT = 16;  // tokens per tile
+// Parallel pass 4 on the matrix cores (fp32 16x16x4 MFMA): one workgroup per
+// (head, chunk, group of up to DEP_TPW 16-token tiles of the chunk), four
+// waves, wave w owning column tiles w, w + 4, ... of the D / 16.  G_{c+1} and
+// W_c are staged once per workgroup, rows padded by 4 floats; per tile
+//     KG = K G                          (B: columns of G, 4 scalar reads)
+//     dV = S~ + H KG,  d_eta += rowsum(KG * U)
+//     dK = part + H (U G^T [- KG W_c^T]) (B: rows of G and W_c, 16-byte reads)
+// with U and KG exchanged as token rows through LDS (their accumulator order
+// is not the A-operand order).  In the update-then-apply order there are no
+// G-free parts and U is V [- K W_c] (computed here).
+template <int D, typename E, bool MSE>
+__global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
+{
+    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    __shared__ __align__(16) float Gm[D][P];
+    __shared__ __align__(16) float Wm[MSE ? D : 1][P];
+    __shared__ __align__(16) float Us[WT][P];
+    __shared__ __align__(16) float KGs[WT][P];
+    __shared__ float dpart[4][WT];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tpc = p.tpc, gpc = (tpc + DEP_TPW - 1) / DEP_TPW;
+    const int h = blockIdx.x / (p.nchunks * gpc), rem = blockIdx.x % (p.nchunks * gpc);
+    const int ch = rem / gpc, grp = rem % gpc;
+    const int chunk = tpc * WT;
+    const int tstart = ch * chunk + grp * DEP_TPW * WT;
+    const int tend = min(min(tstart + DEP_TPW * WT, (ch + 1) * chunk), p.T);
+    const long tok0 = (long)h * p.T;
+    const long cb = (long)h * p.nchunks + ch;
+    const bool nc = p.order == 1;
+    {
+        const float *gs = p.gnext + cb * D * D, *wsrc = p.states + cb * D * D;
+        for (int e = tid; e < D * D / 4; e += 256) {
+            const int r = e / (D / 4), c = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4 *>(&Gm[r][c]) = *reinterpret_cast<const f32x4 *>(gs + (long)r * D + c);
+            if constexpr (MSE)
+                *reinterpret_cast<f32x4 *>(&Wm[r][c]) = *reinterpret_cast<const f32x4 *>(wsrc + (long)r * D + c);
+        }
+    }
+    for (int t0 = tstart; t0 < tend; t0 += WT) {
+        const int n = min(WT, tend - t0);
+        const long row0 = (long)h * p.rstride + t0;  // the tile's rows in the per-token buffers
+        // U rows: the forward's residuals (MSE, stored by the local pass) or V
+        for (int e = tid; e < WT * D / 4; e += 256) {
+            const int i = e / (D / 4), c = 4 * (e % (D / 4));
+            const int ic = min(i, n - 1);
+            const f32x4 x = (MSE && !nc) ? *reinterpret_cast<const f32x4 *>(p.ub + (row0 + ic) * D + c)
+                                         : ld4f<E>(p.v, (tok0 + t0 + ic) * D + c);
+            *reinterpret_cast<f32x4 *>(&Us[i][c]) = i < n ? x : zero4();
+        }
+        f32x4 Ka[NS];  // A operand: K[t0 + m][16 s + 4 g + j]
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const f32x4 x = ld4f<E>(p.k, (tok0 + t0 + min(m, n - 1)) * D + 16 * s + 4 * g);
+            Ka[s] = m < n ? x : zero4();
+        }
+        f32x4 e4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = p.eta[tok0 + t0 + min(4 * g + r, n - 1)];
+            e4[r] = 4 * g + r < n ? x : 0.f;
+        }
+        __syncthreads();  // G, W_c (first tile) and U staged
+        if (MSE && nc) {  // U = V - K W_c
+            f32x4 Uc[NCT];
+#pragma unroll
+            for (int u = 0; u < NCT; ++u) {
+                const int ct = wv + 4 * u;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    acc = mma16(acc, Ka[s],
+                                f32x4{Wm[16 * s + 4 * g][16 * ct + m], Wm[16 * s + 4 * g + 1][16 * ct + m],
+                                      Wm[16 * s + 4 * g + 2][16 * ct + m], Wm[16 * s + 4 * g + 3][16 * ct + m]});
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Uc[u][r] = Us[4 * g + r][16 * ct + m] - acc[r];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < NCT; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Us[4 * g + r][16 * (wv + 4 * u) + m] = Uc[u][r];
+            __syncthreads();
+        }
+        // KG, dV, this wave's part of d_eta; KG rows to LDS
+        float dp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) {
+            const int ct = wv + 4 * u, col = 16 * ct + m;
+            f32x4 kg = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                kg = mma16(kg, Ka[s],
+                           f32x4{Gm[16 * s + 4 * g][col], Gm[16 * s + 4 * g + 1][col], Gm[16 * s + 4 * g + 2][col],
+                                 Gm[16 * s + 4 * g + 3][col]});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g + r;
+                dp[r] += kg[r] * Us[i][col];
+                KGs[i][col] = kg[r];
+                if (i < n)
+                    stf<E>(p.dv, (tok0 + t0 + i) * D + col, (nc ? 0.f : p.st[(row0 + i) * D + col]) + e4[r] * kg[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) dp[r] += __shfl_xor(dp[r], o, 64);
+            if (m == 0) dpart[wv][4 * g + r] = dp[r];
+        }
+        __syncthreads();  // KG rows and the d_eta parts
+        if (tid < n) {
+            const long te = tok0 + t0 + tid;
+            p.deta[te] = (nc ? 0.f : p.deta[te]) + (dpart[0][tid] + dpart[1][tid] + dpart[2][tid] + dpart[3][tid]);
+        }
+        // dK = part + H (U G^T [- KG W_c^T])
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) {
+            const int ct = wv + 4 * u, col = 16 * ct + m;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                acc = mma16(acc, *reinterpret_cast<const f32x4 *>(&Us[m][16 * s + 4 * g]),
+                            *reinterpret_cast<const f32x4 *>(&Gm[col][16 * s + 4 * g]));
+            if constexpr (MSE) {
+                f32x4 acc2 = zero4();
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    acc2 = mma16(acc2, *reinterpret_cast<const f32x4 *>(&KGs[m][16 * s + 4 * g]),
+                                 *reinterpret_cast<const f32x4 *>(&Wm[col][16 * s + 4 * g]));
+                acc -= acc2;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g + r;
+                if (i < n)
+                    stf<E>(p.dk, (tok0 + t0 + i) * D + col, (nc ? 0.f : p.dkl[(row0 + i) * D + col]) + e4[r] * acc[r]);
+            }
+        }
+        __syncthreads();  // the next tile overwrites U, KG and the d_eta parts
+    }
+}
 
 // U = V - K W_c for one tile (MSE), into the per-token buffer.
 template <int D, typename E>
@@ -1154,6 +1168,17 @@ static void lbw_serial_grad(const LinBwdParams &p, int NH, hipStream_t st)
         lbw_grad_m<D, E, false><<<dim3(NH * p.nseg * NC), b, 0, st>>>(p, 0);
 }
 
+// The dependent pass: one workgroup per (head, chunk, group of DEP_TPW tiles).
+template <int D, typename E>
+static void lbw_dep_launch(const LinBwdParams &p, int NH, hipStream_t st)
+{
+    const dim3 grid(NH * p.nchunks * ((p.tpc + DEP_TPW - 1) / DEP_TPW));
+    if (p.loss == 1)
+        lbw_dep_m<D, E, true><<<grid, dim3(256), 0, st>>>(p);
+    else
+        lbw_dep_m<D, E, false><<<grid, dim3(256), 0, st>>>(p);
+}
+
 template <int D, int B, typename E>
 static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
 {
@@ -1169,7 +1194,7 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_serial_grad<D, B, E>(p, NH, st);
-    lbw_dep<D, B, E><<<dim3(NH * p.nchunks * ((p.sub + DEP_TPW - 1) / DEP_TPW)), b, 0, st>>>(p);
+    lbw_dep_launch<D, E>(p, NH, st);
 }
 
 // Chunks of 16 k tokens (k > 1, or d = 128 with 32): the serial and dependent
@@ -1189,7 +1214,7 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_serial_grad<D, TT, E>(p, NH, st);
-    lbw_dep<D, TT, E><<<dim3(NH * p.nchunks * ((p.sub + DEP_TPW - 1) / DEP_TPW)), b, 0, st>>>(p);
+    lbw_dep_launch<D, E>(p, NH, st);
 }
 
 hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
