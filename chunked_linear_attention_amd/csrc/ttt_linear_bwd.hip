@@ -767,6 +767,17 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Chunks of more than 32 tokens (causal order).  The chunk's B x B products
+// (A = (Q K^T) * M and dS = (dO U^T) * M) are taken 16 x 16 blocks at a time:
+// one workgroup per (head, 16-token tile I) walks the tiles of its chunk after
+// I (for the columns i of A and dS that I owns: S~, d_eta's first part, the
+// dA^T Q part of dK) and before I (for the rows t it owns: dA K in dQ).  The
+// residuals U of every tile come first (they are read by the other tiles'
+// workgroups), R_c last (a sum over the whole chunk).
+// ---------------------------------------------------------------------------
+constexpr int TT = 16;  // tokens per tile
+
 // U = V - K W_c for one tile (MSE), into the per-token buffer.
 template <int D, typename E>
 __global__ __launch_bounds__(256) void lbw_u(LinBwdParams p)
