@@ -270,17 +270,6 @@ __global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
     lbw_local_body<D, B, E>(p);
 }
 
-// d = 64, chunk 16: three waves per SIMD (three workgroups per CU; the LDS
-// allows it).  The register cap costs a few spilled values (10 VGPRs) and
-// still measured ~3.5% faster on the whole backward than two waves per SIMD.
-// The other shapes keep the compiler's own occupancy (at d = 128 the LDS
-// allows one workgroup per CU, so a cap would only cost registers).
-template <typename E>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void lbw_local_w3(LinBwdParams p)
-{
-    lbw_local_body<64, 16, E>(p);
-}
-
 // ---------------------------------------------------------------------------
 // The serial passes on the matrix cores (fp32 16x16x4 MFMA).  One wave per
 // (head, segment, 16 columns) steps over 16-token tiles (a chunk of b tokens
@@ -622,6 +611,154 @@ template <typename E> __device__ __forceinline__ f32x4 ld4f(const void *p, long 
         return to_f32x4(*reinterpret_cast<const bf16x4 *>(static_cast<const __bf16 *>(p) + i));
     else
         return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + i);
+}
+
+// Parallel pass 2 on the matrix cores for 16-token chunks (fp32 16x16x4
+// MFMA): one workgroup per (head, chunk), four waves, wave w owning column
+// tiles w, w + 4, ... of the D / 16.  W_c and the chunk's token rows are
+// staged in LDS (rows padded by 4 floats); the chunk's 16 x 16 products A =
+// (Q K^T) * M and dA = (dO U^T) * M are formed by every wave (one tile each),
+// and their accumulators serve directly as the A operand of A^T X and dA^T X.
+template <int D, typename E, bool MSE>
+__global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
+{
+    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    __shared__ __align__(16) float Wm[D][P];
+    __shared__ __align__(16) float Qs[WT][P], Ks[WT][P], Os[WT][P], Us[WT][P], Ss[WT][P];
+    __shared__ __align__(16) float dAs[WT][WT + 4];
+    __shared__ float et[WT];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks;
+    const long tok0 = (long)h * p.T;
+    const int t0 = c * WT, n = min(WT, p.T - t0);
+    const long cb = (long)h * p.nchunks + c;
+    const long row0 = (long)h * p.rstride + t0;  // the chunk's rows in the per-token buffers
+    {
+        const float *src = p.states + cb * D * D;
+        for (int e = tid; e < D * D / 4; e += 256) {
+            const int r = e / (D / 4), col = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4 *>(&Wm[r][col]) = *reinterpret_cast<const f32x4 *>(src + (long)r * D + col);
+        }
+        for (int e = tid; e < WT * D / 4; e += 256) {
+            const int i = e / (D / 4), col = 4 * (e % (D / 4));
+            const long gi = (tok0 + t0 + min(i, n - 1)) * D + col;
+            const bool ok = i < n;
+            const f32x4 q = ld4f<E>(p.q, gi), k = ld4f<E>(p.k, gi), v = ld4f<E>(p.v, gi), o = ld4f<E>(p.dout, gi);
+            *reinterpret_cast<f32x4 *>(&Qs[i][col]) = ok ? q : zero4();
+            *reinterpret_cast<f32x4 *>(&Ks[i][col]) = ok ? k : zero4();
+            *reinterpret_cast<f32x4 *>(&Us[i][col]) = ok ? v : zero4();
+            *reinterpret_cast<f32x4 *>(&Os[i][col]) = ok ? o : zero4();
+        }
+        if (tid < WT) et[tid] = tid < n ? p.eta[tok0 + t0 + tid] : 0.f;
+    }
+    __syncthreads();
+    if constexpr (MSE) {  // U = V - K W_c (rows stored for the dependent pass)
+        f32x4 Uc[NCT];
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) {
+            const int col = 16 * (wv + 4 * u) + m;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                acc = mma16(acc, *reinterpret_cast<const f32x4 *>(&Ks[m][16 * s + 4 * g]),
+                            f32x4{Wm[16 * s + 4 * g][col], Wm[16 * s + 4 * g + 1][col], Wm[16 * s + 4 * g + 2][col],
+                                  Wm[16 * s + 4 * g + 3][col]});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Uc[u][r] = Us[4 * g + r][col] - acc[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) {
+            const int col = 16 * (wv + 4 * u) + m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Us[4 * g + r][col] = Uc[u][r];
+                p.ub[(row0 + 4 * g + r) * D + col] = Uc[u][r];
+            }
+        }
+        __syncthreads();
+    }
+    // A = (Q K^T) * M and dA = (dO U^T) * M: lane (g, n) holds [t = 4 g + r][i = n]
+    f32x4 A = zero4(), dA = zero4();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        A = mma16(A, *reinterpret_cast<const f32x4 *>(&Qs[m][16 * s + 4 * g]),
+                  *reinterpret_cast<const f32x4 *>(&Ks[m][16 * s + 4 * g]));
+        dA = mma16(dA, *reinterpret_cast<const f32x4 *>(&Os[m][16 * s + 4 * g]),
+                   *reinterpret_cast<const f32x4 *>(&Us[m][16 * s + 4 * g]));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool keep = 4 * g + r >= m;  // key i = m not after query t
+        A[r] = keep ? A[r] : 0.f;
+        dA[r] = keep ? dA[r] : 0.f;
+    }
+    const float eti = et[m];
+    if (wv == 0) {  // d_eta, the G-free part: sum_t dS[t][i] A[t][i]
+        float x = dA[0] * A[0] + dA[1] * A[1] + dA[2] * A[2] + dA[3] * A[3];
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        if (g == 0 && m < n) p.deta[tok0 + t0 + m] = x;
+    }
+    dA = dA * eti;  // dA H (column i scaled by eta_i)
+    if (wv == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dAs[4 * g + r][m] = dA[r];
+    // S~ = H A^T dO (rows i), kept for dK and R_c and stored for the dependent pass
+#pragma unroll
+    for (int u = 0; u < NCT; ++u) {
+        const int col = 16 * (wv + 4 * u) + m;
+        f32x4 sv = mma16(zero4(), A, f32x4{Os[4 * g][col], Os[4 * g + 1][col], Os[4 * g + 2][col], Os[4 * g + 3][col]});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = et[4 * g + r] * sv[r];
+            Ss[4 * g + r][col] = x;
+            p.st[(row0 + 4 * g + r) * D + col] = x;
+        }
+    }
+    __syncthreads();  // S~ rows and dA H complete
+#pragma unroll
+    for (int u = 0; u < NCT; ++u) {
+        const int col = 16 * (wv + 4 * u) + m;
+        // dQ = dO W_c^T + dA K
+        f32x4 dq = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            dq = mma16(dq, *reinterpret_cast<const f32x4 *>(&Os[m][16 * s + 4 * g]),
+                       *reinterpret_cast<const f32x4 *>(&Wm[col][16 * s + 4 * g]));
+        dq = mma16(dq, *reinterpret_cast<const f32x4 *>(&dAs[m][4 * g]),
+                   f32x4{Ks[4 * g][col], Ks[4 * g + 1][col], Ks[4 * g + 2][col], Ks[4 * g + 3][col]});
+        // dK part = dA^T Q [- S~ W_c^T]
+        f32x4 dk = mma16(zero4(), dA, f32x4{Qs[4 * g][col], Qs[4 * g + 1][col], Qs[4 * g + 2][col], Qs[4 * g + 3][col]});
+        if constexpr (MSE) {
+            f32x4 sw = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                sw = mma16(sw, *reinterpret_cast<const f32x4 *>(&Ss[m][16 * s + 4 * g]),
+                           *reinterpret_cast<const f32x4 *>(&Wm[col][16 * s + 4 * g]));
+            dk -= sw;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            if (i < n) stf<E>(p.dq, (tok0 + t0 + i) * D + col, dq[r]);
+            p.dkl[(row0 + i) * D + col] = dk[r];
+        }
+        // R_c = Q^T dO [- K^T S~], rows a = 16 ra + 4 g + r of this column tile
+        float *R = p.rc + cb * D * D;
+        const f32x4 ob = f32x4{Os[4 * g][col], Os[4 * g + 1][col], Os[4 * g + 2][col], Os[4 * g + 3][col]};
+        const f32x4 sb = f32x4{Ss[4 * g][col], Ss[4 * g + 1][col], Ss[4 * g + 2][col], Ss[4 * g + 3][col]};
+#pragma unroll
+        for (int ra = 0; ra < NS; ++ra) {
+            const int a = 16 * ra + m;
+            f32x4 rv = mma16(zero4(), f32x4{Qs[4 * g][a], Qs[4 * g + 1][a], Qs[4 * g + 2][a], Qs[4 * g + 3][a]}, ob);
+            if constexpr (MSE)
+                rv -= mma16(zero4(), f32x4{Ks[4 * g][a], Ks[4 * g + 1][a], Ks[4 * g + 2][a], Ks[4 * g + 3][a]}, sb);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[(long)(16 * ra + 4 * g + r) * D + col] = rv[r];
+        }
+    }
 }
 
 // Parallel pass 4 on the matrix cores (fp32 16x16x4 MFMA): one workgroup per
@@ -1196,10 +1333,14 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
     const dim3 b(256);
     lbw_serial_states<D, B, E>(p, NH, st);
     if (p.order == 0) {
-        if constexpr (D == 64 && B == 16)
-            lbw_local_w3<E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
-        else
+        if constexpr (B == 16) {
+            if (p.loss == 1)
+                lbw_local_m<D, E, true><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+            else
+                lbw_local_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        } else {
             lbw_local<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        }
     } else {
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
