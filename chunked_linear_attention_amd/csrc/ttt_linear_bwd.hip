@@ -907,272 +907,314 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
 // ---------------------------------------------------------------------------
 // Chunks of more than 32 tokens (causal order).  The chunk's B x B products
 // (A = (Q K^T) * M and dS = (dO U^T) * M) are taken 16 x 16 blocks at a time:
-// one workgroup per (head, 16-token tile I) walks the tiles of its chunk after
-// I (for the columns i of A and dS that I owns: S~, d_eta's first part, the
-// dA^T Q part of dK) and before I (for the rows t it owns: dA K in dQ).  The
-// residuals U of every tile come first (they are read by the other tiles'
-// workgroups), R_c last (a sum over the whole chunk).
+// the wave of tile I walks the tiles of its chunk after I (for the columns i
+// of A and dS that I owns: S~, d_eta's first part, the dA^T Q part of dK) and
+// before I (for the rows t it owns: dA K in dQ).  The residuals U of every
+// tile come first (they are read by the other tiles' waves), R_c last (a sum
+// over the whole chunk).
 // ---------------------------------------------------------------------------
 constexpr int TT = 16;  // tokens per tile
 
-// U = V - K W_c for one tile (MSE), into the per-token buffer.
+// U = V - K W_c (MSE) of 16-token tiles on the matrix cores: one workgroup per
+// (head, chunk, group of up to DEP_TPW tiles), W_c staged once, wave w owning
+// column tiles w, w + 4, ...
 template <int D, typename E>
-__global__ __launch_bounds__(256) void lbw_u(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_u_m(LinBwdParams p)
 {
-    __shared__ float Wc[D][D + 1];
-    __shared__ __align__(16) float Ks[TT][D + 4];
-    const int h = blockIdx.x / p.ntiles, t = blockIdx.x % p.ntiles, tid = threadIdx.x;
+    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    __shared__ __align__(16) float Wm[D][P];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tpc = p.tpc, gpc = (tpc + DEP_TPW - 1) / DEP_TPW;
+    const int h = blockIdx.x / (p.nchunks * gpc), rem = blockIdx.x % (p.nchunks * gpc);
+    const int ch = rem / gpc, grp = rem % gpc;
+    const int tstart = ch * tpc * WT + grp * DEP_TPW * WT;
+    const int tend = min(min(tstart + DEP_TPW * WT, (ch + 1) * tpc * WT), p.T);
     const long tok0 = (long)h * p.T;
-    const int c0 = t * TT, n = min(TT, p.T - c0);
-    const float *src = p.states + ((long)h * p.nchunks + t / p.sub) * D * D;
-    for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
-    for (int e = tid; e < TT * D; e += 256) {
-        const int i = e / D, a = e % D;
-        Ks[i][a] = i < n ? ldf<E>(p.k, (tok0 + c0 + i) * D + a) : 0.f;
+    {
+        const float *src = p.states + ((long)h * p.nchunks + ch) * D * D;
+        for (int e = tid; e < D * D / 4; e += 256) {
+            const int r = e / (D / 4), c = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4 *>(&Wm[r][c]) = *reinterpret_cast<const f32x4 *>(src + (long)r * D + c);
+        }
     }
     __syncthreads();
-    const long row0 = (long)h * p.rstride + c0;
-    for (int e = tid; e < TT * D; e += 256) {
-        const int i = e / D, j = e % D;
-        float sacc = 0.f;
-#pragma unroll 4
-        for (int a = 0; a < D; a += 4) {
-            const f32x4 kv = lds4(&Ks[i][a]);
+    for (int t0 = tstart; t0 < tend; t0 += WT) {
+        const int n = min(WT, tend - t0);
+        const long row0 = (long)h * p.rstride + t0;
+        f32x4 Ka[NS];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) sacc += kv[x] * Wc[a + x][j];
+        for (int s = 0; s < NS; ++s) {
+            const f32x4 x = ld4f<E>(p.k, (tok0 + t0 + min(m, n - 1)) * D + 16 * s + 4 * g);
+            Ka[s] = m < n ? x : zero4();
         }
-        const float v = i < n ? ldf<E>(p.v, (tok0 + c0 + i) * D + j) : 0.f;
-        p.ub[(row0 + i) * D + j] = v - sacc;
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) {
+            const int col = 16 * (wv + 4 * u) + m;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                acc = mma16(acc, Ka[s],
+                            f32x4{Wm[16 * s + 4 * g][col], Wm[16 * s + 4 * g + 1][col], Wm[16 * s + 4 * g + 2][col],
+                                  Wm[16 * s + 4 * g + 3][col]});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g + r;
+                const float v = ldf<E>(p.v, (tok0 + t0 + min(i, n - 1)) * D + col);
+                p.ub[(row0 + i) * D + col] = i < n ? v - acc[r] : 0.f;
+            }
+        }
     }
 }
 
-// Everything of tile I that needs no G: dQ, d_eta's first part, S~ and the
-// G-free part of dK (as lbw_local does for a whole chunk).
-template <int D, typename E>
-__global__ __launch_bounds__(256) void lbw_local_tiled(LinBwdParams p)
+// R_c = Q^T dO [- K^T S~] over a whole chunk on the matrix cores: one
+// workgroup per (head, chunk), wave w owning column tiles w, w + 4, ... and
+// every row tile; the chunk's 16-token tiles are staged in LDS one at a time
+// (the next one loaded into registers meanwhile).
+template <int D, typename E, bool MSE>
+__global__ __launch_bounds__(256) void lbw_rc_m(LinBwdParams p)
 {
-    constexpr int P = D + 4, RS = 256 / D, NR = TT / RS;  // thread outputs (i0 + RS r, j)
-    __shared__ float Wc[D][D + 1];
-    __shared__ __align__(16) float QI[TT][P], KI[TT][P], UI[TT][P], dOI[TT][P], XJ[TT][P], YJ[TT][P];
-    __shared__ float Am[TT][TT + 1], dAm[TT][TT + 1];
-    __shared__ float etI[TT], etJ[TT];
-    const int h = blockIdx.x / p.ntiles, I = blockIdx.x % p.ntiles, tid = threadIdx.x;
+    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    constexpr int NL = WT * D / 4 / 256;  // 4-element pieces per thread and tensor
+    __shared__ __align__(16) float Qs[WT][P], Os[WT][P], Ks[MSE ? WT : 1][P], Ss[MSE ? WT : 1][P];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks;
     const long tok0 = (long)h * p.T;
-    const int cI = I / p.sub;
-    const int J0 = cI * p.sub, J1 = min(p.ntiles, J0 + p.sub);  // the chunk's tiles [J0, J1)
-    const int c0 = I * TT, n = min(TT, p.T - c0);
-    const long row0 = (long)h * p.rstride;  // the head's rows in the per-token buffers
-    const bool mse = p.loss == 1;
-    const float *src = p.states + ((long)h * p.nchunks + cI) * D * D;
-    for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
-    for (int e = tid; e < TT * D; e += 256) {
-        const int i = e / D, a = e % D;
-        const bool ok = i < n;
-        const long g = (tok0 + c0 + i) * D + a;
-        QI[i][a] = ok ? ldf<E>(p.q, g) : 0.f;
-        KI[i][a] = ok ? ldf<E>(p.k, g) : 0.f;
-        dOI[i][a] = ok ? ldf<E>(p.dout, g) : 0.f;
-        UI[i][a] = mse ? p.ub[(row0 + c0 + i) * D + a] : (ok ? ldf<E>(p.v, g) : 0.f);
-    }
-    if (tid < TT) etI[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
-    const int i0 = tid / D, j = tid % D;
-    float sv[NR], dk[NR], dq[NR];
+    const int t0 = c * p.tpc * WT, t1 = min(p.T, t0 + p.tpc * WT);
+    f32x4 acc[NS][NCT];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) sv[r] = dk[r] = dq[r] = 0.f;
-    float de = 0.f;  // d_eta's first part for row tid (< TT)
-    __syncthreads();
-    // The other tiles' operands go global -> registers one tile ahead.
-    constexpr int NL = TT * D / 256;
-    float xr[NL], yr[NL], er = 0.f;
-    auto load_after = [&](int J) {  // Q and dO of tile J (phase J >= I)
-        const int cj = J * TT, nj = min(TT, p.T - cj);
+    for (int ra = 0; ra < NS; ++ra)
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) acc[ra][u] = zero4();
+    f32x4 rq[NL], ro[NL], rk[MSE ? NL : 1], rs[MSE ? NL : 1];
+    auto load = [&](int s0) {
+        const int n = min(WT, t1 - s0);
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
-            const int e = tid + 256 * k, t = e / D, a = e % D;
-            const bool ok = t < nj;
-            xr[k] = ok ? ldf<E>(p.q, (tok0 + cj + t) * D + a) : 0.f;
-            yr[k] = ok ? ldf<E>(p.dout, (tok0 + cj + t) * D + a) : 0.f;
+            const int e = tid + 256 * k, i = e / (D / 4), col = 4 * (e % (D / 4));
+            const int ic = min(i, n - 1);
+            const bool ok = i < n;
+            const long gi = (tok0 + s0 + ic) * D + col;
+            const f32x4 q = ld4f<E>(p.q, gi), o = ld4f<E>(p.dout, gi);
+            rq[k] = ok ? q : zero4();
+            ro[k] = ok ? o : zero4();
+            if constexpr (MSE) {
+                const f32x4 kk = ld4f<E>(p.k, gi);
+                const f32x4 ss = *reinterpret_cast<const f32x4 *>(p.st + ((long)h * p.rstride + s0 + ic) * D + col);
+                rk[k] = ok ? kk : zero4();
+                rs[k] = ok ? ss : zero4();
+            }
         }
     };
-    auto load_before = [&](int J) {  // U (or V) and K of tile J, and its eta (phase J <= I)
-        const int cj = J * TT, nj = min(TT, p.T - cj);
+    load(t0);
+    for (int s0 = t0; s0 < t1; s0 += WT) {
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
-            const int e = tid + 256 * k, t = e / D, a = e % D;
-            const bool ok = t < nj;
-            xr[k] = mse ? p.ub[(row0 + cj + t) * D + a] : (ok ? ldf<E>(p.v, (tok0 + cj + t) * D + a) : 0.f);
-            yr[k] = ok ? ldf<E>(p.k, (tok0 + cj + t) * D + a) : 0.f;
-        }
-        if (tid < TT) er = tid < nj ? p.eta[tok0 + cj + tid] : 0.f;
-    };
-    auto put = [&]() {
-#pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            const int e = tid + 256 * k;
-            XJ[e / D][e % D] = xr[k];
-            YJ[e / D][e % D] = yr[k];
-        }
-        if (tid < TT) etJ[tid] = er;
-    };
-    // the chunk's tiles J >= I: A[t][i] = q_t . k_i, dS[t][i] = dO_t . u_i (t in J, i in I, t >= i)
-    load_after(I);
-    for (int J = I; J < J1; ++J) {
-        put();
-        __syncthreads();
-        if (J + 1 < J1) load_after(J + 1);
-        else load_before(J0);
-        {
-            const int t = tid / TT, i = tid % TT;  // one (t, i) pair per thread
-            float sa = 0.f, sd = 0.f;
-            if (J > I || t >= i) {
-#pragma unroll 4
-                for (int a = 0; a < D; a += 4) {
-                    const f32x4 x = lds4(&XJ[t][a]), y = lds4(&YJ[t][a]);
-                    const f32x4 kk = lds4(&KI[i][a]), u = lds4(&UI[i][a]);
-#pragma unroll
-                    for (int z = 0; z < 4; ++z) {
-                        sa += x[z] * kk[z];
-                        sd += y[z] * u[z];
-                    }
-                }
+            const int e = tid + 256 * k, i = e / (D / 4), col = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4 *>(&Qs[i][col]) = rq[k];
+            *reinterpret_cast<f32x4 *>(&Os[i][col]) = ro[k];
+            if constexpr (MSE) {
+                *reinterpret_cast<f32x4 *>(&Ks[i][col]) = rk[k];
+                *reinterpret_cast<f32x4 *>(&Ss[i][col]) = rs[k];
             }
-            Am[t][i] = sa;
-            dAm[t][i] = sd;
         }
         __syncthreads();
-        if (tid < TT)
-            for (int t = 0; t < TT; ++t) de += dAm[t][tid] * Am[t][tid];
+        if (s0 + WT < t1) load(s0 + WT);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int i = i0 + RS * r;
-            float s1 = 0.f, s2 = 0.f;
-            for (int t = 0; t < TT; ++t) {
-                s1 += Am[t][i] * YJ[t][j];   // S~ (before eta)
-                s2 += dAm[t][i] * XJ[t][j];  // dA^T Q (before eta)
+        for (int u = 0; u < NCT; ++u) {
+            const int col = 16 * (wv + 4 * u) + m;
+            const f32x4 ob = f32x4{Os[4 * g][col], Os[4 * g + 1][col], Os[4 * g + 2][col], Os[4 * g + 3][col]};
+            f32x4 sb = zero4();
+            if constexpr (MSE) sb = -f32x4{Ss[4 * g][col], Ss[4 * g + 1][col], Ss[4 * g + 2][col], Ss[4 * g + 3][col]};
+#pragma unroll
+            for (int ra = 0; ra < NS; ++ra) {
+                const int a = 16 * ra + m;
+                acc[ra][u] = mma16(acc[ra][u], f32x4{Qs[4 * g][a], Qs[4 * g + 1][a], Qs[4 * g + 2][a], Qs[4 * g + 3][a]}, ob);
+                if constexpr (MSE)
+                    acc[ra][u] =
+                        mma16(acc[ra][u], f32x4{Ks[4 * g][a], Ks[4 * g + 1][a], Ks[4 * g + 2][a], Ks[4 * g + 3][a]}, sb);
             }
-            sv[r] += s1;
-            dk[r] += s2;
-        }
-        __syncthreads();
-    }
-    // the chunk's tiles J <= I: dA[t][s] = eta_s dO_t . u_s (t in I, s in J, s <= t)
-    for (int J = J0; J <= I; ++J) {
-        put();
-        __syncthreads();
-        if (J + 1 <= I) load_before(J + 1);
-        {
-            const int t = tid / TT, s2 = tid % TT;
-            float sd = 0.f;
-            if (J < I || s2 <= t) {
-#pragma unroll 4
-                for (int a = 0; a < D; a += 4) {
-                    const f32x4 y = lds4(&dOI[t][a]), u = lds4(&XJ[s2][a]);
-#pragma unroll
-                    for (int z = 0; z < 4; ++z) sd += y[z] * u[z];
-                }
-            }
-            dAm[t][s2] = sd * etJ[s2];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int t = i0 + RS * r;
-            float s1 = 0.f;
-            for (int s2 = 0; s2 < TT; ++s2) s1 += dAm[t][s2] * YJ[s2][j];
-            dq[r] += s1;
-        }
-        __syncthreads();
-    }
-    // finish: S~ = eta_i (A^T dO), dK part = eta_i (dS^T Q) [- S~ W_c^T], dQ += dO W_c^T
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int i = i0 + RS * r;
-        sv[r] *= etI[i];
-        XJ[i][j] = sv[r];
-        p.st[(row0 + c0 + i) * D + j] = sv[r];
-    }
-    if (tid < TT && tid < n) p.deta[tok0 + c0 + tid] = de;
-    __syncthreads();
-    const int a = j;  // outputs (i0 + RS r, a)
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int i = i0 + RS * r;
-        float sq = 0.f, sk = 0.f;
-        for (int jj = 0; jj < D; ++jj) {
-            const float w = Wc[a][jj];
-            sq += dOI[i][jj] * w;
-            if (mse) sk += XJ[i][jj] * w;
-        }
-        if (i < n) stf<E>(p.dq, (tok0 + c0 + i) * D + a, dq[r] + sq);
-        p.dkl[(row0 + c0 + i) * D + a] = etI[i] * dk[r] - sk;
-    }
-}
-
-// R_c = Q^T dO [- K^T S~] over a whole chunk, one workgroup per (head,
-// chunk, 16 columns), tokens in tiles of 32.
-template <int D, typename E>
-__global__ __launch_bounds__(256) void lbw_rc(LinBwdParams p)
-{
-    constexpr int NCB = D / CB, NR = D * CB / 256, TK = 32;
-    __shared__ float Qs[TK][D + 1], Ks[TK][D + 1], dOs[TK][CB + 1], Ss[TK][CB + 1];
-    const int h = blockIdx.x / (p.nchunks * NCB), rem = blockIdx.x % (p.nchunks * NCB);
-    const int c = rem / NCB, j0 = (rem % NCB) * CB, tid = threadIdx.x;
-    const long tok0 = (long)h * p.T, row0 = (long)h * p.rstride;
-    const int chunk = p.sub * TT;
-    const int t0 = c * chunk, t1 = min(p.T, t0 + chunk);
-    const bool mse = p.loss == 1;
-    const int jj = tid % CB, ab = tid / CB;  // outputs (ab + 16 r, j0 + jj)
-    float acc[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-    // the next 32 tokens' operands go global -> registers while these compute
-    constexpr int NQ = TK * D / 256, NS = TK * CB / 256;
-    float qr[NQ], kr[NQ], orr[NS], sr[NS];
-    auto load = [&](int s) {
-        const int n = min(TK, t1 - s);
-#pragma unroll
-        for (int k = 0; k < NQ; ++k) {
-            const int e = tid + 256 * k, t = e / D, a = e % D;
-            const bool ok = t < n;
-            qr[k] = ok ? ldf<E>(p.q, (tok0 + s + t) * D + a) : 0.f;
-            kr[k] = (ok && mse) ? ldf<E>(p.k, (tok0 + s + t) * D + a) : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const int e = tid + 256 * k, t = e / CB, q = e % CB;
-            const bool ok = t < n;
-            orr[k] = ok ? ldf<E>(p.dout, (tok0 + s + t) * D + j0 + q) : 0.f;
-            sr[k] = (ok && mse) ? p.st[(row0 + s + t) * D + j0 + q] : 0.f;
-        }
-    };
-    if (t0 < t1) load(t0);
-    for (int s = t0; s < t1; s += TK) {
-#pragma unroll
-        for (int k = 0; k < NQ; ++k) {
-            const int e = tid + 256 * k;
-            Qs[e / D][e % D] = qr[k];
-            Ks[e / D][e % D] = kr[k];
-        }
-#pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const int e = tid + 256 * k;
-            dOs[e / CB][e % CB] = orr[k];
-            Ss[e / CB][e % CB] = sr[k];
-        }
-        __syncthreads();
-        if (s + TK < t1) load(s + TK);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int a = ab + (256 / CB) * r;
-            float x = 0.f;
-            for (int t = 0; t < TK; ++t) x += Qs[t][a] * dOs[t][jj] - Ks[t][a] * Ss[t][jj];
-            acc[r] += x;
         }
         __syncthreads();
     }
     float *R = p.rc + ((long)h * p.nchunks + c) * D * D;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) R[(long)(ab + (256 / CB) * r) * D + j0 + jj] = acc[r];
+    for (int u = 0; u < NCT; ++u)
+#pragma unroll
+        for (int ra = 0; ra < NS; ++ra)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[(long)(16 * ra + 4 * g + r) * D + 16 * (wv + 4 * u) + m] = acc[ra][u][r];
+}
+
+// Everything of the tiles of a chunk that needs no G, on the matrix cores:
+// one workgroup per (head, chunk, group of 4 tiles), one wave per tile I
+// (K_I, U_I and dO_I held as fragments, its S~, dK part and dQ as
+// accumulators over all columns).  The chunk's other tiles J are staged in
+// LDS once for the four waves: first J >= I (Q_J and dO_J: A[t][i] = q_t . k_i
+// and dS[t][i] = dO_t . u_i for t in J, i in I, giving S~ += A^T dO_J,
+// dK += dS^T Q_J and d_eta), then J <= I (U_J and K_J: dA^T[s][t] = eta_s
+// u_s . dO_t for s in J, t in I, giving dQ += dA K_J).  Last, dQ += dO_I W_c^T
+// and dK = H dK [- S~ W_c^T] with W_c read from L2.
+template <int D, typename E, bool MSE>
+__global__ __launch_bounds__(256) void lbw_local_tiled_m(LinBwdParams p)
+{
+    constexpr int NS = D / 16, P = D + 4;
+    constexpr int NL = WT * D / 4 / 256;  // 4-element pieces per thread and tensor of a J tile
+    __shared__ __align__(16) float XJ[WT][P], YJ[WT][P];
+    __shared__ __align__(16) float SW[4][WT][P];  // each wave's S~ rows
+    __shared__ float etJ[WT];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tpc = p.tpc, gpc = (tpc + 3) / 4;
+    const int h = blockIdx.x / (p.nchunks * gpc), rem = blockIdx.x % (p.nchunks * gpc);
+    const int ch = rem / gpc, grp = rem % gpc;
+    const int J0 = ch * tpc, J1 = min(J0 + tpc, p.nwt);  // the chunk's tiles [J0, J1)
+    const int Imin = J0 + 4 * grp, Imax = min(Imin + 3, J1 - 1);
+    if (Imin >= J1) return;  // a group past the end of a short last chunk (uniform: before any barrier)
+    const int I = Imin + wv;
+    const bool valid = I <= Imax;
+    const long tok0 = (long)h * p.T, hrow = (long)h * p.rstride;
+    const int c0 = min(I, Imax) * WT, n = min(WT, p.T - c0);
+    // this wave's tile: K, U (or V) and dO rows as fragments, eta of its rows
+    f32x4 KIf[NS], UIf[NS], OIf[NS], etI;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const long gi = (tok0 + c0 + min(m, n - 1)) * D + 16 * s + 4 * g;
+        const f32x4 kk = ld4f<E>(p.k, gi), oo = ld4f<E>(p.dout, gi);
+        const f32x4 uu = MSE ? *reinterpret_cast<const f32x4 *>(p.ub + (hrow + c0 + min(m, n - 1)) * D + 16 * s + 4 * g)
+                             : ld4f<E>(p.v, gi);
+        KIf[s] = m < n ? kk : zero4();
+        UIf[s] = m < n ? uu : zero4();
+        OIf[s] = m < n ? oo : zero4();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float x = p.eta[tok0 + c0 + min(4 * g + r, n - 1)];
+        etI[r] = 4 * g + r < n ? x : 0.f;
+    }
+    f32x4 sv[NS], dk[NS], dq[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sv[s] = dk[s] = dq[s] = zero4();
+    float de = 0.f;
+    // J tiles go global -> registers one tile ahead
+    f32x4 rx[NL], ry[NL];
+    float re = 0.f;
+    auto load = [&](int J, bool after) {
+        const int cj = J * WT, nj = min(WT, p.T - cj);
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int e = tid + 256 * k, i = e / (D / 4), col = 4 * (e % (D / 4));
+            const int ic = min(i, nj - 1);
+            const long gi = (tok0 + cj + ic) * D + col;
+            f32x4 x, y;
+            if (after) {
+                x = ld4f<E>(p.q, gi);
+                y = ld4f<E>(p.dout, gi);
+            } else {
+                x = MSE ? *reinterpret_cast<const f32x4 *>(p.ub + (hrow + cj + ic) * D + col) : ld4f<E>(p.v, gi);
+                y = ld4f<E>(p.k, gi);
+            }
+            rx[k] = i < nj ? x : zero4();
+            ry[k] = i < nj ? y : zero4();
+        }
+        if (!after && tid < WT) re = tid < nj ? p.eta[tok0 + cj + tid] : 0.f;
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int e = tid + 256 * k, i = e / (D / 4), col = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4 *>(&XJ[i][col]) = rx[k];
+            *reinterpret_cast<f32x4 *>(&YJ[i][col]) = ry[k];
+        }
+        if (tid < WT) etJ[tid] = re;
+    };
+    // J >= I
+    load(Imin, true);
+    for (int J = Imin; J < J1; ++J) {
+        put();
+        __syncthreads();
+        if (J + 1 < J1)
+            load(J + 1, true);
+        else
+            load(J0, false);
+        if (valid && J >= I) {
+            f32x4 A = zero4(), dS = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                A = mma16(A, *reinterpret_cast<const f32x4 *>(&XJ[m][16 * s + 4 * g]), KIf[s]);
+                dS = mma16(dS, *reinterpret_cast<const f32x4 *>(&YJ[m][16 * s + 4 * g]), UIf[s]);
+            }
+            if (J == I) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    A[r] = 4 * g + r >= m ? A[r] : 0.f;
+                    dS[r] = 4 * g + r >= m ? dS[r] : 0.f;
+                }
+            }
+            de += dS[0] * A[0] + dS[1] * A[1] + dS[2] * A[2] + dS[3] * A[3];
+#pragma unroll
+            for (int ct = 0; ct < NS; ++ct) {
+                const int col = 16 * ct + m;
+                sv[ct] = mma16(sv[ct], A, f32x4{YJ[4 * g][col], YJ[4 * g + 1][col], YJ[4 * g + 2][col], YJ[4 * g + 3][col]});
+                dk[ct] = mma16(dk[ct], dS, f32x4{XJ[4 * g][col], XJ[4 * g + 1][col], XJ[4 * g + 2][col], XJ[4 * g + 3][col]});
+            }
+        }
+        __syncthreads();
+    }
+    // J <= I
+    for (int J = J0; J <= Imax; ++J) {
+        put();
+        __syncthreads();
+        if (J + 1 <= Imax) load(J + 1, false);
+        if (valid && J <= I) {
+            f32x4 dAT = zero4();  // lane (g, n): dA^T[s = 4 g + r][t = n]
+#pragma unroll
+            for (int s = 0; s < NS; ++s) dAT = mma16(dAT, *reinterpret_cast<const f32x4 *>(&XJ[m][16 * s + 4 * g]), OIf[s]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = dAT[r] * etJ[4 * g + r];
+                dAT[r] = (J < I || 4 * g + r <= m) ? x : 0.f;
+            }
+#pragma unroll
+            for (int ct = 0; ct < NS; ++ct) {
+                const int col = 16 * ct + m;
+                dq[ct] = mma16(dq[ct], dAT, f32x4{YJ[4 * g][col], YJ[4 * g + 1][col], YJ[4 * g + 2][col], YJ[4 * g + 3][col]});
+            }
+        }
+        __syncthreads();
+    }
+    if (!valid) return;
+    // S~ = H A^T dO: stored, and kept as rows for S~ W_c^T
+#pragma unroll
+    for (int ct = 0; ct < NS; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = etI[r] * sv[ct][r];
+            SW[wv][4 * g + r][16 * ct + m] = x;
+            p.st[(hrow + c0 + 4 * g + r) * D + 16 * ct + m] = x;
+        }
+    de += __shfl_xor(de, 16, 64);
+    de += __shfl_xor(de, 32, 64);
+    if (g == 0 && m < n) p.deta[tok0 + c0 + m] = de;
+    const float *Wc = p.states + ((long)h * p.nchunks + ch) * D * D;
+#pragma unroll
+    for (int ct = 0; ct < NS; ++ct) {
+        const int col = 16 * ct + m;
+        f32x4 fq = dq[ct], sk = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const f32x4 wf = *reinterpret_cast<const f32x4 *>(Wc + (long)col * D + 16 * s + 4 * g);
+            fq = mma16(fq, OIf[s], wf);
+            if constexpr (MSE) sk = mma16(sk, *reinterpret_cast<const f32x4 *>(&SW[wv][m][16 * s + 4 * g]), wf);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            if (i < n) stf<E>(p.dq, (tok0 + c0 + i) * D + col, fq[r]);
+            p.dkl[(hrow + c0 + i) * D + col] = etI[r] * dk[ct][r] - sk[r];
+        }
+    }
 }
 
 // Update-then-apply order, the apply's adjoint: G_final = dW_final + Q^T dO
@@ -1358,9 +1400,15 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
     const dim3 b(256);
     lbw_serial_states<D, TT, E>(p, NH, st);
     if (p.order == 0) {
-        if (p.loss == 1) lbw_u<D, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
-        lbw_local_tiled<D, E><<<dim3(NH * p.ntiles), b, 0, st>>>(p);
-        lbw_rc<D, E><<<dim3(NH * p.nchunks * (D / CB)), b, 0, st>>>(p);
+        const int ngrp = NH * p.nchunks * ((p.tpc + 3) / 4);
+        if (p.loss == 1) {
+            lbw_u_m<D, E><<<dim3(NH * p.nchunks * ((p.tpc + DEP_TPW - 1) / DEP_TPW)), b, 0, st>>>(p);
+            lbw_local_tiled_m<D, E, true><<<dim3(ngrp), b, 0, st>>>(p);
+            lbw_rc_m<D, E, true><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        } else {
+            lbw_local_tiled_m<D, E, false><<<dim3(ngrp), b, 0, st>>>(p);
+            lbw_rc_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        }
     } else {
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
