@@ -47,11 +47,7 @@ struct LinBwdParams {
     int order, Tq;         // order 1: update over all key/value chunks, then apply to Tq queries
     float *wfinal;         // [NH][D][D] (order 1) final state
     float *ginit;          // [NH][D][D] (order 1) dL/dW_final incl. the apply's Q^T dO
-    // The serial passes and the dependent pass step over `ntiles` tiles of the
-    // kernels' B tokens; a chunk is `sub` tiles (sub = 1: a tile is a chunk;
-    // sub > 1 only with B = 16).  The per-token buffers have head stride
-    // rstride = nchunks * chunk rows.
-    int sub, ntiles;
+    // The per-token buffers have head stride rstride = nchunks * chunk rows.
     long rstride;
     // Segments of the serial passes: nseg runs of seg_chunks chunks (the last
     // may be shorter) per head.  ssum: [NH][nseg][D][2D], each segment's affine
@@ -59,8 +55,7 @@ struct LinBwdParams {
     // start state (states) or end adjoint (G).
     int nseg, seg_chunks;
     float *ssum, *sstart;
-    // The serial passes on the matrix cores step over 16-token tiles: tpc per
-    // chunk, nwt per head.
+    // Every pass steps over 16-token tiles: tpc per chunk, nwt per head.
     int tpc, nwt;
 };
 
@@ -93,182 +88,6 @@ __device__ __forceinline__ f32x4 lds4(const float *x) { return *reinterpret_cast
 // dir 0 (states): X_0 = w_init, X_{s+1} = L_s X_s + F_s, storing X_s for s >= 1;
 // dir 1 (G): X_{S-1} = g0 (d_w_final, or the apply's G in the update-then-apply
 // order, or zero), X_{s-1} = L_s X_s + F_s, storing X_s for s <= S - 2.
-
-// Parallel pass 2, one workgroup per (head, chunk): every term that does not
-// need G.  Writes dQ, d_eta's first part and the chunk's U, S~, dK part, R_c.
-template <int D, int B, typename E>
-__device__ __forceinline__ void lbw_local_body(const LinBwdParams &p)
-{
-    __shared__ float Wc[D][D + 1];
-    // token rows padded to D + 4 floats: 16-byte aligned, so the loops below read
-    // four consecutive elements of a row (the same row for the whole wave) at once
-    constexpr int P = D + 4;
-    __shared__ __align__(16) float Qs[B][P], Ks[B][P], dOs[B][P], Us[B][P], Ss[B][P];
-    __shared__ float As[B][B + 1], dAs[B][B + 1];
-    __shared__ float et[B];
-    constexpr int NBD = B * D / 256;
-    constexpr int RS = 256 / D;  // row stride of one thread's outputs (rows i0 + RS r)
-    const int h = blockIdx.x / p.nchunks, c = blockIdx.x % p.nchunks, tid = threadIdx.x;
-    const long tok0 = (long)h * p.T;
-    const int c0 = c * B, n = min(B, p.T - c0);
-    const long cb = ((long)h * p.nchunks + c);
-    const float *src = p.states + cb * D * D;
-    for (int e = tid; e < D * D; e += 256) Wc[e / D][e % D] = src[e];
-    for (int e = tid; e < B * D; e += 256) {
-        const int i = e / D, j = e % D;
-        const bool ok = i < n;
-        const long g = (tok0 + c0 + i) * D + j;
-        Qs[i][j] = ok ? ldf<E>(p.q, g) : 0.f;
-        Ks[i][j] = ok ? ldf<E>(p.k, g) : 0.f;
-        Us[i][j] = ok ? ldf<E>(p.v, g) : 0.f;
-        dOs[i][j] = ok ? ldf<E>(p.dout, g) : 0.f;
-    }
-    if (tid < B) et[tid] = tid < n ? p.eta[tok0 + c0 + tid] : 0.f;
-    __syncthreads();
-    const long row0 = (long)h * p.rstride + (long)c * B;  // this chunk's rows in the per-token buffers
-    if (p.loss == 1) {
-        float u[NBD];
-        {
-            const int i0 = tid / D, j = tid % D;  // outputs (i0 + RS r, j)
-#pragma unroll
-            for (int r = 0; r < NBD; ++r) u[r] = 0.f;
-            #pragma unroll 2
-            for (int a = 0; a < D; a += 4) {
-                const float w0 = Wc[a][j], w1 = Wc[a + 1][j], w2 = Wc[a + 2][j], w3 = Wc[a + 3][j];
-#pragma unroll
-                for (int r = 0; r < NBD; ++r) {
-                    const f32x4 kv = lds4(&Ks[i0 + RS * r][a]);
-                    u[r] += kv[0] * w0;
-                    u[r] += kv[1] * w1;
-                    u[r] += kv[2] * w2;
-                    u[r] += kv[3] * w3;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < NBD; ++r) u[r] = Us[i0 + RS * r][j] - u[r];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int e = tid + 256 * r;
-            Us[e / D][e % D] = u[r];
-            p.ub[(row0 + e / D) * D + e % D] = u[r];
-        }
-    }
-    for (int e = tid; e < B * B; e += 256) {
-        const int t = e / B, i = e % B;
-        float s = 0.f;
-        if (i <= t)
-            for (int a = 0; a < D; ++a) s += Qs[t][a] * Ks[i][a];
-        As[t][i] = s;
-    }
-    __syncthreads();
-    // S~ = S^T dO (S = A H);  dS = (dO U^T) * M
-    {
-        const int i0 = tid / D, j = tid % D;
-        float sv[NBD];
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) sv[r] = 0.f;
-        for (int t = 0; t < B; ++t) {
-            const float x = dOs[t][j];
-#pragma unroll
-            for (int r = 0; r < NBD; ++r) sv[r] += As[t][i0 + RS * r] * x;  // A is zero for t < i
-        }
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int i = i0 + RS * r;
-            Ss[i][j] = et[i] * sv[r];
-            p.st[(row0 + i) * D + j] = et[i] * sv[r];
-        }
-    }
-    for (int e = tid; e < B * B; e += 256) {
-        const int t = e / B, i = e % B;
-        float s = 0.f;
-        if (i <= t)
-            for (int a = 0; a < D; ++a) s += dOs[t][a] * Us[i][a];
-        dAs[t][i] = s;
-    }
-    __syncthreads();
-    if (tid < 64) {  // d_eta, the G-free part: sum_t dS[t][i] A[t][i]
-        for (int i = 0; i < B; ++i) {
-            float s = 0.f;
-            for (int t = tid; t < B; t += 64) s += dAs[t][i] * As[t][i];
-            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-            if (tid == 0 && i < n) p.deta[tok0 + c0 + i] = s;
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < B * B; e += 256) dAs[e / B][e % B] *= et[e % B];
-    __syncthreads();
-    // dQ = dO Wc^T + dA K;  dK part = dA^T Q [- S~ Wc^T]
-    {
-        const int i0 = tid / D, a = tid % D;  // outputs (i0 + RS r, a)
-        float sq[NBD], sk[NBD];
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) sq[r] = sk[r] = 0.f;
-        #pragma unroll 2
-        for (int j = 0; j < D; j += 4) {
-            const float w[4] = {Wc[a][j], Wc[a][j + 1], Wc[a][j + 2], Wc[a][j + 3]};
-#pragma unroll
-            for (int r = 0; r < NBD; ++r) {
-                const f32x4 ov = lds4(&dOs[i0 + RS * r][j]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) sq[r] += ov[x] * w[x];
-                if (p.loss == 1) {
-                    const f32x4 sv4 = lds4(&Ss[i0 + RS * r][j]);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) sk[r] -= sv4[x] * w[x];
-                }
-            }
-        }
-        for (int t = 0; t < B; ++t) {
-            const float kk = Ks[t][a], qq = Qs[t][a];
-#pragma unroll
-            for (int r = 0; r < NBD; ++r) {
-                sq[r] += dAs[i0 + RS * r][t] * kk;
-                sk[r] += dAs[t][i0 + RS * r] * qq;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < NBD; ++r) {
-            const int i = i0 + RS * r;
-            if (i < n) stf<E>(p.dq, (tok0 + c0 + i) * D + a, sq[r]);
-            p.dkl[(row0 + i) * D + a] = sk[r];
-        }
-    }
-    // R_c = Q^T dO [- K^T S~]
-    float *R = p.rc + cb * D * D;
-    {
-        constexpr int NR = D * D / 256;
-        const int a0 = (tid / D) * NR, j = tid % D;  // outputs (a0 + r, j)
-        float sr[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) sr[r] = 0.f;
-        #pragma unroll 2
-        for (int i = 0; i < B; ++i) {
-            const float x = dOs[i][j], y = Ss[i][j];
-#pragma unroll
-            for (int r = 0; r < NR; r += 4) {
-                const f32x4 qv = lds4(&Qs[i][a0 + r]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sr[r + e] += qv[e] * x;
-                if (p.loss == 1) {
-                    const f32x4 kv = lds4(&Ks[i][a0 + r]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sr[r + e] -= kv[e] * y;
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < NR; ++r) R[(long)(a0 + r) * D + j] = sr[r];
-    }
-}
-
-template <int D, int B, typename E>
-__global__ __launch_bounds__(256) void lbw_local(LinBwdParams p)
-{
-    lbw_local_body<D, B, E>(p);
-}
 
 // ---------------------------------------------------------------------------
 // The serial passes on the matrix cores (fp32 16x16x4 MFMA).  One wave per
@@ -913,7 +732,6 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
 // tile come first (they are read by the other tiles' waves), R_c last (a sum
 // over the whole chunk).
 // ---------------------------------------------------------------------------
-constexpr int TT = 16;  // tokens per tile
 
 // U = V - K W_c (MSE) of 16-token tiles on the matrix cores: one workgroup per
 // (head, chunk, group of up to DEP_TPW tiles), W_c staged once, wave w owning
@@ -1328,7 +1146,7 @@ size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
 // The two serial recursions, each as segment maps, chain, walks.
 // (one wave per (head, segment, 16 columns), four waves a workgroup: the
 // column counts D / 16 and 2 D / 16 are multiples of four)
-template <int D, int B, typename E>
+template <int D, typename E>
 static void lbw_serial_states(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
@@ -1340,7 +1158,7 @@ static void lbw_serial_states(const LinBwdParams &p, int NH, hipStream_t st)
     lbw_states_m<D, E><<<dim3(NH * p.nseg * NC), b, 0, st>>>(p, 0);
 }
 
-template <int D, int B, typename E>
+template <int D, typename E>
 static void lbw_serial_grad(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
@@ -1369,36 +1187,32 @@ static void lbw_dep_launch(const LinBwdParams &p, int NH, hipStream_t st)
         lbw_dep_m<D, E, false><<<grid, dim3(256), 0, st>>>(p);
 }
 
-template <int D, int B, typename E>
+template <int D, typename E>
 static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
-    lbw_serial_states<D, B, E>(p, NH, st);
+    lbw_serial_states<D, E>(p, NH, st);
     if (p.order == 0) {
-        if constexpr (B == 16) {
-            if (p.loss == 1)
-                lbw_local_m<D, E, true><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
-            else
-                lbw_local_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
-        } else {
-            lbw_local<D, B, E><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
-        }
+        if (p.loss == 1)
+            lbw_local_m<D, E, true><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+        else
+            lbw_local_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
     } else {
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
-    lbw_serial_grad<D, B, E>(p, NH, st);
+    lbw_serial_grad<D, E>(p, NH, st);
     lbw_dep_launch<D, E>(p, NH, st);
 }
 
-// Chunks of 16 k tokens (k > 1, or d = 128 with 32): the serial and dependent
+// Chunks of 16 k tokens, k > 1: the serial and dependent
 // passes step over 16-token tiles (snapshotting the chunk-start state and
 // G_{c+1}), the G-free terms run tile against tile.
 template <int D, typename E>
 static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 b(256);
-    lbw_serial_states<D, TT, E>(p, NH, st);
+    lbw_serial_states<D, E>(p, NH, st);
     if (p.order == 0) {
         const int ngrp = NH * p.nchunks * ((p.tpc + 3) / 4);
         if (p.loss == 1) {
@@ -1413,7 +1227,7 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
         lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
-    lbw_serial_grad<D, TT, E>(p, NH, st);
+    lbw_serial_grad<D, E>(p, NH, st);
     lbw_dep_launch<D, E>(p, NH, st);
 }
 
@@ -1436,23 +1250,15 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
     p.sstart = p.ssum + (size_t)NH * p.nseg * 2 * d * d;
     p.tpc = chunk / 16;
     p.nwt = (Tkv + 15) / 16;
-    const bool whole = (d == 64 && (chunk == 16 || chunk == 32)) || (d == 128 && chunk == 16);
-    if (whole) {  // a chunk is one step of the serial passes
-        p.sub = 1;
-        p.ntiles = nch;
+    if (chunk == 16) {  // a chunk is one tile
         if (d == 128) {
-            if (bf16) lbw_run<128, 16, __bf16>(p, NH, st);
-            else lbw_run<128, 16, float>(p, NH, st);
-        } else if (chunk == 16) {
-            if (bf16) lbw_run<64, 16, __bf16>(p, NH, st);
-            else lbw_run<64, 16, float>(p, NH, st);
+            if (bf16) lbw_run<128, __bf16>(p, NH, st);
+            else lbw_run<128, float>(p, NH, st);
         } else {
-            if (bf16) lbw_run<64, 32, __bf16>(p, NH, st);
-            else lbw_run<64, 32, float>(p, NH, st);
+            if (bf16) lbw_run<64, __bf16>(p, NH, st);
+            else lbw_run<64, float>(p, NH, st);
         }
-    } else {  // chunk = 16 sub tokens
-        p.sub = chunk / TT;
-        p.ntiles = (Tkv + TT - 1) / TT;
+    } else {  // several tiles a chunk
         if (d == 128) {
             if (bf16) lbw_run_tiled<128, __bf16>(p, NH, st);
             else lbw_run_tiled<128, float>(p, NH, st);
