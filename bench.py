@@ -810,7 +810,7 @@ def main():
         c["hbm_frac_of_measured"] = c["hbm_gbs"] / peaks["hbm_copy_gbs"]
     for key in ("lact", "lact_rules", "window_attention", "backward"):
         for e in line.get(key, []):
-            if "tflops" in e:
+            if "mfma_frac" in e:  # bf16 products (the fp32 TTT-Linear backward has its own fp32_frac)
                 e["mfma_frac_of_measured"] = e["tflops"] / peaks["bf16_mfma_tflops"]
     for e in line.get("decode", []):
         if "hbm_gbs" in e:

@@ -423,6 +423,33 @@ __global__ __launch_bounds__(256) void lbw_chain_m(LinBwdParams p, int dir)
     }
 }
 
+// Stage one or two D x D fp32 matrices (row-major) into LDS rows of pitch P,
+// 256 threads: eight 16-byte loads per matrix in flight per thread before
+// their stores (a load-store loop would wait out the memory latency once per
+// piece).
+template <int D, int P, bool TWO>
+__device__ __forceinline__ void stage_mats(float (*d0)[P], const float *s0, float (*d1)[P], const float *s1, int tid)
+{
+    constexpr int N = D * D / 4 / 256, BT = N < 8 ? N : 8;
+    static_assert(N % BT == 0, "staging shape");
+#pragma unroll
+    for (int b0 = 0; b0 < N; b0 += BT) {
+        f32x4 v0[BT], v1[BT];
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+            const int e = tid + 256 * (b0 + i), r = e / (D / 4), c = 4 * (e % (D / 4));
+            v0[i] = *reinterpret_cast<const f32x4 *>(s0 + (long)r * D + c);
+            if constexpr (TWO) v1[i] = *reinterpret_cast<const f32x4 *>(s1 + (long)r * D + c);
+        }
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+            const int e = tid + 256 * (b0 + i), r = e / (D / 4), c = 4 * (e % (D / 4));
+            *reinterpret_cast<f32x4 *>(&d0[r][c]) = v0[i];
+            if constexpr (TWO) *reinterpret_cast<f32x4 *>(&d1[r][c]) = v1[i];
+        }
+    }
+}
+
 // Four consecutive elements of a token-major tensor as floats (i a multiple of 4).
 template <typename E> __device__ __forceinline__ f32x4 ld4f(const void *p, long i)
 {
@@ -454,11 +481,7 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
     const long cb = (long)h * p.nchunks + c;
     const long row0 = (long)h * p.rstride + t0;  // the chunk's rows in the per-token buffers
     {
-        const float *src = p.states + cb * D * D;
-        for (int e = tid; e < D * D / 4; e += 256) {
-            const int r = e / (D / 4), col = 4 * (e % (D / 4));
-            *reinterpret_cast<f32x4 *>(&Wm[r][col]) = *reinterpret_cast<const f32x4 *>(src + (long)r * D + col);
-        }
+        stage_mats<D, P, false>(Wm, p.states + cb * D * D, Wm, nullptr, tid);
         for (int e = tid; e < WT * D / 4; e += 256) {
             const int i = e / (D / 4), col = 4 * (e % (D / 4));
             const long gi = (tok0 + t0 + min(i, n - 1)) * D + col;
@@ -611,13 +634,7 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
     const long cb = (long)h * p.nchunks + ch;
     const bool nc = p.order == 1;
     {
-        const float *gs = p.gnext + cb * D * D, *wsrc = p.states + cb * D * D;
-        for (int e = tid; e < D * D / 4; e += 256) {
-            const int r = e / (D / 4), c = 4 * (e % (D / 4));
-            *reinterpret_cast<f32x4 *>(&Gm[r][c]) = *reinterpret_cast<const f32x4 *>(gs + (long)r * D + c);
-            if constexpr (MSE)
-                *reinterpret_cast<f32x4 *>(&Wm[r][c]) = *reinterpret_cast<const f32x4 *>(wsrc + (long)r * D + c);
-        }
+        stage_mats<D, P, MSE>(Gm, p.gnext + cb * D * D, Wm, p.states + cb * D * D, tid);
     }
     for (int t0 = tstart; t0 < tend; t0 += WT) {
         const int n = min(WT, tend - t0);
@@ -750,11 +767,7 @@ __global__ __launch_bounds__(256) void lbw_u_m(LinBwdParams p)
     const int tend = min(min(tstart + DEP_TPW * WT, (ch + 1) * tpc * WT), p.T);
     const long tok0 = (long)h * p.T;
     {
-        const float *src = p.states + ((long)h * p.nchunks + ch) * D * D;
-        for (int e = tid; e < D * D / 4; e += 256) {
-            const int r = e / (D / 4), c = 4 * (e % (D / 4));
-            *reinterpret_cast<f32x4 *>(&Wm[r][c]) = *reinterpret_cast<const f32x4 *>(src + (long)r * D + c);
-        }
+        stage_mats<D, P, false>(Wm, p.states + ((long)h * p.nchunks + ch) * D * D, Wm, nullptr, tid);
     }
     __syncthreads();
     for (int t0 = tstart; t0 < tend; t0 += WT) {
