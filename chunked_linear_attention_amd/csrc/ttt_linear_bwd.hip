@@ -405,21 +405,60 @@ __global__ __launch_bounds__(256) void lbw_chain_m(LinBwdParams p, int dir)
         slice_load<NS>(X, x0 + (long)h * D * D + j0, D, g, m);
     else
         slice_identity<NS>(X, j0, g, m, false);
-    for (int t = 0; t < S - 1; ++t) {
-        const int s = dir == 0 ? t : S - 1 - t;  // the map applied
-        const int o = dir == 0 ? s + 1 : s - 1;  // the segment whose start it gives
-        const float *M = p.ssum + ((long)h * S + s) * D * 2 * D;
-        f32x4 Xn[NS];
-        slice_load<NS>(Xn, M + D + j0, 2 * D, g, m);  // F_s
+    const int nst = S - 1;  // maps applied
+    if constexpr (D == 64) {
+        // the next map's fragments (80 registers) load while this one applies;
+        // steps in pairs so the two register sets are fixed, loads clamped to
+        // the last map (no branch around a load)
+        f32x4 L[2][NS][NS], F[2][NS];
+        auto fetch = [&](int k, int t) {
+            t = min(t, nst - 1);
+            const float *M = p.ssum + ((long)h * S + (dir == 0 ? t : S - 1 - t)) * D * 2 * D;
+            slice_load<NS>(F[k], M + D + j0, 2 * D, g, m);
 #pragma unroll
-        for (int a = 0; a < NS; ++a)
+            for (int a = 0; a < NS; ++a)
 #pragma unroll
-            for (int b = 0; b < NS; ++b)
-                Xn[a] = mma16(Xn[a], *reinterpret_cast<const f32x4 *>(M + (long)(16 * a + m) * 2 * D + 16 * b + 4 * g),
-                              X[b]);
+                for (int b = 0; b < NS; ++b)
+                    L[k][a][b] = *reinterpret_cast<const f32x4 *>(M + (long)(16 * a + m) * 2 * D + 16 * b + 4 * g);
+        };
+        if (nst > 0) fetch(0, 0);
+        for (int t0 = 0; t0 < nst; t0 += 2) {
 #pragma unroll
-        for (int a = 0; a < NS; ++a) X[a] = Xn[a];
-        slice_store<NS>(p.sstart + ((long)h * S + o) * D * D + j0, X, D, g, m);
+            for (int k = 0; k < 2; ++k) {
+                const int t = t0 + k;
+                fetch(k ^ 1, t + 1);
+                if (t < nst) {
+                    const int o = dir == 0 ? t + 1 : S - 2 - t;  // the segment whose start this gives
+                    f32x4 Xn[NS];
+#pragma unroll
+                    for (int a = 0; a < NS; ++a) {
+                        Xn[a] = F[k][a];
+#pragma unroll
+                        for (int b = 0; b < NS; ++b) Xn[a] = mma16(Xn[a], L[k][a][b], X[b]);
+                    }
+#pragma unroll
+                    for (int a = 0; a < NS; ++a) X[a] = Xn[a];
+                    slice_store<NS>(p.sstart + ((long)h * S + o) * D * D + j0, X, D, g, m);
+                }
+            }
+        }
+    } else {
+        for (int t = 0; t < nst; ++t) {
+            const int s = dir == 0 ? t : S - 1 - t;  // the map applied
+            const int o = dir == 0 ? s + 1 : s - 1;  // the segment whose start it gives
+            const float *M = p.ssum + ((long)h * S + s) * D * 2 * D;
+            f32x4 Xn[NS];
+            slice_load<NS>(Xn, M + D + j0, 2 * D, g, m);  // F_s
+#pragma unroll
+            for (int a = 0; a < NS; ++a)
+#pragma unroll
+                for (int b = 0; b < NS; ++b)
+                    Xn[a] = mma16(Xn[a], *reinterpret_cast<const f32x4 *>(M + (long)(16 * a + m) * 2 * D + 16 * b + 4 * g),
+                                  X[b]);
+#pragma unroll
+            for (int a = 0; a < NS; ++a) X[a] = Xn[a];
+            slice_store<NS>(p.sstart + ((long)h * S + o) * D * D + j0, X, D, g, m);
+        }
     }
 }
 
