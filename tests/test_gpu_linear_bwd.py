@@ -124,6 +124,14 @@ def test_bwd_d128_large_chunks(loss, order, chunk):
              Tq=T if order == 0 else 60, d=128)
 
 
+@pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_bwd_d128_large_chunks_f32(loss, chunk):
+    """d = 128 with fp32 inputs through the tile kernels (their fp32
+    instantiations hold more registers), ragged tail, held to 1e-4 normwise."""
+    run_case(1, 2, 200, chunk, loss, "f32", seed=240 + chunk + loss, d=128)
+
+
 @pytest.mark.parametrize("chunk", [64, 256, 1024])
 def test_bwd_d128_sweep_shape_sampled_heads(chunk):
     """The chunk-size sweep's shape (B2 H16 T16384 d128, MSE, bf16) at chunks
