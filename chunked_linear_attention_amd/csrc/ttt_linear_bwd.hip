@@ -1087,68 +1087,88 @@ __global__ __launch_bounds__(256) void lbw_local_tiled_m(LinBwdParams p)
     }
 }
 
-// Update-then-apply order, the apply's adjoint: G_final = dW_final + Q^T dO
-// (one workgroup per (head, 16 columns), queries in tiles of 64) ...
+// Update-then-apply order on the matrix cores.  The apply's adjoint G_final =
+// dW_final + Q^T dO: one workgroup per (head, 16 columns), its four waves
+// taking a quarter of the queries each (16-token tiles staged in the wave's
+// own LDS, the walk's fragments: Q^T as the A operand, dO in accumulator
+// order as B), the four partial sums added in a fixed order at the end.
 template <int D, typename E>
-__global__ __launch_bounds__(256) void lbw_nc_g(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_nc_g_m(LinBwdParams p)
 {
-    __shared__ float Qs[64][D + 1], dOs[64][CB + 1];
-    constexpr int NCB = D / CB;
-    const int h = blockIdx.x / NCB, j0 = (blockIdx.x % NCB) * CB, tid = threadIdx.x;
+    constexpr int NS = D / 16;
+    __shared__ WalkTile<D> tiles[4];
+    __shared__ __align__(16) f32x4 part[4][NS][64];
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int h = blockIdx.x / NS, j0 = (blockIdx.x % NS) * 16;
     const long q0 = (long)h * p.Tq;
-    float acc[D * CB / 256];
+    const int ntq = (p.Tq + WT - 1) / WT, per = (ntq + 3) / 4;
+    const int ta = wv * per, tb = min(ntq, ta + per);
+    f32x4 X[NS];
 #pragma unroll
-    for (int r = 0; r < D * CB / 256; ++r) {
-        const int e = tid + 256 * r;
-        acc[r] = p.dwf ? p.dwf[(long)h * D * D + (e / CB) * D + j0 + e % CB] : 0.f;
+    for (int s = 0; s < NS; ++s) X[s] = zero4();
+    WalkK<D, E> nk;
+    WalkCol<E> on;
+    if (ta < tb) {
+        nk.load(p.q, q0, ta * WT, p.Tq, lane);
+        on = walk_col4<E>(p.dout, q0, ta * WT, p.Tq, D, j0 + m, g);
     }
-    for (int t0 = 0; t0 < p.Tq; t0 += 64) {
-        const int n = min(64, p.Tq - t0);
-        for (int e = tid; e < 64 * D; e += 256) {
-            const int t = e / D, a = e % D;
-            Qs[t][a] = t < n ? ldf<E>(p.q, (q0 + t0 + t) * D + a) : 0.f;
-        }
-        for (int e = tid; e < 64 * CB; e += 256) {
-            const int t = e / CB, j = e % CB;
-            dOs[t][j] = t < n ? ldf<E>(p.dout, (q0 + t0 + t) * D + j0 + j) : 0.f;
-        }
-        __syncthreads();
+    for (int t = ta; t < tb; ++t) {
+        nk.put(tiles[wv], lane, p.Tq - t * WT);
+        const f32x4 oc = walk_f32(on, t * WT, p.Tq, g);
+        const int tn = min(t + 1, tb - 1);  // clamped: no branch around the loads
+        nk.load(p.q, q0, tn * WT, p.Tq, lane);
+        on = walk_col4<E>(p.dout, q0, tn * WT, p.Tq, D, j0 + m, g);
 #pragma unroll
-        for (int r = 0; r < D * CB / 256; ++r) {
-            const int e = tid + 256 * r, a = e / CB, j = e % CB;
-            float sacc = 0.f;
-            for (int t = 0; t < 64; ++t) sacc += Qs[t][a] * dOs[t][j];
-            acc[r] += sacc;
-        }
-        __syncthreads();
+        for (int s = 0; s < NS; ++s) X[s] = mma16(X[s], walk_cols<D>(tiles[wv], s, m, g), oc);
     }
 #pragma unroll
-    for (int r = 0; r < D * CB / 256; ++r) {
-        const int e = tid + 256 * r;
-        p.ginit[(long)h * D * D + (e / CB) * D + j0 + e % CB] = acc[r];
+    for (int s = 0; s < NS; ++s) part[wv][s][lane] = X[s];
+    __syncthreads();
+    if (wv == 0) {
+        f32x4 Gf[NS];
+        if (p.dwf)
+            slice_load<NS>(Gf, p.dwf + (long)h * D * D + j0, D, g, m);
+        else
+            slice_identity<NS>(Gf, j0, g, m, false);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) Gf[s] += ((part[0][s][lane] + part[1][s][lane]) + part[2][s][lane]) + part[3][s][lane];
+        slice_store<NS>(p.ginit + (long)h * D * D + j0, Gf, D, g, m);
     }
 }
 
-// ... and dQ = dO W_final^T (one workgroup per (head, 64 queries)).
+// ... and dQ = dO W_final^T: one workgroup per (head, 64 queries), W_final
+// staged in LDS, wave w owning column tiles w, w + 4, ...
 template <int D, typename E>
-__global__ __launch_bounds__(256) void lbw_nc_dq(LinBwdParams p)
+__global__ __launch_bounds__(256) void lbw_nc_dq_m(LinBwdParams p)
 {
-    __shared__ float Wf[D][D + 1], dOs[64][D + 1];
+    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    __shared__ __align__(16) float Wm[D][P];
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nqt = (p.Tq + 63) / 64;
-    const int h = blockIdx.x / nqt, t0 = (blockIdx.x % nqt) * 64, tid = threadIdx.x;
+    const int h = blockIdx.x / nqt, tq0 = (blockIdx.x % nqt) * 64;
     const long q0 = (long)h * p.Tq;
-    const int n = min(64, p.Tq - t0);
-    for (int e = tid; e < D * D; e += 256) Wf[e / D][e % D] = p.wfinal[(long)h * D * D + e];
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int t = e / D, j = e % D;
-        dOs[t][j] = t < n ? ldf<E>(p.dout, (q0 + t0 + t) * D + j) : 0.f;
-    }
+    stage_mats<D, P, false>(Wm, p.wfinal + (long)h * D * D, Wm, nullptr, tid);
     __syncthreads();
-    for (int e = tid; e < 64 * D; e += 256) {
-        const int t = e / D, a = e % D;
-        float sacc = 0.f;
-        for (int j = 0; j < D; ++j) sacc += dOs[t][j] * Wf[a][j];
-        if (t < n) stf<E>(p.dq, (q0 + t0 + t) * D + a, sacc);
+    for (int t0 = tq0; t0 < min(tq0 + 64, p.Tq); t0 += WT) {
+        const int n = min(WT, p.Tq - t0);
+        f32x4 Oa[NS];  // A operand: dO[t0 + m][16 s + 4 g + j]
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const f32x4 x = ld4f<E>(p.dout, (q0 + t0 + min(m, n - 1)) * D + 16 * s + 4 * g);
+            Oa[s] = m < n ? x : zero4();
+        }
+#pragma unroll
+        for (int u = 0; u < NCT; ++u) {
+            const int col = 16 * (wv + 4 * u) + m;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc = mma16(acc, Oa[s], *reinterpret_cast<const f32x4 *>(&Wm[col][16 * s + 4 * g]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r < n) stf<E>(p.dq, (q0 + t0 + 4 * g + r) * D + col, acc[r]);
+        }
     }
 }
 
@@ -1250,8 +1270,8 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
         else
             lbw_local_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
     } else {
-        lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
-        if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
+        lbw_nc_g_m<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+        if (p.Tq > 0) lbw_nc_dq_m<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_serial_grad<D, E>(p, NH, st);
     lbw_dep_launch<D, E>(p, NH, st);
@@ -1276,8 +1296,8 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
             lbw_rc_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
         }
     } else {
-        lbw_nc_g<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
-        if (p.Tq > 0) lbw_nc_dq<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
+        lbw_nc_g_m<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
+        if (p.Tq > 0) lbw_nc_dq_m<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
     }
     lbw_serial_grad<D, E>(p, NH, st);
     lbw_dep_launch<D, E>(p, NH, st);
