@@ -466,28 +466,33 @@ __global__ __launch_bounds__(256) void lbw_chain_m(LinBwdParams p, int dir)
 // 256 threads: eight 16-byte loads per matrix in flight per thread before
 // their stores (a load-store loop would wait out the memory latency once per
 // piece).
-template <int D, int P, bool TWO>
+template <int D, int P, bool TWO, int NT = 256>
 __device__ __forceinline__ void stage_mats(float (*d0)[P], const float *s0, float (*d1)[P], const float *s1, int tid)
 {
-    constexpr int N = D * D / 4 / 256, BT = N < 8 ? N : 8;
+    constexpr int N = D * D / 4 / NT, BT = N < 8 ? N : 8;
     static_assert(N % BT == 0, "staging shape");
 #pragma unroll
     for (int b0 = 0; b0 < N; b0 += BT) {
         f32x4 v0[BT], v1[BT];
 #pragma unroll
         for (int i = 0; i < BT; ++i) {
-            const int e = tid + 256 * (b0 + i), r = e / (D / 4), c = 4 * (e % (D / 4));
+            const int e = tid + NT * (b0 + i), r = e / (D / 4), c = 4 * (e % (D / 4));
             v0[i] = *reinterpret_cast<const f32x4 *>(s0 + (long)r * D + c);
             if constexpr (TWO) v1[i] = *reinterpret_cast<const f32x4 *>(s1 + (long)r * D + c);
         }
 #pragma unroll
         for (int i = 0; i < BT; ++i) {
-            const int e = tid + 256 * (b0 + i), r = e / (D / 4), c = 4 * (e % (D / 4));
+            const int e = tid + NT * (b0 + i), r = e / (D / 4), c = 4 * (e % (D / 4));
             *reinterpret_cast<f32x4 *>(&d0[r][c]) = v0[i];
             if constexpr (TWO) *reinterpret_cast<f32x4 *>(&d1[r][c]) = v1[i];
         }
     }
 }
+
+// Waves per workgroup of the local and dependent passes: eight at d = 128,
+// where their LDS allows one workgroup per CU (two waves per SIMD then), four
+// at d = 64.
+template <int D> constexpr int PW = D == 128 ? 8 : 4;
 
 // Four consecutive elements of a token-major tensor as floats (i a multiple of 4).
 template <typename E> __device__ __forceinline__ f32x4 ld4f(const void *p, long i)
@@ -505,9 +510,9 @@ template <typename E> __device__ __forceinline__ f32x4 ld4f(const void *p, long 
 // (Q K^T) * M and dA = (dO U^T) * M are formed by every wave (one tile each),
 // and their accumulators serve directly as the A operand of A^T X and dA^T X.
 template <int D, typename E, bool MSE>
-__global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
+__global__ __launch_bounds__(64 * PW<D>) void lbw_local_m(LinBwdParams p)
 {
-    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    constexpr int NS = D / 16, NW = PW<D>, NT = 64 * NW, NCT = NS / NW, P = D + 4;
     __shared__ __align__(16) float Wm[D][P];
     __shared__ __align__(16) float Qs[WT][P], Ks[WT][P], Os[WT][P], Us[WT][P], Ss[WT][P];
     __shared__ __align__(16) float dAs[WT][WT + 4];
@@ -520,8 +525,8 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
     const long cb = (long)h * p.nchunks + c;
     const long row0 = (long)h * p.rstride + t0;  // the chunk's rows in the per-token buffers
     {
-        stage_mats<D, P, false>(Wm, p.states + cb * D * D, Wm, nullptr, tid);
-        for (int e = tid; e < WT * D / 4; e += 256) {
+        stage_mats<D, P, false, NT>(Wm, p.states + cb * D * D, Wm, nullptr, tid);
+        for (int e = tid; e < WT * D / 4; e += NT) {
             const int i = e / (D / 4), col = 4 * (e % (D / 4));
             const long gi = (tok0 + t0 + min(i, n - 1)) * D + col;
             const bool ok = i < n;
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
         f32x4 Uc[NCT];
 #pragma unroll
         for (int u = 0; u < NCT; ++u) {
-            const int col = 16 * (wv + 4 * u) + m;
+            const int col = 16 * (wv + NW * u) + m;
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < NS; ++s)
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < NCT; ++u) {
-            const int col = 16 * (wv + 4 * u) + m;
+            const int col = 16 * (wv + NW * u) + m;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 Us[4 * g + r][col] = Uc[u][r];
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
     // S~ = H A^T dO (rows i), kept for dK and R_c and stored for the dependent pass
 #pragma unroll
     for (int u = 0; u < NCT; ++u) {
-        const int col = 16 * (wv + 4 * u) + m;
+        const int col = 16 * (wv + NW * u) + m;
         f32x4 sv = mma16(zero4(), A, f32x4{Os[4 * g][col], Os[4 * g + 1][col], Os[4 * g + 2][col], Os[4 * g + 3][col]});
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
     __syncthreads();  // S~ rows and dA H complete
 #pragma unroll
     for (int u = 0; u < NCT; ++u) {
-        const int col = 16 * (wv + 4 * u) + m;
+        const int col = 16 * (wv + NW * u) + m;
         // dQ = dO W_c^T + dA K
         f32x4 dq = zero4();
 #pragma unroll
@@ -653,14 +658,14 @@ __global__ __launch_bounds__(256) void lbw_local_m(LinBwdParams p)
 // is not the A-operand order).  In the update-then-apply order there are no
 // G-free parts and U is V [- K W_c] (computed here).
 template <int D, typename E, bool MSE>
-__global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
+__global__ __launch_bounds__(64 * PW<D>) void lbw_dep_m(LinBwdParams p)
 {
-    constexpr int NS = D / 16, NCT = D / 64, P = D + 4;
+    constexpr int NS = D / 16, NW = PW<D>, NT = 64 * NW, NCT = NS / NW, P = D + 4;
     __shared__ __align__(16) float Gm[D][P];
     __shared__ __align__(16) float Wm[MSE ? D : 1][P];
     __shared__ __align__(16) float Us[WT][P];
     __shared__ __align__(16) float KGs[WT][P];
-    __shared__ float dpart[4][WT];
+    __shared__ float dpart[NW][WT];
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tpc = p.tpc, gpc = (tpc + DEP_TPW - 1) / DEP_TPW;
@@ -673,13 +678,13 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
     const long cb = (long)h * p.nchunks + ch;
     const bool nc = p.order == 1;
     {
-        stage_mats<D, P, MSE>(Gm, p.gnext + cb * D * D, Wm, p.states + cb * D * D, tid);
+        stage_mats<D, P, MSE, NT>(Gm, p.gnext + cb * D * D, Wm, p.states + cb * D * D, tid);
     }
     for (int t0 = tstart; t0 < tend; t0 += WT) {
         const int n = min(WT, tend - t0);
         const long row0 = (long)h * p.rstride + t0;  // the tile's rows in the per-token buffers
         // U rows: the forward's residuals (MSE, stored by the local pass) or V
-        for (int e = tid; e < WT * D / 4; e += 256) {
+        for (int e = tid; e < WT * D / 4; e += NT) {
             const int i = e / (D / 4), c = 4 * (e % (D / 4));
             const int ic = min(i, n - 1);
             const f32x4 x = (MSE && !nc) ? *reinterpret_cast<const f32x4 *>(p.ub + (row0 + ic) * D + c)
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
             f32x4 Uc[NCT];
 #pragma unroll
             for (int u = 0; u < NCT; ++u) {
-                const int ct = wv + 4 * u;
+                const int ct = wv + NW * u;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
@@ -717,14 +722,14 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
 #pragma unroll
             for (int u = 0; u < NCT; ++u)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Us[4 * g + r][16 * (wv + 4 * u) + m] = Uc[u][r];
+                for (int r = 0; r < 4; ++r) Us[4 * g + r][16 * (wv + NW * u) + m] = Uc[u][r];
             __syncthreads();
         }
         // KG, dV, this wave's part of d_eta; KG rows to LDS
         float dp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NCT; ++u) {
-            const int ct = wv + 4 * u, col = 16 * ct + m;
+            const int ct = wv + NW * u, col = 16 * ct + m;
             f32x4 kg = zero4();
 #pragma unroll
             for (int s = 0; s < NS; ++s)
@@ -749,12 +754,15 @@ __global__ __launch_bounds__(256) void lbw_dep_m(LinBwdParams p)
         __syncthreads();  // KG rows and the d_eta parts
         if (tid < n) {
             const long te = tok0 + t0 + tid;
-            p.deta[te] = (nc ? 0.f : p.deta[te]) + (dpart[0][tid] + dpart[1][tid] + dpart[2][tid] + dpart[3][tid]);
+            float x = dpart[0][tid];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) x += dpart[w][tid];
+            p.deta[te] = (nc ? 0.f : p.deta[te]) + x;
         }
         // dK = part + H (U G^T [- KG W_c^T])
 #pragma unroll
         for (int u = 0; u < NCT; ++u) {
-            const int ct = wv + 4 * u, col = 16 * ct + m;
+            const int ct = wv + NW * u, col = 16 * ct + m;
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < NS; ++s)
@@ -1254,9 +1262,9 @@ static void lbw_dep_launch(const LinBwdParams &p, int NH, hipStream_t st)
 {
     const dim3 grid(NH * p.nchunks * ((p.tpc + DEP_TPW - 1) / DEP_TPW));
     if (p.loss == 1)
-        lbw_dep_m<D, E, true><<<grid, dim3(256), 0, st>>>(p);
+        lbw_dep_m<D, E, true><<<grid, dim3(64 * PW<D>), 0, st>>>(p);
     else
-        lbw_dep_m<D, E, false><<<grid, dim3(256), 0, st>>>(p);
+        lbw_dep_m<D, E, false><<<grid, dim3(64 * PW<D>), 0, st>>>(p);
 }
 
 template <int D, typename E>
@@ -1266,9 +1274,9 @@ static void lbw_run(const LinBwdParams &p, int NH, hipStream_t st)
     lbw_serial_states<D, E>(p, NH, st);
     if (p.order == 0) {
         if (p.loss == 1)
-            lbw_local_m<D, E, true><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+            lbw_local_m<D, E, true><<<dim3(NH * p.nchunks), dim3(64 * PW<D>), 0, st>>>(p);
         else
-            lbw_local_m<D, E, false><<<dim3(NH * p.nchunks), b, 0, st>>>(p);
+            lbw_local_m<D, E, false><<<dim3(NH * p.nchunks), dim3(64 * PW<D>), 0, st>>>(p);
     } else {
         lbw_nc_g_m<D, E><<<dim3(NH * (D / CB)), b, 0, st>>>(p);
         if (p.Tq > 0) lbw_nc_dq_m<D, E><<<dim3(NH * ((p.Tq + 63) / 64)), b, 0, st>>>(p);
