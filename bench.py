@@ -516,7 +516,7 @@ def linear_bwd_flops(NH, T, d, b, loss):
     return NH * f
 
 
-def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
+def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150, order=0):
     import numpy as np
     import torch
     import chunked_linear_attention_amd as cla
@@ -527,7 +527,7 @@ def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
     eta, w0 = torch.from_numpy(inp["eta"]).cuda(), torch.from_numpy(inp["w0"]).cuda()
     dy = up(ti.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32)))
     import chunked_linear_attention_amd._lib as L
-    nb = L.load().ttt_linear_bwd_workspace_bytes(B, H, T, T, d, chunk, loss, 0, 1)
+    nb = L.load().ttt_linear_bwd_workspace_bytes(B, H, T, T, d, chunk, loss, order, 1)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
 
     class _One:
@@ -535,8 +535,11 @@ def bench_linear_bwd(B, H, T, d, chunk, loss, steps, warmup, seed=150):
             return None
 
     ms, med, _ = time_calls(lambda _: cla.ttt_linear_bwd(q, k, v, eta, w0, dy, chunk=chunk,
-                                                          loss=loss, workspace=ws),
+                                                          loss=loss, order=order, workspace=ws),
                             _One(), steps, warmup)
+    if order == 1:  # update-then-apply: no intra-chunk terms; reported as time and rate only
+        return {"workload": f"ttt_linear_bwd_noncausal_{'mse' if loss else 'dot'}_B{B}_H{H}_T{T}_Tq{T}_d{d}_b{chunk}_bf16",
+                "ms": ms, "ms_median": med, "tokens_per_s": B * T / (ms * 1e-3)}
     fl = linear_bwd_flops(B * H, T, d, chunk, loss)
     return {"workload": f"ttt_linear_bwd_{'mse' if loss else 'dot'}_B{B}_H{H}_T{T}_d{d}_b{chunk}_bf16",
             "ms": ms, "ms_median": med, "tokens_per_s": B * T / (ms * 1e-3), "alg_flops": fl,
@@ -711,11 +714,14 @@ def main():
         print(json.dumps({"gemm_probe": gemm_probe(args.steps, args.warmup)}), flush=True)
         return
     if args.bwd_only:
-        # the headline shape, the d = 128 chunk-size sweep's shape, then LaCT
+        # the headline shape, the d = 128 chunk-size sweep's shape, the headline
+        # shape in the update-then-apply order, then LaCT
         bwd = [bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps, args.warmup)]
         for b in (16, 64, 256, 1024):
             log(f"[bench] TTT-Linear backward B2 H16 T16384 d128 b{b}")
             bwd.append(bench_linear_bwd(2, 16, 16384, 128, b, 1, max(5, args.steps // 10), 2))
+        log("[bench] TTT-Linear backward, update-then-apply order, B4 H8 T4096 d64 b16")
+        bwd.append(bench_linear_bwd(4, 8, 4096, 64, 16, 1, args.steps, args.warmup, order=1))
         bwd.append(bench_lact_bwd(ti.LACT_CAUSAL, args.steps, args.warmup))
         print(json.dumps({"backward": bwd}), flush=True)
         return

@@ -151,3 +151,22 @@ def test_bwd_many_segments(loss, chunk, dtype):
 @pytest.mark.parametrize("loss", [0, 1])
 def test_bwd_many_segments_noncausal_d128(loss):
     run_case(1, 2, 2000, 16, loss, "f32", seed=230 + loss, order=1, Tq=90, d=128)
+
+
+@pytest.mark.parametrize("d,chunk,order", [(64, 16, 0), (128, 64, 0), (64, 32, 1)])
+def test_bwd_repeat_runs_are_bitwise_identical(d, chunk, order):
+    """Every reduction of the backward sums in a fixed order (no atomics), so
+    two calls on the same inputs give the same bits."""
+    cla = _cla()
+    T = 600
+    inp = ti.gen_linear(1, 2, T, T, d, seed=250 + d + chunk, dtype="bf16", w0="normal")
+    g = {n: dev(inp[n], inp.get(n + "16"), torch.bfloat16) for n in ("q", "k", "v")}
+    dy = ti.f32_to_bf16_bits(np.random.default_rng(251).standard_normal((1, 2, T, d)).astype(np.float32))
+    g_dy = dev(None, dy, torch.bfloat16)
+    dwf = dev(np.random.default_rng(252).standard_normal((1, 2, d, d)).astype(np.float32))
+    print(f"[case] bwd repeat d={d} b={chunk} order={order}", flush=True)
+    outs = [cla.ttt_linear_bwd(g["q"], g["k"], g["v"], dev(inp["eta"]), dev(inp["w0"]), g_dy, dwf,
+                               chunk=chunk, loss=1, order=order) for _ in range(2)]
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
