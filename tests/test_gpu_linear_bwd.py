@@ -114,6 +114,15 @@ def test_bwd_large_chunks(loss, chunk, dtype):
 
 
 @pytest.mark.parametrize("loss", [0, 1])
+@pytest.mark.parametrize("chunk", [48, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_large_chunks_noncausal(loss, chunk, dtype):
+    """d = 64, update-then-apply order over several chunks and a ragged tail
+    (T = 300), fewer queries than keys."""
+    run_case(1, 2, 300, chunk, loss, dtype, seed=260 + chunk + loss, order=1, Tq=70)
+
+
+@pytest.mark.parametrize("loss", [0, 1])
 @pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("chunk", [32, 64, 1024])
 def test_bwd_d128_large_chunks(loss, order, chunk):
