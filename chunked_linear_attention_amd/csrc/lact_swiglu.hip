@@ -84,8 +84,9 @@ __global__ __launch_bounds__(256) void lact_prep_weights(LactParams p)
 // for 20 fragment reads.
 // ---------------------------------------------------------------------------
 // k step, LDS row pitch (96-byte rows: measured ~3% faster on both LaCT
-// workloads than 80-byte ones, whose reads lost 42% of LDS-active cycles to
-// bank conflicts), register stages (even, divides d / FBK)
+// workloads than 80-byte ones; the bank-conflict counter reads ~41% of
+// LDS-active cycles with either pitch, so the conflicts come from other
+// accesses), register stages (even, divides d / FBK)
 constexpr int FBK = 32, FPITCH = FBK + 16, FPD = 2;
 constexpr int F2PITCH = 128 + 16;  // W2 slice rows: transposing reads of 8 rows hit distinct banks
 
