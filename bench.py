@@ -168,17 +168,19 @@ def measured_peaks():
 
 
 def gemm_probe(steps=20, warmup=3):
-    """The LaCT kernels' shared 128 x 128 GEMM tile on plain bf16 products
-    (ttt_probe_gemm_bf16, fp32 out), beside the vendor GEMM behind torch.matmul
-    on the same shapes (bf16 in and out) for context; each checked against an
-    fp32 product of the same bf16 values on a small shape first."""
+    """The LaCT kernels' shared GEMM tile (128 x 128 and 256 x 128 blocks) on
+    plain bf16 products (ttt_probe_gemm_bf16, fp32 out), beside the vendor GEMM
+    behind torch.matmul on the same shapes (bf16 in and out) for context; each
+    checked against an fp32 product of the same bf16 values on a small shape
+    first."""
     import torch
     import chunked_linear_attention_amd._lib as L
     lib = L.load()
     st = torch.cuda.current_stream()
 
-    def ours(a, b, c, M, N, K, ak, bk):
-        rc = lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk, st.cuda_stream)
+    def ours(a, b, c, M, N, K, ak, bk, rows=128):
+        rc = lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk, rows,
+                                     st.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"ttt_probe_gemm_bf16 failed ({rc})")
 
@@ -199,13 +201,15 @@ def gemm_probe(steps=20, warmup=3):
     for (M, N, K, ak, bk) in [(512, 384, 320, 0, 0), (512, 384, 320, 1, 1), (512, 384, 320, 0, 1)]:
         a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
         b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
-        c = torch.empty(M, N, device="cuda")
-        ours(a, b, c, M, N, K, ak, bk)
         ref = (a.float().t() if ak else a.float()) @ (b.float() if bk else b.float().t())
-        torch.cuda.synchronize()
-        err = float((c - ref).abs().max() / ref.abs().max())
-        if err > 1e-5:
-            raise RuntimeError(f"GEMM tile probe mismatch {err:.2e} at {M}x{N}x{K} ({ak}, {bk})")
+        for rows in (128, 256):
+            c = torch.empty(M, N, device="cuda")
+            ours(a, b, c, M, N, K, ak, bk, rows)
+            torch.cuda.synchronize()
+            err = float((c - ref).abs().max() / ref.abs().max())
+            if err > 1e-5:
+                raise RuntimeError(f"GEMM tile probe mismatch {err:.2e} at {M}x{N}x{K} ({ak}, {bk}), "
+                                   f"{rows}-row blocks")
     for (M, N, K, ak, bk, what) in [(4096, 4096, 4096, 0, 0, "square, both operands k-contiguous"),
                                     (4096, 4096, 4096, 1, 1, "square, both operands k-major"),
                                     (8192, 8192, 8192, 0, 0, "square 8192, k-contiguous"),
@@ -215,6 +219,7 @@ def gemm_probe(steps=20, warmup=3):
         b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
         c = torch.empty(M, N, device="cuda")
         ms = timed(lambda: ours(a, b, c, M, N, K, ak, bk))
+        ms_w = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 256))
         at = a.t() if ak else a
         bt = b if bk else b.t()
         at, bt = at.contiguous(), bt.contiguous()
@@ -222,6 +227,7 @@ def gemm_probe(steps=20, warmup=3):
         fl = 2.0 * M * N * K
         out.append({"shape": f"{M}x{N}x{K}", "layout": what, "tile_us": ms * 1e3,
                     "tile_tflops": fl / (ms * 1e-3) / 1e12, "tile_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "wide_tile_us": ms_w * 1e3, "wide_tile_tflops": fl / (ms_w * 1e-3) / 1e12,
                     "vendor_us": vms * 1e3, "vendor_tflops": fl / (vms * 1e-3) / 1e12})
         del a, b, c, at, bt
     return out

@@ -32,69 +32,86 @@ __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rc
 
 // ---------------------------------------------------------------------------
 // Generic GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16), block tile
-// 128 x 128, 4 waves as 2 x 2 of 64 x 64, k step 64, K a multiple of 64.  An
-// operand is stored either k-contiguous (row m of A at A + m * lda, 128-byte
-// rows per stage) or, with AT / BT, k-major (row k at A + k * lda, holding
-// M contiguous elements: a token-major tensor read as its transpose), whose
-// fragments come from the transposing LDS read.  Rows of A past M and rows of
-// B past N read as zero, and so do rows k >= kvalid of a k-major operand.  The
-// epilogue gets the wave's 4 x 4 accumulator tiles: tile (i, q) holds C at
-// rows mbase + 16 i + 4 g + (0..3), column nbase + 16 q + (lane & 15).
+// BM x 128 with BM = 32 MB, 4 waves as 2 x 2 of (16 MB) x 64, k step 64, K a
+// multiple of 64.  MB = 4 is the 128 x 128 tile; MB = 8 (256 x 128, wave tiles
+// of 128 x 64) reads half as many LDS bytes per multiply-add from the A side.
+// An operand is stored either k-contiguous (row m of A at A + m * lda,
+// 128-byte rows per stage) or, with AT / BT, k-major (row k at A + k * lda,
+// holding M contiguous elements: a token-major tensor read as its transpose),
+// whose fragments come from the transposing LDS read.  Rows of A past M and
+// rows of B past N read as zero, and so do rows k >= kvalid of a k-major
+// operand.  The epilogue gets the wave's MB x 4 accumulator tiles: tile (i, q)
+// holds C at rows mbase + 16 i + 4 g + (0..3), column nbase + 16 q + (lane & 15).
 // ---------------------------------------------------------------------------
 constexpr int GBK = 64;
 constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): 16-byte fragment reads hit distinct banks per 8 lanes
 constexpr int GTPITCH = 128 + 16;  // k-major stage rows: transposing reads of 8 rows hit distinct banks
 constexpr int GPD = 2;           // register stages in flight (even: LDS buffer = stage parity)
 
-struct GemmLds {
-    bf16 a[2][128][GPITCH];
+template <int BM> struct GemmLdsT {
+    bf16 a[2][BM][GPITCH];
     bf16 b[2][128][GPITCH];
 };
+using GemmLds = GemmLdsT<128>;
 static_assert(sizeof(bf16[GBK][GTPITCH]) <= sizeof(bf16[128][GPITCH]), "k-major stage fits the buffer");
+static_assert(sizeof(bf16[GBK][256 + 16]) <= sizeof(bf16[256][GPITCH]), "k-major stage fits the buffer");
 
 // K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
 // from As[s] and B from Bs[s] (same leading dimensions).  This sums products
 // of split operands (hi and lo bf16 parts) in one accumulation.
-template <bool AT = false, bool BT = false, typename Epi>
-__device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, long lda,
+template <bool AT = false, bool BT = false, int MB = 4, typename Epi>
+__device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *const *As, long lda,
                                              const bf16 *const *Bs, long ldb, int M, int N,
                                              int kseg, int nseg, int m0, int n0, int kvalid, Epi &&epi)
 {
+    static_assert(MB == 4 || MB == 8, "block rows 128 or 256");
+    constexpr int BM = 32 * MB;
+    constexpr int TPA = BM + 16;        // k-major A stage pitch
+    constexpr int AKT = BM / 8;         // threads per k-major A row (8 elements each)
     constexpr bool TR = AT || BT;  // fragments in the transposing read's k order
     const int K = kseg * nseg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
-    // 4 pieces of 16 bytes per thread and operand.  k-contiguous: rows
-    // tid/8 + 32 i, 8 columns each.  k-major: k rows tid/16 + 16 i, 8 of the
-    // 128 row elements each.
-    int lrow[4], lcol, krow[4], kcol;
+    // Pieces of 16 bytes per thread: MB for A, 4 for B.  k-contiguous: rows
+    // tid/8 + 32 i, 8 columns each.  k-major: k rows tid/(BM/8) + (2048/BM) i
+    // of A (tid/16 + 16 i of B), 8 of the row's elements each.
+    int lrow[MB], lcol, krow[4], kcol, akrow[MB], akcol;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MB; ++i) {
         lrow[i] = (tid >> 3) + 32 * i;
-        krow[i] = (tid >> 4) + 16 * i;
+        akrow[i] = tid / AKT + (256 / AKT) * i;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) krow[i] = (tid >> 4) + 16 * i;
     lcol = (tid & 7) * 8;
     kcol = (tid & 15) * 8;
-    const bool aok[4] = {m0 + lrow[0] < M, m0 + lrow[1] < M, m0 + lrow[2] < M, m0 + lrow[3] < M};
-    const bool bok[4] = {n0 + lrow[0] < N, n0 + lrow[1] < N, n0 + lrow[2] < N, n0 + lrow[3] < N};
+    akcol = (tid % AKT) * 8;
+    bool aok[MB], bok[4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) aok[i] = m0 + lrow[i] < M;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bok[i] = n0 + lrow[i] < N;
     const int nst = K / GBK;
     const int ngroups = (nst + GPD - 1) / GPD;
-    B8 ra[GPD][4], rb[GPD][4];
+    B8 ra[GPD][MB], rb[GPD][4];
     auto issue = [&](int s, int st) {
         const int kk = min(st, nst - 1) * GBK;
         const int sg = kk / kseg, kin = kk - sg * kseg;
         const bf16 *A = As[sg], *B = Bs[sg];
+        // A piece i, then B piece i (the order of the 128-row tile)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MB; ++i) {
             if constexpr (AT)
-                ra[s][i] = ld16(A + (long)min(kin + krow[i], kvalid - 1) * lda + m0 + kcol);
+                ra[s][i] = ld16(A + (long)min(kin + akrow[i], kvalid - 1) * lda + m0 + akcol);
             else
                 ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
-            if constexpr (BT)
-                rb[s][i] = ld16(B + (long)min(kin + krow[i], kvalid - 1) * ldb + n0 + kcol);
-            else
-                rb[s][i] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
+            if (i < 4) {
+                if constexpr (BT)
+                    rb[s][i & 3] = ld16(B + (long)min(kin + krow[i & 3], kvalid - 1) * ldb + n0 + kcol);
+                else
+                    rb[s][i & 3] = ld16(B + (long)min(n0 + lrow[i], N - 1) * ldb + kin + lcol);
+            }
         }
     };
     // Past the last k step the stage holds zeros, so every step computes (the
@@ -103,43 +120,47 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
         const bool live = st < nst;
         const int kin = (min(st, nst - 1) * GBK) % kseg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MB; ++i) {
             if constexpr (AT) {
-                bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.a[buf][0][0]);
-                st16(&T[krow[i]][kcol], (live && kin + krow[i] < kvalid) ? ra[s][i] : zero16());
+                bf16(*T)[TPA] = reinterpret_cast<bf16(*)[TPA]>(&L.a[buf][0][0]);
+                st16(&T[akrow[i]][akcol], (live && kin + akrow[i] < kvalid) ? ra[s][i] : zero16());
             } else {
                 st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
             }
-            if constexpr (BT) {
-                bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.b[buf][0][0]);
-                st16(&T[krow[i]][kcol], (live && kin + krow[i] < kvalid) ? rb[s][i] : zero16());
-            } else {
-                st16(&L.b[buf][lrow[i]][lcol], (live && bok[i]) ? rb[s][i] : zero16());
+            if (i < 4) {
+                if constexpr (BT) {
+                    bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.b[buf][0][0]);
+                    st16(&T[krow[i & 3]][kcol], (live && kin + krow[i & 3] < kvalid) ? rb[s][i & 3] : zero16());
+                } else {
+                    st16(&L.b[buf][lrow[i]][lcol], (live && bok[i & 3]) ? rb[s][i & 3] : zero16());
+                }
             }
         }
     };
     // fragment of row r (m or n) for the 32-wide half kh: natural k order
     // (8 consecutive k per lane) or, when an operand is k-major, k = 4g + j
-    // and 16 + 4g + j on both sides
-    auto frag = [&](const bf16 (*X)[GPITCH], bool kmajor, int r, int kh) {
+    // and 16 + 4g + j on both sides (tp: the k-major stage's row pitch)
+    auto frag = [&](const bf16 (*X)[GPITCH], bool kmajor, int tp, int r, int kh) {
         if (!TR) return as_bf8(ld16(&X[r][32 * kh + 8 * g]));
         if (kmajor) {
-            const bf16(*T)[GTPITCH] = reinterpret_cast<const bf16(*)[GTPITCH]>(&X[0][0]);
+            const bf16 *T = &X[0][0];
             const int rb0 = r - mm;  // first row of the 16-row block
-            const bf16x4 x0 = lds_read_tr(&T[32 * kh + 4 * g + (mm >> 2)][rb0 + 4 * (mm & 3)]);
-            const bf16x4 x1 = lds_read_tr(&T[32 * kh + 16 + 4 * g + (mm >> 2)][rb0 + 4 * (mm & 3)]);
+            const bf16x4 x0 = lds_read_tr(T + (32 * kh + 4 * g + (mm >> 2)) * tp + rb0 + 4 * (mm & 3));
+            const bf16x4 x1 = lds_read_tr(T + (32 * kh + 16 + 4 * g + (mm >> 2)) * tp + rb0 + 4 * (mm & 3));
             return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
         const bf16x4 x0 = load4<bf16>(&X[r][32 * kh + 4 * g]);
         const bf16x4 x1 = load4<bf16>(&X[r][32 * kh + 16 + 4 * g]);
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    f32x4 acc[4][4];
+    f32x4 acc[MB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[i][q] = zero4();
 
+    // per 32-wide half: MB x 4 MFMAs, MB + 4 loads (or LDS writes) between them
+    constexpr int NMF = 4 * MB, NLD = MB + 4;
 #pragma unroll
     for (int s = 0; s < GPD; ++s) {
         issue(s, s);
@@ -156,34 +177,34 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLds &L, const bf16 *const *As, 
             // steps' loads (first half) or LDS writes (second half) between them
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                bf16x8 af[4], bfr[4];
+                bf16x8 af[MB], bfr[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    af[i] = frag(L.a[buf], AT, wm * 64 + 16 * i + mm, kh);
-                    bfr[i] = frag(L.b[buf], BT, wn * 64 + 16 * i + mm, kh);
-                }
+                for (int i = 0; i < MB; ++i) af[i] = frag(L.a[buf], AT, TPA, wm * (16 * MB) + 16 * i + mm, kh);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bfr[i] = frag(L.b[buf], BT, GTPITCH, wn * 64 + 16 * i + mm, kh);
                 if (kh == 0)
                     issue(j, st + GPD);
                 else
                     commit((j + 1) % GPD, (j + 1) & 1, st + 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
-                __builtin_amdgcn_sched_group_barrier(0x100, TR ? 16 : 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, TR ? 2 * NLD : NLD, 0);
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
+                for (int x = 0; x < NLD; ++x) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                     if (kh == 0)
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                     else
                         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
                 }
+                if constexpr (NMF > 2 * NLD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - 2 * NLD, 0);
             }
             lds_barrier();
         }
     }
-    epi(acc, m0 + wm * 64, n0 + wn * 64, g, mm);
+    epi(acc, m0 + wm * (16 * MB), n0 + wn * 64, g, mm);
 }
 
 // ---------------------------------------------------------------------------

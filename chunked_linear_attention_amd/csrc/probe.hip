@@ -41,46 +41,57 @@ __global__ __launch_bounds__(256) void probe_mfma_loop(float *out, int iters)
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// C[m][n] = sum_k A[m][k] B[n][k] on the shared 128 x 128 tile, fp32 out;
+// C[m][n] = sum_k A[m][k] B[n][k] on the shared (32 MB) x 128 tile, fp32 out;
 // one workgroup per output tile.
-template <bool AT, bool BT>
+template <bool AT, bool BT, int MB>
 __global__ __launch_bounds__(256) void probe_gemm_tile(const bf16 *A, const bf16 *B, float *C, int M, int N, int K)
 {
-    __shared__ GemmLds L;
+    __shared__ GemmLdsT<32 * MB> L;
     const int tn_n = N / 128;
     const int bid = xcd_block(blockIdx.x, gridDim.x);
     const int tm = bid / tn_n, tn = bid % tn_n;
     const bf16 *as[1] = {A}, *bs[1] = {B};
-    gemm_nt_tile<AT, BT>(L, as, AT ? M : K, bs, BT ? N : K, M, N, K, 1, tm * 128, tn * 128, K,
-                         [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+    gemm_nt_tile<AT, BT, MB>(L, as, AT ? M : K, bs, BT ? N : K, M, N, K, 1, tm * (32 * MB), tn * 128, K,
+                             [&](f32x4 (&acc)[MB][4], int mb, int nb, int g, int mm) {
 #pragma unroll
-                             for (int i = 0; i < 4; ++i)
+                                 for (int i = 0; i < MB; ++i)
 #pragma unroll
-                                 for (int q = 0; q < 4; ++q)
+                                     for (int q = 0; q < 4; ++q)
 #pragma unroll
-                                     for (int r = 0; r < 4; ++r)
-                                         C[(long)(mb + 16 * i + 4 * g + r) * N + nb + 16 * q + mm] = acc[i][q][r];
-                         });
+                                         for (int r = 0; r < 4; ++r)
+                                             C[(long)(mb + 16 * i + 4 * g + r) * N + nb + 16 * q + mm] = acc[i][q][r];
+                             });
+}
+
+template <int MB>
+static void probe_gemm_launch(const bf16 *A, const bf16 *B, float *c, int M, int N, int K, int ak, int bk,
+                              hipStream_t st)
+{
+    const dim3 grid((M / (32 * MB)) * (N / 128)), block(256);
+    if (ak && bk)
+        probe_gemm_tile<true, true, MB><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    else if (ak)
+        probe_gemm_tile<true, false, MB><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    else if (bk)
+        probe_gemm_tile<false, true, MB><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    else
+        probe_gemm_tile<false, false, MB><<<grid, block, 0, st>>>(A, B, c, M, N, K);
 }
 
 }  // namespace tttk
 
 extern "C" ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c, int M, int N, int K, int a_kmajor,
-                                          int b_kmajor, void *stream)
+                                          int b_kmajor, int block_rows, void *stream)
 {
-    if (!a || !b || !c || M < 128 || N < 128 || K < 64 || M % 128 || N % 128 || K % 64) return TTT_EINVAL;
-    if ((long long)(M / 128) * (N / 128) > (1 << 24)) return TTT_EUNSUPPORTED;
-    const dim3 grid((M / 128) * (N / 128)), block(256);
+    if (!a || !b || !c || (block_rows != 128 && block_rows != 256)) return TTT_EINVAL;
+    if (M < block_rows || N < 128 || K < 64 || M % block_rows || N % 128 || K % 64) return TTT_EINVAL;
+    if ((long long)(M / block_rows) * (N / 128) > (1 << 24)) return TTT_EUNSUPPORTED;
     const tttk::bf16 *A = (const tttk::bf16 *)a, *B = (const tttk::bf16 *)b;
     hipStream_t st = (hipStream_t)stream;
-    if (a_kmajor && b_kmajor)
-        tttk::probe_gemm_tile<true, true><<<grid, block, 0, st>>>(A, B, c, M, N, K);
-    else if (a_kmajor)
-        tttk::probe_gemm_tile<true, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
-    else if (b_kmajor)
-        tttk::probe_gemm_tile<false, true><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    if (block_rows == 256)
+        tttk::probe_gemm_launch<8>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
     else
-        tttk::probe_gemm_tile<false, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+        tttk::probe_gemm_launch<4>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
     return hipGetLastError() == hipSuccess ? TTT_OK : TTT_EHIP;
 }
 

@@ -383,16 +383,17 @@ ttt_status ttt_linear_fwd_noalloc(const void *q, const void *k, const void *v, i
 ttt_status ttt_probe_mfma_bf16(float *out, int blocks, int iters, void *stream);
 
 /* ------------------------------------------------------------------------
- * Measurement helper (not part of the layer): the 128 x 128 bf16 GEMM tile
- * the LaCT kernels share, on a plain product, so its rate can be measured:
+ * Measurement helper (not part of the layer): the bf16 GEMM tile the LaCT
+ * kernels share, on a plain product, so its rate can be measured:
  * C[m][n] = sum_k A[m][k] B[n][k], fp32 accumulation and output, one
- * workgroup per 128 x 128 tile of C.  A is [M][K] bf16 (a_kmajor = 0) or
+ * workgroup per block_rows x 128 tile of C (block_rows 128: four 64 x 64 wave
+ * tiles; 256: four 128 x 64 wave tiles).  A is [M][K] bf16 (a_kmajor = 0) or
  * [K][M] (a_kmajor = 1, read as its transpose); B likewise [N][K] or [K][N];
- * C [M][N] fp32, all row-major, device memory, 16-byte aligned.  M, N
- * multiples of 128, K a multiple of 64, else TTT_EINVAL.
+ * C [M][N] fp32, all row-major, device memory, 16-byte aligned.  M a multiple
+ * of block_rows, N of 128, K of 64, block_rows 128 or 256, else TTT_EINVAL.
  * ------------------------------------------------------------------------ */
 ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c, int M, int N, int K, int a_kmajor,
-                               int b_kmajor, void *stream);
+                               int b_kmajor, int block_rows, void *stream);
 
 #ifdef __cplusplus
 }

@@ -8,17 +8,18 @@ import torch
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("rows", [128, 256])
 @pytest.mark.parametrize("ak,bk", [(0, 0), (1, 0), (0, 1), (1, 1)])
-def test_gemm_tile_probe_matches_fp32_product(ak, bk):
+def test_gemm_tile_probe_matches_fp32_product(ak, bk, rows):
     import chunked_linear_attention_amd._lib as L
     lib = L.load()
-    M, N, K = 384, 256, 448
+    M, N, K = 512 if rows == 256 else 384, 256, 448
     g = torch.Generator(device="cuda").manual_seed(11 + 2 * ak + bk)
     a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
     b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
     c = torch.full((M, N), float("nan"), device="cuda")
     st = torch.cuda.current_stream()
-    assert lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk,
+    assert lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk, rows,
                                    st.cuda_stream) == 0
     ref = (a.float().t() if ak else a.float()) @ (b.float() if bk else b.float().t())
     torch.cuda.synchronize()
@@ -31,6 +32,8 @@ def test_probe_argument_checks():
     lib = L.load()
     x = torch.empty(128 * 128, device="cuda", dtype=torch.bfloat16)
     c = torch.empty(128 * 128, device="cuda")
-    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 100, 128, 64, 0, 0, None) == L.TTT_EINVAL
-    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 96, 0, 0, None) == L.TTT_EINVAL
+    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 100, 128, 64, 0, 0, 128, None) == L.TTT_EINVAL
+    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 96, 0, 0, 128, None) == L.TTT_EINVAL
+    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 256, None) == L.TTT_EINVAL
+    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 64, None) == L.TTT_EINVAL
     assert lib.ttt_probe_mfma_bf16(c.data_ptr(), 0, 1, None) == L.TTT_EINVAL
