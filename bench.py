@@ -168,8 +168,9 @@ def measured_peaks():
 
 
 def gemm_probe(steps=20, warmup=3):
-    """The LaCT kernels' shared GEMM tile (128 x 128 and 256 x 128 blocks) on
-    plain bf16 products (ttt_probe_gemm_bf16, fp32 out), beside the vendor GEMM
+    """The LaCT kernels' shared GEMM tile (128 x 128 blocks of four or eight
+    waves, 256 x 128 blocks of four) on plain bf16 products
+    (ttt_probe_gemm_bf16, fp32 out), beside the vendor GEMM
     behind torch.matmul on the same shapes (bf16 in and out) for context; each
     checked against an fp32 product of the same bf16 values on a small shape
     first."""
@@ -178,8 +179,8 @@ def gemm_probe(steps=20, warmup=3):
     lib = L.load()
     st = torch.cuda.current_stream()
 
-    def ours(a, b, c, M, N, K, ak, bk, rows=128):
-        rc = lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk, rows,
+    def ours(a, b, c, M, N, K, ak, bk, rows=128, groups=1):
+        rc = lib.ttt_probe_gemm_bf16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, ak, bk, rows, groups,
                                      st.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"ttt_probe_gemm_bf16 failed ({rc})")
@@ -202,24 +203,27 @@ def gemm_probe(steps=20, warmup=3):
         a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
         b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
         ref = (a.float().t() if ak else a.float()) @ (b.float() if bk else b.float().t())
-        for rows in (128, 256):
+        for rows, groups in ((128, 1), (256, 1), (128, 2)):
             c = torch.empty(M, N, device="cuda")
-            ours(a, b, c, M, N, K, ak, bk, rows)
+            ours(a, b, c, M, N, K, ak, bk, rows, groups)
             torch.cuda.synchronize()
             err = float((c - ref).abs().max() / ref.abs().max())
             if err > 1e-5:
                 raise RuntimeError(f"GEMM tile probe mismatch {err:.2e} at {M}x{N}x{K} ({ak}, {bk}), "
-                                   f"{rows}-row blocks")
+                                   f"{rows}-row blocks, {groups} wave groups")
     for (M, N, K, ak, bk, what) in [(4096, 4096, 4096, 0, 0, "square, both operands k-contiguous"),
                                     (4096, 4096, 4096, 1, 1, "square, both operands k-major"),
                                     (8192, 8192, 8192, 0, 0, "square 8192, k-contiguous"),
                                     (16384, 1024, 256, 0, 0, "LaCT key-forward aspect (tokens x hidden x d)"),
-                                    (1024, 512, 32768, 0, 1, "LaCT weight-gradient aspect (hidden x d x tokens)")]:
+                                    (1024, 512, 32768, 0, 1, "LaCT weight-gradient aspect (hidden x d x tokens)"),
+                                    (2048, 2048, 768, 0, 1, "one tile per CU, 768-deep (LaCT backward GEMMs)"),
+                                    (768, 1024, 512, 1, 1, "48 tiles, 512-deep (Newton-Schulz Gram)")]:
         a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
         b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
         c = torch.empty(M, N, device="cuda")
         ms = timed(lambda: ours(a, b, c, M, N, K, ak, bk))
-        ms_w = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 256))
+        ms_w = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 256)) if M % 256 == 0 else float("nan")
+        ms_2 = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 128, 2))
         at = a.t() if ak else a
         bt = b if bk else b.t()
         at, bt = at.contiguous(), bt.contiguous()
@@ -228,6 +232,7 @@ def gemm_probe(steps=20, warmup=3):
         out.append({"shape": f"{M}x{N}x{K}", "layout": what, "tile_us": ms * 1e3,
                     "tile_tflops": fl / (ms * 1e-3) / 1e12, "tile_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                     "wide_tile_us": ms_w * 1e3, "wide_tile_tflops": fl / (ms_w * 1e-3) / 1e12,
+                    "eight_wave_tile_us": ms_2 * 1e3, "eight_wave_tile_tflops": fl / (ms_2 * 1e-3) / 1e12,
                     "vendor_us": vms * 1e3, "vendor_tflops": fl / (vms * 1e-3) / 1e12})
         del a, b, c, at, bt
     return out

@@ -82,7 +82,7 @@ def load() -> ctypes.CDLL:
         lib.lact_swiglu_decode.restype = i
         lib.ttt_probe_mfma_bf16.argtypes = [vp, i, i, vp]
         lib.ttt_probe_mfma_bf16.restype = i
-        lib.ttt_probe_gemm_bf16.argtypes = [vp, vp, vp] + [i] * 6 + [vp]
+        lib.ttt_probe_gemm_bf16.argtypes = [vp, vp, vp] + [i] * 7 + [vp]
         lib.ttt_probe_gemm_bf16.restype = i
         lib.ttt_linear_noalloc_max_scratch_bytes.argtypes = []
         lib.ttt_linear_noalloc_max_scratch_bytes.restype = sz

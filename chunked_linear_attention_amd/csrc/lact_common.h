@@ -59,10 +59,15 @@ static_assert(sizeof(bf16[GBK][256 + 16]) <= sizeof(bf16[256][GPITCH]), "k-major
 // K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
 // from As[s] and B from Bs[s] (same leading dimensions).  This sums products
 // of split operands (hi and lo bf16 parts) in one accumulation.
-template <bool AT = false, bool BT = false, int MB = 4, typename Epi>
-__device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *const *As, long lda,
-                                             const bf16 *const *Bs, long ldb, int M, int N,
-                                             int kseg, int nseg, int m0, int n0, int kvalid, Epi &&epi)
+// Core of the tile: accumulates the k steps [st_lo, st_lo + nlive) of the
+// product into acc, running nloop steps (a multiple of GPD; steps past nlive
+// compute zeros) so that wave groups with different ranges meet the same
+// barriers.  tid: the thread's index within its group of 256.
+template <bool AT, bool BT, int MB>
+__device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 *const *As, long lda,
+                                               const bf16 *const *Bs, long ldb, int M, int N, int kseg,
+                                               int nseg, int m0, int n0, int kvalid, int st_lo, int nlive,
+                                               int nloop, int tid, f32x4 (&acc)[MB][4])
 {
     static_assert(MB == 4 || MB == 8, "block rows 128 or 256");
     constexpr int BM = 32 * MB;
@@ -70,7 +75,7 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *c
     constexpr int AKT = BM / 8;         // threads per k-major A row (8 elements each)
     constexpr bool TR = AT || BT;  // fragments in the transposing read's k order
     const int K = kseg * nseg;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
     // Pieces of 16 bytes per thread: MB for A, 4 for B.  k-contiguous: rows
@@ -93,10 +98,10 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *c
 #pragma unroll
     for (int i = 0; i < 4; ++i) bok[i] = n0 + lrow[i] < N;
     const int nst = K / GBK;
-    const int ngroups = (nst + GPD - 1) / GPD;
+    const int ngroups = nloop / GPD;
     B8 ra[GPD][MB], rb[GPD][4];
     auto issue = [&](int s, int st) {
-        const int kk = min(st, nst - 1) * GBK;
+        const int kk = min(st_lo + st, nst - 1) * GBK;
         const int sg = kk / kseg, kin = kk - sg * kseg;
         const bf16 *A = As[sg], *B = Bs[sg];
         // A piece i, then B piece i (the order of the 128-row tile)
@@ -117,8 +122,8 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *c
     // Past the last k step the stage holds zeros, so every step computes (the
     // loads, LDS writes and MFMAs of a step stay in one basic block).
     auto commit = [&](int s, int buf, int st) {
-        const bool live = st < nst;
-        const int kin = (min(st, nst - 1) * GBK) % kseg;
+        const bool live = st < nlive;
+        const int kin = (min(st_lo + st, nst - 1) * GBK) % kseg;
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             if constexpr (AT) {
@@ -153,7 +158,6 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *c
         const bf16x4 x1 = load4<bf16>(&X[r][32 * kh + 16 + 4 * g]);
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    f32x4 acc[MB][4];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -204,7 +208,56 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *c
             lds_barrier();
         }
     }
-    epi(acc, m0 + wm * (16 * MB), n0 + wn * 64, g, mm);
+}
+
+template <bool AT = false, bool BT = false, int MB = 4, typename Epi>
+__device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *const *As, long lda,
+                                             const bf16 *const *Bs, long ldb, int M, int N,
+                                             int kseg, int nseg, int m0, int n0, int kvalid, Epi &&epi)
+{
+    const int nst = kseg * nseg / GBK;
+    f32x4 acc[MB][4];
+    gemm_tile_core<AT, BT, MB>(L, As, lda, Bs, ldb, M, N, kseg, nseg, m0, n0, kvalid, 0, nst,
+                               (nst + GPD - 1) / GPD * GPD, threadIdx.x, acc);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    epi(acc, m0 + (wave >> 1) * (16 * MB), n0 + (wave & 1) * 64, lane >> 4, lane & 15);
+}
+
+// The same 128 x 128 tile with eight waves (512 threads): waves 4-7 take the
+// second half of the k steps in their own LDS buffers, so each SIMD runs two
+// waves of one tile and one hides the other's load and LDS latency (for
+// launches with one workgroup per CU).  Their sums are handed to waves 0-3
+// through LDS; waves 4-7 then leave the kernel, and waves 0-3 run the
+// epilogue as in the four-wave tile.  The epilogue must therefore not use a
+// workgroup barrier, and the call must end the kernel.
+template <bool AT = false, bool BT = false, typename Epi>
+__device__ __forceinline__ void gemm_nt_tile_kg2(GemmLds (&L)[2], const bf16 *const *As, long lda,
+                                                 const bf16 *const *Bs, long ldb, int M, int N, int kseg,
+                                                 int nseg, int m0, int n0, int kvalid, Epi &&epi)
+{
+    const int nst = kseg * nseg / GBK;
+    const int half = (nst + 1) / 2;
+    const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+    f32x4 acc[4][4];
+    gemm_tile_core<AT, BT, 4>(L[grp], As, lda, Bs, ldb, M, N, kseg, nseg, m0, n0, kvalid, grp ? half : 0,
+                              grp ? nst - half : half, (half + GPD - 1) / GPD * GPD, tid, acc);
+    // hand-off: lane-linear f32x4 slots in group 1's buffer (64 KB)
+    f32x4 *x = reinterpret_cast<f32x4 *>(&L[1]) + (tid >> 6) * 16 * 64 + (tid & 63);
+    static_assert(sizeof(f32x4) * 4 * 16 * 64 <= sizeof(GemmLds), "hand-off fits the buffer");
+    if (grp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[(4 * i + q) * 64] = acc[i][q];
+    }
+    lds_barrier();
+    if (grp) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] += x[(4 * i + q) * 64];
+    const int lane = tid & 63, wave = tid >> 6;
+    epi(acc, m0 + (wave >> 1) * 64, n0 + (wave & 1) * 64, lane >> 4, lane & 15);
 }
 
 // ---------------------------------------------------------------------------

@@ -63,6 +63,28 @@ __global__ __launch_bounds__(256) void probe_gemm_tile(const bf16 *A, const bf16
                              });
 }
 
+// The eight-wave form of the 128 x 128 tile (two groups of waves splitting k).
+template <bool AT, bool BT>
+__global__ __launch_bounds__(512) void probe_gemm_tile_kg2(const bf16 *A, const bf16 *B, float *C, int M, int N,
+                                                           int K)
+{
+    __shared__ GemmLds L[2];
+    const int tn_n = N / 128;
+    const int bid = xcd_block(blockIdx.x, gridDim.x);
+    const int tm = bid / tn_n, tn = bid % tn_n;
+    const bf16 *as[1] = {A}, *bs[1] = {B};
+    gemm_nt_tile_kg2<AT, BT>(L, as, AT ? M : K, bs, BT ? N : K, M, N, K, 1, tm * 128, tn * 128, K,
+                             [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+#pragma unroll
+                                 for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                     for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                         for (int r = 0; r < 4; ++r)
+                                             C[(long)(mb + 16 * i + 4 * g + r) * N + nb + 16 * q + mm] = acc[i][q][r];
+                             });
+}
+
 template <int MB>
 static void probe_gemm_launch(const bf16 *A, const bf16 *B, float *c, int M, int N, int K, int ak, int bk,
                               hipStream_t st)
@@ -81,14 +103,25 @@ static void probe_gemm_launch(const bf16 *A, const bf16 *B, float *c, int M, int
 }  // namespace tttk
 
 extern "C" ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c, int M, int N, int K, int a_kmajor,
-                                          int b_kmajor, int block_rows, void *stream)
+                                          int b_kmajor, int block_rows, int wave_groups, void *stream)
 {
     if (!a || !b || !c || (block_rows != 128 && block_rows != 256)) return TTT_EINVAL;
+    if (wave_groups != 1 && (wave_groups != 2 || block_rows != 128)) return TTT_EINVAL;
     if (M < block_rows || N < 128 || K < 64 || M % block_rows || N % 128 || K % 64) return TTT_EINVAL;
     if ((long long)(M / block_rows) * (N / 128) > (1 << 24)) return TTT_EUNSUPPORTED;
     const tttk::bf16 *A = (const tttk::bf16 *)a, *B = (const tttk::bf16 *)b;
     hipStream_t st = (hipStream_t)stream;
-    if (block_rows == 256)
+    if (wave_groups == 2) {
+        const dim3 grid((M / 128) * (N / 128)), block(512);
+        if (a_kmajor && b_kmajor)
+            tttk::probe_gemm_tile_kg2<true, true><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+        else if (a_kmajor)
+            tttk::probe_gemm_tile_kg2<true, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+        else if (b_kmajor)
+            tttk::probe_gemm_tile_kg2<false, true><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+        else
+            tttk::probe_gemm_tile_kg2<false, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
+    } else if (block_rows == 256)
         tttk::probe_gemm_launch<8>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
     else
         tttk::probe_gemm_launch<4>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
