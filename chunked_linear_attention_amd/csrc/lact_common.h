@@ -48,6 +48,13 @@ constexpr int GPITCH = GBK + 8;  // LDS row pitch (bf16): 16-byte fragment reads
 constexpr int GTPITCH = 128 + 16;  // k-major stage rows: transposing reads of 8 rows hit distinct banks
 constexpr int GPD = 2;           // register stages in flight (even: LDS buffer = stage parity)
 
+// Row of a k-major stage that holds k row k (see the fragment reads).
+__device__ __forceinline__ int kperm(int k)
+{
+    const int r = k & 31;
+    return (k & ~31) | ((r & 4) ? 16 : 0) | ((r >> 3) << 2) | (r & 3);
+}
+
 template <int BM> struct GemmLdsT {
     bf16 a[2][BM][GPITCH];
     bf16 b[2][128][GPITCH];
@@ -73,7 +80,6 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 
     constexpr int BM = 32 * MB;
     constexpr int TPA = BM + 16;        // k-major A stage pitch
     constexpr int AKT = BM / 8;         // threads per k-major A row (8 elements each)
-    constexpr bool TR = AT || BT;  // fragments in the transposing read's k order
     const int K = kseg * nseg;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, mm = lane & 15;
@@ -128,34 +134,32 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 
         for (int i = 0; i < MB; ++i) {
             if constexpr (AT) {
                 bf16(*T)[TPA] = reinterpret_cast<bf16(*)[TPA]>(&L.a[buf][0][0]);
-                st16(&T[akrow[i]][akcol], (live && kin + akrow[i] < kvalid) ? ra[s][i] : zero16());
+                st16(&T[kperm(akrow[i])][akcol], (live && kin + akrow[i] < kvalid) ? ra[s][i] : zero16());
             } else {
                 st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
             }
             if (i < 4) {
                 if constexpr (BT) {
                     bf16(*T)[GTPITCH] = reinterpret_cast<bf16(*)[GTPITCH]>(&L.b[buf][0][0]);
-                    st16(&T[krow[i & 3]][kcol], (live && kin + krow[i & 3] < kvalid) ? rb[s][i & 3] : zero16());
+                    st16(&T[kperm(krow[i & 3])][kcol], (live && kin + krow[i & 3] < kvalid) ? rb[s][i & 3] : zero16());
                 } else {
                     st16(&L.b[buf][lrow[i]][lcol], (live && bok[i & 3]) ? rb[s][i & 3] : zero16());
                 }
             }
         }
     };
-    // fragment of row r (m or n) for the 32-wide half kh: natural k order
-    // (8 consecutive k per lane) or, when an operand is k-major, k = 4g + j
-    // and 16 + 4g + j on both sides (tp: the k-major stage's row pitch)
+    // fragment of row r (m or n) for the 32-wide half kh, k = 8g + (0..7)
+    // (tp: the k-major stage's row pitch).  A k-major stage stores k row
+    // 8g + j of each 32-row block at row kperm: 4g + j for j < 4, 16 + 4g +
+    // j - 4 otherwise, so the two transposing reads (rows 4g + j and 16 + 4g
+    // + j) return the same natural k order as one 16-byte read of a
+    // k-contiguous row.
     auto frag = [&](const bf16 (*X)[GPITCH], bool kmajor, int tp, int r, int kh) {
-        if (!TR) return as_bf8(ld16(&X[r][32 * kh + 8 * g]));
-        if (kmajor) {
-            const bf16 *T = &X[0][0];
-            const int rb0 = r - mm;  // first row of the 16-row block
-            const bf16x4 x0 = lds_read_tr(T + (32 * kh + 4 * g + (mm >> 2)) * tp + rb0 + 4 * (mm & 3));
-            const bf16x4 x1 = lds_read_tr(T + (32 * kh + 16 + 4 * g + (mm >> 2)) * tp + rb0 + 4 * (mm & 3));
-            return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        const bf16x4 x0 = load4<bf16>(&X[r][32 * kh + 4 * g]);
-        const bf16x4 x1 = load4<bf16>(&X[r][32 * kh + 16 + 4 * g]);
+        if (!kmajor) return as_bf8(ld16(&X[r][32 * kh + 8 * g]));
+        const bf16 *T = &X[0][0];
+        const int rb0 = r - mm;  // first row of the 16-row block
+        const bf16x4 x0 = lds_read_tr(T + (32 * kh + 4 * g + (mm >> 2)) * tp + rb0 + 4 * (mm & 3));
+        const bf16x4 x1 = lds_read_tr(T + (32 * kh + 16 + 4 * g + (mm >> 2)) * tp + rb0 + 4 * (mm & 3));
         return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 #pragma unroll
@@ -165,6 +169,7 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 
 
     // per 32-wide half: MB x 4 MFMAs, MB + 4 loads (or LDS writes) between them
     constexpr int NMF = 4 * MB, NLD = MB + 4;
+    constexpr int RDS = (AT ? 2 : 1) * MB + (BT ? 2 : 1) * 4;  // LDS reads per half
 #pragma unroll
     for (int s = 0; s < GPD; ++s) {
         issue(s, s);
@@ -194,7 +199,7 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[i][q] = mfma32(acc[i][q], af[i], bfr[q]);
-                __builtin_amdgcn_sched_group_barrier(0x100, TR ? 2 * NLD : NLD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, RDS, 0);
 #pragma unroll
                 for (int x = 0; x < NLD; ++x) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
