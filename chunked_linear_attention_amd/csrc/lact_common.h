@@ -64,15 +64,16 @@ static_assert(sizeof(bf16[GBK][GTPITCH]) <= sizeof(bf16[128][GPITCH]), "k-major 
 static_assert(sizeof(bf16[GBK][256 + 16]) <= sizeof(bf16[256][GPITCH]), "k-major stage fits the buffer");
 
 // K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
-// from As[s] and B from Bs[s] (same leading dimensions).  This sums products
-// of split operands (hi and lo bf16 parts) in one accumulation.
+// from As[s] and B from Bs[s] (same leading dimensions; As and Bs are arrays
+// of pointers or anything indexable by the segment number).  This sums
+// products of split operands (hi and lo bf16 parts) in one accumulation.
 // Core of the tile: accumulates the k steps [st_lo, st_lo + nlive) of the
 // product into acc, running nloop steps (a multiple of GPD; steps past nlive
 // compute zeros) so that wave groups with different ranges meet the same
 // barriers.  tid: the thread's index within its group of 256.
-template <bool AT, bool BT, int MB>
-__device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 *const *As, long lda,
-                                               const bf16 *const *Bs, long ldb, int M, int N, int kseg,
+template <bool AT, bool BT, int MB, typename PA, typename PB>
+__device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const PA &As, long lda,
+                                               const PB &Bs, long ldb, int M, int N, int kseg,
                                                int nseg, int m0, int n0, int kvalid, int st_lo, int nlive,
                                                int nloop, int tid, f32x4 (&acc)[MB][4])
 {
@@ -215,9 +216,9 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const bf16 
     }
 }
 
-template <bool AT = false, bool BT = false, int MB = 4, typename Epi>
-__device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *const *As, long lda,
-                                             const bf16 *const *Bs, long ldb, int M, int N,
+template <bool AT = false, bool BT = false, int MB = 4, typename PA, typename PB, typename Epi>
+__device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const PA &As, long lda,
+                                             const PB &Bs, long ldb, int M, int N,
                                              int kseg, int nseg, int m0, int n0, int kvalid, Epi &&epi)
 {
     const int nst = kseg * nseg / GBK;
@@ -235,9 +236,9 @@ __device__ __forceinline__ void gemm_nt_tile(GemmLdsT<32 * MB> &L, const bf16 *c
 // through LDS; waves 4-7 then leave the kernel, and waves 0-3 run the
 // epilogue as in the four-wave tile.  The epilogue must therefore not use a
 // workgroup barrier, and the call must end the kernel.
-template <bool AT = false, bool BT = false, typename Epi>
-__device__ __forceinline__ void gemm_nt_tile_kg2(GemmLds (&L)[2], const bf16 *const *As, long lda,
-                                                 const bf16 *const *Bs, long ldb, int M, int N, int kseg,
+template <bool AT = false, bool BT = false, typename PA, typename PB, typename Epi>
+__device__ __forceinline__ void gemm_nt_tile_kg2(GemmLds (&L)[2], const PA &As, long lda,
+                                                 const PB &Bs, long ldb, int M, int N, int kseg,
                                                  int nseg, int m0, int n0, int kvalid, Epi &&epi)
 {
     const int nst = kseg * nseg / GBK;

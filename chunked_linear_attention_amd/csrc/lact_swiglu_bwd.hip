@@ -70,6 +70,16 @@ struct BwdGemm {
     long p_ss, p_hs;
 };
 
+// Operand of segment s of a job: the job's pointer for segment s0 + s (read
+// from the kernel arguments with a scalar load when the tile needs it, so the
+// twelve segment pointers never occupy registers) at head h and k offset.
+struct BwdSegPtr {
+    const bf16 *const *p;
+    int s0;
+    long off;
+    __device__ __forceinline__ const bf16 *operator[](int s) const { return p[s0 + s] + off; }
+};
+
 template <bool AT, bool BT>
 __global__ __launch_bounds__(256) void lbk_gemm(BwdGemm j)
 {
@@ -96,12 +106,7 @@ __global__ __launch_bounds__(256) void lbk_gemm(BwdGemm j)
             s0 = ks * ns;
         }
     }
-    const bf16 *as[BWD_MAXSEG], *bs[BWD_MAXSEG];
-#pragma unroll
-    for (int s = 0; s < BWD_MAXSEG; ++s) {
-        as[s] = (s < ns) ? j.A[s0 + s] + (long)h * j.a_hs + koff_a : nullptr;
-        bs[s] = (s < ns) ? j.B[s0 + s] + (long)h * j.b_hs + koff_b : nullptr;
-    }
+    const BwdSegPtr as{j.A, s0, (long)h * j.a_hs + koff_a}, bs{j.B, s0, (long)h * j.b_hs + koff_b};
     float *P = j.P ? j.P + (long)ks * j.p_ss + (long)h * j.p_hs : nullptr;
     float *C = j.C ? j.C + (long)h * j.c_hs : nullptr;
     bf16 *Cb = j.Cb ? j.Cb + (long)h * j.c_hs : nullptr;
