@@ -144,32 +144,47 @@ __global__ __launch_bounds__(256) void lbk_gemm(BwdGemm j)
                          });
 }
 
-// lam[i] += sum_ks P[ks stride + i], in split order
+// Sum of ksplit fp32 partial planes in split order, four consecutive elements
+// per thread with up to eight planes' loads in flight at once (the adds keep
+// the order k = 0, 1, ..., so the result is the same as one plane at a time).
+__device__ __forceinline__ f32x4 red_planes(const float *P, int ksplit, long stride, long e)
+{
+    f32x4 x = zero4();
+    for (int k0 = 0; k0 < ksplit; k0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (k0 + k < ksplit) ? load4<float>(P + (long)(k0 + k) * stride + e) : zero4();
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k0 + k < ksplit) x += v[k];
+    }
+    return x;
+}
+
+// lam[i] += sum_ks P[ks stride + i], in split order (n and stride multiples
+// of 4, 16-byte aligned planes)
 __global__ __launch_bounds__(256) void lbk_red_add(const float *P, int ksplit, long stride, float *lam, long n)
 {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-        float x = 0.f;
-        for (int k = 0; k < ksplit; ++k) x += P[(long)k * stride + i];
-        lam[i] += x;
-    }
+    for (long i = 4 * ((long)blockIdx.x * 256 + threadIdx.x); i < n; i += 4 * (long)gridDim.x * 256)
+        store4<float>(lam + i, load4<float>(lam + i) + red_planes(P, ksplit, stride, i));
 }
 
 // out[h][t][i] = sum_ks P[ks stride + (h rpad + t) d + i] for t < rows; out as
-// bf16 (ob, head stride o_hs) or fp32 (of, same layout as the partials)
+// bf16 (ob, head stride o_hs) or fp32 (of, same layout as the partials); d and
+// stride multiples of 4
 __global__ __launch_bounds__(256) void lbk_red_rows(const float *P, int ksplit, long stride, int NH, int rows,
                                                     int rpad, int d, bf16 *ob, long o_hs, float *of)
 {
     const long n = (long)NH * rows * d;
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    for (long i = 4 * ((long)blockIdx.x * 256 + threadIdx.x); i < n; i += 4 * (long)gridDim.x * 256) {
         const int h = (int)(i / ((long)rows * d));
         const long r = i % ((long)rows * d);
         const long src = (long)h * rpad * d + r;
-        float x = 0.f;
-        for (int k = 0; k < ksplit; ++k) x += P[(long)k * stride + src];
+        const f32x4 x = red_planes(P, ksplit, stride, src);
         if (ob)
-            ob[(long)h * o_hs + r] = (bf16)x;
+            store4<bf16>(ob + (long)h * o_hs + r, to_bf16x4(x));
         else
-            of[src] = x;
+            store4<float>(of + src, x);
     }
 }
 
@@ -463,6 +478,8 @@ static int split_tokens(BwdGemm &j, int NH, int ntok)
 }
 
 static unsigned ew_grid(long n) { return (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192); }
+// grid of the four-element reductions
+static unsigned ew_grid4(long n) { return ew_grid((n + 3) / 4); }
 
 static BwdGemm gemm_job(int M, int N, int kseg, int kvalid, long lda, long a_hs, long ldb, long b_hs)
 {
@@ -524,7 +541,7 @@ static void weight_adjoints(BwdGemm (&jobs)[3], const BwdBufs &b, int NH, long n
     }
     if (ks > 1) {
         const long n = (long)NH * 3 * n13;
-        lbk_red_add<<<dim3(ew_grid(n)), dim3(256), 0, st>>>(b.part, ks, n, b.lam, n);
+        lbk_red_add<<<dim3(ew_grid4(n)), dim3(256), 0, st>>>(b.part, ks, n, b.lam, n);
     }
 }
 
@@ -545,7 +562,7 @@ static void token_side(BwdGemm &j, const BwdBufs &b, const LactBwdPlan &pl, int 
     j.ldc = d;
     run_gemm<false, BT>(j, NH, st);
     const long n = (long)NH * rows * d;
-    lbk_red_rows<<<dim3(ew_grid(n)), dim3(256), 0, st>>>(b.part, j.ksplit, j.p_ss, NH, rows, pl.rpad, d, ob, o_hs,
+    lbk_red_rows<<<dim3(ew_grid4(n)), dim3(256), 0, st>>>(b.part, j.ksplit, j.p_ss, NH, rows, pl.rpad, d, ob, o_hs,
                                                          of);
 }
 
