@@ -794,15 +794,17 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
     // w_init itself, or the summary's copy of it when w_final is the same
     // buffer (the last segment writes it while earlier ones may still read).
     const float *ws = (p.wsW0 ? p.wsW0 : p.w_init) + (size_t)h * D * D;
+    // Only R (and, for chunks longer than a super-block, the chunk-start
+    // snapshot Ss) is carried from one super-block to the next; the bf16
+    // split of R is formed where a super-block starts, so it is not live
+    // across the tile loads.
     f32x4 R[ND];
-    SplitFrag<E> Rs[ND], Ss[SNAP ? ND : 1];
+    SplitFrag<E> Ss[SNAP ? ND : 1];
 #pragma unroll
     for (int r = 0; r < ND; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j) R[r][j] = ws[(size_t)(16 * r + 4 * g + j) * D + 16 * c + m];
     if (seg > 0) chain_maps<E, D, MSE, NT, NPB>(R, p, h, seg, lds.pst, c, m, g);
-#pragma unroll
-    for (int r = 0; r < ND; ++r) Rs[r].set(R[r]);
 
     SbLoader<E, D, ST, PD, NT> ld;
     ld.init(threadIdx.x, p.q, p.k, p.v, p.eta, h, T, tend);
@@ -813,6 +815,9 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
         const int lim = min(tend, s + len);
         f32x4 et[4];
         load_eta(t, len, g, et);
+        SplitFrag<E> Rs[ND];
+#pragma unroll
+        for (int r = 0; r < ND; ++r) Rs[r].set(R[r]);
         if (SNAP && sc.chunk_start(n)) {
 #pragma unroll
             for (int r = 0; r < ND; ++r) Ss[r] = Rs[r];
@@ -881,7 +886,6 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
         for (int r = 0; r < ND; ++r) {
             R[r] = mma32(R[r], k_tok(t, 0, r, m, g), k_tok(t, 1, r, m, g), EU[0], EU[1]);
             R[r] = mma32(R[r], k_tok(t, 2, r, m, g), k_tok(t, 3, r, m, g), EU[2], EU[3]);
-            Rs[r].set(R[r]);
         }
     });
 
