@@ -93,28 +93,38 @@ class Rotated:
 
 def time_calls(fn, sets, steps, warmup):
     """Warm up, then time exactly `steps` calls between two device syncs with
-    HIP events recorded on the current stream (the one the library launches on).
-    An event is also recorded between consecutive calls, so every call's own
-    duration is known.  Returns (mean ms per call over the bracketed region,
-    median ms per call, wall seconds of the timed region)."""
+    HIP events recorded on the current stream (the one the library launches
+    on), only before the first and after the last call, so nothing but the
+    calls runs in between.  A second pass of the same calls records an event
+    between consecutive calls for each call's own duration (the median).
+    Returns (mean ms per call over the bracketed region of the first pass,
+    median ms per call of the second, wall seconds of the first pass's timed
+    region)."""
     import torch
     for i in range(warmup):
         fn(sets[i])
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(st)
+    for i in range(steps):
+        fn(sets[i])
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(st)
     for i in range(steps):
         fn(sets[i])
         ev[i + 1].record(st)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     mid = steps // 2
     median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
-    return ev[0].elapsed_time(ev[steps]) / steps, median, wall
+    return mean, median, wall
 
 
 # The pages' benchmark method: 10 warm-up calls, then 100 timed calls with the
