@@ -30,9 +30,12 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # against the compiler's own choice in one process (library variants timed
 # back to back): TTT-Linear keeps it (its state sits in MFMA accumulators that
 # the vector code updates); the LaCT forward gained ~4% on the causal and ~2%
-# on the non-causal workload with it; the LaCT backward is ~1% slower with it.
+# on the non-causal workload with it; the LaCT backward, once its GEMM no
+# longer held its segment pointers in registers, gained ~1.6% (9.61 -> 9.46 ms;
+# before that change it was ~1% slower with the flag).
 FLAGS = {"ttt_linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "lact_swiglu.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "lact_swiglu.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "lact_swiglu_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
