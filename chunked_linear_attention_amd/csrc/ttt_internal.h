@@ -92,5 +92,11 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
                              const float *eta, const float *w0, const void *dout, const float *dwf,
                              void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
                              hipStream_t stream);
+// chunks of several 16-token tiles (a separately compiled unit)
+hipError_t linear_bwd_launch_tiled(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                                   int bf16, const void *q, const void *k, const void *v,
+                                   const float *eta, const float *w0, const void *dout, const float *dwf,
+                                   void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
+                                   hipStream_t stream);
 
 }  // namespace tttk

@@ -1210,6 +1210,7 @@ static void seg_plan(int NH, int nch, int chunk, int d, int &nseg, int &seg_chun
     }
 }
 
+#ifndef TTT_LBW_TILED_UNIT
 size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
 {
     const size_t nch = (Tkv + chunk - 1) / chunk;
@@ -1222,6 +1223,7 @@ size_t linear_bwd_workspace(int NH, int Tkv, int d, int chunk)
            (nch * (3 * (size_t)d * d + 3 * (size_t)chunk * d) + 2 * (size_t)d * d + (size_t)nseg * 3 * d * d) *
            sizeof(float);
 }
+#endif
 
 // The two serial recursions, each as segment maps, chain, walks.
 // (one wave per (head, segment, 16 columns), four waves a workgroup: the
@@ -1311,11 +1313,10 @@ static void lbw_run_tiled(const LinBwdParams &p, int NH, hipStream_t st)
     lbw_dep_launch<D, E>(p, NH, st);
 }
 
-hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
-                             int bf16, const void *q, const void *k, const void *v,
-                             const float *eta, const float *w0, const void *dout, const float *dwf,
-                             void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
-                             hipStream_t st)
+static LinBwdParams lbw_params(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                               const void *q, const void *k, const void *v, const float *eta, const float *w0,
+                               const void *dout, const float *dwf, void *dq, void *dk, void *dv, float *deta,
+                               float *dw0, void *ws)
 {
     const int nch = (Tkv + chunk - 1) / chunk;
     float *base = static_cast<float *>(ws);
@@ -1330,24 +1331,53 @@ hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss
     p.sstart = p.ssum + (size_t)NH * p.nseg * 2 * d * d;
     p.tpc = chunk / 16;
     p.nwt = (Tkv + 15) / 16;
-    if (chunk == 16) {  // a chunk is one tile
-        if (d == 128) {
-            if (bf16) lbw_run<128, __bf16>(p, NH, st);
-            else lbw_run<128, float>(p, NH, st);
-        } else {
-            if (bf16) lbw_run<64, __bf16>(p, NH, st);
-            else lbw_run<64, float>(p, NH, st);
-        }
-    } else {  // several tiles a chunk
-        if (d == 128) {
-            if (bf16) lbw_run_tiled<128, __bf16>(p, NH, st);
-            else lbw_run_tiled<128, float>(p, NH, st);
-        } else {
-            if (bf16) lbw_run_tiled<64, __bf16>(p, NH, st);
-            else lbw_run_tiled<64, float>(p, NH, st);
-        }
+    return p;
+}
+
+// This source is compiled twice: the main unit runs 16-token chunks (a chunk
+// is one tile) and the unit built with TTT_LBW_TILED_UNIT, whose MFMA
+// operands are forced into VGPRs, runs chunks of several tiles (measured: the
+// VGPR form is 3-18% faster on every multi-tile chunk size and 2-4% slower
+// on 16-token chunks).
+#ifdef TTT_LBW_TILED_UNIT
+hipError_t linear_bwd_launch_tiled(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                                   int bf16, const void *q, const void *k, const void *v,
+                                   const float *eta, const float *w0, const void *dout, const float *dwf,
+                                   void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
+                                   hipStream_t st)
+{
+    const LinBwdParams p = lbw_params(NH, Tq, Tkv, d, chunk, loss, order, q, k, v, eta, w0, dout, dwf, dq, dk,
+                                      dv, deta, dw0, ws);
+    if (d == 128) {
+        if (bf16) lbw_run_tiled<128, __bf16>(p, NH, st);
+        else lbw_run_tiled<128, float>(p, NH, st);
+    } else {
+        if (bf16) lbw_run_tiled<64, __bf16>(p, NH, st);
+        else lbw_run_tiled<64, float>(p, NH, st);
     }
     return hipGetLastError();
 }
+#else
+hipError_t linear_bwd_launch(int NH, int Tq, int Tkv, int d, int chunk, int loss, int order,
+                             int bf16, const void *q, const void *k, const void *v,
+                             const float *eta, const float *w0, const void *dout, const float *dwf,
+                             void *dq, void *dk, void *dv, float *deta, float *dw0, void *ws,
+                             hipStream_t st)
+{
+    if (chunk != 16)  // several tiles a chunk
+        return linear_bwd_launch_tiled(NH, Tq, Tkv, d, chunk, loss, order, bf16, q, k, v, eta, w0, dout, dwf,
+                                       dq, dk, dv, deta, dw0, ws, st);
+    const LinBwdParams p = lbw_params(NH, Tq, Tkv, d, chunk, loss, order, q, k, v, eta, w0, dout, dwf, dq, dk,
+                                      dv, deta, dw0, ws);
+    if (d == 128) {
+        if (bf16) lbw_run<128, __bf16>(p, NH, st);
+        else lbw_run<128, float>(p, NH, st);
+    } else {
+        if (bf16) lbw_run<64, __bf16>(p, NH, st);
+        else lbw_run<64, float>(p, NH, st);
+    }
+    return hipGetLastError();
+}
+#endif
 
 }  // namespace tttk
