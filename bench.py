@@ -91,8 +91,30 @@ class Rotated:
         return self.sets[i % self.n]
 
 
+SPIN_UP_S = 0.2
+
+
+def spin_up(seconds=SPIN_UP_S):
+    """Keep the matrix cores busy for about `seconds` (back-to-back launches of
+    the library's MFMA loop, ttt_probe_mfma_bf16) so that the timed calls do
+    not start from the clocks of an idle GPU: measured after a second of idle,
+    the first ~50 ms of TTT-Linear calls run up to 25% slower than the rate the
+    part settles at.  No part of any timed workload runs here."""
+    import torch
+    import chunked_linear_attention_amd._lib as L
+    lib = L.load()
+    st = torch.cuda.current_stream()
+    out = torch.empty(2048 * 256, device="cuda")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            if lib.ttt_probe_mfma_bf16(out.data_ptr(), 2048, 2000, st.cuda_stream) != 0:
+                raise RuntimeError("ttt_probe_mfma_bf16 failed")
+        torch.cuda.synchronize()
+
+
 def time_calls(fn, sets, steps, warmup):
-    """Warm up, then time exactly `steps` calls between two device syncs with
+    """Spin the GPU up (spin_up), warm up, then time exactly `steps` calls between two device syncs with
     HIP events recorded on the current stream (the one the library launches
     on), only before the first and after the last call, so nothing but the
     calls runs in between.  A second pass of the same calls records an event
@@ -101,6 +123,7 @@ def time_calls(fn, sets, steps, warmup):
     median ms per call of the second, wall seconds of the first pass's timed
     region)."""
     import torch
+    spin_up()
     for i in range(warmup):
         fn(sets[i])
     torch.cuda.synchronize()
@@ -781,7 +804,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "heads": wl.H, "seq_len": wl.T,
                    "head_dim": wl.d, "chunk": wl.chunk, "loss": "mse", "order": "causal",
-                   "state": "fp32", "input_copies_rotated": r["copies"]},
+                   "state": "fp32", "input_copies_rotated": r["copies"],
+                   "gpu_spin_up_s_before_warmup": SPIN_UP_S},
         "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
                      "unit_of_launch": "one ttt_linear_fwd call (summary and replay kernels)",
