@@ -189,7 +189,7 @@ __global__ __launch_bounds__(64 * NW) void lact_fwdgrad(LactParams p, int c, int
             st16(&L.ay[buf][row][lcol], B8{__builtin_bit_cast(u32x4v, o)});
             st16(&L.b1[buf][row][lcol], r1[s][i]);
             st16(&L.b3[buf][row][lcol], r3[s][i]);
-            st16(&L.b2[buf][orow + 16 * i][hcol], r2[s][i]);
+            st16(&L.b2[buf][kperm(orow + 16 * i)][hcol], r2[s][i]);
         }
     };
     // wave (wm, wn): tokens TOKW wm .. TOKW wm + TOKW - 1 (MI m-tiles), hidden
@@ -209,18 +209,17 @@ __global__ __launch_bounds__(64 * NW) void lact_fwdgrad(LactParams p, int c, int
         for (int j = 0; j < FPD; ++j) {
             const int st = gi * FPD + j;
             const int buf = j & 1;  // FPD is even: the LDS buffer is the k-step parity
-            // All fragments of the step first.  K x W1/W3: natural k order (8
-            // consecutive k per lane).  dY x W2: W2's fragments come from the
-            // transposing read (k = 4g + j and 16 + 4g + j), and dY's use the
-            // same k order.
+            // All fragments of the step first, all in natural k order (8
+            // consecutive k per lane).  W2's fragments come from the
+            // transposing read; its stage holds k row 8g + j at row kperm (4g +
+            // j, or 16 + 4g + j - 4), so the two reads return k = 8g .. 8g + 7
+            // and dY's fragments are one 16-byte read like K's.
             bf16x8 fk[MI], fy[MI], f1[4], f3[4], f2[4];
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int row = wm * TOKW + 16 * i + mm;
                 fk[i] = as_bf8(ld16(&L.ak[buf][row][8 * g]));
-                const bf16x4 y0 = load4<bf16>(&L.ay[buf][row][4 * g]);
-                const bf16x4 y1 = load4<bf16>(&L.ay[buf][row][16 + 4 * g]);
-                fy[i] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+                fy[i] = as_bf8(ld16(&L.ay[buf][row][8 * g]));
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -244,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void lact_fwdgrad(LactParams p, int c, int
                 }
             // schedule: the fragment reads, then the MFMAs with a global load
             // or an LDS write after every second one
-            __builtin_amdgcn_sched_group_barrier(0x100, 3 * MI + 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MI + 16, 0);
 #pragma unroll
             for (int x = 0; x < 5 * NI; ++x) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
