@@ -68,8 +68,10 @@ struct LinParams {
 constexpr int SB = 64;  // tokens per super-block tile (four 16-token tiles)
 
 // Which tensors a kernel stages; STAGE_SWZ: bf16 tiles use the swizzled
-// layout below instead of padded rows.
-enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8, STAGE_SWZ = 16 };
+// layout below instead of padded rows; STAGE_PERM: padded bf16 rows whose
+// 4-column groups are permuted (pcol below) so that the two 16-column halves a
+// 32-deep row fragment pairs are one 16-byte read.
+enum { STAGE_Q = 1, STAGE_K = 2, STAGE_V = 4, STAGE_E = 8, STAGE_SWZ = 16, STAGE_PERM = 32 };
 
 // Swizzled position of the 4-column group starting at column col (a multiple
 // of 4) in row row of an unpadded bf16 tile: inside each 64-column group the
@@ -84,6 +86,20 @@ __device__ __forceinline__ int swz(int row, int col)
     return (col & ~63) | ((((col >> 3) & 7) ^ v) << 3) | ((((col >> 2) & 1) ^ hs) << 2);
 }
 
+// Permuted position of the 4-column group starting at column col (a multiple
+// of 4): inside each 32-column block, group g of the first 16 columns goes to
+// 8g and group g of the second 16 to 8g + 4.  A 32-deep row fragment pairs
+// columns 32s + 4g + (0..3) with 32s + 16 + 4g + (0..3) (the state's
+// accumulator order), which then lie side by side.
+__device__ __forceinline__ bf16x8 as_bf8x(const __bf16 *p)
+{
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ int pcol(int col)
+{
+    return (col & ~31) | (((col >> 2) & 3) << 3) | (((col >> 4) & 1) << 2) | (col & 3);
+}
+
 // LDS image of one 64-token super-block.  bf16: token-major tiles; fragments
 // that need four consecutive tokens of one feature come from the transposing
 // read.  fp32: queries token-major, keys and values feature-major (rows
@@ -92,6 +108,7 @@ template <typename E, int D, int ST> struct alignas(16) SbTile {
     static constexpr bool TR = sizeof(E) == 2;
     static constexpr bool LQ = (ST & STAGE_Q) != 0, LK = (ST & STAGE_K) != 0, LV = (ST & STAGE_V) != 0;
     static constexpr bool SW = TR && (ST & STAGE_SWZ) != 0;
+    static constexpr bool PM = TR && !SW && (ST & STAGE_PERM) != 0;
     static constexpr int RP = SW ? D : D + (TR ? 8 : 4);  // token-major row pitch
     static constexpr int FP = SB + 4;            // feature-major row pitch (fp32)
     E qs[LQ ? SB : 1][RP];
@@ -105,20 +122,23 @@ template <typename E, int D, int ST> struct alignas(16) SbTile {
 // Row fragment (rows = tokens of tile i, contraction over features 16r..16r+15):
 // lane (m, g) gets X[16i + m][16r + 4g + j].
 // column of the 4-column group at col in row row of a token-major tile
-template <bool SW> __device__ __forceinline__ int tcol(int row, int col) { return SW ? swz(row, col) : col; }
+template <bool SW, bool PM = false> __device__ __forceinline__ int tcol(int row, int col)
+{
+    return SW ? swz(row, col) : PM ? pcol(col) : col;
+}
 
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type q_row(const SbTile<E, D, ST> &t, int i, int r, int m, int g)
 {
-    constexpr bool SW = SbTile<E, D, ST>::SW;
-    return load4<E>(&t.qs[16 * i + m][tcol<SW>(16 * i + m, 16 * r + 4 * g)]);
+    constexpr bool SW = SbTile<E, D, ST>::SW, PM = SbTile<E, D, ST>::PM;
+    return load4<E>(&t.qs[16 * i + m][tcol<SW, PM>(16 * i + m, 16 * r + 4 * g)]);
 }
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type k_row(const SbTile<E, D, ST> &t, int i, int r, int m, int g)
 {
-    constexpr bool SW = SbTile<E, D, ST>::SW;
+    constexpr bool SW = SbTile<E, D, ST>::SW, PM = SbTile<E, D, ST>::PM;
     if constexpr (SbTile<E, D, ST>::TR) {
-        return load4<E>(&t.ks[16 * i + m][tcol<SW>(16 * i + m, 16 * r + 4 * g)]);
+        return load4<E>(&t.ks[16 * i + m][tcol<SW, PM>(16 * i + m, 16 * r + 4 * g)]);
     } else {
         f32x4 x;
 #pragma unroll
@@ -132,22 +152,51 @@ __device__ __forceinline__ typename Frag<E>::type k_row(const SbTile<E, D, ST> &
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type k_tok(const SbTile<E, D, ST> &t, int i, int c, int m, int g)
 {
-    constexpr bool SW = SbTile<E, D, ST>::SW;
+    constexpr bool SW = SbTile<E, D, ST>::SW, PM = SbTile<E, D, ST>::PM;
     const int row = 16 * i + 4 * g + (m >> 2);
     if constexpr (SbTile<E, D, ST>::TR)
-        return lds_read_tr(&t.ks[row][tcol<SW>(row, 16 * c + 4 * (m & 3))]);
+        return lds_read_tr(&t.ks[row][tcol<SW, PM>(row, 16 * c + 4 * (m & 3))]);
     else
         return load4<E>(&t.kt[16 * c + m][16 * i + 4 * g]);
 }
 template <typename E, int D, int ST>
 __device__ __forceinline__ typename Frag<E>::type v_tok(const SbTile<E, D, ST> &t, int i, int c, int m, int g)
 {
-    constexpr bool SW = SbTile<E, D, ST>::SW;
+    constexpr bool SW = SbTile<E, D, ST>::SW, PM = SbTile<E, D, ST>::PM;
     const int row = 16 * i + 4 * g + (m >> 2);
     if constexpr (SbTile<E, D, ST>::TR)
-        return lds_read_tr(&t.vs[row][tcol<SW>(row, 16 * c + 4 * (m & 3))]);
+        return lds_read_tr(&t.vs[row][tcol<SW, PM>(row, 16 * c + 4 * (m & 3))]);
     else
         return load4<E>(&t.vt[16 * c + m][16 * i + 4 * g]);
+}
+
+// Row fragments r and r + 1 (r even) of tile i: with the permuted layout one
+// 16-byte read, otherwise two 8-byte ones.
+template <typename E, int D, int ST>
+__device__ __forceinline__ void q_row2(const SbTile<E, D, ST> &t, int i, int r, int m, int g,
+                                       typename Frag<E>::type &a, typename Frag<E>::type &b)
+{
+    if constexpr (SbTile<E, D, ST>::PM) {
+        const bf16x8 x = as_bf8x(&t.qs[16 * i + m][pcol(16 * r + 4 * g)]);
+        a = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+        b = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    } else {
+        a = q_row(t, i, r, m, g);
+        b = q_row(t, i, r + 1, m, g);
+    }
+}
+template <typename E, int D, int ST>
+__device__ __forceinline__ void k_row2(const SbTile<E, D, ST> &t, int i, int r, int m, int g,
+                                       typename Frag<E>::type &a, typename Frag<E>::type &b)
+{
+    if constexpr (SbTile<E, D, ST>::PM) {
+        const bf16x8 x = as_bf8x(&t.ks[16 * i + m][pcol(16 * r + 4 * g)]);
+        a = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+        b = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    } else {
+        a = k_row(t, i, r, m, g);
+        b = k_row(t, i, r + 1, m, g);
+    }
 }
 
 // Transformed keys Kt = T K of one super-block, shared by the waves: each wave
@@ -241,14 +290,29 @@ template <typename E, int D, int ST, int PD, int NT> struct SbLoader {
     {
         return ((r >> 3) & 1) ? u32x4{x[2], x[3], x[0], x[1]} : x;
     }
+    // The two 8-byte halves of a piece, to their own places.
+    static __device__ __forceinline__ void put_halves(E *a, E *b, u32x4 x)
+    {
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2v *>(a) = u32x2v{x[0], x[1]};
+        *reinterpret_cast<u32x2v *>(b) = u32x2v{x[2], x[3]};
+    }
     // Write slot s to LDS.
     __device__ __forceinline__ void commit(int s, Tile &tl)
     {
-        constexpr bool SW = Tile::SW;
+        constexpr bool SW = Tile::SW, PM = Tile::PM;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int r = row[i], c0 = PE * col[i];
             const int c = SW ? (swz(r, c0) & ~7) : c0;
+            if constexpr (PM) {
+                // the piece's two 4-column groups land at their own permuted places
+                const int ca = pcol(c0), cb = pcol(c0 + 4);
+                if (LQ) put_halves(&tl.qs[r][ca], &tl.qs[r][cb], vq[s][i]);
+                if (LK) put_halves(&tl.ks[r][ca], &tl.ks[r][cb], vk[s][i]);
+                if (LV) put_halves(&tl.vs[r][ca], &tl.vs[r][cb], vv[s][i]);
+                continue;
+            }
             if (LQ) *reinterpret_cast<u32x4 *>(&tl.qs[r][c]) = SW ? halves(vq[s][i], r) : vq[s][i];
             if (LK) {
                 if constexpr (TR) {
@@ -431,12 +495,16 @@ __device__ __forceinline__ void pair_blocks(const SbTile<E, D, ST> &t, typename 
         }
         F Kj[ND], Xi[ND];
 #pragma unroll
-        for (int r = 0; r < ND; ++r) {
-            Kj[r] = k_row(t, j, r, m, g);
-            if constexpr (SbTile<E, D, ST>::LQ)
-                Xi[r] = isL ? k_row(t, i, r, m, g) : q_row(t, i, r, m, g);
-            else
-                Xi[r] = k_row(t, i, r, m, g);
+        for (int r = 0; r < ND; r += 2) {
+            k_row2(t, j, r, m, g, Kj[r], Kj[r + 1]);
+            if constexpr (SbTile<E, D, ST>::LQ) {
+                if (isL)
+                    k_row2(t, i, r, m, g, Xi[r], Xi[r + 1]);
+                else
+                    q_row2(t, i, r, m, g, Xi[r], Xi[r + 1]);
+            } else {
+                k_row2(t, i, r, m, g, Xi[r], Xi[r + 1]);
+            }
         }
         f32x4 acc = mma_b<F, ND>(zero4(), Kj, Xi);
         if (isL) {
@@ -495,7 +563,7 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_summary(LinParams p)
     constexpr int ND = D / 16;
     constexpr int NT = ND * 64;
     constexpr int NBUF = sizeof(E) == 2 ? 2 : 1;
-    constexpr int ST = STAGE_K | STAGE_V | STAGE_E;
+    constexpr int ST = STAGE_K | STAGE_V | STAGE_E | STAGE_PERM;
     __shared__ SbTile<E, D, ST> tiles[NBUF];
     __shared__ KtTile<E, LT ? D : 16> kts;
     __shared__ F gb[LT ? 16 : 1][64];
@@ -578,11 +646,13 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_summary(LinParams p)
         for (int i = 0; i < 4; ++i) {
             F Ka[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) {
-                if constexpr (LT)
+            for (int r = 0; r < ND; r += 2) {
+                if constexpr (LT) {
                     Ka[r] = kts.row(i, r, m, g);
-                else
-                    Ka[r] = k_row(t, i, r, m, g);
+                    Ka[r + 1] = kts.row(i, r + 1, m, g);
+                } else {
+                    k_row2(t, i, r, m, g, Ka[r], Ka[r + 1]);
+                }
             }
             const f32x4 Up = Kc[i] - mma_b<F, ND>(zero4(), Ka, SNAP ? Xps : Xpr);
             const f32x4 Ub = Vc[i] - mma_b<F, ND>(zero4(), Ka, SNAP ? Xbs : Xbr);
@@ -771,7 +841,7 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
     constexpr int ND = D / 16;
     constexpr int NT = ND * 64;
     constexpr int NBUF = sizeof(E) == 2 ? 2 : 1;
-    constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E;
+    constexpr int ST = STAGE_Q | STAGE_K | STAGE_V | STAGE_E | STAGE_PERM;
     constexpr int NPB = (sizeof(E) == 4 && D == 128) ? 1 : 2;
     // The super-block tiles and the staged P of the segment-start chain are
     // never live at the same time.
@@ -846,11 +916,13 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
             for (int i = 0; i < 4; ++i) {
                 F Ka[ND];
 #pragma unroll
-                for (int r = 0; r < ND; ++r) {
-                    if constexpr (LT)
+                for (int r = 0; r < ND; r += 2) {
+                    if constexpr (LT) {
                         Ka[r] = kts.row(i, r, m, g);
-                    else
-                        Ka[r] = k_row(t, i, r, m, g);
+                        Ka[r + 1] = kts.row(i, r + 1, m, g);
+                    } else {
+                        k_row2(t, i, r, m, g, Ka[r], Ka[r + 1]);
+                    }
                 }
                 U[i] = U[i] - mma_state_b<E, ND>(zero4(), Ka, SNAP ? Ss : Rs);
             }
@@ -869,7 +941,7 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_replay(LinParams p)
             if (16 * i >= len) break;
             F Qa[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) Qa[r] = q_row(t, i, r, m, g);
+            for (int r = 0; r < ND; r += 2) q_row2(t, i, r, m, g, Qa[r], Qa[r + 1]);
             f32x4 O = mma_state_a<E, ND>(zero4(), Rs, Qa);
 #pragma unroll
             for (int j = 0; j <= i; j += 2) {
@@ -1636,7 +1708,7 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_apply(LinParams p, const fl
     typedef typename Frag<E>::type F;
     constexpr int ND = D / 16;
     constexpr int NT = ND * 64;
-    constexpr int ST = STAGE_Q;
+    constexpr int ST = STAGE_Q | STAGE_PERM;
     __shared__ SbTile<E, D, ST> tiles[2];
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
     const int c = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // column block
@@ -1664,7 +1736,7 @@ __global__ __launch_bounds__((D / 16) * 64) void lin_apply(LinParams p, const fl
         for (int i = 0; i < 4; ++i) {
             F Qa[ND];
 #pragma unroll
-            for (int r = 0; r < ND; ++r) Qa[r] = q_row(t, i, r, m, g);
+            for (int r = 0; r < ND; r += 2) q_row2(t, i, r, m, g, Qa[r], Qa[r + 1]);
             const f32x4 O = mma_state_a<E, ND>(zero4(), Wr, Qa);
             const int tk = s + 16 * i + m;
             if (tk < tend) store4<E>(out_h + (size_t)tk * D + 16 * c + 4 * g, out4<E>(O));
