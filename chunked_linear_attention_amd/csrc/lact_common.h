@@ -34,7 +34,8 @@ __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rc
 // Generic GEMM tile: C[m][n] = sum_k A[m][k] B[n][k] (bf16), block tile
 // BM x 128 with BM = 32 MB, 4 waves as 2 x 2 of (16 MB) x 64, k step 64, K a
 // multiple of 64.  MB = 4 is the 128 x 128 tile; MB = 8 (256 x 128, wave tiles
-// of 128 x 64) reads half as many LDS bytes per multiply-add from the A side.
+// of 128 x 64) reads half as many LDS bytes per multiply-add from the A side;
+// MB = 2 (64 x 128) gives small products twice the workgroups.
 // An operand is stored either k-contiguous (row m of A at A + m * lda,
 // 128-byte rows per stage) or, with AT / BT, k-major (row k at A + k * lda,
 // holding M contiguous elements: a token-major tensor read as its transpose),
@@ -56,12 +57,15 @@ __device__ __forceinline__ int kperm(int k)
 }
 
 template <int BM> struct GemmLdsT {
-    bf16 a[2][BM][GPITCH];
+    // at BM = 64 the k-major A stage (64 k rows of BM + 16) needs 72 rows
+    static constexpr int AR = BM < 72 ? 72 : BM;
+    bf16 a[2][AR][GPITCH];
     bf16 b[2][128][GPITCH];
 };
 using GemmLds = GemmLdsT<128>;
 static_assert(sizeof(bf16[GBK][GTPITCH]) <= sizeof(bf16[128][GPITCH]), "k-major stage fits the buffer");
 static_assert(sizeof(bf16[GBK][256 + 16]) <= sizeof(bf16[256][GPITCH]), "k-major stage fits the buffer");
+static_assert(sizeof(bf16[GBK][64 + 16]) <= sizeof(bf16[GemmLdsT<64>::AR][GPITCH]), "k-major stage fits the buffer");
 
 // K is cut into nseg segments of kseg (a multiple of 64); segment s reads A
 // from As[s] and B from Bs[s] (same leading dimensions; As and Bs are arrays
@@ -77,7 +81,8 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const PA &A
                                                int nseg, int m0, int n0, int kvalid, int st_lo, int nlive,
                                                int nloop, int tid, f32x4 (&acc)[MB][4])
 {
-    static_assert(MB == 4 || MB == 8, "block rows 128 or 256");
+    static_assert(MB == 2 || MB == 4 || MB == 8, "block rows 64, 128 or 256");
+    constexpr int NP = MB > 4 ? MB : 4;  // pieces per thread and side, at most
     constexpr int BM = 32 * MB;
     constexpr int TPA = BM + 16;        // k-major A stage pitch
     constexpr int AKT = BM / 8;         // threads per k-major A row (8 elements each)
@@ -88,12 +93,11 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const PA &A
     // Pieces of 16 bytes per thread: MB for A, 4 for B.  k-contiguous: rows
     // tid/8 + 32 i, 8 columns each.  k-major: k rows tid/(BM/8) + (2048/BM) i
     // of A (tid/16 + 16 i of B), 8 of the row's elements each.
-    int lrow[MB], lcol, krow[4], kcol, akrow[MB], akcol;
+    int lrow[NP], lcol, krow[4], kcol, akrow[MB], akcol;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        lrow[i] = (tid >> 3) + 32 * i;
-        akrow[i] = tid / AKT + (256 / AKT) * i;
-    }
+    for (int i = 0; i < NP; ++i) lrow[i] = (tid >> 3) + 32 * i;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) akrow[i] = tid / AKT + (256 / AKT) * i;
 #pragma unroll
     for (int i = 0; i < 4; ++i) krow[i] = (tid >> 4) + 16 * i;
     lcol = (tid & 7) * 8;
@@ -113,11 +117,13 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const PA &A
         const bf16 *A = As[sg], *B = Bs[sg];
         // A piece i, then B piece i (the order of the 128-row tile)
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            if constexpr (AT)
-                ra[s][i] = ld16(A + (long)min(kin + akrow[i], kvalid - 1) * lda + m0 + akcol);
-            else
-                ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
+        for (int i = 0; i < NP; ++i) {
+            if (i < MB) {
+                if constexpr (AT)
+                    ra[s][i] = ld16(A + (long)min(kin + akrow[i], kvalid - 1) * lda + m0 + akcol);
+                else
+                    ra[s][i] = ld16(A + (long)min(m0 + lrow[i], M - 1) * lda + kin + lcol);
+            }
             if (i < 4) {
                 if constexpr (BT)
                     rb[s][i & 3] = ld16(B + (long)min(kin + krow[i & 3], kvalid - 1) * ldb + n0 + kcol);
@@ -132,12 +138,14 @@ __device__ __forceinline__ void gemm_tile_core(GemmLdsT<32 * MB> &L, const PA &A
         const bool live = st < nlive;
         const int kin = (min(st_lo + st, nst - 1) * GBK) % kseg;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            if constexpr (AT) {
-                bf16(*T)[TPA] = reinterpret_cast<bf16(*)[TPA]>(&L.a[buf][0][0]);
-                st16(&T[kperm(akrow[i])][akcol], (live && kin + akrow[i] < kvalid) ? ra[s][i] : zero16());
-            } else {
-                st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
+        for (int i = 0; i < NP; ++i) {
+            if (i < MB) {
+                if constexpr (AT) {
+                    bf16(*T)[TPA] = reinterpret_cast<bf16(*)[TPA]>(&L.a[buf][0][0]);
+                    st16(&T[kperm(akrow[i])][akcol], (live && kin + akrow[i] < kvalid) ? ra[s][i] : zero16());
+                } else {
+                    st16(&L.a[buf][lrow[i]][lcol], (live && aok[i]) ? ra[s][i] : zero16());
+                }
             }
             if (i < 4) {
                 if constexpr (BT) {

@@ -538,29 +538,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
 // by it.  Operands are bf16 copies of the iterate; the iterate itself and all
 // accumulations are fp32.
 // ---------------------------------------------------------------------------
-// fp32 staging of a 128 x 128 product tile in the GEMM's LDS (rows padded by
-// 4: a fragment write's 4 row groups fall 16 banks apart)
+// Both kernels run 64 x 128 output tiles: the matrices are small (a few
+// hundred rows), so the launches are latency-bound and the smaller tile
+// doubles the workgroups and halves each wave's products per k step.
+constexpr int NSMB = 2, NSBM = 32 * NSMB;
+using NsLds = GemmLdsT<NSBM>;
+// fp32 staging of a product tile in the GEMM's LDS (rows padded by 4: a
+// fragment write's 4 row groups fall 16 banks apart)
 constexpr int NSPITCH = 128 + 4;
-static_assert(sizeof(float[128][NSPITCH]) <= sizeof(GemmLds), "staged tile fits the GEMM's LDS");
+static_assert(sizeof(float[NSBM][NSPITCH]) <= sizeof(NsLds), "staged tile fits the GEMM's LDS");
 
 __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
 {
-    __shared__ GemmLds L;
+    __shared__ NsLds L;
     const int d = p.d, hid = p.hid;
-    const int tpm = d / 128;
+    const int tpn = d / 128, tpt = (d / NSBM) * tpn;
     int bid = xcd_block(blockIdx.x, gridDim.x);
-    const int tile = bid % (tpm * tpm);
-    bid /= tpm * tpm;
+    const int tile = bid % tpt;
+    bid /= tpt;
     const int which = bid % 3, h = bid / 3;
-    const int tm = tile / tpm, tn = tile % tpm;
+    const int tm = tile / tpn, tn = tile % tpn;
     const long n13 = (long)hid * d;
     const bf16 *x = p.nsb + (long)(step & 1) * p.NH * 3 * n13 + ((long)h * 3 + which) * n13;
     bf16 *gr = p.gram + ((long)h * 3 + which) * d * d;
     float *dg = p.diag + ((long)h * 3 + which) * d;
     // direct stores: staging this small bf16 tile through LDS measured ~1% slower
-    auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+    auto epi = [&](f32x4 (&acc)[NSMB][4], int mb, int nb, int g, int mm) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NSMB; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -572,17 +577,17 @@ __global__ __launch_bounds__(256) void lact_ns_gram(LactParams p, int step)
     };
     const bf16 *as[1] = {x};
     if (which < 2)  // T = X [hid][d]: T^T T, both operands k-major
-        gemm_nt_tile<true, true>(L, as, d, as, d, d, d, hid, 1, tm * 128, tn * 128, hid, epi);
+        gemm_nt_tile<true, true, NSMB>(L, as, d, as, d, d, d, hid, 1, tm * NSBM, tn * 128, hid, epi);
     else            // T = X^T, X [d][hid]: X X^T
-        gemm_nt_tile<false, false>(L, as, hid, as, hid, d, d, hid, 1, tm * 128, tn * 128, 1 << 30, epi);
+        gemm_nt_tile<false, false, NSMB>(L, as, hid, as, hid, d, d, hid, 1, tm * NSBM, tn * 128, 1 << 30, epi);
 }
 
 __global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
 {
-    __shared__ GemmLds L;
+    __shared__ NsLds L;
     __shared__ float red[4];
     const int d = p.d, hid = p.hid;
-    const int tpm = (hid / 128) * (d / 128);
+    const int tpm = (hid / NSBM) * (d / 128);  // tiles per matrix (either orientation)
     int bid = xcd_block(blockIdx.x, gridDim.x);
     const int tile = bid % tpm;
     bid /= tpm;
@@ -609,13 +614,13 @@ __global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
     const int N = (which < 2) ? d : hid;
     const int tm = (which < 2) ? tile / (d / 128) : tile / (hid / 128);
     const int tn = (which < 2) ? tile % (d / 128) : tile % (hid / 128);
-    const int m0 = tm * 128, n0 = tn * 128;
-    auto epi = [&](f32x4 (&acc)[4][4], int mb, int nb, int g, int mm) {
+    const int m0 = tm * NSBM, n0 = tn * 128;
+    auto epi = [&](f32x4 (&acc)[NSMB][4], int mb, int nb, int g, int mm) {
         // the product tile goes through LDS (free after the k loop's last
         // barrier); the iterate is then read and written as whole rows
         float(*S)[NSPITCH] = reinterpret_cast<float(*)[NSPITCH]>(&L);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NSMB; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
         __syncthreads();
         const int t = threadIdx.x;
 #pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < NSBM / 8; ++it) {
             const int r = (t >> 5) + 8 * it, c = (t & 31) * 4;
             const long e = (long)(m0 + r) * N + n0 + c;
             const f32x4 xo = load4<float>(xf + e);
@@ -643,11 +648,11 @@ __global__ __launch_bounds__(256) void lact_ns_apply(LactParams p, int step)
     if (which < 2) {  // X [hid][d]: X G, G symmetric (row-major = its own transpose)
         const bf16 *as[1] = {x};
         const bf16 *bs[1] = {gr};
-        gemm_nt_tile<false, false>(L, as, d, bs, d, hid, d, d, 1, tm * 128, tn * 128, 1 << 30, epi);
+        gemm_nt_tile<false, false, NSMB>(L, as, d, bs, d, hid, d, d, 1, m0, n0, 1 << 30, epi);
     } else {          // X [d][hid]: G X, X read k-major
         const bf16 *as[1] = {gr};
         const bf16 *bs[1] = {x};
-        gemm_nt_tile<false, true>(L, as, d, bs, hid, d, hid, d, 1, tm * 128, tn * 128, d, epi);
+        gemm_nt_tile<false, true, NSMB>(L, as, d, bs, hid, d, hid, d, 1, m0, n0, d, epi);
     }
 }
 
@@ -962,8 +967,8 @@ hipError_t lact_launch(const LactShape &s, const LactPlan &pl, const void *q, co
         if (s.rule == 2) {
             lact_update<<<dim3((urows + 3) / 4), dim3(256), 0, st>>>(p, dst, 1);
             for (int j = 0; j < s.ns_steps; ++j) {
-                lact_ns_gram<<<dim3(s.NH * 3 * (s.d / 128) * (s.d / 128)), dim3(256), 0, st>>>(p, j);
-                lact_ns_apply<<<dim3(s.NH * 3 * t13), dim3(256), 0, st>>>(p, j);
+                lact_ns_gram<<<dim3(s.NH * 3 * (s.d / NSBM) * (s.d / 128)), dim3(256), 0, st>>>(p, j);
+                lact_ns_apply<<<dim3(s.NH * 3 * (s.hid / NSBM) * (s.d / 128)), dim3(256), 0, st>>>(p, j);
             }
         }
         p.save_c = c;

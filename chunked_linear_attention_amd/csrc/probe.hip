@@ -105,7 +105,7 @@ static void probe_gemm_launch(const bf16 *A, const bf16 *B, float *c, int M, int
 extern "C" ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c, int M, int N, int K, int a_kmajor,
                                           int b_kmajor, int block_rows, int wave_groups, void *stream)
 {
-    if (!a || !b || !c || (block_rows != 128 && block_rows != 256)) return TTT_EINVAL;
+    if (!a || !b || !c || (block_rows != 64 && block_rows != 128 && block_rows != 256)) return TTT_EINVAL;
     if (wave_groups != 1 && (wave_groups != 2 || block_rows != 128)) return TTT_EINVAL;
     if (M < block_rows || N < 128 || K < 64 || M % block_rows || N % 128 || K % 64) return TTT_EINVAL;
     if ((long long)(M / block_rows) * (N / 128) > (1 << 24)) return TTT_EUNSUPPORTED;
@@ -123,6 +123,8 @@ extern "C" ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c
             tttk::probe_gemm_tile_kg2<false, false><<<grid, block, 0, st>>>(A, B, c, M, N, K);
     } else if (block_rows == 256)
         tttk::probe_gemm_launch<8>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
+    else if (block_rows == 64)
+        tttk::probe_gemm_launch<2>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
     else
         tttk::probe_gemm_launch<4>(A, B, c, M, N, K, a_kmajor, b_kmajor, st);
     return hipGetLastError() == hipSuccess ? TTT_OK : TTT_EHIP;

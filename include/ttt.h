@@ -387,12 +387,12 @@ ttt_status ttt_probe_mfma_bf16(float *out, int blocks, int iters, void *stream);
  * kernels share, on a plain product, so its rate can be measured:
  * C[m][n] = sum_k A[m][k] B[n][k], fp32 accumulation and output, one
  * workgroup per block_rows x 128 tile of C (block_rows 128: four 64 x 64 wave
- * tiles; 256: four 128 x 64 wave tiles).  wave_groups 2 (block_rows 128 only)
+ * tiles; 256: four 128 x 64 wave tiles; 64: four 32 x 64 wave tiles).  wave_groups 2 (block_rows 128 only)
  * runs each tile with eight waves, the second four taking the second half of
  * the k steps.  A is [M][K] bf16 (a_kmajor = 0) or [K][M] (a_kmajor = 1,
  * read as its transpose); B likewise [N][K] or [K][N]; C [M][N] fp32, all
  * row-major, device memory, 16-byte aligned.  M a multiple of block_rows, N
- * of 128, K of 64, block_rows 128 or 256, wave_groups 1 or 2, else
+ * of 128, K of 64, block_rows 64, 128 or 256, wave_groups 1 or 2, else
  * TTT_EINVAL.
  * ------------------------------------------------------------------------ */
 ttt_status ttt_probe_gemm_bf16(const void *a, const void *b, float *c, int M, int N, int K, int a_kmajor,

@@ -8,7 +8,7 @@ import torch
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("rows,groups", [(128, 1), (256, 1), (128, 2)])
+@pytest.mark.parametrize("rows,groups", [(128, 1), (256, 1), (64, 1), (128, 2)])
 @pytest.mark.parametrize("ak,bk", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_gemm_tile_probe_matches_fp32_product(ak, bk, rows, groups):
     import chunked_linear_attention_amd._lib as L
@@ -37,7 +37,8 @@ def test_probe_argument_checks():
     assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 100, 128, 64, 0, 0, 128, 1, None) == L.TTT_EINVAL
     assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 96, 0, 0, 128, 1, None) == L.TTT_EINVAL
     assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 256, 1, None) == L.TTT_EINVAL
-    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 64, 1, None) == L.TTT_EINVAL
+    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 96, 1, None) == L.TTT_EINVAL
+    assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 64, 2, None) == L.TTT_EINVAL
     assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 128, 128, 64, 0, 0, 128, 3, None) == L.TTT_EINVAL
     assert lib.ttt_probe_gemm_bf16(x.data_ptr(), x.data_ptr(), c.data_ptr(), 256, 128, 64, 0, 0, 256, 2, None) == L.TTT_EINVAL
     assert lib.ttt_probe_mfma_bf16(c.data_ptr(), 0, 1, None) == L.TTT_EINVAL
