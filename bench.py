@@ -202,7 +202,7 @@ def measured_peaks():
 
 def gemm_probe(steps=20, warmup=3):
     """The LaCT kernels' shared GEMM tile (128 x 128 blocks of four or eight
-    waves, 256 x 128 blocks of four) on plain bf16 products
+    waves, 256 x 128 and 64 x 128 blocks of four) on plain bf16 products
     (ttt_probe_gemm_bf16, fp32 out), beside the vendor GEMM
     behind torch.matmul on the same shapes (bf16 in and out) for context; each
     checked against an fp32 product of the same bf16 values on a small shape
@@ -236,7 +236,7 @@ def gemm_probe(steps=20, warmup=3):
         a = torch.randn((K, M) if ak else (M, K), device="cuda", generator=g).to(torch.bfloat16)
         b = torch.randn((K, N) if bk else (N, K), device="cuda", generator=g).to(torch.bfloat16)
         ref = (a.float().t() if ak else a.float()) @ (b.float() if bk else b.float().t())
-        for rows, groups in ((128, 1), (256, 1), (128, 2)):
+        for rows, groups in ((128, 1), (256, 1), (64, 1), (128, 2)):
             c = torch.empty(M, N, device="cuda")
             ours(a, b, c, M, N, K, ak, bk, rows, groups)
             torch.cuda.synchronize()
@@ -257,6 +257,7 @@ def gemm_probe(steps=20, warmup=3):
         ms = timed(lambda: ours(a, b, c, M, N, K, ak, bk))
         ms_w = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 256)) if M % 256 == 0 else float("nan")
         ms_2 = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 128, 2))
+        ms_n = timed(lambda: ours(a, b, c, M, N, K, ak, bk, 64))
         at = a.t() if ak else a
         bt = b if bk else b.t()
         at, bt = at.contiguous(), bt.contiguous()
@@ -266,6 +267,7 @@ def gemm_probe(steps=20, warmup=3):
                     "tile_tflops": fl / (ms * 1e-3) / 1e12, "tile_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                     "wide_tile_us": ms_w * 1e3, "wide_tile_tflops": fl / (ms_w * 1e-3) / 1e12,
                     "eight_wave_tile_us": ms_2 * 1e3, "eight_wave_tile_tflops": fl / (ms_2 * 1e-3) / 1e12,
+                    "narrow_tile_us": ms_n * 1e3, "narrow_tile_tflops": fl / (ms_n * 1e-3) / 1e12,
                     "vendor_us": vms * 1e3, "vendor_tflops": fl / (vms * 1e-3) / 1e12})
         del a, b, c, at, bt
     return out
